@@ -1,0 +1,225 @@
+/*
+ * moe.h - C ABI of the routed-expert layer step on AMD Instinct MI355X (gfx950).
+ *
+ * One MoE layer of a GLM-5.2-shaped model, as the Colibri pages state it
+ * ("Public Colibri Observation and Revision Ledger", section "Exact
+ * Architecture and Data-Flow Reconstruction"): per layer and batch,
+ * (1) Route: a float32 sigmoid gate scores every expert (n_group = 1) and the
+ *     top-k experts are selected,
+ * (2) Union: requests of the batch are merged so each distinct expert is used
+ *     once (same page, "Cache/Prefetch Design Comparison", figure on async
+ *     I/O and prefetch: "batch-union"),
+ * (5) Learn: per-expert hit counters are bumped,
+ * and the expert math: each chosen expert is a three-matrix MLP, plus an
+ * always-on shared expert. The experts sit in an HBM-resident pool; the
+ * pages' Place and Overlap stages (disk, RAM and VRAM tiers) have no
+ * counterpart here because every expert is resident.
+ *
+ * Readings where the pages are silent:
+ *   score      s[t][e] = sigmoid(b[e] + sum_i Wr[e][i] x[t][i]), float32
+ *   top-k      k largest s per token, ties to the lower expert id, ids in rank
+ *              order; the gate weight of a slot is its raw score
+ *   expert     o = Wd (silu(Wg x) * (Wu x)), silu(z) = z / (1 + exp(-z))
+ *   weights    W[r][c] = q[r][c] * scale[r][c / G] (symmetric codes)
+ *   combine    y[t] = shared(x_t) + sum_j w[t][j] * o_{t,j}
+ *   counters   counters[e] += number of (token, slot) assignments to e
+ *
+ * Conventions for every call:
+ *   - Array arguments are DEVICE pointers unless marked (host). The caller
+ *     owns every buffer; the library allocates nothing and keeps no state
+ *     between calls. Calls on different streams with disjoint outputs may
+ *     run concurrently.
+ *   - Calls enqueue work on `stream` and return without synchronising.
+ *     n_union and the permutation stay on the device; moe_expert_forward
+ *     reads them there, so a layer step needs no host round trip.
+ *   - Arguments are checked on the host before any HIP call. A failed check
+ *     returns a negative moe_status and enqueues nothing. A launch failure
+ *     returns MOE_EHIP. Faults during execution surface at the caller's next
+ *     synchronisation. After an error the outputs are unspecified.
+ *   - n_tokens == 0 is a successful no-op.
+ *   - Row-major layouts throughout. x is [n_tokens][d_model] float32.
+ *   - The activations are staged through float16 inside the expert kernels
+ *     with a per-token power-of-two scale: inputs must be finite and every
+ *     hidden value |silu(g) * u| (times its token's scale) must stay below
+ *     65504, which holds with a wide margin for normalised activations.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,          /* null pointer, negative size, bad k, bad wbits */
+    MOE_ESHAPE = -2,          /* shape the kernels do not support (see below) */
+    MOE_EALIGN = -3,          /* pointer or stride not aligned as required */
+    MOE_EWORKSPACE = -4,      /* workspace missing or smaller than required */
+    MOE_EHIP = -5             /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+#define MOE_MAX_K 32          /* largest top-k */
+#define MOE_MAX_EXPERTS 1024  /* largest number of routed experts per layer */
+#define MOE_ALIGN 256         /* alignment of pools, blocks and workspaces */
+
+/*
+ * One layer's expert pool (the struct itself is host memory; the blocks are
+ * device memory).
+ *
+ * Block format. The Colibri pages store an expert's three matrices next to
+ * each other and read them as one block ("Storage, Memory, and I/O Formulas";
+ * README "Never wait for the disk twice"); their container is int4 with
+ * group scales (README "Get started") and the draft head is int8 (README
+ * "Speculative decoding, honestly"). A block holds, in order:
+ *   gate codes [f][d], up codes [f][d], down codes [d][f]
+ *   gate scales [f][d/G], up scales [f][d/G], down scales [d][f/G]  (float32)
+ * with f = d_ff, d = d_model and G = group (G == 0: one scale per row, so
+ * d and f scales per gate/up and down row respectively). Codes are
+ * wbits-bit integers stored offset-binary on the device (code + 8 per nibble,
+ * code + 128 per byte); int4 packs element 2i in the low nibble of byte i.
+ * moe_pack_expert writes this layout from the two's-complement canonical one.
+ *
+ * Supported shapes: wbits 4 or 8; e = 32 (int4) or 16 (int8) elements per
+ * 16-byte chunk; d and f multiples of e with d/e and f/e each either a power
+ * of two from 2 to 64 or 64 times one of 1, 2, 3, 4, 6, 8 (int4: up to
+ * d_model 16384); G == 0 or G a multiple of e
+ * dividing both d and f; pool, shared and expert_bytes multiples of MOE_ALIGN,
+ * expert_bytes >= moe_block_bytes(...).
+ */
+typedef struct {
+    int32_t d_model;
+    int32_t d_ff;
+    int32_t n_experts;        /* routed experts, 1..MOE_MAX_EXPERTS */
+    int32_t wbits;            /* 4 or 8 */
+    int32_t group;            /* scale group along the input dimension; 0 = per row */
+    const void *pool;         /* n_experts blocks, expert_bytes apart */
+    size_t expert_bytes;      /* block stride */
+    const void *shared;       /* the shared expert's block, or NULL for none */
+} moe_expert_pool;
+
+/*
+ * Route. scores = sigmoid(x Wr^T + b) in float32 (workspace), then per token
+ * the k best experts: topk_ids [n_tokens][k] int32 in rank order (ties to the
+ * lower id; a NaN score ranks above every number) and topk_w [n_tokens][k]
+ * float32, the chosen scores.
+ *   w_router [n_experts][d_model] float32; b_router [n_experts] or NULL.
+ *   d_model must be a multiple of 16; x and w_router 16-byte aligned.
+ *   workspace: at least moe_route_workspace_size(n_tokens, n_experts) bytes,
+ *   MOE_ALIGN-aligned.
+ * Colibri pages: "Exact Architecture and Data-Flow Reconstruction" (sigmoid
+ * router, n_group = 1, float32 gate parameters).
+ */
+moe_status moe_route_topk(const float *x, int n_tokens, int d_model,
+                          const float *w_router, const float *b_router,
+                          int n_experts, int k,
+                          int32_t *topk_ids, float *topk_w,
+                          void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Union and permutation of the batch's n_tokens*k assignments a = t*k + j.
+ *   union_ids [n_experts]: the distinct routed ids ascending (first *n_union
+ *   entries valid); n_union [1]; expert_offsets [n_experts+1]: exclusive
+ *   prefix of the per-expert counts; perm [n_tokens*k]: the assignments
+ *   grouped by expert, expert_offsets[e] .. expert_offsets[e+1] holding
+ *   expert e's assignments in ascending a (a stable counting sort, so the
+ *   result does not depend on thread timing). Ids outside [0, n_experts) are
+ *   left out of every output.
+ * Colibri pages: "Exact Architecture and Data-Flow Reconstruction", stage (2)
+ * Union; "Cache/Prefetch Design Comparison", batch-union.
+ */
+moe_status moe_union(const int32_t *topk_ids, int n_tokens, int k, int n_experts,
+                     int32_t *union_ids, int32_t *n_union,
+                     int32_t *expert_offsets, int32_t *perm, hipStream_t stream);
+
+/*
+ * Expert math and combine:
+ *   y[t] = shared(x_t) + sum_{j<k} topk_w[t][j] * E_{e(t,j)}(x_t),
+ *   E(x) = Wd (silu(Wg x) * (Wu x)),
+ * over the union produced by moe_union (union_ids, n_union, expert_offsets,
+ * perm are its outputs for the same n_tokens and k). topk_w is an input, so a
+ * caller may inject gate weights. Each distinct expert's weights are streamed
+ * once per call for all of its tokens. y [n_tokens][d_model] float32 is
+ * overwritten. workspace: at least moe_forward_workspace_size(pool, n_tokens,
+ * k) bytes, MOE_ALIGN-aligned.
+ * Colibri pages: "Exact Architecture and Data-Flow Reconstruction" (three-
+ * matrix expert MLP, always-on shared expert); README "Get started" (int4
+ * group-scaled experts).
+ */
+moe_status moe_expert_forward(const moe_expert_pool *pool /* (host) */,
+                              const float *x, int n_tokens, int k,
+                              const float *topk_w,
+                              const int32_t *union_ids, const int32_t *n_union,
+                              const int32_t *expert_offsets, const int32_t *perm,
+                              float *y, void *workspace, size_t ws_bytes,
+                              hipStream_t stream);
+
+/*
+ * moe_expert_forward with timing: the same computation, and when `events` is
+ * not NULL each non-NULL event in it is recorded on `stream` right before or
+ * after the kernel it names (events are created and owned by the caller).
+ * Lets a caller time the expert kernels alone with HIP events.
+ */
+typedef struct {
+    hipEvent_t gateup_start, gateup_end;  /* around the gate/up kernel */
+    hipEvent_t down_start, down_end;      /* around the down kernel */
+} moe_forward_events;
+
+moe_status moe_expert_forward_timed(const moe_expert_pool *pool /* (host) */,
+                                    const float *x, int n_tokens, int k,
+                                    const float *topk_w,
+                                    const int32_t *union_ids, const int32_t *n_union,
+                                    const int32_t *expert_offsets, const int32_t *perm,
+                                    float *y, void *workspace, size_t ws_bytes,
+                                    hipStream_t stream,
+                                    const moe_forward_events *events /* (host) */);
+
+/*
+ * Learn: counters[e] += #{(t, j) : topk_ids[t][j] == e}, uint64, accumulated
+ * in place (device atomics, so concurrent calls on one counter table add up).
+ * The shared expert is not counted. Ids outside [0, n_experts) are ignored.
+ * Colibri pages: "Exact Architecture and Data-Flow Reconstruction", stage (5)
+ * Learn: per-expert hit counters.
+ */
+moe_status moe_hit_count(const int32_t *topk_ids, int n_tokens, int k, int n_experts,
+                         uint64_t *counters, hipStream_t stream);
+
+/*
+ * Residual chaining of stacked layers (not one of the pages' stages; the
+ * pages keep layer norms resident in float32 and give no formula):
+ *   h[t] += y[t] (skipped when y is NULL), then
+ *   a[t] = h[t] / sqrt(mean_i h[t][i]^2 + eps).
+ * h, y, a are [n_tokens][d_model] float32; a may not alias h.
+ */
+moe_status moe_residual_rmsnorm(float *h, const float *y, float *a, int n_tokens,
+                                int d_model, float eps, hipStream_t stream);
+
+/* Workspace sizes in bytes (host-only arithmetic, no HIP calls). */
+size_t moe_route_workspace_size(int n_tokens, int n_experts);
+size_t moe_forward_workspace_size(const moe_expert_pool *pool, int n_tokens, int k);
+/* The larger of the two, for one buffer shared by a layer step's calls. */
+size_t moe_workspace_size(const moe_expert_pool *pool, int n_tokens, int k);
+
+/* Bytes of one expert block (same for the canonical and device layouts). */
+size_t moe_block_bytes(int d_model, int d_ff, int wbits, int group);
+
+/*
+ * (host) Converts one canonical block (two's-complement codes, layout as
+ * above) into the device layout. Both buffers are host memory of
+ * moe_block_bytes(...) bytes; they may be the same buffer.
+ */
+moe_status moe_pack_expert(const void *canonical_block, const moe_expert_pool *shape,
+                           void *block_out);
+
+/* Static text for a status code. */
+const char *moe_strerror(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

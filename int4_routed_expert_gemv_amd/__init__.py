@@ -1,0 +1,257 @@
+"""Python binding of the routed-expert layer step (libmoe.so, include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI. PyTorch provides device memory and the stream. If the
+library has not been built, the binding raises. There is no fallback path.
+
+The layer (after the Colibri pages, "Public Colibri Observation and Revision
+Ledger", section "Exact Architecture and Data-Flow Reconstruction"):
+  route_topk      float32 sigmoid router over all experts (n_group = 1) + top-k
+  union           batch union of the routed experts + token->expert permutation
+  hit_count       per-expert hit counters (the Learn stage)
+  expert_forward  int4/int8 SwiGLU experts over the union + the shared expert,
+                  combined by gate weight
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4, -5
+MOE_MAX_K = 32
+MOE_MAX_EXPERTS = 1024
+MOE_ALIGN = 256
+
+EXPORTED = [
+    "moe_route_topk", "moe_union", "moe_expert_forward", "moe_expert_forward_timed",
+    "moe_hit_count", "moe_residual_rmsnorm", "moe_route_workspace_size", "moe_forward_workspace_size",
+    "moe_workspace_size", "moe_block_bytes", "moe_pack_expert", "moe_strerror",
+]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {strerror(status)} (status {status})")
+
+
+class ForwardEvents(ctypes.Structure):
+    """struct moe_forward_events (HIP event handles, NULL = not recorded)"""
+    _fields_ = [("gateup_start", ctypes.c_void_p), ("gateup_end", ctypes.c_void_p),
+                ("down_start", ctypes.c_void_p), ("down_end", ctypes.c_void_p)]
+
+
+class PoolDesc(ctypes.Structure):
+    """struct moe_expert_pool"""
+    _fields_ = [
+        ("d_model", ctypes.c_int32),
+        ("d_ff", ctypes.c_int32),
+        ("n_experts", ctypes.c_int32),
+        ("wbits", ctypes.c_int32),
+        ("group", ctypes.c_int32),
+        ("pool", ctypes.c_void_p),
+        ("expert_bytes", ctypes.c_size_t),
+        ("shared", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m int4_routed_expert_gemv_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+        P = ctypes.POINTER(PoolDesc)
+        L.moe_route_topk.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, vp, vp, sz, vp]
+        L.moe_union.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp]
+        L.moe_expert_forward.argtypes = [P, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_expert_forward_timed.argtypes = [P, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                               ctypes.POINTER(ForwardEvents)]
+        L.moe_hit_count.argtypes = [vp, i32, i32, i32, vp, vp]
+        L.moe_residual_rmsnorm.argtypes = [vp, vp, vp, i32, i32, f32, vp]
+        L.moe_route_workspace_size.argtypes = [i32, i32]
+        L.moe_forward_workspace_size.argtypes = [P, i32, i32]
+        L.moe_workspace_size.argtypes = [P, i32, i32]
+        L.moe_block_bytes.argtypes = [i32, i32, i32, i32]
+        L.moe_pack_expert.argtypes = [vp, P, vp]
+        L.moe_strerror.argtypes = [i32]
+        L.moe_strerror.restype = ctypes.c_char_p
+        for name in ("moe_route_topk", "moe_union", "moe_expert_forward",
+                     "moe_expert_forward_timed", "moe_hit_count",
+                     "moe_residual_rmsnorm", "moe_pack_expert"):
+            getattr(L, name).restype = i32
+        for name in ("moe_route_workspace_size", "moe_forward_workspace_size",
+                     "moe_workspace_size", "moe_block_bytes"):
+            getattr(L, name).restype = sz
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().moe_strerror(status).decode()
+
+
+def _check(status: int, call: str):
+    if status != MOE_OK:
+        raise MoeError(status, call)
+
+
+def _ptr(t) -> int | None:
+    """Device pointer of a tensor (None stays NULL)."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _expect(t, dtype, name):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor")
+
+
+# --------------------------------------------------------------------- sizes
+
+def block_bytes(d_model, d_ff, wbits, group) -> int:
+    return int(lib().moe_block_bytes(d_model, d_ff, wbits, group))
+
+
+def route_workspace_size(n_tokens, n_experts) -> int:
+    return int(lib().moe_route_workspace_size(n_tokens, n_experts))
+
+
+def forward_workspace_size(pool: PoolDesc, n_tokens, k) -> int:
+    return int(lib().moe_forward_workspace_size(ctypes.byref(pool), n_tokens, k))
+
+
+def workspace_size(pool: PoolDesc, n_tokens, k) -> int:
+    return int(lib().moe_workspace_size(ctypes.byref(pool), n_tokens, k))
+
+
+# --------------------------------------------------------------------- calls
+
+def route_topk(x, w_router, b_router, k, topk_ids, topk_w, workspace, stream=None):
+    import torch
+    _expect(x, torch.float32, "x")
+    _expect(w_router, torch.float32, "w_router")
+    _expect(b_router, torch.float32, "b_router")
+    _expect(topk_ids, torch.int32, "topk_ids")
+    _expect(topk_w, torch.float32, "topk_w")
+    N, d = x.shape
+    E = w_router.shape[0]
+    _check(lib().moe_route_topk(_ptr(x), N, d, _ptr(w_router), _ptr(b_router), E, k,
+                                _ptr(topk_ids), _ptr(topk_w), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)),
+           "moe_route_topk")
+
+
+def union(topk_ids, n_experts, union_ids, n_union, expert_offsets, perm, stream=None):
+    import torch
+    for t, n in ((topk_ids, "topk_ids"), (union_ids, "union_ids"), (n_union, "n_union"),
+                 (expert_offsets, "expert_offsets"), (perm, "perm")):
+        _expect(t, torch.int32, n)
+    N, k = topk_ids.shape
+    _check(lib().moe_union(_ptr(topk_ids), N, k, n_experts, _ptr(union_ids), _ptr(n_union),
+                           _ptr(expert_offsets), _ptr(perm), _stream(stream)), "moe_union")
+
+
+def hit_count(topk_ids, n_experts, counters, stream=None):
+    import torch
+    _expect(topk_ids, torch.int32, "topk_ids")
+    if counters.dtype not in (torch.int64, torch.uint64):
+        raise TypeError("counters: expected a 64-bit integer tensor")
+    N, k = topk_ids.shape
+    _check(lib().moe_hit_count(_ptr(topk_ids), N, k, n_experts, _ptr(counters), _stream(stream)),
+           "moe_hit_count")
+
+
+def expert_forward(pool: PoolDesc, x, k, topk_w, union_ids, n_union, expert_offsets, perm, y,
+                   workspace, stream=None, events: ForwardEvents | None = None):
+    """moe_expert_forward, or moe_expert_forward_timed when events are given."""
+    import torch
+    _expect(x, torch.float32, "x")
+    _expect(topk_w, torch.float32, "topk_w")
+    _expect(y, torch.float32, "y")
+    N = x.shape[0]
+    args = (ctypes.byref(pool), _ptr(x), N, k, _ptr(topk_w), _ptr(union_ids), _ptr(n_union),
+            _ptr(expert_offsets), _ptr(perm), _ptr(y), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    if events is None:
+        _check(lib().moe_expert_forward(*args), "moe_expert_forward")
+    else:
+        _check(lib().moe_expert_forward_timed(*args, ctypes.byref(events)),
+               "moe_expert_forward_timed")
+
+
+def residual_rmsnorm(h, y, a, eps=1e-6, stream=None):
+    N, d = h.shape
+    _check(lib().moe_residual_rmsnorm(_ptr(h), _ptr(y), _ptr(a), N, d, eps, _stream(stream)),
+           "moe_residual_rmsnorm")
+
+
+# --------------------------------------------------------------------- pools
+
+def pack_expert(canonical: np.ndarray, shape: PoolDesc, out: np.ndarray | None = None) -> np.ndarray:
+    """Canonical block (host bytes) -> device layout (host bytes); in place if out is canonical."""
+    canonical = np.ascontiguousarray(canonical, np.uint8)
+    out = canonical if out is None else out
+    _check(lib().moe_pack_expert(canonical.ctypes.data, ctypes.byref(shape), out.ctypes.data),
+           "moe_pack_expert")
+    return out
+
+
+class DevicePool:
+    """One layer's experts resident in HBM: packed blocks plus the descriptor.
+
+    blocks: uint8 [n_experts][stride] canonical blocks (host); packed in place.
+    shared: uint8 [stride or block bytes] canonical shared-expert block, or None.
+    """
+
+    def __init__(self, d_model, d_ff, n_experts, wbits, group, blocks, shared, device="cuda"):
+        import torch
+        bb = block_bytes(d_model, d_ff, wbits, group)
+        if bb == 0:
+            raise MoeError(MOE_ESHAPE, "moe_block_bytes")
+        stride = (bb + MOE_ALIGN - 1) // MOE_ALIGN * MOE_ALIGN
+        self.desc = PoolDesc(d_model, d_ff, n_experts, wbits, group, None, stride, None)
+        assert blocks.shape[0] == n_experts and blocks.shape[1] >= bb
+        if blocks.shape[1] != stride:
+            padded = np.zeros((n_experts, stride), np.uint8)
+            padded[:, :blocks.shape[1]] = blocks
+            blocks = padded
+        for e in range(n_experts):
+            pack_expert(blocks[e], self.desc)
+        self.pool = torch.from_numpy(blocks).to(device)
+        self.desc.pool = self.pool.data_ptr()
+        self.shared = None
+        if shared is not None:
+            sh = np.zeros(stride, np.uint8)
+            sh[:bb] = shared[:bb]
+            pack_expert(sh, self.desc)
+            self.shared = torch.from_numpy(sh).to(device)
+            self.desc.shared = self.shared.data_ptr()
+        if self.desc.pool % MOE_ALIGN or (self.shared is not None and self.desc.shared % MOE_ALIGN):
+            raise MoeError(MOE_EALIGN, "DevicePool")
+        self.stride = stride
+        self.block_bytes = bb

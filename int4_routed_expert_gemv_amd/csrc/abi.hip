@@ -1,0 +1,321 @@
+// abi.hip - the C entry points: argument checks, workspace layout, launches.
+//
+// Every check runs on the host before any HIP call, so a rejected call
+// enqueues nothing. The Colibri pages' engine stops the process on bad input
+// ("Failure, Corruption, and Restart Behavior" on the ledger page, which also
+// recommends turning such failures into clear errors); here each failure is a
+// status code instead.
+#include <string.h>
+
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr long long kAlign = MOE_ALIGN;
+
+long long align_up(long long v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p) { return ((uintptr_t)p % kAlign) == 0; }
+
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// Split a row of `cols` codes into lanes-per-row x chunks-per-lane.
+bool row_split(int cols, int epc, int *lpr, int *cpl)
+{
+    if (cols <= 0 || cols % epc) return false;
+    const int cpr = cols / epc;
+    if (cpr >= kWave) {
+        if (cpr % kWave) return false;
+        const int c = cpr / kWave;
+        if (c != 1 && c != 2 && c != 3 && c != 4 && c != 6 && c != 8) return false;
+        *lpr = kWave;
+        *cpl = c;
+        return true;
+    }
+    if (!pow2(cpr) || cpr < 2) return false;
+    *lpr = cpr;
+    *cpl = 1;
+    return true;
+}
+
+long long n_scales(long long rows, long long cols, int group)
+{
+    return group ? rows * (cols / group) : rows;
+}
+
+// Workspace of moe_expert_forward, laid out in this order.
+struct FwdLayout {
+    int tb_gu, tb_dn, max_gu, max_dn, P;
+    long long items_gu, items_dn, n_items, h, o, total;
+};
+
+FwdLayout fwd_layout(const Geo &g, int N, int k, int has_shared)
+{
+    FwdLayout L;
+    const long long A = (long long)N * k;
+    L.tb_gu = tokens_per_item(g.wbits, g.gu_cpl);
+    L.tb_dn = tokens_per_item(g.wbits, g.dn_cpl);
+    const long long ue = A < g.E ? A : g.E;
+    L.max_gu = (int)((A + L.tb_gu - 1) / L.tb_gu + ue + (has_shared ? (N + L.tb_gu - 1) / L.tb_gu : 0));
+    L.max_dn = (int)((A + L.tb_dn - 1) / L.tb_dn + ue + (has_shared ? (N + L.tb_dn - 1) / L.tb_dn : 0));
+    L.P = (int)(A + (has_shared ? N : 0));
+    long long off = 0;
+    L.items_gu = off; off = align_up(off + (long long)L.max_gu * (long long)sizeof(Item));
+    L.items_dn = off; off = align_up(off + (long long)L.max_dn * (long long)sizeof(Item));
+    L.n_items = off; off = align_up(off + 2 * 4);
+    L.h = off; off = align_up(off + (long long)L.P * g.f * 4);
+    L.o = off; off = align_up(off + (long long)L.P * g.d * 4);
+    L.total = off;
+    return L;
+}
+
+moe_status check_k(int k, int E)
+{
+    if (E < 1 || E > MOE_MAX_EXPERTS) return MOE_EINVAL;
+    if (k < 1 || k > MOE_MAX_K || k > E) return MOE_EINVAL;
+    return MOE_OK;
+}
+
+}  // namespace
+
+int tokens_per_item(int wbits, int cpl);
+
+moe_status resolve_geo(const moe_expert_pool *p, Geo *g)
+{
+    if (!p) return MOE_EINVAL;
+    if (p->wbits != 4 && p->wbits != 8) return MOE_EINVAL;
+    if (p->n_experts < 1 || p->n_experts > MOE_MAX_EXPERTS) return MOE_EINVAL;
+    if (p->d_model <= 0 || p->d_ff <= 0 || p->group < 0) return MOE_EINVAL;
+    Geo r;
+    memset(&r, 0, sizeof(r));
+    r.d = p->d_model;
+    r.f = p->d_ff;
+    r.E = p->n_experts;
+    r.wbits = p->wbits;
+    r.group = p->group;
+    r.epc = p->wbits == 4 ? 32 : 16;
+    if (!row_split(r.d, r.epc, &r.gu_lpr, &r.gu_cpl)) return MOE_ESHAPE;
+    if (!row_split(r.f, r.epc, &r.dn_lpr, &r.dn_cpl)) return MOE_ESHAPE;
+    if (r.group) {
+        if (r.group % r.epc || r.d % r.group || r.f % r.group) return MOE_ESHAPE;
+    }
+    r.row_gu = (long long)r.d * r.wbits / 8;
+    r.row_dn = (long long)r.f * r.wbits / 8;
+    r.spr_gu = r.group ? r.d / r.group : 1;
+    r.spr_dn = r.group ? r.f / r.group : 1;
+    const long long q_gu = (long long)r.f * r.row_gu, q_dn = (long long)r.d * r.row_dn;
+    r.off_up = q_gu;
+    r.off_dn = 2 * q_gu;
+    r.off_gs = 2 * q_gu + q_dn;
+    r.off_us = r.off_gs + 4 * n_scales(r.f, r.d, r.group);
+    r.off_ds = r.off_us + 4 * n_scales(r.f, r.d, r.group);
+    *g = r;
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_block_bytes(int d_model, int d_ff, int wbits, int group)
+{
+    if (d_model <= 0 || d_ff <= 0 || (wbits != 4 && wbits != 8) || group < 0) return 0;
+    if (group && (d_model % group || d_ff % group)) return 0;
+    const long long q = (long long)d_model * d_ff * wbits / 8;
+    return (size_t)(3 * q + 4 * (2 * n_scales(d_ff, d_model, group) + n_scales(d_model, d_ff, group)));
+}
+
+size_t moe_route_workspace_size(int n_tokens, int n_experts)
+{
+    if (n_tokens < 0 || n_experts < 1) return 0;
+    return (size_t)align_up((long long)n_tokens * n_experts * 4);
+}
+
+size_t moe_forward_workspace_size(const moe_expert_pool *pool, int n_tokens, int k)
+{
+    Geo g;
+    if (resolve_geo(pool, &g) != MOE_OK || n_tokens < 0 || k < 1) return 0;
+    return (size_t)fwd_layout(g, n_tokens, k, pool->shared != nullptr).total;
+}
+
+size_t moe_workspace_size(const moe_expert_pool *pool, int n_tokens, int k)
+{
+    if (!pool) return 0;
+    size_t a = moe_route_workspace_size(n_tokens, pool->n_experts);
+    size_t b = moe_forward_workspace_size(pool, n_tokens, k);
+    return a > b ? a : b;
+}
+
+const char *moe_strerror(moe_status st)
+{
+    switch (st) {
+    case MOE_OK: return "success";
+    case MOE_EINVAL: return "invalid argument (null pointer, negative size, bad k or wbits)";
+    case MOE_ESHAPE: return "unsupported shape (d_model, d_ff or group)";
+    case MOE_EALIGN: return "pointer or stride not aligned to MOE_ALIGN";
+    case MOE_EWORKSPACE: return "workspace missing or too small";
+    case MOE_EHIP: return "HIP runtime call or kernel launch failed";
+    }
+    return "unknown status";
+}
+
+moe_status moe_route_topk(const float *x, int n_tokens, int d_model, const float *w_router,
+                          const float *b_router, int n_experts, int k, int32_t *topk_ids,
+                          float *topk_w, void *workspace, size_t ws_bytes, hipStream_t stream)
+{
+    if (n_tokens < 0 || d_model <= 0) return MOE_EINVAL;
+    moe_status st = check_k(k, n_experts);
+    if (st != MOE_OK) return st;
+    if (d_model % 16) return MOE_ESHAPE;
+    if ((long long)n_tokens * n_experts > 0x7FFFFFFFLL || (long long)n_tokens * d_model > 0x7FFFFFFFLL)
+        return MOE_ESHAPE;
+    if (n_tokens == 0) return MOE_OK;
+    if (!x || !w_router || !topk_ids || !topk_w) return MOE_EINVAL;
+    if (((uintptr_t)x % 16) || ((uintptr_t)w_router % 16)) return MOE_EALIGN;
+    if (!workspace || ws_bytes < moe_route_workspace_size(n_tokens, n_experts)) return MOE_EWORKSPACE;
+    if (!aligned(workspace)) return MOE_EALIGN;
+    float *scores = static_cast<float *>(workspace);
+    if (launch_router(x, n_tokens, d_model, w_router, b_router, n_experts, scores, stream) !=
+        hipSuccess)
+        return MOE_EHIP;
+    if (launch_topk(scores, n_tokens, n_experts, k, topk_ids, topk_w, stream) != hipSuccess)
+        return MOE_EHIP;
+    return MOE_OK;
+}
+
+moe_status moe_union(const int32_t *topk_ids, int n_tokens, int k, int n_experts,
+                     int32_t *union_ids, int32_t *n_union, int32_t *expert_offsets, int32_t *perm,
+                     hipStream_t stream)
+{
+    if (n_tokens < 0) return MOE_EINVAL;
+    moe_status st = check_k(k, n_experts);
+    if (st != MOE_OK) return st;
+    if ((long long)n_tokens * k > 0x7FFFFFFFLL) return MOE_ESHAPE;
+    if (n_tokens == 0) return MOE_OK;
+    if (!topk_ids || !union_ids || !n_union || !expert_offsets || !perm) return MOE_EINVAL;
+    if (launch_union(topk_ids, n_tokens * k, n_experts, union_ids, n_union, expert_offsets, perm,
+                     stream) != hipSuccess)
+        return MOE_EHIP;
+    return MOE_OK;
+}
+
+moe_status moe_hit_count(const int32_t *topk_ids, int n_tokens, int k, int n_experts,
+                         uint64_t *counters, hipStream_t stream)
+{
+    if (n_tokens < 0) return MOE_EINVAL;
+    moe_status st = check_k(k, n_experts);
+    if (st != MOE_OK) return st;
+    if ((long long)n_tokens * k > 0x7FFFFFFFLL) return MOE_ESHAPE;
+    if (n_tokens == 0) return MOE_OK;
+    if (!topk_ids || !counters) return MOE_EINVAL;
+    if ((uintptr_t)counters % 8) return MOE_EALIGN;
+    if (launch_hit_count(topk_ids, n_tokens * k, n_experts, counters, stream) != hipSuccess)
+        return MOE_EHIP;
+    return MOE_OK;
+}
+
+static bool record(hipEvent_t ev, hipStream_t s)
+{
+    return ev == nullptr || hipEventRecord(ev, s) == hipSuccess;
+}
+
+moe_status moe_expert_forward(const moe_expert_pool *pool, const float *x, int n_tokens, int k,
+                              const float *topk_w, const int32_t *union_ids,
+                              const int32_t *n_union, const int32_t *expert_offsets,
+                              const int32_t *perm, float *y, void *workspace, size_t ws_bytes,
+                              hipStream_t stream)
+{
+    return moe_expert_forward_timed(pool, x, n_tokens, k, topk_w, union_ids, n_union,
+                                    expert_offsets, perm, y, workspace, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_expert_forward_timed(const moe_expert_pool *pool, const float *x, int n_tokens,
+                                    int k, const float *topk_w, const int32_t *union_ids,
+                                    const int32_t *n_union, const int32_t *expert_offsets,
+                                    const int32_t *perm, float *y, void *workspace,
+                                    size_t ws_bytes, hipStream_t stream,
+                                    const moe_forward_events *ev)
+{
+    Geo g;
+    moe_status st = resolve_geo(pool, &g);
+    if (st != MOE_OK) return st;
+    if (n_tokens < 0) return MOE_EINVAL;
+    st = check_k(k, g.E);
+    if (st != MOE_OK) return st;
+    if (!pool->pool) return MOE_EINVAL;
+    if (!aligned(pool->pool) || (pool->shared && !aligned(pool->shared)) ||
+        pool->expert_bytes % kAlign)
+        return MOE_EALIGN;
+    if (pool->expert_bytes < moe_block_bytes(g.d, g.f, g.wbits, g.group)) return MOE_ESHAPE;
+    const long long A = (long long)n_tokens * k;
+    if (A + n_tokens > 0x7FFFFFFFLL || (A + n_tokens) * (long long)(g.d > g.f ? g.d : g.f) > 0x7FFFFFFFFFFFLL)
+        return MOE_ESHAPE;
+    if (n_tokens == 0) return MOE_OK;
+    if (!x || !topk_w || !union_ids || !n_union || !expert_offsets || !perm || !y)
+        return MOE_EINVAL;
+    if (((uintptr_t)x % 16) || ((uintptr_t)y % 16)) return MOE_EALIGN;
+    const int has_shared = pool->shared != nullptr;
+    const FwdLayout L = fwd_layout(g, n_tokens, k, has_shared);
+    if (!workspace || ws_bytes < (size_t)L.total) return MOE_EWORKSPACE;
+    if (!aligned(workspace)) return MOE_EALIGN;
+
+    char *ws = static_cast<char *>(workspace);
+    Item *items_gu = reinterpret_cast<Item *>(ws + L.items_gu);
+    Item *items_dn = reinterpret_cast<Item *>(ws + L.items_dn);
+    int32_t *n_items = reinterpret_cast<int32_t *>(ws + L.n_items);
+    float *h = reinterpret_cast<float *>(ws + L.h);
+    float *o = reinterpret_cast<float *>(ws + L.o);
+    const uint8_t *base = static_cast<const uint8_t *>(pool->pool);
+    const uint8_t *shared = static_cast<const uint8_t *>(pool->shared);
+
+    if (launch_plan(union_ids, n_union, expert_offsets, g.E, (int)A, n_tokens, has_shared, L.tb_gu,
+                    L.tb_dn, L.max_gu, L.max_dn, items_gu, items_dn, n_items, stream) != hipSuccess)
+        return MOE_EHIP;
+    if (ev && !record(ev->gateup_start, stream)) return MOE_EHIP;
+    if (launch_gateup(g, base, pool->expert_bytes, shared, x, k, perm, (int)A, items_gu, n_items,
+                      L.max_gu, h, stream) != hipSuccess)
+        return MOE_EHIP;
+    if (ev && !record(ev->gateup_end, stream)) return MOE_EHIP;
+    if (ev && !record(ev->down_start, stream)) return MOE_EHIP;
+    if (launch_down(g, base, pool->expert_bytes, shared, h, k, perm, (int)A, items_dn, n_items + 1,
+                    L.max_dn, o, stream) != hipSuccess)
+        return MOE_EHIP;
+    if (ev && !record(ev->down_end, stream)) return MOE_EHIP;
+    if (launch_combine(o, topk_w, n_tokens, k, g.d, (int)A, has_shared, y, stream) != hipSuccess)
+        return MOE_EHIP;
+    return MOE_OK;
+}
+
+moe_status moe_residual_rmsnorm(float *h, const float *y, float *a, int n_tokens, int d_model,
+                                float eps, hipStream_t stream)
+{
+    if (n_tokens < 0 || d_model <= 0 || !(eps >= 0.0f)) return MOE_EINVAL;
+    if (n_tokens == 0) return MOE_OK;
+    if (!h || !a || a == h) return MOE_EINVAL;
+    if (launch_residual_rmsnorm(h, y, a, n_tokens, d_model, eps, stream) != hipSuccess)
+        return MOE_EHIP;
+    return MOE_OK;
+}
+
+moe_status moe_pack_expert(const void *canonical_block, const moe_expert_pool *shape,
+                           void *block_out)
+{
+    Geo g;
+    moe_status st = resolve_geo(shape, &g);
+    if (st != MOE_OK) return st;
+    if (!canonical_block || !block_out) return MOE_EINVAL;
+    const size_t bytes = moe_block_bytes(g.d, g.f, g.wbits, g.group);
+    const size_t q_bytes = (size_t)g.off_gs;  // the three code matrices come first
+    const uint8_t flip = g.wbits == 4 ? 0x88 : 0x80;  // two's complement -> offset binary
+    const uint8_t *src = static_cast<const uint8_t *>(canonical_block);
+    uint8_t *dst = static_cast<uint8_t *>(block_out);
+    for (size_t i = 0; i < q_bytes; ++i) dst[i] = src[i] ^ flip;
+    if (dst != src) memcpy(dst + q_bytes, src + q_bytes, bytes - q_bytes);
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// internal.h - shared declarations of the routed-expert library (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// One unit of expert work: up to TB consecutive positions p0 .. p0+count-1 of
+// one expert's slice of the permutation (expert >= 0), or of the shared
+// expert (expert == -1), whose positions are A + t for token t.
+struct Item {
+    int32_t expert;
+    int32_t p0;
+    int32_t count;
+    int32_t pad;
+};
+
+// Geometry of one layer's expert blocks, resolved and checked on the host.
+struct Geo {
+    int d, f, E, wbits, group;
+    int epc;                 // code elements per 16-byte chunk (32 int4, 16 int8)
+    int gu_lpr, gu_cpl;      // gate/up rows: lanes per row, chunks per lane
+    int dn_lpr, dn_cpl;      // down rows
+    long long row_gu;        // bytes of one gate (or up) code row = d * wbits / 8
+    long long row_dn;        // bytes of one down code row = f * wbits / 8
+    long long spr_gu, spr_dn;  // scales per gate/up row, per down row
+    long long off_up, off_dn, off_gs, off_us, off_ds;  // byte offsets in a block
+};
+
+// ---- host helpers (abi.hip) --------------------------------------------
+moe_status resolve_geo(const moe_expert_pool *p, Geo *g);
+int tokens_per_item(int wbits, int cpl);
+
+// ---- launchers (each in its own translation unit) ----------------------
+hipError_t launch_router(const float *x, int N, int d, const float *wr, const float *b,
+                         int E, float *scores, hipStream_t s);
+hipError_t launch_topk(const float *scores, int N, int E, int k, int32_t *ids, float *w,
+                       hipStream_t s);
+hipError_t launch_union(const int32_t *ids, int A, int E, int32_t *union_ids, int32_t *n_union,
+                        int32_t *offsets, int32_t *perm, hipStream_t s);
+hipError_t launch_hit_count(const int32_t *ids, int A, int E, uint64_t *counters, hipStream_t s);
+hipError_t launch_plan(const int32_t *union_ids, const int32_t *n_union, const int32_t *offsets,
+                       int E, int A, int N, int has_shared, int tb_gu, int tb_dn, int max_gu,
+                       int max_dn, Item *items_gu, Item *items_dn, int32_t *n_items, hipStream_t s);
+hipError_t launch_gateup(const Geo &g, const uint8_t *pool, size_t stride, const uint8_t *shared,
+                         const float *x, int k, const int32_t *perm, int A,
+                         const Item *items, const int32_t *n_items, int max_items,
+                         float *h, hipStream_t s);
+hipError_t launch_down(const Geo &g, const uint8_t *pool, size_t stride, const uint8_t *shared,
+                       const float *h, int k, const int32_t *perm, int A,
+                       const Item *items, const int32_t *n_items, int max_items,
+                       float *o, hipStream_t s);
+hipError_t launch_combine(const float *o, const float *w, int N, int k, int d, int A,
+                          int has_shared, float *y, hipStream_t s);
+hipError_t launch_residual_rmsnorm(float *h, const float *y, float *a, int N, int d, float eps,
+                                   hipStream_t s);
+
+// ---- device helpers ----------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// sum over aligned groups of L lanes (L a power of two <= 64)
+template <int L>
+__device__ __forceinline__ float segment_sum(float v) {
+#pragma unroll
+    for (int o = L / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+}  // namespace moe

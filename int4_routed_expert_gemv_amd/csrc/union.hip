@@ -1,0 +1,154 @@
+// union.hip - Union and Learn stages.
+//
+// Colibri pages, "Public Colibri Observation and Revision Ledger", section
+// "Exact Architecture and Data-Flow Reconstruction": stage (2) Union merges the
+// batch's requests so that each distinct expert is used once, and stage (5)
+// Learn records which experts were used (per-expert hit counters). Same page,
+// "Cache/Prefetch Design Comparison" (figure on async I/O and prefetch): the
+// batch-union reads each unique expert once.
+//
+// Union also produces the token -> expert permutation that lets one pass over
+// an expert's weights serve all of its tokens: a stable counting sort of the
+// assignments a = t*k + j by expert id. Order comes from prefix sums and wave
+// ballots, never from the order in which atomics land, so the permutation is
+// the same on every run.
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kUnionThreads = 1024;
+
+__global__ __launch_bounds__(kUnionThreads) void union_kernel(
+    const int32_t *__restrict__ ids, int A, int E, int32_t *__restrict__ union_ids,
+    int32_t *__restrict__ n_union, int32_t *__restrict__ offsets, int32_t *__restrict__ perm)
+{
+    __shared__ int cnt[MOE_MAX_EXPERTS];
+    __shared__ int base[MOE_MAX_EXPERTS];
+    __shared__ int wsum[kUnionThreads / kWave];
+    const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+
+    for (int e = tid; e < E; e += kUnionThreads) cnt[e] = 0;
+    __syncthreads();
+    // integer histogram: the result does not depend on the order of the adds
+    for (int a = tid; a < A; a += kUnionThreads) {
+        int e = ids[a];
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+
+    // exclusive prefix sums over experts, one expert per thread (E <= 1024):
+    // counts -> offsets, and "used" flags -> positions in union_ids
+    const int c = tid < E ? cnt[tid] : 0;
+    const int used = c > 0 ? 1 : 0;
+    // wave-level inclusive scans of (c, used) packed as c * 2048 + used
+    // (c <= A < 2^20 is checked on the host, so the pack cannot overflow)
+    long long v = (long long)c * 2048 + used;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        long long u = __shfl_up(v, o, kWave);
+        if (lane >= o) v += u;
+    }
+    __shared__ long long wtot[kUnionThreads / kWave];
+    if (lane == kWave - 1) wtot[wv] = v;
+    __syncthreads();
+    if (wv == 0) {
+        long long s = lane < kUnionThreads / kWave ? wtot[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            long long u = __shfl_up(s, o, kWave);
+            if (lane >= o) s += u;
+        }
+        if (lane < kUnionThreads / kWave) wtot[lane] = s;  // inclusive
+    }
+    __syncthreads();
+    long long incl = v + (wv > 0 ? wtot[wv - 1] : 0);
+    long long excl = incl - ((long long)c * 2048 + used);
+    const int off = (int)(excl / 2048), upos = (int)(excl % 2048);
+    if (tid < E) {
+        offsets[tid] = off;
+        base[tid] = off;
+        if (used) union_ids[upos] = tid;
+    }
+    if (tid == kUnionThreads - 1) {
+        const long long tot = wtot[kUnionThreads / kWave - 1];
+        offsets[E] = (int)(tot / 2048);
+        *n_union = (int)(tot % 2048);
+    }
+    (void)wsum;
+    __syncthreads();
+
+    // stable scatter by one wave, 64 assignments at a time in ascending a: the
+    // rank of an assignment among the earlier lanes with the same expert comes
+    // from ballots on the bits of the expert id
+    if (wv == 0) {
+        const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+        for (int a0 = 0; a0 < A; a0 += kWave) {
+            const int a = a0 + lane;
+            int e = a < A ? ids[a] : -1;
+            const bool valid = e >= 0 && e < E;
+            if (!valid) e = -1;
+            unsigned long long peers = __ballot(valid);
+#pragma unroll
+            for (int bit = 0; bit < 11; ++bit) {  // E <= 1024 < 2^11, and -1 stays apart
+                const unsigned long long m = __ballot((e >> bit) & 1);
+                peers &= ((e >> bit) & 1) ? m : ~m;
+            }
+            int rank = 0, b = 0;
+            if (valid) {
+                rank = __popcll(peers & lt);
+                b = base[e];
+            }
+            // all reads of base[] finish before any lane writes it back
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_wave_barrier();
+            if (valid) {
+                perm[b + rank] = a;
+                const bool last = (peers >> lane) == 1ull;  // highest peer lane
+                if (last) base[e] = b + rank + 1;
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
+constexpr int kHitThreads = 256;
+constexpr int kHitPerBlock = 4096;
+
+__global__ __launch_bounds__(kHitThreads) void hit_count_kernel(
+    const int32_t *__restrict__ ids, int A, int E, unsigned long long *__restrict__ counters)
+{
+    __shared__ int hist[MOE_MAX_EXPERTS];
+    for (int e = threadIdx.x; e < E; e += kHitThreads) hist[e] = 0;
+    __syncthreads();
+    const int a0 = blockIdx.x * kHitPerBlock;
+    const int a1 = min(A, a0 + kHitPerBlock);
+    for (int a = a0 + threadIdx.x; a < a1; a += kHitThreads) {
+        int e = ids[a];
+        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kHitThreads)
+        if (hist[e]) atomicAdd(&counters[e], (unsigned long long)hist[e]);
+}
+
+}  // namespace
+
+hipError_t launch_union(const int32_t *ids, int A, int E, int32_t *union_ids, int32_t *n_union,
+                        int32_t *offsets, int32_t *perm, hipStream_t s)
+{
+    hipLaunchKernelGGL(union_kernel, dim3(1), dim3(kUnionThreads), 0, s, ids, A, E, union_ids,
+                       n_union, offsets, perm);
+    return hipGetLastError();
+}
+
+hipError_t launch_hit_count(const int32_t *ids, int A, int E, uint64_t *counters, hipStream_t s)
+{
+    hipLaunchKernelGGL(hit_count_kernel, dim3((A + kHitPerBlock - 1) / kHitPerBlock),
+                       dim3(kHitThreads), 0, s, ids, A, E,
+                       reinterpret_cast<unsigned long long *>(counters));
+    return hipGetLastError();
+}
+
+}  // namespace moe

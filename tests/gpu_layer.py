@@ -1,0 +1,47 @@
+"""Runs one layer step on the GPU through the C ABI (binding in
+int4_routed_expert_gemv_amd) and returns the results as numpy arrays."""
+import numpy as np
+import torch
+
+import int4_routed_expert_gemv_amd as moe
+
+
+def upload_pool(spec, blocks, shared, device="cuda"):
+    return moe.DevicePool(spec.d, spec.f, spec.n_experts, spec.wbits, spec.group, blocks, shared,
+                          device)
+
+
+def workspace(pool, N, k, device="cuda"):
+    n = max(moe.workspace_size(pool.desc, N, k), 1)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def run_layer(pool, x, wr, b, k, ids_in=None, w_in=None, counters=None, device="cuda"):
+    """route_topk (unless ids_in/w_in are given) -> union -> hit_count -> expert_forward."""
+    N, d = x.shape
+    E = pool.desc.n_experts
+    xd = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(device)
+    ws = workspace(pool, N, k, device)
+    if ids_in is None:
+        wrd = torch.from_numpy(np.ascontiguousarray(wr, np.float32)).to(device)
+        bd = None if b is None else torch.from_numpy(np.ascontiguousarray(b, np.float32)).to(device)
+        ids = torch.empty((N, k), dtype=torch.int32, device=device)
+        w = torch.empty((N, k), dtype=torch.float32, device=device)
+        moe.route_topk(xd, wrd, bd, k, ids, w, ws)
+    else:
+        ids = torch.from_numpy(np.ascontiguousarray(ids_in, np.int32)).to(device)
+        w = torch.from_numpy(np.ascontiguousarray(w_in, np.float32)).to(device)
+    union_ids = torch.full((E,), -1, dtype=torch.int32, device=device)
+    n_union = torch.zeros(1, dtype=torch.int32, device=device)
+    offsets = torch.zeros(E + 1, dtype=torch.int32, device=device)
+    perm = torch.full((N * k,), -1, dtype=torch.int32, device=device)
+    moe.union(ids, E, union_ids, n_union, offsets, perm)
+    cnt = torch.zeros(E, dtype=torch.int64, device=device) if counters is None else counters
+    moe.hit_count(ids, E, cnt)
+    y = torch.empty((N, d), dtype=torch.float32, device=device)
+    moe.expert_forward(pool.desc, xd, k, w, union_ids, n_union, offsets, perm, y, ws)
+    torch.cuda.synchronize()
+    nu = int(n_union.item())
+    return dict(ids=ids.cpu().numpy(), w=w.cpu().numpy(), union_ids=union_ids.cpu().numpy()[:nu],
+                n_union=nu, offsets=offsets.cpu().numpy(), perm=perm.cpu().numpy(),
+                counters=cnt.cpu().numpy().astype(np.uint64), y=y.cpu().numpy(), counters_t=cnt)

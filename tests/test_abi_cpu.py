@@ -1,0 +1,154 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments with the documented codes before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import int4_routed_expert_gemv_amd as moe
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(moe.LIB_PATH), reason="libmoe.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(moe.EXPORTED)
+    out = subprocess.check_output(["nm", "-D", "--defined-only", moe.LIB_PATH], text=True)
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(moe.lib(), n)
+
+
+def _pool(d=256, f=128, E=16, wbits=4, group=32, pool=4096, stride=None, shared=None):
+    bb = moe.block_bytes(d, f, wbits, group)
+    stride = stride if stride is not None else (bb + 255) // 256 * 256
+    return moe.PoolDesc(d, f, E, wbits, group, pool, stride, shared)
+
+
+FAKE = 1 << 20  # aligned non-null address: never dereferenced, every call below fails first
+
+
+def test_route_topk_argument_checks():
+    L = moe.lib()
+    ws = FAKE
+    big = 1 << 30
+    # k out of range
+    assert L.moe_route_topk(FAKE, 4, 256, FAKE, None, 16, 0, FAKE, FAKE, ws, big, None) == moe.MOE_EINVAL
+    assert L.moe_route_topk(FAKE, 4, 256, FAKE, None, 16, 17, FAKE, FAKE, ws, big, None) == moe.MOE_EINVAL
+    assert L.moe_route_topk(FAKE, 4, 256, FAKE, None, 64, 33, FAKE, FAKE, ws, big, None) == moe.MOE_EINVAL
+    assert L.moe_route_topk(FAKE, 4, 256, FAKE, None, 2000, 8, FAKE, FAKE, ws, big, None) == moe.MOE_EINVAL
+    # negative tokens, null pointers, workspace, alignment
+    assert L.moe_route_topk(FAKE, -1, 256, FAKE, None, 16, 1, FAKE, FAKE, ws, big, None) == moe.MOE_EINVAL
+    assert L.moe_route_topk(None, 4, 256, FAKE, None, 16, 1, FAKE, FAKE, ws, big, None) == moe.MOE_EINVAL
+    assert L.moe_route_topk(FAKE, 4, 256, FAKE, None, 16, 1, None, FAKE, ws, big, None) == moe.MOE_EINVAL
+    assert L.moe_route_topk(FAKE, 4, 256, FAKE, None, 16, 1, FAKE, FAKE, ws, 10, None) == moe.MOE_EWORKSPACE
+    assert L.moe_route_topk(FAKE, 4, 256, FAKE, None, 16, 1, FAKE, FAKE, None, big, None) == moe.MOE_EWORKSPACE
+    assert L.moe_route_topk(FAKE + 4, 4, 256, FAKE, None, 16, 1, FAKE, FAKE, ws, big, None) == moe.MOE_EALIGN
+    assert L.moe_route_topk(FAKE, 4, 256, FAKE, None, 16, 1, FAKE, FAKE, ws + 16, big, None) == moe.MOE_EALIGN
+    assert L.moe_route_topk(FAKE, 4, 250, FAKE, None, 16, 1, FAKE, FAKE, ws, big, None) == moe.MOE_ESHAPE
+    # zero tokens: success, nothing touched (even with null pointers)
+    assert L.moe_route_topk(None, 0, 256, None, None, 16, 1, None, None, None, 0, None) == moe.MOE_OK
+
+
+def test_union_and_hit_count_argument_checks():
+    L = moe.lib()
+    assert L.moe_union(FAKE, 4, 0, 16, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_EINVAL
+    assert L.moe_union(FAKE, 4, 2, 0, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_EINVAL
+    assert L.moe_union(FAKE, -4, 2, 16, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_EINVAL
+    assert L.moe_union(FAKE, 4, 2, 16, FAKE, None, FAKE, FAKE, None) == moe.MOE_EINVAL
+    assert L.moe_union(None, 0, 2, 16, None, None, None, None, None) == moe.MOE_OK
+    assert L.moe_hit_count(FAKE, 4, 3, 2, FAKE, None) == moe.MOE_EINVAL
+    assert L.moe_hit_count(FAKE, 4, 1, 2, None, None) == moe.MOE_EINVAL
+    assert L.moe_hit_count(FAKE, 4, 1, 2, FAKE + 4, None) == moe.MOE_EALIGN
+    assert L.moe_hit_count(None, 0, 1, 2, None, None) == moe.MOE_OK
+
+
+def _fwd(pool, N=4, k=1, ws=FAKE, wsb=1 << 30, x=FAKE, y=FAKE):
+    return moe.lib().moe_expert_forward(ctypes.byref(pool), x, N, k, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        y, ws, wsb, None)
+
+
+def test_expert_forward_argument_checks():
+    assert _fwd(_pool(wbits=3)) == moe.MOE_EINVAL
+    assert _fwd(_pool(d=250)) == moe.MOE_ESHAPE            # not a multiple of 32
+    assert _fwd(_pool(d=96 * 32)) == moe.MOE_ESHAPE        # 96 chunks: not 2^n and not 64*{1,2,3,4,6,8}
+    assert _fwd(_pool(group=48)) == moe.MOE_ESHAPE         # group not a multiple of 32
+    assert _fwd(_pool(group=64, f=96 * 32)) == moe.MOE_ESHAPE
+    assert _fwd(_pool(E=0)) == moe.MOE_EINVAL
+    assert _fwd(_pool(E=2000)) == moe.MOE_EINVAL
+    assert _fwd(_pool(), k=17) == moe.MOE_EINVAL
+    assert _fwd(_pool(pool=None)) == moe.MOE_EINVAL
+    assert _fwd(_pool(pool=FAKE + 64)) == moe.MOE_EALIGN
+    assert _fwd(_pool(shared=FAKE + 64)) == moe.MOE_EALIGN
+    assert _fwd(_pool(stride=61440 + 16)) == moe.MOE_EALIGN
+    assert _fwd(_pool(stride=256)) == moe.MOE_ESHAPE       # stride smaller than a block
+    assert _fwd(_pool(), wsb=100) == moe.MOE_EWORKSPACE
+    assert _fwd(_pool(), ws=None) == moe.MOE_EWORKSPACE
+    assert _fwd(_pool(), ws=FAKE + 32) == moe.MOE_EALIGN
+    assert _fwd(_pool(), x=FAKE + 4) == moe.MOE_EALIGN
+    assert _fwd(_pool(), N=-1) == moe.MOE_EINVAL
+    assert _fwd(_pool(), N=0, x=None, y=None, ws=None, wsb=0) == moe.MOE_OK
+    assert moe.lib().moe_residual_rmsnorm(FAKE, None, FAKE, 2, 0, 1e-6, None) == moe.MOE_EINVAL
+    assert moe.lib().moe_residual_rmsnorm(FAKE, None, FAKE, 2, 8, -1.0, None) == moe.MOE_EINVAL
+    assert moe.lib().moe_residual_rmsnorm(FAKE, None, FAKE, 0, 8, 1e-6, None) == moe.MOE_OK
+
+
+def test_sizes():
+    for name, cfg in synth.CONFIGS.items():
+        for spec in cfg.layers:
+            assert moe.block_bytes(spec.d, spec.f, spec.wbits, spec.group) == synth.block_bytes(spec)
+    assert moe.block_bytes(6144, 2048, 4, 128) == 20054016
+    assert moe.block_bytes(6144, 2048, 8, 0) == 37789696
+    p = _pool(d=6144, f=2048, E=256, group=128, shared=FAKE)
+    N, k = 64, 8
+    A = N * k
+    ws = moe.forward_workspace_size(p, N, k)
+    # hidden [A+N][f] and expert outputs [A+N][d] in float32 dominate
+    assert ws >= (A + N) * (2048 + 6144) * 4
+    assert ws < (A + N) * (2048 + 6144) * 4 + 2 * 1024 * 1024
+    assert moe.route_workspace_size(N, 256) == N * 256 * 4
+    assert moe.workspace_size(p, N, k) == max(ws, N * 256 * 4)
+    assert moe.forward_workspace_size(_pool(wbits=5), N, k) == 0
+    # without a shared expert there are no shared rows
+    p0 = _pool(d=6144, f=2048, E=256, group=128)
+    assert moe.forward_workspace_size(p0, N, k) < ws - N * (2048 + 6144) * 4 + 4096
+
+
+def test_pack_expert_flips_codes_only():
+    cfg = synth.CONFIGS["tiny"]
+    spec = cfg.layer
+    blk = synth.expert_pool(cfg, count=1)[0]
+    p = _pool()
+    out = np.empty_like(blk)
+    moe.pack_expert(blk, p, out)
+    off = synth.canonical_offsets(spec)
+    q = off["gate_s"]
+    assert np.array_equal(out[:q], blk[:q] ^ 0x88)
+    assert np.array_equal(out[q:], blk[q:])
+    p8 = _pool(d=6144, f=2048, wbits=8, group=0)
+    c8 = np.arange(moe.block_bytes(6144, 2048, 8, 0), dtype=np.int64).astype(np.uint8)
+    o8 = moe.pack_expert(c8.copy(), p8)
+    q8 = 3 * 6144 * 2048
+    assert np.array_equal(o8[:q8], c8[:q8] ^ 0x80) and np.array_equal(o8[q8:], c8[q8:])
+    with pytest.raises(moe.MoeError):
+        moe.pack_expert(blk, _pool(d=250))
+
+
+def test_strerror():
+    for s in range(-5, 1):
+        assert moe.strerror(s)
+    assert "workspace" in moe.strerror(moe.MOE_EWORKSPACE)

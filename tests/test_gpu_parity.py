@@ -1,0 +1,183 @@
+"""GPU parity of the layer step against the CPU oracle, through the C ABI.
+
+Integers (expert ids, union, offsets, permutation, hit counters) must match
+bit for bit; float outputs must satisfy, for every token,
+max_i |y - y_ref| / max_i |y_ref| <= 2e-3. The gate weights are the chosen
+float32 scores and must agree to 2e-6 (they differ by float32 rounding
+only). Inputs whose top-(k+1) scores are closer than 1e-6 are redrawn first
+(tests/layer_cases.py).
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import layer_cases as lc
+from tests.gpu_layer import run_layer, upload_pool, workspace
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+W_TOL = 2e-6
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def check_routing(got, ref, E):
+    np.testing.assert_array_equal(got["ids"], ref["ids"])
+    assert np.max(np.abs(got["w"].astype(np.float64) - ref["w"])) <= W_TOL
+    np.testing.assert_array_equal(got["union_ids"], ref["union_ids"])
+    assert got["n_union"] == len(ref["union_ids"])
+    np.testing.assert_array_equal(got["offsets"], ref["offsets"])
+    np.testing.assert_array_equal(got["perm"], ref["perm"])
+    np.testing.assert_array_equal(got["counters"], ref["counters"])
+
+
+def check_y(y, ref_y, tol=TOL):
+    err = lc.rel_err_rows(y, ref_y)
+    assert np.all(np.isfinite(y))
+    assert err.max() <= tol, f"max per-token relative error {err.max():.3e} > {tol}"
+    return float(err.max())
+
+
+def oracle_then_pool(cfg, layer=0, x=None):
+    spec = cfg.layers[layer]
+    if x is None:
+        x, wr, b, _, nre = lc.layer_inputs(cfg, layer)
+    else:
+        wr, b = synth.router(cfg, layer)
+        nre = 0
+    blocks, shared = lc.canonical_pool(cfg, layer)
+    return spec, x, wr, b, blocks, shared, nre
+
+
+def full_parity(cfg, layer=0):
+    spec, x, wr, b, blocks, shared, nre = oracle_then_pool(cfg, layer)
+    say(f"[{cfg.name}] N={cfg.n_tokens} k={cfg.k} d={spec.d} f={spec.f} E={spec.n_experts} "
+        f"wbits={spec.wbits} G={spec.group} redrawn={nre}")
+    ref = oracle.layer_step(x, wr, b, cfg.k, blocks, shared, spec.d, spec.f, spec.wbits,
+                            spec.group)
+    pool = upload_pool(spec, blocks, shared)   # packs the blocks in place: oracle first
+    say(f"[{cfg.name}] oracle done, union={len(ref['union_ids'])}; running GPU step")
+    got = run_layer(pool, x, wr, b, cfg.k)
+    check_routing(got, ref, spec.n_experts)
+    err = check_y(got["y"], ref["y"])
+    say(f"[{cfg.name}] parity ok, max rel err {err:.2e}")
+    return pool, x, wr, b, got, ref
+
+
+def test_tiny_layer():
+    full_parity(synth.CONFIGS["tiny"])
+
+
+def test_decode1_layer():
+    full_parity(synth.CONFIGS["decode1"])
+    torch.cuda.empty_cache()
+
+
+def test_decode64_layer():
+    full_parity(synth.CONFIGS["decode64"])
+    torch.cuda.empty_cache()
+
+
+def test_prefill4096_layer_sampled():
+    """Full-size prefill: routing, union, permutation and counters over all 4096
+    tokens; layer outputs on 48 sampled tokens (the oracle computes those
+    tokens alone, which is exact because tokens do not interact)."""
+    cfg = synth.CONFIGS["prefill4096"]
+    spec, x, wr, b, blocks, shared, nre = oracle_then_pool(cfg)
+    say(f"[prefill4096] redrawn={nre}")
+    s = oracle.router(x, wr, b)
+    ids, w = oracle.topk(s, cfg.k)
+    u, off, perm = oracle.union(ids, spec.n_experts)
+    cnt = oracle.hit_count(ids, spec.n_experts)
+    sample = np.unique(np.concatenate([[0, 1, 2, cfg.n_tokens - 1],
+                                       np.linspace(3, cfg.n_tokens - 2, 44).astype(int)]))
+    y_ref = oracle.expert_forward(blocks, shared, spec.d, spec.f, spec.wbits, spec.group,
+                                  x[sample], ids[sample], w[sample])
+    pool = upload_pool(spec, blocks, shared)
+    say("[prefill4096] oracle done; running GPU step")
+    got = run_layer(pool, x, wr, b, cfg.k)
+    ref = dict(ids=ids, w=w, union_ids=u, offsets=off, perm=perm, counters=cnt)
+    check_routing(got, ref, spec.n_experts)
+    err = check_y(got["y"][sample], y_ref)
+    say(f"[prefill4096] parity ok on {len(sample)} tokens, max rel err {err:.2e}")
+    del pool
+    torch.cuda.empty_cache()
+
+
+def test_draft_int8_layer():
+    """The int8 per-row-scale draft layer at full shape with 64 tokens."""
+    cfg = dataclasses.replace(synth.CONFIGS["stack8_draft"], n_tokens=64)
+    full_parity(cfg, layer=8)
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ edge cases
+
+def tiny(**kw):
+    return dataclasses.replace(synth.CONFIGS["tiny"], **kw)
+
+
+@pytest.mark.parametrize("N,k", [(1, 1), (5, 1), (6, 2), (33, 3), (64, 4), (100, 16)])
+def test_tiny_ragged_batches(N, k):
+    """Token counts that leave partial work items and partial router tiles,
+    k from 1 to E (k = E routes every token to every expert)."""
+    pool, *_ = full_parity(tiny(n_tokens=N, k=k))
+
+
+def test_determinism_and_counter_accumulation():
+    cfg = synth.CONFIGS["decode64"]
+    spec, x, wr, b, blocks, shared, _ = oracle_then_pool(cfg)
+    pool = upload_pool(spec, blocks, shared)
+    r1 = run_layer(pool, x, wr, b, cfg.k)
+    r2 = run_layer(pool, x, wr, b, cfg.k, counters=r1["counters_t"])
+    for key in ("ids", "w", "union_ids", "offsets", "perm", "y"):
+        np.testing.assert_array_equal(r1[key], r2[key])
+    np.testing.assert_array_equal(r2["counters"], 2 * r1["counters"])
+    assert r2["counters"].sum() == 2 * cfg.n_tokens * cfg.k
+    del pool
+    torch.cuda.empty_cache()
+
+
+def test_zero_gate_equals_dropped_slot():
+    """w[:, 1] = 0 with k = 2 gives bit for bit the k = 1 result on slot 0."""
+    cfg = tiny(n_tokens=12, k=2)
+    spec, x, wr, b, blocks, shared, _ = oracle_then_pool(cfg)
+    ids, w = oracle.topk(oracle.router(x, wr, b), 2)
+    pool = upload_pool(spec, blocks, shared)
+    w0 = w.copy()
+    w0[:, 1] = 0.0
+    r2 = run_layer(pool, x, wr, b, 2, ids_in=ids, w_in=w0)
+    r1 = run_layer(pool, x, wr, b, 1, ids_in=ids[:, :1].copy(), w_in=w[:, :1].copy())
+    np.testing.assert_array_equal(r2["y"], r1["y"])
+
+
+def test_batch_invariance():
+    """A token's output does not depend on the other tokens of the batch."""
+    cfg = synth.CONFIGS["decode64"]
+    spec, x, wr, b, blocks, shared, _ = oracle_then_pool(cfg)
+    pool = upload_pool(spec, blocks, shared)
+    full = run_layer(pool, x, wr, b, cfg.k)
+    sub = np.arange(3, 64, 3)[:40] if len(np.arange(3, 64, 3)) >= 40 else np.arange(40) + 7
+    sub = np.arange(40) + 7
+    part = run_layer(pool, x[sub], wr, b, cfg.k)
+    np.testing.assert_array_equal(part["ids"], full["ids"][sub])
+    np.testing.assert_array_equal(part["y"], full["y"][sub])
+    del pool
+    torch.cuda.empty_cache()
+
+
+def test_zero_tokens_is_a_no_op():
+    cfg = synth.CONFIGS["tiny"]
+    spec, x, wr, b, blocks, shared, _ = oracle_then_pool(cfg)
+    pool = upload_pool(spec, blocks, shared)
+    r = run_layer(pool, x[:0], wr, b, 1)
+    assert r["y"].shape == (0, spec.d) and r["counters"].sum() == 0
