@@ -47,24 +47,22 @@ long long n_scales(long long rows, long long cols, int group)
 
 // Workspace of moe_expert_forward, laid out in this order.
 struct FwdLayout {
-    int tb_gu, tb_dn, max_gu, max_dn, P;
-    long long items_gu, items_dn, n_items, h, o, total;
+    int tb, max_items, P;
+    long long items, n_items, h, o, total;
 };
 
 FwdLayout fwd_layout(const Geo &g, int N, int k, int has_shared)
 {
     FwdLayout L;
     const long long A = (long long)N * k;
-    L.tb_gu = tokens_per_item(g.wbits, g.gu_cpl);
-    L.tb_dn = tokens_per_item(g.wbits, g.dn_cpl);
+    L.tb = gemv_tokens_per_item(g, N);
+    // each union expert adds at most one partly filled item
     const long long ue = A < g.E ? A : g.E;
-    L.max_gu = (int)((A + L.tb_gu - 1) / L.tb_gu + ue + (has_shared ? (N + L.tb_gu - 1) / L.tb_gu : 0));
-    L.max_dn = (int)((A + L.tb_dn - 1) / L.tb_dn + ue + (has_shared ? (N + L.tb_dn - 1) / L.tb_dn : 0));
+    L.max_items = (int)((A + L.tb - 1) / L.tb + ue + (has_shared ? (N + L.tb - 1) / L.tb : 0));
     L.P = (int)(A + (has_shared ? N : 0));
     long long off = 0;
-    L.items_gu = off; off = align_up(off + (long long)L.max_gu * (long long)sizeof(Item));
-    L.items_dn = off; off = align_up(off + (long long)L.max_dn * (long long)sizeof(Item));
-    L.n_items = off; off = align_up(off + 2 * 4);
+    L.items = off; off = align_up(off + (long long)L.max_items * (long long)sizeof(Item));
+    L.n_items = off; off = align_up(off + 4);
     L.h = off; off = align_up(off + (long long)L.P * g.f * 4);
     L.o = off; off = align_up(off + (long long)L.P * g.d * 4);
     L.total = off;
@@ -79,8 +77,6 @@ moe_status check_k(int k, int E)
 }
 
 }  // namespace
-
-int tokens_per_item(int wbits, int cpl);
 
 moe_status resolve_geo(const moe_expert_pool *p, Geo *g)
 {
@@ -264,28 +260,36 @@ moe_status moe_expert_forward_timed(const moe_expert_pool *pool, const float *x,
     if (!aligned(workspace)) return MOE_EALIGN;
 
     char *ws = static_cast<char *>(workspace);
-    Item *items_gu = reinterpret_cast<Item *>(ws + L.items_gu);
-    Item *items_dn = reinterpret_cast<Item *>(ws + L.items_dn);
-    int32_t *n_items = reinterpret_cast<int32_t *>(ws + L.n_items);
-    float *h = reinterpret_cast<float *>(ws + L.h);
-    float *o = reinterpret_cast<float *>(ws + L.o);
-    const uint8_t *base = static_cast<const uint8_t *>(pool->pool);
-    const uint8_t *shared = static_cast<const uint8_t *>(pool->shared);
+    Fwd f;
+    f.g = g;
+    f.pool = static_cast<const uint8_t *>(pool->pool);
+    f.stride = pool->expert_bytes;
+    f.shared = static_cast<const uint8_t *>(pool->shared);
+    f.x = x;
+    f.w = topk_w;
+    f.k = k;
+    f.N = n_tokens;
+    f.A = (int)A;
+    f.has_shared = has_shared;
+    f.union_ids = union_ids;
+    f.n_union = n_union;
+    f.offsets = expert_offsets;
+    f.perm = perm;
+    f.h = reinterpret_cast<float *>(ws + L.h);
+    f.o = reinterpret_cast<float *>(ws + L.o);
+    f.y = y;
+    f.items = reinterpret_cast<Item *>(ws + L.items);
+    f.n_items = reinterpret_cast<int32_t *>(ws + L.n_items);
+    f.tb = L.tb;
+    f.max_items = L.max_items;
 
-    if (launch_plan(union_ids, n_union, expert_offsets, g.E, (int)A, n_tokens, has_shared, L.tb_gu,
-                    L.tb_dn, L.max_gu, L.max_dn, items_gu, items_dn, n_items, stream) != hipSuccess)
-        return MOE_EHIP;
     if (ev && !record(ev->gateup_start, stream)) return MOE_EHIP;
-    if (launch_gateup(g, base, pool->expert_bytes, shared, x, k, perm, (int)A, items_gu, n_items,
-                      L.max_gu, h, stream) != hipSuccess)
-        return MOE_EHIP;
+    if (launch_gateup(f, stream) != hipSuccess) return MOE_EHIP;
     if (ev && !record(ev->gateup_end, stream)) return MOE_EHIP;
     if (ev && !record(ev->down_start, stream)) return MOE_EHIP;
-    if (launch_down(g, base, pool->expert_bytes, shared, h, k, perm, (int)A, items_dn, n_items + 1,
-                    L.max_dn, o, stream) != hipSuccess)
-        return MOE_EHIP;
+    if (launch_down(f, stream) != hipSuccess) return MOE_EHIP;
     if (ev && !record(ev->down_end, stream)) return MOE_EHIP;
-    if (launch_combine(o, topk_w, n_tokens, k, g.d, (int)A, has_shared, y, stream) != hipSuccess)
+    if (launch_combine(f.o, topk_w, n_tokens, k, g.d, (int)A, has_shared, y, stream) != hipSuccess)
         return MOE_EHIP;
     return MOE_OK;
 }

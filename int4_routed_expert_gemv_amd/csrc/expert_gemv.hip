@@ -37,44 +37,37 @@ __device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2
 
 constexpr uint32_t kMagic = 0x64006400u;  // two float16 1024.0
 
-// 8 offset-binary int4 codes (element j in bits 4j..4j+3) against staged
-// activations xs = {(x0,x4), (x1/16,x5/16), (x2,x6), (x3/16,x7/16)}.
-__device__ __forceinline__ float dot8_i4(uint32_t w, const uint32_t *xs, float acc)
-{
-    const uint32_t w8 = w >> 8;
-    acc = __builtin_amdgcn_fdot2(as_h2((w & 0x000F000Fu) | kMagic), as_h2(xs[0]), acc, false);
-    acc = __builtin_amdgcn_fdot2(as_h2((w & 0x00F000F0u) | kMagic), as_h2(xs[1]), acc, false);
-    acc = __builtin_amdgcn_fdot2(as_h2((w8 & 0x000F000Fu) | kMagic), as_h2(xs[2]), acc, false);
-    acc = __builtin_amdgcn_fdot2(as_h2((w8 & 0x00F000F0u) | kMagic), as_h2(xs[3]), acc, false);
-    return acc;
-}
-
-// 4 offset-binary int8 codes against xs = {(x0,x2), (x1,x3)}.
-__device__ __forceinline__ float dot4_i8(uint32_t w, const uint32_t *xs, float acc)
-{
-    acc = __builtin_amdgcn_fdot2(as_h2((w & 0x00FF00FFu) | kMagic), as_h2(xs[0]), acc, false);
-    acc = __builtin_amdgcn_fdot2(as_h2(((w >> 8) & 0x00FF00FFu) | kMagic), as_h2(xs[1]), acc, false);
-    return acc;
-}
-
 template <int WB> struct Fmt;
 template <> struct Fmt<4> { static constexpr int epc = 32, xdw = 16; };
 template <> struct Fmt<8> { static constexpr int epc = 16, xdw = 8; };
 
+// The float16 pairs of one 16-byte chunk of offset-binary codes (1024 + code
+// + offset in each half), in the order the staged activations use.
 template <int WB>
-__device__ __forceinline__ float dot_chunk(uint4 w, const uint32_t *xs, float acc)
+__device__ __forceinline__ void extract_chunk(uint4 w, uint32_t *h)
 {
-    if constexpr (WB == 4) {
-        acc = dot8_i4(w.x, xs + 0, acc);
-        acc = dot8_i4(w.y, xs + 4, acc);
-        acc = dot8_i4(w.z, xs + 8, acc);
-        acc = dot8_i4(w.w, xs + 12, acc);
-    } else {
-        acc = dot4_i8(w.x, xs + 0, acc);
-        acc = dot4_i8(w.y, xs + 2, acc);
-        acc = dot4_i8(w.z, xs + 4, acc);
-        acc = dot4_i8(w.w, xs + 6, acc);
+    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if constexpr (WB == 4) {
+            const uint32_t d8 = d[q] >> 8;
+            h[4 * q + 0] = (d[q] & 0x000F000Fu) | kMagic;
+            h[4 * q + 1] = (d[q] & 0x00F000F0u) | kMagic;
+            h[4 * q + 2] = (d8 & 0x000F000Fu) | kMagic;
+            h[4 * q + 3] = (d8 & 0x00F000F0u) | kMagic;
+        } else {
+            h[2 * q + 0] = (d[q] & 0x00FF00FFu) | kMagic;
+            h[2 * q + 1] = ((d[q] >> 8) & 0x00FF00FFu) | kMagic;
+        }
     }
+}
+
+template <int N>
+__device__ __forceinline__ float dot_halves(const uint32_t *h, const uint32_t *xs)
+{
+    float acc = 0.0f;
+#pragma unroll
+    for (int q = 0; q < N; ++q) acc = __builtin_amdgcn_fdot2(as_h2(h[q]), as_h2(xs[q]), acc, false);
     return acc;
 }
 
@@ -136,272 +129,402 @@ __device__ __forceinline__ float stage_chunk(const float *src, float scale, uint
     }
 }
 
-struct GemvArgs {
-    Geo g;
-    const uint8_t *pool;
-    size_t stride;
-    const uint8_t *shared;
-    const float *in;        // x [N][d] (gate/up) or h [P][f] (down)
-    int k;
-    const int32_t *perm;
-    int A;
-    int N;
-    const Item *items;
-    const int32_t *n_items;
-    int n_rbg;              // row groups (workgroups) per item
-    float *out;             // h [P][f] (gate/up) or o [P][d] (down)
-};
+constexpr int kGemvThreads = 256;
+constexpr int kGemvWaves = kGemvThreads / kWave;
 
-constexpr int kTB = 4;      // tokens per item
+// staged activations per token per row chunk: XDW dwords + one correction
+__host__ __device__ constexpr int stage_bytes(int wb) { return (wb == 4 ? 16 : 8) * 4 + 4; }
 
-// One workgroup = KS x RG waves working on ROWS = RG * R * (64/LPR) rows of
-// one item. The KS waves of a row group split the row into KS slices of 64
-// 16-byte chunks (rows of at most 64 chunks use KS = 1 and LPR lanes per
-// row). Each wave stages the activations of its chunk for the item's tokens
-// in registers, streams R rows with one 128-bit load per lane per row and
-// matrix, adds partial sums across the row's lanes with shuffles and, for
-// KS > 1, across the KS waves in LDS in slice order.
-template <bool GATEUP, int WB, int KS, int LPR, int RG, int R>
-__global__ __launch_bounds__(KS * RG * kWave) void gemv_kernel(GemvArgs a)
+// rows per wave per row block
+__host__ __device__ constexpr int rows_of(bool gateup, int cpl)
 {
-    constexpr int XDW = Fmt<WB>::xdw, EPC = Fmt<WB>::epc;
-    constexpr int RPI = kWave / LPR;
-    constexpr int NW = KS * RG;
-    constexpr int ROWS = RG * R * RPI;
-    constexpr int NM = GATEUP ? 2 : 1;  // matrices per row: gate and up, or down
-    static_assert(KS == 1 || LPR == kWave, "row slices need full-wave rows");
-
-    __shared__ float smax[kTB][NW];
-    __shared__ float red[KS > 1 ? RG * R * kTB * KS * NM : 1];
-
-    const Geo &g = a.g;
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int ks = wave % KS, rg = wave / KS;
-    const int item_idx = blockIdx.x / a.n_rbg;
-    if (item_idx >= *a.n_items) return;  // uniform over the workgroup
-    const int rbg = blockIdx.x % a.n_rbg;
-    const Item it = a.items[item_idx];
-    const uint8_t *blk = it.expert >= 0 ? a.pool + (size_t)it.expert * a.stride : a.shared;
-    const int seg = lane / LPR, li = lane % LPR;
-    const int c = ks * kWave + li;  // this lane's chunk of the row
-    const int cols = GATEUP ? g.d : g.f;
-    const int rows = GATEUP ? g.f : g.d;
-
-    // tokens: input row and output row of each position
-    const float *src[kTB];
-    int orow[kTB];
-#pragma unroll
-    for (int i = 0; i < kTB; ++i) {
-        const int p = it.p0 + min(i, it.count - 1);
-        // values read from the permutation are clamped into range, so
-        // inconsistent caller buffers cannot move an access out of bounds
-        const int a_idx = it.expert >= 0 ? min(max(a.perm[p], 0), a.A - 1) : 0;
-        if (GATEUP) {
-            const int t = it.expert >= 0 ? a_idx / a.k : p - a.A;
-            src[i] = a.in + (size_t)t * cols;
-            orow[i] = p;
-        } else {
-            src[i] = a.in + (size_t)p * cols;
-            orow[i] = it.expert >= 0 ? a_idx : p;
-        }
-    }
-
-    // per-token power-of-two scale from the largest |value| of the row
-#pragma unroll
-    for (int i = 0; i < kTB; ++i) {
-        if (i >= it.count) break;
-        const float4 *s4 = reinterpret_cast<const float4 *>(src[i] + (size_t)c * EPC);
-        float mx = 0.0f;
-#pragma unroll
-        for (int q = 0; q < EPC / 4; ++q) {
-            const float4 f4 = s4[q];
-            mx = fmaxf(mx, fmaxf(fmaxf(fabsf(f4.x), fabsf(f4.y)), fmaxf(fabsf(f4.z), fabsf(f4.w))));
-        }
-        mx = wave_max(mx);
-        if (lane == 0) smax[i][wave] = mx;
-    }
-    __syncthreads();
-    uint32_t xs[kTB][XDW];
-    float corr[kTB], inv[kTB];
-#pragma unroll
-    for (int i = 0; i < kTB; ++i) {
-        inv[i] = 0.0f;
-        corr[i] = 0.0f;
-        if (i < it.count) {
-            float mx = smax[i][0];
-#pragma unroll
-            for (int w = 1; w < NW; ++w) mx = fmaxf(mx, smax[i][w]);
-            int sh = 0;
-            if (mx > 0.0f && mx <= 3.4e38f) {
-                int ex;
-                frexpf(mx, &ex);
-                sh = min(126, max(-126, 14 - ex));
-            }
-            inv[i] = ldexpf(1.0f, -sh);
-            corr[i] = stage_chunk<WB>(src[i] + (size_t)c * EPC, ldexpf(1.0f, sh), xs[i]);
-        } else {
-#pragma unroll
-            for (int q = 0; q < XDW; ++q) xs[i][q] = 0u;
-        }
-    }
-
-    // weights: R rows, one 16-byte chunk per lane per matrix, and its scale
-    const int row0 = rbg * ROWS + rg * R * RPI;
-    const long long grp = g.group ? (long long)c * EPC / g.group : 0;
-    const long long row_bytes = GATEUP ? g.row_gu : g.row_dn;
-    const long long spr = GATEUP ? g.spr_gu : g.spr_dn;
-    const uint8_t *q0 = blk + (GATEUP ? 0 : g.off_dn) + (long long)c * 16;
-    const uint8_t *q1 = blk + g.off_up + (long long)c * 16;
-    const uint8_t *s0 = blk + (GATEUP ? g.off_gs : g.off_ds) + grp * 4;
-    const uint8_t *s1 = blk + g.off_us + grp * 4;
-    uint4 w[R][NM];
-    float sc[R][NM];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const long long row = min(row0 + r * RPI + seg, rows - 1);
-        w[r][0] = *reinterpret_cast<const uint4 *>(q0 + row * row_bytes);
-        sc[r][0] = *reinterpret_cast<const float *>(s0 + row * spr * 4);
-        if (GATEUP) {
-            w[r][NM - 1] = *reinterpret_cast<const uint4 *>(q1 + row * row_bytes);
-            sc[r][NM - 1] = *reinterpret_cast<const float *>(s1 + row * spr * 4);
-        }
-    }
-
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int row = row0 + r * RPI + seg;
-#pragma unroll
-        for (int i = 0; i < kTB; ++i) {
-            if (i >= it.count) break;
-            float acc[NM];
-#pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                const float cm = dot_chunk<WB>(w[r][m], xs[i], 0.0f);
-                acc[m] = segment_sum<LPR>(sc[r][m] * (cm - corr[i]));
-            }
-            if (KS == 1) {
-                if (li == 0 && row < rows) {
-                    float v;
-                    if (GATEUP) {
-                        const float gv = acc[0] * inv[i], uv = acc[NM - 1] * inv[i];
-                        v = gv / (1.0f + expf(-gv)) * uv;
-                    } else {
-                        v = acc[0] * inv[i];
-                    }
-                    a.out[(size_t)orow[i] * rows + row] = v;
-                }
-            } else if (lane == 0) {
-#pragma unroll
-                for (int m = 0; m < NM; ++m)
-                    red[(((rg * R + r) * kTB + i) * KS + ks) * NM + m] = acc[m];
-            }
-        }
-    }
-    if (KS > 1) {
-        __syncthreads();
-        // one thread per (row group, row, token): add the slices in order
-        for (int idx = threadIdx.x; idx < RG * R * kTB; idx += NW * kWave) {
-            const int i = idx % kTB, rr = idx / kTB;
-            const int row = rbg * ROWS + rr;  // RPI == 1 here
-            if (i >= it.count || row >= rows) continue;
-            float acc[NM];
-#pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                acc[m] = red[(idx * KS + 0) * NM + m];
-#pragma unroll
-                for (int q = 1; q < KS; ++q) acc[m] += red[(idx * KS + q) * NM + m];
-            }
-            float v;
-            if (GATEUP) {
-                const float gv = acc[0] * inv[i], uv = acc[NM - 1] * inv[i];
-                v = gv / (1.0f + expf(-gv)) * uv;
-            } else {
-                v = acc[0] * inv[i];
-            }
-            a.out[(size_t)orow[i] * rows + row] = v;
-        }
-    }
+    return gateup ? (cpl == 1 ? 2 : 1) : (cpl == 1 ? 4 : (cpl <= 3 ? 2 : 1));
 }
 
-// ---- work list -------------------------------------------------------------
-
-constexpr int kPlanThreads = 1024;
-
-__device__ int block_exclusive_scan(int v, int &total)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
 {
-    __shared__ int wt[kPlanThreads / kWave];
-    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
-    int incl = v;
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                              0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float lane_f(float v, int l)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// Sum over aligned groups of L lanes (L a power of two <= 64); the result is
+// valid in the first lane of each group.
+template <int L>
+__device__ __forceinline__ float seg_sum(float v)
+{
+    if constexpr (L >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+    if constexpr (L >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+    if constexpr (L >= 8) v += dpp<0x141>(v);   // row_half_mirror
+    if constexpr (L >= 16) v += dpp<0x140>(v);  // row_mirror
+    if constexpr (L == 32) v += __shfl_xor(v, 16, kWave);
+    if constexpr (L == 64) v = (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v)
+{
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
+    return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v)
+{
+    const int lane = threadIdx.x % kWave;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
-        int u = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += u;
+        const int u = __shfl_up(v, o, kWave);
+        if (lane >= o) v += u;
     }
-    if (lane == kWave - 1) wt[wv] = incl;
-    __syncthreads();
-    if (wv == 0) {
-        int s = lane < kPlanThreads / kWave ? wt[lane] : 0;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            int u = __shfl_up(s, o, kWave);
-            if (lane >= o) s += u;
-        }
-        if (lane < kPlanThreads / kWave) wt[lane] = s;
-    }
-    __syncthreads();
-    total = wt[kPlanThreads / kWave - 1];
-    const int r = incl - v + (wv > 0 ? wt[wv - 1] : 0);
-    __syncthreads();
-    return r;
+    return v;
 }
 
-// Splits every union expert's slice of the permutation (and the shared
-// expert's N tokens) into items of at most tb tokens, for both GEMV passes.
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(
-    const int32_t *__restrict__ union_ids, const int32_t *__restrict__ n_union,
-    const int32_t *__restrict__ offsets, int E, int A, int N, int has_shared, int tb_gu,
-    int tb_dn, int max_gu, int max_dn, Item *__restrict__ items_gu, Item *__restrict__ items_dn,
-    int32_t *__restrict__ n_items)
+struct GemvArgs {
+    Fwd f;
+    int n_rbg;              // workgroups per item
+    int iters;              // row blocks per workgroup
+    int plan_here;          // gate/up pass: find the item in-kernel (union of <= 64)
+};
+
+// Finds work item `item_idx` of the current call when the union has at most
+// 64 experts. Items are the shared expert's tokens in slices of TB first
+// (their workgroups need nothing from the union to start loading weights),
+// then the union experts in union order, each cut into slices of TB of its
+// permutation positions. One wave; writes *out (count == 0: no such item)
+// and returns the item total.
+template <int TB>
+__device__ int find_item(const Fwd &f, int item_idx, Item *out)
 {
-    const int u = threadIdx.x;
-    const int nu = min(max(*n_union, 0), E);
+    const int lane = threadIdx.x % kWave;
+    const int nsh = f.has_shared ? (f.N + TB - 1) / TB : 0;
+    if (item_idx < nsh) {
+        if (lane == 0) {
+            Item it;
+            it.expert = -1;
+            it.p0 = f.A + item_idx * TB;
+            it.count = min(TB, f.N - item_idx * TB);
+            it.pad = 0;
+            *out = it;
+        }
+        return -1;  // total not needed by shared-expert workgroups
+    }
+    const int E = f.g.E;
+    const int nu = min(max(*f.n_union, 0), min(E, kWave));
     int e = -1, s0 = 0, T = 0;
-    if (u < nu) {
-        e = union_ids[u];
+    if (lane < nu) {
+        e = f.union_ids[lane];
         if (e >= 0 && e < E) {
-            s0 = min(max(offsets[e], 0), A);
-            const int s1 = min(max(offsets[e + 1], s0), A);
-            T = s1 - s0;
+            s0 = min(max(f.offsets[e], 0), f.A);
+            T = min(max(f.offsets[e + 1], s0), f.A) - s0;
         } else {
             e = -1;
         }
     }
-    for (int pass = 0; pass < 2; ++pass) {
-        const int tb = pass == 0 ? tb_gu : tb_dn;
-        const int cap = pass == 0 ? max_gu : max_dn;  // host bound of the item count
-        Item *items = pass == 0 ? items_gu : items_dn;
-        const int nb = (T + tb - 1) / tb;
-        int total;
-        const int base = block_exclusive_scan(nb, total);
-        for (int b = 0; b < nb; ++b) {
-            Item it;
-            it.expert = e;
-            it.p0 = s0 + b * tb;
-            it.count = min(tb, T - b * tb);
-            it.pad = 0;
-            if (base + b < cap) items[base + b] = it;
-        }
-        const int nsh = has_shared ? (N + tb - 1) / tb : 0;
-        for (int b = threadIdx.x; b < nsh; b += kPlanThreads) {
-            Item it;
-            it.expert = -1;
-            it.p0 = A + b * tb;
-            it.count = min(tb, N - b * tb);
-            it.pad = 0;
-            if (total + b < cap) items[total + b] = it;
-        }
-        if (threadIdx.x == 0) n_items[pass] = min(total + nsh, cap);
+    if (lane == 0) out->count = 0;
+    const int nb = (T + TB - 1) / TB;
+    const int incl = wave_incl_scan(nb);
+    const int excl = incl - nb;
+    const int rel = item_idx - nsh;
+    if (nb > 0 && rel >= excl && rel < incl) {
+        const int b = rel - excl;
+        Item it;
+        it.expert = e;
+        it.p0 = s0 + b * TB;
+        it.count = min(TB, T - b * TB);
+        it.pad = 0;
+        *out = it;
     }
+    return nsh + __builtin_amdgcn_readlane(incl, kWave - 1);
+}
+
+// One workgroup (4 waves) works on one item: up to TB tokens of one expert.
+// The item's activations are staged once in LDS (float16, scaled by a power of
+// two per token, in the order the dot product consumes them). Each wave then
+// owns R rows (times 64/LPR rows that share a wave when rows are short) per
+// row block; every lane reads CPL 16-byte chunks of each row, one 128-bit load
+// per chunk, with the next block's loads issued before the current block is
+// computed. Row sums are added across lanes with DPP and lane reads.
+//
+// gate/up pass with a union of at most 64 experts: the workgroup finds its
+// item from the union itself (no separate planning launch) and records the
+// item list for the down pass.
+template <bool GATEUP, int WB, int CPL, int LPR, int TB>
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs ga)
+{
+    constexpr int XDW = Fmt<WB>::xdw, EPC = Fmt<WB>::epc;
+    constexpr int XQ = XDW / 4;              // uint4 per staged chunk
+    constexpr int RPI = kWave / LPR;         // rows sharing a wave
+    constexpr int NCH = CPL * LPR;           // chunks per row
+    constexpr int R = rows_of(GATEUP, CPL);
+    constexpr int ROWS = kGemvWaves * R * RPI;  // rows per row block
+    constexpr int NM = GATEUP ? 2 : 1;          // gate and up, or down
+    static_assert(CPL == 1 || LPR == kWave, "multi-chunk lanes need full-wave rows");
+
+    extern __shared__ uint4 lds_x[];          // [TB][XQ][NCH] staged activations
+    float *lds_corr = reinterpret_cast<float *>(lds_x + TB * XQ * NCH);  // [TB][NCH]
+    __shared__ float smax[TB][kGemvWaves];
+    __shared__ float sinv[TB];
+    __shared__ Item s_item;
+
+    const Fwd &f = ga.f;
+    const Geo &g = f.g;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int item_idx = blockIdx.x / ga.n_rbg;
+    const int rbg = blockIdx.x % ga.n_rbg;
+    if (GATEUP && ga.plan_here) {
+        if (wave == 0) {
+            const int total = find_item<TB>(f, item_idx, &s_item);
+            if (lane == 0) {
+                if (rbg == 0 && s_item.count > 0) f.items[item_idx] = s_item;
+                // the first routed item's first workgroup publishes the total
+                const int nsh = f.has_shared ? (f.N + TB - 1) / TB : 0;
+                if (rbg == 0 && item_idx == nsh) *f.n_items = min(total, f.max_items);
+            }
+        }
+        __syncthreads();
+        if (s_item.count <= 0) return;  // beyond the last item: uniform exit
+    } else {
+        if (item_idx >= *f.n_items) return;  // uniform over the workgroup
+        if (tid == 0) s_item = f.items[item_idx];
+        __syncthreads();
+    }
+    const Item it = s_item;
+    const int count = min(it.count, TB);
+    const uint8_t *blk = it.expert >= 0 ? f.pool + (size_t)it.expert * f.stride : f.shared;
+    const int seg = lane / LPR, li = lane % LPR;
+    const int cols = GATEUP ? g.d : g.f;
+    const int rows = GATEUP ? g.f : g.d;
+    const long long row_bytes = GATEUP ? g.row_gu : g.row_dn;
+    const long long spr = GATEUP ? g.spr_gu : g.spr_dn;
+    const uint8_t *q0 = blk + (GATEUP ? 0 : g.off_dn);
+    const uint8_t *q1 = blk + g.off_up;
+    const uint8_t *s0 = blk + (GATEUP ? g.off_gs : g.off_ds);
+    const uint8_t *s1 = blk + g.off_us;
+    const float *in = GATEUP ? f.x : f.h;
+    float *out = GATEUP ? f.h : f.o;
+
+    uint4 w[R][CPL][NM];
+    float sc[R][CPL][NM];
+    auto load_block = [&](int blk_idx, uint4 (&wv)[R][CPL][NM], float (&sv)[R][CPL][NM]) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const long long row = min(blk_idx * ROWS + (wave * R + r) * RPI + seg, rows - 1);
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const int c = li + j * LPR;
+                const long long grp = g.group ? (long long)c * EPC / g.group : 0;
+                wv[r][j][0] = *reinterpret_cast<const uint4 *>(q0 + row * row_bytes + c * 16);
+                sv[r][j][0] = *reinterpret_cast<const float *>(s0 + (row * spr + grp) * 4);
+                if (GATEUP) {
+                    wv[r][j][NM - 1] = *reinterpret_cast<const uint4 *>(q1 + row * row_bytes + c * 16);
+                    sv[r][j][NM - 1] = *reinterpret_cast<const float *>(s1 + (row * spr + grp) * 4);
+                }
+            }
+        }
+    };
+    const int first_blk = rbg * ga.iters;
+    load_block(first_blk, w, sc);  // weights do not depend on the tokens: issue first
+
+    // ---- stage the item's activations in LDS, one token at a time ------------
+    auto token_row = [&](int i) -> const float * {
+        const int p = it.p0 + i;
+        if (GATEUP) {
+            // values read from the permutation are clamped into range, so
+            // inconsistent caller buffers cannot move an access out of bounds
+            const int t = it.expert >= 0 ? min(max(f.perm[p], 0), f.A - 1) / f.k : p - f.A;
+            return in + (size_t)t * cols;
+        }
+        return in + (size_t)p * cols;
+    };
+#pragma unroll 1
+    for (int i = 0; i < count; ++i) {
+        const float *row = token_row(i);
+        float m = 0.0f;
+        for (int c = tid; c < NCH; c += kGemvThreads) {
+            const float4 *s4 = reinterpret_cast<const float4 *>(row + (size_t)c * EPC);
+#pragma unroll
+            for (int q = 0; q < EPC / 4; ++q) {
+                const float4 f4 = s4[q];
+                m = fmaxf(m, fmaxf(fmaxf(fabsf(f4.x), fabsf(f4.y)), fmaxf(fabsf(f4.z), fabsf(f4.w))));
+            }
+        }
+        m = wave_max_dpp(m);
+        if (lane == 0) smax[i][wave] = m;
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int i = 0; i < count; ++i) {
+        const float *row = token_row(i);
+        const float m = fmaxf(fmaxf(smax[i][0], smax[i][1]), fmaxf(smax[i][2], smax[i][3]));
+        int sh = 0;
+        if (m > 0.0f && m <= 3.4e38f) {
+            int ex;
+            frexpf(m, &ex);
+            sh = min(126, max(-126, 14 - ex));
+        }
+        const float scale = ldexpf(1.0f, sh);
+        if (tid == 0) sinv[i] = ldexpf(1.0f, -sh);
+        for (int c = tid; c < NCH; c += kGemvThreads) {
+            uint32_t xs[XDW];
+            lds_corr[i * NCH + c] = stage_chunk<WB>(row + (size_t)c * EPC, scale, xs);
+#pragma unroll
+            for (int q = 0; q < XQ; ++q)
+                lds_x[(i * XQ + q) * NCH + c] =
+                    make_uint4(xs[4 * q], xs[4 * q + 1], xs[4 * q + 2], xs[4 * q + 3]);
+        }
+    }
+    __syncthreads();
+    float inv[TB];
+    int orow[TB];
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+        const int p = it.p0 + min(i, count - 1);
+        inv[i] = sinv[min(i, count - 1)];
+        orow[i] = (!GATEUP && it.expert >= 0) ? min(max(f.perm[p], 0), f.A - 1) : p;
+    }
+
+    // ---- stream the rows ------------------------------------------------------
+    const int n_blk = (rows + ROWS - 1) / ROWS;
+    const int last_blk = min(first_blk + ga.iters, n_blk);
+    for (int b = first_blk; b < last_blk; ++b) {
+        uint4 wn[R][CPL][NM];
+        float sn[R][CPL][NM];
+        if (b + 1 < last_blk) load_block(b + 1, wn, sn);
+        float acc[R][TB][NM];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < TB; ++i)
+#pragma unroll
+                for (int m = 0; m < NM; ++m) acc[r][i][m] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = li + j * LPR;
+            // codes -> float16 once per chunk, then used for every token
+            uint32_t hw[R][NM][XDW];
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < NM; ++m) extract_chunk<WB>(w[r][j][m], hw[r][m]);
+#pragma unroll
+            for (int i = 0; i < TB; ++i) {
+                if (i >= count) break;
+                uint32_t xs[XDW];
+#pragma unroll
+                for (int q = 0; q < XQ; ++q) {
+                    const uint4 v = lds_x[(i * XQ + q) * NCH + c];
+                    xs[4 * q] = v.x;
+                    xs[4 * q + 1] = v.y;
+                    xs[4 * q + 2] = v.z;
+                    xs[4 * q + 3] = v.w;
+                }
+                const float corr = lds_corr[i * NCH + c];
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int m = 0; m < NM; ++m)
+                        acc[r][i][m] = fmaf(sc[r][j][m], dot_halves<XDW>(hw[r][m], xs) - corr,
+                                            acc[r][i][m]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = b * ROWS + (wave * R + r) * RPI + seg;
+#pragma unroll
+            for (int i = 0; i < TB; ++i) {
+                if (i >= count) break;
+                float v[NM];
+#pragma unroll
+                for (int m = 0; m < NM; ++m) v[m] = seg_sum<LPR>(acc[r][i][m]);
+                if (li == 0 && row < rows) {
+                    float o;
+                    if (GATEUP) {
+                        const float gv = v[0] * inv[i], uv = v[NM - 1] * inv[i];
+                        o = gv / (1.0f + expf(-gv)) * uv;
+                    } else {
+                        o = v[0] * inv[i];
+                    }
+                    out[(size_t)orow[i] * rows + row] = o;
+                }
+            }
+        }
+        if (b + 1 < last_blk) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int j = 0; j < CPL; ++j)
+#pragma unroll
+                    for (int m = 0; m < NM; ++m) {
+                        w[r][j][m] = wn[r][j][m];
+                        sc[r][j][m] = sn[r][j][m];
+                    }
+        }
+    }
+
+}
+
+// ---- work list for larger unions ---------------------------------------------
+
+constexpr int kPlanThreads = 1024;
+
+// Same item order as find_item, for unions of any size (<= 1024 experts):
+// one workgroup, one thread per union slot, a block-wide exclusive scan.
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(Fwd f)
+{
+    __shared__ int wt[kPlanThreads / kWave];
+    const int u = threadIdx.x, lane = u % kWave, wv = u / kWave;
+    const int E = f.g.E, TB = f.tb;
+    const int nu = min(max(*f.n_union, 0), E);
+    int e = -1, s0 = 0, T = 0;
+    if (u < nu) {
+        e = f.union_ids[u];
+        if (e >= 0 && e < E) {
+            s0 = min(max(f.offsets[e], 0), f.A);
+            T = min(max(f.offsets[e + 1], s0), f.A) - s0;
+        } else {
+            e = -1;
+        }
+    }
+    const int nb = (T + TB - 1) / TB;
+    const int incl = wave_incl_scan(nb);
+    if (lane == kWave - 1) wt[wv] = incl;
+    __syncthreads();
+    if (wv == 0) {
+        int v = lane < kPlanThreads / kWave ? wt[lane] : 0;
+        v = wave_incl_scan(v);
+        if (lane < kPlanThreads / kWave) wt[lane] = v;
+    }
+    __syncthreads();
+    const int nsh = f.has_shared ? (f.N + TB - 1) / TB : 0;
+    const int base = nsh + incl - nb + (wv > 0 ? wt[wv - 1] : 0);
+    const int routed = wt[kPlanThreads / kWave - 1];
+    for (int b = u; b < nsh; b += kPlanThreads) {
+        if (b >= f.max_items) break;
+        Item it;
+        it.expert = -1;
+        it.p0 = f.A + b * TB;
+        it.count = min(TB, f.N - b * TB);
+        it.pad = 0;
+        f.items[b] = it;
+    }
+    for (int b = 0; b < nb; ++b) {
+        if (base + b >= f.max_items) break;
+        Item it;
+        it.expert = e;
+        it.p0 = s0 + b * TB;
+        it.count = min(TB, T - b * TB);
+        it.pad = 0;
+        f.items[base + b] = it;
+    }
+    if (u == 0) *f.n_items = min(nsh + routed, f.max_items);
 }
 
 // ---- combine and chaining ---------------------------------------------------
@@ -452,107 +575,147 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
 
 // ---- dispatch -------------------------------------------------------------
 
-// rows per wave for each pass
-constexpr int kRowsGateUp = 4;
-constexpr int kRowsDown = 8;
-
-template <bool GATEUP, int WB, int KS, int LPR>
-hipError_t run_gemv(GemvArgs a, int max_items, hipStream_t s)
+template <bool GATEUP, int WB, int CPL>
+constexpr int rows_per_block(int lpr)
 {
-    constexpr int RG = KS >= 4 ? 1 : (KS == 1 ? 4 : 2);
-    constexpr int R = GATEUP ? kRowsGateUp : kRowsDown;
-    constexpr int ROWS = RG * R * (kWave / LPR);
-    const int rows = GATEUP ? a.g.f : a.g.d;
-    a.n_rbg = (rows + ROWS - 1) / ROWS;
-    const long long blocks = (long long)max_items * a.n_rbg;
-    if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemv_kernel<GATEUP, WB, KS, LPR, RG, R>), dim3((unsigned)blocks),
-                       dim3(KS * RG * kWave), 0, s, a);
+    return kGemvWaves * rows_of(GATEUP, CPL) * (kWave / lpr);
+}
+
+struct Launch {
+    int n_rbg, iters;
+    long long blocks;
+};
+
+// Workgroups the device keeps resident at once for a kernel (a per-process
+// cache of the occupancy query; 0 when the query fails).
+template <typename K>
+long long resident_blocks(K kernel, size_t lds)
+{
+    static long long cache[16] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 0;
+    if (cache[dev] == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kGemvThreads, lds) !=
+                hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cache[dev] = (long long)per_cu * cus;
+    }
+    return cache[dev];
+}
+
+Launch plan_launch(int rows, int rows_per_blk, int max_items, long long resident = 0)
+{
+    Launch L;
+    const long long n_blk = (rows + rows_per_blk - 1) / rows_per_blk;
+    // one workgroup per row block while the grid fits the chip in one
+    // resident round; beyond that each workgroup takes several row blocks,
+    // loading the next one while it computes the current one
+    const long long cap = resident > 0 ? resident : 2048;
+    long long iters = ((long long)max_items * n_blk + cap - 1) / cap;
+    iters = iters < 1 ? 1 : (iters > 8 ? 8 : iters);
+    L.iters = (int)iters;
+    L.n_rbg = (int)((n_blk + iters - 1) / iters);
+    L.blocks = (long long)max_items * L.n_rbg;
+    return L;
+}
+
+template <bool GATEUP, int WB, int CPL, int LPR, int TB>
+hipError_t run_gemv(GemvArgs a, hipStream_t s)
+{
+    constexpr int ROWS = kGemvWaves * rows_of(GATEUP, CPL) * (kWave / LPR);
+    const size_t lds = (size_t)TB * CPL * LPR * stage_bytes(WB);
+    const Launch L = plan_launch(GATEUP ? a.f.g.f : a.f.g.d, ROWS, a.f.max_items,
+                                 resident_blocks(gemv_kernel<GATEUP, WB, CPL, LPR, TB>, lds));
+    a.n_rbg = L.n_rbg;
+    a.iters = L.iters;
+    if (L.blocks <= 0) return hipSuccess;
+    if (L.blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemv_kernel<GATEUP, WB, CPL, LPR, TB>), dim3((unsigned)L.blocks),
+                       dim3(kGemvThreads), lds, s, a);
     return hipGetLastError();
 }
 
+template <bool GATEUP, int WB, int CPL, int LPR>
+hipError_t run_tb(const GemvArgs &a, hipStream_t s)
+{
+    switch (a.f.tb) {
+    case 1: return run_gemv<GATEUP, WB, CPL, LPR, 1>(a, s);
+    case 2: return run_gemv<GATEUP, WB, CPL, LPR, 2>(a, s);
+    case 4:
+        if constexpr (4 * CPL * LPR * stage_bytes(WB) <= 65536)
+            return run_gemv<GATEUP, WB, CPL, LPR, 4>(a, s);
+        return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <bool GATEUP, int WB>
-hipError_t dispatch_shape(int cpl, int lpr, const GemvArgs &a, int max_items, hipStream_t s)
+hipError_t dispatch_shape(int cpl, int lpr, const GemvArgs &a, hipStream_t s)
 {
     if (lpr == kWave) {
         switch (cpl) {
-        case 1: return run_gemv<GATEUP, WB, 1, 64>(a, max_items, s);
-        case 2: return run_gemv<GATEUP, WB, 2, 64>(a, max_items, s);
-        case 3: return run_gemv<GATEUP, WB, 3, 64>(a, max_items, s);
-        case 4: return run_gemv<GATEUP, WB, 4, 64>(a, max_items, s);
-        case 6: return run_gemv<GATEUP, WB, 6, 64>(a, max_items, s);
-        case 8: return run_gemv<GATEUP, WB, 8, 64>(a, max_items, s);
+        case 1: return run_tb<GATEUP, WB, 1, 64>(a, s);
+        case 2: return run_tb<GATEUP, WB, 2, 64>(a, s);
+        case 3: return run_tb<GATEUP, WB, 3, 64>(a, s);
+        case 4: return run_tb<GATEUP, WB, 4, 64>(a, s);
+        case 6: return run_tb<GATEUP, WB, 6, 64>(a, s);
+        case 8: return run_tb<GATEUP, WB, 8, 64>(a, s);
         default: return hipErrorInvalidValue;
         }
     }
     if (cpl != 1) return hipErrorInvalidValue;
     switch (lpr) {
-    case 2: return run_gemv<GATEUP, WB, 1, 2>(a, max_items, s);
-    case 4: return run_gemv<GATEUP, WB, 1, 4>(a, max_items, s);
-    case 8: return run_gemv<GATEUP, WB, 1, 8>(a, max_items, s);
-    case 16: return run_gemv<GATEUP, WB, 1, 16>(a, max_items, s);
-    case 32: return run_gemv<GATEUP, WB, 1, 32>(a, max_items, s);
+    case 2: return run_tb<GATEUP, WB, 1, 2>(a, s);
+    case 4: return run_tb<GATEUP, WB, 1, 4>(a, s);
+    case 8: return run_tb<GATEUP, WB, 1, 8>(a, s);
+    case 16: return run_tb<GATEUP, WB, 1, 16>(a, s);
+    case 32: return run_tb<GATEUP, WB, 1, 32>(a, s);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_pass(bool gateup, const Geo &g, const uint8_t *pool, size_t stride,
-                       const uint8_t *shared, const float *in, int k, const int32_t *perm, int A,
-                       int N, const Item *items, const int32_t *n_items, int max_items, float *out,
-                       hipStream_t s)
-{
-    GemvArgs a;
-    a.g = g;
-    a.pool = pool;
-    a.stride = stride;
-    a.shared = shared;
-    a.in = in;
-    a.k = k;
-    a.perm = perm;
-    a.A = A;
-    a.N = N;
-    a.items = items;
-    a.n_items = n_items;
-    a.n_rbg = 0;
-    a.out = out;
-    const int lpr = gateup ? g.gu_lpr : g.dn_lpr;
-    const int cpl = gateup ? g.gu_cpl : g.dn_cpl;
-    if (gateup)
-        return g.wbits == 4 ? dispatch_shape<true, 4>(cpl, lpr, a, max_items, s)
-                            : dispatch_shape<true, 8>(cpl, lpr, a, max_items, s);
-    return g.wbits == 4 ? dispatch_shape<false, 4>(cpl, lpr, a, max_items, s)
-                        : dispatch_shape<false, 8>(cpl, lpr, a, max_items, s);
-}
-
 }  // namespace
 
-int tokens_per_item(int, int) { return kTB; }
-
-hipError_t launch_plan(const int32_t *union_ids, const int32_t *n_union, const int32_t *offsets,
-                       int E, int A, int N, int has_shared, int tb_gu, int tb_dn, int max_gu,
-                       int max_dn, Item *items_gu, Item *items_dn, int32_t *n_items, hipStream_t s)
+int gemv_tokens_per_item(const Geo &g, int n_tokens)
 {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, union_ids, n_union,
-                       offsets, E, A, N, has_shared, tb_gu, tb_dn, max_gu, max_dn, items_gu,
-                       items_dn, n_items);
-    return hipGetLastError();
+    // the smallest of 1, 2, 4 that covers the batch, within 64 KB of staged
+    // activations for both passes (an expert has at most n_tokens tokens)
+    int tb = n_tokens <= 1 ? 1 : (n_tokens <= 2 ? 2 : 4);
+    const int worst = (g.gu_cpl * g.gu_lpr > g.dn_cpl * g.dn_lpr ? g.gu_cpl * g.gu_lpr
+                                                                  : g.dn_cpl * g.dn_lpr) *
+                      stage_bytes(g.wbits);
+    while (tb > 1 && tb * worst > 65536) tb /= 2;
+    return tb;
 }
 
-hipError_t launch_gateup(const Geo &g, const uint8_t *pool, size_t stride, const uint8_t *shared,
-                         const float *x, int k, const int32_t *perm, int A, const Item *items,
-                         const int32_t *n_items, int max_items, float *h, hipStream_t s)
+hipError_t launch_gateup(const Fwd &f, hipStream_t s)
 {
-    return launch_pass(true, g, pool, stride, shared, x, k, perm, A, A / k, items, n_items,
-                       max_items, h, s);
+    GemvArgs a;
+    a.f = f;
+    a.n_rbg = a.iters = 0;
+    // a union of at most 64 experts is scanned inside the kernel; larger
+    // ones get their work list from one planning workgroup first
+    const int max_union = f.A < f.g.E ? f.A : f.g.E;
+    a.plan_here = max_union <= kWave;
+    if (!a.plan_here) {
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, f);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return f.g.wbits == 4 ? dispatch_shape<true, 4>(f.g.gu_cpl, f.g.gu_lpr, a, s)
+                          : dispatch_shape<true, 8>(f.g.gu_cpl, f.g.gu_lpr, a, s);
 }
 
-hipError_t launch_down(const Geo &g, const uint8_t *pool, size_t stride, const uint8_t *shared,
-                       const float *h, int k, const int32_t *perm, int A, const Item *items,
-                       const int32_t *n_items, int max_items, float *o, hipStream_t s)
+hipError_t launch_down(const Fwd &f, hipStream_t s)
 {
-    return launch_pass(false, g, pool, stride, shared, h, k, perm, A, A / k, items, n_items,
-                       max_items, o, s);
+    GemvArgs a;
+    a.f = f;
+    a.n_rbg = a.iters = 0;
+    a.plan_here = 0;
+    return f.g.wbits == 4 ? dispatch_shape<false, 4>(f.g.dn_cpl, f.g.dn_lpr, a, s)
+                          : dispatch_shape<false, 8>(f.g.dn_cpl, f.g.dn_lpr, a, s);
 }
 
 hipError_t launch_combine(const float *o, const float *w, int N, int k, int d, int A,

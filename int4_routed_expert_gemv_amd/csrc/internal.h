@@ -33,9 +33,27 @@ struct Geo {
     long long off_up, off_dn, off_gs, off_us, off_ds;  // byte offsets in a block
 };
 
+// Everything the expert kernels of one moe_expert_forward call need.
+struct Fwd {
+    Geo g;
+    const uint8_t *pool;
+    size_t stride;
+    const uint8_t *shared;
+    const float *x;          // [N][d] layer input
+    const float *w;          // [N][k] gate weights
+    int k, N, A, has_shared; // A = N * k assignments
+    const int32_t *union_ids, *n_union, *offsets, *perm;  // moe_union outputs
+    float *h;                // [A + N][f] hidden (workspace)
+    float *o;                // [A + N][d] expert outputs (workspace)
+    float *y;                // [N][d] layer output
+    Item *items;             // [max_items] work list (workspace)
+    int32_t *n_items;        // [1]
+    int tb;                  // tokens per work item
+    int max_items;           // host bound of the number of items
+};
+
 // ---- host helpers (abi.hip) --------------------------------------------
 moe_status resolve_geo(const moe_expert_pool *p, Geo *g);
-int tokens_per_item(int wbits, int cpl);
 
 // ---- launchers (each in its own translation unit) ----------------------
 hipError_t launch_router(const float *x, int N, int d, const float *wr, const float *b,
@@ -45,17 +63,9 @@ hipError_t launch_topk(const float *scores, int N, int E, int k, int32_t *ids, f
 hipError_t launch_union(const int32_t *ids, int A, int E, int32_t *union_ids, int32_t *n_union,
                         int32_t *offsets, int32_t *perm, hipStream_t s);
 hipError_t launch_hit_count(const int32_t *ids, int A, int E, uint64_t *counters, hipStream_t s);
-hipError_t launch_plan(const int32_t *union_ids, const int32_t *n_union, const int32_t *offsets,
-                       int E, int A, int N, int has_shared, int tb_gu, int tb_dn, int max_gu,
-                       int max_dn, Item *items_gu, Item *items_dn, int32_t *n_items, hipStream_t s);
-hipError_t launch_gateup(const Geo &g, const uint8_t *pool, size_t stride, const uint8_t *shared,
-                         const float *x, int k, const int32_t *perm, int A,
-                         const Item *items, const int32_t *n_items, int max_items,
-                         float *h, hipStream_t s);
-hipError_t launch_down(const Geo &g, const uint8_t *pool, size_t stride, const uint8_t *shared,
-                       const float *h, int k, const int32_t *perm, int A,
-                       const Item *items, const int32_t *n_items, int max_items,
-                       float *o, hipStream_t s);
+int gemv_tokens_per_item(const Geo &g, int n_tokens);
+hipError_t launch_gateup(const Fwd &f, hipStream_t s);
+hipError_t launch_down(const Fwd &f, hipStream_t s);
 hipError_t launch_combine(const float *o, const float *w, int N, int k, int d, int A,
                           int has_shared, float *y, hipStream_t s);
 hipError_t launch_residual_rmsnorm(float *h, const float *y, float *a, int N, int d, float eps,

@@ -17,13 +17,38 @@ constexpr int kMaxRowVec = 16;  // row of Wr cached in registers up to 16 float4
 
 __device__ __forceinline__ float sigmoidf(float l) { return 1.0f / (1.0f + expf(-l)); }
 
-// Decode-sized batches: one workgroup per expert streams its router row once
-// (kept in registers) and dots it with every token.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                              0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float lane_f(float v, int l)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// Sum over the wave (uniform result): DPP within rows of 16, then lane reads.
+__device__ __forceinline__ float wave_sum_dpp(float v)
+{
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    v += dpp<0x141>(v);
+    v += dpp<0x140>(v);
+    return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+
+constexpr int kTokGroup = 4;
+
+// Decode-sized batches: one workgroup per expert keeps its router row in
+// registers (read from HBM once) and dots it with the tokens, four tokens per
+// reduction round.
 __global__ __launch_bounds__(kRouterThreads) void router_gemv_kernel(
     const float *__restrict__ x, int N, int d, const float *__restrict__ wr,
     const float *__restrict__ b, int E, float *__restrict__ scores)
 {
-    __shared__ float part[kRouterThreads / kWave];
+    __shared__ float part[kTokGroup][kRouterThreads / kWave];
     const int e = blockIdx.x;
     const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
     const int nq = d / 4;
@@ -31,32 +56,38 @@ __global__ __launch_bounds__(kRouterThreads) void router_gemv_kernel(
     float4 w[kMaxRowVec];
 #pragma unroll
     for (int m = 0; m < kMaxRowVec; ++m) {
-        int q = tid + m * kRouterThreads;
+        const int q = tid + m * kRouterThreads;
         w[m] = q < nq ? row[q] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     const float bias = b ? b[e] : 0.0f;
-    for (int t = 0; t < N; ++t) {
-        const float4 *xt = reinterpret_cast<const float4 *>(x + (size_t)t * d);
-        float acc = 0.0f;
+    for (int t0 = 0; t0 < N; t0 += kTokGroup) {
+        float acc[kTokGroup];
 #pragma unroll
-        for (int m = 0; m < kMaxRowVec; ++m) {
-            int q = tid + m * kRouterThreads;
-            if (q < nq) {
-                float4 v = xt[q];
-                acc = fmaf(w[m].x, v.x, acc);
-                acc = fmaf(w[m].y, v.y, acc);
-                acc = fmaf(w[m].z, v.z, acc);
-                acc = fmaf(w[m].w, v.w, acc);
+        for (int i = 0; i < kTokGroup; ++i) {
+            acc[i] = 0.0f;
+            if (t0 + i >= N) continue;
+            const float4 *xt = reinterpret_cast<const float4 *>(x + (size_t)(t0 + i) * d);
+#pragma unroll
+            for (int m = 0; m < kMaxRowVec; ++m) {
+                const int q = tid + m * kRouterThreads;
+                if (q < nq) {
+                    const float4 v = xt[q];
+                    acc[i] = fmaf(w[m].x, v.x, acc[i]);
+                    acc[i] = fmaf(w[m].y, v.y, acc[i]);
+                    acc[i] = fmaf(w[m].z, v.z, acc[i]);
+                    acc[i] = fmaf(w[m].w, v.w, acc[i]);
+                }
             }
         }
-        acc = wave_sum(acc);
-        if (lane == 0) part[wv] = acc;
-        __syncthreads();
-        if (tid == 0) {
-            float l = part[0];
 #pragma unroll
-            for (int i = 1; i < kRouterThreads / kWave; ++i) l += part[i];
-            scores[(size_t)t * E + e] = sigmoidf(l + bias);
+        for (int i = 0; i < kTokGroup; ++i) {
+            const float v = wave_sum_dpp(acc[i]);
+            if (lane == 0) part[i][wv] = v;
+        }
+        __syncthreads();
+        if (tid < kTokGroup && t0 + tid < N) {
+            const float l = (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]);
+            scores[(size_t)(t0 + tid) * E + e] = sigmoidf(l + bias);
         }
         __syncthreads();
     }
@@ -206,7 +237,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
 hipError_t launch_router(const float *x, int N, int d, const float *wr, const float *b, int E,
                          float *scores, hipStream_t s)
 {
-    if (N <= 32) {
+    if (N <= 512) {
         if (d <= 4 * kMaxRowVec * kRouterThreads)
             hipLaunchKernelGGL(router_gemv_kernel, dim3(E), dim3(kRouterThreads), 0, s, x, N, d,
                                wr, b, E, scores);
