@@ -146,7 +146,7 @@ def main():
         if ev is None:
             rc |= Lb.moe_expert_forward(*fwd)
         else:
-            rc |= Lb.moe_expert_forward_timed(*fwd, ctypes.byref(ev))
+            rc |= Lb.moe_expert_forward_ex(*fwd, ctypes.byref(ev))
         if rc:
             raise RuntimeError(f"layer step failed with status {rc}")
 
@@ -164,7 +164,7 @@ def main():
 
     # --- timed region -------------------------------------------------------
     K = args.steps
-    evs = [moe.ForwardEvents(hip.event(), hip.event(), hip.event(), hip.event()) for _ in range(K)]
+    evs = [moe.ForwardOptions(*[hip.event() for _ in range(8)], 0) for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
@@ -176,7 +176,8 @@ def main():
     gu_ms = [hip.elapsed_ms(e.gateup_start, e.gateup_end) for e in evs]
     dn_ms = [hip.elapsed_ms(e.down_start, e.down_end) for e in evs]
     for e in evs:
-        for h in (e.gateup_start, e.gateup_end, e.down_start, e.down_end):
+        for h in (e.gateup_start, e.gateup_end, e.down_start, e.down_end, e.mfma_gateup_start,
+                  e.mfma_gateup_end, e.mfma_down_start, e.mfma_down_end):
             hip.L.hipEventDestroy(h)
 
     # --- algorithmic bytes ---------------------------------------------------

@@ -143,9 +143,10 @@ moe_status moe_union(const int32_t *topk_ids, int n_tokens, int k, int n_experts
  * over the union produced by moe_union (union_ids, n_union, expert_offsets,
  * perm are its outputs for the same n_tokens and k). topk_w is an input, so a
  * caller may inject gate weights. Each distinct expert's weights are streamed
- * once per call for all of its tokens. y [n_tokens][d_model] float32 is
- * overwritten. workspace: at least moe_forward_workspace_size(pool, n_tokens,
- * k) bytes, MOE_ALIGN-aligned.
+ * once per call for all of its tokens (decode-sized groups on GEMV kernels,
+ * larger groups on the matrix cores, see moe_expert_forward_ex). y
+ * [n_tokens][d_model] float32 is overwritten. workspace: at least
+ * moe_forward_workspace_size(pool, n_tokens, k) bytes, MOE_ALIGN-aligned.
  * Colibri pages: "Exact Architecture and Data-Flow Reconstruction" (three-
  * matrix expert MLP, always-on shared expert); README "Get started" (int4
  * group-scaled experts).
@@ -159,24 +160,37 @@ moe_status moe_expert_forward(const moe_expert_pool *pool /* (host) */,
                               hipStream_t stream);
 
 /*
- * moe_expert_forward with timing: the same computation, and when `events` is
- * not NULL each non-NULL event in it is recorded on `stream` right before or
- * after the kernel it names (events are created and owned by the caller).
- * Lets a caller time the expert kernels alone with HIP events.
+ * moe_expert_forward with options (options may be NULL: same as
+ * moe_expert_forward).
+ *   mfma_min_tokens: experts with at least this many tokens in the batch
+ *     (and the shared expert when n_tokens reaches it) are computed by the
+ *     grouped-GEMM kernels on the matrix cores, the others by the GEMV
+ *     kernels; 0 selects the default (32), a negative value keeps every
+ *     expert on the GEMV kernels. The matrix-core path needs int4 weights
+ *     and d_model, d_ff multiples of 64; otherwise every expert uses GEMV.
+ *   events: each non-NULL event is taken by the dispatch of the kernel it
+ *     names (hipExtLaunchKernelGGL), at that kernel's start or end. Events
+ *     are created and owned by the caller; a kernel that a call does not
+ *     launch leaves its events untouched.
+ * The results agree with moe_expert_forward to the library's tolerance for
+ * every mfma_min_tokens (bit for bit when the same kernels are selected).
  */
 typedef struct {
-    hipEvent_t gateup_start, gateup_end;  /* around the gate/up kernel */
-    hipEvent_t down_start, down_end;      /* around the down kernel */
-} moe_forward_events;
+    hipEvent_t gateup_start, gateup_end;              /* GEMV gate/up kernel */
+    hipEvent_t down_start, down_end;                  /* GEMV down kernel */
+    hipEvent_t mfma_gateup_start, mfma_gateup_end;    /* matrix-core gate/up kernel */
+    hipEvent_t mfma_down_start, mfma_down_end;        /* matrix-core down kernel */
+    int32_t mfma_min_tokens;
+} moe_forward_options;
 
-moe_status moe_expert_forward_timed(const moe_expert_pool *pool /* (host) */,
-                                    const float *x, int n_tokens, int k,
-                                    const float *topk_w,
-                                    const int32_t *union_ids, const int32_t *n_union,
-                                    const int32_t *expert_offsets, const int32_t *perm,
-                                    float *y, void *workspace, size_t ws_bytes,
-                                    hipStream_t stream,
-                                    const moe_forward_events *events /* (host) */);
+moe_status moe_expert_forward_ex(const moe_expert_pool *pool /* (host) */,
+                                 const float *x, int n_tokens, int k,
+                                 const float *topk_w,
+                                 const int32_t *union_ids, const int32_t *n_union,
+                                 const int32_t *expert_offsets, const int32_t *perm,
+                                 float *y, void *workspace, size_t ws_bytes,
+                                 hipStream_t stream,
+                                 const moe_forward_options *options /* (host) */);
 
 /*
  * Learn: counters[e] += #{(t, j) : topk_ids[t][j] == e}, uint64, accumulated

@@ -28,7 +28,7 @@ MOE_MAX_EXPERTS = 1024
 MOE_ALIGN = 256
 
 EXPORTED = [
-    "moe_route_topk", "moe_union", "moe_expert_forward", "moe_expert_forward_timed",
+    "moe_route_topk", "moe_union", "moe_expert_forward", "moe_expert_forward_ex",
     "moe_hit_count", "moe_residual_rmsnorm", "moe_route_workspace_size", "moe_forward_workspace_size",
     "moe_workspace_size", "moe_block_bytes", "moe_pack_expert", "moe_strerror",
 ]
@@ -40,10 +40,13 @@ class MoeError(RuntimeError):
         super().__init__(f"{call}: {strerror(status)} (status {status})")
 
 
-class ForwardEvents(ctypes.Structure):
-    """struct moe_forward_events (HIP event handles, NULL = not recorded)"""
+class ForwardOptions(ctypes.Structure):
+    """struct moe_forward_options (HIP event handles, NULL = not taken)"""
     _fields_ = [("gateup_start", ctypes.c_void_p), ("gateup_end", ctypes.c_void_p),
-                ("down_start", ctypes.c_void_p), ("down_end", ctypes.c_void_p)]
+                ("down_start", ctypes.c_void_p), ("down_end", ctypes.c_void_p),
+                ("mfma_gateup_start", ctypes.c_void_p), ("mfma_gateup_end", ctypes.c_void_p),
+                ("mfma_down_start", ctypes.c_void_p), ("mfma_down_end", ctypes.c_void_p),
+                ("mfma_min_tokens", ctypes.c_int32)]
 
 
 class PoolDesc(ctypes.Structure):
@@ -76,8 +79,8 @@ def lib():
         L.moe_route_topk.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, vp, vp, sz, vp]
         L.moe_union.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp]
         L.moe_expert_forward.argtypes = [P, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        L.moe_expert_forward_timed.argtypes = [P, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp,
-                                               ctypes.POINTER(ForwardEvents)]
+        L.moe_expert_forward_ex.argtypes = [P, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                            ctypes.POINTER(ForwardOptions)]
         L.moe_hit_count.argtypes = [vp, i32, i32, i32, vp, vp]
         L.moe_residual_rmsnorm.argtypes = [vp, vp, vp, i32, i32, f32, vp]
         L.moe_route_workspace_size.argtypes = [i32, i32]
@@ -88,7 +91,7 @@ def lib():
         L.moe_strerror.argtypes = [i32]
         L.moe_strerror.restype = ctypes.c_char_p
         for name in ("moe_route_topk", "moe_union", "moe_expert_forward",
-                     "moe_expert_forward_timed", "moe_hit_count",
+                     "moe_expert_forward_ex", "moe_hit_count",
                      "moe_residual_rmsnorm", "moe_pack_expert"):
             getattr(L, name).restype = i32
         for name in ("moe_route_workspace_size", "moe_forward_workspace_size",
@@ -187,8 +190,8 @@ def hit_count(topk_ids, n_experts, counters, stream=None):
 
 
 def expert_forward(pool: PoolDesc, x, k, topk_w, union_ids, n_union, expert_offsets, perm, y,
-                   workspace, stream=None, events: ForwardEvents | None = None):
-    """moe_expert_forward, or moe_expert_forward_timed when events are given."""
+                   workspace, stream=None, options: ForwardOptions | None = None):
+    """moe_expert_forward, or moe_expert_forward_ex when options are given."""
     import torch
     _expect(x, torch.float32, "x")
     _expect(topk_w, torch.float32, "topk_w")
@@ -197,11 +200,10 @@ def expert_forward(pool: PoolDesc, x, k, topk_w, union_ids, n_union, expert_offs
     args = (ctypes.byref(pool), _ptr(x), N, k, _ptr(topk_w), _ptr(union_ids), _ptr(n_union),
             _ptr(expert_offsets), _ptr(perm), _ptr(y), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
-    if events is None:
+    if options is None:
         _check(lib().moe_expert_forward(*args), "moe_expert_forward")
     else:
-        _check(lib().moe_expert_forward_timed(*args, ctypes.byref(events)),
-               "moe_expert_forward_timed")
+        _check(lib().moe_expert_forward_ex(*args, ctypes.byref(options)), "moe_expert_forward_ex")
 
 
 def residual_rmsnorm(h, y, a, eps=1e-6, stream=None):

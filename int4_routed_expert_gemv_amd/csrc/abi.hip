@@ -45,13 +45,16 @@ long long n_scales(long long rows, long long cols, int group)
     return group ? rows * (cols / group) : rows;
 }
 
+// Default: experts with at least this many tokens use the MFMA pass.
+constexpr int kDefaultMfmaMinTokens = 32;
+
 // Workspace of moe_expert_forward, laid out in this order.
 struct FwdLayout {
-    int tb, max_items, P;
-    long long items, n_items, h, o, total;
+    int tb, max_items, max_mitems, tstar, P;
+    long long items, n_items, mitems, n_mitems, h, o, total;
 };
 
-FwdLayout fwd_layout(const Geo &g, int N, int k, int has_shared)
+FwdLayout fwd_layout(const Geo &g, int N, int k, int has_shared, int mfma_min_tokens)
 {
     FwdLayout L;
     const long long A = (long long)N * k;
@@ -59,10 +62,19 @@ FwdLayout fwd_layout(const Geo &g, int N, int k, int has_shared)
     // each union expert adds at most one partly filled item
     const long long ue = A < g.E ? A : g.E;
     L.max_items = (int)((A + L.tb - 1) / L.tb + ue + (has_shared ? (N + L.tb - 1) / L.tb : 0));
+    // the MFMA pass runs when some expert can reach the threshold (an expert
+    // has at most N tokens)
+    L.tstar = mfma_min_tokens > 0 ? mfma_min_tokens : kDefaultMfmaMinTokens;
+    const bool mfma = mfma_min_tokens >= 0 && mfma_supported(g) && N >= L.tstar;
+    const long long mt = mfma_tokens_per_item();
+    L.max_mitems = mfma ? (int)((A + mt - 1) / mt + A / L.tstar + (has_shared ? (N + mt - 1) / mt : 0))
+                        : 0;
     L.P = (int)(A + (has_shared ? N : 0));
     long long off = 0;
     L.items = off; off = align_up(off + (long long)L.max_items * (long long)sizeof(Item));
     L.n_items = off; off = align_up(off + 4);
+    L.mitems = off; off = align_up(off + (long long)L.max_mitems * (long long)sizeof(Item));
+    L.n_mitems = off; off = align_up(off + 4);
     L.h = off; off = align_up(off + (long long)L.P * g.f * 4);
     L.o = off; off = align_up(off + (long long)L.P * g.d * 4);
     L.total = off;
@@ -135,7 +147,10 @@ size_t moe_forward_workspace_size(const moe_expert_pool *pool, int n_tokens, int
 {
     Geo g;
     if (resolve_geo(pool, &g) != MOE_OK || n_tokens < 0 || k < 1) return 0;
-    return (size_t)fwd_layout(g, n_tokens, k, pool->shared != nullptr).total;
+    // the largest of the layouts any option can select
+    const size_t a = (size_t)fwd_layout(g, n_tokens, k, pool->shared != nullptr, 1).total;
+    const size_t b = (size_t)fwd_layout(g, n_tokens, k, pool->shared != nullptr, -1).total;
+    return a > b ? a : b;
 }
 
 size_t moe_workspace_size(const moe_expert_pool *pool, int n_tokens, int k)
@@ -214,27 +229,21 @@ moe_status moe_hit_count(const int32_t *topk_ids, int n_tokens, int k, int n_exp
     return MOE_OK;
 }
 
-static bool record(hipEvent_t ev, hipStream_t s)
-{
-    return ev == nullptr || hipEventRecord(ev, s) == hipSuccess;
-}
-
 moe_status moe_expert_forward(const moe_expert_pool *pool, const float *x, int n_tokens, int k,
                               const float *topk_w, const int32_t *union_ids,
                               const int32_t *n_union, const int32_t *expert_offsets,
                               const int32_t *perm, float *y, void *workspace, size_t ws_bytes,
                               hipStream_t stream)
 {
-    return moe_expert_forward_timed(pool, x, n_tokens, k, topk_w, union_ids, n_union,
-                                    expert_offsets, perm, y, workspace, ws_bytes, stream, nullptr);
+    return moe_expert_forward_ex(pool, x, n_tokens, k, topk_w, union_ids, n_union, expert_offsets,
+                                 perm, y, workspace, ws_bytes, stream, nullptr);
 }
 
-moe_status moe_expert_forward_timed(const moe_expert_pool *pool, const float *x, int n_tokens,
-                                    int k, const float *topk_w, const int32_t *union_ids,
-                                    const int32_t *n_union, const int32_t *expert_offsets,
-                                    const int32_t *perm, float *y, void *workspace,
-                                    size_t ws_bytes, hipStream_t stream,
-                                    const moe_forward_events *ev)
+moe_status moe_expert_forward_ex(const moe_expert_pool *pool, const float *x, int n_tokens, int k,
+                                 const float *topk_w, const int32_t *union_ids,
+                                 const int32_t *n_union, const int32_t *expert_offsets,
+                                 const int32_t *perm, float *y, void *workspace, size_t ws_bytes,
+                                 hipStream_t stream, const moe_forward_options *ev)
 {
     Geo g;
     moe_status st = resolve_geo(pool, &g);
@@ -255,7 +264,7 @@ moe_status moe_expert_forward_timed(const moe_expert_pool *pool, const float *x,
         return MOE_EINVAL;
     if (((uintptr_t)x % 16) || ((uintptr_t)y % 16)) return MOE_EALIGN;
     const int has_shared = pool->shared != nullptr;
-    const FwdLayout L = fwd_layout(g, n_tokens, k, has_shared);
+    const FwdLayout L = fwd_layout(g, n_tokens, k, has_shared, ev ? ev->mfma_min_tokens : 0);
     if (!workspace || ws_bytes < (size_t)L.total) return MOE_EWORKSPACE;
     if (!aligned(workspace)) return MOE_EALIGN;
 
@@ -282,13 +291,23 @@ moe_status moe_expert_forward_timed(const moe_expert_pool *pool, const float *x,
     f.n_items = reinterpret_cast<int32_t *>(ws + L.n_items);
     f.tb = L.tb;
     f.max_items = L.max_items;
+    f.mitems = reinterpret_cast<Item *>(ws + L.mitems);
+    f.n_mitems = reinterpret_cast<int32_t *>(ws + L.n_mitems);
+    f.max_mitems = L.max_mitems;
+    f.tstar = L.tstar;
 
-    if (ev && !record(ev->gateup_start, stream)) return MOE_EHIP;
+    f.ev_gu[0] = ev ? ev->gateup_start : nullptr;
+    f.ev_gu[1] = ev ? ev->gateup_end : nullptr;
+    f.ev_dn[0] = ev ? ev->down_start : nullptr;
+    f.ev_dn[1] = ev ? ev->down_end : nullptr;
+    f.ev_mgu[0] = ev ? ev->mfma_gateup_start : nullptr;
+    f.ev_mgu[1] = ev ? ev->mfma_gateup_end : nullptr;
+    f.ev_mdn[0] = ev ? ev->mfma_down_start : nullptr;
+    f.ev_mdn[1] = ev ? ev->mfma_down_end : nullptr;
     if (launch_gateup(f, stream) != hipSuccess) return MOE_EHIP;
-    if (ev && !record(ev->gateup_end, stream)) return MOE_EHIP;
-    if (ev && !record(ev->down_start, stream)) return MOE_EHIP;
+    if (f.max_mitems > 0 && launch_mfma(f, true, stream) != hipSuccess) return MOE_EHIP;
     if (launch_down(f, stream) != hipSuccess) return MOE_EHIP;
-    if (ev && !record(ev->down_end, stream)) return MOE_EHIP;
+    if (f.max_mitems > 0 && launch_mfma(f, false, stream) != hipSuccess) return MOE_EHIP;
     if (launch_combine(f.o, topk_w, n_tokens, k, g.d, (int)A, has_shared, y, stream) != hipSuccess)
         return MOE_EHIP;
     return MOE_OK;

@@ -26,6 +26,8 @@
 //  * the group scale multiplies each chunk's float32 partial sum;
 //  * partial sums of a row are added across its lanes with shuffles and
 //    across the waves of a split row in LDS, always in the same order.
+#include <hip/hip_ext.h>
+
 #include "internal.h"
 
 namespace moe {
@@ -475,13 +477,35 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs ga)
 
 constexpr int kPlanThreads = 1024;
 
-// Same item order as find_item, for unions of any size (<= 1024 experts):
-// one workgroup, one thread per union slot, a block-wide exclusive scan.
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(Fwd f)
+__device__ int block_excl_scan(int v, int &total)
 {
     __shared__ int wt[kPlanThreads / kWave];
-    const int u = threadIdx.x, lane = u % kWave, wv = u / kWave;
-    const int E = f.g.E, TB = f.tb;
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    const int incl = wave_incl_scan(v);
+    if (lane == kWave - 1) wt[wv] = incl;
+    __syncthreads();
+    if (wv == 0) {
+        int x = lane < kPlanThreads / kWave ? wt[lane] : 0;
+        x = wave_incl_scan(x);
+        if (lane < kPlanThreads / kWave) wt[lane] = x;
+    }
+    __syncthreads();
+    total = wt[kPlanThreads / kWave - 1];
+    const int r = incl - v + (wv > 0 ? wt[wv - 1] : 0);
+    __syncthreads();
+    return r;
+}
+
+// Work lists for unions of any size (<= 1024 experts), one thread per union
+// slot. Experts with at least tstar tokens (and the shared expert when the
+// batch has at least tstar tokens) go to the MFMA list in slices of 128
+// tokens, the others to the GEMV list in slices of tb; in both lists the
+// shared expert comes first, then the union experts in union order.
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(Fwd f)
+{
+    const int u = threadIdx.x;
+    const int E = f.g.E, TB = f.tb, MT = 128;
+    const bool mfma = f.max_mitems > 0;
     const int nu = min(max(*f.n_union, 0), E);
     int e = -1, s0 = 0, T = 0;
     if (u < nu) {
@@ -493,38 +517,39 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Fwd f)
             e = -1;
         }
     }
-    const int nb = (T + TB - 1) / TB;
-    const int incl = wave_incl_scan(nb);
-    if (lane == kWave - 1) wt[wv] = incl;
-    __syncthreads();
-    if (wv == 0) {
-        int v = lane < kPlanThreads / kWave ? wt[lane] : 0;
-        v = wave_incl_scan(v);
-        if (lane < kPlanThreads / kWave) wt[lane] = v;
-    }
-    __syncthreads();
-    const int nsh = f.has_shared ? (f.N + TB - 1) / TB : 0;
-    const int base = nsh + incl - nb + (wv > 0 ? wt[wv - 1] : 0);
-    const int routed = wt[kPlanThreads / kWave - 1];
-    for (int b = u; b < nsh; b += kPlanThreads) {
+    const bool big = mfma && T >= f.tstar;
+    const int nb_g = big ? 0 : (T + TB - 1) / TB;
+    const int nb_m = big ? (T + MT - 1) / MT : 0;
+    const bool sh_big = f.has_shared && mfma && f.N >= f.tstar;
+    const int nsh_g = f.has_shared && !sh_big ? (f.N + TB - 1) / TB : 0;
+    const int nsh_m = sh_big ? (f.N + MT - 1) / MT : 0;
+    int tot_g, tot_m;
+    const int base_g = nsh_g + block_excl_scan(nb_g, tot_g);
+    const int base_m = nsh_m + block_excl_scan(nb_m, tot_m);
+    for (int b = u; b < nsh_g; b += kPlanThreads) {
         if (b >= f.max_items) break;
-        Item it;
-        it.expert = -1;
-        it.p0 = f.A + b * TB;
-        it.count = min(TB, f.N - b * TB);
-        it.pad = 0;
+        Item it = {-1, f.A + b * TB, min(TB, f.N - b * TB), 0};
         f.items[b] = it;
     }
-    for (int b = 0; b < nb; ++b) {
-        if (base + b >= f.max_items) break;
-        Item it;
-        it.expert = e;
-        it.p0 = s0 + b * TB;
-        it.count = min(TB, T - b * TB);
-        it.pad = 0;
-        f.items[base + b] = it;
+    for (int b = u; b < nsh_m; b += kPlanThreads) {
+        if (b >= f.max_mitems) break;
+        Item it = {-1, f.A + b * MT, min(MT, f.N - b * MT), 0};
+        f.mitems[b] = it;
     }
-    if (u == 0) *f.n_items = min(nsh + routed, f.max_items);
+    for (int b = 0; b < nb_g; ++b) {
+        if (base_g + b >= f.max_items) break;
+        Item it = {e, s0 + b * TB, min(TB, T - b * TB), 0};
+        f.items[base_g + b] = it;
+    }
+    for (int b = 0; b < nb_m; ++b) {
+        if (base_m + b >= f.max_mitems) break;
+        Item it = {e, s0 + b * MT, min(MT, T - b * MT), 0};
+        f.mitems[base_m + b] = it;
+    }
+    if (u == 0) {
+        *f.n_items = min(nsh_g + tot_g, f.max_items);
+        if (mfma) *f.n_mitems = min(nsh_m + tot_m, f.max_mitems);
+    }
 }
 
 // ---- combine and chaining ---------------------------------------------------
@@ -632,8 +657,13 @@ hipError_t run_gemv(GemvArgs a, hipStream_t s)
     a.iters = L.iters;
     if (L.blocks <= 0) return hipSuccess;
     if (L.blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemv_kernel<GATEUP, WB, CPL, LPR, TB>), dim3((unsigned)L.blocks),
-                       dim3(kGemvThreads), lds, s, a);
+    const hipEvent_t *ev = GATEUP ? a.f.ev_gu : a.f.ev_dn;
+    if (ev[0] || ev[1])  // events taken by the dispatch itself, around this kernel only
+        hipExtLaunchKernelGGL((gemv_kernel<GATEUP, WB, CPL, LPR, TB>), dim3((unsigned)L.blocks),
+                              dim3(kGemvThreads), lds, s, ev[0], ev[1], 0, a);
+    else
+        hipLaunchKernelGGL((gemv_kernel<GATEUP, WB, CPL, LPR, TB>), dim3((unsigned)L.blocks),
+                           dim3(kGemvThreads), lds, s, a);
     return hipGetLastError();
 }
 
@@ -695,10 +725,11 @@ hipError_t launch_gateup(const Fwd &f, hipStream_t s)
     GemvArgs a;
     a.f = f;
     a.n_rbg = a.iters = 0;
-    // a union of at most 64 experts is scanned inside the kernel; larger
-    // ones get their work list from one planning workgroup first
+    // a union of at most 64 experts is scanned inside the kernel when no
+    // expert goes to the MFMA pass; otherwise one planning workgroup builds
+    // both work lists first
     const int max_union = f.A < f.g.E ? f.A : f.g.E;
-    a.plan_here = max_union <= kWave;
+    a.plan_here = max_union <= kWave && f.max_mitems == 0;
     if (!a.plan_here) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, f);
         const hipError_t e = hipGetLastError();

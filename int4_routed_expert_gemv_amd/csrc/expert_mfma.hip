@@ -1,0 +1,273 @@
+// expert_mfma.hip - expert math for token groups large enough to be a dense
+// contraction (prefill, the shared expert of a large batch, hot experts).
+//
+// Colibri pages: "Public Colibri Observation and Revision Ledger", section
+// "Exact Architecture and Data-Flow Reconstruction" (three-matrix expert MLP,
+// always-on shared expert), README "Get started" (int4 experts with group
+// scales).
+//
+// For one expert and up to 128 of its tokens, a workgroup computes 128 output
+// rows (of gate and up together, or of down) over the full contraction:
+//   gate/up:  h[p][r] = silu(sum_c Wg[r][c] x_t[c]) * (sum_c Wu[r][c] x_t[c])
+//   down:     o[out(p)][r] = sum_c Wd[r][c] h[p][c]
+// on v_mfma_f32_32x32x16_f16 (float16 products, float32 accumulation):
+//  * activations (x or h, float32) are converted to float16 and staged in LDS,
+//    64 columns at a time, double-buffered;
+//  * every lane reads its weights straight from HBM, 16 bytes (32 int4 codes
+//    of one row) per step, and expands them in registers: OR into the
+//    mantissa of 1024 (exact), subtract 1032 (exact), multiply by the group
+//    scale (one float16 rounding);
+//  * within each 8-column group the columns are taken in the order
+//    0,4,1,5,2,6,3,7 on both operands, which lets one 32-bit word of codes
+//    feed one MFMA operand without shuffles;
+//  * each wave owns 32 rows and all 128 tokens (4 x 1 blocks of 32 x 32).
+// Workgroups are mapped so that those sharing an expert (and so its weights
+// and its tokens) land on the same XCD and share its L2.
+#include <hip/hip_ext.h>
+
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kMT = 128;            // tokens per tile
+constexpr int kNW = 32;             // rows per wave
+constexpr int kNT = 4 * kNW;        // rows per workgroup
+constexpr int kKB = 64;             // columns per step
+constexpr int kAStride = kKB + 8;   // LDS row stride (halves), padded
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+
+// 8 offset-binary int4 codes (element j in bits 4j..4j+3) times the scale,
+// as float16 in the column order 0,4,1,5,2,6,3,7.
+__device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t s2)
+{
+    const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const uint32_t m = 0x000F000Fu, magic = 0x64006400u;
+    const half2_t p0 = (as_h2((w & m) | magic) - off) * s2;
+    const half2_t p1 = (as_h2(((w >> 4) & m) | magic) - off) * s2;
+    const half2_t p2 = (as_h2(((w >> 8) & m) | magic) - off) * s2;
+    const half2_t p3 = (as_h2(((w >> 12) & m) | magic) - off) * s2;
+    half8_t r;
+    r[0] = p0[0]; r[1] = p0[1];
+    r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1];
+    r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+struct MfmaArgs {
+    Fwd f;
+    int n_tiles;        // row tiles per item
+    int n_blocks;       // grid size
+};
+
+template <bool GATEUP>
+__global__ __launch_bounds__(kThreads, 2) void mfma_kernel(MfmaArgs ma)
+{
+    constexpr int NM = GATEUP ? 2 : 1;
+    __shared__ _Float16 As[2][kMT][kAStride];
+    __shared__ int s_src[kMT];   // input row of each tile token (-1: none)
+
+    const Fwd &f = ma.f;
+    const Geo &g = f.g;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+
+    // XCD-aware order: workgroups are dealt to the XCDs round robin, so give
+    // each XCD a contiguous range of (item, row tile) pairs
+    const int b = blockIdx.x;
+    const int per_xcd = (ma.n_blocks + kXcds - 1) / kXcds;
+    const int logical = (b % kXcds) * per_xcd + b / kXcds;
+    if (logical >= ma.n_blocks) return;
+    const int item_idx = logical / ma.n_tiles;
+    const int ntile = logical % ma.n_tiles;
+    if (item_idx >= *f.n_mitems) return;
+    const Item it = f.mitems[item_idx];
+    const int count = min(it.count, kMT);
+    const uint8_t *blk = it.expert >= 0 ? f.pool + (size_t)it.expert * f.stride : f.shared;
+    const int K = GATEUP ? g.d : g.f;       // contraction length
+    const int rows = GATEUP ? g.f : g.d;    // output rows
+    const float *in = GATEUP ? f.x : f.h;
+    float *out = GATEUP ? f.h : f.o;
+
+    // input row of every tile token
+    if (tid < kMT) {
+        int src = -1;
+        if (tid < count) {
+            const int p = it.p0 + tid;
+            if (GATEUP)
+                src = it.expert >= 0 ? min(max(f.perm[p], 0), f.A - 1) / f.k : p - f.A;
+            else
+                src = p;
+        }
+        s_src[tid] = src;
+    }
+    __syncthreads();
+
+    // activation loads: thread -> (token row, half of the 64 columns)
+    const int a_row = tid / 2, a_half = tid % 2;
+    const int a_src = s_src[a_row];
+    const float *a_ptr = a_src >= 0 ? in + (size_t)a_src * K + a_half * 32 : nullptr;
+    float4 av[8];
+    auto load_a = [&](int k0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            av[q] = a_ptr ? reinterpret_cast<const float4 *>(a_ptr + k0)[q]
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    };
+    auto store_a = [&](int buf) {
+        // 32 columns = 4 groups of 8, each written in the order 0,4,1,5,2,6,3,7
+        const float *v = reinterpret_cast<const float *>(av);
+        _Float16 *dst = &As[buf][a_row][a_half * 32];
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+            half8_t h;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                h[2 * j] = (_Float16)v[8 * gi + j];
+                h[2 * j + 1] = (_Float16)v[8 * gi + 4 + j];
+            }
+            *reinterpret_cast<half8_t *>(dst + 8 * gi) = h;
+        }
+    };
+
+    // weights: this lane's row and 32-column half of each 64-column step
+    const int hh = lane / 32;
+    const int row = ntile * kNT + wave * kNW + (lane % 32);
+    const int row_c = min(row, rows - 1);
+    const long long row_bytes = K / 2;
+    const uint8_t *qb[NM];
+    const float *sb[NM];
+    const long long spr = g.group ? K / g.group : 1;
+    if (GATEUP) {
+        qb[0] = blk + (long long)row_c * row_bytes;
+        qb[NM - 1] = blk + g.off_up + (long long)row_c * row_bytes;
+        sb[0] = reinterpret_cast<const float *>(blk + g.off_gs) + (long long)row_c * spr;
+        sb[NM - 1] = reinterpret_cast<const float *>(blk + g.off_us) + (long long)row_c * spr;
+    } else {
+        qb[0] = blk + g.off_dn + (long long)row_c * row_bytes;
+        sb[0] = reinterpret_cast<const float *>(blk + g.off_ds) + (long long)row_c * spr;
+    }
+    uint4 bw[NM];
+    float bs[NM];
+    auto load_b = [&](int k0) {
+        const int col = k0 + 32 * hh;
+        const long long grp = g.group ? col / g.group : 0;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            bw[m] = *reinterpret_cast<const uint4 *>(qb[m] + col / 2);
+            bs[m] = sb[m][grp];
+        }
+    };
+
+    f32x16_t acc[NM][4];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[m][mf][r] = 0.0f;
+
+    const int steps = K / kKB;
+    load_a(0);
+    load_b(0);
+    store_a(0);
+    __syncthreads();
+    for (int ks = 0; ks < steps; ++ks) {
+        const int cur = ks & 1;
+        uint4 bw_c[NM];
+        half2_t s2[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            bw_c[m] = bw[m];
+            s2[m] = half2_t{(_Float16)bs[m], (_Float16)bs[m]};
+        }
+        if (ks + 1 < steps) {
+            load_a((ks + 1) * kKB);
+            load_b((ks + 1) * kKB);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            half8_t bf[NM];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                const uint32_t w = s == 0 ? bw_c[m].x : (s == 1 ? bw_c[m].y : (s == 2 ? bw_c[m].z : bw_c[m].w));
+                bf[m] = dequant8(w, s2[m]);
+            }
+#pragma unroll
+            for (int mf = 0; mf < 4; ++mf) {
+                const half8_t af =
+                    *reinterpret_cast<const half8_t *>(&As[cur][mf * 32 + (lane % 32)][32 * hh + 8 * s]);
+#pragma unroll
+                for (int m = 0; m < NM; ++m)
+                    acc[m][mf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[m], acc[m][mf], 0, 0, 0);
+            }
+        }
+        if (ks + 1 < steps) store_a(cur ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: lane holds column `row` of four 32x32 blocks; register r of
+    // block mf is token mf*32 + (r/4)*8 + (lane/32)*4 + r%4
+    if (row >= rows) return;
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int tok = mf * 32 + (r / 4) * 8 + hh * 4 + (r % 4);
+            if (tok >= count) continue;
+            const int p = it.p0 + tok;
+            if (GATEUP) {
+                const float gv = acc[0][mf][r], uv = acc[NM - 1][mf][r];
+                out[(size_t)p * rows + row] = gv / (1.0f + expf(-gv)) * uv;
+            } else {
+                const int orow = it.expert >= 0 ? min(max(f.perm[p], 0), f.A - 1) : p;
+                out[(size_t)orow * rows + row] = acc[0][mf][r];
+            }
+        }
+    }
+}
+
+}  // namespace
+
+bool mfma_supported(const Geo &g)
+{
+    return g.wbits == 4 && g.d % kKB == 0 && g.f % kKB == 0;
+}
+
+int mfma_tokens_per_item() { return kMT; }
+
+hipError_t launch_mfma(const Fwd &f, bool gateup, hipStream_t s)
+{
+    MfmaArgs a;
+    a.f = f;
+    const int rows = gateup ? f.g.f : f.g.d;
+    a.n_tiles = (rows + kNT - 1) / kNT;
+    const long long blocks = (long long)f.max_mitems * a.n_tiles;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    a.n_blocks = (int)blocks;
+    const hipEvent_t *ev = gateup ? f.ev_mgu : f.ev_mdn;
+    if (gateup) {
+        if (ev[0] || ev[1])
+            hipExtLaunchKernelGGL(mfma_kernel<true>, dim3(a.n_blocks), dim3(kThreads), 0, s, ev[0],
+                                  ev[1], 0, a);
+        else
+            hipLaunchKernelGGL(mfma_kernel<true>, dim3(a.n_blocks), dim3(kThreads), 0, s, a);
+    } else {
+        if (ev[0] || ev[1])
+            hipExtLaunchKernelGGL(mfma_kernel<false>, dim3(a.n_blocks), dim3(kThreads), 0, s, ev[0],
+                                  ev[1], 0, a);
+        else
+            hipLaunchKernelGGL(mfma_kernel<false>, dim3(a.n_blocks), dim3(kThreads), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -48,8 +48,16 @@ struct Fwd {
     float *y;                // [N][d] layer output
     Item *items;             // [max_items] work list (workspace)
     int32_t *n_items;        // [1]
-    int tb;                  // tokens per work item
-    int max_items;           // host bound of the number of items
+    int tb;                  // tokens per GEMV work item
+    int max_items;           // host bound of the number of GEMV items
+    Item *mitems;            // [max_mitems] MFMA work list (workspace)
+    int32_t *n_mitems;       // [1]
+    int max_mitems;          // host bound of the number of MFMA items (0: no MFMA pass)
+    int tstar;               // experts with at least this many tokens use the MFMA pass
+    hipEvent_t ev_gu[2];     // optional: taken at the GEMV gate/up kernel's start and end
+    hipEvent_t ev_dn[2];     // optional: the same for the GEMV down kernel
+    hipEvent_t ev_mgu[2];    // optional: the same for the MFMA gate/up kernel
+    hipEvent_t ev_mdn[2];    // optional: the same for the MFMA down kernel
 };
 
 // ---- host helpers (abi.hip) --------------------------------------------
@@ -66,6 +74,9 @@ hipError_t launch_hit_count(const int32_t *ids, int A, int E, uint64_t *counters
 int gemv_tokens_per_item(const Geo &g, int n_tokens);
 hipError_t launch_gateup(const Fwd &f, hipStream_t s);
 hipError_t launch_down(const Fwd &f, hipStream_t s);
+bool mfma_supported(const Geo &g);
+int mfma_tokens_per_item();
+hipError_t launch_mfma(const Fwd &f, bool gateup, hipStream_t s);
 hipError_t launch_combine(const float *o, const float *w, int N, int k, int d, int A,
                           int has_shared, float *y, hipStream_t s);
 hipError_t launch_residual_rmsnorm(float *h, const float *y, float *a, int N, int d, float eps,

@@ -16,8 +16,10 @@ def workspace(pool, N, k, device="cuda"):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def run_layer(pool, x, wr, b, k, ids_in=None, w_in=None, counters=None, device="cuda"):
-    """route_topk (unless ids_in/w_in are given) -> union -> hit_count -> expert_forward."""
+def run_layer(pool, x, wr, b, k, ids_in=None, w_in=None, counters=None, device="cuda",
+              mfma_min_tokens=None):
+    """route_topk (unless ids_in/w_in are given) -> union -> hit_count -> expert_forward
+    (moe_expert_forward_ex with that threshold when mfma_min_tokens is given)."""
     N, d = x.shape
     E = pool.desc.n_experts
     xd = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(device)
@@ -39,7 +41,12 @@ def run_layer(pool, x, wr, b, k, ids_in=None, w_in=None, counters=None, device="
     cnt = torch.zeros(E, dtype=torch.int64, device=device) if counters is None else counters
     moe.hit_count(ids, E, cnt)
     y = torch.empty((N, d), dtype=torch.float32, device=device)
-    moe.expert_forward(pool.desc, xd, k, w, union_ids, n_union, offsets, perm, y, ws)
+    opts = None
+    if mfma_min_tokens is not None:
+        opts = moe.ForwardOptions()
+        opts.mfma_min_tokens = mfma_min_tokens
+    moe.expert_forward(pool.desc, xd, k, w, union_ids, n_union, offsets, perm, y, ws,
+                       options=opts)
     torch.cuda.synchronize()
     nu = int(n_union.item())
     return dict(ids=ids.cpu().numpy(), w=w.cpu().numpy(), union_ids=union_ids.cpu().numpy()[:nu],

@@ -58,15 +58,16 @@ def oracle_then_pool(cfg, layer=0, x=None):
     return spec, x, wr, b, blocks, shared, nre
 
 
-def full_parity(cfg, layer=0):
+def full_parity(cfg, layer=0, mfma_min_tokens=None):
     spec, x, wr, b, blocks, shared, nre = oracle_then_pool(cfg, layer)
     say(f"[{cfg.name}] N={cfg.n_tokens} k={cfg.k} d={spec.d} f={spec.f} E={spec.n_experts} "
         f"wbits={spec.wbits} G={spec.group} redrawn={nre}")
     ref = oracle.layer_step(x, wr, b, cfg.k, blocks, shared, spec.d, spec.f, spec.wbits,
                             spec.group)
     pool = upload_pool(spec, blocks, shared)   # packs the blocks in place: oracle first
-    say(f"[{cfg.name}] oracle done, union={len(ref['union_ids'])}; running GPU step")
-    got = run_layer(pool, x, wr, b, cfg.k)
+    say(f"[{cfg.name}] oracle done, union={len(ref['union_ids'])}; running GPU step "
+        f"(mfma_min_tokens={mfma_min_tokens})")
+    got = run_layer(pool, x, wr, b, cfg.k, mfma_min_tokens=mfma_min_tokens)
     check_routing(got, ref, spec.n_experts)
     err = check_y(got["y"], ref["y"])
     say(f"[{cfg.name}] parity ok, max rel err {err:.2e}")
@@ -131,6 +132,21 @@ def test_tiny_ragged_batches(N, k):
     """Token counts that leave partial work items and partial router tiles,
     k from 1 to E (k = E routes every token to every expert)."""
     pool, *_ = full_parity(tiny(n_tokens=N, k=k))
+
+
+@pytest.mark.parametrize("mfma_min_tokens", [1, -1])
+@pytest.mark.parametrize("N,k", [(7, 3), (64, 4), (200, 16)])
+def test_tiny_forced_paths(N, k, mfma_min_tokens):
+    """Every expert on the matrix-core kernels (threshold 1) or on the GEMV
+    kernels (negative threshold): both agree with the oracle; the batches give
+    partly filled 128-token tiles and multi-tile experts."""
+    full_parity(tiny(n_tokens=N, k=k), mfma_min_tokens=mfma_min_tokens)
+
+
+@pytest.mark.parametrize("mfma_min_tokens", [1, -1])
+def test_decode64_forced_paths(mfma_min_tokens):
+    full_parity(synth.CONFIGS["decode64"], mfma_min_tokens=mfma_min_tokens)
+    torch.cuda.empty_cache()
 
 
 def test_determinism_and_counter_accumulation():
