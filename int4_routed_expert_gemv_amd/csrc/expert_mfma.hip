@@ -20,7 +20,8 @@
 //  * within each 8-column group the columns are taken in the order
 //    0,4,1,5,2,6,3,7 on both operands, which lets one 32-bit word of codes
 //    feed one MFMA operand without shuffles;
-//  * each wave owns 32 rows and all 128 tokens (4 x 1 blocks of 32 x 32).
+//  * each of the 4 waves owns 32 rows and all 128 tokens (4 x 1 blocks of
+//    32 x 32); loads run two steps ahead of the matrix cores.
 // Workgroups are mapped so that those sharing an expert (and so its weights
 // and its tokens) land on the same XCD and share its L2.
 #include <hip/hip_ext.h>
@@ -37,7 +38,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kThreads = 256;
 constexpr int kMT = 128;            // tokens per tile
 constexpr int kNW = 32;             // rows per wave
-constexpr int kNT = 4 * kNW;        // rows per workgroup
+constexpr int kNT = (kThreads / 64) * kNW;  // rows per workgroup
 constexpr int kKB = 64;             // columns per step
 constexpr int kAStride = kKB + 8;   // LDS row stride (halves), padded
 constexpr int kXcds = 8;
@@ -65,11 +66,14 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t s2)
 struct MfmaArgs {
     Fwd f;
     int n_tiles;        // row tiles per item
-    int n_blocks;       // grid size
 };
 
+// One workgroup: one MFMA item (<= 128 tokens of one expert) x kNT rows;
+// each wave owns 32 rows and all 128 tokens. Loads run two 64-column steps
+// ahead of the matrix cores (registers), activations are double-buffered in
+// LDS.
 template <bool GATEUP>
-__global__ __launch_bounds__(kThreads, 2) void mfma_kernel(MfmaArgs ma)
+__global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
 {
     constexpr int NM = GATEUP ? 2 : 1;
     __shared__ _Float16 As[2][kMT][kAStride];
@@ -79,15 +83,19 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_kernel(MfmaArgs ma)
     const Geo &g = f.g;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
 
-    // XCD-aware order: workgroups are dealt to the XCDs round robin, so give
-    // each XCD a contiguous range of (item, row tile) pairs
+    // XCD-aware order over the items that exist: workgroups are dealt to the
+    // XCDs round robin, so give each XCD a contiguous range of (item, row
+    // tile) pairs; tiles of one item share its tokens, items of one expert
+    // are adjacent and share its weights
+    const int n_items = min(*f.n_mitems, f.max_mitems);
+    const int n_active = n_items * ma.n_tiles;
     const int b = blockIdx.x;
-    const int per_xcd = (ma.n_blocks + kXcds - 1) / kXcds;
-    const int logical = (b % kXcds) * per_xcd + b / kXcds;
-    if (logical >= ma.n_blocks) return;
+    if (b >= n_active) return;
+    const int q = n_active / kXcds, rem = n_active % kXcds;
+    const int xcd = b % kXcds, i = b / kXcds;
+    const int logical = xcd * q + min(xcd, rem) + i;
     const int item_idx = logical / ma.n_tiles;
     const int ntile = logical % ma.n_tiles;
-    if (item_idx >= *f.n_mitems) return;
     const Item it = f.mitems[item_idx];
     const int count = min(it.count, kMT);
     const uint8_t *blk = it.expert >= 0 ? f.pool + (size_t)it.expert * f.stride : f.shared;
@@ -110,23 +118,25 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_kernel(MfmaArgs ma)
     }
     __syncthreads();
 
-    // activation loads: thread -> (token row, half of the 64 columns)
-    const int a_row = tid / 2, a_half = tid % 2;
+    // activation loads: thread -> (token row, part of the 64 columns)
+    constexpr int kParts = kThreads / kMT;          // threads per token row
+    constexpr int kCols = kKB / kParts;             // columns per thread
+    constexpr int kVec = kCols / 4;                 // float4 per thread
+    const int a_row = tid / kParts, a_q = tid % kParts;
     const int a_src = s_src[a_row];
-    const float *a_ptr = a_src >= 0 ? in + (size_t)a_src * K + a_half * 32 : nullptr;
-    float4 av[8];
-    auto load_a = [&](int k0) {
+    const float *a_ptr = a_src >= 0 ? in + (size_t)a_src * K + a_q * kCols : nullptr;
+    auto load_a = [&](int k0, float4 (&av)[kVec]) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-            av[q] = a_ptr ? reinterpret_cast<const float4 *>(a_ptr + k0)[q]
+        for (int c = 0; c < kVec; ++c)
+            av[c] = a_ptr ? reinterpret_cast<const float4 *>(a_ptr + k0)[c]
                           : make_float4(0.f, 0.f, 0.f, 0.f);
     };
-    auto store_a = [&](int buf) {
-        // 32 columns = 4 groups of 8, each written in the order 0,4,1,5,2,6,3,7
+    auto store_a = [&](int buf, const float4 (&av)[kVec]) {
+        // groups of 8 columns, each written in the order 0,4,1,5,2,6,3,7
         const float *v = reinterpret_cast<const float *>(av);
-        _Float16 *dst = &As[buf][a_row][a_half * 32];
+        _Float16 *dst = &As[buf][a_row][a_q * kCols];
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
+        for (int gi = 0; gi < kCols / 8; ++gi) {
             half8_t h;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -154,9 +164,7 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_kernel(MfmaArgs ma)
         qb[0] = blk + g.off_dn + (long long)row_c * row_bytes;
         sb[0] = reinterpret_cast<const float *>(blk + g.off_ds) + (long long)row_c * spr;
     }
-    uint4 bw[NM];
-    float bs[NM];
-    auto load_b = [&](int k0) {
+    auto load_b = [&](int k0, uint4 (&bw)[NM], float (&bs)[NM]) {
         const int col = k0 + 32 * hh;
         const long long grp = g.group ? col / g.group : 0;
 #pragma unroll
@@ -174,30 +182,17 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_kernel(MfmaArgs ma)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[m][mf][r] = 0.0f;
 
-    const int steps = K / kKB;
-    load_a(0);
-    load_b(0);
-    store_a(0);
-    __syncthreads();
-    for (int ks = 0; ks < steps; ++ks) {
-        const int cur = ks & 1;
-        uint4 bw_c[NM];
+    // one 64-column step on LDS buffer `cur` and weights (bw, bs)
+    auto compute = [&](int cur, const uint4 (&bw)[NM], const float (&bs)[NM]) {
         half2_t s2[NM];
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            bw_c[m] = bw[m];
-            s2[m] = half2_t{(_Float16)bs[m], (_Float16)bs[m]};
-        }
-        if (ks + 1 < steps) {
-            load_a((ks + 1) * kKB);
-            load_b((ks + 1) * kKB);
-        }
+        for (int m = 0; m < NM; ++m) s2[m] = half2_t{(_Float16)bs[m], (_Float16)bs[m]};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             half8_t bf[NM];
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                const uint32_t w = s == 0 ? bw_c[m].x : (s == 1 ? bw_c[m].y : (s == 2 ? bw_c[m].z : bw_c[m].w));
+                const uint32_t w = s == 0 ? bw[m].x : (s == 1 ? bw[m].y : (s == 2 ? bw[m].z : bw[m].w));
                 bf[m] = dequant8(w, s2[m]);
             }
 #pragma unroll
@@ -209,8 +204,51 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_kernel(MfmaArgs ma)
                     acc[m][mf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[m], acc[m][mf], 0, 0, 0);
             }
         }
-        if (ks + 1 < steps) store_a(cur ^ 1);
-        __syncthreads();
+    };
+
+    const int steps = K / kKB;
+    // ring of two register stages: stage j holds step ks with ks % 2 == j
+    float4 av0[kVec], av1[kVec];
+    uint4 bw0[NM], bw1[NM];
+    float bs0[NM], bs1[NM];
+    load_a(0, av0);
+    load_b(0, bw0, bs0);
+    if (steps > 1) {
+        load_a(kKB, av1);
+        load_b(kKB, bw1, bs1);
+    }
+    store_a(0, av0);
+    __syncthreads();
+    for (int ks = 0; ks < steps; ks += 2) {
+        // even step ks: LDS buffer 0, weights in stage 0
+        {
+            uint4 bw[NM];
+            float bs[NM];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) { bw[m] = bw0[m]; bs[m] = bs0[m]; }
+            if (ks + 2 < steps) {
+                load_a((ks + 2) * kKB, av0);
+                load_b((ks + 2) * kKB, bw0, bs0);
+            }
+            compute(0, bw, bs);
+            if (ks + 1 < steps) store_a(1, av1);
+            __syncthreads();
+        }
+        if (ks + 1 >= steps) break;
+        // odd step ks + 1: LDS buffer 1, weights in stage 1
+        {
+            uint4 bw[NM];
+            float bs[NM];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) { bw[m] = bw1[m]; bs[m] = bs1[m]; }
+            if (ks + 3 < steps) {
+                load_a((ks + 3) * kKB, av1);
+                load_b((ks + 3) * kKB, bw1, bs1);
+            }
+            compute(1, bw, bs);
+            if (ks + 2 < steps) store_a(0, av0);
+            __syncthreads();
+        }
     }
 
     // epilogue: lane holds column `row` of four 32x32 blocks; register r of
@@ -252,20 +290,18 @@ hipError_t launch_mfma(const Fwd &f, bool gateup, hipStream_t s)
     const long long blocks = (long long)f.max_mitems * a.n_tiles;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    a.n_blocks = (int)blocks;
     const hipEvent_t *ev = gateup ? f.ev_mgu : f.ev_mdn;
+    const dim3 grid((unsigned)blocks);
     if (gateup) {
         if (ev[0] || ev[1])
-            hipExtLaunchKernelGGL(mfma_kernel<true>, dim3(a.n_blocks), dim3(kThreads), 0, s, ev[0],
-                                  ev[1], 0, a);
+            hipExtLaunchKernelGGL(mfma_kernel<true>, grid, dim3(kThreads), 0, s, ev[0], ev[1], 0, a);
         else
-            hipLaunchKernelGGL(mfma_kernel<true>, dim3(a.n_blocks), dim3(kThreads), 0, s, a);
+            hipLaunchKernelGGL(mfma_kernel<true>, grid, dim3(kThreads), 0, s, a);
     } else {
         if (ev[0] || ev[1])
-            hipExtLaunchKernelGGL(mfma_kernel<false>, dim3(a.n_blocks), dim3(kThreads), 0, s, ev[0],
-                                  ev[1], 0, a);
+            hipExtLaunchKernelGGL(mfma_kernel<false>, grid, dim3(kThreads), 0, s, ev[0], ev[1], 0, a);
         else
-            hipLaunchKernelGGL(mfma_kernel<false>, dim3(a.n_blocks), dim3(kThreads), 0, s, a);
+            hipLaunchKernelGGL(mfma_kernel<false>, grid, dim3(kThreads), 0, s, a);
     }
     return hipGetLastError();
 }
