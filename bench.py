@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s and expert-weight HBM GB/s (% of 8 TB/s peak) on 1 MI355X"
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0   # dense float16 matrix-core peak
 
 
 def parse():
@@ -84,8 +85,14 @@ def main():
     torch.cuda.set_device(dev)
     base = synth.CONFIGS[args.config]
     spec = base.layer
-    L_rot = args.layers
-    cfg = dataclasses.replace(base, layers=(spec,) * L_rot)
+    stack = len(base.layers) > 1
+    if stack:
+        # a step is one pass through the whole stack (layers chained on the GPU)
+        cfg = base
+        L_rot = len(cfg.layers)
+    else:
+        L_rot = args.layers
+        cfg = dataclasses.replace(base, layers=(spec,) * L_rot)
     N, k, E, d, f = cfg.n_tokens, cfg.k, spec.n_experts, spec.d, spec.f
     A = N * k
     nb = max(1, min(args.batches, args.steps + args.warmup))
@@ -94,9 +101,10 @@ def main():
     # --- inputs resident in HBM -------------------------------------------
     pools, routers = [], []
     for l in range(L_rot):
+        ls = cfg.layers[l]
         blocks = synth.expert_pool(cfg, l)
         shared = synth.shared_block(cfg, l)
-        pools.append(moe.DevicePool(d, f, E, spec.wbits, spec.group, blocks, shared, dev))
+        pools.append(moe.DevicePool(d, f, E, ls.wbits, ls.group, blocks, shared, dev))
         del blocks
         wr, b = synth.router(cfg, l)
         routers.append((torch.from_numpy(wr).to(dev), torch.from_numpy(b).to(dev)))
@@ -111,7 +119,9 @@ def main():
     perm = torch.empty(A, dtype=torch.int32, device=dev)
     counters = torch.zeros((L_rot, E), dtype=torch.int64, device=dev)
     y = torch.empty((N, d), dtype=torch.float32, device=dev)
-    ws_bytes = moe.workspace_size(pools[0].desc, N, k)
+    ws_bytes = max(moe.workspace_size(p.desc, N, k) for p in pools)
+    hbuf = torch.empty((N, d), dtype=torch.float32, device=dev)   # residual stream
+    abuf = torch.empty((N, d), dtype=torch.float32, device=dev)   # normalised layer input
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
@@ -123,7 +133,7 @@ def main():
 
     def step_args(s):
         l, bi = s % L_rot, s % nb
-        x = xs[bi]
+        x = abuf if stack else xs[bi]
         wr, b = routers[l]
         route = (vp(x.data_ptr()), N, d, vp(wr.data_ptr()), vp(b.data_ptr()), E, k,
                  vp(ids.data_ptr()), vp(w.data_ptr()), vp(ws.data_ptr()), ws_bytes, stream)
@@ -135,10 +145,12 @@ def main():
                vp(perm.data_ptr()), vp(y.data_ptr()), vp(ws.data_ptr()), ws_bytes, stream)
         return route, uni, hit, fwd
 
-    plans = [step_args(s) for s in range(L_rot * nb)]
+    plans = [step_args(s) for s in range(L_rot if stack else L_rot * nb)]
     n_plan = len(plans)
+    hip_rt = ctypes.CDLL("libamdhip64.so")
+    hip_rt.hipMemcpyAsync.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
 
-    def run(s, ev=None):
+    def run_layer(s, ev=None):
         route, uni, hit, fwd = plans[s % n_plan]
         rc = Lb.moe_route_topk(*route)
         rc |= Lb.moe_union(*uni)
@@ -150,16 +162,58 @@ def main():
         if rc:
             raise RuntimeError(f"layer step failed with status {rc}")
 
-    # union size of every (layer, batch) step: the experts a step streams
-    u_of = []
-    for s in range(n_plan):
-        run(s)
+    def run(s, ev=None):
+        if not stack:
+            run_layer(s, ev)
+            return
+        # h = x (device copy), then per layer: h += y (from layer 1 on),
+        # a = rms(h), layer(a) -> y
+        x = xs[s % nb]
+        rc = hip_rt.hipMemcpyAsync(vp(hbuf.data_ptr()), vp(x.data_ptr()), x.numel() * 4, 3, stream)
+        for l in range(L_rot):
+            rc |= Lb.moe_residual_rmsnorm(vp(hbuf.data_ptr()), vp(y.data_ptr()) if l else None,
+                                          vp(abuf.data_ptr()), N, d, ctypes.c_float(1e-6), stream)
+            if rc:
+                raise RuntimeError(f"stack step failed with status {rc}")
+            run_layer(l, ev if l == 0 else None)
+
+    # which experts each (layer, batch) step streams and on which kernels:
+    # experts with at least MFMA_MIN tokens (and the shared expert of a batch
+    # of that size) go to the matrix-core kernels, the others to the GEMVs
+    MFMA_MIN = 32
+    mfma_ok = spec.wbits == 4 and d % 64 == 0 and f % 64 == 0
+    calib = {}
+
+    def record(key, l):
         torch.cuda.synchronize()
-        u_of.append(int(n_union.item()))
+        nu = int(n_union.item())
+        uid = union_ids[:nu].cpu().numpy()
+        off = offsets.cpu().numpy()
+        T = off[uid + 1] - off[uid]
+        big = (T >= MFMA_MIN) if (mfma_ok and N >= MFMA_MIN) else np.zeros(nu, bool)
+        sh_big = bool(mfma_ok and N >= MFMA_MIN)
+        calib[key] = dict(union=nu, gemv_experts=int((~big).sum()) + (0 if sh_big else 1),
+                          mfma_experts=int(big.sum()) + (1 if sh_big else 0),
+                          mfma_tokens=int(T[big].sum()) + (N if sh_big else 0),
+                          wbits=cfg.layers[l].wbits, group=cfg.layers[l].group)
+
+    if stack:
+        x0 = xs[0]
+        hip_rt.hipMemcpyAsync(vp(hbuf.data_ptr()), vp(x0.data_ptr()), x0.numel() * 4, 3, stream)
+        for l in range(L_rot):
+            Lb.moe_residual_rmsnorm(vp(hbuf.data_ptr()), vp(y.data_ptr()) if l else None,
+                                    vp(abuf.data_ptr()), N, d, ctypes.c_float(1e-6), stream)
+            run_layer(l)
+            record(l, l)
+    else:
+        for s_ in range(n_plan):
+            run(s_)
+            record(s_, s_ % L_rot)
     for _ in range(args.warmup):
         run(_)
     torch.cuda.synchronize()
-    print(f"[bench] setup {time.time() - t_setup:.1f}s; mean union {np.mean(u_of):.1f}",
+    mean_union = float(np.mean([c["union"] for c in calib.values()]))
+    print(f"[bench] setup {time.time() - t_setup:.1f}s; mean union {mean_union:.1f}",
           file=sys.stderr, flush=True)
 
     # --- timed region -------------------------------------------------------
@@ -167,37 +221,90 @@ def main():
     evs = [moe.ForwardOptions(*[hip.event() for _ in range(8)], 0) for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(K):
-        run(args.warmup + s, evs[s])
+    for s_ in range(K):
+        run(args.warmup + s_, evs[s_])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
 
-    gu_ms = [hip.elapsed_ms(e.gateup_start, e.gateup_end) for e in evs]
-    dn_ms = [hip.elapsed_ms(e.down_start, e.down_end) for e in evs]
+    def ms(e, a, b):
+        try:
+            return hip.elapsed_ms(getattr(e, a), getattr(e, b))
+        except AssertionError:  # the kernel was not launched in that step
+            return None
+
+    gu = [ms(e, "gateup_start", "gateup_end") for e in evs]
+    dn = [ms(e, "down_start", "down_end") for e in evs]
+    mgu = [ms(e, "mfma_gateup_start", "mfma_gateup_end") for e in evs]
+    mdn = [ms(e, "mfma_down_start", "mfma_down_end") for e in evs]
     for e in evs:
         for h in (e.gateup_start, e.gateup_end, e.down_start, e.down_end, e.mfma_gateup_start,
                   e.mfma_gateup_end, e.mfma_down_start, e.mfma_down_end):
             hip.L.hipEventDestroy(h)
 
-    # --- algorithmic bytes ---------------------------------------------------
-    bb = moe.block_bytes(d, f, spec.wbits, spec.group)
-    q_gu = f * d * spec.wbits // 8
-    s_gu = f * (d // spec.group if spec.group else 1) * 4
-    gu_bytes_per_expert = 2 * (q_gu + s_gu)          # gate + up codes and scales
-    dn_bytes_per_expert = bb - gu_bytes_per_expert
-    steps_u = [u_of[(args.warmup + s) % n_plan] for s in range(K)]
-    n_exp = [u + 1 for u in steps_u]                 # union + shared expert
-    gu_bytes = [n * gu_bytes_per_expert for n in n_exp]
-    expert_bytes = sum(n * bb for n in n_exp)
-    router_bytes = E * d * 4 + E * 4
-    gu_avg_ms = float(np.mean(gu_ms))
-    gu_achieved = (float(np.mean(gu_bytes)) / 1e9) / (gu_avg_ms / 1e3)
-    dn_avg_ms = float(np.mean(dn_ms))
-    dn_achieved = (float(np.mean([n * dn_bytes_per_expert for n in n_exp])) / 1e9) / (dn_avg_ms / 1e3)
+    # --- algorithmic bytes and flops ------------------------------------------
+    def sizes(c):
+        bb = moe.block_bytes(d, f, c["wbits"], c["group"])
+        q_gu = f * d * c["wbits"] // 8
+        s_gu = f * (d // c["group"] if c["group"] else 1) * 4
+        return bb, 2 * (q_gu + s_gu)
+
+    # the calibration entry of the (first) layer the events of a step cover
+    step_key = [0 if stack else (args.warmup + s_) % n_plan for s_ in range(K)]
+    layer_keys = list(range(L_rot)) if stack else None
+    expert_bytes = 0
+    router_bytes = 0
+    for s_ in range(K):
+        keys = layer_keys if stack else [step_key[s_]]
+        for key in keys:
+            c = calib[key]
+            bb, _ = sizes(c)
+            expert_bytes += (c["union"] + 1) * bb
+            router_bytes += E * d * 4 + E * 4
     ms_per_step = elapsed / K * 1e3
     tokens_per_s = N * K / elapsed
     expert_gbs = expert_bytes / 1e9 / elapsed
+
+    def avg(v):
+        v = [x for x in v if x is not None]
+        return float(np.mean(v)) if v else None
+
+    # GEMV gate/up: HBM-bound, algorithmic bytes = codes + scales of the
+    # gate and up matrices of every expert it handles, once
+    gu_bytes = [c["gemv_experts"] * sizes(c)[1] for c in (calib[k_] for k_ in step_key)]
+    dn_bytes = [c["gemv_experts"] * (sizes(c)[0] - sizes(c)[1])
+                for c in (calib[k_] for k_ in step_key)]
+    gemv = {"avg_launch_us": None, "achieved_GBps": None}
+    if avg(gu):
+        gemv = {"avg_launch_us": avg(gu) * 1e3,
+                "achieved_GBps": float(np.mean(gu_bytes)) / 1e9 / (avg(gu) / 1e3),
+                "bytes_per_launch": float(np.mean(gu_bytes)),
+                "down_avg_launch_us": avg(dn) * 1e3 if avg(dn) else None,
+                "down_GBps": float(np.mean(dn_bytes)) / 1e9 / (avg(dn) / 1e3) if avg(dn) else None}
+    # MFMA gate/up: matrix-core bound, algorithmic flops = 2 (gate, up) x
+    # 2 x d x f per token it handles
+    mflops = [4.0 * d * f * c["mfma_tokens"] for c in (calib[k_] for k_ in step_key)]
+    mfma = None
+    if avg(mgu):
+        mfma = {"avg_launch_us": avg(mgu) * 1e3,
+                "achieved_TFLOPs": float(np.mean(mflops)) / 1e12 / (avg(mgu) / 1e3),
+                "flops_per_launch": float(np.mean(mflops)),
+                "down_avg_launch_us": avg(mdn) * 1e3 if avg(mdn) else None}
+    if mfma and (gemv["avg_launch_us"] is None or mfma["avg_launch_us"] > gemv["avg_launch_us"]):
+        roof = {"kernel": "mfma_kernel<gate/up> (grouped GEMM of gate and up, SiLU product)",
+                "bound": "mfma", "achieved": mfma["achieved_TFLOPs"], "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": mfma["achieved_TFLOPs"] / MFMA_F16_PEAK_TFLOPS,
+                "traffic": None, "avg_launch_us": mfma["avg_launch_us"],
+                "flops_per_launch": mfma["flops_per_launch"], "gemv": gemv}
+    else:
+        roof = {"kernel": "gemv_kernel<gate/up> (expert gate and up projections, SiLU product)",
+                "bound": "hbm", "achieved": gemv["achieved_GBps"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s",
+                "frac": gemv["achieved_GBps"] / HBM_PEAK_GBS if gemv["achieved_GBps"] else None,
+                "traffic": None, "avg_launch_us": gemv["avg_launch_us"],
+                "bytes_per_launch": gemv.get("bytes_per_launch"),
+                "down_avg_launch_us": gemv.get("down_avg_launch_us"),
+                "down_GBps": gemv.get("down_GBps"), "mfma": mfma}
 
     result = {
         "metric": METRIC,
@@ -210,30 +317,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4xf16->f32",
+        "dtype": "int4xf16->f32" if spec.wbits == 4 else "int8xf16->f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{cfg.name}: {base.description}; {L_rot} layer pools rotated",
+            "workload": (f"{cfg.name}: {base.description}" +
+                         ("" if stack else f"; {L_rot} layer pools rotated")),
             "n_tokens": N, "k": k, "d_model": d, "d_ff": f, "n_experts": E,
-            "wbits": spec.wbits, "group": spec.group, "layer_pools": L_rot,
-            "mean_union": float(np.mean(steps_u)),
+            "wbits": spec.wbits, "group": spec.group, "layers_per_step": L_rot if stack else 1,
+            "layer_pools": L_rot, "mean_union": mean_union,
         },
         "expert_GBps": expert_gbs,
         "expert_frac_of_peak": expert_gbs / HBM_PEAK_GBS,
-        "step_GBps": (expert_bytes + K * router_bytes) / 1e9 / elapsed,
-        "roofline": {
-            "kernel": "gemv_kernel<gate/up> (expert gate and up projections, SiLU product)",
-            "bound": "hbm",
-            "achieved": gu_achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": gu_achieved / HBM_PEAK_GBS,
-            "traffic": None,
-            "avg_launch_us": gu_avg_ms * 1e3,
-            "bytes_per_launch": float(np.mean(gu_bytes)),
-            "down_kernel_GBps": dn_achieved,
-            "down_avg_launch_us": dn_avg_ms * 1e3,
-        },
+        "step_GBps": (expert_bytes + router_bytes) / 1e9 / elapsed,
+        "roofline": roof,
         "cpu_baseline": None,
     }
 
@@ -262,9 +358,13 @@ def cpu_baseline(cfg, spec, args, xs_host):
         if time.perf_counter() - t0 >= args.cpu_seconds:
             break
     el = time.perf_counter() - t0
-    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    n_layers = len(cfg.layers) if len(set(cfg.layers)) > 1 else 1
+    # a stack step runs every layer: scale the first layer's rate to the stack
+    return {"value": tokens / el / n_layers, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{n_steps} steps ({tokens} tokens) of the {cfg.name} layer step on the "
-                      f"first layer pool, {el:.1f}s, float64 oracle with OpenMP"}
+                      f"first layer pool, {el:.1f}s, float64 oracle with OpenMP"
+                      + (f"; rate divided by the {n_layers} layers of a stack step"
+                         if n_layers > 1 else "")}
 
 
 if __name__ == "__main__":

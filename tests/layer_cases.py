@@ -61,3 +61,36 @@ def rel_err_rows(y, ref):
     num = np.abs(y - ref).max(axis=1)
     den = np.abs(ref).max(axis=1)
     return num / np.maximum(den, 1e-30)
+
+
+# ---------------------------------------------------------------- layer stacks
+
+RMS_EPS = 1e-6
+
+
+def stack_chain(cfg: synth.Config, attempts, tokens=None, on_layer=None):
+    """Oracle pass through a stack of layers with residual chaining:
+    h_0 = x, a_l = h_l / sqrt(mean(h_l^2) + eps), y_l = layer_l(a_l),
+    h_{l+1} = h_l + y_l. Each layer's pool is drawn, used and dropped in turn.
+
+    tokens: indices of the tokens to run (default: all). on_layer(l, spec,
+    a_l, ref, blocks, shared, wr, b) is called after the oracle of layer l,
+    with the canonical blocks still intact. Returns the indices (within
+    `tokens`) of tokens with a top-(k+1) gap below GAP at some layer."""
+    N = cfg.n_tokens
+    tokens = np.arange(N) if tokens is None else np.asarray(tokens)
+    x = synth.tokens(cfg, attempts)[tokens]
+    h = x.astype(np.float64)
+    flagged = set()
+    for l, spec in enumerate(cfg.layers):
+        a = oracle.rms_normalize(h, RMS_EPS)
+        wr, b = synth.router(cfg, l)
+        blocks, shared = canonical_pool(cfg, l)
+        ref = oracle.layer_step(a, wr, b, cfg.k, blocks, shared, spec.d, spec.f, spec.wbits,
+                                spec.group)
+        flagged.update(small_gap_tokens(ref["scores"], cfg.k).tolist())
+        if on_layer is not None:
+            on_layer(l, spec, a, ref, blocks, shared, wr, b)
+        del blocks
+        h = h + ref["y"]
+    return sorted(flagged)
