@@ -43,7 +43,46 @@ def parse():
     p.add_argument("--batches", type=int, default=16, help="distinct token batches rotated")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run one plain device copy of 1 GiB (to scale HBM counters)")
     return p.parse_args()
+
+
+def copy_calibration():
+    """One plain device-to-device copy kernel of exactly 1 GiB read + 1 GiB
+    written, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = (1 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": 4 * n}), flush=True)
+
+
+def kernel_source_hash():
+    """Hash of the expert kernel sources (counters are only valid for them)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("expert_gemv.hip", "expert_mfma.hip", "internal.h"):
+        with open(os.path.join(ROOT, "int4_routed_expert_gemv_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config, kernel):
+    """HBM bytes per launch of `kernel` on `config` from the committed counter
+    summary, or None when there is none or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        data = json.load(fh)
+    entry = data.get(config, {}).get(kernel)
+    if not entry or entry.get("source_hash") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
 
 
 class Hip:
@@ -69,6 +108,9 @@ class Hip:
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -294,14 +336,14 @@ def main():
         roof = {"kernel": "mfma_kernel<gate/up> (grouped GEMM of gate and up, SiLU product)",
                 "bound": "mfma", "achieved": mfma["achieved_TFLOPs"], "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": mfma["achieved_TFLOPs"] / MFMA_F16_PEAK_TFLOPS,
-                "traffic": None, "avg_launch_us": mfma["avg_launch_us"],
+                "traffic": measured_traffic(args.config, "moe::mfma_kernel<true"), "avg_launch_us": mfma["avg_launch_us"],
                 "flops_per_launch": mfma["flops_per_launch"], "gemv": gemv}
     else:
         roof = {"kernel": "gemv_kernel<gate/up> (expert gate and up projections, SiLU product)",
                 "bound": "hbm", "achieved": gemv["achieved_GBps"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s",
                 "frac": gemv["achieved_GBps"] / HBM_PEAK_GBS if gemv["achieved_GBps"] else None,
-                "traffic": None, "avg_launch_us": gemv["avg_launch_us"],
+                "traffic": measured_traffic(args.config, "moe::gemv_kernel<true"), "avg_launch_us": gemv["avg_launch_us"],
                 "bytes_per_launch": gemv.get("bytes_per_launch"),
                 "down_avg_launch_us": gemv.get("down_avg_launch_us"),
                 "down_GBps": gemv.get("down_GBps"), "mfma": mfma}

@@ -54,7 +54,10 @@ struct FwdLayout {
     long long items, n_items, mitems, n_mitems, h, o, total;
 };
 
-FwdLayout fwd_layout(const Geo &g, int N, int k, int has_shared, int mfma_min_tokens)
+// upper = true: the largest layout any value of mfma_min_tokens can select
+// (each list at its own largest), for sizing the workspace
+FwdLayout fwd_layout(const Geo &g, int N, int k, int has_shared, int mfma_min_tokens,
+                     bool upper = false)
 {
     FwdLayout L;
     const long long A = (long long)N * k;
@@ -64,11 +67,17 @@ FwdLayout fwd_layout(const Geo &g, int N, int k, int has_shared, int mfma_min_to
     L.max_items = (int)((A + L.tb - 1) / L.tb + ue + (has_shared ? (N + L.tb - 1) / L.tb : 0));
     // the MFMA pass runs when some expert can reach the threshold (an expert
     // has at most N tokens)
-    L.tstar = mfma_min_tokens > 0 ? mfma_min_tokens : kDefaultMfmaMinTokens;
-    const bool mfma = mfma_min_tokens >= 0 && mfma_supported(g) && N >= L.tstar;
+    L.tstar = upper ? 1 : (mfma_min_tokens > 0 ? mfma_min_tokens : kDefaultMfmaMinTokens);
+    const bool mfma = (upper || mfma_min_tokens >= 0) && mfma_supported(g) && N >= L.tstar;
     const long long mt = mfma_tokens_per_item();
     L.max_mitems = mfma ? (int)((A + mt - 1) / mt + A / L.tstar + (has_shared ? (N + mt - 1) / mt : 0))
                         : 0;
+    if (mfma && !upper) {
+        // with the MFMA pass on, the GEMV list holds only experts with fewer
+        // than tstar tokens (the shared expert, with N >= tstar, is not one)
+        const long long per = (L.tstar - 1 + L.tb - 1) / L.tb;
+        if (ue * per < L.max_items) L.max_items = (int)(ue * per);
+    }
     L.P = (int)(A + (has_shared ? N : 0));
     long long off = 0;
     L.items = off; off = align_up(off + (long long)L.max_items * (long long)sizeof(Item));
@@ -147,10 +156,7 @@ size_t moe_forward_workspace_size(const moe_expert_pool *pool, int n_tokens, int
 {
     Geo g;
     if (resolve_geo(pool, &g) != MOE_OK || n_tokens < 0 || k < 1) return 0;
-    // the largest of the layouts any option can select
-    const size_t a = (size_t)fwd_layout(g, n_tokens, k, pool->shared != nullptr, 1).total;
-    const size_t b = (size_t)fwd_layout(g, n_tokens, k, pool->shared != nullptr, -1).total;
-    return a > b ? a : b;
+    return (size_t)fwd_layout(g, n_tokens, k, pool->shared != nullptr, 0, true).total;
 }
 
 size_t moe_workspace_size(const moe_expert_pool *pool, int n_tokens, int k)

@@ -89,13 +89,13 @@ __device__ __forceinline__ uint32_t pack2(__fp16 lo, __fp16 hi)
 // Stage one chunk of activations (already scaled) for the dot product and
 // return the correction 1032*sum(A) + 1152*sum(B) (int4) or 1152*sum (int8).
 template <int WB>
-__device__ __forceinline__ float stage_chunk(const float *src, float scale, uint32_t *xs)
+__device__ __forceinline__ float stage_chunk(const float4 *src, float scale, uint32_t *xs)
 {
     constexpr int epc = Fmt<WB>::epc;
     float v[epc];
 #pragma unroll
     for (int q = 0; q < epc / 4; ++q) {
-        float4 f4 = reinterpret_cast<const float4 *>(src)[q];
+        const float4 f4 = src[q];
         v[4 * q + 0] = f4.x * scale;
         v[4 * q + 1] = f4.y * scale;
         v[4 * q + 2] = f4.z * scale;
@@ -134,8 +134,12 @@ __device__ __forceinline__ float stage_chunk(const float *src, float scale, uint
 constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / kWave;
 
-// staged activations per token per row chunk: XDW dwords + one correction
-__host__ __device__ constexpr int stage_bytes(int wb) { return (wb == 4 ? 16 : 8) * 4 + 4; }
+// staged activations per token per row chunk: XDW dwords, the correction and
+// the chunk's inverse scale
+__host__ __device__ constexpr int stage_bytes(int wb) { return (wb == 4 ? 16 : 8) * 4 + 8; }
+
+// rounds of (token, chunk) activation pairs loaded before the weight loads
+constexpr int kPreRounds = 2;
 
 // rows per wave per row block
 __host__ __device__ constexpr int rows_of(bool gateup, int cpl)
@@ -193,7 +197,8 @@ struct GemvArgs {
     Fwd f;
     int n_rbg;              // workgroups per item
     int iters;              // row blocks per workgroup
-    int plan_here;          // gate/up pass: find the item in-kernel (union of <= 64)
+    int plan_here;          // gate/up pass: 0 read the work list, 1 scan a union of
+                            // <= 64 in-kernel, 2 one item per union slot (n_tokens <= TB)
 };
 
 // Finds work item `item_idx` of the current call when the union has at most
@@ -271,17 +276,41 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs ga)
     static_assert(CPL == 1 || LPR == kWave, "multi-chunk lanes need full-wave rows");
 
     extern __shared__ uint4 lds_x[];          // [TB][XQ][NCH] staged activations
-    float *lds_corr = reinterpret_cast<float *>(lds_x + TB * XQ * NCH);  // [TB][NCH]
-    __shared__ float smax[TB][kGemvWaves];
-    __shared__ float sinv[TB];
+    float2 *lds_ci = reinterpret_cast<float2 *>(lds_x + TB * XQ * NCH);  // [TB][NCH]
     __shared__ Item s_item;
+    __shared__ int s_expert;
 
     const Fwd &f = ga.f;
     const Geo &g = f.g;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int item_idx = blockIdx.x / ga.n_rbg;
     const int rbg = blockIdx.x % ga.n_rbg;
-    if (GATEUP && ga.plan_here) {
+    // The expert is needed first (the weight loads only depend on it); the
+    // item's tokens are resolved after those loads are issued when possible.
+    int expert;
+    Item it;
+    bool resolved = true;
+    if (GATEUP && ga.plan_here == 2) {
+        // every expert has at most n_tokens <= TB tokens: one item per union
+        // slot, after the shared expert's single item
+        const int nsh = f.has_shared ? 1 : 0;
+        resolved = false;
+        if (item_idx < nsh) {
+            expert = -1;
+        } else {
+            if (tid == 0) {
+                const int rel = item_idx - nsh;
+                const int lim = min(g.E, f.A);
+                const int nu = min(max(*f.n_union, 0), lim);   // both loads in flight together
+                const int e = rel < lim ? f.union_ids[rel] : -1;
+                s_expert = (rel < nu && e >= 0 && e < g.E) ? e : -2;
+                if (rbg == 0 && rel == 0) *f.n_items = nsh + nu;
+            }
+            __syncthreads();
+            expert = s_expert;
+            if (expert == -2) return;  // beyond the union: uniform exit
+        }
+    } else if (GATEUP && ga.plan_here == 1) {
         if (wave == 0) {
             const int total = find_item<TB>(f, item_idx, &s_item);
             if (lane == 0) {
@@ -292,15 +321,17 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs ga)
             }
         }
         __syncthreads();
-        if (s_item.count <= 0) return;  // beyond the last item: uniform exit
+        it = s_item;
+        expert = it.expert;
     } else {
         if (item_idx >= *f.n_items) return;  // uniform over the workgroup
         if (tid == 0) s_item = f.items[item_idx];
         __syncthreads();
+        it = s_item;
+        expert = it.expert;
     }
-    const Item it = s_item;
-    const int count = min(it.count, TB);
-    const uint8_t *blk = it.expert >= 0 ? f.pool + (size_t)it.expert * f.stride : f.shared;
+    if (resolved && it.count <= 0) return;  // no such item: uniform exit
+    const uint8_t *blk = expert >= 0 ? f.pool + (size_t)expert * f.stride : f.shared;
     const int seg = lane / LPR, li = lane % LPR;
     const int cols = GATEUP ? g.d : g.f;
     const int rows = GATEUP ? g.f : g.d;
@@ -332,64 +363,115 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs ga)
             }
         }
     };
-    const int first_blk = rbg * ga.iters;
-    load_block(first_blk, w, sc);  // weights do not depend on the tokens: issue first
-
-    // ---- stage the item's activations in LDS, one token at a time ------------
-    auto token_row = [&](int i) -> const float * {
-        const int p = it.p0 + i;
-        if (GATEUP) {
-            // values read from the permutation are clamped into range, so
-            // inconsistent caller buffers cannot move an access out of bounds
-            const int t = it.expert >= 0 ? min(max(f.perm[p], 0), f.A - 1) / f.k : p - f.A;
-            return in + (size_t)t * cols;
-        }
-        return in + (size_t)p * cols;
-    };
-#pragma unroll 1
-    for (int i = 0; i < count; ++i) {
-        const float *row = token_row(i);
-        float m = 0.0f;
-        for (int c = tid; c < NCH; c += kGemvThreads) {
-            const float4 *s4 = reinterpret_cast<const float4 *>(row + (size_t)c * EPC);
-#pragma unroll
-            for (int q = 0; q < EPC / 4; ++q) {
-                const float4 f4 = s4[q];
-                m = fmaxf(m, fmaxf(fmaxf(fabsf(f4.x), fabsf(f4.y)), fmaxf(fabsf(f4.z), fabsf(f4.w))));
+    // ---- the item's tokens -----------------------------------------------------
+    if (!resolved) {
+        if (expert < 0) {
+            it.expert = -1;
+            it.p0 = f.A;
+            it.count = f.N;
+            it.pad = 0;
+        } else if (f.N == 1) {
+            // one token: every union expert holds one assignment, at the
+            // permutation position equal to its union slot
+            it.expert = expert;
+            it.p0 = item_idx - (f.has_shared ? 1 : 0);
+            it.count = 1;
+            it.pad = 0;
+        } else {
+            if (tid == 0) {
+                const int s0 = min(max(f.offsets[expert], 0), f.A);
+                Item r;
+                r.expert = expert;
+                r.p0 = s0;
+                r.count = min(max(f.offsets[expert + 1], s0), f.A) - s0;
+                r.pad = 0;
+                s_item = r;
             }
+            __syncthreads();
+            it = s_item;
         }
-        m = wave_max_dpp(m);
-        if (lane == 0) smax[i][wave] = m;
+        if (rbg == 0 && tid == 0 && it.count > 0) f.items[item_idx] = it;
+        if (it.count <= 0) return;  // uniform: inconsistent offsets give no tokens
     }
-    __syncthreads();
-#pragma unroll 1
-    for (int i = 0; i < count; ++i) {
-        const float *row = token_row(i);
-        const float m = fmaxf(fmaxf(smax[i][0], smax[i][1]), fmaxf(smax[i][2], smax[i][3]));
+    const int count = min(it.count, TB);
+
+    // ---- stage the activations: loads first, then the weights ----------------
+    // (token, chunk) pairs are spread over the threads; a round covers one
+    // pair per thread. Each pair is staged on its own: float16 scaled by the
+    // power of two that brings the chunk's largest magnitude into
+    // [2^13, 2^14) (exact, undone per chunk with the group scale). The first
+    // rounds are loaded before the weight loads are issued, so their data do
+    // not wait behind the weights.
+    constexpr int NPAIR = TB * NCH;
+    constexpr int ROUNDS = (NPAIR + kGemvThreads - 1) / kGemvThreads;
+    constexpr int PRE = ROUNDS < kPreRounds ? ROUNDS : kPreRounds;
+    auto pair_src = [&](int q) -> const float * {
+        const int i = q / NCH, c = q % NCH;
+        if (i >= count) return nullptr;
+        const int p = it.p0 + i;
+        size_t r;
+        if (!GATEUP)
+            r = (size_t)p;
+        else if (it.expert < 0)
+            r = (size_t)(p - f.A);
+        else  // values read from the permutation are clamped into range
+            r = f.N == 1 ? 0 : (size_t)(min(max(f.perm[p], 0), f.A - 1) / f.k);
+        return in + r * cols + (size_t)c * EPC;
+    };
+    float4 xv[PRE][EPC / 4];
+#pragma unroll
+    for (int r = 0; r < PRE; ++r) {
+        const int q = tid + r * kGemvThreads;
+        const float *src = q < NPAIR ? pair_src(q) : nullptr;
+        if (src) {
+#pragma unroll
+            for (int v = 0; v < EPC / 4; ++v) xv[r][v] = reinterpret_cast<const float4 *>(src)[v];
+        }
+    }
+    const int first_blk = rbg * ga.iters;
+    load_block(first_blk, w, sc);
+    auto stage_pair = [&](int q, const float4 (&v)[EPC / 4]) {
+        const int i = q / NCH, c = q % NCH;
+        float m = 0.0f;
+#pragma unroll
+        for (int u = 0; u < EPC / 4; ++u)
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)),
+                               fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
         int sh = 0;
         if (m > 0.0f && m <= 3.4e38f) {
             int ex;
             frexpf(m, &ex);
             sh = min(126, max(-126, 14 - ex));
         }
-        const float scale = ldexpf(1.0f, sh);
-        if (tid == 0) sinv[i] = ldexpf(1.0f, -sh);
-        for (int c = tid; c < NCH; c += kGemvThreads) {
-            uint32_t xs[XDW];
-            lds_corr[i * NCH + c] = stage_chunk<WB>(row + (size_t)c * EPC, scale, xs);
+        uint32_t xs[XDW];
+        const float corr = stage_chunk<WB>(v, ldexpf(1.0f, sh), xs);
+        lds_ci[i * NCH + c] = make_float2(corr, ldexpf(1.0f, -sh));
 #pragma unroll
-            for (int q = 0; q < XQ; ++q)
-                lds_x[(i * XQ + q) * NCH + c] =
-                    make_uint4(xs[4 * q], xs[4 * q + 1], xs[4 * q + 2], xs[4 * q + 3]);
+        for (int u = 0; u < XQ; ++u)
+            lds_x[(i * XQ + u) * NCH + c] = make_uint4(xs[4 * u], xs[4 * u + 1], xs[4 * u + 2],
+                                                       xs[4 * u + 3]);
+    };
+#pragma unroll
+    for (int r = 0; r < PRE; ++r) {
+        const int q = tid + r * kGemvThreads;
+        if (q < NPAIR && q / NCH < count) stage_pair(q, xv[r]);
+    }
+#pragma unroll 1
+    for (int r = PRE; r < ROUNDS; ++r) {
+        const int q = tid + r * kGemvThreads;
+        const float *src = q < NPAIR ? pair_src(q) : nullptr;
+        if (src) {
+            float4 v[EPC / 4];
+#pragma unroll
+            for (int u = 0; u < EPC / 4; ++u) v[u] = reinterpret_cast<const float4 *>(src)[u];
+            stage_pair(q, v);
         }
     }
     __syncthreads();
-    float inv[TB];
     int orow[TB];
 #pragma unroll
     for (int i = 0; i < TB; ++i) {
         const int p = it.p0 + min(i, count - 1);
-        inv[i] = sinv[min(i, count - 1)];
         orow[i] = (!GATEUP && it.expert >= 0) ? min(max(f.perm[p], 0), f.A - 1) : p;
     }
 
@@ -410,7 +492,6 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs ga)
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int c = li + j * LPR;
-            // codes -> float16 once per chunk, then used for every token
             uint32_t hw[R][NM][XDW];
 #pragma unroll
             for (int r = 0; r < R; ++r)
@@ -428,13 +509,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs ga)
                     xs[4 * q + 2] = v.z;
                     xs[4 * q + 3] = v.w;
                 }
-                const float corr = lds_corr[i * NCH + c];
+                const float2 ci = lds_ci[i * NCH + c];
 #pragma unroll
                 for (int r = 0; r < R; ++r)
 #pragma unroll
                     for (int m = 0; m < NM; ++m)
-                        acc[r][i][m] = fmaf(sc[r][j][m], dot_halves<XDW>(hw[r][m], xs) - corr,
-                                            acc[r][i][m]);
+                        acc[r][i][m] = fmaf(sc[r][j][m] * ci.y,
+                                            dot_halves<XDW>(hw[r][m], xs) - ci.x, acc[r][i][m]);
             }
         }
 #pragma unroll
@@ -449,10 +530,10 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs ga)
                 if (li == 0 && row < rows) {
                     float o;
                     if (GATEUP) {
-                        const float gv = v[0] * inv[i], uv = v[NM - 1] * inv[i];
+                        const float gv = v[0], uv = v[NM - 1];
                         o = gv / (1.0f + expf(-gv)) * uv;
                     } else {
-                        o = v[0] * inv[i];
+                        o = v[0];
                     }
                     out[(size_t)orow[i] * rows + row] = o;
                 }
@@ -470,7 +551,6 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs ga)
                     }
         }
     }
-
 }
 
 // ---- work list for larger unions ---------------------------------------------
@@ -729,7 +809,7 @@ hipError_t launch_gateup(const Fwd &f, hipStream_t s)
     // expert goes to the MFMA pass; otherwise one planning workgroup builds
     // both work lists first
     const int max_union = f.A < f.g.E ? f.A : f.g.E;
-    a.plan_here = max_union <= kWave && f.max_mitems == 0;
+    a.plan_here = max_union <= kWave && f.max_mitems == 0 ? (f.N <= f.tb ? 2 : 1) : 0;
     if (!a.plan_here) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, f);
         const hipError_t e = hipGetLastError();

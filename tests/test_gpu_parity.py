@@ -197,3 +197,12 @@ def test_zero_tokens_is_a_no_op():
     pool = upload_pool(spec, blocks, shared)
     r = run_layer(pool, x[:0], wr, b, 1)
     assert r["y"].shape == (0, spec.d) and r["counters"].sum() == 0
+
+
+@pytest.mark.parametrize("mfma_min_tokens", [None, 1, 2, 7, 33, -1])
+@pytest.mark.parametrize("N,k", [(40, 8), (100, 3), (129, 16)])
+def test_workspace_size_covers_every_threshold(N, k, mfma_min_tokens):
+    """The workspace is sized once per (pool, N, k) and must hold the work
+    lists of every MFMA threshold a call can choose; run_layer allocates
+    exactly moe_workspace_size bytes."""
+    full_parity(tiny(n_tokens=N, k=min(k, 16)), mfma_min_tokens=mfma_min_tokens)
