@@ -62,12 +62,17 @@ def copy_calibration():
 
 
 def kernel_source_hash():
-    """Hash of the expert kernel sources (counters are only valid for them)."""
+    """Hash of the expert kernel sources with comments and blank space taken
+    out (counters taken with other kernel code do not apply)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for name in ("expert_gemv.hip", "expert_mfma.hip", "internal.h"):
-        with open(os.path.join(ROOT, "int4_routed_expert_gemv_amd", "csrc", name), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "int4_routed_expert_gemv_amd", "csrc", name)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -38,10 +38,13 @@
  *     synchronisation. After an error the outputs are unspecified.
  *   - n_tokens == 0 is a successful no-op.
  *   - Row-major layouts throughout. x is [n_tokens][d_model] float32.
- *   - The activations are staged through float16 inside the expert kernels
- *     with a per-token power-of-two scale: inputs must be finite and every
- *     hidden value |silu(g) * u| (times its token's scale) must stay below
- *     65504, which holds with a wide margin for normalised activations.
+ *   - The activations are staged through float16 inside the expert kernels.
+ *     The GEMV kernels first scale each run of 32 (int4) or 16 (int8)
+ *     consecutive values by the power of two that brings its largest
+ *     magnitude into [2^13, 2^14); the matrix-core kernels convert x and the
+ *     hidden values without scaling. Inputs must be finite, and |x| and every
+ *     hidden value |silu(g) * u| must stay below 65504, which holds with a
+ *     wide margin for normalised activations.
  */
 #ifndef MOE_H
 #define MOE_H

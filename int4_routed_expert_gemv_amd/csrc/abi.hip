@@ -65,6 +65,8 @@ FwdLayout fwd_layout(const Geo &g, int N, int k, int has_shared, int mfma_min_to
     // each union expert adds at most one partly filled item
     const long long ue = A < g.E ? A : g.E;
     L.max_items = (int)((A + L.tb - 1) / L.tb + ue + (has_shared ? (N + L.tb - 1) / L.tb : 0));
+    // no expert has more than N tokens: with N <= tb every expert is one item
+    if (N <= L.tb) L.max_items = (int)(ue + (has_shared ? 1 : 0));
     // the MFMA pass runs when some expert can reach the threshold (an expert
     // has at most N tokens)
     L.tstar = upper ? 1 : (mfma_min_tokens > 0 ? mfma_min_tokens : kDefaultMfmaMinTokens);

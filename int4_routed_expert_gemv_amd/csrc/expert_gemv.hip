@@ -20,12 +20,12 @@
 //    exactly) and multiplied with float16 activations by v_dot2_f32_f16,
 //    which accumulates in float32; 1032 (or 1152) times the activation sum
 //    is taken off once per chunk;
-//  * each token's activations are staged once per wave in registers, as
-//    float16 scaled by a power of two that brings the token's largest value
-//    into [2^13, 2^14) (an exact scaling, undone on the output);
-//  * the group scale multiplies each chunk's float32 partial sum;
-//  * partial sums of a row are added across its lanes with shuffles and
-//    across the waves of a split row in LDS, always in the same order.
+//  * a work item's activations are staged once per workgroup in LDS, each
+//    chunk as float16 scaled by the power of two that brings the chunk's
+//    largest magnitude into [2^13, 2^14) (an exact scaling, undone on the
+//    chunk's partial sum together with the group scale);
+//  * partial sums of a row are added across its lanes with DPP and lane
+//    reads, always in the same order.
 #include <hip/hip_ext.h>
 
 #include "internal.h"
@@ -254,7 +254,7 @@ __device__ int find_item(const Fwd &f, int item_idx, Item *out)
 
 // One workgroup (4 waves) works on one item: up to TB tokens of one expert.
 // The item's activations are staged once in LDS (float16, scaled by a power of
-// two per token, in the order the dot product consumes them). Each wave then
+// two per chunk, in the order the dot product consumes them). Each wave then
 // owns R rows (times 64/LPR rows that share a wave when rows are short) per
 // row block; every lane reads CPL 16-byte chunks of each row, one 128-bit load
 // per chunk, with the next block's loads issued before the current block is
