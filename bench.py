@@ -224,25 +224,33 @@ def main():
                 raise RuntimeError(f"stack step failed with status {rc}")
             run_layer(l, ev if l == 0 else None)
 
-    # which experts each (layer, batch) step streams and on which kernels:
-    # experts with at least MFMA_MIN tokens (and the shared expert of a batch
-    # of that size) go to the matrix-core kernels, the others to the GEMVs
-    MFMA_MIN = 32
+    # which experts each (layer, batch) step streams and on which kernels
+    # (the library's default thresholds): experts with at least MFMA_MIN
+    # tokens go to the 128-token matrix-core pass, those with at least
+    # SMALL_MIN to the 32-token pass, the rest to the GEMVs; the shared
+    # expert by the batch size
+    MFMA_MIN, SMALL_MIN = 32, 2
     mfma_ok = spec.wbits == 4 and d % 64 == 0 and f % 64 == 0
     calib = {}
+
+    def pass_of(T):
+        T = np.asarray(T)
+        big = (T >= MFMA_MIN) & mfma_ok
+        small = ~big & (T >= SMALL_MIN) & mfma_ok
+        return np.where(big, 1, np.where(small, 2, 0))
 
     def record(key, l):
         torch.cuda.synchronize()
         nu = int(n_union.item())
         uid = union_ids[:nu].cpu().numpy()
         off = offsets.cpu().numpy()
-        T = off[uid + 1] - off[uid]
-        big = (T >= MFMA_MIN) if (mfma_ok and N >= MFMA_MIN) else np.zeros(nu, bool)
-        sh_big = bool(mfma_ok and N >= MFMA_MIN)
-        calib[key] = dict(union=nu, gemv_experts=int((~big).sum()) + (0 if sh_big else 1),
-                          mfma_experts=int(big.sum()) + (1 if sh_big else 0),
-                          mfma_tokens=int(T[big].sum()) + (N if sh_big else 0),
-                          wbits=cfg.layers[l].wbits, group=cfg.layers[l].group)
+        T = np.concatenate([off[uid + 1] - off[uid], [N]])  # routed, then shared
+        ps = pass_of(T)
+        c = dict(union=nu, wbits=cfg.layers[l].wbits, group=cfg.layers[l].group)
+        for name, code in (("gemv", 0), ("mfma", 1), ("small", 2)):
+            c[name + "_experts"] = int((ps == code).sum())
+            c[name + "_tokens"] = int(T[ps == code].sum())
+        calib[key] = c
 
     if stack:
         x0 = xs[0]
@@ -265,7 +273,7 @@ def main():
 
     # --- timed region -------------------------------------------------------
     K = args.steps
-    evs = [moe.ForwardOptions(*[hip.event() for _ in range(8)], 0) for _ in range(K)]
+    evs = [moe.ForwardOptions(*[hip.event() for _ in range(12)], 0, 0) for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s_ in range(K):
@@ -280,14 +288,14 @@ def main():
         except AssertionError:  # the kernel was not launched in that step
             return None
 
-    gu = [ms(e, "gateup_start", "gateup_end") for e in evs]
-    dn = [ms(e, "down_start", "down_end") for e in evs]
-    mgu = [ms(e, "mfma_gateup_start", "mfma_gateup_end") for e in evs]
-    mdn = [ms(e, "mfma_down_start", "mfma_down_end") for e in evs]
+    # per pass: event-timed gate/up and down launches of every timed step
+    timed = {}
+    for name, pre in (("gemv", ""), ("mfma", "mfma_"), ("small", "small_")):
+        timed[name] = ([ms(e, pre + "gateup_start", pre + "gateup_end") for e in evs],
+                       [ms(e, pre + "down_start", pre + "down_end") for e in evs])
     for e in evs:
-        for h in (e.gateup_start, e.gateup_end, e.down_start, e.down_end, e.mfma_gateup_start,
-                  e.mfma_gateup_end, e.mfma_down_start, e.mfma_down_end):
-            hip.L.hipEventDestroy(h)
+        for fld, _ in moe.ForwardOptions._fields_[:12]:
+            hip.L.hipEventDestroy(getattr(e, fld))
 
     # --- algorithmic bytes and flops ------------------------------------------
     def sizes(c):
@@ -316,42 +324,46 @@ def main():
         v = [x for x in v if x is not None]
         return float(np.mean(v)) if v else None
 
-    # GEMV gate/up: HBM-bound, algorithmic bytes = codes + scales of the
-    # gate and up matrices of every expert it handles, once
-    gu_bytes = [c["gemv_experts"] * sizes(c)[1] for c in (calib[k_] for k_ in step_key)]
-    dn_bytes = [c["gemv_experts"] * (sizes(c)[0] - sizes(c)[1])
-                for c in (calib[k_] for k_ in step_key)]
-    gemv = {"avg_launch_us": None, "achieved_GBps": None}
-    if avg(gu):
-        gemv = {"avg_launch_us": avg(gu) * 1e3,
-                "achieved_GBps": float(np.mean(gu_bytes)) / 1e9 / (avg(gu) / 1e3),
-                "bytes_per_launch": float(np.mean(gu_bytes)),
-                "down_avg_launch_us": avg(dn) * 1e3 if avg(dn) else None,
-                "down_GBps": float(np.mean(dn_bytes)) / 1e9 / (avg(dn) / 1e3) if avg(dn) else None}
-    # MFMA gate/up: matrix-core bound, algorithmic flops = 2 (gate, up) x
-    # 2 x d x f per token it handles
-    mflops = [4.0 * d * f * c["mfma_tokens"] for c in (calib[k_] for k_ in step_key)]
-    mfma = None
-    if avg(mgu):
-        mfma = {"avg_launch_us": avg(mgu) * 1e3,
-                "achieved_TFLOPs": float(np.mean(mflops)) / 1e12 / (avg(mgu) / 1e3),
-                "flops_per_launch": float(np.mean(mflops)),
-                "down_avg_launch_us": avg(mdn) * 1e3 if avg(mdn) else None}
-    if mfma and (gemv["avg_launch_us"] is None or mfma["avg_launch_us"] > gemv["avg_launch_us"]):
-        roof = {"kernel": "mfma_kernel<gate/up> (grouped GEMM of gate and up, SiLU product)",
-                "bound": "mfma", "achieved": mfma["achieved_TFLOPs"], "peak": MFMA_F16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": mfma["achieved_TFLOPs"] / MFMA_F16_PEAK_TFLOPS,
-                "traffic": measured_traffic(args.config, "moe::mfma_kernel<true"), "avg_launch_us": mfma["avg_launch_us"],
-                "flops_per_launch": mfma["flops_per_launch"], "gemv": gemv}
-    else:
-        roof = {"kernel": "gemv_kernel<gate/up> (expert gate and up projections, SiLU product)",
-                "bound": "hbm", "achieved": gemv["achieved_GBps"], "peak": HBM_PEAK_GBS,
-                "unit": "GB/s",
-                "frac": gemv["achieved_GBps"] / HBM_PEAK_GBS if gemv["achieved_GBps"] else None,
-                "traffic": measured_traffic(args.config, "moe::gemv_kernel<true"), "avg_launch_us": gemv["avg_launch_us"],
-                "bytes_per_launch": gemv.get("bytes_per_launch"),
-                "down_avg_launch_us": gemv.get("down_avg_launch_us"),
-                "down_GBps": gemv.get("down_GBps"), "mfma": mfma}
+    # Gate/up kernels of the three passes. The GEMV and 32-token passes are
+    # HBM-bound: algorithmic bytes = gate and up codes + scales of every
+    # expert the pass handles, once. The 128-token pass is matrix-core bound:
+    # algorithmic flops = 2 (gate, up) x 2 x d x f per token it handles.
+    steps_c = [calib[k_] for k_ in step_key]
+    passes = {}
+    for name in ("gemv", "small", "mfma"):
+        gu_t, dn_t = timed[name]
+        if not avg(gu_t):
+            continue
+        t_gu, t_dn = avg(gu_t) / 1e3, (avg(dn_t) / 1e3 if avg(dn_t) else None)
+        gu_b = float(np.mean([c[name + "_experts"] * sizes(c)[1] for c in steps_c]))
+        dn_b = float(np.mean([c[name + "_experts"] * (sizes(c)[0] - sizes(c)[1]) for c in steps_c]))
+        fl = float(np.mean([4.0 * d * f * c[name + "_tokens"] for c in steps_c]))
+        passes[name] = {"avg_launch_us": t_gu * 1e6, "bytes_per_launch": gu_b,
+                        "achieved_GBps": gu_b / 1e9 / t_gu, "flops_per_launch": fl,
+                        "achieved_TFLOPs": fl / 1e12 / t_gu,
+                        "down_avg_launch_us": t_dn * 1e6 if t_dn else None,
+                        "down_GBps": dn_b / 1e9 / t_dn if t_dn else None}
+    labels = {"gemv": ("gemv_kernel<gate/up> (expert gate and up projections, SiLU product)",
+                       "moe::gemv_kernel<true"),
+              "small": ("mfma_kernel<gate/up, 32 tokens> (small-group gate and up on the "
+                        "matrix cores)", "moe::mfma_kernel<true, 32"),
+              "mfma": ("mfma_kernel<gate/up, 128 tokens> (grouped GEMM of gate and up, SiLU "
+                       "product)", "moe::mfma_kernel<true, 128")}
+    roof = None
+    if passes:
+        # the roofline is reported for the pass whose gate/up launch is longest
+        top = max(passes, key=lambda n: passes[n]["avg_launch_us"])
+        pz = passes[top]
+        if top == "mfma":
+            roof = {"bound": "mfma", "achieved": pz["achieved_TFLOPs"],
+                    "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": pz["achieved_TFLOPs"] / MFMA_F16_PEAK_TFLOPS}
+        else:
+            roof = {"bound": "hbm", "achieved": pz["achieved_GBps"], "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": pz["achieved_GBps"] / HBM_PEAK_GBS}
+        roof["traffic"] = measured_traffic(args.config, labels[top][1])
+        roof["kernel"] = labels[top][0]
+        roof["passes"] = passes
 
     result = {
         "metric": METRIC,

@@ -146,8 +146,8 @@ moe_status moe_union(const int32_t *topk_ids, int n_tokens, int k, int n_experts
  * over the union produced by moe_union (union_ids, n_union, expert_offsets,
  * perm are its outputs for the same n_tokens and k). topk_w is an input, so a
  * caller may inject gate weights. Each distinct expert's weights are streamed
- * once per call for all of its tokens (decode-sized groups on GEMV kernels,
- * larger groups on the matrix cores, see moe_expert_forward_ex). y
+ * from HBM once per work item: single tokens on GEMV kernels, groups of up to
+ * 32 or 128 tokens on the matrix cores (see moe_expert_forward_ex). y
  * [n_tokens][d_model] float32 is overwritten. workspace: at least
  * moe_forward_workspace_size(pool, n_tokens, k) bytes, MOE_ALIGN-aligned.
  * Colibri pages: "Exact Architecture and Data-Flow Reconstruction" (three-
@@ -164,26 +164,32 @@ moe_status moe_expert_forward(const moe_expert_pool *pool /* (host) */,
 
 /*
  * moe_expert_forward with options (options may be NULL: same as
- * moe_expert_forward).
- *   mfma_min_tokens: experts with at least this many tokens in the batch
- *     (and the shared expert when n_tokens reaches it) are computed by the
- *     grouped-GEMM kernels on the matrix cores, the others by the GEMV
- *     kernels; 0 selects the default (32), a negative value keeps every
- *     expert on the GEMV kernels. The matrix-core path needs int4 weights
- *     and d_model, d_ff multiples of 64; otherwise every expert uses GEMV.
- *   events: each non-NULL event is taken by the dispatch of the kernel it
- *     names (hipExtLaunchKernelGGL), at that kernel's start or end. Events
- *     are created and owned by the caller; a kernel that a call does not
- *     launch leaves its events untouched.
+ * moe_expert_forward). Each expert of the call is computed by one of three
+ * passes, chosen by its number of tokens T in the batch (the shared expert
+ * by n_tokens):
+ *   T >= mfma_min_tokens: grouped GEMM on the matrix cores, 128-token tiles;
+ *     0 selects the default (32), a negative value turns this pass off;
+ *   mfma_small_min_tokens <= T < mfma_min_tokens: the same kernels with
+ *     32-token tiles; 0 selects the default (2), negative turns it off;
+ *   otherwise: the streaming GEMV kernels.
+ * The matrix-core passes need int4 weights and d_model, d_ff multiples of
+ * 64; otherwise every expert uses the GEMV.
+ * events: each non-NULL event is taken by the dispatch of the kernel it
+ *   names (hipExtLaunchKernelGGL), at that kernel's start or end. Events are
+ *   created and owned by the caller; a kernel that a call does not launch
+ *   leaves its events untouched.
  * The results agree with moe_expert_forward to the library's tolerance for
- * every mfma_min_tokens (bit for bit when the same kernels are selected).
+ * every choice of thresholds (bit for bit when the same kernels are chosen).
  */
 typedef struct {
     hipEvent_t gateup_start, gateup_end;              /* GEMV gate/up kernel */
     hipEvent_t down_start, down_end;                  /* GEMV down kernel */
-    hipEvent_t mfma_gateup_start, mfma_gateup_end;    /* matrix-core gate/up kernel */
-    hipEvent_t mfma_down_start, mfma_down_end;        /* matrix-core down kernel */
+    hipEvent_t mfma_gateup_start, mfma_gateup_end;    /* 128-token matrix-core gate/up */
+    hipEvent_t mfma_down_start, mfma_down_end;        /* 128-token matrix-core down */
+    hipEvent_t small_gateup_start, small_gateup_end;  /* 32-token matrix-core gate/up */
+    hipEvent_t small_down_start, small_down_end;      /* 32-token matrix-core down */
     int32_t mfma_min_tokens;
+    int32_t mfma_small_min_tokens;
 } moe_forward_options;
 
 moe_status moe_expert_forward_ex(const moe_expert_pool *pool /* (host) */,

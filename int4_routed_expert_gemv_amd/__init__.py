@@ -46,7 +46,9 @@ class ForwardOptions(ctypes.Structure):
                 ("down_start", ctypes.c_void_p), ("down_end", ctypes.c_void_p),
                 ("mfma_gateup_start", ctypes.c_void_p), ("mfma_gateup_end", ctypes.c_void_p),
                 ("mfma_down_start", ctypes.c_void_p), ("mfma_down_end", ctypes.c_void_p),
-                ("mfma_min_tokens", ctypes.c_int32)]
+                ("small_gateup_start", ctypes.c_void_p), ("small_gateup_end", ctypes.c_void_p),
+                ("small_down_start", ctypes.c_void_p), ("small_down_end", ctypes.c_void_p),
+                ("mfma_min_tokens", ctypes.c_int32), ("mfma_small_min_tokens", ctypes.c_int32)]
 
 
 class PoolDesc(ctypes.Structure):

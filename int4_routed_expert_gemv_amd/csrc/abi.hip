@@ -45,40 +45,64 @@ long long n_scales(long long rows, long long cols, int group)
     return group ? rows * (cols / group) : rows;
 }
 
-// Default: experts with at least this many tokens use the MFMA pass.
+// Defaults: experts with at least this many tokens use the 128-token MFMA
+// pass; experts with at least kDefaultSmallMinTokens (and fewer than the
+// former) use the 32-token MFMA pass; single-token experts stay on the GEMV.
 constexpr int kDefaultMfmaMinTokens = 32;
+constexpr int kDefaultSmallMinTokens = 2;
 
 // Workspace of moe_expert_forward, laid out in this order.
 struct FwdLayout {
-    int tb, max_items, max_mitems, tstar, P;
-    long long items, n_items, mitems, n_mitems, h, o, total;
+    int tb, max_items, max_mitems, max_sitems, tstar, tsmall, P;
+    long long items, n_items, mitems, n_mitems, sitems, n_sitems, h, o, total;
 };
 
-// upper = true: the largest layout any value of mfma_min_tokens can select
-// (each list at its own largest), for sizing the workspace
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+// The passes and work-list bounds of one call. upper = true: a bound of the
+// layout over every option value, for sizing the workspace.
 FwdLayout fwd_layout(const Geo &g, int N, int k, int has_shared, int mfma_min_tokens,
-                     bool upper = false)
+                     int small_min_tokens, bool upper = false)
 {
     FwdLayout L;
     const long long A = (long long)N * k;
-    L.tb = gemv_tokens_per_item(g, N);
-    // each union expert adds at most one partly filled item
-    const long long ue = A < g.E ? A : g.E;
-    L.max_items = (int)((A + L.tb - 1) / L.tb + ue + (has_shared ? (N + L.tb - 1) / L.tb : 0));
-    // no expert has more than N tokens: with N <= tb every expert is one item
-    if (N <= L.tb) L.max_items = (int)(ue + (has_shared ? 1 : 0));
-    // the MFMA pass runs when some expert can reach the threshold (an expert
-    // has at most N tokens)
-    L.tstar = upper ? 1 : (mfma_min_tokens > 0 ? mfma_min_tokens : kDefaultMfmaMinTokens);
-    const bool mfma = (upper || mfma_min_tokens >= 0) && mfma_supported(g) && N >= L.tstar;
-    const long long mt = mfma_tokens_per_item();
-    L.max_mitems = mfma ? (int)((A + mt - 1) / mt + A / L.tstar + (has_shared ? (N + mt - 1) / mt : 0))
-                        : 0;
-    if (mfma && !upper) {
-        // with the MFMA pass on, the GEMV list holds only experts with fewer
-        // than tstar tokens (the shared expert, with N >= tstar, is not one)
-        const long long per = (L.tstar - 1 + L.tb - 1) / L.tb;
-        if (ue * per < L.max_items) L.max_items = (int)(ue * per);
+    const long long ue = A < g.E ? A : g.E;  // union experts at most
+    const bool mf = mfma_supported(g);
+    L.tstar = mfma_min_tokens > 0 ? mfma_min_tokens : kDefaultMfmaMinTokens;
+    L.tsmall = small_min_tokens > 0 ? small_min_tokens : kDefaultSmallMinTokens;
+    // a pass runs when some expert can reach its threshold (an expert has at
+    // most N tokens); the small pass only takes what the large one leaves
+    const bool big = mf && mfma_min_tokens >= 0 && N >= L.tstar;
+    const bool small = mf && small_min_tokens >= 0 && N >= L.tsmall && !(big && L.tsmall >= L.tstar);
+    // most tokens of an expert on the GEMV pass
+    long long cap = N;
+    if (small) cap = L.tsmall - 1;
+    else if (big) cap = L.tstar - 1;
+    L.tb = gemv_tokens_per_item(g, (int)(cap < 1 ? 1 : cap));
+    if (upper) {
+        // every list at the most items any threshold can give it (1-token
+        // GEMV items, and every assignment its own MFMA expert)
+        L.tb = gemv_tokens_per_item(g, N);
+        L.max_items = (int)(A + ue + N);
+        L.max_mitems = mf ? (int)(ceil_div(A, kMfmaBigTokens) + A + ceil_div(N, kMfmaBigTokens)) : 0;
+        L.max_sitems = mf ? (int)(ceil_div(A, kMfmaSmallTokens) + A + ceil_div(N, kMfmaSmallTokens)) : 0;
+    } else {
+        if (cap < 1) {
+            L.max_items = 0;
+        } else {
+            // each expert adds at most one partly filled item; none has more
+            // than cap tokens
+            const long long per = ceil_div(cap, L.tb);
+            long long routed = ceil_div(A, L.tb) + ue;
+            if (ue * per < routed) routed = ue * per;
+            L.max_items = (int)(routed + (has_shared && N <= cap ? ceil_div(N, L.tb) : 0));
+        }
+        L.max_mitems = big ? (int)(ceil_div(A, kMfmaBigTokens) + A / L.tstar +
+                                   (has_shared ? ceil_div(N, kMfmaBigTokens) : 0))
+                           : 0;
+        L.max_sitems = small ? (int)(ceil_div(A, kMfmaSmallTokens) + A / L.tsmall +
+                                     (has_shared ? ceil_div(N, kMfmaSmallTokens) : 0))
+                             : 0;
     }
     L.P = (int)(A + (has_shared ? N : 0));
     long long off = 0;
@@ -86,6 +110,8 @@ FwdLayout fwd_layout(const Geo &g, int N, int k, int has_shared, int mfma_min_to
     L.n_items = off; off = align_up(off + 4);
     L.mitems = off; off = align_up(off + (long long)L.max_mitems * (long long)sizeof(Item));
     L.n_mitems = off; off = align_up(off + 4);
+    L.sitems = off; off = align_up(off + (long long)L.max_sitems * (long long)sizeof(Item));
+    L.n_sitems = off; off = align_up(off + 4);
     L.h = off; off = align_up(off + (long long)L.P * g.f * 4);
     L.o = off; off = align_up(off + (long long)L.P * g.d * 4);
     L.total = off;
@@ -158,7 +184,7 @@ size_t moe_forward_workspace_size(const moe_expert_pool *pool, int n_tokens, int
 {
     Geo g;
     if (resolve_geo(pool, &g) != MOE_OK || n_tokens < 0 || k < 1) return 0;
-    return (size_t)fwd_layout(g, n_tokens, k, pool->shared != nullptr, 0, true).total;
+    return (size_t)fwd_layout(g, n_tokens, k, pool->shared != nullptr, 0, 0, true).total;
 }
 
 size_t moe_workspace_size(const moe_expert_pool *pool, int n_tokens, int k)
@@ -272,7 +298,8 @@ moe_status moe_expert_forward_ex(const moe_expert_pool *pool, const float *x, in
         return MOE_EINVAL;
     if (((uintptr_t)x % 16) || ((uintptr_t)y % 16)) return MOE_EALIGN;
     const int has_shared = pool->shared != nullptr;
-    const FwdLayout L = fwd_layout(g, n_tokens, k, has_shared, ev ? ev->mfma_min_tokens : 0);
+    const FwdLayout L = fwd_layout(g, n_tokens, k, has_shared, ev ? ev->mfma_min_tokens : 0,
+                                   ev ? ev->mfma_small_min_tokens : 0);
     if (!workspace || ws_bytes < (size_t)L.total) return MOE_EWORKSPACE;
     if (!aligned(workspace)) return MOE_EALIGN;
 
@@ -303,6 +330,10 @@ moe_status moe_expert_forward_ex(const moe_expert_pool *pool, const float *x, in
     f.n_mitems = reinterpret_cast<int32_t *>(ws + L.n_mitems);
     f.max_mitems = L.max_mitems;
     f.tstar = L.tstar;
+    f.sitems = reinterpret_cast<Item *>(ws + L.sitems);
+    f.n_sitems = reinterpret_cast<int32_t *>(ws + L.n_sitems);
+    f.max_sitems = L.max_sitems;
+    f.tsmall = L.tsmall;
 
     f.ev_gu[0] = ev ? ev->gateup_start : nullptr;
     f.ev_gu[1] = ev ? ev->gateup_end : nullptr;
@@ -312,10 +343,18 @@ moe_status moe_expert_forward_ex(const moe_expert_pool *pool, const float *x, in
     f.ev_mgu[1] = ev ? ev->mfma_gateup_end : nullptr;
     f.ev_mdn[0] = ev ? ev->mfma_down_start : nullptr;
     f.ev_mdn[1] = ev ? ev->mfma_down_end : nullptr;
+    f.ev_sgu[0] = ev ? ev->small_gateup_start : nullptr;
+    f.ev_sgu[1] = ev ? ev->small_gateup_end : nullptr;
+    f.ev_sdn[0] = ev ? ev->small_down_start : nullptr;
+    f.ev_sdn[1] = ev ? ev->small_down_end : nullptr;
+    // gate/up of every pass (the first launch also builds the work lists),
+    // then down of every pass, then the combine
     if (launch_gateup(f, stream) != hipSuccess) return MOE_EHIP;
-    if (f.max_mitems > 0 && launch_mfma(f, true, stream) != hipSuccess) return MOE_EHIP;
+    if (launch_mfma(f, true, false, stream) != hipSuccess) return MOE_EHIP;
+    if (launch_mfma(f, true, true, stream) != hipSuccess) return MOE_EHIP;
     if (launch_down(f, stream) != hipSuccess) return MOE_EHIP;
-    if (f.max_mitems > 0 && launch_mfma(f, false, stream) != hipSuccess) return MOE_EHIP;
+    if (launch_mfma(f, false, false, stream) != hipSuccess) return MOE_EHIP;
+    if (launch_mfma(f, false, true, stream) != hipSuccess) return MOE_EHIP;
     if (launch_combine(f.o, topk_w, n_tokens, k, g.d, (int)A, has_shared, y, stream) != hipSuccess)
         return MOE_EHIP;
     return MOE_OK;

@@ -576,16 +576,24 @@ __device__ int block_excl_scan(int v, int &total)
     return r;
 }
 
+// Which pass computes an expert with T tokens: 0 the GEMV kernels, 1 the
+// 128-token MFMA kernels (T >= tstar), 2 the 32-token MFMA kernels
+// (tsmall <= T < tstar). A pass with no list (max_* == 0) takes nothing.
+__device__ __forceinline__ int pass_of(const Fwd &f, int T)
+{
+    if (f.max_mitems > 0 && T >= f.tstar) return 1;
+    if (f.max_sitems > 0 && T >= f.tsmall) return 2;
+    return 0;
+}
+
 // Work lists for unions of any size (<= 1024 experts), one thread per union
-// slot. Experts with at least tstar tokens (and the shared expert when the
-// batch has at least tstar tokens) go to the MFMA list in slices of 128
-// tokens, the others to the GEMV list in slices of tb; in both lists the
-// shared expert comes first, then the union experts in union order.
+// slot. Each expert goes to the list of its pass in slices of that list's
+// tokens per item (tb, 128 or 32); in every list the shared expert comes
+// first, then the union experts in union order.
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Fwd f)
 {
     const int u = threadIdx.x;
-    const int E = f.g.E, TB = f.tb, MT = 128;
-    const bool mfma = f.max_mitems > 0;
+    const int E = f.g.E;
     const int nu = min(max(*f.n_union, 0), E);
     int e = -1, s0 = 0, T = 0;
     if (u < nu) {
@@ -597,38 +605,29 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Fwd f)
             e = -1;
         }
     }
-    const bool big = mfma && T >= f.tstar;
-    const int nb_g = big ? 0 : (T + TB - 1) / TB;
-    const int nb_m = big ? (T + MT - 1) / MT : 0;
-    const bool sh_big = f.has_shared && mfma && f.N >= f.tstar;
-    const int nsh_g = f.has_shared && !sh_big ? (f.N + TB - 1) / TB : 0;
-    const int nsh_m = sh_big ? (f.N + MT - 1) / MT : 0;
-    int tot_g, tot_m;
-    const int base_g = nsh_g + block_excl_scan(nb_g, tot_g);
-    const int base_m = nsh_m + block_excl_scan(nb_m, tot_m);
-    for (int b = u; b < nsh_g; b += kPlanThreads) {
-        if (b >= f.max_items) break;
-        Item it = {-1, f.A + b * TB, min(TB, f.N - b * TB), 0};
-        f.items[b] = it;
-    }
-    for (int b = u; b < nsh_m; b += kPlanThreads) {
-        if (b >= f.max_mitems) break;
-        Item it = {-1, f.A + b * MT, min(MT, f.N - b * MT), 0};
-        f.mitems[b] = it;
-    }
-    for (int b = 0; b < nb_g; ++b) {
-        if (base_g + b >= f.max_items) break;
-        Item it = {e, s0 + b * TB, min(TB, T - b * TB), 0};
-        f.items[base_g + b] = it;
-    }
-    for (int b = 0; b < nb_m; ++b) {
-        if (base_m + b >= f.max_mitems) break;
-        Item it = {e, s0 + b * MT, min(MT, T - b * MT), 0};
-        f.mitems[base_m + b] = it;
-    }
-    if (u == 0) {
-        *f.n_items = min(nsh_g + tot_g, f.max_items);
-        if (mfma) *f.n_mitems = min(nsh_m + tot_m, f.max_mitems);
+    const int pass = pass_of(f, T);
+    const int sh_pass = f.has_shared ? pass_of(f, f.N) : -1;
+    Item *const lists[3] = {f.items, f.mitems, f.sitems};
+    int32_t *const counts[3] = {f.n_items, f.n_mitems, f.n_sitems};
+    const int maxes[3] = {f.max_items, f.max_mitems, f.max_sitems};
+    const int sizes[3] = {f.tb, kMfmaBigTokens, kMfmaSmallTokens};
+#pragma unroll
+    for (int l = 0; l < 3; ++l) {
+        const int sz = sizes[l], mx = maxes[l];
+        const int nsh = sh_pass == l ? (f.N + sz - 1) / sz : 0;
+        const int nb = pass == l ? (T + sz - 1) / sz : 0;
+        int tot;
+        const int base = nsh + block_excl_scan(nb, tot);  // uniform call: every thread
+        if (mx <= 0) continue;
+        for (int b = u; b < nsh && b < mx; b += kPlanThreads) {
+            Item it = {-1, f.A + b * sz, min(sz, f.N - b * sz), 0};
+            lists[l][b] = it;
+        }
+        for (int b = 0; b < nb && base + b < mx; ++b) {
+            Item it = {e, s0 + b * sz, min(sz, T - b * sz), 0};
+            lists[l][base + b] = it;
+        }
+        if (u == 0) *counts[l] = min(nsh + tot, mx);
     }
 }
 
@@ -809,7 +808,9 @@ hipError_t launch_gateup(const Fwd &f, hipStream_t s)
     // expert goes to the MFMA pass; otherwise one planning workgroup builds
     // both work lists first
     const int max_union = f.A < f.g.E ? f.A : f.g.E;
-    a.plan_here = max_union <= kWave && f.max_mitems == 0 ? (f.N <= f.tb ? 2 : 1) : 0;
+    a.plan_here = max_union <= kWave && f.max_mitems == 0 && f.max_sitems == 0
+                      ? (f.N <= f.tb ? 2 : 1)
+                      : 0;
     if (!a.plan_here) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, f);
         const hipError_t e = hipGetLastError();

@@ -6,8 +6,9 @@
 // always-on shared expert), README "Get started" (int4 experts with group
 // scales).
 //
-// For one expert and up to 128 of its tokens, a workgroup computes 128 output
-// rows (of gate and up together, or of down) over the full contraction:
+// For one expert and up to MT of its tokens (MT = 128 for large groups, 32
+// for small ones), a workgroup computes 128 output rows (of gate and up
+// together, or of down) over the full contraction:
 //   gate/up:  h[p][r] = silu(sum_c Wg[r][c] x_t[c]) * (sum_c Wu[r][c] x_t[c])
 //   down:     o[out(p)][r] = sum_c Wd[r][c] h[p][c]
 // on v_mfma_f32_32x32x16_f16 (float16 products, float32 accumulation):
@@ -20,7 +21,7 @@
 //  * within each 8-column group the columns are taken in the order
 //    0,4,1,5,2,6,3,7 on both operands, which lets one 32-bit word of codes
 //    feed one MFMA operand without shuffles;
-//  * each of the 4 waves owns 32 rows and all 128 tokens (4 x 1 blocks of
+//  * each of the 4 waves owns 32 rows and all MT tokens (MT/32 blocks of
 //    32 x 32); loads run two steps ahead of the matrix cores.
 // Workgroups are mapped so that those sharing an expert (and so its weights
 // and its tokens) land on the same XCD and share its L2.
@@ -36,7 +37,6 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
-constexpr int kMT = 128;            // tokens per tile
 constexpr int kNW = 32;             // rows per wave
 constexpr int kNT = (kThreads / 64) * kNW;  // rows per workgroup
 constexpr int kKB = 64;             // columns per step
@@ -66,18 +66,22 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t s2)
 struct MfmaArgs {
     Fwd f;
     int n_tiles;        // row tiles per item
+    const Item *items;  // the work list of this pass
+    const int32_t *n_items;
+    int max_items;
 };
 
-// One workgroup: one MFMA item (<= 128 tokens of one expert) x kNT rows;
-// each wave owns 32 rows and all 128 tokens. Loads run two 64-column steps
+// One workgroup: one MFMA item (<= MT tokens of one expert) x kNT rows;
+// each wave owns 32 rows and all MT tokens. Loads run two 64-column steps
 // ahead of the matrix cores (registers), activations are double-buffered in
 // LDS.
-template <bool GATEUP>
-__global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
+template <bool GATEUP, int MT>
+__global__ __launch_bounds__(kThreads, MT > 32 ? 1 : 2) void mfma_kernel(MfmaArgs ma)
 {
     constexpr int NM = GATEUP ? 2 : 1;
-    __shared__ _Float16 As[2][kMT][kAStride];
-    __shared__ int s_src[kMT];   // input row of each tile token (-1: none)
+    constexpr int MF = MT / 32;  // 32 x 32 blocks per wave
+    __shared__ _Float16 As[2][MT][kAStride];
+    __shared__ int s_src[MT];   // input row of each tile token (-1: none)
 
     const Fwd &f = ma.f;
     const Geo &g = f.g;
@@ -87,7 +91,7 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
     // XCDs round robin, so give each XCD a contiguous range of (item, row
     // tile) pairs; tiles of one item share its tokens, items of one expert
     // are adjacent and share its weights
-    const int n_items = min(*f.n_mitems, f.max_mitems);
+    const int n_items = min(*ma.n_items, ma.max_items);
     const int n_active = n_items * ma.n_tiles;
     const int b = blockIdx.x;
     if (b >= n_active) return;
@@ -96,8 +100,8 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
     const int logical = xcd * q + min(xcd, rem) + i;
     const int item_idx = logical / ma.n_tiles;
     const int ntile = logical % ma.n_tiles;
-    const Item it = f.mitems[item_idx];
-    const int count = min(it.count, kMT);
+    const Item it = ma.items[item_idx];
+    const int count = min(it.count, MT);
     const uint8_t *blk = it.expert >= 0 ? f.pool + (size_t)it.expert * f.stride : f.shared;
     const int K = GATEUP ? g.d : g.f;       // contraction length
     const int rows = GATEUP ? g.f : g.d;    // output rows
@@ -105,7 +109,7 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
     float *out = GATEUP ? f.h : f.o;
 
     // input row of every tile token
-    if (tid < kMT) {
+    if (tid < MT) {
         int src = -1;
         if (tid < count) {
             const int p = it.p0 + tid;
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
     __syncthreads();
 
     // activation loads: thread -> (token row, part of the 64 columns)
-    constexpr int kParts = kThreads / kMT;          // threads per token row
+    constexpr int kParts = kThreads / MT;           // threads per token row
     constexpr int kCols = kKB / kParts;             // columns per thread
     constexpr int kVec = kCols / 4;                 // float4 per thread
     const int a_row = tid / kParts, a_q = tid % kParts;
@@ -174,11 +178,11 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
         }
     };
 
-    f32x16_t acc[NM][4];
+    f32x16_t acc[NM][MF];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int mf = 0; mf < 4; ++mf)
+        for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[m][mf][r] = 0.0f;
 
@@ -196,7 +200,7 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
                 bf[m] = dequant8(w, s2[m]);
             }
 #pragma unroll
-            for (int mf = 0; mf < 4; ++mf) {
+            for (int mf = 0; mf < MF; ++mf) {
                 const half8_t af =
                     *reinterpret_cast<const half8_t *>(&As[cur][mf * 32 + (lane % 32)][32 * hh + 8 * s]);
 #pragma unroll
@@ -251,11 +255,11 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
         }
     }
 
-    // epilogue: lane holds column `row` of four 32x32 blocks; register r of
+    // epilogue: lane holds column `row` of MF 32x32 blocks; register r of
     // block mf is token mf*32 + (r/4)*8 + (lane/32)*4 + r%4
     if (row >= rows) return;
 #pragma unroll
-    for (int mf = 0; mf < 4; ++mf) {
+    for (int mf = 0; mf < MF; ++mf) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int tok = mf * 32 + (r / 4) * 8 + hh * 4 + (r % 4);
@@ -279,31 +283,36 @@ bool mfma_supported(const Geo &g)
     return g.wbits == 4 && g.d % kKB == 0 && g.f % kKB == 0;
 }
 
-int mfma_tokens_per_item() { return kMT; }
+template <bool GATEUP, int MT>
+hipError_t run_mfma(const MfmaArgs &a, long long blocks, const hipEvent_t *ev, hipStream_t s)
+{
+    const dim3 grid((unsigned)blocks);
+    if (ev[0] || ev[1])  // events taken by the dispatch itself, around this kernel only
+        hipExtLaunchKernelGGL((mfma_kernel<GATEUP, MT>), grid, dim3(kThreads), 0, s, ev[0], ev[1],
+                              0, a);
+    else
+        hipLaunchKernelGGL((mfma_kernel<GATEUP, MT>), grid, dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
 
-hipError_t launch_mfma(const Fwd &f, bool gateup, hipStream_t s)
+hipError_t launch_mfma(const Fwd &f, bool gateup, bool small, hipStream_t s)
 {
     MfmaArgs a;
     a.f = f;
+    a.items = small ? f.sitems : f.mitems;
+    a.n_items = small ? f.n_sitems : f.n_mitems;
+    a.max_items = small ? f.max_sitems : f.max_mitems;
     const int rows = gateup ? f.g.f : f.g.d;
     a.n_tiles = (rows + kNT - 1) / kNT;
-    const long long blocks = (long long)f.max_mitems * a.n_tiles;
+    const long long blocks = (long long)a.max_items * a.n_tiles;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    const hipEvent_t *ev = gateup ? f.ev_mgu : f.ev_mdn;
-    const dim3 grid((unsigned)blocks);
-    if (gateup) {
-        if (ev[0] || ev[1])
-            hipExtLaunchKernelGGL(mfma_kernel<true>, grid, dim3(kThreads), 0, s, ev[0], ev[1], 0, a);
-        else
-            hipLaunchKernelGGL(mfma_kernel<true>, grid, dim3(kThreads), 0, s, a);
-    } else {
-        if (ev[0] || ev[1])
-            hipExtLaunchKernelGGL(mfma_kernel<false>, grid, dim3(kThreads), 0, s, ev[0], ev[1], 0, a);
-        else
-            hipLaunchKernelGGL(mfma_kernel<false>, grid, dim3(kThreads), 0, s, a);
-    }
-    return hipGetLastError();
+    const hipEvent_t *ev = small ? (gateup ? f.ev_sgu : f.ev_sdn) : (gateup ? f.ev_mgu : f.ev_mdn);
+    if (small)
+        return gateup ? run_mfma<true, kMfmaSmallTokens>(a, blocks, ev, s)
+                      : run_mfma<false, kMfmaSmallTokens>(a, blocks, ev, s);
+    return gateup ? run_mfma<true, kMfmaBigTokens>(a, blocks, ev, s)
+                  : run_mfma<false, kMfmaBigTokens>(a, blocks, ev, s);
 }
 
 }  // namespace moe

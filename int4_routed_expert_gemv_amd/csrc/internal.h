@@ -50,14 +50,20 @@ struct Fwd {
     int32_t *n_items;        // [1]
     int tb;                  // tokens per GEMV work item
     int max_items;           // host bound of the number of GEMV items
-    Item *mitems;            // [max_mitems] MFMA work list (workspace)
+    Item *mitems;            // [max_mitems] MFMA work list, 128-token items (workspace)
     int32_t *n_mitems;       // [1]
-    int max_mitems;          // host bound of the number of MFMA items (0: no MFMA pass)
-    int tstar;               // experts with at least this many tokens use the MFMA pass
+    int max_mitems;          // host bound of the number of 128-token items (0: no such pass)
+    int tstar;               // experts with at least this many tokens use 128-token items
+    Item *sitems;            // [max_sitems] MFMA work list, 32-token items (workspace)
+    int32_t *n_sitems;       // [1]
+    int max_sitems;          // host bound of the number of 32-token items (0: no such pass)
+    int tsmall;              // experts with tsmall <= tokens < tstar use 32-token items
     hipEvent_t ev_gu[2];     // optional: taken at the GEMV gate/up kernel's start and end
     hipEvent_t ev_dn[2];     // optional: the same for the GEMV down kernel
-    hipEvent_t ev_mgu[2];    // optional: the same for the MFMA gate/up kernel
-    hipEvent_t ev_mdn[2];    // optional: the same for the MFMA down kernel
+    hipEvent_t ev_mgu[2];    // optional: the same for the 128-token MFMA gate/up kernel
+    hipEvent_t ev_mdn[2];    // optional: the same for the 128-token MFMA down kernel
+    hipEvent_t ev_sgu[2];    // optional: the same for the 32-token MFMA gate/up kernel
+    hipEvent_t ev_sdn[2];    // optional: the same for the 32-token MFMA down kernel
 };
 
 // ---- host helpers (abi.hip) --------------------------------------------
@@ -75,8 +81,10 @@ int gemv_tokens_per_item(const Geo &g, int n_tokens);
 hipError_t launch_gateup(const Fwd &f, hipStream_t s);
 hipError_t launch_down(const Fwd &f, hipStream_t s);
 bool mfma_supported(const Geo &g);
-int mfma_tokens_per_item();
-hipError_t launch_mfma(const Fwd &f, bool gateup, hipStream_t s);
+constexpr int kMfmaBigTokens = 128;   // tokens per item of the large-group MFMA pass
+constexpr int kMfmaSmallTokens = 32;  // tokens per item of the small-group MFMA pass
+// small = false: the 128-token items (mitems), true: the 32-token items (sitems)
+hipError_t launch_mfma(const Fwd &f, bool gateup, bool small, hipStream_t s);
 hipError_t launch_combine(const float *o, const float *w, int N, int k, int d, int A,
                           int has_shared, float *y, hipStream_t s);
 hipError_t launch_residual_rmsnorm(float *h, const float *y, float *a, int N, int d, float eps,

@@ -17,9 +17,10 @@ def workspace(pool, N, k, device="cuda"):
 
 
 def run_layer(pool, x, wr, b, k, ids_in=None, w_in=None, counters=None, device="cuda",
-              mfma_min_tokens=None):
+              mfma_min_tokens=None, mfma_small_min_tokens=None):
     """route_topk (unless ids_in/w_in are given) -> union -> hit_count -> expert_forward
-    (moe_expert_forward_ex with that threshold when mfma_min_tokens is given)."""
+    (moe_expert_forward_ex with those thresholds when either is given; None
+    leaves a threshold at its default)."""
     N, d = x.shape
     E = pool.desc.n_experts
     xd = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(device)
@@ -42,9 +43,10 @@ def run_layer(pool, x, wr, b, k, ids_in=None, w_in=None, counters=None, device="
     moe.hit_count(ids, E, cnt)
     y = torch.empty((N, d), dtype=torch.float32, device=device)
     opts = None
-    if mfma_min_tokens is not None:
+    if mfma_min_tokens is not None or mfma_small_min_tokens is not None:
         opts = moe.ForwardOptions()
-        opts.mfma_min_tokens = mfma_min_tokens
+        opts.mfma_min_tokens = mfma_min_tokens or 0
+        opts.mfma_small_min_tokens = mfma_small_min_tokens or 0
     moe.expert_forward(pool.desc, xd, k, w, union_ids, n_union, offsets, perm, y, ws,
                        options=opts)
     torch.cuda.synchronize()

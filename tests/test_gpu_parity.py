@@ -58,7 +58,7 @@ def oracle_then_pool(cfg, layer=0, x=None):
     return spec, x, wr, b, blocks, shared, nre
 
 
-def full_parity(cfg, layer=0, mfma_min_tokens=None):
+def full_parity(cfg, layer=0, mfma_min_tokens=None, mfma_small_min_tokens=None):
     spec, x, wr, b, blocks, shared, nre = oracle_then_pool(cfg, layer)
     say(f"[{cfg.name}] N={cfg.n_tokens} k={cfg.k} d={spec.d} f={spec.f} E={spec.n_experts} "
         f"wbits={spec.wbits} G={spec.group} redrawn={nre}")
@@ -66,8 +66,9 @@ def full_parity(cfg, layer=0, mfma_min_tokens=None):
                             spec.group)
     pool = upload_pool(spec, blocks, shared)   # packs the blocks in place: oracle first
     say(f"[{cfg.name}] oracle done, union={len(ref['union_ids'])}; running GPU step "
-        f"(mfma_min_tokens={mfma_min_tokens})")
-    got = run_layer(pool, x, wr, b, cfg.k, mfma_min_tokens=mfma_min_tokens)
+        f"(mfma_min_tokens={mfma_min_tokens}, mfma_small_min_tokens={mfma_small_min_tokens})")
+    got = run_layer(pool, x, wr, b, cfg.k, mfma_min_tokens=mfma_min_tokens,
+                    mfma_small_min_tokens=mfma_small_min_tokens)
     check_routing(got, ref, spec.n_experts)
     err = check_y(got["y"], ref["y"])
     say(f"[{cfg.name}] parity ok, max rel err {err:.2e}")
@@ -134,18 +135,23 @@ def test_tiny_ragged_batches(N, k):
     pool, *_ = full_parity(tiny(n_tokens=N, k=k))
 
 
-@pytest.mark.parametrize("mfma_min_tokens", [1, -1])
+# (128-token threshold, 32-token threshold): every expert on the 128-token
+# matrix-core pass, every expert on the 32-token pass, every expert on the
+# GEMV, and the three mixed by thresholds 3 and 2
+PASSES = [(1, -1), (-1, 1), (-1, -1), (3, 2)]
+
+
+@pytest.mark.parametrize("big,small", PASSES)
 @pytest.mark.parametrize("N,k", [(7, 3), (64, 4), (200, 16)])
-def test_tiny_forced_paths(N, k, mfma_min_tokens):
-    """Every expert on the matrix-core kernels (threshold 1) or on the GEMV
-    kernels (negative threshold): both agree with the oracle; the batches give
-    partly filled 128-token tiles and multi-tile experts."""
-    full_parity(tiny(n_tokens=N, k=k), mfma_min_tokens=mfma_min_tokens)
+def test_tiny_forced_paths(N, k, big, small):
+    """Each pass on its own agrees with the oracle; the batches give partly
+    filled 32- and 128-token tiles and multi-tile experts."""
+    full_parity(tiny(n_tokens=N, k=k), mfma_min_tokens=big, mfma_small_min_tokens=small)
 
 
-@pytest.mark.parametrize("mfma_min_tokens", [1, -1])
-def test_decode64_forced_paths(mfma_min_tokens):
-    full_parity(synth.CONFIGS["decode64"], mfma_min_tokens=mfma_min_tokens)
+@pytest.mark.parametrize("big,small", PASSES)
+def test_decode64_forced_paths(big, small):
+    full_parity(synth.CONFIGS["decode64"], mfma_min_tokens=big, mfma_small_min_tokens=small)
     torch.cuda.empty_cache()
 
 
@@ -163,28 +169,39 @@ def test_determinism_and_counter_accumulation():
     torch.cuda.empty_cache()
 
 
-def test_zero_gate_equals_dropped_slot():
-    """w[:, 1] = 0 with k = 2 gives bit for bit the k = 1 result on slot 0."""
+# one pass for every expert, so that the same kernels run whatever the
+# token counts: GEMV only, 32-token MFMA only, 128-token MFMA only
+SINGLE_PASS = [(-1, -1), (-1, 1), (1, -1)]
+
+
+@pytest.mark.parametrize("big,small", SINGLE_PASS)
+def test_zero_gate_equals_dropped_slot(big, small):
+    """w[:, 1] = 0 with k = 2 gives bit for bit the k = 1 result on slot 0
+    (within one pass: the passes round differently)."""
     cfg = tiny(n_tokens=12, k=2)
     spec, x, wr, b, blocks, shared, _ = oracle_then_pool(cfg)
     ids, w = oracle.topk(oracle.router(x, wr, b), 2)
     pool = upload_pool(spec, blocks, shared)
     w0 = w.copy()
     w0[:, 1] = 0.0
-    r2 = run_layer(pool, x, wr, b, 2, ids_in=ids, w_in=w0)
-    r1 = run_layer(pool, x, wr, b, 1, ids_in=ids[:, :1].copy(), w_in=w[:, :1].copy())
+    r2 = run_layer(pool, x, wr, b, 2, ids_in=ids, w_in=w0, mfma_min_tokens=big,
+                   mfma_small_min_tokens=small)
+    r1 = run_layer(pool, x, wr, b, 1, ids_in=ids[:, :1].copy(), w_in=w[:, :1].copy(),
+                   mfma_min_tokens=big, mfma_small_min_tokens=small)
     np.testing.assert_array_equal(r2["y"], r1["y"])
 
 
-def test_batch_invariance():
-    """A token's output does not depend on the other tokens of the batch."""
+@pytest.mark.parametrize("big,small", SINGLE_PASS)
+def test_batch_invariance(big, small):
+    """A token's output does not depend on the other tokens of the batch
+    (within one pass)."""
     cfg = synth.CONFIGS["decode64"]
     spec, x, wr, b, blocks, shared, _ = oracle_then_pool(cfg)
     pool = upload_pool(spec, blocks, shared)
-    full = run_layer(pool, x, wr, b, cfg.k)
-    sub = np.arange(3, 64, 3)[:40] if len(np.arange(3, 64, 3)) >= 40 else np.arange(40) + 7
+    full = run_layer(pool, x, wr, b, cfg.k, mfma_min_tokens=big, mfma_small_min_tokens=small)
     sub = np.arange(40) + 7
-    part = run_layer(pool, x[sub], wr, b, cfg.k)
+    part = run_layer(pool, x[sub], wr, b, cfg.k, mfma_min_tokens=big,
+                     mfma_small_min_tokens=small)
     np.testing.assert_array_equal(part["ids"], full["ids"][sub])
     np.testing.assert_array_equal(part["y"], full["y"][sub])
     del pool
@@ -199,10 +216,11 @@ def test_zero_tokens_is_a_no_op():
     assert r["y"].shape == (0, spec.d) and r["counters"].sum() == 0
 
 
-@pytest.mark.parametrize("mfma_min_tokens", [None, 1, 2, 7, 33, -1])
+@pytest.mark.parametrize("big,small", [(None, None), (1, None), (2, 1), (7, 3), (33, 5),
+                                       (-1, None), (None, -1), (-1, -1), (-1, 40)])
 @pytest.mark.parametrize("N,k", [(40, 8), (100, 3), (129, 16)])
-def test_workspace_size_covers_every_threshold(N, k, mfma_min_tokens):
+def test_workspace_size_covers_every_threshold(N, k, big, small):
     """The workspace is sized once per (pool, N, k) and must hold the work
-    lists of every MFMA threshold a call can choose; run_layer allocates
+    lists of every pair of thresholds a call can choose; run_layer allocates
     exactly moe_workspace_size bytes."""
-    full_parity(tiny(n_tokens=N, k=min(k, 16)), mfma_min_tokens=mfma_min_tokens)
+    full_parity(tiny(n_tokens=N, k=min(k, 16)), mfma_min_tokens=big, mfma_small_min_tokens=small)
