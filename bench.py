@@ -12,10 +12,13 @@ drawn layer pools (each its own router and experts), as a decode pass walks
 through a model's layers, so the 256 MB Infinity Cache cannot serve a
 repeated working set.
 
-Prints one JSON line. `roofline` is for the gate/up GEMV kernel (the largest
-kernel of a decode step), timed with HIP events recorded on the library's
-stream around that kernel in every timed step. `cpu_baseline` is the CPU
-oracle timed on this host on a bounded sample of the same workload.
+Prints one JSON line. `roofline` is for the gate/up kernel of the pass
+(GEMV, 32-token or 128-token matrix-core) whose launches take longest, timed
+with HIP events that the kernel dispatches take on the library's stream, on
+an evenly spread sample of about 64 timed steps (event-taking launches cost
+the host tens of microseconds, so the other steps run without them).
+`cpu_baseline` is the CPU oracle timed on this host on a bounded sample of
+the same workload.
 """
 import argparse
 import ctypes
@@ -273,11 +276,18 @@ def main():
 
     # --- timed region -------------------------------------------------------
     K = args.steps
-    evs = [moe.ForwardOptions(*[hip.event() for _ in range(12)], 0, 0) for _ in range(K)]
+    # Kernel durations come from HIP events that the dispatches themselves
+    # take (start and end of each expert kernel) on a sample of the timed
+    # steps, evenly spread: about 64 of them, or every step of a short run.
+    # Event-taking launches cost the host tens of microseconds per step, so
+    # the other steps run without them.
+    every = max(1, K // 64)
+    sampled = [s_ for s_ in range(K) if s_ % every == 0]
+    evs = {s_: moe.ForwardOptions(*[hip.event() for _ in range(12)], 0, 0) for s_ in sampled}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s_ in range(K):
-        run(args.warmup + s_, evs[s_])
+        run(args.warmup + s_, evs.get(s_))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
@@ -291,9 +301,9 @@ def main():
     # per pass: event-timed gate/up and down launches of every timed step
     timed = {}
     for name, pre in (("gemv", ""), ("mfma", "mfma_"), ("small", "small_")):
-        timed[name] = ([ms(e, pre + "gateup_start", pre + "gateup_end") for e in evs],
-                       [ms(e, pre + "down_start", pre + "down_end") for e in evs])
-    for e in evs:
+        timed[name] = ([ms(evs[s_], pre + "gateup_start", pre + "gateup_end") for s_ in sampled],
+                       [ms(evs[s_], pre + "down_start", pre + "down_end") for s_ in sampled])
+    for e in evs.values():
         for fld, _ in moe.ForwardOptions._fields_[:12]:
             hip.L.hipEventDestroy(getattr(e, fld))
 
@@ -328,7 +338,7 @@ def main():
     # HBM-bound: algorithmic bytes = gate and up codes + scales of every
     # expert the pass handles, once. The 128-token pass is matrix-core bound:
     # algorithmic flops = 2 (gate, up) x 2 x d x f per token it handles.
-    steps_c = [calib[k_] for k_ in step_key]
+    steps_c = [calib[step_key[s_]] for s_ in sampled]  # the steps whose kernels were timed
     passes = {}
     for name in ("gemv", "small", "mfma"):
         gu_t, dn_t = timed[name]

@@ -78,21 +78,30 @@ typedef enum {
  * each other and read them as one block ("Storage, Memory, and I/O Formulas";
  * README "Never wait for the disk twice"); their container is int4 with
  * group scales (README "Get started") and the draft head is int8 (README
- * "Speculative decoding, honestly"). A block holds, in order:
- *   gate codes [f][d], up codes [f][d], down codes [d][f]
- *   gate scales [f][d/G], up scales [f][d/G], down scales [d][f/G]  (float32)
- * with f = d_ff, d = d_model and G = group (G == 0: one scale per row, so
- * d and f scales per gate/up and down row respectively). Codes are
- * wbits-bit integers stored offset-binary on the device (code + 8 per nibble,
- * code + 128 per byte); int4 packs element 2i in the low nibble of byte i.
- * moe_pack_expert writes this layout from the two's-complement canonical one.
+ * "Speculative decoding, honestly").
  *
- * Supported shapes: wbits 4 or 8; e = 32 (int4) or 16 (int8) elements per
- * 16-byte chunk; d and f multiples of e with d/e and f/e each either a power
- * of two from 2 to 64 or 64 times one of 1, 2, 3, 4, 6, 8 (int4: up to
- * d_model 16384); G == 0 or G a multiple of e
- * dividing both d and f; pool, shared and expert_bytes multiples of MOE_ALIGN,
- * expert_bytes >= moe_block_bytes(...).
+ * Canonical block (the input of moe_pack_expert), in order:
+ *   gate codes [f][d], up codes [f][d], down codes [d][f]   (row-major)
+ *   gate scales [f][d/G], up scales [f][d/G], down scales [d][f/G] (float32)
+ * with f = d_ff, d = d_model and G = group (G == 0: one scale per row).
+ * Codes are two's-complement wbits-bit integers; int4 packs element 2i in
+ * the low nibble of byte i.
+ *
+ * Device block (what the pool holds): the same sections at the same
+ * offsets, rearranged for the kernels. Each code matrix [R][K] is cut into
+ * 1024-byte units of 16 rows x U columns (U = 128 for int4, 64 for int8),
+ * stored by unit row then unit column: unit (rt, kb) at byte offset
+ * (rt * K/U + kb) * 1024 of the matrix. Slot L = r + 16 q (r = 0..15,
+ * q = 0..3) of a unit holds bytes 16 L .. 16 L + 15: the 16 canonical bytes
+ * of row 16 rt + r covering columns kb U + q U/4 .. + U/4, with the codes
+ * made offset-binary (code + 8 per nibble, code + 128 per byte). Each scale
+ * matrix [R][groups] becomes [R/16][groups][16]. moe_pack_expert writes this
+ * layout; moe_block_bytes is the same for both.
+ *
+ * Supported shapes: wbits 4 or 8; d and f multiples of 128 (int4) or 64
+ * (int8), at most 16384; G == 0 or G a multiple of 32 (int4) or 16 (int8)
+ * dividing both d and f; pool, shared and expert_bytes multiples of
+ * MOE_ALIGN, expert_bytes >= moe_block_bytes(...).
  */
 typedef struct {
     int32_t d_model;

@@ -7,6 +7,8 @@
 // status code instead.
 #include <string.h>
 
+#include <vector>
+
 #include "internal.h"
 
 namespace moe {
@@ -19,26 +21,6 @@ long long align_up(long long v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void *p) { return ((uintptr_t)p % kAlign) == 0; }
 
-bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
-
-// Split a row of `cols` codes into lanes-per-row x chunks-per-lane.
-bool row_split(int cols, int epc, int *lpr, int *cpl)
-{
-    if (cols <= 0 || cols % epc) return false;
-    const int cpr = cols / epc;
-    if (cpr >= kWave) {
-        if (cpr % kWave) return false;
-        const int c = cpr / kWave;
-        if (c != 1 && c != 2 && c != 3 && c != 4 && c != 6 && c != 8) return false;
-        *lpr = kWave;
-        *cpl = c;
-        return true;
-    }
-    if (!pow2(cpr) || cpr < 2) return false;
-    *lpr = cpr;
-    *cpl = 1;
-    return true;
-}
 
 long long n_scales(long long rows, long long cols, int group)
 {
@@ -141,16 +123,19 @@ moe_status resolve_geo(const moe_expert_pool *p, Geo *g)
     r.wbits = p->wbits;
     r.group = p->group;
     r.epc = p->wbits == 4 ? 32 : 16;
-    if (!row_split(r.d, r.epc, &r.gu_lpr, &r.gu_cpl)) return MOE_ESHAPE;
-    if (!row_split(r.f, r.epc, &r.dn_lpr, &r.dn_cpl)) return MOE_ESHAPE;
+    r.ucols = 4 * r.epc;
+    // whole units along both matrices' rows and columns; activations of one
+    // token row staged in LDS stay within budget
+    if (r.d % r.ucols || r.f % r.ucols) return MOE_ESHAPE;
+    if (r.d > kMaxModelDim || r.f > kMaxModelDim) return MOE_ESHAPE;
     if (r.group) {
         if (r.group % r.epc || r.d % r.group || r.f % r.group) return MOE_ESHAPE;
     }
-    r.row_gu = (long long)r.d * r.wbits / 8;
-    r.row_dn = (long long)r.f * r.wbits / 8;
-    r.spr_gu = r.group ? r.d / r.group : 1;
-    r.spr_dn = r.group ? r.f / r.group : 1;
-    const long long q_gu = (long long)r.f * r.row_gu, q_dn = (long long)r.d * r.row_dn;
+    r.kb_gu = r.d / r.ucols;
+    r.kb_dn = r.f / r.ucols;
+    r.ng_gu = r.group ? r.d / r.group : 1;
+    r.ng_dn = r.group ? r.f / r.group : 1;
+    const long long q_gu = (long long)r.f * r.d * r.wbits / 8, q_dn = q_gu;
     r.off_up = q_gu;
     r.off_dn = 2 * q_gu;
     r.off_gs = 2 * q_gu + q_dn;
@@ -379,12 +364,46 @@ moe_status moe_pack_expert(const void *canonical_block, const moe_expert_pool *s
     if (st != MOE_OK) return st;
     if (!canonical_block || !block_out) return MOE_EINVAL;
     const size_t bytes = moe_block_bytes(g.d, g.f, g.wbits, g.group);
-    const size_t q_bytes = (size_t)g.off_gs;  // the three code matrices come first
-    const uint8_t flip = g.wbits == 4 ? 0x88 : 0x80;  // two's complement -> offset binary
+    // build in a host copy, so that the output may be the input
+    std::vector<uint8_t> tmp(bytes);
     const uint8_t *src = static_cast<const uint8_t *>(canonical_block);
-    uint8_t *dst = static_cast<uint8_t *>(block_out);
-    for (size_t i = 0; i < q_bytes; ++i) dst[i] = src[i] ^ flip;
-    if (dst != src) memcpy(dst + q_bytes, src + q_bytes, bytes - q_bytes);
+    uint8_t *dst = tmp.data();
+    const uint8_t flip = g.wbits == 4 ? 0x88 : 0x80;  // two's complement -> offset binary
+    const uint64_t flip8 = 0x0101010101010101ULL * flip;
+    // the three code matrices: canonical row-major [R][K] -> units
+    struct Mat { long long off; int R, K; };
+    const Mat mats[3] = {{0, g.f, g.d}, {g.off_up, g.f, g.d}, {g.off_dn, g.d, g.f}};
+    for (const Mat &m : mats) {
+        const long long row_bytes = (long long)m.K * g.wbits / 8;
+        const int n_kb = m.K / g.ucols;
+        for (int rt = 0; rt < m.R / kUnitRows; ++rt)
+            for (int kb = 0; kb < n_kb; ++kb)
+                for (int slot = 0; slot < kWave; ++slot) {
+                    const int r = slot % kUnitRows, q = slot / kUnitRows;
+                    const long long row = (long long)rt * kUnitRows + r;
+                    const long long from = m.off + row * row_bytes +
+                                           ((long long)kb * g.ucols + (long long)q * g.epc) *
+                                               g.wbits / 8;
+                    const long long to = m.off + ((long long)rt * n_kb + kb) * kUnitBytes + 16LL * slot;
+                    uint64_t v[2];
+                    memcpy(v, src + from, 16);
+                    v[0] ^= flip8;
+                    v[1] ^= flip8;
+                    memcpy(dst + to, v, 16);
+                }
+    }
+    // scales: canonical [R][groups] -> [R / 16][groups][16]
+    struct Sc { long long off; int R, ng; };
+    const Sc scs[3] = {{g.off_gs, g.f, g.ng_gu}, {g.off_us, g.f, g.ng_gu}, {g.off_ds, g.d, g.ng_dn}};
+    for (const Sc &sc : scs)
+        for (int row = 0; row < sc.R; ++row)
+            for (int gi = 0; gi < sc.ng; ++gi) {
+                const long long from = sc.off + ((long long)row * sc.ng + gi) * 4;
+                const long long to = sc.off + (((long long)(row / kUnitRows) * sc.ng + gi) * kUnitRows +
+                                               row % kUnitRows) * 4;
+                memcpy(dst + to, src + from, 4);
+            }
+    memcpy(block_out, dst, bytes);
     return MOE_OK;
 }
 

@@ -43,6 +43,16 @@ template <int WB> struct Fmt;
 template <> struct Fmt<4> { static constexpr int epc = 32, xdw = 16; };
 template <> struct Fmt<8> { static constexpr int epc = 16, xdw = 8; };
 
+// (a & m) | o in one instruction (v_and_or_b32; the compiler emits an AND
+// and an OR for constant masks). m goes in a scalar register, o in a vector
+// register: one scalar operand per instruction.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
+    return r;
+}
+
 // The float16 pairs of one 16-byte chunk of offset-binary codes (1024 + code
 // + offset in each half), in the order the staged activations use.
 template <int WB>
@@ -53,24 +63,30 @@ __device__ __forceinline__ void extract_chunk(uint4 w, uint32_t *h)
     for (int q = 0; q < 4; ++q) {
         if constexpr (WB == 4) {
             const uint32_t d8 = d[q] >> 8;
-            h[4 * q + 0] = (d[q] & 0x000F000Fu) | kMagic;
-            h[4 * q + 1] = (d[q] & 0x00F000F0u) | kMagic;
-            h[4 * q + 2] = (d8 & 0x000F000Fu) | kMagic;
-            h[4 * q + 3] = (d8 & 0x00F000F0u) | kMagic;
+            h[4 * q + 0] = and_or(d[q], 0x000F000Fu, kMagic);
+            h[4 * q + 1] = and_or(d[q], 0x00F000F0u, kMagic);
+            h[4 * q + 2] = and_or(d8, 0x000F000Fu, kMagic);
+            h[4 * q + 3] = and_or(d8, 0x00F000F0u, kMagic);
         } else {
-            h[2 * q + 0] = (d[q] & 0x00FF00FFu) | kMagic;
-            h[2 * q + 1] = ((d[q] >> 8) & 0x00FF00FFu) | kMagic;
+            h[2 * q + 0] = and_or(d[q], 0x00FF00FFu, kMagic);
+            h[2 * q + 1] = and_or(d[q] >> 8, 0x00FF00FFu, kMagic);
         }
     }
 }
 
+// Sum of N float16 pair products in float32, as two interleaved chains (the
+// even and the odd pairs) added at the end, so that consecutive dot
+// instructions do not wait on each other.
 template <int N>
 __device__ __forceinline__ float dot_halves(const uint32_t *h, const uint32_t *xs)
 {
-    float acc = 0.0f;
+    float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-    for (int q = 0; q < N; ++q) acc = __builtin_amdgcn_fdot2(as_h2(h[q]), as_h2(xs[q]), acc, false);
-    return acc;
+    for (int q = 0; q < N; q += 2) {
+        a0 = __builtin_amdgcn_fdot2(as_h2(h[q]), as_h2(xs[q]), a0, false);
+        a1 = __builtin_amdgcn_fdot2(as_h2(h[q + 1]), as_h2(xs[q + 1]), a1, false);
+    }
+    return a0 + a1;
 }
 
 // float -> float16 with values below the smallest normal float16 set to zero,
@@ -131,56 +147,24 @@ __device__ __forceinline__ float stage_chunk(const float4 *src, float scale, uin
     }
 }
 
-constexpr int kGemvThreads = 256;
-constexpr int kGemvWaves = kGemvThreads / kWave;
 
-// staged activations per token per row chunk: XDW dwords, the correction and
-// the chunk's inverse scale
+// staged activations per token per chunk: XDW dwords, the correction and the
+// chunk's inverse scale
 __host__ __device__ constexpr int stage_bytes(int wb) { return (wb == 4 ? 16 : 8) * 4 + 8; }
 
 // rounds of (token, chunk) activation pairs loaded before the weight loads
-constexpr int kPreRounds = 2;
+__host__ __device__ constexpr int pre_rounds(int tb) { return tb == 1 ? 1 : 2; }
 
-// rows per wave per row block
-__host__ __device__ constexpr int rows_of(bool gateup, int cpl)
-{
-    return gateup ? (cpl == 1 ? 2 : 1) : (cpl == 1 ? 4 : (cpl <= 3 ? 2 : 1));
-}
+// units a wave holds in registers at a time: 4, 6 or 12 (a template parameter)
+constexpr int kUnitBatch = 12;
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
-                                                              0xF, 0xF, true));
-}
+// below this many 4-wave workgroups in a pass, single-token rows of 17..48
+// units go to 8-wave workgroups instead (more waves per unit row to overlap
+// the products with the loads when few items fill the chip)
+constexpr long long kFewWorkgroups = 1024;
 
-__device__ __forceinline__ float lane_f(float v, int l)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
-}
-
-// Sum over aligned groups of L lanes (L a power of two <= 64); the result is
-// valid in the first lane of each group.
-template <int L>
-__device__ __forceinline__ float seg_sum(float v)
-{
-    if constexpr (L >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
-    if constexpr (L >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
-    if constexpr (L >= 8) v += dpp<0x141>(v);   // row_half_mirror
-    if constexpr (L >= 16) v += dpp<0x140>(v);  // row_mirror
-    if constexpr (L == 32) v += __shfl_xor(v, 16, kWave);
-    if constexpr (L == 64) v = (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
-    return v;
-}
-
-__device__ __forceinline__ float wave_max_dpp(float v)
-{
-    v = fmaxf(v, dpp<0xB1>(v));
-    v = fmaxf(v, dpp<0x4E>(v));
-    v = fmaxf(v, dpp<0x141>(v));
-    v = fmaxf(v, dpp<0x140>(v));
-    return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
-}
+// LDS a GEMV workgroup may use for staged activations
+constexpr int kStageBudget = 150 * 1024;
 
 __device__ __forceinline__ int wave_incl_scan(int v)
 {
@@ -195,8 +179,7 @@ __device__ __forceinline__ int wave_incl_scan(int v)
 
 struct GemvArgs {
     Fwd f;
-    int n_rbg;              // workgroups per item
-    int iters;              // row blocks per workgroup
+    int n_wg;               // workgroups per item
     int plan_here;          // gate/up pass: 0 read the work list, 1 scan a union of
                             // <= 64 in-kernel, 2 one item per union slot (n_tokens <= TB)
 };
@@ -252,41 +235,41 @@ __device__ int find_item(const Fwd &f, int item_idx, Item *out)
     return nsh + __builtin_amdgcn_readlane(incl, kWave - 1);
 }
 
-// One workgroup (4 waves) works on one item: up to TB tokens of one expert.
-// The item's activations are staged once in LDS (float16, scaled by a power of
-// two per chunk, in the order the dot product consumes them). Each wave then
-// owns R rows (times 64/LPR rows that share a wave when rows are short) per
-// row block; every lane reads CPL 16-byte chunks of each row, one 128-bit load
-// per chunk, with the next block's loads issued before the current block is
-// computed. Row sums are added across lanes with DPP and lane reads.
+// One workgroup (4 waves) computes 4/KS unit rows (16 output rows each) of
+// one work item: up to TB tokens of one expert. KS waves share a unit row,
+// each taking every KS-th unit along it. The item's activations are staged
+// once in LDS (float16, each chunk scaled by a power of two, in the order the
+// dot product consumes them). Each lane reads one 16-byte slot per unit (a
+// wave reads the whole 1 KB unit), turns its 32 (int4) or 16 (int8) codes
+// into float16 pairs once and takes dot products with every token's chunk.
+// Partial sums are added over the four lanes of a row with lane shuffles and
+// over the KS waves of a unit row in LDS, always in the same order.
 //
 // gate/up pass with a union of at most 64 experts: the workgroup finds its
 // item from the union itself (no separate planning launch) and records the
 // item list for the down pass.
-template <bool GATEUP, int WB, int CPL, int LPR, int TB>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs ga)
+template <bool GATEUP, int WB, int TB, int NW, int KS, int UB>
+__global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
 {
+    constexpr int kGemvThreads = NW * kWave;
     constexpr int XDW = Fmt<WB>::xdw, EPC = Fmt<WB>::epc;
     constexpr int XQ = XDW / 4;              // uint4 per staged chunk
-    constexpr int RPI = kWave / LPR;         // rows sharing a wave
-    constexpr int NCH = CPL * LPR;           // chunks per row
-    constexpr int R = rows_of(GATEUP, CPL);
-    constexpr int ROWS = kGemvWaves * R * RPI;  // rows per row block
-    constexpr int NM = GATEUP ? 2 : 1;          // gate and up, or down
-    static_assert(CPL == 1 || LPR == kWave, "multi-chunk lanes need full-wave rows");
+    constexpr int UC = 4 * EPC;              // columns per unit
+    constexpr int NM = GATEUP ? 2 : 1;       // gate and up, or down
+    constexpr int TPW = NW / KS;             // unit rows per workgroup
 
-    extern __shared__ uint4 lds_x[];          // [TB][XQ][NCH] staged activations
-    float2 *lds_ci = reinterpret_cast<float2 *>(lds_x + TB * XQ * NCH);  // [TB][NCH]
+    extern __shared__ uint4 lds_x[];         // [TB][XQ][NCH] staged activations
     __shared__ Item s_item;
     __shared__ int s_expert;
+    __shared__ float red[NW][TB][NM][kUnitRows];
 
     const Fwd &f = ga.f;
     const Geo &g = f.g;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int item_idx = blockIdx.x / ga.n_rbg;
-    const int rbg = blockIdx.x % ga.n_rbg;
+    const int item_idx = blockIdx.x / ga.n_wg;
+    const int wg = blockIdx.x % ga.n_wg;
     // The expert is needed first (the weight loads only depend on it); the
-    // item's tokens are resolved after those loads are issued when possible.
+    // item's tokens are resolved after when possible.
     int expert;
     Item it;
     bool resolved = true;
@@ -304,7 +287,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs ga)
                 const int nu = min(max(*f.n_union, 0), lim);   // both loads in flight together
                 const int e = rel < lim ? f.union_ids[rel] : -1;
                 s_expert = (rel < nu && e >= 0 && e < g.E) ? e : -2;
-                if (rbg == 0 && rel == 0) *f.n_items = nsh + nu;
+                if (wg == 0 && rel == 0) *f.n_items = nsh + nu;
             }
             __syncthreads();
             expert = s_expert;
@@ -314,10 +297,10 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs ga)
         if (wave == 0) {
             const int total = find_item<TB>(f, item_idx, &s_item);
             if (lane == 0) {
-                if (rbg == 0 && s_item.count > 0) f.items[item_idx] = s_item;
+                if (wg == 0 && s_item.count > 0) f.items[item_idx] = s_item;
                 // the first routed item's first workgroup publishes the total
                 const int nsh = f.has_shared ? (f.N + TB - 1) / TB : 0;
-                if (rbg == 0 && item_idx == nsh) *f.n_items = min(total, f.max_items);
+                if (wg == 0 && item_idx == nsh) *f.n_items = min(total, f.max_items);
             }
         }
         __syncthreads();
@@ -331,39 +314,6 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs ga)
         expert = it.expert;
     }
     if (resolved && it.count <= 0) return;  // no such item: uniform exit
-    const uint8_t *blk = expert >= 0 ? f.pool + (size_t)expert * f.stride : f.shared;
-    const int seg = lane / LPR, li = lane % LPR;
-    const int cols = GATEUP ? g.d : g.f;
-    const int rows = GATEUP ? g.f : g.d;
-    const long long row_bytes = GATEUP ? g.row_gu : g.row_dn;
-    const long long spr = GATEUP ? g.spr_gu : g.spr_dn;
-    const uint8_t *q0 = blk + (GATEUP ? 0 : g.off_dn);
-    const uint8_t *q1 = blk + g.off_up;
-    const uint8_t *s0 = blk + (GATEUP ? g.off_gs : g.off_ds);
-    const uint8_t *s1 = blk + g.off_us;
-    const float *in = GATEUP ? f.x : f.h;
-    float *out = GATEUP ? f.h : f.o;
-
-    uint4 w[R][CPL][NM];
-    float sc[R][CPL][NM];
-    auto load_block = [&](int blk_idx, uint4 (&wv)[R][CPL][NM], float (&sv)[R][CPL][NM]) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const long long row = min(blk_idx * ROWS + (wave * R + r) * RPI + seg, rows - 1);
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-                const int c = li + j * LPR;
-                const long long grp = g.group ? (long long)c * EPC / g.group : 0;
-                wv[r][j][0] = *reinterpret_cast<const uint4 *>(q0 + row * row_bytes + c * 16);
-                sv[r][j][0] = *reinterpret_cast<const float *>(s0 + (row * spr + grp) * 4);
-                if (GATEUP) {
-                    wv[r][j][NM - 1] = *reinterpret_cast<const uint4 *>(q1 + row * row_bytes + c * 16);
-                    sv[r][j][NM - 1] = *reinterpret_cast<const float *>(s1 + (row * spr + grp) * 4);
-                }
-            }
-        }
-    };
-    // ---- the item's tokens -----------------------------------------------------
     if (!resolved) {
         if (expert < 0) {
             it.expert = -1;
@@ -390,10 +340,52 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs ga)
             __syncthreads();
             it = s_item;
         }
-        if (rbg == 0 && tid == 0 && it.count > 0) f.items[item_idx] = it;
+        if (wg == 0 && tid == 0 && it.count > 0) f.items[item_idx] = it;
         if (it.count <= 0) return;  // uniform: inconsistent offsets give no tokens
     }
     const int count = min(it.count, TB);
+
+    const uint8_t *blk = expert >= 0 ? f.pool + (size_t)expert * f.stride : f.shared;
+    const int K = GATEUP ? g.d : g.f;        // contraction length
+    const int rows = GATEUP ? g.f : g.d;     // output rows
+    const int NCH = K / EPC;                 // chunks per row
+    const int n_kb = K / UC;                 // units per row
+    const int ng = GATEUP ? g.ng_gu : g.ng_dn;
+    float2 *lds_ci = reinterpret_cast<float2 *>(lds_x + TB * XQ * NCH);  // [TB][NCH]
+    const float *in = GATEUP ? f.x : f.h;
+    float *out = GATEUP ? f.h : f.o;
+    const int r16 = lane % kUnitRows, q = lane / kUnitRows;
+    const int tw = wave / KS, slice = wave % KS;   // unit row in the workgroup, K slice
+    const int n_rt = rows / kUnitRows;
+    const int rt = wg * TPW + tw;
+    const bool live = rt < n_rt;                    // uniform per wave
+    const size_t unit0 = (size_t)min(rt, n_rt - 1) * n_kb * kUnitBytes + (size_t)lane * 16;
+    const uint8_t *q0 = blk + (GATEUP ? 0 : g.off_dn) + unit0;
+    const uint8_t *q1 = blk + g.off_up + unit0;
+    const size_t sc0 = (size_t)min(rt, n_rt - 1) * ng * kUnitRows + r16;
+    const float *s0 = reinterpret_cast<const float *>(blk + (GATEUP ? g.off_gs : g.off_ds)) + sc0;
+    const float *s1 = reinterpret_cast<const float *>(blk + g.off_us) + sc0;
+
+    // units kb = slice + KS * j of this wave, UB at a time. Every load of a
+    // batch is issued (past the wave's last unit it reads that unit again),
+    // so the number of loads in flight is the same on every path and each
+    // unit's products wait for that unit only.
+    const int n_mine = live ? (n_kb - slice + KS - 1) / KS : 0;
+    uint4 w[UB][NM];
+    float sc[UB][NM];
+    auto load_units = [&](int j0) {
+#pragma unroll
+        for (int u = 0; u < UB; ++u) {
+            const int kb = slice + KS * max(min(j0 + u, n_mine - 1), 0);
+            const int grp = g.group ? (kb * UC + q * EPC) / g.group : 0;
+            w[u][0] = *reinterpret_cast<const uint4 *>(q0 + (size_t)kb * kUnitBytes);
+            sc[u][0] = s0[grp * kUnitRows];
+            if (GATEUP) {
+                w[u][NM - 1] = *reinterpret_cast<const uint4 *>(q1 + (size_t)kb * kUnitBytes);
+                sc[u][NM - 1] = s1[grp * kUnitRows];
+            }
+        }
+    };
 
     // ---- stage the activations: loads first, then the weights ----------------
     // (token, chunk) pairs are spread over the threads; a round covers one
@@ -402,11 +394,10 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs ga)
     // [2^13, 2^14) (exact, undone per chunk with the group scale). The first
     // rounds are loaded before the weight loads are issued, so their data do
     // not wait behind the weights.
-    constexpr int NPAIR = TB * NCH;
-    constexpr int ROUNDS = (NPAIR + kGemvThreads - 1) / kGemvThreads;
-    constexpr int PRE = ROUNDS < kPreRounds ? ROUNDS : kPreRounds;
-    auto pair_src = [&](int q) -> const float * {
-        const int i = q / NCH, c = q % NCH;
+    const int NPAIR = TB * NCH;
+    const int ROUNDS = (NPAIR + kGemvThreads - 1) / kGemvThreads;
+    auto pair_src = [&](int pq) -> const float * {
+        const int i = pq / NCH, c = pq % NCH;
         if (i >= count) return nullptr;
         const int p = it.p0 + i;
         size_t r;
@@ -416,22 +407,22 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs ga)
             r = (size_t)(p - f.A);
         else  // values read from the permutation are clamped into range
             r = f.N == 1 ? 0 : (size_t)(min(max(f.perm[p], 0), f.A - 1) / f.k);
-        return in + r * cols + (size_t)c * EPC;
+        return in + r * K + (size_t)c * EPC;
     };
+    constexpr int PRE = pre_rounds(TB);
     float4 xv[PRE][EPC / 4];
 #pragma unroll
     for (int r = 0; r < PRE; ++r) {
-        const int q = tid + r * kGemvThreads;
-        const float *src = q < NPAIR ? pair_src(q) : nullptr;
+        const int pq = tid + r * kGemvThreads;
+        const float *src = pq < NPAIR ? pair_src(pq) : nullptr;
         if (src) {
 #pragma unroll
             for (int v = 0; v < EPC / 4; ++v) xv[r][v] = reinterpret_cast<const float4 *>(src)[v];
         }
     }
-    const int first_blk = rbg * ga.iters;
-    load_block(first_blk, w, sc);
-    auto stage_pair = [&](int q, const float4 (&v)[EPC / 4]) {
-        const int i = q / NCH, c = q % NCH;
+    load_units(0);
+    auto stage_pair = [&](int pq, const float4 (&v)[EPC / 4]) {
+        const int i = pq / NCH, c = pq % NCH;
         float m = 0.0f;
 #pragma unroll
         for (int u = 0; u < EPC / 4; ++u)
@@ -453,102 +444,94 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs ga)
     };
 #pragma unroll
     for (int r = 0; r < PRE; ++r) {
-        const int q = tid + r * kGemvThreads;
-        if (q < NPAIR && q / NCH < count) stage_pair(q, xv[r]);
+        const int pq = tid + r * kGemvThreads;
+        if (pq < NPAIR && pq / NCH < count) stage_pair(pq, xv[r]);
     }
 #pragma unroll 1
     for (int r = PRE; r < ROUNDS; ++r) {
-        const int q = tid + r * kGemvThreads;
-        const float *src = q < NPAIR ? pair_src(q) : nullptr;
+        const int pq = tid + r * kGemvThreads;
+        const float *src = pq < NPAIR ? pair_src(pq) : nullptr;
         if (src) {
             float4 v[EPC / 4];
 #pragma unroll
             for (int u = 0; u < EPC / 4; ++u) v[u] = reinterpret_cast<const float4 *>(src)[u];
-            stage_pair(q, v);
+            stage_pair(pq, v);
         }
     }
     __syncthreads();
-    int orow[TB];
-#pragma unroll
-    for (int i = 0; i < TB; ++i) {
-        const int p = it.p0 + min(i, count - 1);
-        orow[i] = (!GATEUP && it.expert >= 0) ? min(max(f.perm[p], 0), f.A - 1) : p;
-    }
 
-    // ---- stream the rows ------------------------------------------------------
-    const int n_blk = (rows + ROWS - 1) / ROWS;
-    const int last_blk = min(first_blk + ga.iters, n_blk);
-    for (int b = first_blk; b < last_blk; ++b) {
-        uint4 wn[R][CPL][NM];
-        float sn[R][CPL][NM];
-        if (b + 1 < last_blk) load_block(b + 1, wn, sn);
-        float acc[R][TB][NM];
+    // ---- stream this wave's units ---------------------------------------------
+    float acc[TB][NM];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+    for (int i = 0; i < TB; ++i)
 #pragma unroll
-            for (int i = 0; i < TB; ++i)
+        for (int m = 0; m < NM; ++m) acc[i][m] = 0.0f;
+#pragma unroll 1
+    for (int j0 = 0; j0 < n_mine; j0 += UB) {
+        if (j0 > 0) load_units(j0);  // the first batch was issued before staging
 #pragma unroll
-                for (int m = 0; m < NM; ++m) acc[r][i][m] = 0.0f;
+        for (int u = 0; u < UB; ++u) {
+            if (j0 + u >= n_mine) break;
+            const int c = (slice + KS * (j0 + u)) * 4 + q;  // this lane's chunk
+            // codes -> float16 once per unit, then used for every token
+            uint32_t hw[NM][XDW];
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const int c = li + j * LPR;
-            uint32_t hw[R][NM][XDW];
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int m = 0; m < NM; ++m) extract_chunk<WB>(w[r][j][m], hw[r][m]);
+            for (int m = 0; m < NM; ++m) extract_chunk<WB>(w[u][m], hw[m]);
 #pragma unroll
             for (int i = 0; i < TB; ++i) {
                 if (i >= count) break;
                 uint32_t xs[XDW];
 #pragma unroll
-                for (int q = 0; q < XQ; ++q) {
-                    const uint4 v = lds_x[(i * XQ + q) * NCH + c];
-                    xs[4 * q] = v.x;
-                    xs[4 * q + 1] = v.y;
-                    xs[4 * q + 2] = v.z;
-                    xs[4 * q + 3] = v.w;
+                for (int qq = 0; qq < XQ; ++qq) {
+                    const uint4 v = lds_x[(i * XQ + qq) * NCH + c];
+                    xs[4 * qq] = v.x;
+                    xs[4 * qq + 1] = v.y;
+                    xs[4 * qq + 2] = v.z;
+                    xs[4 * qq + 3] = v.w;
                 }
-                const float2 ci = lds_ci[i * NCH + c];
+                const float2 ci = lds_ci[i * NCH + c];  // correction, inverse scale
 #pragma unroll
-                for (int r = 0; r < R; ++r)
-#pragma unroll
-                    for (int m = 0; m < NM; ++m)
-                        acc[r][i][m] = fmaf(sc[r][j][m] * ci.y,
-                                            dot_halves<XDW>(hw[r][m], xs) - ci.x, acc[r][i][m]);
+                for (int m = 0; m < NM; ++m)
+                    acc[i][m] = fmaf(sc[u][m] * ci.y, dot_halves<XDW>(hw[m], xs) - ci.x,
+                                     acc[i][m]);
             }
         }
+    }
+
+    // ---- row sums: the four lanes of a row, then the waves of a unit row -----
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int row = b * ROWS + (wave * R + r) * RPI + seg;
+    for (int i = 0; i < TB; ++i)
 #pragma unroll
-            for (int i = 0; i < TB; ++i) {
-                if (i >= count) break;
-                float v[NM];
-#pragma unroll
-                for (int m = 0; m < NM; ++m) v[m] = seg_sum<LPR>(acc[r][i][m]);
-                if (li == 0 && row < rows) {
-                    float o;
-                    if (GATEUP) {
-                        const float gv = v[0], uv = v[NM - 1];
-                        o = gv / (1.0f + expf(-gv)) * uv;
-                    } else {
-                        o = v[0];
-                    }
-                    out[(size_t)orow[i] * rows + row] = o;
-                }
-            }
+        for (int m = 0; m < NM; ++m) {
+            float v = acc[i][m];
+            v += __shfl_xor(v, 16, kWave);
+            v += __shfl_xor(v, 32, kWave);
+            if (lane < kUnitRows) red[wave][i][m][lane] = v;
         }
-        if (b + 1 < last_blk) {
+    __syncthreads();
+    if (tid < TPW * TB * kUnitRows) {
+        const int t = tid / (TB * kUnitRows), i = (tid / kUnitRows) % TB, r = tid % kUnitRows;
+        const int row_tile = wg * TPW + t;
+        if (i < count && row_tile < n_rt) {
+            float v[NM];
 #pragma unroll
-            for (int r = 0; r < R; ++r)
+            for (int m = 0; m < NM; ++m) {
+                float sum = 0.0f;
 #pragma unroll
-                for (int j = 0; j < CPL; ++j)
-#pragma unroll
-                    for (int m = 0; m < NM; ++m) {
-                        w[r][j][m] = wn[r][j][m];
-                        sc[r][j][m] = sn[r][j][m];
-                    }
+                for (int ww = 0; ww < KS; ++ww) sum += red[t * KS + ww][i][m][r];
+                v[m] = sum;
+            }
+            const int p = it.p0 + i;
+            const int orow = (!GATEUP && it.expert >= 0) ? min(max(f.perm[p], 0), f.A - 1) : p;
+            const int row = row_tile * kUnitRows + r;
+            float o;
+            if (GATEUP) {
+                const float gv = v[0], uv = v[NM - 1];
+                o = gv / (1.0f + expf(-gv)) * uv;
+            } else {
+                o = v[0];
+            }
+            out[(size_t)orow * rows + row] = o;
         }
     }
 }
@@ -679,123 +662,66 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
 
 // ---- dispatch -------------------------------------------------------------
 
-template <bool GATEUP, int WB, int CPL>
-constexpr int rows_per_block(int lpr)
-{
-    return kGemvWaves * rows_of(GATEUP, CPL) * (kWave / lpr);
-}
-
-struct Launch {
-    int n_rbg, iters;
-    long long blocks;
-};
-
-// Workgroups the device keeps resident at once for a kernel (a per-process
-// cache of the occupancy query; 0 when the query fails).
-template <typename K>
-long long resident_blocks(K kernel, size_t lds)
-{
-    static long long cache[16] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 0;
-    if (cache[dev] == 0) {
-        int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kGemvThreads, lds) !=
-                hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return 0;
-        cache[dev] = (long long)per_cu * cus;
-    }
-    return cache[dev];
-}
-
-Launch plan_launch(int rows, int rows_per_blk, int max_items, long long resident = 0)
-{
-    Launch L;
-    const long long n_blk = (rows + rows_per_blk - 1) / rows_per_blk;
-    // one workgroup per row block while the grid fits the chip in one
-    // resident round; beyond that each workgroup takes several row blocks,
-    // loading the next one while it computes the current one
-    const long long cap = resident > 0 ? resident : 2048;
-    long long iters = ((long long)max_items * n_blk + cap - 1) / cap;
-    iters = iters < 1 ? 1 : (iters > 8 ? 8 : iters);
-    L.iters = (int)iters;
-    L.n_rbg = (int)((n_blk + iters - 1) / iters);
-    L.blocks = (long long)max_items * L.n_rbg;
-    return L;
-}
-
-template <bool GATEUP, int WB, int CPL, int LPR, int TB>
+template <bool GATEUP, int WB, int TB, int NW, int KS, int UB>
 hipError_t run_gemv(GemvArgs a, hipStream_t s)
 {
-    constexpr int ROWS = kGemvWaves * rows_of(GATEUP, CPL) * (kWave / LPR);
-    const size_t lds = (size_t)TB * CPL * LPR * stage_bytes(WB);
-    const Launch L = plan_launch(GATEUP ? a.f.g.f : a.f.g.d, ROWS, a.f.max_items,
-                                 resident_blocks(gemv_kernel<GATEUP, WB, CPL, LPR, TB>, lds));
-    a.n_rbg = L.n_rbg;
-    a.iters = L.iters;
-    if (L.blocks <= 0) return hipSuccess;
-    if (L.blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    const Geo &g = a.f.g;
+    const int K = GATEUP ? g.d : g.f;
+    const int rows = GATEUP ? g.f : g.d;
+    const size_t lds = (size_t)TB * (K / Fmt<WB>::epc) * stage_bytes(WB);
+    constexpr int TPW = NW / KS;
+    a.n_wg = (rows / kUnitRows + TPW - 1) / TPW;
+    const long long blocks = (long long)a.f.max_items * a.n_wg;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFFLL || lds > (size_t)kStageBudget) return hipErrorInvalidValue;
     const hipEvent_t *ev = GATEUP ? a.f.ev_gu : a.f.ev_dn;
     if (ev[0] || ev[1])  // events taken by the dispatch itself, around this kernel only
-        hipExtLaunchKernelGGL((gemv_kernel<GATEUP, WB, CPL, LPR, TB>), dim3((unsigned)L.blocks),
-                              dim3(kGemvThreads), lds, s, ev[0], ev[1], 0, a);
+        hipExtLaunchKernelGGL((gemv_kernel<GATEUP, WB, TB, NW, KS, UB>), dim3((unsigned)blocks),
+                              dim3(NW * kWave), lds, s, ev[0], ev[1], 0, a);
     else
-        hipLaunchKernelGGL((gemv_kernel<GATEUP, WB, CPL, LPR, TB>), dim3((unsigned)L.blocks),
-                           dim3(kGemvThreads), lds, s, a);
+        hipLaunchKernelGGL((gemv_kernel<GATEUP, WB, TB, NW, KS, UB>), dim3((unsigned)blocks),
+                           dim3(NW * kWave), lds, s, a);
     return hipGetLastError();
 }
 
-template <bool GATEUP, int WB, int CPL, int LPR>
-hipError_t run_tb(const GemvArgs &a, hipStream_t s)
+// How a unit row is shared: every wave of a 4-wave workgroup on one unit row
+// (fewer when the rows are shorter than 4 units), holding 4 or 12 units at a
+// time; when few workgroups would fill the chip, single-token rows of up to
+// 48 units on 8 waves of 6 units.
+template <bool GATEUP, int WB, int TB>
+hipError_t run_ks(const GemvArgs &a, hipStream_t s)
 {
-    switch (a.f.tb) {
-    case 1: return run_gemv<GATEUP, WB, CPL, LPR, 1>(a, s);
-    case 2: return run_gemv<GATEUP, WB, CPL, LPR, 2>(a, s);
-    case 4:
-        if constexpr (4 * CPL * LPR * stage_bytes(WB) <= 65536)
-            return run_gemv<GATEUP, WB, CPL, LPR, 4>(a, s);
-        return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
-    }
+    const int K = GATEUP ? a.f.g.d : a.f.g.f;
+    const int rows = GATEUP ? a.f.g.f : a.f.g.d;
+    const int n_kb = K / (4 * Fmt<WB>::epc);
+    if (n_kb == 1) return run_gemv<GATEUP, WB, TB, 4, 1, 4>(a, s);
+    if (n_kb < 4) return run_gemv<GATEUP, WB, TB, 4, 2, 4>(a, s);
+    if (n_kb <= 16) return run_gemv<GATEUP, WB, TB, 4, 4, 4>(a, s);
+    const long long wgs = (long long)a.f.max_items * (rows / kUnitRows);
+    if (TB == 1 && n_kb <= 48 && wgs < kFewWorkgroups) return run_gemv<GATEUP, WB, TB, 8, 8, 6>(a, s);
+    return run_gemv<GATEUP, WB, TB, 4, 4, kUnitBatch>(a, s);
 }
 
 template <bool GATEUP, int WB>
-hipError_t dispatch_shape(int cpl, int lpr, const GemvArgs &a, hipStream_t s)
+hipError_t run_tb(const GemvArgs &a, hipStream_t s)
 {
-    if (lpr == kWave) {
-        switch (cpl) {
-        case 1: return run_tb<GATEUP, WB, 1, 64>(a, s);
-        case 2: return run_tb<GATEUP, WB, 2, 64>(a, s);
-        case 3: return run_tb<GATEUP, WB, 3, 64>(a, s);
-        case 4: return run_tb<GATEUP, WB, 4, 64>(a, s);
-        case 6: return run_tb<GATEUP, WB, 6, 64>(a, s);
-        case 8: return run_tb<GATEUP, WB, 8, 64>(a, s);
-        default: return hipErrorInvalidValue;
-        }
-    }
-    if (cpl != 1) return hipErrorInvalidValue;
-    switch (lpr) {
-    case 2: return run_tb<GATEUP, WB, 1, 2>(a, s);
-    case 4: return run_tb<GATEUP, WB, 1, 4>(a, s);
-    case 8: return run_tb<GATEUP, WB, 1, 8>(a, s);
-    case 16: return run_tb<GATEUP, WB, 1, 16>(a, s);
-    case 32: return run_tb<GATEUP, WB, 1, 32>(a, s);
+    switch (a.f.tb) {
+    case 1: return run_ks<GATEUP, WB, 1>(a, s);
+    case 2: return run_ks<GATEUP, WB, 2>(a, s);
+    case 4: return run_ks<GATEUP, WB, 4>(a, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-int gemv_tokens_per_item(const Geo &g, int n_tokens)
+int gemv_tokens_per_item(const Geo &g, int max_tokens)
 {
-    // the smallest of 1, 2, 4 that covers the batch, within 64 KB of staged
-    // activations for both passes (an expert has at most n_tokens tokens)
-    int tb = n_tokens <= 1 ? 1 : (n_tokens <= 2 ? 2 : 4);
-    const int worst = (g.gu_cpl * g.gu_lpr > g.dn_cpl * g.dn_lpr ? g.gu_cpl * g.gu_lpr
-                                                                  : g.dn_cpl * g.dn_lpr) *
-                      stage_bytes(g.wbits);
-    while (tb > 1 && tb * worst > 65536) tb /= 2;
+    // the smallest of 1, 2, 4 that covers the largest group the GEMV pass
+    // gets, within the LDS budget of staged activations for both passes
+    int tb = max_tokens <= 1 ? 1 : (max_tokens <= 2 ? 2 : 4);
+    const int nch = (g.d > g.f ? g.d : g.f) / g.epc;
+    while (tb > 1 && tb * nch * stage_bytes(g.wbits) > kStageBudget) tb /= 2;
     return tb;
 }
 
@@ -803,10 +729,10 @@ hipError_t launch_gateup(const Fwd &f, hipStream_t s)
 {
     GemvArgs a;
     a.f = f;
-    a.n_rbg = a.iters = 0;
-    // a union of at most 64 experts is scanned inside the kernel when no
-    // expert goes to the MFMA pass; otherwise one planning workgroup builds
-    // both work lists first
+    a.n_wg = 0;
+    // a union of at most 64 experts is scanned inside the kernel when every
+    // expert is on the GEMV pass; otherwise one planning workgroup builds the
+    // work lists first
     const int max_union = f.A < f.g.E ? f.A : f.g.E;
     a.plan_here = max_union <= kWave && f.max_mitems == 0 && f.max_sitems == 0
                       ? (f.N <= f.tb ? 2 : 1)
@@ -816,18 +742,16 @@ hipError_t launch_gateup(const Fwd &f, hipStream_t s)
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    return f.g.wbits == 4 ? dispatch_shape<true, 4>(f.g.gu_cpl, f.g.gu_lpr, a, s)
-                          : dispatch_shape<true, 8>(f.g.gu_cpl, f.g.gu_lpr, a, s);
+    return f.g.wbits == 4 ? run_tb<true, 4>(a, s) : run_tb<true, 8>(a, s);
 }
 
 hipError_t launch_down(const Fwd &f, hipStream_t s)
 {
     GemvArgs a;
     a.f = f;
-    a.n_rbg = a.iters = 0;
+    a.n_wg = 0;
     a.plan_here = 0;
-    return f.g.wbits == 4 ? dispatch_shape<false, 4>(f.g.dn_cpl, f.g.dn_lpr, a, s)
-                          : dispatch_shape<false, 8>(f.g.dn_cpl, f.g.dn_lpr, a, s);
+    return f.g.wbits == 4 ? run_tb<false, 4>(a, s) : run_tb<false, 8>(a, s);
 }
 
 hipError_t launch_combine(const float *o, const float *w, int N, int k, int d, int A,

@@ -1,5 +1,6 @@
 // expert_mfma.hip - expert math for token groups large enough to be a dense
-// contraction (prefill, the shared expert of a large batch, hot experts).
+// contraction (prefill, the shared expert of a batch, experts hit by several
+// tokens).
 //
 // Colibri pages: "Public Colibri Observation and Revision Ledger", section
 // "Exact Architecture and Data-Flow Reconstruction" (three-matrix expert MLP,
@@ -7,22 +8,23 @@
 // scales).
 //
 // For one expert and up to MT of its tokens (MT = 128 for large groups, 32
-// for small ones), a workgroup computes 128 output rows (of gate and up
-// together, or of down) over the full contraction:
+// for small ones), a workgroup of 4 waves computes 128 output rows (of gate
+// and up together, or of down) over the full contraction:
 //   gate/up:  h[p][r] = silu(sum_c Wg[r][c] x_t[c]) * (sum_c Wu[r][c] x_t[c])
 //   down:     o[out(p)][r] = sum_c Wd[r][c] h[p][c]
-// on v_mfma_f32_32x32x16_f16 (float16 products, float32 accumulation):
-//  * activations (x or h, float32) are converted to float16 and staged in LDS,
-//    64 columns at a time, double-buffered;
-//  * every lane reads its weights straight from HBM, 16 bytes (32 int4 codes
-//    of one row) per step, and expands them in registers: OR into the
-//    mantissa of 1024 (exact), subtract 1032 (exact), multiply by the group
-//    scale (one float16 rounding);
+// on v_mfma_f32_16x16x32_f16 (float16 products, float32 accumulation):
+//  * the weights are read in their 1 KB units (16 rows x 128 int4 columns):
+//    one 16-byte load per lane is one unit, and the lane's 32 codes are its
+//    weight operand for four MFMA steps; they are expanded in registers: OR
+//    into the mantissa of 1024 (exact), subtract 1032 (exact), multiply by
+//    the group scale (one float16 rounding);
 //  * within each 8-column group the columns are taken in the order
 //    0,4,1,5,2,6,3,7 on both operands, which lets one 32-bit word of codes
 //    feed one MFMA operand without shuffles;
-//  * each of the 4 waves owns 32 rows and all MT tokens (MT/32 blocks of
-//    32 x 32); loads run two steps ahead of the matrix cores.
+//  * activations (x or h, float32) are converted to float16 and staged in LDS
+//    one unit (128 columns) at a time, double-buffered, loaded one step ahead;
+//  * each wave owns two unit rows (32 weight rows) and all MT tokens; weight
+//    loads run two steps ahead of the matrix cores.
 // Workgroups are mapped so that those sharing an expert (and so its weights
 // and its tokens) land on the same XCD and share its L2.
 #include <hip/hip_ext.h>
@@ -34,13 +36,14 @@ namespace {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kNW = 32;             // rows per wave
-constexpr int kNT = (kThreads / 64) * kNW;  // rows per workgroup
-constexpr int kKB = 64;             // columns per step
-constexpr int kAStride = kKB + 8;   // LDS row stride (halves), padded
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kTilesPerWave = 2;                                 // unit rows per wave
+constexpr int kNT = kWaves * kTilesPerWave * kUnitRows;          // rows per workgroup
+constexpr int kUC = 128;                                         // columns per step (one unit)
+constexpr int kAStride = kUC + 8;                                // LDS row stride (halves), padded
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
@@ -72,16 +75,17 @@ struct MfmaArgs {
 };
 
 // One workgroup: one MFMA item (<= MT tokens of one expert) x kNT rows;
-// each wave owns 32 rows and all MT tokens. Loads run two 64-column steps
+// each wave owns 32 rows and all MT tokens. Loads run two 128-column steps
 // ahead of the matrix cores (registers), activations are double-buffered in
 // LDS.
-template <bool GATEUP, int MT>
-__global__ __launch_bounds__(kThreads, MT > 32 ? 1 : 2) void mfma_kernel(MfmaArgs ma)
+template <bool GATEUP, int MF>
+__global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
 {
+    constexpr int MT = 16 * MF;  // tokens per item
     constexpr int NM = GATEUP ? 2 : 1;
-    constexpr int MF = MT / 32;  // 32 x 32 blocks per wave
+    constexpr int TW = kTilesPerWave;
     __shared__ _Float16 As[2][MT][kAStride];
-    __shared__ int s_src[MT];   // input row of each tile token (-1: none)
+    __shared__ int s_src[MT];   // input row of each item token (-1: none)
 
     const Fwd &f = ma.f;
     const Geo &g = f.g;
@@ -95,9 +99,9 @@ __global__ __launch_bounds__(kThreads, MT > 32 ? 1 : 2) void mfma_kernel(MfmaArg
     const int n_active = n_items * ma.n_tiles;
     const int b = blockIdx.x;
     if (b >= n_active) return;
-    const int q = n_active / kXcds, rem = n_active % kXcds;
+    const int qx = n_active / kXcds, rem = n_active % kXcds;
     const int xcd = b % kXcds, i = b / kXcds;
-    const int logical = xcd * q + min(xcd, rem) + i;
+    const int logical = xcd * qx + min(xcd, rem) + i;
     const int item_idx = logical / ma.n_tiles;
     const int ntile = logical % ma.n_tiles;
     const Item it = ma.items[item_idx];
@@ -105,10 +109,12 @@ __global__ __launch_bounds__(kThreads, MT > 32 ? 1 : 2) void mfma_kernel(MfmaArg
     const uint8_t *blk = it.expert >= 0 ? f.pool + (size_t)it.expert * f.stride : f.shared;
     const int K = GATEUP ? g.d : g.f;       // contraction length
     const int rows = GATEUP ? g.f : g.d;    // output rows
+    const int n_kb = K / kUC;               // steps = units per row
+    const int ng = GATEUP ? g.ng_gu : g.ng_dn;
     const float *in = GATEUP ? f.x : f.h;
     float *out = GATEUP ? f.h : f.o;
 
-    // input row of every tile token
+    // input row of every item token
     if (tid < MT) {
         int src = -1;
         if (tid < count) {
@@ -122,23 +128,34 @@ __global__ __launch_bounds__(kThreads, MT > 32 ? 1 : 2) void mfma_kernel(MfmaArg
     }
     __syncthreads();
 
-    // activation loads: thread -> (token row, part of the 64 columns)
-    constexpr int kParts = kThreads / MT;           // threads per token row
-    constexpr int kCols = kKB / kParts;             // columns per thread
-    constexpr int kVec = kCols / 4;                 // float4 per thread
+    // activation loads, one half step (64 columns) at a time: thread ->
+    // (token row, part of the 64 columns)
+    constexpr int kHalf = kUC / 2;
+    constexpr int kParts = kThreads / MT;          // threads per token row
+    constexpr int kCols = kHalf / kParts;          // columns per thread per half
+    constexpr int kVec = kCols / 4;                // float4 per thread
     const int a_row = tid / kParts, a_q = tid % kParts;
     const int a_src = s_src[a_row];
-    const float *a_ptr = a_src >= 0 ? in + (size_t)a_src * K + a_q * kCols : nullptr;
-    auto load_a = [&](int k0, float4 (&av)[kVec]) {
+    // rows past the item's tokens load token 0's row (every load is issued on
+    // every path, so waits stay exact) and store zeros
+    const float *a_ptr = in + (size_t)(a_src >= 0 ? a_src : s_src[0]) * K + a_q * kCols;
+    const float a_keep = a_src >= 0 ? 1.0f : 0.0f;
+    auto load_a = [&](int kb, int hf, float4 (&av)[kVec]) {
 #pragma unroll
         for (int c = 0; c < kVec; ++c)
-            av[c] = a_ptr ? reinterpret_cast<const float4 *>(a_ptr + k0)[c]
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
+            av[c] = reinterpret_cast<const float4 *>(a_ptr + (size_t)kb * kUC + hf * kHalf)[c];
     };
-    auto store_a = [&](int buf, const float4 (&av)[kVec]) {
+    auto store_a = [&](int buf, int hf, const float4 (&av)[kVec]) {
         // groups of 8 columns, each written in the order 0,4,1,5,2,6,3,7
-        const float *v = reinterpret_cast<const float *>(av);
-        _Float16 *dst = &As[buf][a_row][a_q * kCols];
+        float v[kCols];
+#pragma unroll
+        for (int c = 0; c < kVec; ++c) {
+            v[4 * c] = av[c].x * a_keep;
+            v[4 * c + 1] = av[c].y * a_keep;
+            v[4 * c + 2] = av[c].z * a_keep;
+            v[4 * c + 3] = av[c].w * a_keep;
+        }
+        _Float16 *dst = &As[buf][a_row][hf * kHalf + a_q * kCols];
 #pragma unroll
         for (int gi = 0; gi < kCols / 8; ++gi) {
             half8_t h;
@@ -151,126 +168,166 @@ __global__ __launch_bounds__(kThreads, MT > 32 ? 1 : 2) void mfma_kernel(MfmaArg
         }
     };
 
-    // weights: this lane's row and 32-column half of each 64-column step
-    const int hh = lane / 32;
-    const int row = ntile * kNT + wave * kNW + (lane % 32);
-    const int row_c = min(row, rows - 1);
-    const long long row_bytes = K / 2;
-    const uint8_t *qb[NM];
-    const float *sb[NM];
-    const long long spr = g.group ? K / g.group : 1;
-    if (GATEUP) {
-        qb[0] = blk + (long long)row_c * row_bytes;
-        qb[NM - 1] = blk + g.off_up + (long long)row_c * row_bytes;
-        sb[0] = reinterpret_cast<const float *>(blk + g.off_gs) + (long long)row_c * spr;
-        sb[NM - 1] = reinterpret_cast<const float *>(blk + g.off_us) + (long long)row_c * spr;
-    } else {
-        qb[0] = blk + g.off_dn + (long long)row_c * row_bytes;
-        sb[0] = reinterpret_cast<const float *>(blk + g.off_ds) + (long long)row_c * spr;
-    }
-    auto load_b = [&](int k0, uint4 (&bw)[NM], float (&bs)[NM]) {
-        const int col = k0 + 32 * hh;
-        const long long grp = g.group ? col / g.group : 0;
+    // weights: this wave's unit rows; lane slot = (row in unit, quarter)
+    const int r16 = lane % kUnitRows, q = lane / kUnitRows;
+    const int rt0 = ntile * (kNT / kUnitRows) + wave * TW;  // first unit row of the wave
+    const int n_rt = rows / kUnitRows;
+    const uint8_t *qb[TW][NM];
+    const float *sb[TW][NM];
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            bw[m] = *reinterpret_cast<const uint4 *>(qb[m] + col / 2);
-            bs[m] = sb[m][grp];
+    for (int t = 0; t < TW; ++t) {
+        const int rt = min(rt0 + t, n_rt - 1);  // rows past the end: loads stay in range
+        const size_t u0 = (size_t)rt * n_kb * kUnitBytes + (size_t)lane * 16;
+        const size_t s0 = (size_t)rt * ng * kUnitRows + r16;
+        if (GATEUP) {
+            qb[t][0] = blk + u0;
+            qb[t][NM - 1] = blk + g.off_up + u0;
+            sb[t][0] = reinterpret_cast<const float *>(blk + g.off_gs) + s0;
+            sb[t][NM - 1] = reinterpret_cast<const float *>(blk + g.off_us) + s0;
+        } else {
+            qb[t][0] = blk + g.off_dn + u0;
+            sb[t][0] = reinterpret_cast<const float *>(blk + g.off_ds) + s0;
         }
+    }
+    auto load_b = [&](int kb, uint4 (&bw)[TW][NM], float (&bs)[TW][NM]) {
+        const int grp = g.group ? (kb * kUC + q * 32) / g.group : 0;
+#pragma unroll
+        for (int t = 0; t < TW; ++t)
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                bw[t][m] = *reinterpret_cast<const uint4 *>(qb[t][m] + (size_t)kb * kUnitBytes);
+                bs[t][m] = sb[t][m][grp * kUnitRows];
+            }
     };
 
-    f32x16_t acc[NM][MF];
+    f32x4_t acc[NM][TW][MF];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int mf = 0; mf < MF; ++mf)
+        for (int t = 0; t < TW; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[m][mf][r] = 0.0f;
+            for (int mb = 0; mb < MF; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[m][t][mb][r] = 0.0f;
 
-    // one 64-column step on LDS buffer `cur` and weights (bw, bs)
-    auto compute = [&](int cur, const uint4 (&bw)[NM], const float (&bs)[NM]) {
-        half2_t s2[NM];
+    // half of a 128-column step on LDS buffer `cur` and weights (bw, bs):
+    // k-steps s_lo and s_lo + 1 of 32, each lane's quarter q covering columns
+    // 32q + 8s .. + 8
+    auto compute = [&](int cur, const uint4 (&bw)[TW][NM], const float (&bs)[TW][NM], int s_lo) {
+        half2_t s2[TW][NM];
 #pragma unroll
-        for (int m = 0; m < NM; ++m) s2[m] = half2_t{(_Float16)bs[m], (_Float16)bs[m]};
+        for (int t = 0; t < TW; ++t)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            half8_t bf[NM];
+            for (int m = 0; m < NM; ++m) s2[t][m] = half2_t{(_Float16)bs[t][m], (_Float16)bs[t][m]};
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                const uint32_t w = s == 0 ? bw[m].x : (s == 1 ? bw[m].y : (s == 2 ? bw[m].z : bw[m].w));
-                bf[m] = dequant8(w, s2[m]);
-            }
+        for (int s = s_lo; s < s_lo + 2; ++s) {
+            half8_t bf[TW][NM];
 #pragma unroll
-            for (int mf = 0; mf < MF; ++mf) {
+            for (int t = 0; t < TW; ++t)
+#pragma unroll
+                for (int m = 0; m < NM; ++m) {
+                    const uint4 u = bw[t][m];
+                    const uint32_t w = s == 0 ? u.x : (s == 1 ? u.y : (s == 2 ? u.z : u.w));
+                    bf[t][m] = dequant8(w, s2[t][m]);
+                }
+#pragma unroll
+            for (int mb = 0; mb < MF; ++mb) {
                 const half8_t af =
-                    *reinterpret_cast<const half8_t *>(&As[cur][mf * 32 + (lane % 32)][32 * hh + 8 * s]);
+                    *reinterpret_cast<const half8_t *>(&As[cur][mb * 16 + r16][32 * q + 8 * s]);
 #pragma unroll
-                for (int m = 0; m < NM; ++m)
-                    acc[m][mf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[m], acc[m][mf], 0, 0, 0);
+                for (int t = 0; t < TW; ++t)
+#pragma unroll
+                    for (int m = 0; m < NM; ++m)
+                        acc[m][t][mb] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[t][m], acc[m][t][mb], 0, 0, 0);
             }
         }
     };
 
-    const int steps = K / kKB;
-    // ring of two register stages: stage j holds step ks with ks % 2 == j
-    float4 av0[kVec], av1[kVec];
-    uint4 bw0[NM], bw1[NM];
-    float bs0[NM], bs1[NM];
-    load_a(0, av0);
+    // weights: a ring of two register stages (stage j holds step ks with
+    // ks % 2 == j); activations: one register stage
+    // of half a step, loaded during the current step's products and stored to
+    // the other LDS buffer
+    float4 av[kVec];
+    uint4 bw0[TW][NM], bw1[TW][NM];
+    float bs0[TW][NM], bs1[TW][NM];
+    load_a(0, 0, av);
     load_b(0, bw0, bs0);
-    if (steps > 1) {
-        load_a(kKB, av1);
-        load_b(kKB, bw1, bs1);
-    }
-    store_a(0, av0);
+    if (n_kb > 1) load_b(1, bw1, bs1);
+    store_a(0, 0, av);
+    load_a(0, 1, av);
+    store_a(0, 1, av);
     __syncthreads();
-    for (int ks = 0; ks < steps; ks += 2) {
-        // even step ks: LDS buffer 0, weights in stage 0
-        {
-            uint4 bw[NM];
-            float bs[NM];
-#pragma unroll
-            for (int m = 0; m < NM; ++m) { bw[m] = bw0[m]; bs[m] = bs0[m]; }
-            if (ks + 2 < steps) {
-                load_a((ks + 2) * kKB, av0);
-                load_b((ks + 2) * kKB, bw0, bs0);
-            }
-            compute(0, bw, bs);
-            if (ks + 1 < steps) store_a(1, av1);
-            __syncthreads();
+    // one step: products on LDS buffer `cur`, the next step's activations
+    // into the other buffer
+    auto step = [&](int ks, int cur, const uint4 (&bw)[TW][NM], const float (&bs)[TW][NM]) {
+        const bool next = ks + 1 < n_kb;
+        if (next) load_a(ks + 1, 0, av);
+        compute(cur, bw, bs, 0);
+        if (next) {
+            store_a(cur ^ 1, 0, av);
+            load_a(ks + 1, 1, av);
         }
-        if (ks + 1 >= steps) break;
-        // odd step ks + 1: LDS buffer 1, weights in stage 1
-        {
-            uint4 bw[NM];
-            float bs[NM];
+        compute(cur, bw, bs, 2);
+        if (next) store_a(cur ^ 1, 1, av);
+        __syncthreads();
+    };
+    // Small items (short steps) compute from a copy of the stage, so the
+    // stage is reloaded before the products; large items (long steps, more
+    // registers) reload the stage after them.
+    constexpr bool kEarly = MF <= 2;
+    for (int ks = 0; ks < n_kb; ks += 2) {
+        // even step ks: LDS buffer 0, weights in stage 0
+        if constexpr (kEarly) {
+            uint4 bw[TW][NM];
+            float bs[TW][NM];
 #pragma unroll
-            for (int m = 0; m < NM; ++m) { bw[m] = bw1[m]; bs[m] = bs1[m]; }
-            if (ks + 3 < steps) {
-                load_a((ks + 3) * kKB, av1);
-                load_b((ks + 3) * kKB, bw1, bs1);
-            }
-            compute(1, bw, bs);
-            if (ks + 2 < steps) store_a(0, av0);
-            __syncthreads();
+            for (int t = 0; t < TW; ++t)
+#pragma unroll
+                for (int m = 0; m < NM; ++m) { bw[t][m] = bw0[t][m]; bs[t][m] = bs0[t][m]; }
+            if (ks + 2 < n_kb) load_b(ks + 2, bw0, bs0);
+            step(ks, 0, bw, bs);
+        } else {
+            step(ks, 0, bw0, bs0);
+            if (ks + 2 < n_kb) load_b(ks + 2, bw0, bs0);
+        }
+        if (ks + 1 >= n_kb) break;
+        // odd step ks + 1: LDS buffer 1, weights in stage 1
+        if constexpr (kEarly) {
+            uint4 bw[TW][NM];
+            float bs[TW][NM];
+#pragma unroll
+            for (int t = 0; t < TW; ++t)
+#pragma unroll
+                for (int m = 0; m < NM; ++m) { bw[t][m] = bw1[t][m]; bs[t][m] = bs1[t][m]; }
+            if (ks + 3 < n_kb) load_b(ks + 3, bw1, bs1);
+            step(ks + 1, 1, bw, bs);
+        } else {
+            step(ks + 1, 1, bw1, bs1);
+            if (ks + 3 < n_kb) load_b(ks + 3, bw1, bs1);
         }
     }
 
-    // epilogue: lane holds column `row` of MF 32x32 blocks; register r of
-    // block mf is token mf*32 + (r/4)*8 + (lane/32)*4 + r%4
-    if (row >= rows) return;
+    // epilogue: register r of block (t, mb) is token mb*16 + 4q + r, weight
+    // row 16 (rt0 + t) + r16
 #pragma unroll
-    for (int mf = 0; mf < MF; ++mf) {
+    for (int t = 0; t < TW; ++t) {
+        const int row = (rt0 + t) * kUnitRows + r16;
+        if (rt0 + t >= n_rt) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int tok = mf * 32 + (r / 4) * 8 + hh * 4 + (r % 4);
-            if (tok >= count) continue;
-            const int p = it.p0 + tok;
-            if (GATEUP) {
-                const float gv = acc[0][mf][r], uv = acc[NM - 1][mf][r];
-                out[(size_t)p * rows + row] = gv / (1.0f + expf(-gv)) * uv;
-            } else {
-                const int orow = it.expert >= 0 ? min(max(f.perm[p], 0), f.A - 1) : p;
-                out[(size_t)orow * rows + row] = acc[0][mf][r];
+        for (int mb = 0; mb < MF; ++mb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tok = mb * 16 + 4 * q + r;
+                if (tok >= count) continue;
+                const int p = it.p0 + tok;
+                if (GATEUP) {
+                    const float gv = acc[0][t][mb][r], uv = acc[NM - 1][t][mb][r];
+                    out[(size_t)p * rows + row] = gv / (1.0f + expf(-gv)) * uv;
+                } else {
+                    const int orow = it.expert >= 0 ? min(max(f.perm[p], 0), f.A - 1) : p;
+                    out[(size_t)orow * rows + row] = acc[0][t][mb][r];
+                }
             }
         }
     }
@@ -280,18 +337,18 @@ __global__ __launch_bounds__(kThreads, MT > 32 ? 1 : 2) void mfma_kernel(MfmaArg
 
 bool mfma_supported(const Geo &g)
 {
-    return g.wbits == 4 && g.d % kKB == 0 && g.f % kKB == 0;
+    return g.wbits == 4 && g.ucols == kUC;
 }
 
-template <bool GATEUP, int MT>
+template <bool GATEUP, int MF>
 hipError_t run_mfma(const MfmaArgs &a, long long blocks, const hipEvent_t *ev, hipStream_t s)
 {
     const dim3 grid((unsigned)blocks);
     if (ev[0] || ev[1])  // events taken by the dispatch itself, around this kernel only
-        hipExtLaunchKernelGGL((mfma_kernel<GATEUP, MT>), grid, dim3(kThreads), 0, s, ev[0], ev[1],
+        hipExtLaunchKernelGGL((mfma_kernel<GATEUP, MF>), grid, dim3(kThreads), 0, s, ev[0], ev[1],
                               0, a);
     else
-        hipLaunchKernelGGL((mfma_kernel<GATEUP, MT>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((mfma_kernel<GATEUP, MF>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -308,11 +365,11 @@ hipError_t launch_mfma(const Fwd &f, bool gateup, bool small, hipStream_t s)
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     const hipEvent_t *ev = small ? (gateup ? f.ev_sgu : f.ev_sdn) : (gateup ? f.ev_mgu : f.ev_mdn);
+    constexpr int kSmall = kMfmaSmallTokens / 16, kBig = kMfmaBigTokens / 16;
     if (small)
-        return gateup ? run_mfma<true, kMfmaSmallTokens>(a, blocks, ev, s)
-                      : run_mfma<false, kMfmaSmallTokens>(a, blocks, ev, s);
-    return gateup ? run_mfma<true, kMfmaBigTokens>(a, blocks, ev, s)
-                  : run_mfma<false, kMfmaBigTokens>(a, blocks, ev, s);
+        return gateup ? run_mfma<true, kSmall>(a, blocks, ev, s)
+                      : run_mfma<false, kSmall>(a, blocks, ev, s);
+    return gateup ? run_mfma<true, kBig>(a, blocks, ev, s) : run_mfma<false, kBig>(a, blocks, ev, s);
 }
 
 }  // namespace moe

@@ -22,16 +22,29 @@ struct Item {
 };
 
 // Geometry of one layer's expert blocks, resolved and checked on the host.
+//
+// Device block layout. Each code matrix [R rows][K columns] is cut into
+// 1 KB units of 16 rows x U columns (U = 128 int4 codes or 64 int8 codes
+// per row), stored unit-row by unit-row: unit (rt, kb) at byte
+// (rt * (K / U) + kb) * 1024. Inside a unit, lane slot L = r + 16 q (r the
+// row within the unit, q = 0..3) holds the 16 bytes of row 16 rt + r that
+// cover columns kb * U + q * U/4 .. + U/4, in canonical byte order with
+// offset-binary codes. One 16-byte load per lane of a wave reads one whole
+// unit, which is also the weight operand of four (int4) or two (int8)
+// 16x16x32 MFMA steps. Scales of a matrix: [R / 16][groups per row][16]
+// float32, so the 16 rows of a unit read one 64-byte run per group.
 struct Geo {
     int d, f, E, wbits, group;
-    int epc;                 // code elements per 16-byte chunk (32 int4, 16 int8)
-    int gu_lpr, gu_cpl;      // gate/up rows: lanes per row, chunks per lane
-    int dn_lpr, dn_cpl;      // down rows
-    long long row_gu;        // bytes of one gate (or up) code row = d * wbits / 8
-    long long row_dn;        // bytes of one down code row = f * wbits / 8
-    long long spr_gu, spr_dn;  // scales per gate/up row, per down row
+    int epc;                 // codes per 16-byte lane chunk (32 int4, 16 int8)
+    int ucols;               // columns per unit = 4 * epc
+    int kb_gu, kb_dn;        // units along a gate/up row (d / ucols), a down row (f / ucols)
+    int ng_gu, ng_dn;        // scale groups per gate/up row (d / G or 1), per down row
     long long off_up, off_dn, off_gs, off_us, off_ds;  // byte offsets in a block
 };
+
+constexpr int kUnitRows = 16;
+constexpr int kMaxModelDim = 16384;  // largest d_model or d_ff
+constexpr int kUnitBytes = 1024;
 
 // Everything the expert kernels of one moe_expert_forward call need.
 struct Fwd {

@@ -84,10 +84,12 @@ def _fwd(pool, N=4, k=1, ws=FAKE, wsb=1 << 30, x=FAKE, y=FAKE):
 
 def test_expert_forward_argument_checks():
     assert _fwd(_pool(wbits=3)) == moe.MOE_EINVAL
-    assert _fwd(_pool(d=250)) == moe.MOE_ESHAPE            # not a multiple of 32
-    assert _fwd(_pool(d=96 * 32)) == moe.MOE_ESHAPE        # 96 chunks: not 2^n and not 64*{1,2,3,4,6,8}
+    assert _fwd(_pool(d=250)) == moe.MOE_ESHAPE            # not a multiple of 128
+    assert _fwd(_pool(d=160)) == moe.MOE_ESHAPE            # a multiple of 32, not of 128
+    assert _fwd(_pool(f=192)) == moe.MOE_ESHAPE
+    assert _fwd(_pool(d=16384 + 128)) == moe.MOE_ESHAPE    # beyond the largest dimension
     assert _fwd(_pool(group=48)) == moe.MOE_ESHAPE         # group not a multiple of 32
-    assert _fwd(_pool(group=64, f=96 * 32)) == moe.MOE_ESHAPE
+    assert _fwd(_pool(group=96)) == moe.MOE_ESHAPE         # group does not divide d or f
     assert _fwd(_pool(E=0)) == moe.MOE_EINVAL
     assert _fwd(_pool(E=2000)) == moe.MOE_EINVAL
     assert _fwd(_pool(), k=17) == moe.MOE_EINVAL
@@ -128,22 +130,46 @@ def test_sizes():
     assert moe.forward_workspace_size(p0, N, k) < ws - N * (2048 + 6144) * 4 + 4096
 
 
-def test_pack_expert_flips_codes_only():
-    cfg = synth.CONFIGS["tiny"]
-    spec = cfg.layer
-    blk = synth.expert_pool(cfg, count=1)[0]
-    p = _pool()
-    out = np.empty_like(blk)
-    moe.pack_expert(blk, p, out)
-    off = synth.canonical_offsets(spec)
-    q = off["gate_s"]
-    assert np.array_equal(out[:q], blk[:q] ^ 0x88)
-    assert np.array_equal(out[q:], blk[q:])
-    p8 = _pool(d=6144, f=2048, wbits=8, group=0)
-    c8 = np.arange(moe.block_bytes(6144, 2048, 8, 0), dtype=np.int64).astype(np.uint8)
-    o8 = moe.pack_expert(c8.copy(), p8)
-    q8 = 3 * 6144 * 2048
-    assert np.array_equal(o8[:q8], c8[:q8] ^ 0x80) and np.array_equal(o8[q8:], c8[q8:])
+def _units(codes, R, K, wbits):
+    """The documented device arrangement of one canonical code matrix:
+    1 KB units of 16 rows x (128 int4 or 64 int8) columns, slot r + 16 q of
+    unit (rt, kb) holding the 16 bytes of row 16 rt + r at quarter q."""
+    rb = K * wbits // 8
+    m = codes.reshape(R // 16, 16, K // (512 // wbits), 4, 16)   # rt, r, kb, q, byte
+    return m.transpose(0, 2, 3, 1, 4).reshape(R * rb)
+
+
+def _scale_units(sc, R, ng):
+    return sc.reshape(R // 16, 16, ng).transpose(0, 2, 1).reshape(R * ng)
+
+
+@pytest.mark.parametrize("wbits,d,f,group", [(4, 256, 128, 32), (4, 384, 256, 128),
+                                              (8, 192, 128, 0), (8, 128, 64, 32)])
+def test_pack_expert_unit_layout(wbits, d, f, group):
+    """moe_pack_expert against the layout the header documents, on random
+    bytes (so every byte's destination is checked)."""
+    nb = moe.block_bytes(d, f, wbits, group)
+    rng = np.random.default_rng(wbits * 1000 + d + f + group)
+    blk = rng.integers(0, 256, nb, dtype=np.uint8)
+    out = moe.pack_expert(blk.copy(), _pool(d=d, f=f, wbits=wbits, group=group))
+    flip = 0x88 if wbits == 4 else 0x80
+    q = d * f * wbits // 8
+    exp = np.empty_like(blk)
+    for off, R, K in ((0, f, d), (q, f, d), (2 * q, d, f)):
+        exp[off:off + q] = _units(blk[off:off + q] ^ flip, R, K, wbits)
+    sc = blk[3 * q:].view(np.float32)
+    ng_gu, ng_dn = (d // group, f // group) if group else (1, 1)
+    s_exp = np.empty_like(sc)
+    o = 0
+    for R, ng in ((f, ng_gu), (f, ng_gu), (d, ng_dn)):
+        s_exp[o:o + R * ng] = _scale_units(sc[o:o + R * ng], R, ng)
+        o += R * ng
+    exp[3 * q:] = s_exp.view(np.uint8)
+    np.testing.assert_array_equal(out, exp)
+    # in place gives the same
+    same = blk.copy()
+    moe.pack_expert(same, _pool(d=d, f=f, wbits=wbits, group=group), same)
+    np.testing.assert_array_equal(same, exp)
     with pytest.raises(moe.MoeError):
         moe.pack_expert(blk, _pool(d=250))
 
