@@ -354,11 +354,11 @@ def main():
                         "down_avg_launch_us": t_dn * 1e6 if t_dn else None,
                         "down_GBps": dn_b / 1e9 / t_dn if t_dn else None}
     labels = {"gemv": ("gemv_kernel<gate/up> (expert gate and up projections, SiLU product)",
-                       "moe::gemv_kernel<true"),
+                       "moe::gemv_kernel<true, 4, 1"),
               "small": ("mfma_kernel<gate/up, 32 tokens> (small-group gate and up on the "
-                        "matrix cores)", "moe::mfma_kernel<true, 32"),
+                        "matrix cores)", "moe::mfma_kernel<true, 2>"),
               "mfma": ("mfma_kernel<gate/up, 128 tokens> (grouped GEMM of gate and up, SiLU "
-                       "product)", "moe::mfma_kernel<true, 128")}
+                       "product)", "moe::mfma_kernel<true, 8>")}
     roof = None
     if passes:
         # the roofline is reported for the pass whose gate/up launch is longest
