@@ -39,8 +39,8 @@ MFMA_F16_PEAK_TFLOPS = 2500.0   # dense float16 matrix-core peak
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=1000)
-    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=400)
     p.add_argument("--config", default="decode1")
     p.add_argument("--layers", type=int, default=8, help="layer pools rotated over the steps")
     p.add_argument("--batches", type=int, default=16, help="distinct token batches rotated")
@@ -236,10 +236,14 @@ def main():
     mfma_ok = spec.wbits == 4 and d % 64 == 0 and f % 64 == 0
     calib = {}
 
+    MIN_BIG_ITEMS = 32  # fewer 128-token items than this join the 32-token pass
+
     def pass_of(T):
         T = np.asarray(T)
         big = (T >= MFMA_MIN) & mfma_ok
         small = ~big & (T >= SMALL_MIN) & mfma_ok
+        if big.any() and np.sum((T[big] + 127) // 128) < MIN_BIG_ITEMS:
+            small, big = small | big, np.zeros_like(big)
         return np.where(big, 1, np.where(small, 2, 0))
 
     def record(key, l):

@@ -115,12 +115,14 @@ typedef struct {
 } moe_expert_pool;
 
 /*
- * Route. scores = sigmoid(x Wr^T + b) in float32 (workspace), then per token
- * the k best experts: topk_ids [n_tokens][k] int32 in rank order (ties to the
- * lower id; a NaN score ranks above every number) and topk_w [n_tokens][k]
- * float32, the chosen scores.
+ * Route. scores = sigmoid(x Wr^T + b) in float32, then per token the k best
+ * experts: topk_ids [n_tokens][k] int32 in rank order (ties to the lower id;
+ * a NaN score ranks above every number) and topk_w [n_tokens][k] float32,
+ * the chosen scores. Batches above 16 tokens sum the router products in up to
+ * 16 slices of the contraction (partial sums in the workspace, added in
+ * slice order before the sigmoid).
  *   w_router [n_experts][d_model] float32; b_router [n_experts] or NULL.
- *   d_model must be a multiple of 16; x and w_router 16-byte aligned.
+ *   d_model must be a multiple of 32; x and w_router 16-byte aligned.
  *   workspace: at least moe_route_workspace_size(n_tokens, n_experts) bytes,
  *   MOE_ALIGN-aligned.
  * Colibri pages: "Exact Architecture and Data-Flow Reconstruction" (sigmoid
@@ -181,6 +183,9 @@ moe_status moe_expert_forward(const moe_expert_pool *pool /* (host) */,
  *   mfma_small_min_tokens <= T < mfma_min_tokens: the same kernels with
  *     32-token tiles; 0 selects the default (2), negative turns it off;
  *   otherwise: the streaming GEMV kernels.
+ * When both matrix-core passes are on and the 128-token pass would get fewer
+ * than 32 items, those experts join the 32-token pass (a few large items
+ * would otherwise run with a few workgroups each).
  * The matrix-core passes need int4 weights and d_model, d_ff multiples of
  * 64; otherwise every expert uses the GEMV.
  * events: each non-NULL event is taken by the dispatch of the kernel it

@@ -162,7 +162,9 @@ size_t moe_block_bytes(int d_model, int d_ff, int wbits, int group)
 size_t moe_route_workspace_size(int n_tokens, int n_experts)
 {
     if (n_tokens < 0 || n_experts < 1) return 0;
-    return (size_t)align_up((long long)n_tokens * n_experts * 4);
+    // scores, or the router's partial sums over up to router_slices_bound slices
+    const long long slices = n_tokens > 0 ? router_slices_bound(n_tokens, n_experts) : 1;
+    return (size_t)align_up(slices * n_tokens * n_experts * 4);
 }
 
 size_t moe_forward_workspace_size(const moe_expert_pool *pool, int n_tokens, int k)
@@ -200,7 +202,7 @@ moe_status moe_route_topk(const float *x, int n_tokens, int d_model, const float
     if (n_tokens < 0 || d_model <= 0) return MOE_EINVAL;
     moe_status st = check_k(k, n_experts);
     if (st != MOE_OK) return st;
-    if (d_model % 16) return MOE_ESHAPE;
+    if (d_model % 32) return MOE_ESHAPE;
     if ((long long)n_tokens * n_experts > 0x7FFFFFFFLL || (long long)n_tokens * d_model > 0x7FFFFFFFLL)
         return MOE_ESHAPE;
     if (n_tokens == 0) return MOE_OK;
@@ -212,7 +214,8 @@ moe_status moe_route_topk(const float *x, int n_tokens, int d_model, const float
     if (launch_router(x, n_tokens, d_model, w_router, b_router, n_experts, scores, stream) !=
         hipSuccess)
         return MOE_EHIP;
-    if (launch_topk(scores, n_tokens, n_experts, k, topk_ids, topk_w, stream) != hipSuccess)
+    if (launch_topk(scores, router_slices(n_tokens, d_model, n_experts), b_router, n_tokens,
+                    n_experts, k, topk_ids, topk_w, stream) != hipSuccess)
         return MOE_EHIP;
     return MOE_OK;
 }

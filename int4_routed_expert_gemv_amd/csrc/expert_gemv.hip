@@ -155,7 +155,7 @@ __host__ __device__ constexpr int stage_bytes(int wb) { return (wb == 4 ? 16 : 8
 // rounds of (token, chunk) activation pairs loaded before the weight loads
 __host__ __device__ constexpr int pre_rounds(int tb) { return tb == 1 ? 1 : 2; }
 
-// units a wave holds in registers at a time: 4, 6 or 12 (a template parameter)
+// units a wave holds in registers at a time: 4 to 16 (a template parameter)
 constexpr int kUnitBatch = 12;
 
 // below this many 4-wave workgroups in a pass, single-token rows of 17..48
@@ -559,6 +559,9 @@ __device__ int block_excl_scan(int v, int &total)
     return r;
 }
 
+// Fewer 128-token items than this go to the 32-token pass.
+constexpr int kMinBigItems = 32;
+
 // Which pass computes an expert with T tokens: 0 the GEMV kernels, 1 the
 // 128-token MFMA kernels (T >= tstar), 2 the 32-token MFMA kernels
 // (tsmall <= T < tstar). A pass with no list (max_* == 0) takes nothing.
@@ -588,8 +591,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Fwd f)
             e = -1;
         }
     }
-    const int pass = pass_of(f, T);
-    const int sh_pass = f.has_shared ? pass_of(f, f.N) : -1;
+    int pass = pass_of(f, T);
+    int sh_pass = f.has_shared ? pass_of(f, f.N) : -1;
+    if (f.max_mitems > 0 && f.max_sitems > 0) {
+        // a handful of 128-token items would run nearly alone (a few
+        // workgroups each): give them to the 32-token pass instead, where
+        // they run among the others
+        int n_big;
+        block_excl_scan(pass == 1 ? (T + kMfmaBigTokens - 1) / kMfmaBigTokens : 0, n_big);
+        if (sh_pass == 1) n_big += (f.N + kMfmaBigTokens - 1) / kMfmaBigTokens;
+        if (n_big < kMinBigItems) {
+            if (pass == 1) pass = 2;
+            if (sh_pass == 1) sh_pass = 2;
+        }
+    }
     Item *const lists[3] = {f.items, f.mitems, f.sitems};
     int32_t *const counts[3] = {f.n_items, f.n_mitems, f.n_sitems};
     const int maxes[3] = {f.max_items, f.max_mitems, f.max_sitems};
@@ -684,21 +699,30 @@ hipError_t run_gemv(GemvArgs a, hipStream_t s)
     return hipGetLastError();
 }
 
-// How a unit row is shared: every wave of a 4-wave workgroup on one unit row
-// (fewer when the rows are shorter than 4 units), holding 4 or 12 units at a
-// time; when few workgroups would fill the chip, single-token rows of up to
-// 48 units on 8 waves of 6 units.
+// How a unit row is shared, by row length and by how many workgroups the
+// pass has (few: spread each unit row over more waves; many: give each wave
+// whole unit rows, so the activations staged per workgroup serve 4 of them):
+//   rows of 1-3 units: 1 or 2 waves per unit row;
+//   rows of 4-16 units: 4 waves of up to 4 units, or (many workgroups) one
+//     wave per unit row with all its units;
+//   longer rows: 4 waves of up to 12 units at a time, or (few workgroups,
+//     single tokens, up to 48 units) 8 waves of 6.
 template <bool GATEUP, int WB, int TB>
 hipError_t run_ks(const GemvArgs &a, hipStream_t s)
 {
     const int K = GATEUP ? a.f.g.d : a.f.g.f;
     const int rows = GATEUP ? a.f.g.f : a.f.g.d;
     const int n_kb = K / (4 * Fmt<WB>::epc);
+    const long long wgs = (long long)a.f.max_items * (rows / kUnitRows);
+    const bool few = wgs < kFewWorkgroups;
     if (n_kb == 1) return run_gemv<GATEUP, WB, TB, 4, 1, 4>(a, s);
     if (n_kb < 4) return run_gemv<GATEUP, WB, TB, 4, 2, 4>(a, s);
-    if (n_kb <= 16) return run_gemv<GATEUP, WB, TB, 4, 4, 4>(a, s);
-    const long long wgs = (long long)a.f.max_items * (rows / kUnitRows);
-    if (TB == 1 && n_kb <= 48 && wgs < kFewWorkgroups) return run_gemv<GATEUP, WB, TB, 8, 8, 6>(a, s);
+    if (n_kb <= 16) {
+        if (few) return run_gemv<GATEUP, WB, TB, 4, 4, 4>(a, s);
+        return n_kb <= 8 ? run_gemv<GATEUP, WB, TB, 4, 1, 8>(a, s)
+                         : run_gemv<GATEUP, WB, TB, 4, 1, 16>(a, s);
+    }
+    if (TB == 1 && n_kb <= 48 && few) return run_gemv<GATEUP, WB, TB, 8, 8, 6>(a, s);
     return run_gemv<GATEUP, WB, TB, 4, 4, kUnitBatch>(a, s);
 }
 

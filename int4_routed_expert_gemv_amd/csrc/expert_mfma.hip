@@ -42,28 +42,60 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTilesPerWave = 2;                                 // unit rows per wave
 constexpr int kNT = kWaves * kTilesPerWave * kUnitRows;          // rows per workgroup
-constexpr int kUC = 128;                                         // columns per step (one unit)
-constexpr int kAStride = kUC + 8;                                // LDS row stride (halves), padded
 constexpr int kXcds = 8;
+
+// Code format: a unit has UC columns (one step), NS k-steps of 32, and each
+// lane's 16 bytes cover QW columns of its row (one quarter of the unit).
+// Activations are loaded in NA parts per step.
+template <int WB> struct MFmt;
+template <> struct MFmt<4> { static constexpr int UC = 128, NS = 4, QW = 32, NA = 2; };
+template <> struct MFmt<8> { static constexpr int UC = 64, NS = 2, QW = 16, NA = 1; };
 
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 
-// 8 offset-binary int4 codes (element j in bits 4j..4j+3) times the scale,
-// as float16 in the column order 0,4,1,5,2,6,3,7.
-__device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t s2)
+// The 8 codes of k-step s of a lane's 16 bytes times the scale, as float16:
+// int4: the codes of 32-bit word s (element j in bits 4j..4j+3), in the
+//   column order 0,4,1,5,2,6,3,7;
+// int8: the bytes of words 2s and 2s+1, in the column order 0,2,1,3,4,6,5,7.
+// Codes are offset binary: ORed into the mantissa of 1024 and the offset
+// taken off exactly, then one rounding by the scale.
+template <int WB>
+__device__ __forceinline__ half8_t dequant8(const uint4 &u, int s, half2_t s2)
 {
-    const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
-    const uint32_t m = 0x000F000Fu, magic = 0x64006400u;
-    const half2_t p0 = (as_h2((w & m) | magic) - off) * s2;
-    const half2_t p1 = (as_h2(((w >> 4) & m) | magic) - off) * s2;
-    const half2_t p2 = (as_h2(((w >> 8) & m) | magic) - off) * s2;
-    const half2_t p3 = (as_h2(((w >> 12) & m) | magic) - off) * s2;
+    const uint32_t magic = 0x64006400u;
+    const uint32_t d[4] = {u.x, u.y, u.z, u.w};
+    half2_t p[4];
+    if constexpr (WB == 4) {
+        const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+        const uint32_t w = d[s], m = 0x000F000Fu;
+        p[0] = (as_h2((w & m) | magic) - off) * s2;
+        p[1] = (as_h2(((w >> 4) & m) | magic) - off) * s2;
+        p[2] = (as_h2(((w >> 8) & m) | magic) - off) * s2;
+        p[3] = (as_h2(((w >> 12) & m) | magic) - off) * s2;
+    } else {
+        const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
+        const uint32_t w0 = d[2 * s], w1 = d[2 * s + 1], m = 0x00FF00FFu;
+        p[0] = (as_h2((w0 & m) | magic) - off) * s2;
+        p[1] = (as_h2(((w0 >> 8) & m) | magic) - off) * s2;
+        p[2] = (as_h2((w1 & m) | magic) - off) * s2;
+        p[3] = (as_h2(((w1 >> 8) & m) | magic) - off) * s2;
+    }
     half8_t r;
-    r[0] = p0[0]; r[1] = p0[1];
-    r[2] = p1[0]; r[3] = p1[1];
-    r[4] = p2[0]; r[5] = p2[1];
-    r[6] = p3[0]; r[7] = p3[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[2 * i] = p[i][0];
+        r[2 * i + 1] = p[i][1];
+    }
     return r;
+}
+
+// Column j of an 8-column group goes to position perm8<WB>(j) of the
+// float16 operand, matching dequant8.
+template <int WB>
+__device__ __forceinline__ int perm8(int j)
+{
+    if constexpr (WB == 4) return j < 4 ? 2 * j : 2 * (j - 4) + 1;
+    else return (j & 4) | ((j & 1) << 1) | ((j >> 1) & 1);
 }
 
 struct MfmaArgs {
@@ -75,15 +107,17 @@ struct MfmaArgs {
 };
 
 // One workgroup: one MFMA item (<= MT tokens of one expert) x kNT rows;
-// each wave owns 32 rows and all MT tokens. Loads run two 128-column steps
+// each wave owns 32 rows and all MT tokens. Weight loads run two unit steps
 // ahead of the matrix cores (registers), activations are double-buffered in
 // LDS.
-template <bool GATEUP, int MF>
+template <bool GATEUP, int WB, int MF>
 __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
 {
     constexpr int MT = 16 * MF;  // tokens per item
     constexpr int NM = GATEUP ? 2 : 1;
     constexpr int TW = kTilesPerWave;
+    constexpr int kUC = MFmt<WB>::UC, NS = MFmt<WB>::NS, QW = MFmt<WB>::QW, NA = MFmt<WB>::NA;
+    constexpr int kAStride = kUC + 8;  // LDS row stride (halves), padded
     __shared__ _Float16 As[2][MT][kAStride];
     __shared__ int s_src[MT];   // input row of each item token (-1: none)
 
@@ -128,9 +162,9 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
     }
     __syncthreads();
 
-    // activation loads, one half step (64 columns) at a time: thread ->
-    // (token row, part of the 64 columns)
-    constexpr int kHalf = kUC / 2;
+    // activation loads, one part of a step (kHalf columns) at a time: thread
+    // -> (token row, part of the kHalf columns)
+    constexpr int kHalf = kUC / NA;
     constexpr int kParts = kThreads / MT;          // threads per token row
     constexpr int kCols = kHalf / kParts;          // columns per thread per half
     constexpr int kVec = kCols / 4;                // float4 per thread
@@ -156,14 +190,12 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
             v[4 * c + 3] = av[c].w * a_keep;
         }
         _Float16 *dst = &As[buf][a_row][hf * kHalf + a_q * kCols];
+        static_assert(kCols % 8 == 0, "whole 8-column groups per thread");
 #pragma unroll
         for (int gi = 0; gi < kCols / 8; ++gi) {
             half8_t h;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                h[2 * j] = (_Float16)v[8 * gi + j];
-                h[2 * j + 1] = (_Float16)v[8 * gi + 4 + j];
-            }
+            for (int j = 0; j < 8; ++j) h[perm8<WB>(j)] = (_Float16)v[8 * gi + j];
             *reinterpret_cast<half8_t *>(dst + 8 * gi) = h;
         }
     };
@@ -190,7 +222,7 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
         }
     }
     auto load_b = [&](int kb, uint4 (&bw)[TW][NM], float (&bs)[TW][NM]) {
-        const int grp = g.group ? (kb * kUC + q * 32) / g.group : 0;
+        const int grp = g.group ? (kb * kUC + q * QW) / g.group : 0;
 #pragma unroll
         for (int t = 0; t < TW; ++t)
 #pragma unroll
@@ -210,9 +242,9 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[m][t][mb][r] = 0.0f;
 
-    // half of a 128-column step on LDS buffer `cur` and weights (bw, bs):
-    // k-steps s_lo and s_lo + 1 of 32, each lane's quarter q covering columns
-    // 32q + 8s .. + 8
+    // half of a unit step on LDS buffer `cur` and weights (bw, bs): k-steps
+    // s_lo .. s_lo + NS/2 - 1 of 32, each lane's quarter q covering columns
+    // QW q + 8s .. + 8
     auto compute = [&](int cur, const uint4 (&bw)[TW][NM], const float (&bs)[TW][NM], int s_lo) {
         half2_t s2[TW][NM];
 #pragma unroll
@@ -220,20 +252,16 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
 #pragma unroll
             for (int m = 0; m < NM; ++m) s2[t][m] = half2_t{(_Float16)bs[t][m], (_Float16)bs[t][m]};
 #pragma unroll
-        for (int s = s_lo; s < s_lo + 2; ++s) {
+        for (int s = s_lo; s < s_lo + NS / 2; ++s) {
             half8_t bf[TW][NM];
 #pragma unroll
             for (int t = 0; t < TW; ++t)
 #pragma unroll
-                for (int m = 0; m < NM; ++m) {
-                    const uint4 u = bw[t][m];
-                    const uint32_t w = s == 0 ? u.x : (s == 1 ? u.y : (s == 2 ? u.z : u.w));
-                    bf[t][m] = dequant8(w, s2[t][m]);
-                }
+                for (int m = 0; m < NM; ++m) bf[t][m] = dequant8<WB>(bw[t][m], s, s2[t][m]);
 #pragma unroll
             for (int mb = 0; mb < MF; ++mb) {
                 const half8_t af =
-                    *reinterpret_cast<const half8_t *>(&As[cur][mb * 16 + r16][32 * q + 8 * s]);
+                    *reinterpret_cast<const half8_t *>(&As[cur][mb * 16 + r16][QW * q + 8 * s]);
 #pragma unroll
                 for (int t = 0; t < TW; ++t)
 #pragma unroll
@@ -255,8 +283,10 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
     load_b(0, bw0, bs0);
     if (n_kb > 1) load_b(1, bw1, bs1);
     store_a(0, 0, av);
-    load_a(0, 1, av);
-    store_a(0, 1, av);
+    if constexpr (NA == 2) {
+        load_a(0, 1, av);
+        store_a(0, 1, av);
+    }
     __syncthreads();
     // one step: products on LDS buffer `cur`, the next step's activations
     // into the other buffer
@@ -266,10 +296,10 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
         compute(cur, bw, bs, 0);
         if (next) {
             store_a(cur ^ 1, 0, av);
-            load_a(ks + 1, 1, av);
+            if constexpr (NA == 2) load_a(ks + 1, 1, av);
         }
-        compute(cur, bw, bs, 2);
-        if (next) store_a(cur ^ 1, 1, av);
+        compute(cur, bw, bs, NS / 2);
+        if (NA == 2 && next) store_a(cur ^ 1, 1, av);
         __syncthreads();
     };
     // Small items (short steps) compute from a copy of the stage, so the
@@ -337,18 +367,18 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
 
 bool mfma_supported(const Geo &g)
 {
-    return g.wbits == 4 && g.ucols == kUC;
+    return (g.wbits == 4 && g.ucols == MFmt<4>::UC) || (g.wbits == 8 && g.ucols == MFmt<8>::UC);
 }
 
-template <bool GATEUP, int MF>
+template <bool GATEUP, int WB, int MF>
 hipError_t run_mfma(const MfmaArgs &a, long long blocks, const hipEvent_t *ev, hipStream_t s)
 {
     const dim3 grid((unsigned)blocks);
     if (ev[0] || ev[1])  // events taken by the dispatch itself, around this kernel only
-        hipExtLaunchKernelGGL((mfma_kernel<GATEUP, MF>), grid, dim3(kThreads), 0, s, ev[0], ev[1],
+        hipExtLaunchKernelGGL((mfma_kernel<GATEUP, WB, MF>), grid, dim3(kThreads), 0, s, ev[0], ev[1],
                               0, a);
     else
-        hipLaunchKernelGGL((mfma_kernel<GATEUP, MF>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((mfma_kernel<GATEUP, WB, MF>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -366,10 +396,17 @@ hipError_t launch_mfma(const Fwd &f, bool gateup, bool small, hipStream_t s)
     if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     const hipEvent_t *ev = small ? (gateup ? f.ev_sgu : f.ev_sdn) : (gateup ? f.ev_mgu : f.ev_mdn);
     constexpr int kSmall = kMfmaSmallTokens / 16, kBig = kMfmaBigTokens / 16;
+    if (f.g.wbits == 8) {
+        if (small)
+            return gateup ? run_mfma<true, 8, kSmall>(a, blocks, ev, s)
+                          : run_mfma<false, 8, kSmall>(a, blocks, ev, s);
+        return gateup ? run_mfma<true, 8, kBig>(a, blocks, ev, s)
+                      : run_mfma<false, 8, kBig>(a, blocks, ev, s);
+    }
     if (small)
-        return gateup ? run_mfma<true, kSmall>(a, blocks, ev, s)
-                      : run_mfma<false, kSmall>(a, blocks, ev, s);
-    return gateup ? run_mfma<true, kBig>(a, blocks, ev, s) : run_mfma<false, kBig>(a, blocks, ev, s);
+        return gateup ? run_mfma<true, 4, kSmall>(a, blocks, ev, s)
+                      : run_mfma<false, 4, kSmall>(a, blocks, ev, s);
+    return gateup ? run_mfma<true, 4, kBig>(a, blocks, ev, s) : run_mfma<false, 4, kBig>(a, blocks, ev, s);
 }
 
 }  // namespace moe

@@ -83,10 +83,14 @@ struct Fwd {
 moe_status resolve_geo(const moe_expert_pool *p, Geo *g);
 
 // ---- launchers (each in its own translation unit) ----------------------
+// Router: final scores [N][E], or raw partial sums [P][N][E] over P slices of
+// the contraction (P = router_slices(N, d, E)) that launch_topk adds up.
+int router_slices_bound(int N, int E);   // the largest P any d can give
+int router_slices(int N, int d, int E);
 hipError_t launch_router(const float *x, int N, int d, const float *wr, const float *b,
-                         int E, float *scores, hipStream_t s);
-hipError_t launch_topk(const float *scores, int N, int E, int k, int32_t *ids, float *w,
-                       hipStream_t s);
+                         int E, float *out, hipStream_t s);
+hipError_t launch_topk(const float *in, int P, const float *b, int N, int E, int k,
+                       int32_t *ids, float *w, hipStream_t s);
 hipError_t launch_union(const int32_t *ids, int A, int E, int32_t *union_ids, int32_t *n_union,
                         int32_t *offsets, int32_t *perm, hipStream_t s);
 hipError_t launch_hit_count(const int32_t *ids, int A, int E, uint64_t *counters, hipStream_t s);

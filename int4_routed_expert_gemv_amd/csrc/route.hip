@@ -40,6 +40,10 @@ __device__ __forceinline__ float wave_sum_dpp(float v)
 }
 
 constexpr int kTokGroup = 4;
+// batches up to this many tokens use the one-workgroup-per-expert GEMV router
+constexpr int kGemvMaxTokens = 16;
+// most slices of the contraction the GEMM router splits into
+constexpr int kMaxSlices = 16;
 
 // Decode-sized batches: one workgroup per expert keeps its router row in
 // registers (read from HBM once) and dots it with the tokens, four tokens per
@@ -126,39 +130,67 @@ __global__ __launch_bounds__(kRouterThreads) void router_gemv_stream_kernel(
     }
 }
 
-// Prefill-sized batches: a 64-token x 64-expert tile per workgroup, operands
-// staged through LDS in K-steps of 16, 4x4 outputs per thread, float32 FMA.
-constexpr int kTM = 64, kTN = 64, kTK = 16;
+// Larger batches: a 64-token x 64-expert tile per workgroup over one K slice
+// (of P), operands staged through LDS in K-steps of 32 (double-buffered, the
+// next step's loads issued before the current step's products), 4x4
+// outputs per thread, float32 FMA. With P == 1 the tile writes final scores;
+// otherwise it writes raw partial sums [P][N][E] that the top-k kernel adds
+// in slice order.
+constexpr int kTM = 64, kTN = 64, kTK = 32;
 
 __global__ __launch_bounds__(256) void router_gemm_kernel(
     const float *__restrict__ x, int N, int d, const float *__restrict__ wr,
-    const float *__restrict__ b, int E, float *__restrict__ scores)
+    const float *__restrict__ b, int E, int P, float *__restrict__ out)
 {
-    __shared__ float xs[kTK][kTM + 4];
-    __shared__ float ws[kTK][kTN + 4];
-    const int t0 = blockIdx.x * kTM, e0 = blockIdx.y * kTN;
+    __shared__ float xs[2][kTK][kTM + 4];
+    __shared__ float ws[2][kTK][kTN + 4];
+    const int t0 = blockIdx.x * kTM, e0 = blockIdx.y * kTN, p = blockIdx.z;
     const int tid = threadIdx.x;
     const int tr = tid / 16, tc = tid % 16;  // 16 x 16 threads, 4x4 each
-    float acc[4][4] = {};
-    // loader: 64 rows x 16 k = 256 float4 -> one float4 per thread
-    const int lr = tid / 4, lk = (tid % 4) * 4;
-    for (int k0 = 0; k0 < d; k0 += kTK) {
-        float4 xv = make_float4(0.f, 0.f, 0.f, 0.f), wv = xv;
-        if (t0 + lr < N) xv = *reinterpret_cast<const float4 *>(x + (size_t)(t0 + lr) * d + k0 + lk);
-        if (e0 + lr < E) wv = *reinterpret_cast<const float4 *>(wr + (size_t)(e0 + lr) * d + k0 + lk);
-        xs[lk + 0][lr] = xv.x; xs[lk + 1][lr] = xv.y; xs[lk + 2][lr] = xv.z; xs[lk + 3][lr] = xv.w;
-        ws[lk + 0][lr] = wv.x; ws[lk + 1][lr] = wv.y; ws[lk + 2][lr] = wv.z; ws[lk + 3][lr] = wv.w;
-        __syncthreads();
-        // each K-step is summed on its own and then added, which keeps the
-        // rounding error of the 6144-term dot products near that of a tree
-        float part[4][4] = {};
+    const int kper = d / P, kbeg = p * kper, steps = kper / kTK;
+    // loader: 64 rows x 32 k = 512 float4 -> two per thread (rows lr, lr + 32);
+    // rows past N or E read the last row (results dropped): every load issued
+    const int lr = tid / 8, lk = (tid % 8) * 4;
+    const float *xr0 = x + (size_t)min(t0 + lr, N - 1) * d + kbeg + lk;
+    const float *xr1 = x + (size_t)min(t0 + lr + 32, N - 1) * d + kbeg + lk;
+    const float *wr0 = wr + (size_t)min(e0 + lr, E - 1) * d + kbeg + lk;
+    const float *wr1 = wr + (size_t)min(e0 + lr + 32, E - 1) * d + kbeg + lk;
+    float4 xv0, xv1, wv0, wv1;
+    auto load = [&](int st) {
+        const int o = st * kTK;
+        xv0 = *reinterpret_cast<const float4 *>(xr0 + o);
+        xv1 = *reinterpret_cast<const float4 *>(xr1 + o);
+        wv0 = *reinterpret_cast<const float4 *>(wr0 + o);
+        wv1 = *reinterpret_cast<const float4 *>(wr1 + o);
+    };
+    auto store = [&](int buf) {
+        const float xa[4] = {xv0.x, xv0.y, xv0.z, xv0.w}, xb[4] = {xv1.x, xv1.y, xv1.z, xv1.w};
+        const float wa[4] = {wv0.x, wv0.y, wv0.z, wv0.w}, wb[4] = {wv1.x, wv1.y, wv1.z, wv1.w};
 #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            xs[buf][lk + j][lr] = xa[j];
+            xs[buf][lk + j][lr + 32] = xb[j];
+            ws[buf][lk + j][lr] = wa[j];
+            ws[buf][lk + j][lr + 32] = wb[j];
+        }
+    };
+    float acc[4][4] = {};
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int st = 0; st < steps; ++st) {
+        const int cur = st & 1;
+        if (st + 1 < steps) load(st + 1);
+        // each K-step is summed on its own and then added, which keeps the
+        // rounding error of the long dot products near that of a tree
+        float part[4][4] = {};
+#pragma unroll 4
         for (int kk = 0; kk < kTK; ++kk) {
             float a[4], c[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = xs[kk][tr * 4 + i];
+            for (int i = 0; i < 4; ++i) a[i] = xs[cur][kk][tr * 4 + i];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) c[j] = ws[kk][tc * 4 + j];
+            for (int j = 0; j < 4; ++j) c[j] = ws[cur][kk][tc * 4 + j];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -168,16 +200,21 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] += part[i][j];
+        if (st + 1 < steps) store(cur ^ 1);
         __syncthreads();
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        int t = t0 + tr * 4 + i;
+        const int t = t0 + tr * 4 + i;
         if (t >= N) continue;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            int e = e0 + tc * 4 + j;
-            if (e < E) scores[(size_t)t * E + e] = sigmoidf(acc[i][j] + (b ? b[e] : 0.0f));
+            const int e = e0 + tc * 4 + j;
+            if (e >= E) continue;
+            if (P == 1)
+                out[(size_t)t * E + e] = sigmoidf(acc[i][j] + (b ? b[e] : 0.0f));
+            else
+                out[((size_t)p * N + t) * E + e] = acc[i][j];
         }
     }
 }
@@ -192,20 +229,41 @@ constexpr int kMaxPerLane = MOE_MAX_EXPERTS / kWave;  // 16
 
 // One wave per token: k rounds of a wave-wide max over 64-bit keys
 // (sortable score, then inverted id so equal scores go to the lower id).
+// With P > 1 the input holds the router's raw partial sums [P][N][E]: the
+// score is sigmoid(sum over slices in order + bias).
 __global__ __launch_bounds__(256) void topk_kernel(
-    const float *__restrict__ scores, int N, int E, int k, int32_t *__restrict__ ids,
-    float *__restrict__ w)
+    const float *__restrict__ in, int P, const float *__restrict__ b, int N, int E, int k,
+    int32_t *__restrict__ ids, float *__restrict__ w)
 {
     const int lane = threadIdx.x % kWave;
     const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     if (t >= N) return;
-    const float *s = scores + (size_t)t * E;
     uint32_t hi[kMaxPerLane];
+    float sv[kMaxPerLane];
     uint32_t taken = 0;
 #pragma unroll
     for (int m = 0; m < kMaxPerLane; ++m) {
-        int e = lane + m * kWave;
-        hi[m] = e < E ? sortable(s[e]) : 0u;
+        const int e = lane + m * kWave;
+        float v = 0.0f;
+        if (e < E) {
+            if (P == 1) {
+                v = in[(size_t)t * E + e];
+            } else {
+                // all slices' loads issued together (slices past P read slice
+                // P - 1 and are not added), then added in slice order
+                float part[kMaxSlices];
+#pragma unroll
+                for (int p = 0; p < kMaxSlices; ++p)
+                    part[p] = in[((size_t)min(p, P - 1) * N + t) * E + e];
+                float l = 0.0f;
+#pragma unroll
+                for (int p = 0; p < kMaxSlices; ++p)
+                    if (p < P) l += part[p];
+                v = sigmoidf(l + (b ? b[e] : 0.0f));
+            }
+        }
+        sv[m] = v;
+        hi[m] = e < E ? sortable(v) : 0u;
         if (e >= E) taken |= 1u << m;
     }
     for (int j = 0; j < k; ++j) {
@@ -218,45 +276,70 @@ __global__ __launch_bounds__(256) void topk_kernel(
             if (bm < 0 || hi[m] > bh || (hi[m] == bh && lo > bl)) { bh = hi[m]; bl = lo; bm = m; }
         }
         if (bm < 0) { bh = 0; bl = 0; }
+        float bs = bm >= 0 ? sv[0] : 0.0f;
+#pragma unroll
+        for (int m = 1; m < kMaxPerLane; ++m)
+            if (m == bm) bs = sv[m];
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) {
             uint32_t oh = __shfl_xor(bh, o, kWave), ol = __shfl_xor(bl, o, kWave);
             if (oh > bh || (oh == bh && ol > bl)) { bh = oh; bl = ol; }
         }
         const int id = (int)(0xFFFFFFFFu - bl);
-        if (bm >= 0 && lane + bm * kWave == id) taken |= 1u << bm;
-        if (lane == 0) {
+        if (bm >= 0 && lane + bm * kWave == id) {
+            // the lane holding the winner records it
+            taken |= 1u << bm;
             ids[(size_t)t * k + j] = id;
-            w[(size_t)t * k + j] = s[id];
+            w[(size_t)t * k + j] = bs;
         }
     }
 }
 
 }  // namespace
 
-hipError_t launch_router(const float *x, int N, int d, const float *wr, const float *b, int E,
-                         float *scores, hipStream_t s)
+int router_slices_bound(int N, int E)
 {
-    if (N <= 512) {
+    // K slices so that the tiles and slices give about 512 workgroups (two
+    // per compute unit), at most 16; none for the GEMV router
+    if (N <= kGemvMaxTokens) return 1;
+    const long long tiles = (long long)((N + kTM - 1) / kTM) * ((E + kTN - 1) / kTN);
+    int p = 1;
+    while (p < kMaxSlices && tiles * p * 2 <= 512) p *= 2;
+    return p;
+}
+
+int router_slices(int N, int d, int E)
+{
+    if (N <= kGemvMaxTokens) return 1;
+    int p = router_slices_bound(N, E);
+    while (p > 1 && (d % (p * kTK)) != 0) p /= 2;
+    return p;
+}
+
+hipError_t launch_router(const float *x, int N, int d, const float *wr, const float *b, int E,
+                         float *out, hipStream_t s)
+{
+    if (N <= kGemvMaxTokens) {
         if (d <= 4 * kMaxRowVec * kRouterThreads)
             hipLaunchKernelGGL(router_gemv_kernel, dim3(E), dim3(kRouterThreads), 0, s, x, N, d,
-                               wr, b, E, scores);
+                               wr, b, E, out);
         else
             hipLaunchKernelGGL(router_gemv_stream_kernel, dim3(E), dim3(kRouterThreads), 0, s, x,
-                               N, d, wr, b, E, scores);
+                               N, d, wr, b, E, out);
     } else {
-        dim3 grid((N + kTM - 1) / kTM, (E + kTN - 1) / kTN);
-        hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(256), 0, s, x, N, d, wr, b, E, scores);
+        const int P = router_slices(N, d, E);
+        dim3 grid((N + kTM - 1) / kTM, (E + kTN - 1) / kTN, P);
+        hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(256), 0, s, x, N, d, wr, b, E, P, out);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_topk(const float *scores, int N, int E, int k, int32_t *ids, float *w,
-                       hipStream_t s)
+hipError_t launch_topk(const float *in, int P, const float *b, int N, int E, int k, int32_t *ids,
+                       float *w, hipStream_t s)
 {
     const int per_block = 4;
     hipLaunchKernelGGL(topk_kernel, dim3((N + per_block - 1) / per_block), dim3(per_block * kWave),
-                       0, s, scores, N, E, k, ids, w);
+                       0, s, in, P, b, N, E, k, ids, w);
     return hipGetLastError();
 }
 

@@ -60,6 +60,7 @@ def test_route_topk_argument_checks():
     assert L.moe_route_topk(FAKE + 4, 4, 256, FAKE, None, 16, 1, FAKE, FAKE, ws, big, None) == moe.MOE_EALIGN
     assert L.moe_route_topk(FAKE, 4, 256, FAKE, None, 16, 1, FAKE, FAKE, ws + 16, big, None) == moe.MOE_EALIGN
     assert L.moe_route_topk(FAKE, 4, 250, FAKE, None, 16, 1, FAKE, FAKE, ws, big, None) == moe.MOE_ESHAPE
+    assert L.moe_route_topk(FAKE, 4, 48, FAKE, None, 16, 1, FAKE, FAKE, ws, big, None) == moe.MOE_ESHAPE
     # zero tokens: success, nothing touched (even with null pointers)
     assert L.moe_route_topk(None, 0, 256, None, None, 16, 1, None, None, None, 0, None) == moe.MOE_OK
 
@@ -122,8 +123,10 @@ def test_sizes():
     # hidden [A+N][f] and expert outputs [A+N][d] in float32 dominate
     assert ws >= (A + N) * (2048 + 6144) * 4
     assert ws < (A + N) * (2048 + 6144) * 4 + 2 * 1024 * 1024
-    assert moe.route_workspace_size(N, 256) == N * 256 * 4
-    assert moe.workspace_size(p, N, k) == max(ws, N * 256 * 4)
+    # scores, or router partial sums over at most 16 slices of the contraction
+    assert N * 256 * 4 <= moe.route_workspace_size(N, 256) <= 16 * N * 256 * 4
+    assert moe.route_workspace_size(1, 256) == 256 * 4
+    assert moe.workspace_size(p, N, k) == max(ws, moe.route_workspace_size(N, 256))
     assert moe.forward_workspace_size(_pool(wbits=5), N, k) == 0
     # without a shared expert there are no shared rows
     p0 = _pool(d=6144, f=2048, E=256, group=128)

@@ -224,3 +224,15 @@ def test_workspace_size_covers_every_threshold(N, k, big, small):
     lists of every pair of thresholds a call can choose; run_layer allocates
     exactly moe_workspace_size bytes."""
     full_parity(tiny(n_tokens=N, k=min(k, 16)), mfma_min_tokens=big, mfma_small_min_tokens=small)
+
+
+@pytest.mark.parametrize("group", [0, 32])
+@pytest.mark.parametrize("big,small", PASSES)
+def test_tiny_int8_passes(group, big, small):
+    """int8 codes (the draft layer's format) on each pass alone and mixed,
+    with per-row and with grouped scales."""
+    base = synth.CONFIGS["tiny"]
+    spec = dataclasses.replace(base.layer, wbits=8, group=group, scale_lo=0.005 / 16,
+                               scale_hi=0.02 / 16)
+    cfg = dataclasses.replace(base, n_tokens=64, k=4, layers=(spec,))
+    full_parity(cfg, mfma_min_tokens=big, mfma_small_min_tokens=small)
