@@ -36,7 +36,7 @@ constexpr int kDefaultSmallMinTokens = 2;
 // Workspace of moe_expert_forward, laid out in this order.
 struct FwdLayout {
     int tb, max_items, max_mitems, max_sitems, tstar, tsmall, P;
-    long long items, n_items, mitems, n_mitems, sitems, n_sitems, h, o, total;
+    long long items, n_items, mitems, n_mitems, sitems, n_sitems, h, o, x16, h16, total;
 };
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
@@ -79,12 +79,24 @@ FwdLayout fwd_layout(const Geo &g, int N, int k, int has_shared, int mfma_min_to
             if (ue * per < routed) routed = ue * per;
             L.max_items = (int)(routed + (has_shared && N <= cap ? ceil_div(N, L.tb) : 0));
         }
-        L.max_mitems = big ? (int)(ceil_div(A, kMfmaBigTokens) + A / L.tstar +
+        // each expert on a pass adds at most one partly filled item; at most
+        // min(ue, A / threshold) experts reach a threshold
+        const long long ue_big = ue < A / L.tstar ? ue : A / L.tstar;
+        const long long ue_small = ue < A / L.tsmall ? ue : A / L.tsmall;
+        L.max_mitems = big ? (int)(ceil_div(A, kMfmaBigTokens) + ue_big +
                                    (has_shared ? ceil_div(N, kMfmaBigTokens) : 0))
                            : 0;
-        L.max_sitems = small ? (int)(ceil_div(A, kMfmaSmallTokens) + A / L.tsmall +
-                                     (has_shared ? ceil_div(N, kMfmaSmallTokens) : 0))
-                             : 0;
+        long long sm = ceil_div(A, kMfmaSmallTokens) + ue_small +
+                       (has_shared ? ceil_div(N, kMfmaSmallTokens) : 0);
+        if (big) {
+            // below tstar an expert is at most ceil((tstar - 1) / 32) items; experts
+            // moved over from the 128-token pass had fewer than kMinBigItems of
+            // its items between them, so at most (kMinBigItems - 1) * 128 tokens
+            const long long below = (ue + (has_shared ? 1 : 0)) * ceil_div(L.tstar - 1, kMfmaSmallTokens);
+            const long long moved = (long long)(kMinBigItems - 1) * (kMfmaBigTokens / kMfmaSmallTokens + 1);
+            if (below + moved < sm) sm = below + moved;
+        }
+        L.max_sitems = small ? (int)sm : 0;
     }
     L.P = (int)(A + (has_shared ? N : 0));
     long long off = 0;
@@ -96,6 +108,10 @@ FwdLayout fwd_layout(const Geo &g, int N, int k, int has_shared, int mfma_min_to
     L.n_sitems = off; off = align_up(off + 4);
     L.h = off; off = align_up(off + (long long)L.P * g.f * 4);
     L.o = off; off = align_up(off + (long long)L.P * g.d * 4);
+    // float16 operands, when a matrix-core pass can run
+    const bool any_mfma = L.max_mitems > 0 || L.max_sitems > 0;
+    L.x16 = off; off = align_up(off + (any_mfma ? (long long)N * g.d * 2 : 0));
+    L.h16 = off; off = align_up(off + (any_mfma ? (long long)L.P * g.f * 2 : 0));
     L.total = off;
     return L;
 }
@@ -309,6 +325,8 @@ moe_status moe_expert_forward_ex(const moe_expert_pool *pool, const float *x, in
     f.perm = perm;
     f.h = reinterpret_cast<float *>(ws + L.h);
     f.o = reinterpret_cast<float *>(ws + L.o);
+    f.x16 = reinterpret_cast<uint16_t *>(ws + L.x16);
+    f.h16 = reinterpret_cast<uint16_t *>(ws + L.h16);
     f.y = y;
     f.items = reinterpret_cast<Item *>(ws + L.items);
     f.n_items = reinterpret_cast<int32_t *>(ws + L.n_items);
@@ -338,6 +356,8 @@ moe_status moe_expert_forward_ex(const moe_expert_pool *pool, const float *x, in
     // gate/up of every pass (the first launch also builds the work lists),
     // then down of every pass, then the combine
     if (launch_gateup(f, stream) != hipSuccess) return MOE_EHIP;
+    if ((f.max_mitems > 0 || f.max_sitems > 0) && launch_stage_x16(f, stream) != hipSuccess)
+        return MOE_EHIP;
     if (launch_mfma(f, true, false, stream) != hipSuccess) return MOE_EHIP;
     if (launch_mfma(f, true, true, stream) != hipSuccess) return MOE_EHIP;
     if (launch_down(f, stream) != hipSuccess) return MOE_EHIP;

@@ -559,9 +559,6 @@ __device__ int block_excl_scan(int v, int &total)
     return r;
 }
 
-// Fewer 128-token items than this go to the 32-token pass.
-constexpr int kMinBigItems = 32;
-
 // Which pass computes an expert with T tokens: 0 the GEMV kernels, 1 the
 // 128-token MFMA kernels (T >= tstar), 2 the 32-token MFMA kernels
 // (tsmall <= T < tstar). A pass with no list (max_* == 0) takes nothing.

@@ -21,9 +21,11 @@
 //  * within each 8-column group the columns are taken in the order
 //    0,4,1,5,2,6,3,7 on both operands, which lets one 32-bit word of codes
 //    feed one MFMA operand without shuffles;
-//  * activations (x or h, float32) are converted to float16 and staged in LDS
-//    one unit (128 columns) at a time, double-buffered, loaded one step ahead;
-//  * each wave owns two unit rows (32 weight rows) and all MT tokens; weight
+//  * activations come as float16 rows already in the operand's column order
+//    (x converted once per call by stage_x16_kernel, h written so by the
+//    gate/up epilogue) and are copied into LDS one unit step at a time,
+//    double-buffered, loaded one step ahead;
+//  * each wave owns two or four unit rows and all MT tokens; weight
 //    loads run two steps ahead of the matrix cores.
 // Workgroups are mapped so that those sharing an expert (and so its weights
 // and its tokens) land on the same XCD and share its L2.
@@ -40,8 +42,17 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kTilesPerWave = 2;                                 // unit rows per wave
-constexpr int kNT = kWaves * kTilesPerWave * kUnitRows;          // rows per workgroup
+// unit rows per wave: 2 for gate/up (two matrices); for down 4 with
+// 128-token items (the same products per activation read as gate/up), 2 with
+// 32-token items (registers for more waves)
+__host__ __device__ constexpr int tiles_per_wave(bool gateup, int mf)
+{
+    return gateup || mf < 8 ? 2 : 4;
+}
+__host__ __device__ constexpr int rows_per_wg(bool gateup, int mf)
+{
+    return kWaves * tiles_per_wave(gateup, mf) * kUnitRows;
+}
 constexpr int kXcds = 8;
 
 // Code format: a unit has UC columns (one step), NS k-steps of 32, and each
@@ -106,8 +117,9 @@ struct MfmaArgs {
     int max_items;
 };
 
-// One workgroup: one MFMA item (<= MT tokens of one expert) x kNT rows;
-// each wave owns 32 rows and all MT tokens. Weight loads run two unit steps
+// One workgroup: one MFMA item (<= MT tokens of one expert) x
+// rows_per_wg(GATEUP, MF) rows; each wave owns 32 or 64 rows and all MT
+// tokens. Weight loads run two unit steps
 // ahead of the matrix cores (registers), activations are double-buffered in
 // LDS.
 template <bool GATEUP, int WB, int MF>
@@ -115,7 +127,8 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
 {
     constexpr int MT = 16 * MF;  // tokens per item
     constexpr int NM = GATEUP ? 2 : 1;
-    constexpr int TW = kTilesPerWave;
+    constexpr int TW = tiles_per_wave(GATEUP, MF);
+    constexpr int kNT = rows_per_wg(GATEUP, MF);
     constexpr int kUC = MFmt<WB>::UC, NS = MFmt<WB>::NS, QW = MFmt<WB>::QW, NA = MFmt<WB>::NA;
     constexpr int kAStride = kUC + 8;  // LDS row stride (halves), padded
     __shared__ _Float16 As[2][MT][kAStride];
@@ -145,8 +158,7 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
     const int rows = GATEUP ? g.f : g.d;    // output rows
     const int n_kb = K / kUC;               // steps = units per row
     const int ng = GATEUP ? g.ng_gu : g.ng_dn;
-    const float *in = GATEUP ? f.x : f.h;
-    float *out = GATEUP ? f.h : f.o;
+    const uint16_t *in = GATEUP ? f.x16 : f.h16;
 
     // input row of every item token
     if (tid < MT) {
@@ -163,41 +175,27 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
     __syncthreads();
 
     // activation loads, one part of a step (kHalf columns) at a time: thread
-    // -> (token row, part of the kHalf columns)
+    // -> (token row, 16-byte chunks of the kHalf columns)
     constexpr int kHalf = kUC / NA;
     constexpr int kParts = kThreads / MT;          // threads per token row
-    constexpr int kCols = kHalf / kParts;          // columns per thread per half
-    constexpr int kVec = kCols / 4;                // float4 per thread
+    constexpr int kCols = kHalf / kParts;          // columns per thread per part
+    constexpr int kVec = kCols / 8;                // 16-byte chunks per thread
+    static_assert(kVec >= 1, "at least one 16-byte chunk per thread");
     const int a_row = tid / kParts, a_q = tid % kParts;
     const int a_src = s_src[a_row];
     // rows past the item's tokens load token 0's row (every load is issued on
     // every path, so waits stay exact) and store zeros
-    const float *a_ptr = in + (size_t)(a_src >= 0 ? a_src : s_src[0]) * K + a_q * kCols;
-    const float a_keep = a_src >= 0 ? 1.0f : 0.0f;
-    auto load_a = [&](int kb, int hf, float4 (&av)[kVec]) {
+    const uint16_t *a_ptr = in + (size_t)(a_src >= 0 ? a_src : s_src[0]) * K + a_q * kCols;
+    const bool a_keep = a_src >= 0;
+    auto load_a = [&](int kb, int hf, uint4 (&av)[kVec]) {
 #pragma unroll
         for (int c = 0; c < kVec; ++c)
-            av[c] = reinterpret_cast<const float4 *>(a_ptr + (size_t)kb * kUC + hf * kHalf)[c];
+            av[c] = reinterpret_cast<const uint4 *>(a_ptr + (size_t)kb * kUC + hf * kHalf)[c];
     };
-    auto store_a = [&](int buf, int hf, const float4 (&av)[kVec]) {
-        // groups of 8 columns, each written in the order 0,4,1,5,2,6,3,7
-        float v[kCols];
+    auto store_a = [&](int buf, int hf, const uint4 (&av)[kVec]) {
+        uint4 *dst = reinterpret_cast<uint4 *>(&As[buf][a_row][hf * kHalf + a_q * kCols]);
 #pragma unroll
-        for (int c = 0; c < kVec; ++c) {
-            v[4 * c] = av[c].x * a_keep;
-            v[4 * c + 1] = av[c].y * a_keep;
-            v[4 * c + 2] = av[c].z * a_keep;
-            v[4 * c + 3] = av[c].w * a_keep;
-        }
-        _Float16 *dst = &As[buf][a_row][hf * kHalf + a_q * kCols];
-        static_assert(kCols % 8 == 0, "whole 8-column groups per thread");
-#pragma unroll
-        for (int gi = 0; gi < kCols / 8; ++gi) {
-            half8_t h;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) h[perm8<WB>(j)] = (_Float16)v[8 * gi + j];
-            *reinterpret_cast<half8_t *>(dst + 8 * gi) = h;
-        }
+        for (int c = 0; c < kVec; ++c) dst[c] = a_keep ? av[c] : make_uint4(0u, 0u, 0u, 0u);
     };
 
     // weights: this wave's unit rows; lane slot = (row in unit, quarter)
@@ -276,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
     // ks % 2 == j); activations: one register stage
     // of half a step, loaded during the current step's products and stored to
     // the other LDS buffer
-    float4 av[kVec];
+    uint4 av[kVec];
     uint4 bw0[TW][NM], bw1[TW][NM];
     float bs0[TW][NM], bs1[TW][NM];
     load_a(0, 0, av);
@@ -352,15 +350,36 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
                 if (tok >= count) continue;
                 const int p = it.p0 + tok;
                 if (GATEUP) {
+                    // hidden value as the down pass's float16 operand: row
+                    // `row` of this pass is column `row` of the down pass
                     const float gv = acc[0][t][mb][r], uv = acc[NM - 1][t][mb][r];
-                    out[(size_t)p * rows + row] = gv / (1.0f + expf(-gv)) * uv;
+                    const _Float16 hv = (_Float16)(gv / (1.0f + expf(-gv)) * uv);
+                    f.h16[(size_t)p * rows + (row & ~7) + perm8<WB>(row & 7)] =
+                        __builtin_bit_cast(uint16_t, hv);
                 } else {
                     const int orow = it.expert >= 0 ? min(max(f.perm[p], 0), f.A - 1) : p;
-                    out[(size_t)orow * rows + row] = acc[0][t][mb][r];
+                    f.o[(size_t)orow * rows + row] = acc[0][t][mb][r];
                 }
             }
         }
     }
+}
+
+// x [N][d] float32 -> x16 [N][d] float16, each 8-column group in the order
+// the MFMA weight operand takes its codes (one thread per group).
+template <int WB>
+__global__ __launch_bounds__(256) void stage_x16_kernel(const float *__restrict__ x, long long n8,
+                                                        uint16_t *__restrict__ x16)
+{
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n8) return;
+    const float4 a = reinterpret_cast<const float4 *>(x)[2 * i];
+    const float4 b = reinterpret_cast<const float4 *>(x)[2 * i + 1];
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    half8_t h;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[perm8<WB>(j)] = (_Float16)v[j];
+    reinterpret_cast<half8_t *>(x16)[i] = h;
 }
 
 }  // namespace
@@ -382,6 +401,17 @@ hipError_t run_mfma(const MfmaArgs &a, long long blocks, const hipEvent_t *ev, h
     return hipGetLastError();
 }
 
+hipError_t launch_stage_x16(const Fwd &f, hipStream_t s)
+{
+    const long long n8 = (long long)f.N * f.g.d / 8;
+    const unsigned blocks = (unsigned)((n8 + 255) / 256);
+    if (f.g.wbits == 8)
+        hipLaunchKernelGGL(stage_x16_kernel<8>, dim3(blocks), dim3(256), 0, s, f.x, n8, f.x16);
+    else
+        hipLaunchKernelGGL(stage_x16_kernel<4>, dim3(blocks), dim3(256), 0, s, f.x, n8, f.x16);
+    return hipGetLastError();
+}
+
 hipError_t launch_mfma(const Fwd &f, bool gateup, bool small, hipStream_t s)
 {
     MfmaArgs a;
@@ -390,7 +420,8 @@ hipError_t launch_mfma(const Fwd &f, bool gateup, bool small, hipStream_t s)
     a.n_items = small ? f.n_sitems : f.n_mitems;
     a.max_items = small ? f.max_sitems : f.max_mitems;
     const int rows = gateup ? f.g.f : f.g.d;
-    a.n_tiles = (rows + kNT - 1) / kNT;
+    const int mf = (small ? kMfmaSmallTokens : kMfmaBigTokens) / 16;
+    a.n_tiles = (rows + rows_per_wg(gateup, mf) - 1) / rows_per_wg(gateup, mf);
     const long long blocks = (long long)a.max_items * a.n_tiles;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;

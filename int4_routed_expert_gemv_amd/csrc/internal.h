@@ -56,8 +56,12 @@ struct Fwd {
     const float *w;          // [N][k] gate weights
     int k, N, A, has_shared; // A = N * k assignments
     const int32_t *union_ids, *n_union, *offsets, *perm;  // moe_union outputs
-    float *h;                // [A + N][f] hidden (workspace)
+    float *h;                // [A + N][f] hidden of the GEMV pass (workspace)
     float *o;                // [A + N][d] expert outputs (workspace)
+    // float16 operands of the matrix-core passes (workspace), each 8-column
+    // group in the order the MFMA weight operand takes its codes:
+    uint16_t *x16;           // [N][d] layer input
+    uint16_t *h16;           // [A + N][f] hidden
     float *y;                // [N][d] layer output
     Item *items;             // [max_items] work list (workspace)
     int32_t *n_items;        // [1]
@@ -100,8 +104,12 @@ hipError_t launch_down(const Fwd &f, hipStream_t s);
 bool mfma_supported(const Geo &g);
 constexpr int kMfmaBigTokens = 128;   // tokens per item of the large-group MFMA pass
 constexpr int kMfmaSmallTokens = 32;  // tokens per item of the small-group MFMA pass
+// fewer 128-token items than this go to the 32-token pass (when both run)
+constexpr int kMinBigItems = 32;
 // small = false: the 128-token items (mitems), true: the 32-token items (sitems)
 hipError_t launch_mfma(const Fwd &f, bool gateup, bool small, hipStream_t s);
+// x -> x16 for the matrix-core passes
+hipError_t launch_stage_x16(const Fwd &f, hipStream_t s);
 hipError_t launch_combine(const float *o, const float *w, int N, int k, int d, int A,
                           int has_shared, float *y, hipStream_t s);
 hipError_t launch_residual_rmsnorm(float *h, const float *y, float *a, int N, int d, float eps,

@@ -47,7 +47,10 @@ constexpr int kMaxSlices = 16;
 
 // Decode-sized batches: one workgroup per expert keeps its router row in
 // registers (read from HBM once) and dots it with the tokens, four tokens per
-// reduction round.
+// reduction round. Loads are issued unconditionally (past the row's end they
+// read its last float4, weighted by zero), so each round's loads are all in
+// flight before the first product waits.
+template <int RV>  // float4 of the row per thread (RV * 1024 >= d)
 __global__ __launch_bounds__(kRouterThreads) void router_gemv_kernel(
     const float *__restrict__ x, int N, int d, const float *__restrict__ wr,
     const float *__restrict__ b, int E, float *__restrict__ scores)
@@ -57,36 +60,40 @@ __global__ __launch_bounds__(kRouterThreads) void router_gemv_kernel(
     const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
     const int nq = d / 4;
     const float4 *row = reinterpret_cast<const float4 *>(wr + (size_t)e * d);
-    float4 w[kMaxRowVec];
+    int qi[RV];
+    float4 w[RV];
 #pragma unroll
-    for (int m = 0; m < kMaxRowVec; ++m) {
+    for (int m = 0; m < RV; ++m) {
         const int q = tid + m * kRouterThreads;
-        w[m] = q < nq ? row[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+        qi[m] = min(q, nq - 1);
+        w[m] = row[qi[m]];
+        if (q >= nq) w[m] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     const float bias = b ? b[e] : 0.0f;
     for (int t0 = 0; t0 < N; t0 += kTokGroup) {
         float acc[kTokGroup];
+        float4 v[kTokGroup][RV];
+#pragma unroll
+        for (int i = 0; i < kTokGroup; ++i) {
+            const float4 *xt = reinterpret_cast<const float4 *>(x + (size_t)min(t0 + i, N - 1) * d);
+#pragma unroll
+            for (int m = 0; m < RV; ++m) v[i][m] = xt[qi[m]];
+        }
 #pragma unroll
         for (int i = 0; i < kTokGroup; ++i) {
             acc[i] = 0.0f;
-            if (t0 + i >= N) continue;
-            const float4 *xt = reinterpret_cast<const float4 *>(x + (size_t)(t0 + i) * d);
 #pragma unroll
-            for (int m = 0; m < kMaxRowVec; ++m) {
-                const int q = tid + m * kRouterThreads;
-                if (q < nq) {
-                    const float4 v = xt[q];
-                    acc[i] = fmaf(w[m].x, v.x, acc[i]);
-                    acc[i] = fmaf(w[m].y, v.y, acc[i]);
-                    acc[i] = fmaf(w[m].z, v.z, acc[i]);
-                    acc[i] = fmaf(w[m].w, v.w, acc[i]);
-                }
+            for (int m = 0; m < RV; ++m) {
+                acc[i] = fmaf(w[m].x, v[i][m].x, acc[i]);
+                acc[i] = fmaf(w[m].y, v[i][m].y, acc[i]);
+                acc[i] = fmaf(w[m].z, v[i][m].z, acc[i]);
+                acc[i] = fmaf(w[m].w, v[i][m].w, acc[i]);
             }
         }
 #pragma unroll
         for (int i = 0; i < kTokGroup; ++i) {
-            const float v = wave_sum_dpp(acc[i]);
-            if (lane == 0) part[i][wv] = v;
+            const float s = wave_sum_dpp(acc[i]);
+            if (lane == 0) part[i][wv] = s;
         }
         __syncthreads();
         if (tid < kTokGroup && t0 + tid < N) {
@@ -320,9 +327,17 @@ hipError_t launch_router(const float *x, int N, int d, const float *wr, const fl
                          float *out, hipStream_t s)
 {
     if (N <= kGemvMaxTokens) {
-        if (d <= 4 * kMaxRowVec * kRouterThreads)
-            hipLaunchKernelGGL(router_gemv_kernel, dim3(E), dim3(kRouterThreads), 0, s, x, N, d,
-                               wr, b, E, out);
+        const int rv = (d / 4 + kRouterThreads - 1) / kRouterThreads;
+        auto go = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, dim3(E), dim3(kRouterThreads), 0, s, x, N, d, wr, b, E, out);
+        };
+        if (rv <= 1) go(router_gemv_kernel<1>);
+        else if (rv <= 2) go(router_gemv_kernel<2>);
+        else if (rv <= 4) go(router_gemv_kernel<4>);
+        else if (rv <= 6) go(router_gemv_kernel<6>);
+        else if (rv <= 8) go(router_gemv_kernel<8>);
+        else if (rv <= 12) go(router_gemv_kernel<12>);
+        else if (rv <= kMaxRowVec) go(router_gemv_kernel<kMaxRowVec>);
         else
             hipLaunchKernelGGL(router_gemv_stream_kernel, dim3(E), dim3(kRouterThreads), 0, s, x,
                                N, d, wr, b, E, out);

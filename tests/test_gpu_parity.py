@@ -236,3 +236,15 @@ def test_tiny_int8_passes(group, big, small):
                                scale_hi=0.02 / 16)
     cfg = dataclasses.replace(base, n_tokens=64, k=4, layers=(spec,))
     full_parity(cfg, mfma_min_tokens=big, mfma_small_min_tokens=small)
+
+
+@pytest.mark.parametrize("wbits,group", [(4, 32), (8, 0)])
+@pytest.mark.parametrize("k", [1, 3, 8])
+def test_single_token_several_experts(wbits, group, k):
+    """One token routed to k experts with d_ff of several units (the
+    one-item-per-union-slot GEMV path), int4 and int8."""
+    base = synth.CONFIGS["tiny"]
+    spec = dataclasses.replace(base.layer, f=512, wbits=wbits, group=group,
+                               scale_lo=base.layer.scale_lo / (16 if wbits == 8 else 1),
+                               scale_hi=base.layer.scale_hi / (16 if wbits == 8 else 1))
+    full_parity(dataclasses.replace(base, n_tokens=1, k=k, layers=(spec,)))
