@@ -43,16 +43,6 @@ template <int WB> struct Fmt;
 template <> struct Fmt<4> { static constexpr int epc = 32, xdw = 16; };
 template <> struct Fmt<8> { static constexpr int epc = 16, xdw = 8; };
 
-// (a & m) | o in one instruction (v_and_or_b32; the compiler emits an AND
-// and an OR for constant masks). m goes in a scalar register, o in a vector
-// register: one scalar operand per instruction.
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o)
-{
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
-    return r;
-}
-
 // The float16 pairs of one 16-byte chunk of offset-binary codes (1024 + code
 // + offset in each half), in the order the staged activations use.
 template <int WB>

@@ -69,8 +69,8 @@ __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast
 //   column order 0,4,1,5,2,6,3,7;
 // int8: the bytes of words 2s and 2s+1, in the column order 0,2,1,3,4,6,5,7.
 // Codes are offset binary: ORed into the mantissa of 1024 and the offset
-// taken off exactly, then one rounding by the scale.
-template <int WB>
+// taken off exactly, then (SCALED) one rounding by the scale.
+template <int WB, bool SCALED = true>
 __device__ __forceinline__ half8_t dequant8(const uint4 &u, int s, half2_t s2)
 {
     const uint32_t magic = 0x64006400u;
@@ -79,17 +79,21 @@ __device__ __forceinline__ half8_t dequant8(const uint4 &u, int s, half2_t s2)
     if constexpr (WB == 4) {
         const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
         const uint32_t w = d[s], m = 0x000F000Fu;
-        p[0] = (as_h2((w & m) | magic) - off) * s2;
-        p[1] = (as_h2(((w >> 4) & m) | magic) - off) * s2;
-        p[2] = (as_h2(((w >> 8) & m) | magic) - off) * s2;
-        p[3] = (as_h2(((w >> 12) & m) | magic) - off) * s2;
+        p[0] = as_h2(and_or(w, m, magic)) - off;
+        p[1] = as_h2(and_or(w >> 4, m, magic)) - off;
+        p[2] = as_h2(and_or(w >> 8, m, magic)) - off;
+        p[3] = as_h2(and_or(w >> 12, m, magic)) - off;
     } else {
         const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
         const uint32_t w0 = d[2 * s], w1 = d[2 * s + 1], m = 0x00FF00FFu;
-        p[0] = (as_h2((w0 & m) | magic) - off) * s2;
-        p[1] = (as_h2(((w0 >> 8) & m) | magic) - off) * s2;
-        p[2] = (as_h2((w1 & m) | magic) - off) * s2;
-        p[3] = (as_h2(((w1 >> 8) & m) | magic) - off) * s2;
+        p[0] = as_h2(and_or(w0, m, magic)) - off;
+        p[1] = as_h2(and_or(w0 >> 8, m, magic)) - off;
+        p[2] = as_h2(and_or(w1, m, magic)) - off;
+        p[3] = as_h2(and_or(w1 >> 8, m, magic)) - off;
+    }
+    if constexpr (SCALED) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = p[i] * s2;
     }
     half8_t r;
 #pragma unroll
@@ -122,7 +126,11 @@ struct MfmaArgs {
 // tokens. Weight loads run two unit steps
 // ahead of the matrix cores (registers), activations are double-buffered in
 // LDS.
-template <bool GATEUP, int WB, int MF>
+// POST: the codes enter the matrix cores unscaled (exact small integers) and
+// each step's float32 products are scaled per row afterwards; for scale
+// groups that cover whole unit steps (or whole rows), with fewer vector
+// instructions per code and no float16 rounding of code x scale.
+template <bool GATEUP, int WB, int MF, bool POST>
 __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
 {
     constexpr int MT = 16 * MF;  // tokens per item
@@ -243,19 +251,32 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
     // half of a unit step on LDS buffer `cur` and weights (bw, bs): k-steps
     // s_lo .. s_lo + NS/2 - 1 of 32, each lane's quarter q covering columns
     // QW q + 8s .. + 8
+    f32x4_t tmp[POST ? NM : 1][POST ? TW : 1][POST ? MF : 1];  // a step's unscaled products
     auto compute = [&](int cur, const uint4 (&bw)[TW][NM], const float (&bs)[TW][NM], int s_lo) {
         half2_t s2[TW][NM];
 #pragma unroll
         for (int t = 0; t < TW; ++t)
 #pragma unroll
             for (int m = 0; m < NM; ++m) s2[t][m] = half2_t{(_Float16)bs[t][m], (_Float16)bs[t][m]};
+        if constexpr (POST) {
+            if (s_lo == 0) {
+#pragma unroll
+                for (int m = 0; m < NM; ++m)
+#pragma unroll
+                    for (int t = 0; t < TW; ++t)
+#pragma unroll
+                        for (int mb = 0; mb < MF; ++mb)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) tmp[m][t][mb][r] = 0.0f;
+            }
+        }
 #pragma unroll
         for (int s = s_lo; s < s_lo + NS / 2; ++s) {
             half8_t bf[TW][NM];
 #pragma unroll
             for (int t = 0; t < TW; ++t)
 #pragma unroll
-                for (int m = 0; m < NM; ++m) bf[t][m] = dequant8<WB>(bw[t][m], s, s2[t][m]);
+                for (int m = 0; m < NM; ++m) bf[t][m] = dequant8<WB, !POST>(bw[t][m], s, s2[t][m]);
 #pragma unroll
             for (int mb = 0; mb < MF; ++mb) {
                 const half8_t af =
@@ -263,9 +284,29 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
 #pragma unroll
                 for (int t = 0; t < TW; ++t)
 #pragma unroll
-                    for (int m = 0; m < NM; ++m)
-                        acc[m][t][mb] =
-                            __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[t][m], acc[m][t][mb], 0, 0, 0);
+                    for (int m = 0; m < NM; ++m) {
+                        if constexpr (POST)
+                            tmp[m][t][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[t][m],
+                                                                                   tmp[m][t][mb], 0, 0, 0);
+                        else
+                            acc[m][t][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[t][m],
+                                                                                   acc[m][t][mb], 0, 0, 0);
+                    }
+            }
+        }
+        if constexpr (POST) {
+            if (s_lo + NS / 2 == NS) {
+                // the lane's accumulator column is its weight row (r16): one
+                // scale for its four tokens
+#pragma unroll
+                for (int m = 0; m < NM; ++m)
+#pragma unroll
+                    for (int t = 0; t < TW; ++t)
+#pragma unroll
+                        for (int mb = 0; mb < MF; ++mb)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                acc[m][t][mb][r] = fmaf(bs[t][m], tmp[m][t][mb][r], acc[m][t][mb][r]);
             }
         }
     };
@@ -389,15 +430,15 @@ bool mfma_supported(const Geo &g)
     return (g.wbits == 4 && g.ucols == MFmt<4>::UC) || (g.wbits == 8 && g.ucols == MFmt<8>::UC);
 }
 
-template <bool GATEUP, int WB, int MF>
+template <bool GATEUP, int WB, int MF, bool POST>
 hipError_t run_mfma(const MfmaArgs &a, long long blocks, const hipEvent_t *ev, hipStream_t s)
 {
     const dim3 grid((unsigned)blocks);
     if (ev[0] || ev[1])  // events taken by the dispatch itself, around this kernel only
-        hipExtLaunchKernelGGL((mfma_kernel<GATEUP, WB, MF>), grid, dim3(kThreads), 0, s, ev[0], ev[1],
+        hipExtLaunchKernelGGL((mfma_kernel<GATEUP, WB, MF, POST>), grid, dim3(kThreads), 0, s, ev[0], ev[1],
                               0, a);
     else
-        hipLaunchKernelGGL((mfma_kernel<GATEUP, WB, MF>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((mfma_kernel<GATEUP, WB, MF, POST>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -427,17 +468,27 @@ hipError_t launch_mfma(const Fwd &f, bool gateup, bool small, hipStream_t s)
     if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     const hipEvent_t *ev = small ? (gateup ? f.ev_sgu : f.ev_sdn) : (gateup ? f.ev_mgu : f.ev_mdn);
     constexpr int kSmall = kMfmaSmallTokens / 16, kBig = kMfmaBigTokens / 16;
+    // small items: scales after the products when every scale group covers
+    // whole unit steps (G == 0: whole rows)
+    const bool post = small && (f.g.group == 0 || f.g.group % f.g.ucols == 0);
     if (f.g.wbits == 8) {
+        if (post)
+            return gateup ? run_mfma<true, 8, kSmall, true>(a, blocks, ev, s)
+                          : run_mfma<false, 8, kSmall, true>(a, blocks, ev, s);
         if (small)
-            return gateup ? run_mfma<true, 8, kSmall>(a, blocks, ev, s)
-                          : run_mfma<false, 8, kSmall>(a, blocks, ev, s);
-        return gateup ? run_mfma<true, 8, kBig>(a, blocks, ev, s)
-                      : run_mfma<false, 8, kBig>(a, blocks, ev, s);
+            return gateup ? run_mfma<true, 8, kSmall, false>(a, blocks, ev, s)
+                          : run_mfma<false, 8, kSmall, false>(a, blocks, ev, s);
+        return gateup ? run_mfma<true, 8, kBig, false>(a, blocks, ev, s)
+                      : run_mfma<false, 8, kBig, false>(a, blocks, ev, s);
     }
+    if (post)
+        return gateup ? run_mfma<true, 4, kSmall, true>(a, blocks, ev, s)
+                      : run_mfma<false, 4, kSmall, true>(a, blocks, ev, s);
     if (small)
-        return gateup ? run_mfma<true, 4, kSmall>(a, blocks, ev, s)
-                      : run_mfma<false, 4, kSmall>(a, blocks, ev, s);
-    return gateup ? run_mfma<true, 4, kBig>(a, blocks, ev, s) : run_mfma<false, 4, kBig>(a, blocks, ev, s);
+        return gateup ? run_mfma<true, 4, kSmall, false>(a, blocks, ev, s)
+                      : run_mfma<false, 4, kSmall, false>(a, blocks, ev, s);
+    return gateup ? run_mfma<true, 4, kBig, false>(a, blocks, ev, s)
+                  : run_mfma<false, 4, kBig, false>(a, blocks, ev, s);
 }
 
 }  // namespace moe

@@ -116,6 +116,17 @@ hipError_t launch_residual_rmsnorm(float *h, const float *y, float *a, int N, in
                                    hipStream_t s);
 
 // ---- device helpers ----------------------------------------------------
+
+// (a & m) | o in one instruction (v_and_or_b32; the compiler emits an AND
+// and an OR for constant masks). m goes in a scalar register, o in a vector
+// register: one scalar operand per instruction.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
+    return r;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
