@@ -185,15 +185,15 @@ def main():
         l, bi = s % L_rot, s % nb
         x = abuf if stack else xs[bi]
         wr, b = routers[l]
+        # Route, Union and Learn in one call (moe_route_union), then the experts
         route = (vp(x.data_ptr()), N, d, vp(wr.data_ptr()), vp(b.data_ptr()), E, k,
-                 vp(ids.data_ptr()), vp(w.data_ptr()), vp(ws.data_ptr()), ws_bytes, stream)
-        uni = (vp(ids.data_ptr()), N, k, E, vp(union_ids.data_ptr()), vp(n_union.data_ptr()),
-               vp(offsets.data_ptr()), vp(perm.data_ptr()), stream)
-        hit = (vp(ids.data_ptr()), N, k, E, vp(counters[l].data_ptr()), stream)
+                 vp(ids.data_ptr()), vp(w.data_ptr()), vp(union_ids.data_ptr()),
+                 vp(n_union.data_ptr()), vp(offsets.data_ptr()), vp(perm.data_ptr()),
+                 vp(counters[l].data_ptr()), vp(ws.data_ptr()), ws_bytes, stream)
         fwd = (ctypes.byref(pools[l].desc), vp(x.data_ptr()), N, k, vp(w.data_ptr()),
                vp(union_ids.data_ptr()), vp(n_union.data_ptr()), vp(offsets.data_ptr()),
                vp(perm.data_ptr()), vp(y.data_ptr()), vp(ws.data_ptr()), ws_bytes, stream)
-        return route, uni, hit, fwd
+        return route, fwd
 
     plans = [step_args(s) for s in range(L_rot if stack else L_rot * nb)]
     n_plan = len(plans)
@@ -201,10 +201,8 @@ def main():
     hip_rt.hipMemcpyAsync.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
 
     def run_layer(s, ev=None):
-        route, uni, hit, fwd = plans[s % n_plan]
-        rc = Lb.moe_route_topk(*route)
-        rc |= Lb.moe_union(*uni)
-        rc |= Lb.moe_hit_count(*hit)
+        route, fwd = plans[s % n_plan]
+        rc = Lb.moe_route_union(*route)
         if ev is None:
             rc |= Lb.moe_expert_forward(*fwd)
         else:

@@ -151,6 +151,25 @@ moe_status moe_union(const int32_t *topk_ids, int n_tokens, int k, int n_experts
                      int32_t *expert_offsets, int32_t *perm, hipStream_t stream);
 
 /*
+ * Route, Union and (when counters is not NULL) Learn of one layer in one call:
+ * the same outputs as moe_route_topk, then moe_union, then moe_hit_count on
+ * the same arguments (same checks, nothing enqueued on an error). Batches of
+ * up to 16 tokens take the top-k, the union and the counting in a single
+ * workgroup after the router kernel (two kernel launches instead of four).
+ * workspace: at least moe_route_workspace_size(n_tokens, n_experts) bytes.
+ * Colibri pages: "Exact Architecture and Data-Flow Reconstruction", stages
+ * (1) Route, (2) Union and (5) Learn.
+ */
+moe_status moe_route_union(const float *x, int n_tokens, int d_model,
+                           const float *w_router, const float *b_router,
+                           int n_experts, int k,
+                           int32_t *topk_ids, float *topk_w,
+                           int32_t *union_ids, int32_t *n_union,
+                           int32_t *expert_offsets, int32_t *perm,
+                           uint64_t *counters /* may be NULL */,
+                           void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Expert math and combine:
  *   y[t] = shared(x_t) + sum_{j<k} topk_w[t][j] * E_{e(t,j)}(x_t),
  *   E(x) = Wd (silu(Wg x) * (Wu x)),

@@ -28,7 +28,7 @@ MOE_MAX_EXPERTS = 1024
 MOE_ALIGN = 256
 
 EXPORTED = [
-    "moe_route_topk", "moe_union", "moe_expert_forward", "moe_expert_forward_ex",
+    "moe_route_topk", "moe_union", "moe_route_union", "moe_expert_forward", "moe_expert_forward_ex",
     "moe_hit_count", "moe_residual_rmsnorm", "moe_route_workspace_size", "moe_forward_workspace_size",
     "moe_workspace_size", "moe_block_bytes", "moe_pack_expert", "moe_strerror",
 ]
@@ -80,6 +80,8 @@ def lib():
         P = ctypes.POINTER(PoolDesc)
         L.moe_route_topk.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, vp, vp, sz, vp]
         L.moe_union.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp]
+        L.moe_route_union.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, sz, vp]
         L.moe_expert_forward.argtypes = [P, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_expert_forward_ex.argtypes = [P, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                             ctypes.POINTER(ForwardOptions)]
@@ -92,7 +94,7 @@ def lib():
         L.moe_pack_expert.argtypes = [vp, P, vp]
         L.moe_strerror.argtypes = [i32]
         L.moe_strerror.restype = ctypes.c_char_p
-        for name in ("moe_route_topk", "moe_union", "moe_expert_forward",
+        for name in ("moe_route_topk", "moe_union", "moe_route_union", "moe_expert_forward",
                      "moe_expert_forward_ex", "moe_hit_count",
                      "moe_residual_rmsnorm", "moe_pack_expert"):
             getattr(L, name).restype = i32
@@ -179,6 +181,29 @@ def union(topk_ids, n_experts, union_ids, n_union, expert_offsets, perm, stream=
     N, k = topk_ids.shape
     _check(lib().moe_union(_ptr(topk_ids), N, k, n_experts, _ptr(union_ids), _ptr(n_union),
                            _ptr(expert_offsets), _ptr(perm), _stream(stream)), "moe_union")
+
+
+def route_union(x, w_router, b_router, k, topk_ids, topk_w, union_ids, n_union, expert_offsets,
+                perm, counters, workspace, stream=None):
+    """moe_route_union: route_topk, union and (counters not None) hit_count in one call."""
+    import torch
+    _expect(x, torch.float32, "x")
+    _expect(w_router, torch.float32, "w_router")
+    _expect(b_router, torch.float32, "b_router")
+    _expect(topk_w, torch.float32, "topk_w")
+    for t, n in ((topk_ids, "topk_ids"), (union_ids, "union_ids"), (n_union, "n_union"),
+                 (expert_offsets, "expert_offsets"), (perm, "perm")):
+        _expect(t, torch.int32, n)
+    if counters is not None and counters.dtype not in (torch.int64, torch.uint64):
+        raise TypeError("counters: expected a 64-bit integer tensor")
+    N, d = x.shape
+    E = w_router.shape[0]
+    _check(lib().moe_route_union(_ptr(x), N, d, _ptr(w_router), _ptr(b_router), E, k,
+                                 _ptr(topk_ids), _ptr(topk_w), _ptr(union_ids), _ptr(n_union),
+                                 _ptr(expert_offsets), _ptr(perm), _ptr(counters),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)),
+           "moe_route_union")
 
 
 def hit_count(topk_ids, n_experts, counters, stream=None):

@@ -267,6 +267,51 @@ moe_status moe_hit_count(const int32_t *topk_ids, int n_tokens, int k, int n_exp
     return MOE_OK;
 }
 
+moe_status moe_route_union(const float *x, int n_tokens, int d_model, const float *w_router,
+                           const float *b_router, int n_experts, int k, int32_t *topk_ids,
+                           float *topk_w, int32_t *union_ids, int32_t *n_union,
+                           int32_t *expert_offsets, int32_t *perm, uint64_t *counters,
+                           void *workspace, size_t ws_bytes, hipStream_t stream)
+{
+    // every check of moe_route_topk, moe_union and moe_hit_count, before any launch
+    if (n_tokens < 0 || d_model <= 0) return MOE_EINVAL;
+    moe_status st = check_k(k, n_experts);
+    if (st != MOE_OK) return st;
+    if (d_model % 32) return MOE_ESHAPE;
+    if ((long long)n_tokens * n_experts > 0x7FFFFFFFLL || (long long)n_tokens * d_model > 0x7FFFFFFFLL ||
+        (long long)n_tokens * k > 0x7FFFFFFFLL)
+        return MOE_ESHAPE;
+    if (n_tokens == 0) return MOE_OK;
+    if (!x || !w_router || !topk_ids || !topk_w || !union_ids || !n_union || !expert_offsets ||
+        !perm)
+        return MOE_EINVAL;
+    if (((uintptr_t)x % 16) || ((uintptr_t)w_router % 16)) return MOE_EALIGN;
+    if (counters && ((uintptr_t)counters % 8)) return MOE_EALIGN;
+    if (!workspace || ws_bytes < moe_route_workspace_size(n_tokens, n_experts))
+        return MOE_EWORKSPACE;
+    if (!aligned(workspace)) return MOE_EALIGN;
+    float *scores = static_cast<float *>(workspace);
+    const int P = router_slices(n_tokens, d_model, n_experts);
+    if (launch_router(x, n_tokens, d_model, w_router, b_router, n_experts, scores, stream) !=
+        hipSuccess)
+        return MOE_EHIP;
+    if (n_tokens <= route_tail_max_tokens())
+        return launch_route_tail(scores, P, b_router, n_tokens, n_experts, k, topk_ids, topk_w,
+                                 union_ids, n_union, expert_offsets, perm, counters,
+                                 stream) == hipSuccess
+                   ? MOE_OK
+                   : MOE_EHIP;
+    if (launch_topk(scores, P, b_router, n_tokens, n_experts, k, topk_ids, topk_w, stream) !=
+            hipSuccess ||
+        launch_union(topk_ids, n_tokens * k, n_experts, union_ids, n_union, expert_offsets, perm,
+                     stream) != hipSuccess)
+        return MOE_EHIP;
+    if (counters && launch_hit_count(topk_ids, n_tokens * k, n_experts, counters, stream) !=
+                        hipSuccess)
+        return MOE_EHIP;
+    return MOE_OK;
+}
+
 moe_status moe_expert_forward(const moe_expert_pool *pool, const float *x, int n_tokens, int k,
                               const float *topk_w, const int32_t *union_ids,
                               const int32_t *n_union, const int32_t *expert_offsets,

@@ -98,6 +98,12 @@ hipError_t launch_topk(const float *in, int P, const float *b, int N, int E, int
 hipError_t launch_union(const int32_t *ids, int A, int E, int32_t *union_ids, int32_t *n_union,
                         int32_t *offsets, int32_t *perm, hipStream_t s);
 hipError_t launch_hit_count(const int32_t *ids, int A, int E, uint64_t *counters, hipStream_t s);
+// Top-k, union and hit counting of a batch of at most route_tail_max_tokens()
+// tokens in one workgroup (counters may be null).
+int route_tail_max_tokens();
+hipError_t launch_route_tail(const float *in, int P, const float *b, int N, int E, int k,
+                             int32_t *ids, float *w, int32_t *union_ids, int32_t *n_union,
+                             int32_t *offsets, int32_t *perm, uint64_t *counters, hipStream_t s);
 int gemv_tokens_per_item(const Geo &g, int n_tokens);
 hipError_t launch_gateup(const Fwd &f, hipStream_t s);
 hipError_t launch_down(const Fwd &f, hipStream_t s);

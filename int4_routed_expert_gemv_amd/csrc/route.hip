@@ -8,14 +8,13 @@
 //   scores[t][e] = 1 / (1 + exp(-(b[e] + sum_i Wr[e][i] x[t][i])))  (float32)
 //   top-k on the float32 score, ties to the lower expert id, ids in rank order.
 #include "internal.h"
+#include "topk.h"
 
 namespace moe {
 namespace {
 
 constexpr int kRouterThreads = 256;
 constexpr int kMaxRowVec = 16;  // row of Wr cached in registers up to 16 float4 per thread
-
-__device__ __forceinline__ float sigmoidf(float l) { return 1.0f / (1.0f + expf(-l)); }
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v)
@@ -42,8 +41,6 @@ __device__ __forceinline__ float wave_sum_dpp(float v)
 constexpr int kTokGroup = 4;
 // batches up to this many tokens use the one-workgroup-per-expert GEMV router
 constexpr int kGemvMaxTokens = 16;
-// most slices of the contraction the GEMM router splits into
-constexpr int kMaxSlices = 16;
 
 // Decode-sized batches: one workgroup per expert keeps its router row in
 // registers (read from HBM once) and dots it with the tokens, four tokens per
@@ -226,80 +223,14 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(
     }
 }
 
-// Order-preserving map of float bits onto unsigned integers (NaN above +inf).
-__device__ __forceinline__ uint32_t sortable(float v) {
-    uint32_t u = __float_as_uint(v);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-constexpr int kMaxPerLane = MOE_MAX_EXPERTS / kWave;  // 16
-
-// One wave per token: k rounds of a wave-wide max over 64-bit keys
-// (sortable score, then inverted id so equal scores go to the lower id).
-// With P > 1 the input holds the router's raw partial sums [P][N][E]: the
-// score is sigmoid(sum over slices in order + bias).
+// One wave per token (the selection itself is topk_wave).
 __global__ __launch_bounds__(256) void topk_kernel(
     const float *__restrict__ in, int P, const float *__restrict__ b, int N, int E, int k,
     int32_t *__restrict__ ids, float *__restrict__ w)
 {
-    const int lane = threadIdx.x % kWave;
     const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     if (t >= N) return;
-    uint32_t hi[kMaxPerLane];
-    float sv[kMaxPerLane];
-    uint32_t taken = 0;
-#pragma unroll
-    for (int m = 0; m < kMaxPerLane; ++m) {
-        const int e = lane + m * kWave;
-        float v = 0.0f;
-        if (e < E) {
-            if (P == 1) {
-                v = in[(size_t)t * E + e];
-            } else {
-                // all slices' loads issued together (slices past P read slice
-                // P - 1 and are not added), then added in slice order
-                float part[kMaxSlices];
-#pragma unroll
-                for (int p = 0; p < kMaxSlices; ++p)
-                    part[p] = in[((size_t)min(p, P - 1) * N + t) * E + e];
-                float l = 0.0f;
-#pragma unroll
-                for (int p = 0; p < kMaxSlices; ++p)
-                    if (p < P) l += part[p];
-                v = sigmoidf(l + (b ? b[e] : 0.0f));
-            }
-        }
-        sv[m] = v;
-        hi[m] = e < E ? sortable(v) : 0u;
-        if (e >= E) taken |= 1u << m;
-    }
-    for (int j = 0; j < k; ++j) {
-        uint32_t bh = 0, bl = 0;  // best key of this lane: (hi, ~id)
-        int bm = -1;
-#pragma unroll
-        for (int m = 0; m < kMaxPerLane; ++m) {
-            if (taken & (1u << m)) continue;
-            uint32_t lo = 0xFFFFFFFFu - (uint32_t)(lane + m * kWave);
-            if (bm < 0 || hi[m] > bh || (hi[m] == bh && lo > bl)) { bh = hi[m]; bl = lo; bm = m; }
-        }
-        if (bm < 0) { bh = 0; bl = 0; }
-        float bs = bm >= 0 ? sv[0] : 0.0f;
-#pragma unroll
-        for (int m = 1; m < kMaxPerLane; ++m)
-            if (m == bm) bs = sv[m];
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            uint32_t oh = __shfl_xor(bh, o, kWave), ol = __shfl_xor(bl, o, kWave);
-            if (oh > bh || (oh == bh && ol > bl)) { bh = oh; bl = ol; }
-        }
-        const int id = (int)(0xFFFFFFFFu - bl);
-        if (bm >= 0 && lane + bm * kWave == id) {
-            // the lane holding the winner records it
-            taken |= 1u << bm;
-            ids[(size_t)t * k + j] = id;
-            w[(size_t)t * k + j] = bs;
-        }
-    }
+    topk_wave(in, P, b, N, E, k, t, ids, w, nullptr);
 }
 
 }  // namespace

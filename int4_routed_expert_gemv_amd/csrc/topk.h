@@ -1,0 +1,98 @@
+// topk.h - the per-token top-k selection of the Route stage, shared by the
+// top-k kernel and the fused route tail (top-k, union and counting in one
+// workgroup).
+//
+// Colibri pages, "Public Colibri Observation and Revision Ledger", section
+// "Exact Architecture and Data-Flow Reconstruction": sigmoid gate over all
+// experts (n_group = 1), float32 gate parameters; the k best experts per token.
+#pragma once
+
+#include "internal.h"
+
+namespace moe {
+
+// most slices of the contraction the GEMM router splits into
+constexpr int kMaxSlices = 16;
+constexpr int kMaxPerLane = MOE_MAX_EXPERTS / kWave;  // 16
+
+__device__ __forceinline__ float sigmoidf(float l) { return 1.0f / (1.0f + expf(-l)); }
+
+// Order-preserving map of float bits onto unsigned integers (NaN above +inf).
+__device__ __forceinline__ uint32_t sortable(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One wave selects token t's k best experts: k rounds of a wave-wide max over
+// 64-bit keys (sortable score, then inverted id so equal scores go to the
+// lower id). With P == 1, `in` holds the scores [N][E]; with P > 1 it holds
+// the router's raw partial sums [P][N][E] and the score is
+// sigmoid(sum over slices in order + bias). The lane holding each round's
+// winner writes ids/w[t * k + j] and, when lds_ids is not null,
+// lds_ids[t * k + j].
+__device__ __forceinline__ void topk_wave(const float *__restrict__ in, int P,
+                                          const float *__restrict__ b, int N, int E, int k, int t,
+                                          int32_t *__restrict__ ids, float *__restrict__ w,
+                                          int32_t *lds_ids)
+{
+    const int lane = threadIdx.x % kWave;
+    uint32_t hi[kMaxPerLane];
+    float sv[kMaxPerLane];
+    uint32_t taken = 0;
+#pragma unroll
+    for (int m = 0; m < kMaxPerLane; ++m) {
+        const int e = lane + m * kWave;
+        float v = 0.0f;
+        if (e < E) {
+            if (P == 1) {
+                v = in[(size_t)t * E + e];
+            } else {
+                // all slices' loads issued together (slices past P read slice
+                // P - 1 and are not added), then added in slice order
+                float part[kMaxSlices];
+#pragma unroll
+                for (int p = 0; p < kMaxSlices; ++p)
+                    part[p] = in[((size_t)min(p, P - 1) * N + t) * E + e];
+                float l = 0.0f;
+#pragma unroll
+                for (int p = 0; p < kMaxSlices; ++p)
+                    if (p < P) l += part[p];
+                v = sigmoidf(l + (b ? b[e] : 0.0f));
+            }
+        }
+        sv[m] = v;
+        hi[m] = e < E ? sortable(v) : 0u;
+        if (e >= E) taken |= 1u << m;
+    }
+    for (int j = 0; j < k; ++j) {
+        uint32_t bh = 0, bl = 0;  // best key of this lane: (hi, ~id)
+        int bm = -1;
+#pragma unroll
+        for (int m = 0; m < kMaxPerLane; ++m) {
+            if (taken & (1u << m)) continue;
+            uint32_t lo = 0xFFFFFFFFu - (uint32_t)(lane + m * kWave);
+            if (bm < 0 || hi[m] > bh || (hi[m] == bh && lo > bl)) { bh = hi[m]; bl = lo; bm = m; }
+        }
+        if (bm < 0) { bh = 0; bl = 0; }
+        float bs = bm >= 0 ? sv[0] : 0.0f;
+#pragma unroll
+        for (int m = 1; m < kMaxPerLane; ++m)
+            if (m == bm) bs = sv[m];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            uint32_t oh = __shfl_xor(bh, o, kWave), ol = __shfl_xor(bl, o, kWave);
+            if (oh > bh || (oh == bh && ol > bl)) { bh = oh; bl = ol; }
+        }
+        const int id = (int)(0xFFFFFFFFu - bl);
+        if (bm >= 0 && lane + bm * kWave == id) {
+            // the lane holding the winner records it
+            taken |= 1u << bm;
+            ids[(size_t)t * k + j] = id;
+            w[(size_t)t * k + j] = bs;
+            if (lds_ids) lds_ids[t * k + j] = id;
+        }
+    }
+}
+
+}  // namespace moe

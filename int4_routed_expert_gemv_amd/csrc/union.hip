@@ -13,19 +13,25 @@
 // ballots, never from the order in which atomics land, so the permutation is
 // the same on every run.
 #include "internal.h"
+#include "topk.h"
 
 namespace moe {
 namespace {
 
 constexpr int kUnionThreads = 1024;
+// s_waitcnt operand that waits for LDS operations only (lgkmcnt 0, vmcnt and
+// expcnt at their maxima, gfx9 encoding)
+constexpr int kLdsWait = 0xC07F;
 
-__global__ __launch_bounds__(kUnionThreads) void union_kernel(
-    const int32_t *__restrict__ ids, int A, int E, int32_t *__restrict__ union_ids,
-    int32_t *__restrict__ n_union, int32_t *__restrict__ offsets, int32_t *__restrict__ perm)
+// Union and permutation by one workgroup of kUnionThreads threads. ids may
+// point to global or LDS memory. On return cnt[e] (LDS) holds expert e's
+// number of assignments for e < E.
+__device__ __forceinline__ void union_block(const int32_t *ids, int A, int E,
+                                            int32_t *__restrict__ union_ids,
+                                            int32_t *__restrict__ n_union,
+                                            int32_t *__restrict__ offsets,
+                                            int32_t *__restrict__ perm, int *cnt, int *base)
 {
-    __shared__ int cnt[MOE_MAX_EXPERTS];
-    __shared__ int base[MOE_MAX_EXPERTS];
-    __shared__ int wsum[kUnionThreads / kWave];
     const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
 
     for (int e = tid; e < E; e += kUnionThreads) cnt[e] = 0;
@@ -75,7 +81,6 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(
         offsets[E] = (int)(tot / 2048);
         *n_union = (int)(tot % 2048);
     }
-    (void)wsum;
     __syncthreads();
 
     // stable scatter by one wave, 64 assignments at a time in ascending a: the
@@ -100,17 +105,55 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(
                 b = base[e];
             }
             // all reads of base[] finish before any lane writes it back
-            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_s_waitcnt(kLdsWait);
             __builtin_amdgcn_wave_barrier();
             if (valid) {
                 perm[b + rank] = a;
                 const bool last = (peers >> lane) == 1ull;  // highest peer lane
                 if (last) base[e] = b + rank + 1;
             }
-            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_s_waitcnt(kLdsWait);
             __builtin_amdgcn_wave_barrier();
         }
     }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kUnionThreads) void union_kernel(
+    const int32_t *__restrict__ ids, int A, int E, int32_t *__restrict__ union_ids,
+    int32_t *__restrict__ n_union, int32_t *__restrict__ offsets, int32_t *__restrict__ perm)
+{
+    __shared__ int cnt[MOE_MAX_EXPERTS];
+    __shared__ int base[MOE_MAX_EXPERTS];
+    union_block(ids, A, E, union_ids, n_union, offsets, perm, cnt, base);
+}
+
+// Route tail of a small batch (N <= kTailTokens): one wave per token selects
+// its top k from the router's output, then the same workgroup forms the union
+// and permutation of the N * k assignments and adds the per-expert counts to
+// the hit counters (counters may be null). Outputs equal those of the top-k,
+// union and hit-count kernels run in turn.
+constexpr int kTailTokens = kUnionThreads / kWave;  // 16
+
+__global__ __launch_bounds__(kUnionThreads) void route_tail_kernel(
+    const float *__restrict__ in, int P, const float *__restrict__ b, int N, int E, int k,
+    int32_t *__restrict__ ids, float *__restrict__ w, int32_t *__restrict__ union_ids,
+    int32_t *__restrict__ n_union, int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
+    unsigned long long *__restrict__ counters)
+{
+    __shared__ int32_t s_ids[kTailTokens * MOE_MAX_K];
+    __shared__ int cnt[MOE_MAX_EXPERTS];
+    __shared__ int base[MOE_MAX_EXPERTS];
+    const int tid = threadIdx.x, A = N * k;
+    for (int a = tid; a < A; a += kUnionThreads) s_ids[a] = -1;
+    __syncthreads();
+    const int t = tid / kWave;
+    if (t < N) topk_wave(in, P, b, N, E, k, t, ids, w, s_ids);
+    __syncthreads();
+    union_block(s_ids, A, E, union_ids, n_union, offsets, perm, cnt, base);
+    if (counters)
+        for (int e = tid; e < E; e += kUnionThreads)
+            if (cnt[e]) atomicAdd(&counters[e], (unsigned long long)cnt[e]);
 }
 
 constexpr int kHitThreads = 256;
@@ -140,6 +183,19 @@ hipError_t launch_union(const int32_t *ids, int A, int E, int32_t *union_ids, in
 {
     hipLaunchKernelGGL(union_kernel, dim3(1), dim3(kUnionThreads), 0, s, ids, A, E, union_ids,
                        n_union, offsets, perm);
+    return hipGetLastError();
+}
+
+int route_tail_max_tokens() { return kTailTokens; }
+
+hipError_t launch_route_tail(const float *in, int P, const float *b, int N, int E, int k,
+                             int32_t *ids, float *w, int32_t *union_ids, int32_t *n_union,
+                             int32_t *offsets, int32_t *perm, uint64_t *counters, hipStream_t s)
+{
+    if (N < 1 || N > kTailTokens) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(route_tail_kernel, dim3(1), dim3(kUnionThreads), 0, s, in, P, b, N, E, k,
+                       ids, w, union_ids, n_union, offsets, perm,
+                       reinterpret_cast<unsigned long long *>(counters));
     return hipGetLastError();
 }
 

@@ -17,30 +17,37 @@ def workspace(pool, N, k, device="cuda"):
 
 
 def run_layer(pool, x, wr, b, k, ids_in=None, w_in=None, counters=None, device="cuda",
-              mfma_min_tokens=None, mfma_small_min_tokens=None):
+              mfma_min_tokens=None, mfma_small_min_tokens=None, fused_route=False, ws=None):
     """route_topk (unless ids_in/w_in are given) -> union -> hit_count -> expert_forward
     (moe_expert_forward_ex with those thresholds when either is given; None
-    leaves a threshold at its default)."""
+    leaves a threshold at its default). fused_route: route, union and count
+    with one moe_route_union call instead. ws: a workspace to reuse."""
     N, d = x.shape
     E = pool.desc.n_experts
     xd = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(device)
-    ws = workspace(pool, N, k, device)
+    if ws is None:
+        ws = workspace(pool, N, k, device)
+    union_ids = torch.full((E,), -1, dtype=torch.int32, device=device)
+    n_union = torch.zeros(1, dtype=torch.int32, device=device)
+    offsets = torch.zeros(E + 1, dtype=torch.int32, device=device)
+    perm = torch.full((N * k,), -1, dtype=torch.int32, device=device)
+    cnt = torch.zeros(E, dtype=torch.int64, device=device) if counters is None else counters
     if ids_in is None:
         wrd = torch.from_numpy(np.ascontiguousarray(wr, np.float32)).to(device)
         bd = None if b is None else torch.from_numpy(np.ascontiguousarray(b, np.float32)).to(device)
         ids = torch.empty((N, k), dtype=torch.int32, device=device)
         w = torch.empty((N, k), dtype=torch.float32, device=device)
-        moe.route_topk(xd, wrd, bd, k, ids, w, ws)
+        if fused_route:
+            moe.route_union(xd, wrd, bd, k, ids, w, union_ids, n_union, offsets, perm, cnt, ws)
+        else:
+            moe.route_topk(xd, wrd, bd, k, ids, w, ws)
     else:
+        assert not fused_route
         ids = torch.from_numpy(np.ascontiguousarray(ids_in, np.int32)).to(device)
         w = torch.from_numpy(np.ascontiguousarray(w_in, np.float32)).to(device)
-    union_ids = torch.full((E,), -1, dtype=torch.int32, device=device)
-    n_union = torch.zeros(1, dtype=torch.int32, device=device)
-    offsets = torch.zeros(E + 1, dtype=torch.int32, device=device)
-    perm = torch.full((N * k,), -1, dtype=torch.int32, device=device)
-    moe.union(ids, E, union_ids, n_union, offsets, perm)
-    cnt = torch.zeros(E, dtype=torch.int64, device=device) if counters is None else counters
-    moe.hit_count(ids, E, cnt)
+    if not fused_route:
+        moe.union(ids, E, union_ids, n_union, offsets, perm)
+        moe.hit_count(ids, E, cnt)
     y = torch.empty((N, d), dtype=torch.float32, device=device)
     opts = None
     if mfma_min_tokens is not None or mfma_small_min_tokens is not None:

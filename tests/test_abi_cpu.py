@@ -42,6 +42,36 @@ def _pool(d=256, f=128, E=16, wbits=4, group=32, pool=4096, stride=None, shared=
 FAKE = 1 << 20  # aligned non-null address: never dereferenced, every call below fails first
 
 
+def test_route_union_argument_checks():
+    """moe_route_union makes every check of the three calls it stands for
+    before launching anything, on both sides of the one-workgroup tail size."""
+    L = moe.lib()
+    big = 1 << 30
+
+    def call(x=FAKE, N=4, d=256, wr=FAKE, E=16, k=1, ids=FAKE, w=FAKE, uid=FAKE, nu=FAKE,
+             off=FAKE, perm=FAKE, cnt=None, ws=FAKE, wsb=big):
+        return L.moe_route_union(x, N, d, wr, None, E, k, ids, w, uid, nu, off, perm, cnt, ws,
+                                 wsb, None)
+
+    for N in (4, 40):
+        assert call(N=N, k=0) == moe.MOE_EINVAL
+        assert call(N=N, k=17) == moe.MOE_EINVAL
+        assert call(N=N, E=2000, k=8) == moe.MOE_EINVAL
+        assert call(N=-1) == moe.MOE_EINVAL
+        assert call(N=N, x=None) == moe.MOE_EINVAL
+        assert call(N=N, uid=None) == moe.MOE_EINVAL
+        assert call(N=N, nu=None) == moe.MOE_EINVAL
+        assert call(N=N, off=None) == moe.MOE_EINVAL
+        assert call(N=N, perm=None) == moe.MOE_EINVAL
+        assert call(N=N, d=48) == moe.MOE_ESHAPE
+        assert call(N=N, wsb=10) == moe.MOE_EWORKSPACE
+        assert call(N=N, ws=None) == moe.MOE_EWORKSPACE
+        assert call(N=N, x=FAKE + 4) == moe.MOE_EALIGN
+        assert call(N=N, cnt=FAKE + 4) == moe.MOE_EALIGN
+        assert call(N=N, ws=FAKE + 16) == moe.MOE_EALIGN
+    assert call(N=0, x=None, ids=None) == moe.MOE_OK  # nothing to do
+
+
 def test_route_topk_argument_checks():
     L = moe.lib()
     ws = FAKE

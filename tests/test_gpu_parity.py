@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+import int4_routed_expert_gemv_amd as moe
 import oracle
 import synth
 from tests import layer_cases as lc
@@ -58,7 +59,8 @@ def oracle_then_pool(cfg, layer=0, x=None):
     return spec, x, wr, b, blocks, shared, nre
 
 
-def full_parity(cfg, layer=0, mfma_min_tokens=None, mfma_small_min_tokens=None):
+def full_parity(cfg, layer=0, mfma_min_tokens=None, mfma_small_min_tokens=None,
+                fused_route=False):
     spec, x, wr, b, blocks, shared, nre = oracle_then_pool(cfg, layer)
     say(f"[{cfg.name}] N={cfg.n_tokens} k={cfg.k} d={spec.d} f={spec.f} E={spec.n_experts} "
         f"wbits={spec.wbits} G={spec.group} redrawn={nre}")
@@ -66,9 +68,10 @@ def full_parity(cfg, layer=0, mfma_min_tokens=None, mfma_small_min_tokens=None):
                             spec.group)
     pool = upload_pool(spec, blocks, shared)   # packs the blocks in place: oracle first
     say(f"[{cfg.name}] oracle done, union={len(ref['union_ids'])}; running GPU step "
-        f"(mfma_min_tokens={mfma_min_tokens}, mfma_small_min_tokens={mfma_small_min_tokens})")
+        f"(mfma_min_tokens={mfma_min_tokens}, mfma_small_min_tokens={mfma_small_min_tokens}, "
+        f"fused_route={fused_route})")
     got = run_layer(pool, x, wr, b, cfg.k, mfma_min_tokens=mfma_min_tokens,
-                    mfma_small_min_tokens=mfma_small_min_tokens)
+                    mfma_small_min_tokens=mfma_small_min_tokens, fused_route=fused_route)
     check_routing(got, ref, spec.n_experts)
     err = check_y(got["y"], ref["y"])
     say(f"[{cfg.name}] parity ok, max rel err {err:.2e}")
@@ -248,3 +251,62 @@ def test_single_token_several_experts(wbits, group, k):
                                scale_lo=base.layer.scale_lo / (16 if wbits == 8 else 1),
                                scale_hi=base.layer.scale_hi / (16 if wbits == 8 else 1))
     full_parity(dataclasses.replace(base, n_tokens=1, k=k, layers=(spec,)))
+
+
+@pytest.mark.parametrize("N,k", [(1, 1), (4, 1), (3, 8), (16, 5), (17, 2), (64, 4)])
+def test_route_union_against_oracle(N, k):
+    """moe_route_union (one call for route, union and counting; one tail
+    workgroup up to 16 tokens, the separate kernels above) on the tiny layer."""
+    full_parity(tiny(n_tokens=N, k=k), fused_route=True)
+
+
+@pytest.mark.parametrize("N,k", [(1, 1), (1, 8), (8, 8), (16, 8), (17, 8)])
+@pytest.mark.parametrize("with_counters", [True, False])
+def test_route_union_equals_separate_calls(N, k, with_counters):
+    """Bit for bit the outputs of moe_route_topk, moe_union and moe_hit_count
+    on the decode layer's router (6144 x 256), counters accumulated in place."""
+    cfg = dataclasses.replace(synth.CONFIGS["decode64"], n_tokens=N, k=k)
+    x, wr, b, _, _ = lc.layer_inputs(cfg, 0)
+    E = wr.shape[0]
+    say(f"[route_union] N={N} k={k} counters={with_counters}")
+    dev = "cuda"
+    xd, wrd, bd = (torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev) for a in (x, wr, b))
+    ws = torch.empty(max(1, moe.route_workspace_size(N, E)), dtype=torch.uint8, device=dev)
+    outs = []
+    for fused in (False, True):
+        ids = torch.full((N, k), -7, dtype=torch.int32, device=dev)
+        w = torch.full((N, k), -7.0, dtype=torch.float32, device=dev)
+        uid = torch.full((E,), -7, dtype=torch.int32, device=dev)
+        nu = torch.full((1,), -7, dtype=torch.int32, device=dev)
+        off = torch.full((E + 1,), -7, dtype=torch.int32, device=dev)
+        perm = torch.full((N * k,), -7, dtype=torch.int32, device=dev)
+        cnt = torch.arange(E, dtype=torch.int64, device=dev) * 3 if with_counters else None
+        if fused:
+            moe.route_union(xd, wrd, bd, k, ids, w, uid, nu, off, perm, cnt, ws)
+        else:
+            moe.route_topk(xd, wrd, bd, k, ids, w, ws)
+            moe.union(ids, E, uid, nu, off, perm)
+            if with_counters:
+                moe.hit_count(ids, E, cnt)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy() for t in (ids, w, uid, nu, off, perm)] +
+                    ([cnt.cpu().numpy()] if with_counters else []))
+    for a, c in zip(*outs):
+        np.testing.assert_array_equal(a, c)
+    ref_ids, _ = oracle.topk(oracle.router(x, wr, b), k)
+    np.testing.assert_array_equal(outs[1][0], ref_ids)
+
+
+def test_workspace_reuse_across_sizes():
+    """One workspace over calls of different sizes on the GEMV-only path:
+    nothing a call leaves in the workspace changes the next call's result
+    (each equals a call on a fresh workspace bit for bit)."""
+    cfg = tiny(n_tokens=9, k=3)
+    spec, x, wr, b, blocks, shared, _ = oracle_then_pool(cfg)
+    pool = upload_pool(spec, blocks, shared)
+    ws = workspace(pool, 9, 3)
+    for n in (1, 9, 2, 9, 1):
+        say(f"[reuse] N={n}")
+        a = run_layer(pool, x[:n], wr, b, 3, mfma_min_tokens=-1, mfma_small_min_tokens=-1, ws=ws)
+        c = run_layer(pool, x[:n], wr, b, 3, mfma_min_tokens=-1, mfma_small_min_tokens=-1)
+        np.testing.assert_array_equal(a["y"], c["y"])
