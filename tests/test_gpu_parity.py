@@ -310,3 +310,36 @@ def test_workspace_reuse_across_sizes():
         a = run_layer(pool, x[:n], wr, b, 3, mfma_min_tokens=-1, mfma_small_min_tokens=-1, ws=ws)
         c = run_layer(pool, x[:n], wr, b, 3, mfma_min_tokens=-1, mfma_small_min_tokens=-1)
         np.testing.assert_array_equal(a["y"], c["y"])
+
+
+@pytest.mark.parametrize("N,k", [(1, 1), (1, 4), (3, 2)])
+def test_without_shared_expert(N, k):
+    """A pool with no shared expert: y is the gate-weighted sum of the routed
+    experts alone."""
+    cfg = tiny(n_tokens=N, k=k)
+    spec, x, wr, b, blocks, _, _ = oracle_then_pool(cfg)
+    say(f"[no shared] N={N} k={k}")
+    ref = oracle.layer_step(x, wr, b, k, blocks, None, spec.d, spec.f, spec.wbits, spec.group)
+    pool = upload_pool(spec, blocks, None)
+    got = run_layer(pool, x, wr, b, k, fused_route=True)
+    check_routing(got, ref, spec.n_experts)
+    check_y(got["y"], ref["y"])
+
+
+@pytest.mark.parametrize("wbits", [4, 8])
+def test_single_token_zero_gate_equals_dropped_slot(wbits):
+    """One token, k = 2 with the second gate weight zero: bit for bit the
+    k = 1 result (that expert adds exact zeros in the combine)."""
+    base = synth.CONFIGS["tiny"]
+    spec = dataclasses.replace(base.layer, f=512, wbits=wbits, group=32 if wbits == 4 else 0,
+                               scale_lo=base.layer.scale_lo / (16 if wbits == 8 else 1),
+                               scale_hi=base.layer.scale_hi / (16 if wbits == 8 else 1))
+    cfg = dataclasses.replace(base, n_tokens=1, k=2, layers=(spec,))
+    _, x, wr, b, blocks, shared, _ = oracle_then_pool(cfg)
+    ids, w = oracle.topk(oracle.router(x, wr, b), 2)
+    pool = upload_pool(spec, blocks, shared)
+    w0 = w.copy()
+    w0[:, 1] = 0.0
+    r2 = run_layer(pool, x, wr, b, 2, ids_in=ids, w_in=w0)
+    r1 = run_layer(pool, x, wr, b, 1, ids_in=ids[:, :1].copy(), w_in=w[:, :1].copy())
+    np.testing.assert_array_equal(r2["y"], r1["y"])
