@@ -2,8 +2,9 @@
 """Throughput of the routed-expert layer step on one MI355X.
 
 A step is one pass of the whole layer step over one batch: route + top-k,
-union + permutation, hit counters, expert math + combine (four C-ABI calls,
-all on one stream). Inputs are synthetic and already resident in HBM.
+union + permutation and hit counters (moe_route_union), then expert math +
+combine (moe_expert_forward), on one stream. Inputs are synthetic and
+already resident in HBM.
 
 Default workload ("decode1"): one GLM-5.2-shaped decode layer (d_model 6144,
 d_ff 2048, 256 routed + 1 shared int4 experts with float32 scales per 128,
@@ -17,6 +18,9 @@ Prints one JSON line. `roofline` is for the gate/up kernel of the pass
 with HIP events that the kernel dispatches take on the library's stream, on
 an evenly spread sample of about 64 timed steps (event-taking launches cost
 the host tens of microseconds, so the other steps run without them).
+`roofline.measured_ceiling` is what the simplest kernel of the same kind
+reaches on this GPU (a plain streaming read of the same bytes per launch, or
+a loop of independent matrix-core products), beside the published peak.
 `cpu_baseline` is the CPU oracle timed on this host on a bounded sample of
 the same workload.
 """
@@ -110,7 +114,11 @@ class Hip:
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
-        assert self.L.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        if self.L.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            # an event that no launch took: clear the runtime's last error so
+            # that later checks (torch's included) do not report it
+            self.L.hipGetLastError()
+            raise AssertionError("event not recorded")
         return ms.value
 
 
@@ -358,9 +366,9 @@ def main():
     labels = {"gemv": ("gemv_kernel<gate/up> (expert gate and up projections, SiLU product)",
                        "moe::gemv_kernel<true, 4, 1"),
               "small": ("mfma_kernel<gate/up, 32 tokens> (small-group gate and up on the "
-                        "matrix cores)", "moe::mfma_kernel<true, 2>"),
+                        "matrix cores)", "moe::mfma_kernel<true, 4, 2"),
               "mfma": ("mfma_kernel<gate/up, 128 tokens> (grouped GEMM of gate and up, SiLU "
-                       "product)", "moe::mfma_kernel<true, 8>")}
+                       "product)", "moe::mfma_kernel<true, 4, 8")}
     roof = None
     if passes:
         # the roofline is reported for the pass whose gate/up launch is longest
@@ -376,6 +384,8 @@ def main():
         roof["traffic"] = measured_traffic(args.config, labels[top][1])
         roof["kernel"] = labels[top][0]
         roof["passes"] = passes
+        roof["measured_ceiling"] = measured_ceiling(moe, hip, torch, roof["bound"],
+                                                    pz["bytes_per_launch"], roof["achieved"])
 
     result = {
         "metric": METRIC,
@@ -407,6 +417,63 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, spec, args, xs.cpu().numpy())
     print(json.dumps(result), flush=True)
+
+
+def measured_ceiling(moe, hip, torch, bound, bytes_per_launch, achieved):
+    """What this GPU delivers to the simplest kernel of the same kind, beside
+    the published peak: for an HBM-bound kernel, a plain streaming read of the
+    same bytes per launch (moe_probe_stream_read, best of three wave shapes,
+    buffers rotated past the 256 MB Infinity Cache); for the matrix-core pass,
+    a loop of independent float16 MFMA products (moe_probe_mfma_f16). Timed
+    with HIP events taken by the probe launches themselves."""
+    import numpy as np
+    L = moe.lib()
+    vp = ctypes.c_void_p
+    stream = vp(torch.cuda.current_stream().cuda_stream)
+    ev = [hip.event() for _ in range(2)]
+    if bound == "hbm":
+        nbytes = int(bytes_per_launch) // 1024 * 1024
+        if nbytes < 1024:
+            return None
+        n_buf = max(2, -(-(1 << 30) // nbytes))
+        bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(n_buf)]
+        sink = torch.empty(nbytes // 1024 + 1, dtype=torch.int32, device="cuda")
+        best = None
+        for ub, nw in ((3, 4), (6, 4), (12, 8)):
+            ts = []
+            for i in range(23):
+                rc = L.moe_probe_stream_read(vp(bufs[i % n_buf].data_ptr()), nbytes, ub, nw,
+                                             vp(sink.data_ptr()), sink.numel(), vp(ev[0]), vp(ev[1]),
+                                             stream)
+                assert rc == 0, rc
+                torch.cuda.synchronize()
+                if i >= 3:
+                    ts.append(hip.elapsed_ms(ev[0], ev[1]))
+            us = float(np.mean(ts)) * 1e3
+            if best is None or us < best[0]:
+                best = (us, ub, nw)
+        del bufs
+        value = nbytes / 1e9 / (best[0] * 1e-6)
+        out = {"what": f"plain streaming read of {nbytes} B per launch, {best[1]} KB per wave, "
+                       f"{best[2]}-wave workgroups ({best[0]:.2f} us)",
+               "value": value, "unit": "GB/s", "frac": achieved / value}
+    else:
+        wgs, iters = 2048, 1000
+        o = torch.empty(4 * wgs, dtype=torch.float32, device="cuda")
+        ts = []
+        for i in range(13):
+            assert L.moe_probe_mfma_f16(vp(o.data_ptr()), wgs, iters, vp(ev[0]), vp(ev[1]), stream) == 0
+            torch.cuda.synchronize()
+            if i >= 3:
+                ts.append(hip.elapsed_ms(ev[0], ev[1]))
+        sec = float(np.mean(ts)) * 1e-3
+        value = wgs * 4 * iters * 4 * 16384 / sec / 1e12
+        out = {"what": f"loop of independent v_mfma_f32_16x16x32_f16 on register operands, "
+                       f"{wgs} workgroups of 4 waves",
+               "value": value, "unit": "TFLOP/s", "frac": achieved / value}
+    for e in ev:
+        hip.L.hipEventDestroy(e)
+    return out
 
 
 def cpu_baseline(cfg, spec, args, xs_host):

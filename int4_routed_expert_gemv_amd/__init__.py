@@ -34,6 +34,10 @@ EXPORTED = [
 ]
 
 
+# measured-ceiling probes (include/moe_probe.h), not part of the layer step
+PROBE_EXPORTED = ["moe_probe_stream_read", "moe_probe_mfma_f16"]
+
+
 class MoeError(RuntimeError):
     def __init__(self, status: int, call: str):
         self.status = status
@@ -92,11 +96,13 @@ def lib():
         L.moe_workspace_size.argtypes = [P, i32, i32]
         L.moe_block_bytes.argtypes = [i32, i32, i32, i32]
         L.moe_pack_expert.argtypes = [vp, P, vp]
+        L.moe_probe_stream_read.argtypes = [vp, sz, i32, i32, vp, sz, vp, vp, vp]
+        L.moe_probe_mfma_f16.argtypes = [vp, i32, i32, vp, vp, vp]
         L.moe_strerror.argtypes = [i32]
         L.moe_strerror.restype = ctypes.c_char_p
         for name in ("moe_route_topk", "moe_union", "moe_route_union", "moe_expert_forward",
                      "moe_expert_forward_ex", "moe_hit_count",
-                     "moe_residual_rmsnorm", "moe_pack_expert"):
+                     "moe_residual_rmsnorm", "moe_pack_expert", *PROBE_EXPORTED):
             getattr(L, name).restype = i32
         for name in ("moe_route_workspace_size", "moe_forward_workspace_size",
                      "moe_workspace_size", "moe_block_bytes"):

@@ -17,20 +17,35 @@ HEADER = os.path.join(ROOT, "include", "moe.h")
 pytestmark = pytest.mark.skipif(not os.path.exists(moe.LIB_PATH), reason="libmoe.so not built")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
+    probes = declared_functions(os.path.join(ROOT, "include", "moe_probe.h"))
     assert set(names) == set(moe.EXPORTED)
+    assert set(probes) == set(moe.PROBE_EXPORTED)
     out = subprocess.check_output(["nm", "-D", "--defined-only", moe.LIB_PATH], text=True)
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
-    for n in names:
+    for n in names + probes:
         assert n in exported, n
         assert hasattr(moe.lib(), n)
+
+
+def test_probe_argument_checks():
+    L = moe.lib()
+    # size not a multiple of 1024, bad batch, bad workgroup, sink too small, misaligned
+    assert L.moe_probe_stream_read(FAKE, 1000, 3, 4, FAKE, 1 << 20, None, None, None) == moe.MOE_EINVAL
+    assert L.moe_probe_stream_read(FAKE, 1 << 20, 5, 4, FAKE, 1 << 20, None, None, None) == moe.MOE_EINVAL
+    assert L.moe_probe_stream_read(FAKE, 1 << 20, 3, 17, FAKE, 1 << 20, None, None, None) == moe.MOE_EINVAL
+    assert L.moe_probe_stream_read(FAKE, 1 << 20, 3, 4, FAKE, 10, None, None, None) == moe.MOE_EINVAL
+    assert L.moe_probe_stream_read(FAKE + 4, 1 << 20, 3, 4, FAKE, 1 << 20, None, None, None) == moe.MOE_EALIGN
+    assert L.moe_probe_stream_read(None, 1 << 20, 3, 4, FAKE, 1 << 20, None, None, None) == moe.MOE_EINVAL
+    assert L.moe_probe_mfma_f16(None, 4, 4, None, None, None) == moe.MOE_EINVAL
+    assert L.moe_probe_mfma_f16(FAKE, 0, 4, None, None, None) == moe.MOE_EINVAL
 
 
 def _pool(d=256, f=128, E=16, wbits=4, group=32, pool=4096, stride=None, shared=None):
