@@ -8,8 +8,8 @@
 // scales).
 //
 // For one expert and up to MT of its tokens (MT = 128 for large groups, 32
-// for small ones), a workgroup of 4 waves computes 128 output rows (of gate
-// and up together, or of down) over the full contraction:
+// for small ones), a workgroup of 4 or 8 waves computes 128 output rows (of
+// gate and up together), or 128 / 256 rows of down, over the full contraction:
 //   gate/up:  h[p][r] = silu(sum_c Wg[r][c] x_t[c]) * (sum_c Wu[r][c] x_t[c])
 //   down:     o[out(p)][r] = sum_c Wd[r][c] h[p][c]
 // on v_mfma_f32_16x16x32_f16 (float16 products, float32 accumulation):
@@ -25,7 +25,7 @@
 //    (x converted once per call by stage_x16_kernel, h written so by the
 //    gate/up epilogue) and are copied into LDS one unit step at a time,
 //    double-buffered, loaded one step ahead;
-//  * each wave owns two or four unit rows and all MT tokens; weight
+//  * each wave owns one or two unit rows and all MT tokens; weight
 //    loads run two steps ahead of the matrix cores.
 // Workgroups are mapped so that those sharing an expert (and so its weights
 // and its tokens) land on the same XCD and share its L2.
@@ -40,18 +40,20 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-// unit rows per wave: 2 for gate/up (two matrices); for down 4 with
-// 128-token items (the same products per activation read as gate/up), 2 with
-// 32-token items (registers for more waves)
+// Waves per workgroup and unit rows per wave. 32-token items: 4 waves of 2
+// unit rows. 128-token items: 8 waves (two per SIMD, so one wave's products
+// overlap the other's operand work) of 1 unit row for gate/up (two matrices)
+// or 2 for down; their accumulators (128 tokens x the wave's rows) then fit
+// the registers of two waves per SIMD. Either way a workgroup covers 128
+// rows of gate/up or 128 / 256 rows of down.
+__host__ __device__ constexpr int waves_per_wg(int mf) { return mf < 8 ? 4 : 8; }
 __host__ __device__ constexpr int tiles_per_wave(bool gateup, int mf)
 {
-    return gateup || mf < 8 ? 2 : 4;
+    return mf < 8 ? 2 : (gateup ? 1 : 2);
 }
 __host__ __device__ constexpr int rows_per_wg(bool gateup, int mf)
 {
-    return kWaves * tiles_per_wave(gateup, mf) * kUnitRows;
+    return waves_per_wg(mf) * tiles_per_wave(gateup, mf) * kUnitRows;
 }
 constexpr int kXcds = 8;
 
@@ -122,7 +124,7 @@ struct MfmaArgs {
 };
 
 // One workgroup: one MFMA item (<= MT tokens of one expert) x
-// rows_per_wg(GATEUP, MF) rows; each wave owns 32 or 64 rows and all MT
+// rows_per_wg(GATEUP, MF) rows; each wave owns 16 or 32 rows and all MT
 // tokens. Weight loads run two unit steps
 // ahead of the matrix cores (registers), activations are double-buffered in
 // LDS.
@@ -131,8 +133,9 @@ struct MfmaArgs {
 // groups that cover whole unit steps (or whole rows), with fewer vector
 // instructions per code and no float16 rounding of code x scale.
 template <bool GATEUP, int WB, int MF, bool POST>
-__global__ __launch_bounds__(kThreads, 1) void mfma_kernel(MfmaArgs ma)
+__global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs ma)
 {
+    constexpr int kThreads = waves_per_wg(MF) * 64;
     constexpr int MT = 16 * MF;  // tokens per item
     constexpr int NM = GATEUP ? 2 : 1;
     constexpr int TW = tiles_per_wave(GATEUP, MF);
@@ -433,6 +436,7 @@ bool mfma_supported(const Geo &g)
 template <bool GATEUP, int WB, int MF, bool POST>
 hipError_t run_mfma(const MfmaArgs &a, long long blocks, const hipEvent_t *ev, hipStream_t s)
 {
+    constexpr int kThreads = waves_per_wg(MF) * 64;
     const dim3 grid((unsigned)blocks);
     if (ev[0] || ev[1])  // events taken by the dispatch itself, around this kernel only
         hipExtLaunchKernelGGL((mfma_kernel<GATEUP, WB, MF, POST>), grid, dim3(kThreads), 0, s, ev[0], ev[1],
