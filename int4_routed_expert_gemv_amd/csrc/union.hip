@@ -23,6 +23,17 @@ constexpr int kUnionThreads = 1024;
 // expcnt at their maxima, gfx9 encoding)
 constexpr int kLdsWait = 0xC07F;
 
+__device__ __forceinline__ int wave_incl_scan_int(int v)
+{
+    const int lane = threadIdx.x % kWave;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int u = __shfl_up(v, o, kWave);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
 // Union and permutation by one workgroup of kUnionThreads threads. ids may
 // point to global or LDS memory. On return cnt[e] (LDS) holds expert e's
 // number of assignments for e < E.
@@ -119,6 +130,76 @@ __device__ __forceinline__ void union_block(const int32_t *ids, int A, int E,
     __syncthreads();
 }
 
+// The same union, permutation and counts for at most 64 assignments, by one
+// wave (wave 0 of the workgroup; no workgroup barrier): lane a holds
+// assignment a; lane l owns experts l * PE .. l * PE + PE - 1 for the prefix
+// sums (PE = ceil(E / 64) <= 16). Outputs equal union_block's; when counters
+// is not null, counters[e] += expert e's count.
+__device__ __forceinline__ void union_wave(const int32_t *ids, int A, int E,
+                                           int32_t *__restrict__ union_ids,
+                                           int32_t *__restrict__ n_union,
+                                           int32_t *__restrict__ offsets,
+                                           int32_t *__restrict__ perm,
+                                           unsigned long long *__restrict__ counters, int *cnt)
+{
+    const int lane = threadIdx.x % kWave;
+    constexpr int kMaxPE = MOE_MAX_EXPERTS / kWave;
+    const int PE = (E + kWave - 1) / kWave;
+    for (int e = lane; e < E; e += kWave) cnt[e] = 0;
+    __builtin_amdgcn_s_waitcnt(kLdsWait);
+    __builtin_amdgcn_wave_barrier();
+    int e = lane < A ? ids[lane] : -1;
+    const bool valid = e >= 0 && e < E;
+    if (!valid) e = -1;
+    if (valid) atomicAdd(&cnt[e], 1);
+    __builtin_amdgcn_s_waitcnt(kLdsWait);
+    __builtin_amdgcn_wave_barrier();
+    // this lane's experts: counts, then exclusive sums over the lanes before
+    int c[kMaxPE];
+    int sc = 0, su = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxPE; ++j) {
+        const int ej = lane * PE + j;
+        c[j] = (j < PE && ej < E) ? cnt[ej] : 0;
+        sc += c[j];
+        su += c[j] > 0 ? 1 : 0;
+    }
+    const int ic = wave_incl_scan_int(sc), iu = wave_incl_scan_int(su);
+    int rc = ic - sc, ru = iu - su;
+#pragma unroll
+    for (int j = 0; j < kMaxPE; ++j) {
+        const int ej = lane * PE + j;
+        if (j < PE && ej < E) {
+            offsets[ej] = rc;
+            cnt[ej] = rc;  // from here on: the expert's first permutation position
+            if (c[j] > 0) {
+                union_ids[ru] = ej;
+                if (counters) atomicAdd(&counters[ej], (unsigned long long)c[j]);
+            }
+            rc += c[j];
+            ru += c[j] > 0 ? 1 : 0;
+        }
+    }
+    if (lane == kWave - 1) {
+        offsets[E] = ic;
+        *n_union = iu;
+    }
+    __builtin_amdgcn_s_waitcnt(kLdsWait);
+    __builtin_amdgcn_wave_barrier();
+    // stable scatter: the rank among the lower lanes with the same expert,
+    // from ballots on the bits of the expert id
+    unsigned long long peers = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 11; ++bit) {  // E <= 1024 < 2^11, and -1 stays apart
+        const unsigned long long m = __ballot((e >> bit) & 1);
+        peers &= ((e >> bit) & 1) ? m : ~m;
+    }
+    if (valid) {
+        const unsigned long long lt = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+        perm[cnt[e] + __popcll(peers & lt)] = lane;
+    }
+}
+
 __global__ __launch_bounds__(kUnionThreads) void union_kernel(
     const int32_t *__restrict__ ids, int A, int E, int32_t *__restrict__ union_ids,
     int32_t *__restrict__ n_union, int32_t *__restrict__ offsets, int32_t *__restrict__ perm)
@@ -132,7 +213,9 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(
 // its top k from the router's output, then the same workgroup forms the union
 // and permutation of the N * k assignments and adds the per-expert counts to
 // the hit counters (counters may be null). Outputs equal those of the top-k,
-// union and hit-count kernels run in turn.
+// union and hit-count kernels run in turn. With at most 64 assignments the
+// workgroup is N waves and wave 0 does the union alone; otherwise it is
+// kUnionThreads threads.
 constexpr int kTailTokens = kUnionThreads / kWave;  // 16
 
 __global__ __launch_bounds__(kUnionThreads) void route_tail_kernel(
@@ -145,11 +228,15 @@ __global__ __launch_bounds__(kUnionThreads) void route_tail_kernel(
     __shared__ int cnt[MOE_MAX_EXPERTS];
     __shared__ int base[MOE_MAX_EXPERTS];
     const int tid = threadIdx.x, A = N * k;
-    for (int a = tid; a < A; a += kUnionThreads) s_ids[a] = -1;
+    for (int a = tid; a < A; a += blockDim.x) s_ids[a] = -1;
     __syncthreads();
     const int t = tid / kWave;
     if (t < N) topk_wave(in, P, b, N, E, k, t, ids, w, s_ids);
     __syncthreads();
+    if (A <= kWave) {  // one wave; the workgroup has one wave per token
+        if (t == 0) union_wave(s_ids, A, E, union_ids, n_union, offsets, perm, counters, cnt);
+        return;
+    }
     union_block(s_ids, A, E, union_ids, n_union, offsets, perm, cnt, base);
     if (counters)
         for (int e = tid; e < E; e += kUnionThreads)
@@ -193,7 +280,8 @@ hipError_t launch_route_tail(const float *in, int P, const float *b, int N, int 
                              int32_t *offsets, int32_t *perm, uint64_t *counters, hipStream_t s)
 {
     if (N < 1 || N > kTailTokens) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(route_tail_kernel, dim3(1), dim3(kUnionThreads), 0, s, in, P, b, N, E, k,
+    const int threads = N * k <= kWave ? N * kWave : kUnionThreads;
+    hipLaunchKernelGGL(route_tail_kernel, dim3(1), dim3(threads), 0, s, in, P, b, N, E, k,
                        ids, w, union_ids, n_union, offsets, perm,
                        reinterpret_cast<unsigned long long *>(counters));
     return hipGetLastError();
