@@ -267,6 +267,10 @@ moe_status moe_hit_count(const int32_t *topk_ids, int n_tokens, int k, int n_exp
     return MOE_OK;
 }
 
+// batches of at least this many assignments form the union over several
+// workgroups (moe_route_union only: it has the router's workspace as scratch)
+constexpr int kChunkedUnionMin = 4096;
+
 moe_status moe_route_union(const float *x, int n_tokens, int d_model, const float *w_router,
                            const float *b_router, int n_experts, int k, int32_t *topk_ids,
                            float *topk_w, int32_t *union_ids, int32_t *n_union,
@@ -302,9 +306,21 @@ moe_status moe_route_union(const float *x, int n_tokens, int d_model, const floa
                    ? MOE_OK
                    : MOE_EHIP;
     if (launch_topk(scores, P, b_router, n_tokens, n_experts, k, topk_ids, topk_w, stream) !=
-            hipSuccess ||
-        launch_union(topk_ids, n_tokens * k, n_experts, union_ids, n_union, expert_offsets, perm,
-                     stream) != hipSuccess)
+        hipSuccess)
+        return MOE_EHIP;
+    const int A = n_tokens * k;
+    if (A >= kChunkedUnionMin) {
+        // the router's output has been consumed (stream order): the
+        // workspace is the chunked union's scratch
+        return launch_union_chunked(topk_ids, A, n_experts, union_ids, n_union, expert_offsets,
+                                    perm, counters, workspace,
+                                    moe_route_workspace_size(n_tokens, n_experts),
+                                    stream) == hipSuccess
+                   ? MOE_OK
+                   : MOE_EHIP;
+    }
+    if (launch_union(topk_ids, A, n_experts, union_ids, n_union, expert_offsets, perm, stream) !=
+        hipSuccess)
         return MOE_EHIP;
     if (counters && launch_hit_count(topk_ids, n_tokens * k, n_experts, counters, stream) !=
                         hipSuccess)

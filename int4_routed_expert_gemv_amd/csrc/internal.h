@@ -101,6 +101,14 @@ hipError_t launch_hit_count(const int32_t *ids, int A, int E, uint64_t *counters
 // Top-k, union and hit counting of a batch of at most route_tail_max_tokens()
 // tokens in one workgroup (counters may be null).
 int route_tail_max_tokens();
+// Union, permutation and (counters not null) hit counts of a large batch
+// over several workgroups, with scratch of at least E * 4 bytes (more allows
+// more chunks); the same outputs as launch_union + launch_hit_count.
+int union_chunks(int A, int E, size_t scratch_bytes);
+hipError_t launch_union_chunked(const int32_t *ids, int A, int E, int32_t *union_ids,
+                                int32_t *n_union, int32_t *offsets, int32_t *perm,
+                                uint64_t *counters, void *scratch, size_t scratch_bytes,
+                                hipStream_t s);
 hipError_t launch_route_tail(const float *in, int P, const float *b, int N, int E, int k,
                              int32_t *ids, float *w, int32_t *union_ids, int32_t *n_union,
                              int32_t *offsets, int32_t *perm, uint64_t *counters, hipStream_t s);

@@ -243,6 +243,147 @@ __global__ __launch_bounds__(kUnionThreads) void route_tail_kernel(
             if (cnt[e]) atomicAdd(&counters[e], (unsigned long long)cnt[e]);
 }
 
+// ---- large batches: union, permutation and counts over several workgroups --
+//
+// The assignments are cut into G contiguous chunks, one workgroup each.
+// 1. union_hist_kernel: per-chunk histograms hist[w][e] (scratch).
+// 2. union_scan_kernel (one workgroup, a thread per expert): per expert the
+//    exclusive sums over the chunks, the totals -> offsets, union_ids,
+//    n_union and the hit counters; hist[w][e] becomes chunk w's first
+//    position for expert e.
+// 3. union_scatter_kernel: each chunk's assignments in ascending order, one
+//    wave, ranks from ballots, at those positions.
+// The result is the same stable counting sort as union_block's.
+constexpr int kChunkThreads = 256;
+
+__global__ __launch_bounds__(kChunkThreads) void union_hist_kernel(
+    const int32_t *__restrict__ ids, int A, int E, int C, int32_t *__restrict__ hist)
+{
+    __shared__ int cnt[MOE_MAX_EXPERTS];
+    const int w = blockIdx.x, tid = threadIdx.x;
+    for (int e = tid; e < E; e += kChunkThreads) cnt[e] = 0;
+    __syncthreads();
+    const int a0 = w * C, a1 = min(A, a0 + C);
+    for (int a = a0 + tid; a < a1; a += kChunkThreads) {
+        const int e = ids[a];
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kChunkThreads) hist[(size_t)w * E + e] = cnt[e];
+}
+
+__global__ __launch_bounds__(kUnionThreads) void union_scan_kernel(
+    int E, int G, int32_t *__restrict__ hist, int32_t *__restrict__ union_ids,
+    int32_t *__restrict__ n_union, int32_t *__restrict__ offsets,
+    unsigned long long *__restrict__ counters)
+{
+    const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+    // per expert: the total over the chunks (16 loads in flight at a time)
+    constexpr int kB = 16;
+    int c = 0;
+    if (tid < E) {
+        for (int w0 = 0; w0 < G; w0 += kB) {
+            int h[kB];
+#pragma unroll
+            for (int j = 0; j < kB; ++j) h[j] = w0 + j < G ? hist[(size_t)(w0 + j) * E + tid] : 0;
+#pragma unroll
+            for (int j = 0; j < kB; ++j) c += h[j];
+        }
+    }
+    const int used = c > 0 ? 1 : 0;
+    // exclusive sums over experts of (count, used), packed as in union_block
+    long long v = (long long)c * 2048 + used;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        long long u = __shfl_up(v, o, kWave);
+        if (lane >= o) v += u;
+    }
+    __shared__ long long wtot[kUnionThreads / kWave];
+    if (lane == kWave - 1) wtot[wv] = v;
+    __syncthreads();
+    if (wv == 0) {
+        long long x = lane < kUnionThreads / kWave ? wtot[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            long long u = __shfl_up(x, o, kWave);
+            if (lane >= o) x += u;
+        }
+        if (lane < kUnionThreads / kWave) wtot[lane] = x;
+    }
+    __syncthreads();
+    const long long incl = v + (wv > 0 ? wtot[wv - 1] : 0);
+    const long long excl = incl - ((long long)c * 2048 + used);
+    const int off = (int)(excl / 2048), upos = (int)(excl % 2048);
+    if (tid < E) {
+        offsets[tid] = off;
+        if (used) union_ids[upos] = tid;
+        if (counters && c) atomicAdd(&counters[tid], (unsigned long long)c);
+        // chunk w's first position for this expert: off + the counts of the
+        // chunks before it
+        int run = off;
+        for (int w0 = 0; w0 < G; w0 += kB) {
+            int h[kB];
+#pragma unroll
+            for (int j = 0; j < kB; ++j) h[j] = w0 + j < G ? hist[(size_t)(w0 + j) * E + tid] : 0;
+#pragma unroll
+            for (int j = 0; j < kB; ++j) {
+                if (w0 + j < G) hist[(size_t)(w0 + j) * E + tid] = run;
+                run += h[j];
+            }
+        }
+    }
+    if (tid == kUnionThreads - 1) {
+        const long long tot = wtot[kUnionThreads / kWave - 1];
+        offsets[E] = (int)(tot / 2048);
+        *n_union = (int)(tot % 2048);
+    }
+}
+
+__global__ __launch_bounds__(kWave) void union_scatter_kernel(
+    const int32_t *__restrict__ ids, int A, int E, int C, const int32_t *__restrict__ hist,
+    int32_t *__restrict__ perm)
+{
+    __shared__ int base[MOE_MAX_EXPERTS];
+    const int w = blockIdx.x, lane = threadIdx.x;
+    for (int e = lane; e < E; e += kWave) base[e] = hist[(size_t)w * E + e];
+    __builtin_amdgcn_s_waitcnt(kLdsWait);
+    __builtin_amdgcn_wave_barrier();
+    const unsigned long long lt = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+    const int a0 = w * C, a1 = min(A, a0 + C);
+    constexpr int kR = 8;  // rounds of 64 assignments whose ids are loaded together
+    for (int r0 = a0; r0 < a1; r0 += kR * kWave) {
+        int ev[kR];
+#pragma unroll
+        for (int j = 0; j < kR; ++j) {
+            const int a = r0 + j * kWave + lane;
+            ev[j] = a < a1 ? ids[a] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < kR; ++j) {
+            const int a = r0 + j * kWave + lane;
+            int e = ev[j];
+            const bool valid = e >= 0 && e < E;
+            if (!valid) e = -1;
+            unsigned long long peers = __ballot(valid);
+#pragma unroll
+            for (int bit = 0; bit < 11; ++bit) {
+                const unsigned long long m = __ballot((e >> bit) & 1);
+                peers &= ((e >> bit) & 1) ? m : ~m;
+            }
+            int pos = 0;
+            if (valid) pos = base[e] + __popcll(peers & lt);
+            __builtin_amdgcn_s_waitcnt(kLdsWait);
+            __builtin_amdgcn_wave_barrier();
+            if (valid) {
+                perm[pos] = a;
+                if ((peers >> lane) == 1ull) base[e] = pos + 1;  // highest peer lane
+            }
+            __builtin_amdgcn_s_waitcnt(kLdsWait);
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
 constexpr int kHitThreads = 256;
 constexpr int kHitPerBlock = 4096;
 
@@ -284,6 +425,31 @@ hipError_t launch_route_tail(const float *in, int P, const float *b, int N, int 
     hipLaunchKernelGGL(route_tail_kernel, dim3(1), dim3(threads), 0, s, in, P, b, N, E, k,
                        ids, w, union_ids, n_union, offsets, perm,
                        reinterpret_cast<unsigned long long *>(counters));
+    return hipGetLastError();
+}
+
+int union_chunks(int A, int E, size_t scratch_bytes)
+{
+    // chunks of at least 512 assignments, at most 256 of them, within the scratch
+    int G = (A + 511) / 512;
+    if (G > 256) G = 256;
+    while (G > 1 && (size_t)G * E * 4 > scratch_bytes) G /= 2;
+    return G;
+}
+
+hipError_t launch_union_chunked(const int32_t *ids, int A, int E, int32_t *union_ids,
+                                int32_t *n_union, int32_t *offsets, int32_t *perm,
+                                uint64_t *counters, void *scratch, size_t scratch_bytes,
+                                hipStream_t s)
+{
+    const int G = union_chunks(A, E, scratch_bytes);
+    if (G < 1 || (size_t)G * E * 4 > scratch_bytes) return hipErrorInvalidValue;
+    const int C = (A + G - 1) / G;
+    int32_t *hist = static_cast<int32_t *>(scratch);
+    hipLaunchKernelGGL(union_hist_kernel, dim3(G), dim3(kChunkThreads), 0, s, ids, A, E, C, hist);
+    hipLaunchKernelGGL(union_scan_kernel, dim3(1), dim3(kUnionThreads), 0, s, E, G, hist, union_ids,
+                       n_union, offsets, reinterpret_cast<unsigned long long *>(counters));
+    hipLaunchKernelGGL(union_scatter_kernel, dim3(G), dim3(kWave), 0, s, ids, A, E, C, hist, perm);
     return hipGetLastError();
 }
 

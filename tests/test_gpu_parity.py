@@ -253,14 +253,17 @@ def test_single_token_several_experts(wbits, group, k):
     full_parity(dataclasses.replace(base, n_tokens=1, k=k, layers=(spec,)))
 
 
-@pytest.mark.parametrize("N,k", [(1, 1), (4, 1), (3, 8), (16, 5), (17, 2), (64, 4)])
+@pytest.mark.parametrize("N,k", [(1, 1), (4, 1), (3, 8), (16, 5), (17, 2), (64, 4), (600, 8),
+                                 (1000, 16)])
 def test_route_union_against_oracle(N, k):
     """moe_route_union (one call for route, union and counting; one tail
-    workgroup up to 16 tokens, the separate kernels above) on the tiny layer."""
+    workgroup up to 16 tokens, the separate kernels above, the chunked union
+    from 4096 assignments) on the tiny layer."""
     full_parity(tiny(n_tokens=N, k=k), fused_route=True)
 
 
-@pytest.mark.parametrize("N,k", [(1, 1), (1, 8), (8, 8), (16, 8), (17, 8)])
+@pytest.mark.parametrize("N,k", [(1, 1), (1, 8), (8, 8), (16, 8), (17, 8), (512, 8), (601, 7),
+                                 (4096, 8)])
 @pytest.mark.parametrize("with_counters", [True, False])
 def test_route_union_equals_separate_calls(N, k, with_counters):
     """Bit for bit the outputs of moe_route_topk, moe_union and moe_hit_count
