@@ -38,31 +38,46 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ in, int P,
 {
     const int lane = threadIdx.x % kWave;
     uint32_t hi[kMaxPerLane];
-    float sv[kMaxPerLane];
+    float sv[kMaxPerLane] = {};
     uint32_t taken = 0;
+    if (P == 1) {
 #pragma unroll
-    for (int m = 0; m < kMaxPerLane; ++m) {
-        const int e = lane + m * kWave;
-        float v = 0.0f;
-        if (e < E) {
-            if (P == 1) {
-                v = in[(size_t)t * E + e];
-            } else {
-                // all slices' loads issued together (slices past P read slice
-                // P - 1 and are not added), then added in slice order
-                float part[kMaxSlices];
+        for (int m = 0; m < kMaxPerLane; ++m) {
+            const int e = lane + m * kWave;
+            sv[m] = e < E ? in[(size_t)t * E + e] : 0.0f;
+        }
+    } else {
+        // the partial sums of kGroup experts per lane at a time, every load
+        // of a group issued together (slices past P and experts past E read
+        // valid entries that are not used), then added in slice order
+        constexpr int kGroup = 4;
+#pragma unroll
+        for (int g = 0; g < kMaxPerLane; g += kGroup) {
+            if (g * kWave >= E) break;
+            float part[kGroup][kMaxSlices], bias[kGroup];
+#pragma unroll
+            for (int mm = 0; mm < kGroup; ++mm) {
+                const int e = min(lane + (g + mm) * kWave, E - 1);
 #pragma unroll
                 for (int p = 0; p < kMaxSlices; ++p)
-                    part[p] = in[((size_t)min(p, P - 1) * N + t) * E + e];
+                    part[mm][p] = in[((size_t)min(p, P - 1) * N + t) * E + e];
+                bias[mm] = b ? b[e] : 0.0f;
+            }
+#pragma unroll
+            for (int mm = 0; mm < kGroup; ++mm) {
+                const int e = lane + (g + mm) * kWave;
                 float l = 0.0f;
 #pragma unroll
                 for (int p = 0; p < kMaxSlices; ++p)
-                    if (p < P) l += part[p];
-                v = sigmoidf(l + (b ? b[e] : 0.0f));
+                    if (p < P) l += part[mm][p];
+                sv[g + mm] = e < E ? sigmoidf(l + bias[mm]) : 0.0f;
             }
         }
-        sv[m] = v;
-        hi[m] = e < E ? sortable(v) : 0u;
+    }
+#pragma unroll
+    for (int m = 0; m < kMaxPerLane; ++m) {
+        const int e = lane + m * kWave;
+        hi[m] = e < E ? sortable(sv[m]) : 0u;
         if (e >= E) taken |= 1u << m;
     }
     for (int j = 0; j < k; ++j) {
