@@ -195,9 +195,9 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
     const int a_row = tid / kParts, a_q = tid % kParts;
     const int a_src = s_src[a_row];
     // rows past the item's tokens load token 0's row (every load is issued on
-    // every path, so waits stay exact) and store zeros
+    // every path, so waits stay exact); their products land in accumulator
+    // rows that are never stored
     const uint16_t *a_ptr = in + (size_t)(a_src >= 0 ? a_src : s_src[0]) * K + a_q * kCols;
-    const bool a_keep = a_src >= 0;
     auto load_a = [&](int kb, int hf, uint4 (&av)[kVec]) {
 #pragma unroll
         for (int c = 0; c < kVec; ++c)
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
     auto store_a = [&](int buf, int hf, const uint4 (&av)[kVec]) {
         uint4 *dst = reinterpret_cast<uint4 *>(&As[buf][a_row][hf * kHalf + a_q * kCols]);
 #pragma unroll
-        for (int c = 0; c < kVec; ++c) dst[c] = a_keep ? av[c] : make_uint4(0u, 0u, 0u, 0u);
+        for (int c = 0; c < kVec; ++c) dst[c] = make_uint4(av[c].x, av[c].y, av[c].z, av[c].w);
     };
 
     // weights: this wave's unit rows; lane slot = (row in unit, quarter)
@@ -323,25 +323,30 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
     float bs0[TW][NM], bs1[TW][NM];
     load_a(0, 0, av);
     load_b(0, bw0, bs0);
-    if (n_kb > 1) load_b(1, bw1, bs1);
+    load_b(min(1, n_kb - 1), bw1, bs1);
     store_a(0, 0, av);
     if constexpr (NA == 2) {
         load_a(0, 1, av);
         store_a(0, 1, av);
     }
     __syncthreads();
-    // one step: products on LDS buffer `cur`, the next step's activations
-    // into the other buffer
+    // one step: products on LDS buffer `cur`; the next step's activations are
+    // loaded before the products and stored to the other buffer after them,
+    // so their latency is covered by the whole step. Loads are issued on
+    // every step (the last step reloads its own activations into the buffer
+    // no later step reads, the last two steps reload their weights), so that
+    // no load sits in a branch: each wait is then for the load it needs, not
+    // for every load in flight.
     auto step = [&](int ks, int cur, const uint4 (&bw)[TW][NM], const float (&bs)[TW][NM]) {
-        const bool next = ks + 1 < n_kb;
-        if (next) load_a(ks + 1, 0, av);
+        const int kn = min(ks + 1, n_kb - 1);
+        uint4 an0[kVec], an1[kVec];
+        load_a(kn, 0, an0);
+        if constexpr (NA == 2) load_a(kn, 1, an1);
+        __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the products
         compute(cur, bw, bs, 0);
-        if (next) {
-            store_a(cur ^ 1, 0, av);
-            if constexpr (NA == 2) load_a(ks + 1, 1, av);
-        }
         compute(cur, bw, bs, NS / 2);
-        if (NA == 2 && next) store_a(cur ^ 1, 1, av);
+        store_a(cur ^ 1, 0, an0);
+        if constexpr (NA == 2) store_a(cur ^ 1, 1, an1);
         __syncthreads();
     };
     // Small items (short steps) compute from a copy of the stage, so the
@@ -357,11 +362,11 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
             for (int t = 0; t < TW; ++t)
 #pragma unroll
                 for (int m = 0; m < NM; ++m) { bw[t][m] = bw0[t][m]; bs[t][m] = bs0[t][m]; }
-            if (ks + 2 < n_kb) load_b(ks + 2, bw0, bs0);
+            load_b(min(ks + 2, n_kb - 1), bw0, bs0);
             step(ks, 0, bw, bs);
         } else {
             step(ks, 0, bw0, bs0);
-            if (ks + 2 < n_kb) load_b(ks + 2, bw0, bs0);
+            load_b(min(ks + 2, n_kb - 1), bw0, bs0);
         }
         if (ks + 1 >= n_kb) break;
         // odd step ks + 1: LDS buffer 1, weights in stage 1
@@ -372,11 +377,11 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
             for (int t = 0; t < TW; ++t)
 #pragma unroll
                 for (int m = 0; m < NM; ++m) { bw[t][m] = bw1[t][m]; bs[t][m] = bs1[t][m]; }
-            if (ks + 3 < n_kb) load_b(ks + 3, bw1, bs1);
+            load_b(min(ks + 3, n_kb - 1), bw1, bs1);
             step(ks + 1, 1, bw, bs);
         } else {
             step(ks + 1, 1, bw1, bs1);
-            if (ks + 3 < n_kb) load_b(ks + 3, bw1, bs1);
+            load_b(min(ks + 3, n_kb - 1), bw1, bs1);
         }
     }
 
