@@ -54,7 +54,15 @@ FwdLayout fwd_layout(const Geo &g, int N, int k, int has_shared, int mfma_min_to
     L.tsmall = small_min_tokens > 0 ? small_min_tokens : kDefaultSmallMinTokens;
     // a pass runs when some expert can reach its threshold (an expert has at
     // most N tokens); the small pass only takes what the large one leaves
-    const bool big = mf && mfma_min_tokens >= 0 && N >= L.tstar;
+    bool big = mf && mfma_min_tokens >= 0 && N >= L.tstar;
+    if (big && mf && small_min_tokens >= 0 && N >= L.tsmall && L.tsmall < L.tstar) {
+        // at most this many 128-token items: each expert reaching tstar adds
+        // one partly filled item. Below kMinBigItems the planner moves them
+        // all to the 32-token pass, so that pass alone is launched.
+        const long long most = ceil_div(A, kMfmaBigTokens) + A / L.tstar +
+                               (has_shared && N >= L.tstar ? ceil_div(N, kMfmaBigTokens) : 0);
+        if (most < kMinBigItems) big = false;
+    }
     const bool small = mf && small_min_tokens >= 0 && N >= L.tsmall && !(big && L.tsmall >= L.tstar);
     // most tokens of an expert on the GEMV pass
     long long cap = N;
