@@ -693,7 +693,7 @@ hipError_t run_gemv(GemvArgs a, hipStream_t s)
 //   rows of 4-16 units: 4 waves of up to 4 units, or (many workgroups) one
 //     wave per unit row with all its units;
 //   longer rows: 4 waves of up to 12 units at a time; single tokens: 4
-//     waves of 6 at a time, or (few workgroups, up to 48 units) 8 waves of 6.
+//     waves of 4 at a time, or (few workgroups, up to 48 units) 8 waves of 6.
 template <bool GATEUP, int WB, int TB>
 hipError_t run_ks(const GemvArgs &a, hipStream_t s)
 {
@@ -710,7 +710,7 @@ hipError_t run_ks(const GemvArgs &a, hipStream_t s)
                          : run_gemv<GATEUP, WB, TB, 4, 1, 16>(a, s);
     }
     if (TB == 1 && n_kb <= 48 && few) return run_gemv<GATEUP, WB, TB, 8, 8, 6>(a, s);
-    if (TB == 1) return run_gemv<GATEUP, WB, TB, 4, 4, 6>(a, s);
+    if (TB == 1) return run_gemv<GATEUP, WB, TB, 4, 4, 4>(a, s);
     return run_gemv<GATEUP, WB, TB, 4, 4, kUnitBatch>(a, s);
 }
 
