@@ -155,8 +155,11 @@ moe_status moe_union(const int32_t *topk_ids, int n_tokens, int k, int n_experts
  * the same outputs as moe_route_topk, then moe_union, then moe_hit_count on
  * the same arguments (same checks, nothing enqueued on an error). Batches of
  * up to 16 tokens take the top-k, the union and the counting in a single
- * workgroup after the router kernel (two kernel launches instead of four).
- * workspace: at least moe_route_workspace_size(n_tokens, n_experts) bytes.
+ * workgroup after the router kernel (two kernel launches instead of four);
+ * from 4096 assignments the union and counting run over several workgroups,
+ * with the workspace (whose router output the top-k has consumed by then) as
+ * scratch. workspace: at least moe_route_workspace_size(n_tokens, n_experts)
+ * bytes; its contents afterwards are unspecified.
  * Colibri pages: "Exact Architecture and Data-Flow Reconstruction", stages
  * (1) Route, (2) Union and (5) Learn.
  */
@@ -204,7 +207,8 @@ moe_status moe_expert_forward(const moe_expert_pool *pool /* (host) */,
  *   otherwise: the streaming GEMV kernels.
  * When both matrix-core passes are on and the 128-token pass would get fewer
  * than 32 items, those experts join the 32-token pass (a few large items
- * would otherwise run with a few workgroups each).
+ * would otherwise run with a few workgroups each); when n_tokens and k alone
+ * bound it below 32 items, the 128-token kernels are not launched at all.
  * The matrix-core passes need int4 weights and d_model, d_ff multiples of
  * 64; otherwise every expert uses the GEMV.
  * events: each non-NULL event is taken by the dispatch of the kernel it
