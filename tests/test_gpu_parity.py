@@ -346,3 +346,16 @@ def test_single_token_zero_gate_equals_dropped_slot(wbits):
     r2 = run_layer(pool, x, wr, b, 2, ids_in=ids, w_in=w0)
     r1 = run_layer(pool, x, wr, b, 1, ids_in=ids[:, :1].copy(), w_in=w[:, :1].copy())
     np.testing.assert_array_equal(r2["y"], r1["y"])
+
+
+@pytest.mark.parametrize("E,N,k", [(1000, 2, 32), (1000, 3, 32), (1024, 1, 7), (65, 9, 7),
+                                   (1000, 40, 32)])
+def test_route_union_many_experts(E, N, k):
+    """Expert counts that are not a multiple of 64, up to the largest
+    supported, on both union paths of the route tail (one wave up to 64
+    assignments, the workgroup above) and the separate kernels (40 tokens)."""
+    base = synth.CONFIGS["tiny"]
+    cfg = dataclasses.replace(base, n_tokens=N, k=k,
+                              layers=(dataclasses.replace(base.layer, n_experts=E),))
+    say(f"[many experts] E={E} N={N} k={k}")
+    full_parity(cfg, fused_route=True)
