@@ -112,6 +112,14 @@ typedef struct {
     const void *pool;         /* n_experts blocks, expert_bytes apart */
     size_t expert_bytes;      /* block stride */
     const void *shared;       /* the shared expert's block, or NULL for none */
+    /* NULL: routed expert e's block is at pool + e * expert_bytes. Otherwise
+     * (device, [n_experts] int32, a pool held partly in HBM, see moe_cache.h)
+     * its block is at pool + slot_of[e] * expert_bytes, pool holding n_slots
+     * blocks; every expert a call uses must then have a slot (slot values
+     * are clamped into [0, n_slots) before use, so a wrong table gives wrong
+     * results, never an access outside the pool). */
+    const int32_t *slot_of;
+    int32_t n_slots;
 } moe_expert_pool;
 
 /*

@@ -36,6 +36,8 @@ EXPORTED = [
 
 # measured-ceiling probes (include/moe_probe.h), not part of the layer step
 PROBE_EXPORTED = ["moe_probe_stream_read", "moe_probe_mfma_f16"]
+# the expert cache of the Place stage (include/moe_cache.h)
+CACHE_EXPORTED = ["moe_cache_create", "moe_cache_destroy", "moe_cache_place", "moe_cache_stats"]
 
 
 class MoeError(RuntimeError):
@@ -66,6 +68,8 @@ class PoolDesc(ctypes.Structure):
         ("pool", ctypes.c_void_p),
         ("expert_bytes", ctypes.c_size_t),
         ("shared", ctypes.c_void_p),
+        ("slot_of", ctypes.c_void_p),
+        ("n_slots", ctypes.c_int32),
     ]
 
 
@@ -98,6 +102,14 @@ def lib():
         L.moe_pack_expert.argtypes = [vp, P, vp]
         L.moe_probe_stream_read.argtypes = [vp, sz, i32, i32, vp, sz, vp, vp, vp]
         L.moe_probe_mfma_f16.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.moe_cache_create.argtypes = [i32, i32, sz, sz, vp, vp, vp, ctypes.POINTER(vp)]
+        L.moe_cache_create.restype = i32
+        L.moe_cache_destroy.argtypes = [vp]
+        L.moe_cache_destroy.restype = None
+        L.moe_cache_place.argtypes = [vp, vp, i32, vp, vp, vp]
+        L.moe_cache_place.restype = i32
+        L.moe_cache_stats.argtypes = [vp, vp, vp]
+        L.moe_cache_stats.restype = i32
         L.moe_strerror.argtypes = [i32]
         L.moe_strerror.restype = ctypes.c_char_p
         for name in ("moe_route_topk", "moe_union", "moe_route_union", "moe_expert_forward",
@@ -290,3 +302,56 @@ class DevicePool:
             raise MoeError(MOE_EALIGN, "DevicePool")
         self.stride = stride
         self.block_bytes = bb
+
+
+class ExpertCache:
+    """A layer's routed experts in pinned host memory with an HBM cache of
+    n_slots block slots (moe_cache_*). host_blocks: pinned uint8 tensor
+    [n_experts][stride] of device-layout blocks (pack_expert output)."""
+
+    def __init__(self, pool_shape: PoolDesc, n_slots, host_blocks, device="cuda"):
+        import torch
+        E, stride = host_blocks.shape
+        if E != pool_shape.n_experts or stride % MOE_ALIGN:
+            raise ValueError("host_blocks must be [n_experts][stride], stride a multiple of 256")
+        if not host_blocks.is_pinned():
+            raise ValueError("host_blocks must be pinned host memory")
+        bb = block_bytes(pool_shape.d_model, pool_shape.d_ff, pool_shape.wbits, pool_shape.group)
+        self.host_blocks = host_blocks
+        self.slots = torch.empty(n_slots * stride, dtype=torch.uint8, device=device)
+        self.table = torch.empty(E, dtype=torch.int32, device=device)
+        self.n_slots = n_slots
+        h = ctypes.c_void_p()
+        _check(lib().moe_cache_create(E, n_slots, bb, stride, host_blocks.data_ptr(),
+                                      self.slots.data_ptr(), self.table.data_ptr(),
+                                      ctypes.byref(h)), "moe_cache_create")
+        self.handle = h
+        self.desc = PoolDesc(pool_shape.d_model, pool_shape.d_ff, E, pool_shape.wbits,
+                             pool_shape.group, self.slots.data_ptr(), stride, pool_shape.shared,
+                             self.table.data_ptr(), n_slots)
+
+    def place(self, union_ids_host, copy_stream=None, compute_stream=None) -> int:
+        """Make the experts of union_ids_host (int32 numpy) resident; returns
+        the number copied in."""
+        ids = np.ascontiguousarray(union_ids_host, np.int32)
+        missed = ctypes.c_int32(0)
+        _check(lib().moe_cache_place(self.handle, ids.ctypes.data if ids.size else None, ids.size,
+                                     _stream(copy_stream), _stream(compute_stream),
+                                     ctypes.byref(missed)), "moe_cache_place")
+        return int(missed.value)
+
+    def stats(self):
+        h, m = ctypes.c_uint64(0), ctypes.c_uint64(0)
+        _check(lib().moe_cache_stats(self.handle, ctypes.byref(h), ctypes.byref(m)), "moe_cache_stats")
+        return int(h.value), int(m.value)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().moe_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

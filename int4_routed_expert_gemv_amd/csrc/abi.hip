@@ -359,6 +359,7 @@ moe_status moe_expert_forward_ex(const moe_expert_pool *pool, const float *x, in
     st = check_k(k, g.E);
     if (st != MOE_OK) return st;
     if (!pool->pool) return MOE_EINVAL;
+    if (pool->slot_of && pool->n_slots < 1) return MOE_EINVAL;
     if (!aligned(pool->pool) || (pool->shared && !aligned(pool->shared)) ||
         pool->expert_bytes % kAlign)
         return MOE_EALIGN;
@@ -381,6 +382,8 @@ moe_status moe_expert_forward_ex(const moe_expert_pool *pool, const float *x, in
     f.g = g;
     f.pool = static_cast<const uint8_t *>(pool->pool);
     f.stride = pool->expert_bytes;
+    f.slot_of = pool->slot_of;
+    f.n_slots = pool->n_slots;
     f.shared = static_cast<const uint8_t *>(pool->shared);
     f.x = x;
     f.w = topk_w;

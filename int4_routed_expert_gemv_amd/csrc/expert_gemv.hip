@@ -335,7 +335,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
     }
     const int count = min(it.count, TB);
 
-    const uint8_t *blk = expert >= 0 ? f.pool + (size_t)expert * f.stride : f.shared;
+    const uint8_t *blk = expert >= 0 ? expert_block(f, expert) : f.shared;
     const int K = GATEUP ? g.d : g.f;        // contraction length
     const int rows = GATEUP ? g.f : g.d;     // output rows
     const int NCH = K / EPC;                 // chunks per row

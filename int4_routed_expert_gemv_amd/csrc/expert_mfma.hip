@@ -164,7 +164,7 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
     const int ntile = logical % ma.n_tiles;
     const Item it = ma.items[item_idx];
     const int count = min(it.count, MT);
-    const uint8_t *blk = it.expert >= 0 ? f.pool + (size_t)it.expert * f.stride : f.shared;
+    const uint8_t *blk = it.expert >= 0 ? expert_block(f, it.expert) : f.shared;
     const int K = GATEUP ? g.d : g.f;       // contraction length
     const int rows = GATEUP ? g.f : g.d;    // output rows
     const int n_kb = K / kUC;               // steps = units per row

@@ -51,6 +51,8 @@ struct Fwd {
     Geo g;
     const uint8_t *pool;
     size_t stride;
+    const int32_t *slot_of;  // null, or the block slot of each routed expert
+    int n_slots;             // blocks in the pool when slot_of is not null
     const uint8_t *shared;
     const float *x;          // [N][d] layer input
     const float *w;          // [N][k] gate weights
@@ -82,6 +84,14 @@ struct Fwd {
     hipEvent_t ev_sgu[2];    // optional: the same for the 32-token MFMA gate/up kernel
     hipEvent_t ev_sdn[2];    // optional: the same for the 32-token MFMA down kernel
 };
+
+// Block of routed expert e (0 <= e < E): its own place in the pool, or the
+// slot the expert cache gave it.
+__device__ __forceinline__ const uint8_t *expert_block(const Fwd &f, int e)
+{
+    const int s = f.slot_of ? min(max(f.slot_of[e], 0), f.n_slots - 1) : e;
+    return f.pool + (size_t)s * f.stride;
+}
 
 // ---- host helpers (abi.hip) --------------------------------------------
 moe_status resolve_geo(const moe_expert_pool *p, Geo *g);

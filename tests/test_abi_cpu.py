@@ -26,11 +26,13 @@ def declared_functions(header=HEADER):
 def test_exports_every_declared_symbol():
     names = declared_functions()
     probes = declared_functions(os.path.join(ROOT, "include", "moe_probe.h"))
+    cache = declared_functions(os.path.join(ROOT, "include", "moe_cache.h"))
     assert set(names) == set(moe.EXPORTED)
     assert set(probes) == set(moe.PROBE_EXPORTED)
+    assert set(cache) == set(moe.CACHE_EXPORTED)
     out = subprocess.check_output(["nm", "-D", "--defined-only", moe.LIB_PATH], text=True)
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
-    for n in names + probes:
+    for n in names + probes + cache:
         assert n in exported, n
         assert hasattr(moe.lib(), n)
 
@@ -227,3 +229,23 @@ def test_strerror():
     for s in range(-5, 1):
         assert moe.strerror(s)
     assert "workspace" in moe.strerror(moe.MOE_EWORKSPACE)
+
+
+def test_cache_argument_checks():
+    """moe_cache_create / moe_cache_place reject bad arguments before any HIP call."""
+    L = moe.lib()
+    h = ctypes.c_void_p()
+    big = 1 << 20
+    assert L.moe_cache_create(16, 4, 1000, 1024, FAKE, FAKE, FAKE, None) == moe.MOE_EINVAL
+    assert L.moe_cache_create(0, 1, 1000, 1024, FAKE, FAKE, FAKE, ctypes.byref(h)) == moe.MOE_EINVAL
+    assert L.moe_cache_create(2000, 4, 1000, 1024, FAKE, FAKE, FAKE, ctypes.byref(h)) == moe.MOE_EINVAL
+    assert L.moe_cache_create(16, 0, 1000, 1024, FAKE, FAKE, FAKE, ctypes.byref(h)) == moe.MOE_EINVAL
+    assert L.moe_cache_create(16, 17, 1000, 1024, FAKE, FAKE, FAKE, ctypes.byref(h)) == moe.MOE_EINVAL
+    assert L.moe_cache_create(16, 4, 2000, 1024, FAKE, FAKE, FAKE, ctypes.byref(h)) == moe.MOE_EINVAL
+    assert L.moe_cache_create(16, 4, 1000, 1024, None, FAKE, FAKE, ctypes.byref(h)) == moe.MOE_EINVAL
+    assert L.moe_cache_create(16, 4, 1000, 1000, FAKE, FAKE, FAKE, ctypes.byref(h)) == moe.MOE_EALIGN
+    assert L.moe_cache_create(16, 4, 1000, 1024, FAKE, FAKE + 16, FAKE, ctypes.byref(h)) == moe.MOE_EALIGN
+    assert not h.value
+    assert L.moe_cache_place(None, FAKE, 1, None, None, None) == moe.MOE_EINVAL
+    assert L.moe_cache_stats(None, None, None) == moe.MOE_EINVAL
+    del big
