@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run one plain device copy of 1 GiB (to scale HBM counters)")
+    p.add_argument("--cache-slots", default=None,
+                   help="comma-separated HBM slot counts: measure the Place stage (experts in "
+                        "pinned host memory, an HBM cache of that many slots per layer) instead")
     return p.parse_args()
 
 
@@ -139,6 +142,9 @@ def main():
     import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.cache_slots:
+        cache_bench(args)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     base = synth.CONFIGS[args.config]
@@ -417,6 +423,102 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, spec, args, xs.cpu().numpy())
     print(json.dumps(result), flush=True)
+
+
+def cache_bench(args):
+    """Place stage: each layer's routed experts in pinned host memory, an HBM
+    cache of C slots per layer (moe_cache_*, least recently used
+    replacement). A step routes the batch (moe_route_union), copies the union
+    to the host, places it (missing blocks copied on a second stream), then
+    runs the expert math through the slot table. Reported per slot count:
+    tokens/s, the hit rate over the timed steps and the bytes copied per
+    token next to the L*k*S*(1-h) estimate (here L = 1 layer per step)."""
+    import numpy as np
+    import torch
+
+    import int4_routed_expert_gemv_amd as moe
+    import synth
+
+    dev = torch.device("cuda:0")
+    base = synth.CONFIGS[args.config]
+    if len(base.layers) > 1:
+        sys.exit("--cache-slots measures single-layer workloads")
+    spec = base.layer
+    L_rot = max(1, min(args.layers, 4))
+    cfg = dataclasses.replace(base, layers=(spec,) * L_rot)
+    N, k, E, d, f = cfg.n_tokens, cfg.k, spec.n_experts, spec.d, spec.f
+    nb = max(1, args.batches)  # distinct token batches cycled through (the access stream)
+    layers = []
+    for l in range(L_rot):
+        pool = moe.DevicePool(d, f, E, spec.wbits, spec.group, synth.expert_pool(cfg, l),
+                              synth.shared_block(cfg, l), dev)
+        host = torch.empty((E, pool.stride), dtype=torch.uint8, pin_memory=True)
+        host.copy_(pool.pool.view(E, pool.stride))
+        shared = pool.shared
+        desc = pool.desc
+        del pool
+        wr, b = synth.router(cfg, l)
+        layers.append(dict(host=host, shared=shared, desc=desc, wr=torch.from_numpy(wr).to(dev),
+                           b=torch.from_numpy(b).to(dev)))
+        torch.cuda.empty_cache()
+        print(f"[cache bench] layer {l + 1}/{L_rot} in pinned host memory", file=sys.stderr,
+              flush=True)
+    tok_cfg = dataclasses.replace(cfg, n_tokens=N * nb)
+    xs = torch.from_numpy(synth.tokens(tok_cfg).reshape(nb, N, d)).to(dev)
+    ids = torch.empty((N, k), dtype=torch.int32, device=dev)
+    w = torch.empty((N, k), dtype=torch.float32, device=dev)
+    uid = torch.empty(E, dtype=torch.int32, device=dev)
+    nu = torch.empty(1, dtype=torch.int32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(N * k, dtype=torch.int32, device=dev)
+    cnt = torch.zeros(E, dtype=torch.int64, device=dev)
+    y = torch.empty((N, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(moe.workspace_size(ly["desc"], N, k) for ly in layers), dtype=torch.uint8,
+                     device=dev)
+    copy_stream = torch.cuda.Stream()  # default priority
+    block = moe.block_bytes(d, f, spec.wbits, spec.group)
+    points = []
+    for C in [int(c) for c in args.cache_slots.split(",")]:
+        caches = [moe.ExpertCache(ly["desc"], C, ly["host"], dev) for ly in layers]
+
+        def run(s_):
+            ly, cache = layers[s_ % L_rot], caches[s_ % L_rot]
+            x = xs[s_ % nb]
+            moe.route_union(x, ly["wr"], ly["b"], k, ids, w, uid, nu, off, perm, cnt, ws)
+            n = int(nu.item())
+            cache.place(uid[:n].cpu().numpy(), copy_stream=copy_stream)
+            moe.expert_forward(cache.desc, x, k, w, uid, nu, off, perm, y, ws)
+
+        for s_ in range(args.warmup):
+            run(s_)
+        torch.cuda.synchronize()
+        h0 = [c.stats() for c in caches]
+        t0 = time.perf_counter()
+        for s_ in range(args.steps):
+            run(args.warmup + s_)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        hits = sum(c.stats()[0] - h[0] for c, h in zip(caches, h0))
+        misses = sum(c.stats()[1] - h[1] for c, h in zip(caches, h0))
+        hr = hits / max(1, hits + misses)
+        tok = N * args.steps
+        points.append({"slots": C, "tokens_per_s": tok / el, "ms_per_step": el / args.steps * 1e3,
+                       "hit_rate": hr, "misses_per_step": misses / args.steps,
+                       "copied_bytes_per_token": misses * block / tok,
+                       "estimate_bytes_per_token": k * block * (1 - hr),
+                       "copied_GBps": misses * block / el / 1e9})
+        print(f"[cache bench] {C} slots: {points[-1]}", file=sys.stderr, flush=True)
+        for c in caches:
+            c.close()
+        del caches
+    print(json.dumps({"metric": "layer-step tokens/s with experts placed from pinned host memory "
+                                "into an HBM cache (Place stage)",
+                      "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "data": "synthetic",
+                      "config": {"workload": f"{cfg.name}: {base.description}; {L_rot} layers, "
+                                             f"one cache per layer", "n_tokens": N, "k": k,
+                                 "n_experts": E, "block_bytes": block},
+                      "points": points}), flush=True)
 
 
 def measured_ceiling(moe, hip, torch, bound, bytes_per_launch, achieved):
