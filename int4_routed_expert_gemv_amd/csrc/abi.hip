@@ -412,6 +412,12 @@ moe_status moe_expert_forward_ex(const moe_expert_pool *pool, const float *x, in
     f.n_sitems = reinterpret_cast<int32_t *>(ws + L.n_sitems);
     f.max_sitems = L.max_sitems;
     f.tsmall = L.tsmall;
+    // Every expert on the GEMV pass and at most two terms per output element
+    // (top-1 with the shared expert, or top-2 without): the down kernel adds
+    // its gate-weighted rows into y with float atomics. Two addends onto zero
+    // give the same sum in either order, so y is deterministic and equal to
+    // the combine kernel's; one launch fewer.
+    f.direct = (L.max_mitems == 0 && L.max_sitems == 0 && k + has_shared <= 2) ? 1 : 0;
 
     f.ev_gu[0] = ev ? ev->gateup_start : nullptr;
     f.ev_gu[1] = ev ? ev->gateup_end : nullptr;
@@ -435,7 +441,8 @@ moe_status moe_expert_forward_ex(const moe_expert_pool *pool, const float *x, in
     if (launch_down(f, stream) != hipSuccess) return MOE_EHIP;
     if (launch_mfma(f, false, false, stream) != hipSuccess) return MOE_EHIP;
     if (launch_mfma(f, false, true, stream) != hipSuccess) return MOE_EHIP;
-    if (launch_combine(f.o, topk_w, n_tokens, k, g.d, (int)A, has_shared, y, stream) != hipSuccess)
+    if (!f.direct &&
+        launch_combine(f.o, topk_w, n_tokens, k, g.d, (int)A, has_shared, y, stream) != hipSuccess)
         return MOE_EHIP;
     return MOE_OK;
 }

@@ -256,6 +256,14 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
     const Fwd &f = ga.f;
     const Geo &g = f.g;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    if (GATEUP && f.direct) {
+        // the down kernel adds its rows into y: clear y one launch ahead
+        // (every workgroup a part, before any of them can leave early)
+        const long long n4 = (long long)f.N * g.d / 4;
+        for (long long i = (long long)blockIdx.x * kGemvThreads + tid; i < n4;
+             i += (long long)gridDim.x * kGemvThreads)
+            reinterpret_cast<float4 *>(f.y)[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
     const int item_idx = blockIdx.x / ga.n_wg;
     const int wg = blockIdx.x % ga.n_wg;
     // The expert is needed first (the weight loads only depend on it); the
@@ -514,14 +522,20 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
             const int p = it.p0 + i;
             const int orow = (!GATEUP && it.expert >= 0) ? min(max(f.perm[p], 0), f.A - 1) : p;
             const int row = row_tile * kUnitRows + r;
-            float o;
             if (GATEUP) {
                 const float gv = v[0], uv = v[NM - 1];
-                o = gv / (1.0f + expf(-gv)) * uv;
+                out[(size_t)orow * rows + row] = gv / (1.0f + expf(-gv)) * uv;
+            } else if (f.direct) {
+                // y[t] gets the shared row and one routed row, or two routed
+                // rows: float atomics onto the cleared y, the same sum in
+                // either order (the combine kernel's order of rounding)
+                const bool routed = it.expert >= 0;
+                const int t = routed ? orow / f.k : p - f.A;
+                const float wt = routed ? f.w[orow] : 1.0f;
+                atomicAdd(&f.y[(size_t)t * rows + row], wt * v[0]);
             } else {
-                o = v[0];
+                out[(size_t)orow * rows + row] = v[0];
             }
-            out[(size_t)orow * rows + row] = o;
         }
     }
 }
@@ -622,6 +636,9 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const float *__restrict__ o, const float *__restrict__ w, int N, int k, int d, int A,
     int has_shared, float *__restrict__ y)
 {
+    // acc + (w * o), each rounded (not fused): the order of rounding of the
+    // direct combine in the down kernel
+#pragma clang fp contract(off)
     const int nq = d / 4;
     const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (long long)N * nq) return;
@@ -631,10 +648,10 @@ __global__ __launch_bounds__(256) void combine_kernel(
     for (int j = 0; j < k; ++j) {
         const float wj = w[(size_t)t * k + j];
         const float4 v = reinterpret_cast<const float4 *>(o + ((size_t)t * k + j) * d)[q];
-        acc.x = fmaf(wj, v.x, acc.x);
-        acc.y = fmaf(wj, v.y, acc.y);
-        acc.z = fmaf(wj, v.z, acc.z);
-        acc.w = fmaf(wj, v.w, acc.w);
+        acc.x = acc.x + wj * v.x;
+        acc.y = acc.y + wj * v.y;
+        acc.z = acc.z + wj * v.z;
+        acc.w = acc.w + wj * v.w;
     }
     reinterpret_cast<float4 *>(y + (size_t)t * d)[q] = acc;
 }

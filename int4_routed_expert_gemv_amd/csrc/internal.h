@@ -65,6 +65,9 @@ struct Fwd {
     uint16_t *x16;           // [N][d] layer input
     uint16_t *h16;           // [A + N][f] hidden
     float *y;                // [N][d] layer output
+    int direct;              // 1: the GEMV down kernel adds the gate-weighted rows into y
+                             // itself (at most two addends per element, y cleared by
+                             // the gate/up kernel); 0: the combine kernel writes y
     Item *items;             // [max_items] work list (workspace)
     int32_t *n_items;        // [1]
     int tb;                  // tokens per GEMV work item
