@@ -139,6 +139,51 @@ void oracle_topk(const float *scores, int n_tokens, int n_experts, int k,
     }
 }
 
+/* Router variant (opt-in; the default reading keeps the bias inside the
+ * sigmoid and the raw score as the weight): the bias only steers the
+ * selection, and the weights may be normalised. scores are the unbiased
+ * sigmoid scores (oracle_router with no bias). Per token:
+ *   key[e] = s[e] + b_sel[e]        (float32 addition: the selection is
+ *                                     decided in float32, like the scores)
+ *   ids    = the k best experts by (key desc, id asc), in rank order
+ *   w[j]   = s[ids[j]]; with normalize, w[j] = s[ids[j]] / sum_j' s[ids[j']]
+ *            * scale (double, rounded to float32 once).
+ * Rows of the pages this follows: the sigmoid gate over all experts with
+ * n_group = 1 ("Public Colibri Observation and Revision Ledger", "Exact
+ * Architecture and Data-Flow Reconstruction"); where the bias enters and
+ * whether weights are renormalised the pages leave open. */
+void oracle_topk_select(const float *scores, const float *b_sel, int n_tokens, int n_experts,
+                        int k, int normalize, double scale, int32_t *topk_ids, float *topk_w)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < n_tokens; ++t) {
+        const float *s = scores + (size_t)t * n_experts;
+        float *key = (float *)malloc(sizeof(float) * n_experts);
+        int *order = (int *)malloc(sizeof(int) * n_experts);
+        for (int e = 0; e < n_experts; ++e) {
+            volatile float kv = s[e] + b_sel[e];  /* one float32 rounding */
+            key[e] = kv;
+        }
+        for (int e = 0; e < n_experts; ++e) {
+            int j = e;
+            while (j > 0 && ranks_before(key[e], e, key[order[j - 1]], order[j - 1])) {
+                order[j] = order[j - 1];
+                --j;
+            }
+            order[j] = e;
+        }
+        double sum = 0.0;
+        for (int j = 0; j < k; ++j) sum += (double)s[order[j]];
+        for (int j = 0; j < k; ++j) {
+            topk_ids[(size_t)t * k + j] = order[j];
+            topk_w[(size_t)t * k + j] =
+                normalize ? (float)((double)s[order[j]] / sum * scale) : s[order[j]];
+        }
+        free(key);
+        free(order);
+    }
+}
+
 /* ---- Union and the token -> expert permutation ------------------------- */
 
 /* union_ids: the distinct routed ids in ascending order (n_union of them);

@@ -109,6 +109,62 @@ def test_topk_all_equal_takes_lowest_ids():
     assert np.all(w == 0.5)
 
 
+# ---------------------------------------------------------------- router variant: selection-only bias
+
+def test_topk_select_hand_computed():
+    """The opt-in variant on a four-expert example worked by hand
+    (tests/golden/route_select_hand.json)."""
+    with open(os.path.join(GOLD, "route_select_hand.json")) as fh:
+        g = json.load(fh)
+    s = np.array([g["scores"]], np.float32)
+    b = np.array(g["bias"], np.float32)
+    ids, w = oracle.topk_select(s, b, g["k"])
+    assert ids[0].tolist() == g["ids"]
+    np.testing.assert_array_equal(w[0], np.array(g["w_raw"], np.float32))
+    ids, w = oracle.topk_select(s, b, g["k"], normalize=True, scale=g["scale"])
+    assert ids[0].tolist() == g["ids"]
+    np.testing.assert_allclose(w[0], g["w_normalized"], rtol=1e-6)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_topk_select_brute_force_with_ties(k):
+    """The chosen set is the unique k-subset whose float32 keys s + b all
+    outrank the rest (ties to the lower id); the weights are the unbiased
+    scores of the chosen experts."""
+    rng = np.random.default_rng(50 + k)
+    E, N = 12, 40
+    s = (rng.integers(1, 6, size=(N, E)).astype(np.float32) / np.float32(8.0))
+    b = (rng.integers(-2, 3, size=E).astype(np.float32) / np.float32(8.0))
+    ids, w = oracle.topk_select(s, b, k)
+    for t in range(N):
+        key = (s[t] + b).astype(np.float32)   # numpy float32 addition
+        best = _brute_topk(key, k)
+        assert list(ids[t]) == best
+        np.testing.assert_array_equal(w[t], s[t, best])
+
+
+def test_topk_select_reduces_to_default_without_bias():
+    """A zero selection bias and no normalisation is the default top-k."""
+    rng = np.random.default_rng(7)
+    s = rng.random((30, 64)).astype(np.float32)
+    ids0, w0 = oracle.topk(s, 8)
+    ids1, w1 = oracle.topk_select(s, np.zeros(64, np.float32), 8)
+    np.testing.assert_array_equal(ids0, ids1)
+    np.testing.assert_array_equal(w0, w1)
+
+
+def test_topk_select_normalised_weights_sum_to_scale():
+    """Normalised weights are proportional to the chosen scores and add up
+    to the scale; the bias never enters the weights."""
+    rng = np.random.default_rng(8)
+    s = rng.random((25, 32)).astype(np.float32)
+    b = (rng.standard_normal(32) * 0.3).astype(np.float32)
+    ids, w = oracle.topk_select(s, b, 6, normalize=True, scale=2.5)
+    np.testing.assert_allclose(w.astype(np.float64).sum(axis=1), 2.5, rtol=1e-6)
+    chosen = np.take_along_axis(s, ids, axis=1).astype(np.float64)
+    np.testing.assert_allclose(w, chosen / chosen.sum(axis=1, keepdims=True) * 2.5, rtol=1e-6)
+
+
 # ---------------------------------------------------------------- union, permutation, counters
 
 @pytest.mark.parametrize("N,k,E", [(1, 1, 4), (5, 3, 8), (17, 4, 16), (64, 8, 256)])
