@@ -109,8 +109,8 @@ def topk(scores, k):
 def topk_select(scores, b_sel, k, normalize=False, scale=1.0):
     """Router variant: the bias b_sel only steers the selection (key = s + b
     in float32); weights are the unbiased scores, optionally divided by their
-    sum over the chosen k and multiplied by scale. scores: unbiased sigmoid
-    scores [N][E] (router(x, Wr) with no bias)."""
+    sum over the chosen k, times scale. scores: unbiased sigmoid scores [N][E]
+    (router(x, Wr) with no bias)."""
     s, sp = _c(scores, np.float32)
     b, bp = _c(b_sel, np.float32)
     N, E = s.shape

@@ -146,8 +146,9 @@ void oracle_topk(const float *scores, int n_tokens, int n_experts, int k,
  *   key[e] = s[e] + b_sel[e]        (float32 addition: the selection is
  *                                     decided in float32, like the scores)
  *   ids    = the k best experts by (key desc, id asc), in rank order
- *   w[j]   = s[ids[j]]; with normalize, w[j] = s[ids[j]] / sum_j' s[ids[j']]
- *            * scale (double, rounded to float32 once).
+ *   w[j]   = s[ids[j]] * scale, or with normalize
+ *            s[ids[j]] / sum_j' s[ids[j']] * scale (double, rounded to
+ *            float32 once).
  * Rows of the pages this follows: the sigmoid gate over all experts with
  * n_group = 1 ("Public Colibri Observation and Revision Ledger", "Exact
  * Architecture and Data-Flow Reconstruction"); where the bias enters and
@@ -177,7 +178,8 @@ void oracle_topk_select(const float *scores, const float *b_sel, int n_tokens, i
         for (int j = 0; j < k; ++j) {
             topk_ids[(size_t)t * k + j] = order[j];
             topk_w[(size_t)t * k + j] =
-                normalize ? (float)((double)s[order[j]] / sum * scale) : s[order[j]];
+                normalize ? (float)((double)s[order[j]] / sum * scale)
+                          : (float)((double)s[order[j]] * scale);
         }
         free(key);
         free(order);

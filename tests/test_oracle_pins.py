@@ -121,6 +121,8 @@ def test_topk_select_hand_computed():
     ids, w = oracle.topk_select(s, b, g["k"])
     assert ids[0].tolist() == g["ids"]
     np.testing.assert_array_equal(w[0], np.array(g["w_raw"], np.float32))
+    ids, w = oracle.topk_select(s, b, g["k"], scale=g["scale"])
+    np.testing.assert_allclose(w[0], g["w_scaled"], rtol=1e-7)
     ids, w = oracle.topk_select(s, b, g["k"], normalize=True, scale=g["scale"])
     assert ids[0].tolist() == g["ids"]
     np.testing.assert_allclose(w[0], g["w_normalized"], rtol=1e-6)
