@@ -181,6 +181,47 @@ moe_status moe_route_union(const float *x, int n_tokens, int d_model,
                            void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Router variant (opt-in). The pages give a sigmoid gate over all experts
+ * with n_group = 1 and float32 gate parameters ("Exact Architecture and
+ * Data-Flow Reconstruction") and leave open where the bias enters and whether
+ * the chosen weights are rescaled; the calls above read them as a bias inside
+ * the sigmoid and the raw score as the weight. The _ex calls take the other
+ * reading on request:
+ *   bias_select_only = 1: scores s = sigmoid(x Wr^T) without the bias; the
+ *     top-k key of expert e is the float32 sum s[e] + b_router[e] (ties to
+ *     the lower id), the weight stays s;
+ *   normalize = 1: each chosen weight is divided by the sum of the token's
+ *     k chosen scores (added in rank order);
+ *   scale: multiplies every chosen weight (after normalising), > 0 and
+ *     finite; 1 leaves the weights as they are.
+ * opt == NULL is the default reading (the same results as the calls above).
+ * A bad option is MOE_EINVAL before anything is enqueued; b_router must be
+ * 4-byte aligned.
+ */
+typedef struct {
+    int32_t bias_select_only; /* 0 or 1 */
+    int32_t normalize;        /* 0 or 1 */
+    float scale;              /* weight multiplier */
+} moe_route_options;
+
+moe_status moe_route_topk_ex(const float *x, int n_tokens, int d_model,
+                             const float *w_router, const float *b_router,
+                             int n_experts, int k,
+                             int32_t *topk_ids, float *topk_w,
+                             void *workspace, size_t ws_bytes, hipStream_t stream,
+                             const moe_route_options *opt);
+
+moe_status moe_route_union_ex(const float *x, int n_tokens, int d_model,
+                              const float *w_router, const float *b_router,
+                              int n_experts, int k,
+                              int32_t *topk_ids, float *topk_w,
+                              int32_t *union_ids, int32_t *n_union,
+                              int32_t *expert_offsets, int32_t *perm,
+                              uint64_t *counters /* may be NULL */,
+                              void *workspace, size_t ws_bytes, hipStream_t stream,
+                              const moe_route_options *opt);
+
+/*
  * Expert math and combine:
  *   y[t] = shared(x_t) + sum_{j<k} topk_w[t][j] * E_{e(t,j)}(x_t),
  *   E(x) = Wd (silu(Wg x) * (Wu x)),

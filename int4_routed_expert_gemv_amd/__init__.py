@@ -28,7 +28,8 @@ MOE_MAX_EXPERTS = 1024
 MOE_ALIGN = 256
 
 EXPORTED = [
-    "moe_route_topk", "moe_union", "moe_route_union", "moe_expert_forward", "moe_expert_forward_ex",
+    "moe_route_topk", "moe_route_topk_ex", "moe_union", "moe_route_union", "moe_route_union_ex",
+    "moe_expert_forward", "moe_expert_forward_ex",
     "moe_hit_count", "moe_residual_rmsnorm", "moe_route_workspace_size", "moe_forward_workspace_size",
     "moe_workspace_size", "moe_block_bytes", "moe_pack_expert", "moe_strerror",
 ]
@@ -55,6 +56,13 @@ class ForwardOptions(ctypes.Structure):
                 ("small_gateup_start", ctypes.c_void_p), ("small_gateup_end", ctypes.c_void_p),
                 ("small_down_start", ctypes.c_void_p), ("small_down_end", ctypes.c_void_p),
                 ("mfma_min_tokens", ctypes.c_int32), ("mfma_small_min_tokens", ctypes.c_int32)]
+
+
+class RouteOptions(ctypes.Structure):
+    """struct moe_route_options: the opt-in router variant (selection-only
+    bias, normalised and scaled weights)"""
+    _fields_ = [("bias_select_only", ctypes.c_int32), ("normalize", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
 
 
 class PoolDesc(ctypes.Structure):
@@ -90,6 +98,10 @@ def lib():
         L.moe_union.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp]
         L.moe_route_union.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                       vp, sz, vp]
+        RO = ctypes.POINTER(RouteOptions)
+        L.moe_route_topk_ex.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, vp, vp, sz, vp, RO]
+        L.moe_route_union_ex.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp,
+                                         vp, vp, sz, vp, RO]
         L.moe_expert_forward.argtypes = [P, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_expert_forward_ex.argtypes = [P, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                             ctypes.POINTER(ForwardOptions)]
@@ -112,7 +124,8 @@ def lib():
         L.moe_cache_stats.restype = i32
         L.moe_strerror.argtypes = [i32]
         L.moe_strerror.restype = ctypes.c_char_p
-        for name in ("moe_route_topk", "moe_union", "moe_route_union", "moe_expert_forward",
+        for name in ("moe_route_topk", "moe_route_topk_ex", "moe_union", "moe_route_union",
+                     "moe_route_union_ex", "moe_expert_forward",
                      "moe_expert_forward_ex", "moe_hit_count",
                      "moe_residual_rmsnorm", "moe_pack_expert", *PROBE_EXPORTED):
             getattr(L, name).restype = i32
@@ -176,7 +189,20 @@ def workspace_size(pool: PoolDesc, n_tokens, k) -> int:
 
 # --------------------------------------------------------------------- calls
 
-def route_topk(x, w_router, b_router, k, topk_ids, topk_w, workspace, stream=None):
+def _route_opt(options):
+    """None, or a RouteOptions pointer from a RouteOptions or a dict of its fields."""
+    if options is None:
+        return None
+    if isinstance(options, dict):
+        options = RouteOptions(int(options.get("bias_select_only", 0)),
+                               int(options.get("normalize", 0)),
+                               float(options.get("scale", 1.0)))
+    return ctypes.byref(options)
+
+
+def route_topk(x, w_router, b_router, k, topk_ids, topk_w, workspace, stream=None, options=None):
+    """moe_route_topk, or moe_route_topk_ex when options (RouteOptions or a
+    dict with bias_select_only / normalize / scale) are given."""
     import torch
     _expect(x, torch.float32, "x")
     _expect(w_router, torch.float32, "w_router")
@@ -185,10 +211,12 @@ def route_topk(x, w_router, b_router, k, topk_ids, topk_w, workspace, stream=Non
     _expect(topk_w, torch.float32, "topk_w")
     N, d = x.shape
     E = w_router.shape[0]
-    _check(lib().moe_route_topk(_ptr(x), N, d, _ptr(w_router), _ptr(b_router), E, k,
-                                _ptr(topk_ids), _ptr(topk_w), _ptr(workspace),
-                                workspace.numel() * workspace.element_size(), _stream(stream)),
-           "moe_route_topk")
+    args = (_ptr(x), N, d, _ptr(w_router), _ptr(b_router), E, k, _ptr(topk_ids), _ptr(topk_w),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if options is None:
+        _check(lib().moe_route_topk(*args), "moe_route_topk")
+    else:
+        _check(lib().moe_route_topk_ex(*args, _route_opt(options)), "moe_route_topk_ex")
 
 
 def union(topk_ids, n_experts, union_ids, n_union, expert_offsets, perm, stream=None):
@@ -202,8 +230,9 @@ def union(topk_ids, n_experts, union_ids, n_union, expert_offsets, perm, stream=
 
 
 def route_union(x, w_router, b_router, k, topk_ids, topk_w, union_ids, n_union, expert_offsets,
-                perm, counters, workspace, stream=None):
-    """moe_route_union: route_topk, union and (counters not None) hit_count in one call."""
+                perm, counters, workspace, stream=None, options=None):
+    """moe_route_union: route_topk, union and (counters not None) hit_count in one call
+    (moe_route_union_ex when options are given, as in route_topk)."""
     import torch
     _expect(x, torch.float32, "x")
     _expect(w_router, torch.float32, "w_router")
@@ -216,12 +245,13 @@ def route_union(x, w_router, b_router, k, topk_ids, topk_w, union_ids, n_union, 
         raise TypeError("counters: expected a 64-bit integer tensor")
     N, d = x.shape
     E = w_router.shape[0]
-    _check(lib().moe_route_union(_ptr(x), N, d, _ptr(w_router), _ptr(b_router), E, k,
-                                 _ptr(topk_ids), _ptr(topk_w), _ptr(union_ids), _ptr(n_union),
-                                 _ptr(expert_offsets), _ptr(perm), _ptr(counters),
-                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                 _stream(stream)),
-           "moe_route_union")
+    args = (_ptr(x), N, d, _ptr(w_router), _ptr(b_router), E, k, _ptr(topk_ids), _ptr(topk_w),
+            _ptr(union_ids), _ptr(n_union), _ptr(expert_offsets), _ptr(perm), _ptr(counters),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if options is None:
+        _check(lib().moe_route_union(*args), "moe_route_union")
+    else:
+        _check(lib().moe_route_union_ex(*args, _route_opt(options)), "moe_route_union_ex")
 
 
 def hit_count(topk_ids, n_experts, counters, stream=None):

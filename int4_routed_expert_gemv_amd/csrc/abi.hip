@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "internal.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -219,9 +220,46 @@ const char *moe_strerror(moe_status st)
     return "unknown status";
 }
 
+}  // extern "C"
+
+namespace {
+
+// Route options -> (bias for the router, top-k options); false on a bad option
+bool route_options(const moe_route_options *opt, const float *b_router, const float **b_in,
+                   TopkOpt *to)
+{
+    *b_in = b_router;
+    *to = TopkOpt();
+    if (!opt) return true;
+    if ((opt->bias_select_only != 0 && opt->bias_select_only != 1) ||
+        (opt->normalize != 0 && opt->normalize != 1) || !(opt->scale > 0.0f) ||
+        !(opt->scale < 3.0e38f))
+        return false;
+    if (opt->bias_select_only) {
+        *b_in = nullptr;       // scores without the bias
+        to->sel = b_router;    // the bias only in the selection keys (null: none)
+    }
+    to->norm = opt->normalize;
+    to->scale = opt->scale;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
 moe_status moe_route_topk(const float *x, int n_tokens, int d_model, const float *w_router,
                           const float *b_router, int n_experts, int k, int32_t *topk_ids,
                           float *topk_w, void *workspace, size_t ws_bytes, hipStream_t stream)
+{
+    return moe_route_topk_ex(x, n_tokens, d_model, w_router, b_router, n_experts, k, topk_ids,
+                             topk_w, workspace, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_route_topk_ex(const float *x, int n_tokens, int d_model, const float *w_router,
+                             const float *b_router, int n_experts, int k, int32_t *topk_ids,
+                             float *topk_w, void *workspace, size_t ws_bytes, hipStream_t stream,
+                             const moe_route_options *opt)
 {
     if (n_tokens < 0 || d_model <= 0) return MOE_EINVAL;
     moe_status st = check_k(k, n_experts);
@@ -234,12 +272,16 @@ moe_status moe_route_topk(const float *x, int n_tokens, int d_model, const float
     if (((uintptr_t)x % 16) || ((uintptr_t)w_router % 16)) return MOE_EALIGN;
     if (!workspace || ws_bytes < moe_route_workspace_size(n_tokens, n_experts)) return MOE_EWORKSPACE;
     if (!aligned(workspace)) return MOE_EALIGN;
+    const float *b_in;
+    TopkOpt to;
+    if (!route_options(opt, b_router, &b_in, &to)) return MOE_EINVAL;
+    if (to.sel && ((uintptr_t)to.sel % 4)) return MOE_EALIGN;
     float *scores = static_cast<float *>(workspace);
-    if (launch_router(x, n_tokens, d_model, w_router, b_router, n_experts, scores, stream) !=
+    if (launch_router(x, n_tokens, d_model, w_router, b_in, n_experts, scores, stream) !=
         hipSuccess)
         return MOE_EHIP;
-    if (launch_topk(scores, router_slices(n_tokens, d_model, n_experts), b_router, n_tokens,
-                    n_experts, k, topk_ids, topk_w, stream) != hipSuccess)
+    if (launch_topk(scores, router_slices(n_tokens, d_model, n_experts), b_in, n_tokens,
+                    n_experts, k, topk_ids, topk_w, stream, to) != hipSuccess)
         return MOE_EHIP;
     return MOE_OK;
 }
@@ -285,6 +327,18 @@ moe_status moe_route_union(const float *x, int n_tokens, int d_model, const floa
                            int32_t *expert_offsets, int32_t *perm, uint64_t *counters,
                            void *workspace, size_t ws_bytes, hipStream_t stream)
 {
+    return moe_route_union_ex(x, n_tokens, d_model, w_router, b_router, n_experts, k, topk_ids,
+                              topk_w, union_ids, n_union, expert_offsets, perm, counters,
+                              workspace, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_route_union_ex(const float *x, int n_tokens, int d_model, const float *w_router,
+                              const float *b_router, int n_experts, int k, int32_t *topk_ids,
+                              float *topk_w, int32_t *union_ids, int32_t *n_union,
+                              int32_t *expert_offsets, int32_t *perm, uint64_t *counters,
+                              void *workspace, size_t ws_bytes, hipStream_t stream,
+                              const moe_route_options *opt)
+{
     // every check of moe_route_topk, moe_union and moe_hit_count, before any launch
     if (n_tokens < 0 || d_model <= 0) return MOE_EINVAL;
     moe_status st = check_k(k, n_experts);
@@ -302,18 +356,22 @@ moe_status moe_route_union(const float *x, int n_tokens, int d_model, const floa
     if (!workspace || ws_bytes < moe_route_workspace_size(n_tokens, n_experts))
         return MOE_EWORKSPACE;
     if (!aligned(workspace)) return MOE_EALIGN;
+    const float *b_in;
+    TopkOpt to;
+    if (!route_options(opt, b_router, &b_in, &to)) return MOE_EINVAL;
+    if (to.sel && ((uintptr_t)to.sel % 4)) return MOE_EALIGN;
     float *scores = static_cast<float *>(workspace);
     const int P = router_slices(n_tokens, d_model, n_experts);
-    if (launch_router(x, n_tokens, d_model, w_router, b_router, n_experts, scores, stream) !=
+    if (launch_router(x, n_tokens, d_model, w_router, b_in, n_experts, scores, stream) !=
         hipSuccess)
         return MOE_EHIP;
     if (n_tokens <= route_tail_max_tokens())
-        return launch_route_tail(scores, P, b_router, n_tokens, n_experts, k, topk_ids, topk_w,
-                                 union_ids, n_union, expert_offsets, perm, counters,
-                                 stream) == hipSuccess
+        return launch_route_tail(scores, P, b_in, n_tokens, n_experts, k, topk_ids, topk_w,
+                                 union_ids, n_union, expert_offsets, perm, counters, stream,
+                                 to) == hipSuccess
                    ? MOE_OK
                    : MOE_EHIP;
-    if (launch_topk(scores, P, b_router, n_tokens, n_experts, k, topk_ids, topk_w, stream) !=
+    if (launch_topk(scores, P, b_in, n_tokens, n_experts, k, topk_ids, topk_w, stream, to) !=
         hipSuccess)
         return MOE_EHIP;
     const int A = n_tokens * k;

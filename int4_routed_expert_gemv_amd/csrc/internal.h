@@ -106,8 +106,9 @@ int router_slices_bound(int N, int E);   // the largest P any d can give
 int router_slices(int N, int d, int E);
 hipError_t launch_router(const float *x, int N, int d, const float *wr, const float *b,
                          int E, float *out, hipStream_t s);
+struct TopkOpt;
 hipError_t launch_topk(const float *in, int P, const float *b, int N, int E, int k,
-                       int32_t *ids, float *w, hipStream_t s);
+                       int32_t *ids, float *w, hipStream_t s, TopkOpt opt);
 hipError_t launch_union(const int32_t *ids, int A, int E, int32_t *union_ids, int32_t *n_union,
                         int32_t *offsets, int32_t *perm, hipStream_t s);
 hipError_t launch_hit_count(const int32_t *ids, int A, int E, uint64_t *counters, hipStream_t s);
@@ -124,7 +125,8 @@ hipError_t launch_union_chunked(const int32_t *ids, int A, int E, int32_t *union
                                 hipStream_t s);
 hipError_t launch_route_tail(const float *in, int P, const float *b, int N, int E, int k,
                              int32_t *ids, float *w, int32_t *union_ids, int32_t *n_union,
-                             int32_t *offsets, int32_t *perm, uint64_t *counters, hipStream_t s);
+                             int32_t *offsets, int32_t *perm, uint64_t *counters, hipStream_t s,
+                             TopkOpt opt);
 int gemv_tokens_per_item(const Geo &g, int n_tokens);
 hipError_t launch_gateup(const Fwd &f, hipStream_t s);
 hipError_t launch_down(const Fwd &f, hipStream_t s);

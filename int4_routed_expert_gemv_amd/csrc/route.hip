@@ -226,11 +226,11 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(
 // One wave per token (the selection itself is topk_wave).
 __global__ __launch_bounds__(256) void topk_kernel(
     const float *__restrict__ in, int P, const float *__restrict__ b, int N, int E, int k,
-    int32_t *__restrict__ ids, float *__restrict__ w)
+    int32_t *__restrict__ ids, float *__restrict__ w, TopkOpt opt)
 {
     const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     if (t >= N) return;
-    topk_wave(in, P, b, N, E, k, t, ids, w, nullptr);
+    topk_wave(in, P, b, N, E, k, t, ids, w, nullptr, opt);
 }
 
 }  // namespace
@@ -281,11 +281,11 @@ hipError_t launch_router(const float *x, int N, int d, const float *wr, const fl
 }
 
 hipError_t launch_topk(const float *in, int P, const float *b, int N, int E, int k, int32_t *ids,
-                       float *w, hipStream_t s)
+                       float *w, hipStream_t s, TopkOpt opt)
 {
     const int per_block = 4;
     hipLaunchKernelGGL(topk_kernel, dim3((N + per_block - 1) / per_block), dim3(per_block * kWave),
-                       0, s, in, P, b, N, E, k, ids, w);
+                       0, s, in, P, b, N, E, k, ids, w, opt);
     return hipGetLastError();
 }
 

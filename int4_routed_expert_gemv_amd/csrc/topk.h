@@ -24,6 +24,18 @@ __device__ __forceinline__ uint32_t sortable(float v)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Opt-in router variant. sel (may be null): a bias that only steers the
+// selection, the key of expert e being the float32 sum s + sel[e] while the
+// weight stays the score; norm: each weight is divided by the sum of the k
+// chosen scores (added in rank order); every weight is then multiplied by
+// scale. The default (sel null, norm 0, scale 1) keeps w = s.
+struct TopkOpt {
+    const float *sel = nullptr;
+    int norm = 0;
+    float scale = 1.0f;
+    bool active() const { return sel || norm || scale != 1.0f; }
+};
+
 // One wave selects token t's k best experts: k rounds of a wave-wide max over
 // 64-bit keys (sortable score, then inverted id so equal scores go to the
 // lower id). With P == 1, `in` holds the scores [N][E]; with P > 1 it holds
@@ -34,7 +46,7 @@ __device__ __forceinline__ uint32_t sortable(float v)
 __device__ __forceinline__ void topk_wave(const float *__restrict__ in, int P,
                                           const float *__restrict__ b, int N, int E, int k, int t,
                                           int32_t *__restrict__ ids, float *__restrict__ w,
-                                          int32_t *lds_ids)
+                                          int32_t *lds_ids, TopkOpt opt = TopkOpt())
 {
     const int lane = threadIdx.x % kWave;
     uint32_t hi[kMaxPerLane];
@@ -77,9 +89,13 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ in, int P,
 #pragma unroll
     for (int m = 0; m < kMaxPerLane; ++m) {
         const int e = lane + m * kWave;
-        hi[m] = e < E ? sortable(sv[m]) : 0u;
+        float key = sv[m];
+        if (opt.sel && e < E) key = sv[m] + opt.sel[e];  // one float32 rounding
+        hi[m] = e < E ? sortable(key) : 0u;
         if (e >= E) taken |= 1u << m;
     }
+    const bool rescale = opt.norm || opt.scale != 1.0f;
+    float wsum = 0.0f, wmine = 0.0f;  // chosen scores: the sum, and lane j's of round j
     for (int j = 0; j < k; ++j) {
         uint32_t bh = 0, bl = 0;  // best key of this lane: (hi, ~id)
         int bm = -1;
@@ -104,10 +120,17 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ in, int P,
             // the lane holding the winner records it
             taken |= 1u << bm;
             ids[(size_t)t * k + j] = id;
-            w[(size_t)t * k + j] = bs;
+            if (!rescale) w[(size_t)t * k + j] = bs;
             if (lds_ids) lds_ids[t * k + j] = id;
         }
+        if (rescale) {
+            const float ws = __shfl(bs, id % kWave, kWave);  // the winner's score
+            wsum += ws;
+            if (lane == j) wmine = ws;
+        }
     }
+    if (rescale && lane < k)
+        w[(size_t)t * k + lane] = opt.norm ? wmine / wsum * opt.scale : wmine * opt.scale;
 }
 
 }  // namespace moe

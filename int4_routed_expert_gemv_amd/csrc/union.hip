@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kUnionThreads) void route_tail_kernel(
     const float *__restrict__ in, int P, const float *__restrict__ b, int N, int E, int k,
     int32_t *__restrict__ ids, float *__restrict__ w, int32_t *__restrict__ union_ids,
     int32_t *__restrict__ n_union, int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
-    unsigned long long *__restrict__ counters)
+    unsigned long long *__restrict__ counters, TopkOpt opt)
 {
     __shared__ int32_t s_ids[kTailTokens * MOE_MAX_K];
     __shared__ int cnt[MOE_MAX_EXPERTS];
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kUnionThreads) void route_tail_kernel(
     for (int a = tid; a < A; a += blockDim.x) s_ids[a] = -1;
     __syncthreads();
     const int t = tid / kWave;
-    if (t < N) topk_wave(in, P, b, N, E, k, t, ids, w, s_ids);
+    if (t < N) topk_wave(in, P, b, N, E, k, t, ids, w, s_ids, opt);
     __syncthreads();
     if (A <= kWave) {  // one wave; the workgroup has one wave per token
         if (t == 0) union_wave(s_ids, A, E, union_ids, n_union, offsets, perm, counters, cnt);
@@ -418,13 +418,14 @@ int route_tail_max_tokens() { return kTailTokens; }
 
 hipError_t launch_route_tail(const float *in, int P, const float *b, int N, int E, int k,
                              int32_t *ids, float *w, int32_t *union_ids, int32_t *n_union,
-                             int32_t *offsets, int32_t *perm, uint64_t *counters, hipStream_t s)
+                             int32_t *offsets, int32_t *perm, uint64_t *counters, hipStream_t s,
+                             TopkOpt opt)
 {
     if (N < 1 || N > kTailTokens) return hipErrorInvalidValue;
     const int threads = N * k <= kWave ? N * kWave : kUnionThreads;
     hipLaunchKernelGGL(route_tail_kernel, dim3(1), dim3(threads), 0, s, in, P, b, N, E, k,
                        ids, w, union_ids, n_union, offsets, perm,
-                       reinterpret_cast<unsigned long long *>(counters));
+                       reinterpret_cast<unsigned long long *>(counters), opt);
     return hipGetLastError();
 }
 

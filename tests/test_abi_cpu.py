@@ -89,6 +89,32 @@ def test_route_union_argument_checks():
     assert call(N=0, x=None, ids=None) == moe.MOE_OK  # nothing to do
 
 
+@pytest.mark.parametrize("sel,norm,scale", [(2, 0, 1.0), (-1, 0, 1.0), (0, 3, 1.0), (1, 1, 0.0),
+                                            (1, 1, -2.0), (0, 0, float("nan")),
+                                            (0, 1, float("inf"))])
+def test_route_options_are_checked_before_launch(sel, norm, scale):
+    """The _ex calls reject a bad router option with MOE_EINVAL (nothing is
+    enqueued, so fake device pointers are never touched)."""
+    L = moe.lib()
+    big = 1 << 30
+    opt = ctypes.byref(moe.RouteOptions(sel, norm, scale))
+    assert L.moe_route_topk_ex(FAKE, 4, 256, FAKE, FAKE, 16, 2, FAKE, FAKE, FAKE, big, None,
+                               opt) == moe.MOE_EINVAL
+    for N in (4, 40):
+        assert L.moe_route_union_ex(FAKE, N, 256, FAKE, FAKE, 16, 2, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, None, FAKE, big, None, opt) == moe.MOE_EINVAL
+
+
+def test_route_options_misaligned_bias_and_empty_batch():
+    L = moe.lib()
+    big = 1 << 30
+    opt = ctypes.byref(moe.RouteOptions(1, 1, 2.5))
+    assert L.moe_route_union_ex(FAKE, 4, 256, FAKE, FAKE + 2, 16, 2, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, None, FAKE, big, None, opt) == moe.MOE_EALIGN
+    assert L.moe_route_union_ex(None, 0, 256, None, None, 16, 2, None, None, None, None, None,
+                                None, None, None, 0, None, opt) == moe.MOE_OK
+
+
 def test_route_topk_argument_checks():
     L = moe.lib()
     ws = FAKE
