@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=400)
     p.add_argument("--config", default="decode1")
+    p.add_argument("--group", type=int, default=None,
+                   help="scale group of the int4 layers instead of the workload's (e.g. 64)")
     p.add_argument("--layers", type=int, default=8, help="layer pools rotated over the steps")
     p.add_argument("--batches", type=int, default=16, help="distinct token batches rotated")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -148,6 +150,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     base = synth.CONFIGS[args.config]
+    if args.group is not None:
+        base = dataclasses.replace(base, layers=tuple(
+            dataclasses.replace(ls, group=args.group) if ls.wbits == 4 else ls
+            for ls in base.layers))
     spec = base.layer
     stack = len(base.layers) > 1
     if stack:
@@ -387,7 +393,8 @@ def main():
         else:
             roof = {"bound": "hbm", "achieved": pz["achieved_GBps"], "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": pz["achieved_GBps"] / HBM_PEAK_GBS}
-        roof["traffic"] = measured_traffic(args.config, labels[top][1])
+        roof["traffic"] = measured_traffic(
+            args.config if args.group is None else f"{args.config}_g{args.group}", labels[top][1])
         roof["kernel"] = labels[top][0]
         roof["passes"] = passes
         roof["measured_ceiling"] = measured_ceiling(moe, hip, torch, roof["bound"],
@@ -408,7 +415,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": (f"{cfg.name}: {base.description}" +
-                         ("" if stack else f"; {L_rot} layer pools rotated")),
+                         ("" if stack else f"; {L_rot} layer pools rotated") +
+                         (f"; int4 scale groups of {args.group}" if args.group else "")),
             "n_tokens": N, "k": k, "d_model": d, "d_ff": f, "n_experts": E,
             "wbits": spec.wbits, "group": spec.group, "layers_per_step": L_rot if stack else 1,
             "layer_pools": L_rot, "mean_union": mean_union,

@@ -359,3 +359,23 @@ def test_route_union_many_experts(E, N, k):
                               layers=(dataclasses.replace(base.layer, n_experts=E),))
     say(f"[many experts] E={E} N={N} k={k}")
     full_parity(cfg, fused_route=True)
+
+
+def test_group64_scales_every_pass():
+    """Scale groups of 64 inputs (the container format the README's "Get
+    started" names, gs64) on the decode layer's shapes: each pass alone and
+    the default mix, against one oracle run."""
+    base = synth.CONFIGS["decode64"]
+    cfg = dataclasses.replace(base, layers=(dataclasses.replace(base.layers[0], group=64),))
+    spec, x, wr, b, blocks, shared, _ = oracle_then_pool(cfg)
+    say(f"[gs64] N={cfg.n_tokens} k={cfg.k} G={spec.group}")
+    ref = oracle.layer_step(x, wr, b, cfg.k, blocks, shared, spec.d, spec.f, spec.wbits,
+                            spec.group)
+    pool = upload_pool(spec, blocks, shared)
+    for big, small in [(-1, -1), (-1, 1), (1, -1), (None, None)]:
+        got = run_layer(pool, x, wr, b, cfg.k, mfma_min_tokens=big, mfma_small_min_tokens=small)
+        check_routing(got, ref, spec.n_experts)
+        err = check_y(got["y"], ref["y"])
+        say(f"[gs64] big={big} small={small} max rel err {err:.2e}")
+    del pool
+    torch.cuda.empty_cache()
