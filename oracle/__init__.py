@@ -50,7 +50,8 @@ def lib():
         L.oracle_dequant_row.argtypes = [vp, vp, i32, i32, i32, i32, vp]
         L.oracle_router.argtypes = [vp, i32, i32, vp, vp, i32, vp, vp]
         L.oracle_topk.argtypes = [vp, i32, i32, i32, vp, vp]
-        L.oracle_topk_select.argtypes = [vp, vp, i32, i32, i32, i32, ctypes.c_double, vp, vp]
+        L.oracle_topk_select.argtypes = [vp, vp, i32, i32, i32, i32, ctypes.c_double,
+                                         ctypes.c_float, vp, vp]
         L.oracle_union.restype = i32
         L.oracle_union.argtypes = [vp, i32, i32, i32, vp, vp, vp]
         L.oracle_hit_count.argtypes = [vp, i32, i32, i32, vp]
@@ -106,19 +107,23 @@ def topk(scores, k):
     return ids, w
 
 
-def topk_select(scores, b_sel, k, normalize=False, scale=1.0):
+def topk_select(scores, b_sel, k, normalize=False, scale=1.0, top_p=0.0):
     """Router variant: the bias b_sel only steers the selection (key = s + b
     in float32); weights are the unbiased scores, optionally divided by their
     sum over the chosen k, times scale. scores: unbiased sigmoid scores [N][E]
-    (router(x, Wr) with no bias)."""
+    (router(x, Wr) with no bias); b_sel None: no selection bias. top_p in
+    (0, 1): ranked slots past that fraction of the chosen score mass get id -1
+    and weight 0."""
     s, sp = _c(scores, np.float32)
-    b, bp = _c(b_sel, np.float32)
     N, E = s.shape
-    assert b.shape == (E,)
+    bp = None
+    if b_sel is not None:
+        b, bp = _c(b_sel, np.float32)
+        assert b.shape == (E,)
     ids = np.empty((N, k), np.int32)
     w = np.empty((N, k), np.float32)
     lib().oracle_topk_select(sp, bp, N, E, k, 1 if normalize else 0, float(scale),
-                             ids.ctypes.data, w.ctypes.data)
+                             float(top_p), ids.ctypes.data, w.ctypes.data)
     return ids, w
 
 

@@ -148,13 +148,24 @@ void oracle_topk(const float *scores, int n_tokens, int n_experts, int k,
  *   ids    = the k best experts by (key desc, id asc), in rank order
  *   w[j]   = s[ids[j]] * scale, or with normalize
  *            s[ids[j]] / sum_j' s[ids[j']] * scale (double, rounded to
- *            float32 once).
+ *            float32 once);
+ *   top_p in (0, 1): a lossy cutoff on the ranked slots. With S the float32
+ *            sum of the k chosen scores in rank order and c_j the float32 sum
+ *            of the scores ranked before slot j, slot j is kept when j == 0
+ *            or c_j < top_p * S (float32); a dropped slot gets id -1 and
+ *            weight 0, and the kept weights are left as above. Off when
+ *            top_p <= 0 or >= 1. (The pages mention a top-p option that trades
+ *            accuracy for speed without defining it; this is the plainest
+ *            reading: the smallest ranked prefix holding a fraction top_p of
+ *            the chosen score mass.)
+ * b_sel may be NULL (no selection bias).
  * Rows of the pages this follows: the sigmoid gate over all experts with
  * n_group = 1 ("Public Colibri Observation and Revision Ledger", "Exact
  * Architecture and Data-Flow Reconstruction"); where the bias enters and
  * whether weights are renormalised the pages leave open. */
 void oracle_topk_select(const float *scores, const float *b_sel, int n_tokens, int n_experts,
-                        int k, int normalize, double scale, int32_t *topk_ids, float *topk_w)
+                        int k, int normalize, double scale, float top_p, int32_t *topk_ids,
+                        float *topk_w)
 {
 #pragma omp parallel for schedule(static)
     for (int t = 0; t < n_tokens; ++t) {
@@ -162,7 +173,7 @@ void oracle_topk_select(const float *scores, const float *b_sel, int n_tokens, i
         float *key = (float *)malloc(sizeof(float) * n_experts);
         int *order = (int *)malloc(sizeof(int) * n_experts);
         for (int e = 0; e < n_experts; ++e) {
-            volatile float kv = s[e] + b_sel[e];  /* one float32 rounding */
+            volatile float kv = s[e] + (b_sel ? b_sel[e] : 0.0f);  /* one float32 rounding */
             key[e] = kv;
         }
         for (int e = 0; e < n_experts; ++e) {
@@ -175,11 +186,19 @@ void oracle_topk_select(const float *scores, const float *b_sel, int n_tokens, i
         }
         double sum = 0.0;
         for (int j = 0; j < k; ++j) sum += (double)s[order[j]];
+        const int cut = top_p > 0.0f && top_p < 1.0f;
+        volatile float mass = 0.0f;  /* float32 sums in rank order */
+        for (int j = 0; j < k; ++j) mass = mass + s[order[j]];
+        volatile float thr = top_p * mass;
+        volatile float before = 0.0f;
         for (int j = 0; j < k; ++j) {
-            topk_ids[(size_t)t * k + j] = order[j];
+            const int keep = !cut || j == 0 || before < thr;
+            before = before + s[order[j]];
+            topk_ids[(size_t)t * k + j] = keep ? order[j] : -1;
             topk_w[(size_t)t * k + j] =
-                normalize ? (float)((double)s[order[j]] / sum * scale)
-                          : (float)((double)s[order[j]] * scale);
+                !keep ? 0.0f
+                      : normalize ? (float)((double)s[order[j]] / sum * scale)
+                                  : (float)((double)s[order[j]] * scale);
         }
         free(key);
         free(order);
@@ -197,7 +216,9 @@ int oracle_union(const int32_t *topk_ids, int n_tokens, int k, int n_experts,
     int n_assign = n_tokens * k;
     int *cnt = (int *)calloc((size_t)n_experts, sizeof(int));
     int *cur = (int *)calloc((size_t)n_experts, sizeof(int));
-    for (int a = 0; a < n_assign; ++a) cnt[topk_ids[a]]++;
+    /* ids outside [0, n_experts) (a dropped slot is -1) are left out */
+    for (int a = 0; a < n_assign; ++a)
+        if (topk_ids[a] >= 0 && topk_ids[a] < n_experts) cnt[topk_ids[a]]++;
     int n_union = 0;
     for (int e = 0; e < n_experts; ++e)
         if (cnt[e]) union_ids[n_union++] = e;
@@ -205,7 +226,7 @@ int oracle_union(const int32_t *topk_ids, int n_tokens, int k, int n_experts,
     for (int e = 0; e < n_experts; ++e) offsets[e + 1] = offsets[e] + cnt[e];
     for (int a = 0; a < n_assign; ++a) {
         int e = topk_ids[a];
-        perm[offsets[e] + cur[e]++] = a;
+        if (e >= 0 && e < n_experts) perm[offsets[e] + cur[e]++] = a;
     }
     free(cnt);
     free(cur);
@@ -217,9 +238,8 @@ int oracle_union(const int32_t *topk_ids, int n_tokens, int k, int n_experts,
 void oracle_hit_count(const int32_t *topk_ids, int n_tokens, int k, int n_experts,
                       uint64_t *counters)
 {
-    (void)n_experts;
     for (int a = 0; a < n_tokens * k; ++a)
-        counters[topk_ids[a]] += 1;
+        if (topk_ids[a] >= 0 && topk_ids[a] < n_experts) counters[topk_ids[a]] += 1;
 }
 
 /* ---- Expert math ------------------------------------------------------- */
@@ -292,8 +312,9 @@ int oracle_expert_forward(const uint8_t *pool, size_t stride, int n_experts,
                           const int32_t *topk_ids, const float *topk_w, double *y)
 {
     int n_assign = n_tokens * k;
+    /* -1 marks a dropped slot (top-p cutoff): no expert, nothing added */
     for (int a = 0; a < n_assign; ++a)
-        if (topk_ids[a] < 0 || topk_ids[a] >= n_experts) return -1;
+        if (topk_ids[a] < -1 || topk_ids[a] >= n_experts) return -1;
 
     double *Xd = (double *)malloc(sizeof(double) * (size_t)n_tokens * d);
     for (size_t i = 0; i < (size_t)n_tokens * d; ++i) Xd[i] = (double)x[i];
@@ -328,6 +349,7 @@ int oracle_expert_forward(const uint8_t *pool, size_t stride, int n_experts,
         memset(y, 0, sizeof(double) * (size_t)n_tokens * d);
     for (int t = 0; t < n_tokens; ++t)
         for (int j = 0; j < k; ++j) {
+            if (topk_ids[(size_t)t * k + j] < 0) continue;
             double w = (double)topk_w[(size_t)t * k + j];
             const double *oj = o + ((size_t)t * k + j) * d;
             double *yt = y + (size_t)t * d;

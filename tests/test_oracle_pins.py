@@ -167,6 +167,72 @@ def test_topk_select_normalised_weights_sum_to_scale():
     np.testing.assert_allclose(w, chosen / chosen.sum(axis=1, keepdims=True) * 2.5, rtol=1e-6)
 
 
+def test_topk_topp_hand_computed():
+    """The top-p cutoff on a worked example (tests/golden/route_topp_hand.json)."""
+    with open(os.path.join(GOLD, "route_topp_hand.json")) as fh:
+        g = json.load(fh)
+    s = np.array([g["scores"]], np.float32)
+    ids, w = oracle.topk_select(s, None, g["k"], top_p=g["top_p"])
+    assert ids[0].tolist() == g["ids"]
+    np.testing.assert_array_equal(w[0], np.array(g["w_raw"], np.float32))
+    ids, w = oracle.topk_select(s, None, g["k"], normalize=True, top_p=g["top_p"])
+    assert ids[0].tolist() == g["ids"]
+    np.testing.assert_allclose(w[0], g["w_normalized"], rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("p", [0.25, 0.5, 0.625, 0.75, 0.875])
+def test_topk_topp_exact_rational(p):
+    """With scores that are multiples of 1/64 and a dyadic p every float32 sum
+    and product is exact, so the kept slots are exactly the ranked prefix whose
+    mass before the slot is below p times the total (checked in rationals)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(int(p * 1000))
+    E, k, N = 16, 6, 50
+    s = (rng.integers(1, 64, size=(N, E)).astype(np.float32) / np.float32(64.0))
+    ids0, _ = oracle.topk(s, k)
+    ids, w = oracle.topk_select(s, None, k, top_p=p)
+    for t in range(N):
+        ranked = [Fraction(int(round(float(s[t, e]) * 64)), 64) for e in ids0[t]]
+        total, before = sum(ranked), Fraction(0)
+        for j, e in enumerate(ids0[t]):
+            keep = j == 0 or before < Fraction(p).limit_denominator(1 << 20) * total
+            before += ranked[j]
+            assert ids[t, j] == (e if keep else -1)
+            assert w[t, j] == (s[t, e] if keep else 0.0)
+
+
+@pytest.mark.parametrize("p", [0.0, 1.0, 1.5, -0.5])
+def test_topk_topp_off(p):
+    rng = np.random.default_rng(3)
+    s = rng.random((20, 32)).astype(np.float32)
+    a = oracle.topk_select(s, None, 5)
+    b = oracle.topk_select(s, None, 5, top_p=p)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_dropped_slot_equals_smaller_k():
+    """A slot dropped by the cutoff (id -1) contributes nothing: the layer
+    equals the one with that slot removed, and union and counters skip it."""
+    cfg = synth.CONFIGS["tiny"]
+    spec = cfg.layer
+    x, wr, b = synth.tokens(cfg), *synth.router(cfg, 0)
+    blocks, shared = synth.expert_pool(cfg, 0), synth.shared_block(cfg, 0)
+    ids, w = oracle.topk(oracle.router(x, wr, b), 2)
+    ids_d, w_d = ids.copy(), w.copy()
+    ids_d[:, 1], w_d[:, 1] = -1, 0.0
+    y2 = oracle.expert_forward(blocks, shared, spec.d, spec.f, spec.wbits, spec.group, x, ids_d, w_d)
+    y1 = oracle.expert_forward(blocks, shared, spec.d, spec.f, spec.wbits, spec.group, x,
+                               ids[:, :1].copy(), w[:, :1].copy())
+    np.testing.assert_array_equal(y2, y1)
+    u2, off2, _ = oracle.union(ids_d, spec.n_experts)
+    u1, off1, _ = oracle.union(ids[:, :1].copy(), spec.n_experts)
+    np.testing.assert_array_equal(u2, u1)
+    np.testing.assert_array_equal(off2, off1)
+    np.testing.assert_array_equal(oracle.hit_count(ids_d, spec.n_experts),
+                                  oracle.hit_count(ids[:, :1].copy(), spec.n_experts))
+
+
 # ---------------------------------------------------------------- union, permutation, counters
 
 @pytest.mark.parametrize("N,k,E", [(1, 1, 4), (5, 3, 8), (17, 4, 16), (64, 8, 256)])
