@@ -193,7 +193,13 @@ moe_status moe_route_union(const float *x, int n_tokens, int d_model,
  *   normalize = 1: each chosen weight is divided by the sum of the token's
  *     k chosen scores (added in rank order);
  *   scale: multiplies every chosen weight (after normalising), > 0 and
- *     finite; 1 leaves the weights as they are.
+ *     finite; 1 leaves the weights as they are;
+ *   top_p: a lossy cutoff (the pages mention a top-p option that trades
+ *     accuracy for speed without defining it), off at 0 or >= 1. With S the
+ *     float32 sum of the token's k chosen scores in rank order, slot j is kept
+ *     when j == 0 or the float32 sum of the scores ranked before it is below
+ *     top_p * S; a dropped slot gets topk_ids -1 and topk_w 0, and the union,
+ *     the permutation, the hit counts and moe_expert_forward leave it out.
  * opt == NULL is the default reading (the same results as the calls above).
  * A bad option is MOE_EINVAL before anything is enqueued; b_router must be
  * 4-byte aligned.
@@ -202,6 +208,7 @@ typedef struct {
     int32_t bias_select_only; /* 0 or 1 */
     int32_t normalize;        /* 0 or 1 */
     float scale;              /* weight multiplier */
+    float top_p;              /* 0: no cutoff */
 } moe_route_options;
 
 moe_status moe_route_topk_ex(const float *x, int n_tokens, int d_model,
@@ -227,7 +234,10 @@ moe_status moe_route_union_ex(const float *x, int n_tokens, int d_model,
  *   E(x) = Wd (silu(Wg x) * (Wu x)),
  * over the union produced by moe_union (union_ids, n_union, expert_offsets,
  * perm are its outputs for the same n_tokens and k). topk_w is an input, so a
- * caller may inject gate weights. Each distinct expert's weights are streamed
+ * caller may inject gate weights; a slot with weight 0 adds nothing, and a
+ * slot left out of the permutation (an id outside [0, n_experts), such as a
+ * slot the top-p cutoff dropped) must have weight 0. Each distinct expert's
+ * weights are streamed
  * from HBM once per work item: single tokens on GEMV kernels, groups of up to
  * 32 or 128 tokens on the matrix cores (see moe_expert_forward_ex). y
  * [n_tokens][d_model] float32 is overwritten. workspace: at least

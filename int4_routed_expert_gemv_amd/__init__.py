@@ -62,7 +62,7 @@ class RouteOptions(ctypes.Structure):
     """struct moe_route_options: the opt-in router variant (selection-only
     bias, normalised and scaled weights)"""
     _fields_ = [("bias_select_only", ctypes.c_int32), ("normalize", ctypes.c_int32),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("top_p", ctypes.c_float)]
 
 
 class PoolDesc(ctypes.Structure):
@@ -196,7 +196,8 @@ def _route_opt(options):
     if isinstance(options, dict):
         options = RouteOptions(int(options.get("bias_select_only", 0)),
                                int(options.get("normalize", 0)),
-                               float(options.get("scale", 1.0)))
+                               float(options.get("scale", 1.0)),
+                               float(options.get("top_p", 0.0)))
     return ctypes.byref(options)
 
 

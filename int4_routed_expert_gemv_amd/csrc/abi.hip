@@ -233,7 +233,7 @@ bool route_options(const moe_route_options *opt, const float *b_router, const fl
     if (!opt) return true;
     if ((opt->bias_select_only != 0 && opt->bias_select_only != 1) ||
         (opt->normalize != 0 && opt->normalize != 1) || !(opt->scale > 0.0f) ||
-        !(opt->scale < 3.0e38f))
+        !(opt->scale < 3.0e38f) || !(opt->top_p >= 0.0f) || !(opt->top_p < 3.0e38f))
         return false;
     if (opt->bias_select_only) {
         *b_in = nullptr;       // scores without the bias
@@ -241,6 +241,7 @@ bool route_options(const moe_route_options *opt, const float *b_router, const fl
     }
     to->norm = opt->normalize;
     to->scale = opt->scale;
+    to->top_p = opt->top_p;
     return true;
 }
 

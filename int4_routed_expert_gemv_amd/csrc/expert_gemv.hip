@@ -647,6 +647,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
                             : make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
         const float wj = w[(size_t)t * k + j];
+        if (wj == 0.0f) continue;  // adds nothing; a dropped slot's row is never written
         const float4 v = reinterpret_cast<const float4 *>(o + ((size_t)t * k + j) * d)[q];
         acc.x = acc.x + wj * v.x;
         acc.y = acc.y + wj * v.y;

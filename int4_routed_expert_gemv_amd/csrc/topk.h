@@ -28,12 +28,15 @@ __device__ __forceinline__ uint32_t sortable(float v)
 // selection, the key of expert e being the float32 sum s + sel[e] while the
 // weight stays the score; norm: each weight is divided by the sum of the k
 // chosen scores (added in rank order); every weight is then multiplied by
-// scale. The default (sel null, norm 0, scale 1) keeps w = s.
+// scale. top_p in (0, 1): a lossy cutoff, slot j kept when j == 0 or the
+// float32 sum of the scores ranked before it is below top_p times the sum of
+// all k (both summed in rank order); a dropped slot gets id -1 and weight 0.
+// The default (sel null, norm 0, scale 1, top_p 0) keeps w = s.
 struct TopkOpt {
     const float *sel = nullptr;
     int norm = 0;
     float scale = 1.0f;
-    bool active() const { return sel || norm || scale != 1.0f; }
+    float top_p = 0.0f;
 };
 
 // One wave selects token t's k best experts: k rounds of a wave-wide max over
@@ -94,8 +97,13 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ in, int P,
         hi[m] = e < E ? sortable(key) : 0u;
         if (e >= E) taken |= 1u << m;
     }
-    const bool rescale = opt.norm || opt.scale != 1.0f;
-    float wsum = 0.0f, wmine = 0.0f;  // chosen scores: the sum, and lane j's of round j
+    const bool cut = opt.top_p > 0.0f && opt.top_p < 1.0f;
+    // with any option, lane j writes slot j after the rounds
+    const bool post = cut || opt.norm || opt.scale != 1.0f;
+    // chosen scores in rank order: their sum, and lane j's round-j score, id
+    // and the sum of the scores ranked before it
+    float wsum = 0.0f, wmine = 0.0f, wbefore = 0.0f;
+    int idmine = -1;
     for (int j = 0; j < k; ++j) {
         uint32_t bh = 0, bl = 0;  // best key of this lane: (hi, ~id)
         int bm = -1;
@@ -119,18 +127,30 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ in, int P,
         if (bm >= 0 && lane + bm * kWave == id) {
             // the lane holding the winner records it
             taken |= 1u << bm;
-            ids[(size_t)t * k + j] = id;
-            if (!rescale) w[(size_t)t * k + j] = bs;
-            if (lds_ids) lds_ids[t * k + j] = id;
+            if (!post) {
+                ids[(size_t)t * k + j] = id;
+                w[(size_t)t * k + j] = bs;
+                if (lds_ids) lds_ids[t * k + j] = id;
+            }
         }
-        if (rescale) {
+        if (post) {
             const float ws = __shfl(bs, id % kWave, kWave);  // the winner's score
+            if (lane == j) {
+                wmine = ws;
+                idmine = id;
+                wbefore = wsum;
+            }
             wsum += ws;
-            if (lane == j) wmine = ws;
         }
     }
-    if (rescale && lane < k)
-        w[(size_t)t * k + lane] = opt.norm ? wmine / wsum * opt.scale : wmine * opt.scale;
+    if (post && lane < k) {
+        const bool keep = !cut || lane == 0 || wbefore < opt.top_p * wsum;
+        const int idv = keep ? idmine : -1;
+        ids[(size_t)t * k + lane] = idv;
+        w[(size_t)t * k + lane] =
+            !keep ? 0.0f : (opt.norm ? wmine / wsum * opt.scale : wmine * opt.scale);
+        if (lds_ids) lds_ids[t * k + lane] = idv;
+    }
 }
 
 }  // namespace moe

@@ -89,15 +89,16 @@ def test_route_union_argument_checks():
     assert call(N=0, x=None, ids=None) == moe.MOE_OK  # nothing to do
 
 
-@pytest.mark.parametrize("sel,norm,scale", [(2, 0, 1.0), (-1, 0, 1.0), (0, 3, 1.0), (1, 1, 0.0),
-                                            (1, 1, -2.0), (0, 0, float("nan")),
-                                            (0, 1, float("inf"))])
-def test_route_options_are_checked_before_launch(sel, norm, scale):
+@pytest.mark.parametrize("sel,norm,scale,top_p", [
+    (2, 0, 1.0, 0.0), (-1, 0, 1.0, 0.0), (0, 3, 1.0, 0.0), (1, 1, 0.0, 0.0), (1, 1, -2.0, 0.0),
+    (0, 0, float("nan"), 0.0), (0, 1, float("inf"), 0.0), (0, 0, 1.0, float("nan")),
+    (0, 0, 1.0, -0.25), (1, 0, 1.0, float("inf"))])
+def test_route_options_are_checked_before_launch(sel, norm, scale, top_p):
     """The _ex calls reject a bad router option with MOE_EINVAL (nothing is
     enqueued, so fake device pointers are never touched)."""
     L = moe.lib()
     big = 1 << 30
-    opt = ctypes.byref(moe.RouteOptions(sel, norm, scale))
+    opt = ctypes.byref(moe.RouteOptions(sel, norm, scale, top_p))
     assert L.moe_route_topk_ex(FAKE, 4, 256, FAKE, FAKE, 16, 2, FAKE, FAKE, FAKE, big, None,
                                opt) == moe.MOE_EINVAL
     for N in (4, 40):

@@ -149,3 +149,89 @@ def test_select_bias_layer_step_tiny():
     np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
     err = lc.rel_err_rows(y.cpu().numpy(), ref_y)
     assert err.max() <= 2e-3, f"max per-token relative error {err.max():.3e}"
+
+
+def clear_of_cut(s, b, k, p, rel=1e-5):
+    """Tokens whose top-p decisions are not within `rel` of the threshold."""
+    key = (s + (b[None, :] if b is not None else 0)).astype(np.float32)
+    order = np.argsort(-key, axis=1, kind="stable")[:, :k]
+    ranked = np.take_along_axis(s, order, axis=1).astype(np.float64)
+    tot = ranked.sum(axis=1, keepdims=True)
+    before = np.cumsum(ranked, axis=1) - ranked
+    return np.all(np.abs(before[:, 1:] - p * tot) > rel * tot, axis=1)
+
+
+@pytest.mark.parametrize("N", [1, 16, 64, 600, 4096])
+@pytest.mark.parametrize("p,select", [(0.5, False), (0.9, True)])
+def test_top_p_route_against_oracle(N, p, select):
+    """The top-p cutoff: ids (-1 for dropped slots), weights (0 for them),
+    union, permutation and counters that leave the dropped slots out."""
+    k = 8
+    cfg = dataclasses.replace(synth.CONFIGS["decode64"], n_tokens=N, k=k)
+    x, wr, b, _, _ = lc.layer_inputs(cfg, 0)
+    say(f"[top-p] N={N} p={p} select={select}")
+    if select:
+        s = oracle.router(x, wr, None)
+        bsel = b
+    else:
+        s = oracle.router(x, wr, b)
+        bsel = None
+    ref_ids, ref_w = oracle.topk_select(s, bsel, k, top_p=p)
+    got = gpu_route(x, wr, b, k, dict(bias_select_only=int(select), top_p=p))
+    ok = clear_tokens(s, bsel if select else np.zeros(wr.shape[0], np.float32), k) & \
+        clear_of_cut(s, bsel, k, p)
+    assert ok.mean() >= 0.9, f"only {ok.mean():.3f} of the tokens are clear"
+    np.testing.assert_array_equal(got["ids"][ok], ref_ids[ok])
+    assert np.all(got["w"][got["ids"] < 0] == 0.0)
+    kept = ok[:, None] & (ref_ids >= 0)
+    dw = np.abs(got["w"].astype(np.float64) - ref_w)
+    assert np.all(dw[kept] <= 2e-6 + 2.0**-23 * np.abs(ref_w[kept]))
+    assert (got["ids"] < 0).any(), "the cutoff dropped nothing"
+    uref, offref, permref = oracle.union(got["ids"], wr.shape[0])
+    np.testing.assert_array_equal(got["union_ids"], uref)
+    np.testing.assert_array_equal(got["offsets"], offref)
+    np.testing.assert_array_equal(got["perm"][:offref[-1]], permref[:offref[-1]])
+    np.testing.assert_array_equal(got["counters"], oracle.hit_count(got["ids"], wr.shape[0]))
+
+
+@pytest.mark.parametrize("N,k,with_shared,p", [(1, 4, True, 0.6), (24, 4, True, 0.6),
+                                               (1, 2, False, 0.5), (24, 3, False, 0.6)])
+def test_top_p_layer_step_tiny(N, k, with_shared, p):
+    """Dropped slots through the expert step (the combine kernel, and at one
+    token without the shared expert the down kernel's direct combine; at
+    k = 2 a cutoff of 0.5 always drops the second slot)."""
+    base = synth.CONFIGS["tiny"]
+    cfg = dataclasses.replace(base, n_tokens=N, k=k)
+    spec = cfg.layers[0]
+    x, wr, b, _, _ = lc.layer_inputs(cfg, 0)
+    s = oracle.router(x, wr, b)
+    ref_ids, ref_w = oracle.topk_select(s, None, k, top_p=p)
+    blocks, shared = lc.canonical_pool(cfg, 0)
+    if not with_shared:
+        shared = None
+    ref_y = oracle.expert_forward(blocks, shared, spec.d, spec.f, spec.wbits, spec.group, x,
+                                  ref_ids, ref_w)
+    pool = upload_pool(spec, blocks, shared)
+    dev = "cuda"
+    E = spec.n_experts
+    xd, wrd, bd = (torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+                   for a in (x, wr, b))
+    ws = torch.empty(max(moe.workspace_size(pool.desc, N, k), 1), dtype=torch.uint8, device=dev)
+    ws.fill_(255)   # stale workspace: a dropped slot's expert row must never be read
+    ids = torch.empty((N, k), dtype=torch.int32, device=dev)
+    w = torch.empty((N, k), dtype=torch.float32, device=dev)
+    uid = torch.empty(E, dtype=torch.int32, device=dev)
+    nu = torch.empty(1, dtype=torch.int32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(N * k, dtype=torch.int32, device=dev)
+    y = torch.empty((N, spec.d), dtype=torch.float32, device=dev)
+    moe.route_union(xd, wrd, bd, k, ids, w, uid, nu, off, perm, None, ws,
+                    options=dict(top_p=p))
+    moe.expert_forward(pool.desc, xd, k, w, uid, nu, off, perm, y, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
+    assert (ref_ids < 0).any()
+    yv = y.cpu().numpy()
+    assert np.all(np.isfinite(yv))
+    err = lc.rel_err_rows(yv, ref_y)
+    assert err.max() <= 2e-3, f"max per-token relative error {err.max():.3e}"
