@@ -224,13 +224,14 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(
 }
 
 // One wave per token (the selection itself is topk_wave).
+template <bool OPT>
 __global__ __launch_bounds__(256) void topk_kernel(
     const float *__restrict__ in, int P, const float *__restrict__ b, int N, int E, int k,
     int32_t *__restrict__ ids, float *__restrict__ w, TopkOpt opt)
 {
     const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     if (t >= N) return;
-    topk_wave(in, P, b, N, E, k, t, ids, w, nullptr, opt);
+    topk_wave<OPT>(in, P, b, N, E, k, t, ids, w, nullptr, opt);
 }
 
 }  // namespace
@@ -284,8 +285,9 @@ hipError_t launch_topk(const float *in, int P, const float *b, int N, int E, int
                        float *w, hipStream_t s, TopkOpt opt)
 {
     const int per_block = 4;
-    hipLaunchKernelGGL(topk_kernel, dim3((N + per_block - 1) / per_block), dim3(per_block * kWave),
-                       0, s, in, P, b, N, E, k, ids, w, opt);
+    hipLaunchKernelGGL(opt.any() ? topk_kernel<true> : topk_kernel<false>,
+                       dim3((N + per_block - 1) / per_block), dim3(per_block * kWave), 0, s, in, P,
+                       b, N, E, k, ids, w, opt);
     return hipGetLastError();
 }
 

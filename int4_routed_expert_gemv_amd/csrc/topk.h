@@ -37,6 +37,10 @@ struct TopkOpt {
     int norm = 0;
     float scale = 1.0f;
     float top_p = 0.0f;
+    bool any() const
+    {
+        return sel || norm || scale != 1.0f || (top_p > 0.0f && top_p < 1.0f);
+    }
 };
 
 // One wave selects token t's k best experts: k rounds of a wave-wide max over
@@ -46,6 +50,9 @@ struct TopkOpt {
 // sigmoid(sum over slices in order + bias). The lane holding each round's
 // winner writes ids/w[t * k + j] and, when lds_ids is not null,
 // lds_ids[t * k + j].
+// OPT false: the options are ignored (the default reading, compiled without
+// them); true: they apply.
+template <bool OPT>
 __device__ __forceinline__ void topk_wave(const float *__restrict__ in, int P,
                                           const float *__restrict__ b, int N, int E, int k, int t,
                                           int32_t *__restrict__ ids, float *__restrict__ w,
@@ -93,13 +100,13 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ in, int P,
     for (int m = 0; m < kMaxPerLane; ++m) {
         const int e = lane + m * kWave;
         float key = sv[m];
-        if (opt.sel && e < E) key = sv[m] + opt.sel[e];  // one float32 rounding
+        if (OPT && opt.sel && e < E) key = sv[m] + opt.sel[e];  // one float32 rounding
         hi[m] = e < E ? sortable(key) : 0u;
         if (e >= E) taken |= 1u << m;
     }
-    const bool cut = opt.top_p > 0.0f && opt.top_p < 1.0f;
+    const bool cut = OPT && opt.top_p > 0.0f && opt.top_p < 1.0f;
     // with any option, lane j writes slot j after the rounds
-    const bool post = cut || opt.norm || opt.scale != 1.0f;
+    const bool post = OPT && (cut || opt.norm || opt.scale != 1.0f);
     // chosen scores in rank order: their sum, and lane j's round-j score, id
     // and the sum of the scores ranked before it
     float wsum = 0.0f, wmine = 0.0f, wbefore = 0.0f;

@@ -218,6 +218,7 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(
 // kUnionThreads threads.
 constexpr int kTailTokens = kUnionThreads / kWave;  // 16
 
+template <bool OPT>
 __global__ __launch_bounds__(kUnionThreads) void route_tail_kernel(
     const float *__restrict__ in, int P, const float *__restrict__ b, int N, int E, int k,
     int32_t *__restrict__ ids, float *__restrict__ w, int32_t *__restrict__ union_ids,
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(kUnionThreads) void route_tail_kernel(
     for (int a = tid; a < A; a += blockDim.x) s_ids[a] = -1;
     __syncthreads();
     const int t = tid / kWave;
-    if (t < N) topk_wave(in, P, b, N, E, k, t, ids, w, s_ids, opt);
+    if (t < N) topk_wave<OPT>(in, P, b, N, E, k, t, ids, w, s_ids, opt);
     __syncthreads();
     if (A <= kWave) {  // one wave; the workgroup has one wave per token
         if (t == 0) union_wave(s_ids, A, E, union_ids, n_union, offsets, perm, counters, cnt);
@@ -423,7 +424,8 @@ hipError_t launch_route_tail(const float *in, int P, const float *b, int N, int 
 {
     if (N < 1 || N > kTailTokens) return hipErrorInvalidValue;
     const int threads = N * k <= kWave ? N * kWave : kUnionThreads;
-    hipLaunchKernelGGL(route_tail_kernel, dim3(1), dim3(threads), 0, s, in, P, b, N, E, k,
+    hipLaunchKernelGGL(opt.any() ? route_tail_kernel<true> : route_tail_kernel<false>, dim3(1),
+                       dim3(threads), 0, s, in, P, b, N, E, k,
                        ids, w, union_ids, n_union, offsets, perm,
                        reinterpret_cast<unsigned long long *>(counters), opt);
     return hipGetLastError();
