@@ -63,7 +63,8 @@ typedef enum {
     MOE_ESHAPE = -2,          /* shape the kernels do not support (see below) */
     MOE_EALIGN = -3,          /* pointer or stride not aligned as required */
     MOE_EWORKSPACE = -4,      /* workspace missing or smaller than required */
-    MOE_EHIP = -5             /* a HIP runtime call or kernel launch failed */
+    MOE_EHIP = -5,            /* a HIP runtime call or kernel launch failed */
+    MOE_EIO = -6              /* a file could not be read or written, or is not a usage file */
 } moe_status;
 
 #define MOE_MAX_K 32          /* largest top-k */

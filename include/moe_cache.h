@@ -68,8 +68,64 @@ moe_status moe_cache_place(moe_cache *cache, const int32_t *union_ids, int n_uni
                            hipStream_t copy_stream, hipStream_t compute_stream,
                            int32_t *n_missed);
 
-/* Totals since creation: experts found resident, experts copied in. */
+/* Totals of moe_cache_place since creation: experts found resident, experts
+ * copied in (pins and prefetches are not counted). */
 moe_status moe_cache_stats(const moe_cache *cache, uint64_t *hits, uint64_t *misses);
+
+/*
+ * Pin: make the experts of ids (host, n of them, ids outside [0, n_experts)
+ * ignored) resident as moe_cache_place does, then keep them: no later Place
+ * or prefetch replaces a pinned slot. The call replaces the previous pin set
+ * (n = 0 unpins everything). A Place whose union needs more slots than the
+ * unpinned ones returns MOE_ESHAPE. The pages pin the experts their hit
+ * counters show hottest ("Cache/Prefetch Design Comparison"; Learn stage);
+ * moe_usage_hottest picks them.
+ * Errors: MOE_EINVAL, MOE_ESHAPE (more distinct ids than slots; nothing is
+ * changed), MOE_EHIP (the pin set is then empty). n_missed (host, may be
+ * NULL): experts copied in.
+ */
+moe_status moe_cache_pin(moe_cache *cache, const int32_t *ids, int n,
+                         hipStream_t copy_stream, hipStream_t compute_stream,
+                         int32_t *n_missed);
+
+/*
+ * Prefetch hint: start copying the experts of ids (host) that are not
+ * resident, in order, as far as the unpinned slots allow (the rest of the
+ * list is ignored), into least-recently-used slots, after the work already
+ * on compute_stream; unlike Place, compute_stream does not wait for these
+ * copies here: the next moe_cache_place on this cache makes it wait. The
+ * experts count as just used. For the next layer's experts predicted by a
+ * lookahead router while the current layer computes (the pages' prefetch of
+ * layer l+1 from layer l's hidden state). n_copied (host, may be NULL).
+ * Errors: MOE_EINVAL, MOE_EHIP.
+ */
+moe_status moe_cache_prefetch(moe_cache *cache, const int32_t *ids, int n,
+                              hipStream_t copy_stream, hipStream_t compute_stream,
+                              int32_t *n_copied);
+
+/* Host view of the cache: slot_of[n_experts] (slot or -1) and
+ * pinned[n_experts] (1 when the expert sits in a pinned slot); either may be
+ * NULL. */
+moe_status moe_cache_resident(const moe_cache *cache, int32_t *slot_of, int32_t *pinned);
+
+/*
+ * Learn across runs: the per-layer hit counters (moe_hit_count /
+ * moe_route_union output, uint64 [n_layers][n_experts], copied to the host)
+ * saved to and loaded from a small file, the counterpart of the pages' usage
+ * file that a run leaves for the next one ("Never wait for the disk twice").
+ * Format: the 8 bytes "MOEUSAGE", uint32 version 1, uint32 n_layers, uint32
+ * n_experts, then the counters, all little-endian.
+ * moe_usage_read: MOE_ESHAPE when the file holds other dimensions, MOE_EIO
+ * when it cannot be read or is not such a file (counters unchanged then).
+ * moe_usage_hottest: the n experts with the most hits (ties to the lower id),
+ * most hits first, from one layer's counters.
+ */
+moe_status moe_usage_write(const char *path /* (host) */, const uint64_t *counters /* (host) */,
+                           int n_layers, int n_experts);
+moe_status moe_usage_read(const char *path /* (host) */, uint64_t *counters /* (host) */,
+                          int n_layers, int n_experts);
+moe_status moe_usage_hottest(const uint64_t *counters /* (host) */, int n_experts, int n,
+                             int32_t *ids /* (host) */);
 
 #ifdef __cplusplus
 }

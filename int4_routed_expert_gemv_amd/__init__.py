@@ -22,7 +22,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4, -5
+MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP, MOE_EIO = (
+    0, -1, -2, -3, -4, -5, -6)
 MOE_MAX_K = 32
 MOE_MAX_EXPERTS = 1024
 MOE_ALIGN = 256
@@ -38,7 +39,9 @@ EXPORTED = [
 # measured-ceiling probes (include/moe_probe.h), not part of the layer step
 PROBE_EXPORTED = ["moe_probe_stream_read", "moe_probe_mfma_f16"]
 # the expert cache of the Place stage (include/moe_cache.h)
-CACHE_EXPORTED = ["moe_cache_create", "moe_cache_destroy", "moe_cache_place", "moe_cache_stats"]
+CACHE_EXPORTED = ["moe_cache_create", "moe_cache_destroy", "moe_cache_place", "moe_cache_stats",
+                  "moe_cache_pin", "moe_cache_prefetch", "moe_cache_resident", "moe_usage_write",
+                  "moe_usage_read", "moe_usage_hottest"]
 
 
 class MoeError(RuntimeError):
@@ -122,6 +125,17 @@ def lib():
         L.moe_cache_place.restype = i32
         L.moe_cache_stats.argtypes = [vp, vp, vp]
         L.moe_cache_stats.restype = i32
+        for name in ("moe_cache_pin", "moe_cache_prefetch"):
+            getattr(L, name).argtypes = [vp, vp, i32, vp, vp, vp]
+            getattr(L, name).restype = i32
+        L.moe_cache_resident.argtypes = [vp, vp, vp]
+        L.moe_cache_resident.restype = i32
+        L.moe_usage_write.argtypes = [ctypes.c_char_p, vp, i32, i32]
+        L.moe_usage_write.restype = i32
+        L.moe_usage_read.argtypes = [ctypes.c_char_p, vp, i32, i32]
+        L.moe_usage_read.restype = i32
+        L.moe_usage_hottest.argtypes = [vp, i32, i32, vp]
+        L.moe_usage_hottest.restype = i32
         L.moe_strerror.argtypes = [i32]
         L.moe_strerror.restype = ctypes.c_char_p
         for name in ("moe_route_topk", "moe_route_topk_ex", "moe_union", "moe_route_union",
@@ -371,6 +385,34 @@ class ExpertCache:
                                      ctypes.byref(missed)), "moe_cache_place")
         return int(missed.value)
 
+    def pin(self, ids_host, copy_stream=None, compute_stream=None) -> int:
+        """Pin these experts (replacing the previous pin set); returns the
+        number copied in."""
+        ids = np.ascontiguousarray(ids_host, np.int32)
+        missed = ctypes.c_int32(0)
+        _check(lib().moe_cache_pin(self.handle, ids.ctypes.data if ids.size else None, ids.size,
+                                   _stream(copy_stream), _stream(compute_stream),
+                                   ctypes.byref(missed)), "moe_cache_pin")
+        return int(missed.value)
+
+    def prefetch(self, ids_host, copy_stream=None, compute_stream=None) -> int:
+        """Start copying these experts in (a hint; the next place waits for
+        the copies); returns the number of copies started."""
+        ids = np.ascontiguousarray(ids_host, np.int32)
+        n = ctypes.c_int32(0)
+        _check(lib().moe_cache_prefetch(self.handle, ids.ctypes.data if ids.size else None,
+                                        ids.size, _stream(copy_stream), _stream(compute_stream),
+                                        ctypes.byref(n)), "moe_cache_prefetch")
+        return int(n.value)
+
+    def resident(self):
+        """(slot_of[E], pinned[E]) on the host."""
+        E = self.table.numel()
+        so, pn = np.empty(E, np.int32), np.empty(E, np.int32)
+        _check(lib().moe_cache_resident(self.handle, so.ctypes.data, pn.ctypes.data),
+               "moe_cache_resident")
+        return so, pn.astype(bool)
+
     def stats(self):
         h, m = ctypes.c_uint64(0), ctypes.c_uint64(0)
         _check(lib().moe_cache_stats(self.handle, ctypes.byref(h), ctypes.byref(m)), "moe_cache_stats")
@@ -386,3 +428,29 @@ class ExpertCache:
             self.close()
         except Exception:
             pass
+
+
+def usage_write(path, counters):
+    """Save per-layer hit counters (uint64/int64 numpy [n_layers][n_experts])
+    to a usage file (moe_usage_write)."""
+    c = np.ascontiguousarray(np.atleast_2d(counters).astype(np.uint64))
+    _check(lib().moe_usage_write(os.fsencode(path), c.ctypes.data, c.shape[0], c.shape[1]),
+           "moe_usage_write")
+
+
+def usage_read(path, n_layers, n_experts):
+    """Load a usage file written by usage_write (moe_usage_read)."""
+    c = np.zeros((n_layers, n_experts), np.uint64)
+    _check(lib().moe_usage_read(os.fsencode(path), c.ctypes.data, n_layers, n_experts),
+           "moe_usage_read")
+    return c
+
+
+def usage_hottest(counters_row, n):
+    """The n experts with the most hits in one layer's counters, most first,
+    ties to the lower id (moe_usage_hottest)."""
+    c = np.ascontiguousarray(counters_row, np.uint64)
+    ids = np.empty(n, np.int32)
+    _check(lib().moe_usage_hottest(c.ctypes.data, c.size, n, ids.ctypes.data if n else None),
+           "moe_usage_hottest")
+    return ids

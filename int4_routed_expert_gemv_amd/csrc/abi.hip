@@ -216,6 +216,7 @@ const char *moe_strerror(moe_status st)
     case MOE_EALIGN: return "pointer or stride not aligned to MOE_ALIGN";
     case MOE_EWORKSPACE: return "workspace missing or too small";
     case MOE_EHIP: return "HIP runtime call or kernel launch failed";
+    case MOE_EIO: return "file not readable, not writable, or not a usage file";
     }
     return "unknown status";
 }

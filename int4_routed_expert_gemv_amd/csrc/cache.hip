@@ -1,10 +1,19 @@
 // cache.hip - Place stage: an HBM cache of expert block slots over a host
 // tier, per-layer least-recently-used replacement, block copies on a copy
-// stream (host code only).
+// stream, pinned experts, prefetch hints, and the persisted hit counters
+// (host code only).
 //
 // Colibri pages: "Public Colibri Observation and Revision Ledger", section
-// "Exact Architecture and Data-Flow Reconstruction" (stage (3) Place) and
-// section "Cache/Prefetch Design Comparison" (per-layer LRU of experts).
+// "Exact Architecture and Data-Flow Reconstruction" (stage (3) Place, stage
+// (5) Learn: hit counters that later runs use to pin the hottest experts) and
+// section "Cache/Prefetch Design Comparison" (per-layer LRU of experts,
+// pinning by measured heat, prefetch of the next layer's experts from a
+// lookahead router); README "Never wait for the disk twice" (the usage file
+// that a run writes and the next run reads).
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
 #include <vector>
 
 #include "internal.h"
@@ -19,6 +28,9 @@ struct moe_cache {
     std::vector<int> slot_of;         // expert -> slot, or -1
     std::vector<int> expert_in;       // slot -> expert, or -1
     std::vector<unsigned long long> last_use;  // slot -> tick of its last use (0: never)
+    std::vector<char> pinned;         // slot -> never replaced
+    int n_pinned = 0;
+    bool unwaited = false;            // copies (prefetch) the compute stream has not waited for
     std::vector<int> mark;            // scratch: expert seen in this call
     std::vector<char> used;           // scratch: slot held by this call's union
     unsigned long long tick = 0;
@@ -45,6 +57,112 @@ void release(moe_cache *c)
     if (c->staging) (void)hipHostFree(c->staging);
     delete c;
 }
+
+// Distinct valid ids of a call (ids outside [0, E) ignored); how many of
+// them are not resident in a pinned slot.
+void count_distinct(moe_cache *c, const int32_t *ids, int n, int *distinct, int *unpinned)
+{
+    *distinct = *unpinned = 0;
+    for (int i = 0; i < n; ++i) {
+        const int e = ids[i];
+        if (e >= 0 && e < c->E && !c->mark[e]) {
+            c->mark[e] = 1;
+            ++*distinct;
+            const int s = c->slot_of[e];
+            if (s < 0 || !c->pinned[s]) ++*unpinned;
+        }
+    }
+    for (int i = 0; i < n; ++i) {
+        const int e = ids[i];
+        if (e >= 0 && e < c->E) c->mark[e] = 0;
+    }
+}
+
+// Make ids[0..n) resident (the caller has checked that they fit): hits are
+// refreshed first, then each missing expert takes the least recently used
+// slot that is neither pinned nor held by this call, its block copied on
+// copy_stream after the work already on compute_stream. The new slot table
+// follows on copy_stream. wait: compute_stream waits for every copy so far
+// (Place); otherwise the copies are left for the next Place to wait for
+// (prefetch). count: add the hits and copies to the cache's totals (Place
+// only). Returns MOE_OK or MOE_EHIP; *missed = experts copied.
+moe_status place_ids(moe_cache *c, const int32_t *ids, int n, hipStream_t copy_stream,
+                     hipStream_t compute_stream, bool wait, bool count, int *missed_out)
+{
+    ++c->tick;
+    std::fill(c->used.begin(), c->used.end(), 0);
+    // hits first: they keep their slots, which no miss may then take
+    for (int i = 0; i < n; ++i) {
+        const int e = ids[i];
+        if (e < 0 || e >= c->E) continue;
+        const int s = c->slot_of[e];
+        if (s >= 0 && !c->used[s]) {
+            c->used[s] = 1;
+            c->last_use[s] = c->tick;
+            if (count) ++c->hits;
+        }
+    }
+    int missed = 0;
+    bool waited = false;
+    for (int i = 0; i < n; ++i) {
+        const int e = ids[i];
+        if (e < 0 || e >= c->E || c->slot_of[e] >= 0) continue;  // out of range, or resident
+        // the least recently used slot this call does not hold and no pin
+        // keeps (free slots first, lowest index among equals)
+        int victim = -1;
+        for (int s = 0; s < c->C; ++s)
+            if (!c->used[s] && !c->pinned[s] &&
+                (victim < 0 || c->last_use[s] < c->last_use[victim]))
+                victim = s;
+        if (victim < 0) return MOE_EHIP;  // cannot happen: the caller checked the room
+        if (!waited) {
+            // a replaced block may still be read by work already on the
+            // compute stream: the copies start after it
+            if (hipEventRecord(c->computed, compute_stream) != hipSuccess ||
+                hipStreamWaitEvent(copy_stream, c->computed, 0) != hipSuccess)
+                return MOE_EHIP;
+            waited = true;
+        }
+        const int old = c->expert_in[victim];
+        if (old >= 0) c->slot_of[old] = -1;
+        c->expert_in[victim] = e;
+        c->slot_of[e] = victim;
+        c->used[victim] = 1;
+        c->last_use[victim] = c->tick;
+        if (hipMemcpyAsync(c->slots + (size_t)victim * c->stride, c->host + (size_t)e * c->stride,
+                           c->bytes, hipMemcpyHostToDevice, copy_stream) != hipSuccess)
+            return MOE_EHIP;
+        ++missed;
+        if (count) ++c->misses;
+    }
+    *missed_out = missed;
+    if (!missed && !(wait && c->unwaited)) return MOE_OK;
+    // the new table (or, for a Place with no copies of its own, only the wait
+    // on earlier prefetch copies), through a staging buffer no copy in flight
+    // still reads
+    const int b = c->cur;
+    if (c->pending[b] && hipEventSynchronize(c->copied[b]) != hipSuccess) return MOE_EHIP;
+    if (missed) {
+        int32_t *st = c->staging + (size_t)b * c->E;
+        for (int e = 0; e < c->E; ++e) st[e] = c->slot_of[e];
+        if (hipMemcpyAsync(c->table_dev, st, sizeof(int32_t) * c->E, hipMemcpyHostToDevice,
+                           copy_stream) != hipSuccess)
+            return MOE_EHIP;
+    }
+    if (hipEventRecord(c->copied[b], copy_stream) != hipSuccess) return MOE_EHIP;
+    c->pending[b] = true;
+    c->cur = b ^ 1;
+    if (wait) {
+        if (hipStreamWaitEvent(compute_stream, c->copied[b], 0) != hipSuccess) return MOE_EHIP;
+        c->unwaited = false;
+    } else {
+        c->unwaited = true;
+    }
+    return MOE_OK;
+}
+
+const char kUsageMagic[8] = {'M', 'O', 'E', 'U', 'S', 'A', 'G', 'E'};
+constexpr uint32_t kUsageVersion = 1;
 
 }  // namespace
 
@@ -73,6 +191,7 @@ moe_status moe_cache_create(int n_experts, int n_slots, size_t block_bytes, size
     c->slot_of.assign(n_experts, -1);
     c->expert_in.assign(n_slots, -1);
     c->last_use.assign(n_slots, 0);
+    c->pinned.assign(n_slots, 0);
     c->mark.assign(n_experts, 0);
     c->used.assign(n_slots, 0);
     if (hipHostMalloc(reinterpret_cast<void **>(&c->staging), 2 * sizeof(int32_t) * n_experts,
@@ -100,78 +219,61 @@ moe_status moe_cache_place(moe_cache *c, const int32_t *union_ids, int n_union,
 {
     if (!c || n_union < 0 || (n_union > 0 && !union_ids)) return MOE_EINVAL;
     if (n_missed) *n_missed = 0;
-    // the distinct valid ids of this call; more than the slots: change nothing
-    int distinct = 0;
-    for (int i = 0; i < n_union; ++i) {
-        const int e = union_ids[i];
-        if (e >= 0 && e < c->E && !c->mark[e]) {
-            c->mark[e] = 1;
-            ++distinct;
-        }
-    }
-    for (int i = 0; i < n_union; ++i) {
-        const int e = union_ids[i];
-        if (e >= 0 && e < c->E) c->mark[e] = 0;
-    }
-    if (distinct > c->C) return MOE_ESHAPE;
+    // more distinct experts than the slots no pin keeps: change nothing
+    int distinct, unpinned;
+    count_distinct(c, union_ids, n_union, &distinct, &unpinned);
+    if (unpinned > c->C - c->n_pinned) return MOE_ESHAPE;
+    int missed = 0;
+    const moe_status st = place_ids(c, union_ids, n_union, copy_stream, compute_stream, true,
+                                    true, &missed);
+    if (n_missed) *n_missed = missed;
+    return st;
+}
 
-    ++c->tick;
-    std::fill(c->used.begin(), c->used.end(), 0);
-    // hits first: they keep their slots, which no miss may then take
-    for (int i = 0; i < n_union; ++i) {
-        const int e = union_ids[i];
+moe_status moe_cache_prefetch(moe_cache *c, const int32_t *ids, int n, hipStream_t copy_stream,
+                              hipStream_t compute_stream, int32_t *n_copied)
+{
+    if (!c || n < 0 || (n > 0 && !ids)) return MOE_EINVAL;
+    if (n_copied) *n_copied = 0;
+    // a hint: the first ids that fit in the slots no pin keeps
+    int take = 0, room = c->C - c->n_pinned;
+    for (int i = 0; i < n; ++i) {
+        int distinct, unpinned;
+        count_distinct(c, ids, i + 1, &distinct, &unpinned);
+        if (unpinned > room) break;
+        take = i + 1;
+    }
+    int copied = 0;
+    const moe_status st = place_ids(c, ids, take, copy_stream, compute_stream, false, false,
+                                    &copied);
+    if (n_copied) *n_copied = copied;
+    return st;
+}
+
+moe_status moe_cache_pin(moe_cache *c, const int32_t *ids, int n, hipStream_t copy_stream,
+                         hipStream_t compute_stream, int32_t *n_missed)
+{
+    if (!c || n < 0 || (n > 0 && !ids)) return MOE_EINVAL;
+    if (n_missed) *n_missed = 0;
+    int distinct, unpinned;
+    count_distinct(c, ids, n, &distinct, &unpinned);
+    if (distinct > c->C) return MOE_ESHAPE;
+    // the new pin set replaces the old one: unpin, place, then pin its slots
+    std::fill(c->pinned.begin(), c->pinned.end(), 0);
+    c->n_pinned = 0;
+    int missed = 0;
+    const moe_status st = place_ids(c, ids, n, copy_stream, compute_stream, true, false, &missed);
+    if (st != MOE_OK) return st;
+    for (int i = 0; i < n; ++i) {
+        const int e = ids[i];
         if (e < 0 || e >= c->E) continue;
         const int s = c->slot_of[e];
-        if (s >= 0 && !c->used[s]) {
-            c->used[s] = 1;
-            c->last_use[s] = c->tick;
-            ++c->hits;
+        if (s >= 0 && !c->pinned[s]) {
+            c->pinned[s] = 1;
+            ++c->n_pinned;
         }
-    }
-    int missed = 0;
-    bool waited = false;
-    for (int i = 0; i < n_union; ++i) {
-        const int e = union_ids[i];
-        if (e < 0 || e >= c->E || c->slot_of[e] >= 0) continue;  // out of range, or resident
-        // the least recently used slot this union does not hold (free slots first)
-        int victim = -1;
-        for (int s = 0; s < c->C; ++s)
-            if (!c->used[s] && (victim < 0 || c->last_use[s] < c->last_use[victim])) victim = s;
-        if (victim < 0) return MOE_EHIP;  // cannot happen: distinct <= C
-        if (!waited) {
-            // a replaced block may still be read by work already on the
-            // compute stream: the copies start after it
-            if (hipEventRecord(c->computed, compute_stream) != hipSuccess ||
-                hipStreamWaitEvent(copy_stream, c->computed, 0) != hipSuccess)
-                return MOE_EHIP;
-            waited = true;
-        }
-        const int old = c->expert_in[victim];
-        if (old >= 0) c->slot_of[old] = -1;
-        c->expert_in[victim] = e;
-        c->slot_of[e] = victim;
-        c->used[victim] = 1;
-        c->last_use[victim] = c->tick;
-        if (hipMemcpyAsync(c->slots + (size_t)victim * c->stride, c->host + (size_t)e * c->stride,
-                           c->bytes, hipMemcpyHostToDevice, copy_stream) != hipSuccess)
-            return MOE_EHIP;
-        ++missed;
-        ++c->misses;
     }
     if (n_missed) *n_missed = missed;
-    if (!missed) return MOE_OK;
-    // the new table, through a staging buffer no copy in flight still reads
-    const int b = c->cur;
-    if (c->pending[b] && hipEventSynchronize(c->copied[b]) != hipSuccess) return MOE_EHIP;
-    int32_t *st = c->staging + (size_t)b * c->E;
-    for (int e = 0; e < c->E; ++e) st[e] = c->slot_of[e];
-    if (hipMemcpyAsync(c->table_dev, st, sizeof(int32_t) * c->E, hipMemcpyHostToDevice,
-                       copy_stream) != hipSuccess ||
-        hipEventRecord(c->copied[b], copy_stream) != hipSuccess)
-        return MOE_EHIP;
-    c->pending[b] = true;
-    c->cur = b ^ 1;
-    if (hipStreamWaitEvent(compute_stream, c->copied[b], 0) != hipSuccess) return MOE_EHIP;
     return MOE_OK;
 }
 
@@ -181,6 +283,72 @@ moe_status moe_cache_stats(const moe_cache *c, uint64_t *hits, uint64_t *misses)
     if (hits) *hits = c->hits;
     if (misses) *misses = c->misses;
     return MOE_OK;
+}
+
+moe_status moe_cache_resident(const moe_cache *c, int32_t *slot_of, int32_t *pinned)
+{
+    if (!c) return MOE_EINVAL;
+    for (int e = 0; e < c->E; ++e) {
+        const int s = c->slot_of[e];
+        if (slot_of) slot_of[e] = s;
+        if (pinned) pinned[e] = (s >= 0 && c->pinned[s]) ? 1 : 0;
+    }
+    return MOE_OK;
+}
+
+moe_status moe_usage_hottest(const uint64_t *counters, int n_experts, int n, int32_t *ids)
+{
+    if (!counters || n_experts < 1 || n < 0 || n > n_experts || (n > 0 && !ids))
+        return MOE_EINVAL;
+    std::vector<int32_t> order(n_experts);
+    for (int e = 0; e < n_experts; ++e) order[e] = e;
+    // most hits first, the lower id among equal counts
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t a, int32_t b) { return counters[a] > counters[b]; });
+    for (int i = 0; i < n; ++i) ids[i] = order[i];
+    return MOE_OK;
+}
+
+moe_status moe_usage_write(const char *path, const uint64_t *counters, int n_layers,
+                           int n_experts)
+{
+    if (!path || !counters || n_layers < 1 || n_experts < 1 || n_experts > MOE_MAX_EXPERTS)
+        return MOE_EINVAL;
+    FILE *fp = fopen(path, "wb");
+    if (!fp) return MOE_EIO;
+    const uint32_t head[3] = {kUsageVersion, (uint32_t)n_layers, (uint32_t)n_experts};
+    const size_t n = (size_t)n_layers * n_experts;
+    bool ok = fwrite(kUsageMagic, 1, 8, fp) == 8 && fwrite(head, 4, 3, fp) == 3 &&
+              fwrite(counters, 8, n, fp) == n;
+    ok = (fclose(fp) == 0) && ok;
+    return ok ? MOE_OK : MOE_EIO;
+}
+
+moe_status moe_usage_read(const char *path, uint64_t *counters, int n_layers, int n_experts)
+{
+    if (!path || !counters || n_layers < 1 || n_experts < 1 || n_experts > MOE_MAX_EXPERTS)
+        return MOE_EINVAL;
+    FILE *fp = fopen(path, "rb");
+    if (!fp) return MOE_EIO;
+    char magic[8];
+    uint32_t head[3];
+    const size_t n = (size_t)n_layers * n_experts;
+    moe_status st = MOE_OK;
+    if (fread(magic, 1, 8, fp) != 8 || memcmp(magic, kUsageMagic, 8) != 0 ||
+        fread(head, 4, 3, fp) != 3 || head[0] != kUsageVersion)
+        st = MOE_EIO;
+    else if (head[1] != (uint32_t)n_layers || head[2] != (uint32_t)n_experts)
+        st = MOE_ESHAPE;
+    else {
+        std::vector<uint64_t> tmp(n);
+        char extra;
+        if (fread(tmp.data(), 8, n, fp) != n || fread(&extra, 1, 1, fp) != 0)
+            st = MOE_EIO;
+        else
+            memcpy(counters, tmp.data(), 8 * n);
+    }
+    fclose(fp);
+    return st;
 }
 
 }  // extern "C"

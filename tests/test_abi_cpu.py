@@ -276,3 +276,57 @@ def test_cache_argument_checks():
     assert L.moe_cache_place(None, FAKE, 1, None, None, None) == moe.MOE_EINVAL
     assert L.moe_cache_stats(None, None, None) == moe.MOE_EINVAL
     del big
+
+
+# ---------------------------------------------------------------- usage file and hottest experts
+
+def test_usage_file_round_trip_and_errors(tmp_path):
+    """moe_usage_write / moe_usage_read: the counters come back exactly;
+    other dimensions, a foreign or damaged file and a missing one are
+    errors that leave the output untouched."""
+    rng = np.random.default_rng(1)
+    c = rng.integers(0, 1 << 40, size=(9, 256)).astype(np.uint64)
+    c[0, 0] = np.uint64((1 << 64) - 1)
+    path = str(tmp_path / "layers.usage")
+    moe.usage_write(path, c)
+    np.testing.assert_array_equal(moe.usage_read(path, 9, 256), c)
+    assert os.path.getsize(path) == 8 + 12 + 9 * 256 * 8
+    with pytest.raises(moe.MoeError) as e:
+        moe.usage_read(path, 8, 256)
+    assert e.value.status == moe.MOE_ESHAPE
+    raw = open(path, "rb").read()
+    for bad in (b"NOTUSAGE" + raw[8:], raw[:-1], raw + b"\0", raw[:10]):
+        (tmp_path / "bad").write_bytes(bad)
+        with pytest.raises(moe.MoeError) as e:
+            moe.usage_read(str(tmp_path / "bad"), 9, 256)
+        assert e.value.status == moe.MOE_EIO
+    with pytest.raises(moe.MoeError) as e:
+        moe.usage_read(str(tmp_path / "missing"), 9, 256)
+    assert e.value.status == moe.MOE_EIO
+    L = moe.lib()
+    out = np.full((9, 256), 7, np.uint64)
+    assert L.moe_usage_read(os.fsencode(str(tmp_path / "bad")), out.ctypes.data, 9, 256) == moe.MOE_EIO
+    assert np.all(out == 7)
+    assert L.moe_usage_write(None, c.ctypes.data, 9, 256) == moe.MOE_EINVAL
+    assert L.moe_usage_write(os.fsencode(path), c.ctypes.data, 0, 256) == moe.MOE_EINVAL
+
+
+def test_usage_hottest_ranks_by_hits_then_id():
+    rng = np.random.default_rng(2)
+    c = rng.integers(0, 6, size=300).astype(np.uint64)   # many equal counts
+    for n in (0, 1, 17, 300):
+        got = moe.usage_hottest(c, n)
+        ref = sorted(range(300), key=lambda e: (-int(c[e]), e))[:n]
+        assert got.tolist() == ref
+    L = moe.lib()
+    ids = np.empty(4, np.int32)
+    assert L.moe_usage_hottest(c.ctypes.data, 300, 301, ids.ctypes.data) == moe.MOE_EINVAL
+    assert L.moe_usage_hottest(None, 300, 4, ids.ctypes.data) == moe.MOE_EINVAL
+
+
+def test_cache_calls_reject_a_null_cache():
+    L = moe.lib()
+    ids = np.zeros(4, np.int32)
+    for name in ("moe_cache_pin", "moe_cache_prefetch"):
+        assert getattr(L, name)(None, ids.ctypes.data, 4, None, None, None) == moe.MOE_EINVAL
+    assert L.moe_cache_resident(None, None, None) == moe.MOE_EINVAL
