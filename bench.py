@@ -54,6 +54,12 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run one plain device copy of 1 GiB (to scale HBM counters)")
+    p.add_argument("--cache-stack", type=int, default=None, metavar="SLOTS",
+                   help="decode through the int4 layers of the stack workload, each layer's "
+                        "experts in pinned host memory with an HBM cache of SLOTS slots; "
+                        "compares LRU, LRU + learned pins, LRU + lookahead prefetch, and both")
+    p.add_argument("--stack-tokens", type=int, default=1, help="tokens per step for --cache-stack")
+    p.add_argument("--pin", type=int, default=32, help="experts pinned per layer (--cache-stack)")
     p.add_argument("--cache-slots", default=None,
                    help="comma-separated HBM slot counts: measure the Place stage (experts in "
                         "pinned host memory, an HBM cache of that many slots per layer) instead")
@@ -146,6 +152,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.cache_slots:
         cache_bench(args)
+        return
+    if args.cache_stack:
+        cache_stack_bench(args)
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -526,6 +535,153 @@ def cache_bench(args):
                       "config": {"workload": f"{cfg.name}: {base.description}; {L_rot} layers, "
                                              f"one cache per layer", "n_tokens": N, "k": k,
                                  "n_experts": E, "block_bytes": block},
+                      "points": points}), flush=True)
+
+
+def cache_stack_bench(args):
+    """Place with the pages' two placement aids, on a decode stack: the int4
+    layers of the stack workload (--layers of them) chained through the
+    residual RMS norm, every layer's experts in pinned host memory with an
+    HBM cache of SLOTS slots (moe_cache_*). Four policies, each on fresh
+    caches over the same token stream:
+      lru        Place only (least recently used replacement);
+      pin        + the --pin hottest experts of each layer pinned, chosen from
+                 the hit counters of a learning pass (moe_usage_hottest);
+      lookahead  + while layer l computes, layer l+1's router runs on layer
+                 l's normalised hidden state and its predicted union is
+                 prefetched (moe_cache_prefetch), the copies overlapping
+                 layer l's expert math;
+      both       pins and lookahead.
+    Reported per policy: tokens/s, the Place hit rate, bytes copied per token
+    (prefetches included) and the lookahead's accuracy (the share of each
+    layer's union that was predicted)."""
+    import numpy as np
+    import torch
+
+    import int4_routed_expert_gemv_amd as moe
+    import synth
+
+    dev = torch.device("cuda:0")
+    base = synth.CONFIGS["stack8_draft"]
+    int4 = [ls for ls in base.layers if ls.wbits == 4]
+    L = max(2, min(args.layers, len(int4)))
+    N = args.stack_tokens
+    cfg = dataclasses.replace(base, layers=tuple(int4[:L]), n_tokens=N)
+    k, C = cfg.k, args.cache_stack
+    n_pin = min(args.pin, C - N * k)   # a union's unpinned experts always find slots
+    if n_pin < 0:
+        sys.exit(f"--cache-stack needs at least {N * k} slots for {N} token(s) of top-{k}")
+    spec = cfg.layers[0]
+    E, d, f = spec.n_experts, spec.d, spec.f
+    layers = []
+    for l in range(L):
+        ls = cfg.layers[l]
+        pool = moe.DevicePool(d, f, E, ls.wbits, ls.group, synth.expert_pool(cfg, l),
+                              synth.shared_block(cfg, l), dev)
+        host = torch.empty((E, pool.stride), dtype=torch.uint8, pin_memory=True)
+        host.copy_(pool.pool.view(E, pool.stride))
+        shared, desc = pool.shared, pool.desc
+        del pool
+        wr, b = synth.router(cfg, l)
+        layers.append(dict(host=host, shared=shared, desc=desc, wr=torch.from_numpy(wr).to(dev),
+                           b=torch.from_numpy(b).to(dev)))
+        torch.cuda.empty_cache()
+        print(f"[cache stack] layer {l + 1}/{L} in pinned host memory", file=sys.stderr, flush=True)
+    nb = args.warmup + args.steps
+    xs = torch.from_numpy(synth.tokens(dataclasses.replace(cfg, n_tokens=N * nb))
+                          .reshape(nb, N, d)).to(dev)
+    ids = torch.empty((N, k), dtype=torch.int32, device=dev)
+    w = torch.empty((N, k), dtype=torch.float32, device=dev)
+    pid = torch.empty((N, k), dtype=torch.int32, device=dev)
+    pw = torch.empty((N, k), dtype=torch.float32, device=dev)
+    uid = torch.empty(E, dtype=torch.int32, device=dev)
+    nu = torch.empty(1, dtype=torch.int32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(N * k, dtype=torch.int32, device=dev)
+    y = torch.empty((N, d), dtype=torch.float32, device=dev)
+    h = torch.empty((N, d), dtype=torch.float32, device=dev)
+    a = torch.empty((N, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(moe.workspace_size(ly["desc"], N, k) for ly in layers), dtype=torch.uint8,
+                     device=dev)
+    copy_stream = torch.cuda.Stream()  # default priority
+    block = moe.block_bytes(d, f, spec.wbits, spec.group)
+    Lb = moe.lib()
+
+    def rmsnorm(first):
+        rc = Lb.moe_residual_rmsnorm(h.data_ptr(), None if first else y.data_ptr(), a.data_ptr(),
+                                     N, d, ctypes.c_float(1e-6), None)
+        if rc:
+            raise RuntimeError(f"moe_residual_rmsnorm failed with status {rc}")
+
+    def token_step(s_, caches, cnt, lookahead, acc):
+        h.copy_(xs[s_])
+        copies = 0
+        for l in range(L):
+            ly, cache = layers[l], caches[l]
+            rmsnorm(l == 0)
+            moe.route_union(a, ly["wr"], ly["b"], k, ids, w, uid, nu, off, perm, cnt[l], ws)
+            union = uid[:int(nu.item())].cpu().numpy()
+            if acc is not None and l > 0 and acc["pred"] is not None:
+                acc["hit"] += len(set(union.tolist()) & acc["pred"])
+                acc["total"] += len(union)
+            copies += cache.place(union, copy_stream=copy_stream)
+            if lookahead and l + 1 < L:
+                nxt = layers[l + 1]
+                moe.route_topk(a, nxt["wr"], nxt["b"], k, pid, pw, ws)
+                pred = np.unique(pid.cpu().numpy())
+                if acc is not None:
+                    acc["pred"] = set(pred.tolist())
+                copies += caches[l + 1].prefetch(pred, copy_stream=copy_stream)
+            moe.expert_forward(cache.desc, a, k, w, uid, nu, off, perm, y, ws)
+        return copies
+
+    learn_steps = max(1, args.warmup)
+    points = []
+    for policy in ("lru", "pin", "lookahead", "both"):
+        caches = [moe.ExpertCache(ly["desc"], C, ly["host"], dev) for ly in layers]
+        cnt = torch.zeros((L, E), dtype=torch.int64, device=dev)
+        pinning = policy in ("pin", "both")
+        lookahead = policy in ("lookahead", "both")
+        for s_ in range(learn_steps):   # learning pass: fills the caches and the counters
+            token_step(s_, caches, cnt, lookahead, None)
+        torch.cuda.synchronize()
+        if pinning:
+            counters = cnt.cpu().numpy().astype(np.uint64)
+            for l in range(L):
+                caches[l].pin(moe.usage_hottest(counters[l], n_pin), copy_stream=copy_stream)
+        torch.cuda.synchronize()
+        st0 = [c.stats() for c in caches]
+        acc = dict(hit=0, total=0, pred=None)
+        copies = 0
+        t0 = time.perf_counter()
+        for s_ in range(args.steps):
+            acc["pred"] = None
+            copies += token_step(learn_steps + s_, caches, cnt, lookahead, acc)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        hits = sum(c.stats()[0] - s0[0] for c, s0 in zip(caches, st0))
+        misses = sum(c.stats()[1] - s0[1] for c, s0 in zip(caches, st0))
+        tok = N * args.steps
+        pt = {"policy": policy, "tokens_per_s": tok / el, "ms_per_token_step": el / args.steps * 1e3,
+              "place_hit_rate": hits / max(1, hits + misses),
+              "copied_bytes_per_token": copies * block / tok,
+              "lookahead_accuracy": (acc["hit"] / acc["total"]) if lookahead and acc["total"]
+              else None}
+        points.append(pt)
+        print(f"[cache stack] {pt}", file=sys.stderr, flush=True)
+        for c in caches:
+            c.close()
+        del caches
+    print(json.dumps({"metric": "decode tokens/s through a layer stack with experts placed from "
+                                "pinned host memory into per-layer HBM caches (Place, learned "
+                                "pinning, lookahead prefetch)",
+                      "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+                      "learning_steps": learn_steps, "data": "synthetic",
+                      "config": {"workload": f"{L} int4 layers of {cfg.name} chained, "
+                                             f"{N} token(s) per step, top-{k}, Zipf(1.1) router "
+                                             f"bias per layer", "slots_per_layer": C,
+                                 "pinned_per_layer": n_pin, "n_experts": E,
+                                 "block_bytes": block},
                       "points": points}), flush=True)
 
 
