@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=400)
     p.add_argument("--config", default="decode1")
+    p.add_argument("--tokens", type=int, default=None,
+                   help="tokens per step instead of the workload's (e.g. a speculative "
+                        "verify batch of 1 + drafts through the stack)")
     p.add_argument("--group", type=int, default=None,
                    help="scale group of the int4 layers instead of the workload's (e.g. 64)")
     p.add_argument("--layers", type=int, default=8, help="layer pools rotated over the steps")
@@ -163,6 +166,8 @@ def main():
         base = dataclasses.replace(base, layers=tuple(
             dataclasses.replace(ls, group=args.group) if ls.wbits == 4 else ls
             for ls in base.layers))
+    if args.tokens is not None:
+        base = dataclasses.replace(base, n_tokens=args.tokens)
     spec = base.layer
     stack = len(base.layers) > 1
     if stack:
@@ -264,11 +269,13 @@ def main():
     calib = {}
 
     MIN_BIG_ITEMS = 32  # fewer 128-token items than this join the 32-token pass
+    GEMV_BATCH = 2      # batches of at most this many tokens keep every expert on the GEMV
 
     def pass_of(T):
         T = np.asarray(T)
         big = (T >= MFMA_MIN) & mfma_ok
-        small = ~big & (T >= SMALL_MIN) & mfma_ok
+        # batches of up to GEMV_BATCH tokens stay on the GEMV (the library's default)
+        small = ~big & (T >= SMALL_MIN) & mfma_ok & (N > GEMV_BATCH)
         if big.any() and np.sum((T[big] + 127) // 128) < MIN_BIG_ITEMS:
             small, big = small | big, np.zeros_like(big)
         return np.where(big, 1, np.where(small, 2, 0))
@@ -402,8 +409,9 @@ def main():
         else:
             roof = {"bound": "hbm", "achieved": pz["achieved_GBps"], "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": pz["achieved_GBps"] / HBM_PEAK_GBS}
-        roof["traffic"] = measured_traffic(
-            args.config if args.group is None else f"{args.config}_g{args.group}", labels[top][1])
+        roof["traffic"] = (None if args.tokens is not None else measured_traffic(
+            args.config if args.group is None else f"{args.config}_g{args.group}",
+            labels[top][1]))
         roof["kernel"] = labels[top][0]
         roof["passes"] = passes
         roof["measured_ceiling"] = measured_ceiling(moe, hip, torch, roof["bound"],
@@ -425,7 +433,8 @@ def main():
         "config": {
             "workload": (f"{cfg.name}: {base.description}" +
                          ("" if stack else f"; {L_rot} layer pools rotated") +
-                         (f"; int4 scale groups of {args.group}" if args.group else "")),
+                         (f"; int4 scale groups of {args.group}" if args.group else "") +
+                         (f"; {N} tokens per step" if args.tokens is not None else "")),
             "n_tokens": N, "k": k, "d_model": d, "d_ff": f, "n_experts": E,
             "wbits": spec.wbits, "group": spec.group, "layers_per_step": L_rot if stack else 1,
             "layer_pools": L_rot, "mean_union": mean_union,

@@ -263,7 +263,9 @@ moe_status moe_expert_forward(const moe_expert_pool *pool /* (host) */,
  *   T >= mfma_min_tokens: grouped GEMM on the matrix cores, 128-token tiles;
  *     0 selects the default (32), a negative value turns this pass off;
  *   mfma_small_min_tokens <= T < mfma_min_tokens: the same kernels with
- *     32-token tiles; 0 selects the default (2), negative turns it off;
+ *     32-token tiles; 0 selects the default (2, and off for batches of up to
+ *     2 tokens, which the GEMV takes in one item per expert), negative turns
+ *     it off;
  *   otherwise: the streaming GEMV kernels.
  * When both matrix-core passes are on and the 128-token pass would get fewer
  * than 32 items, those experts join the 32-token pass (a few large items

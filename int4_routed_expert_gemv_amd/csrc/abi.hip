@@ -28,6 +28,11 @@ long long n_scales(long long rows, long long cols, int group)
     return group ? rows * (cols / group) : rows;
 }
 
+// Batches of at most this many tokens keep every expert on the GEMV by default
+// (measured through the stack workload: 2 tokens 1.49 -> 1.03 ms per step on
+// the GEMV; 4 tokens 1.70 ms on the 32-token pass against 1.82 on the GEMV)
+constexpr int kGemvBatchTokens = 2;
+
 // Defaults: experts with at least this many tokens use the 128-token MFMA
 // pass; experts with at least kDefaultSmallMinTokens (and fewer than the
 // former) use the 32-token MFMA pass; single-token experts stay on the GEMV.
@@ -64,7 +69,11 @@ FwdLayout fwd_layout(const Geo &g, int N, int k, int has_shared, int mfma_min_to
                                (has_shared && N >= L.tstar ? ceil_div(N, kMfmaBigTokens) : 0);
         if (most < kMinBigItems) big = false;
     }
-    const bool small = mf && small_min_tokens >= 0 && N >= L.tsmall && !(big && L.tsmall >= L.tstar);
+    bool small = mf && small_min_tokens >= 0 && N >= L.tsmall && !(big && L.tsmall >= L.tstar);
+    // By default, the smallest batches stay on the GEMV: one item per expert
+    // reads its weights once, while the 32-token pass would give a handful of
+    // experts a handful of workgroups each, behind extra launches
+    if (small && small_min_tokens == 0 && !big && N <= kGemvBatchTokens) small = false;
     // most tokens of an expert on the GEMV pass
     long long cap = N;
     if (small) cap = L.tsmall - 1;

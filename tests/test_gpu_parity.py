@@ -379,3 +379,13 @@ def test_group64_scales_every_pass():
         say(f"[gs64] big={big} small={small} max rel err {err:.2e}")
     del pool
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("N", [2, 3])
+def test_small_verify_batches(N):
+    """Two and three tokens of top-8 on the decode layer's shapes (a
+    speculative verify batch): two tokens stay on the GEMV by default (items
+    of two tokens), three take the 32-token pass for experts hit twice."""
+    cfg = dataclasses.replace(synth.CONFIGS["decode64"], n_tokens=N)
+    full_parity(cfg)
+    full_parity(cfg, fused_route=True)
