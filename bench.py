@@ -49,6 +49,7 @@ def parse():
     p.add_argument("--tokens", type=int, default=None,
                    help="tokens per step instead of the workload's (e.g. a speculative "
                         "verify batch of 1 + drafts through the stack)")
+    p.add_argument("--k", type=int, default=None, help="experts per token instead of the workload's")
     p.add_argument("--group", type=int, default=None,
                    help="scale group of the int4 layers instead of the workload's (e.g. 64)")
     p.add_argument("--layers", type=int, default=8, help="layer pools rotated over the steps")
@@ -168,6 +169,8 @@ def main():
             for ls in base.layers))
     if args.tokens is not None:
         base = dataclasses.replace(base, n_tokens=args.tokens)
+    if args.k is not None:
+        base = dataclasses.replace(base, k=args.k)
     spec = base.layer
     stack = len(base.layers) > 1
     if stack:
@@ -409,7 +412,7 @@ def main():
         else:
             roof = {"bound": "hbm", "achieved": pz["achieved_GBps"], "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": pz["achieved_GBps"] / HBM_PEAK_GBS}
-        roof["traffic"] = (None if args.tokens is not None else measured_traffic(
+        roof["traffic"] = (None if args.tokens is not None or args.k is not None else measured_traffic(
             args.config if args.group is None else f"{args.config}_g{args.group}",
             labels[top][1]))
         roof["kernel"] = labels[top][0]
@@ -434,7 +437,8 @@ def main():
             "workload": (f"{cfg.name}: {base.description}" +
                          ("" if stack else f"; {L_rot} layer pools rotated") +
                          (f"; int4 scale groups of {args.group}" if args.group else "") +
-                         (f"; {N} tokens per step" if args.tokens is not None else "")),
+                         (f"; {N} tokens per step" if args.tokens is not None else "") +
+                         (f"; top-{k}" if args.k is not None else "")),
             "n_tokens": N, "k": k, "d_model": d, "d_ff": f, "n_experts": E,
             "wbits": spec.wbits, "group": spec.group, "layers_per_step": L_rot if stack else 1,
             "layer_pools": L_rot, "mean_union": mean_union,
