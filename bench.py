@@ -64,6 +64,8 @@ def parse():
                         "compares LRU, LRU + learned pins, LRU + lookahead prefetch, and both")
     p.add_argument("--stack-tokens", type=int, default=1, help="tokens per step for --cache-stack")
     p.add_argument("--pin", type=int, default=32, help="experts pinned per layer (--cache-stack)")
+    p.add_argument("--lookahead-top", type=int, default=None,
+                   help="--cache-stack: prefetch only each token's first M predicted experts")
     p.add_argument("--cache-slots", default=None,
                    help="comma-separated HBM slot counts: measure the Place stage (experts in "
                         "pinned host memory, an HBM cache of that many slots per layer) instead")
@@ -561,9 +563,10 @@ def cache_stack_bench(args):
       pin        + the --pin hottest experts of each layer pinned, chosen from
                  the hit counters of a learning pass (moe_usage_hottest);
       lookahead  + while layer l computes, layer l+1's router runs on layer
-                 l's normalised hidden state and its predicted union is
-                 prefetched (moe_cache_prefetch), the copies overlapping
-                 layer l's expert math;
+                 l's normalised hidden state and its predicted union (each
+                 token's first --lookahead-top ranked experts, all k by
+                 default) is prefetched (moe_cache_prefetch), the copies
+                 overlapping layer l's expert math;
       both       pins and lookahead.
     Reported per policy: tokens/s, the Place hit rate, bytes copied per token
     (prefetches included) and the lookahead's accuracy (the share of each
@@ -641,7 +644,8 @@ def cache_stack_bench(args):
             if lookahead and l + 1 < L:
                 nxt = layers[l + 1]
                 moe.route_topk(a, nxt["wr"], nxt["b"], k, pid, pw, ws)
-                pred = np.unique(pid.cpu().numpy())
+                pred_ids = pid.cpu().numpy()
+                pred = np.unique(pred_ids[:, :top] if top else pred_ids)
                 if acc is not None:
                     acc["pred"] = set(pred.tolist())
                 copies += caches[l + 1].prefetch(pred, copy_stream=copy_stream)
@@ -649,6 +653,7 @@ def cache_stack_bench(args):
         return copies
 
     learn_steps = max(1, args.warmup)
+    top = args.lookahead_top   # ranked predictions kept per token (None: all k)
     points = []
     for policy in ("lru", "pin", "lookahead", "both"):
         caches = [moe.ExpertCache(ly["desc"], C, ly["host"], dev) for ly in layers]
@@ -693,7 +698,8 @@ def cache_stack_bench(args):
                       "config": {"workload": f"{L} int4 layers of {cfg.name} chained, "
                                              f"{N} token(s) per step, top-{k}, Zipf(1.1) router "
                                              f"bias per layer", "slots_per_layer": C,
-                                 "pinned_per_layer": n_pin, "n_experts": E,
+                                 "pinned_per_layer": n_pin, "lookahead_top": top or k,
+                                 "n_experts": E,
                                  "block_bytes": block},
                       "points": points}), flush=True)
 
