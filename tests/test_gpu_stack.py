@@ -25,11 +25,13 @@ GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def progress(msg):
-    """Progress on stdout, and in a file so a long run is visibly alive."""
+    """Progress on stdout and, when MOE_TEST_PROGRESS names a file, appended
+    to it (a long run that captures stdout stays visibly alive)."""
     print(msg, flush=True)
-    os.makedirs("gpurun_out", exist_ok=True)
-    with open(os.path.join("gpurun_out", "progress_stack8.txt"), "a") as fh:
-        fh.write(f"{time.strftime('%H:%M:%S')} {msg}\n")
+    path = os.environ.get("MOE_TEST_PROGRESS")
+    if path:
+        with open(path, "a") as fh:
+            fh.write(f"{time.strftime('%H:%M:%S')} {msg}\n")
 
 
 @pytest.mark.timeout(1200)
