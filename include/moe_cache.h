@@ -118,7 +118,8 @@ moe_status moe_cache_resident(const moe_cache *cache, int32_t *slot_of, int32_t 
  * moe_usage_read: MOE_ESHAPE when the file holds other dimensions, MOE_EIO
  * when it cannot be read or is not such a file (counters unchanged then).
  * moe_usage_hottest: the n experts with the most hits (ties to the lower id),
- * most hits first, from one layer's counters.
+ * most hits first, from one layer's counters (n_experts up to
+ * MOE_MAX_EXPERTS).
  */
 moe_status moe_usage_write(const char *path /* (host) */, const uint64_t *counters /* (host) */,
                            int n_layers, int n_experts);

@@ -235,13 +235,24 @@ moe_status moe_cache_prefetch(moe_cache *c, const int32_t *ids, int n, hipStream
 {
     if (!c || n < 0 || (n > 0 && !ids)) return MOE_EINVAL;
     if (n_copied) *n_copied = 0;
-    // a hint: the first ids that fit in the slots no pin keeps
-    int take = 0, room = c->C - c->n_pinned;
+    // a hint: the longest prefix of ids whose distinct experts fit in the
+    // slots no pin keeps (one pass, marks cleared after)
+    const int room = c->C - c->n_pinned;
+    int take = 0, need = 0;
     for (int i = 0; i < n; ++i) {
-        int distinct, unpinned;
-        count_distinct(c, ids, i + 1, &distinct, &unpinned);
-        if (unpinned > room) break;
+        const int e = ids[i];
+        if (e >= 0 && e < c->E && !c->mark[e]) {
+            const int s = c->slot_of[e];
+            const bool kept = s >= 0 && c->pinned[s];
+            if (!kept && need + 1 > room) break;
+            c->mark[e] = 1;
+            if (!kept) ++need;
+        }
         take = i + 1;
+    }
+    for (int i = 0; i < take; ++i) {
+        const int e = ids[i];
+        if (e >= 0 && e < c->E) c->mark[e] = 0;
     }
     int copied = 0;
     const moe_status st = place_ids(c, ids, take, copy_stream, compute_stream, false, false,
@@ -298,7 +309,8 @@ moe_status moe_cache_resident(const moe_cache *c, int32_t *slot_of, int32_t *pin
 
 moe_status moe_usage_hottest(const uint64_t *counters, int n_experts, int n, int32_t *ids)
 {
-    if (!counters || n_experts < 1 || n < 0 || n > n_experts || (n > 0 && !ids))
+    if (!counters || n_experts < 1 || n_experts > MOE_MAX_EXPERTS || n < 0 || n > n_experts ||
+        (n > 0 && !ids))
         return MOE_EINVAL;
     std::vector<int32_t> order(n_experts);
     for (int e = 0; e < n_experts; ++e) order[e] = e;
@@ -340,12 +352,21 @@ moe_status moe_usage_read(const char *path, uint64_t *counters, int n_layers, in
     else if (head[1] != (uint32_t)n_layers || head[2] != (uint32_t)n_experts)
         st = MOE_ESHAPE;
     else {
-        std::vector<uint64_t> tmp(n);
-        char extra;
-        if (fread(tmp.data(), 8, n, fp) != n || fread(&extra, 1, 1, fp) != 0)
+        // read into a copy, so that a short or overlong file leaves counters
+        // as they were (no exception crosses the C interface)
+        std::vector<uint64_t> tmp;
+        try {
+            tmp.resize(n);
+        } catch (...) {
             st = MOE_EIO;
-        else
-            memcpy(counters, tmp.data(), 8 * n);
+        }
+        char extra;
+        if (st == MOE_OK) {
+            if (fread(tmp.data(), 8, n, fp) != n || fread(&extra, 1, 1, fp) != 0)
+                st = MOE_EIO;
+            else
+                memcpy(counters, tmp.data(), 8 * n);
+        }
     }
     fclose(fp);
     return st;

@@ -389,3 +389,18 @@ def test_small_verify_batches(N):
     cfg = dataclasses.replace(synth.CONFIGS["decode64"], n_tokens=N)
     full_parity(cfg)
     full_parity(cfg, fused_route=True)
+
+
+def test_decode1_direct_combine_is_deterministic():
+    """One token, top-1 with the shared expert: the down kernel adds the two
+    gate-weighted rows into y with float atomics (two addends onto zero, the
+    same sum in either order), so repeated runs give the same bits."""
+    cfg = synth.CONFIGS["decode1"]
+    spec, x, wr, b, blocks, shared, _ = oracle_then_pool(cfg)
+    pool = upload_pool(spec, blocks, shared)
+    first = run_layer(pool, x, wr, b, cfg.k, fused_route=True)
+    for _ in range(5):
+        again = run_layer(pool, x, wr, b, cfg.k, fused_route=True)
+        np.testing.assert_array_equal(again["y"], first["y"])
+    del pool
+    torch.cuda.empty_cache()
