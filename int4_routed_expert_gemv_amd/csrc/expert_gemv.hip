@@ -15,15 +15,18 @@
 //    one chunk per lane, so every 128-bit load instruction of a wave covers
 //    1 KB of contiguous row; rows longer than 64 chunks are split across the
 //    waves of the workgroup, shorter rows share a wave;
-//  * codes are turned into float16 in registers by OR-ing them into the
-//    mantissa of 1024.0 (offset-binary codes, so the value is 1024 + q + 8
-//    exactly) and multiplied with float16 activations by v_dot2_f32_f16,
-//    which accumulates in float32; 1032 (or 1152) times the activation sum
-//    is taken off once per chunk;
 //  * a work item's activations are staged once per workgroup in LDS, each
-//    chunk as float16 scaled by the power of two that brings the chunk's
-//    largest magnitude into [2^13, 2^14) (an exact scaling, undone on the
-//    chunk's partial sum together with the group scale);
+//    chunk scaled by the power of two that brings its largest magnitude into
+//    [2^13, 2^14) (exact, undone on the chunk's partial sum together with
+//    the group scale);
+//  * int4: each staged chunk is rounded to 16-bit integers and kept as four
+//    signed base-16 digit planes; a dword of codes (offset binary, one XOR
+//    to two's complement) meets each plane in one v_dot8c_i32_i4, exact in
+//    int32 (stage_chunk_int4, dot_int4);
+//  * int8: codes are turned into float16 in registers by OR-ing them into
+//    the mantissa of 1024.0 (offset binary, so the value is 1024 + q + 128
+//    exactly) and multiplied with the float16 chunk by v_dot2_f32_f16, which
+//    accumulates in float32; 1152 times the chunk's sum is taken off once;
 //  * partial sums of a row are added across its lanes with DPP and lane
 //    reads, always in the same order.
 #include <hip/hip_ext.h>
@@ -43,24 +46,15 @@ template <int WB> struct Fmt;
 template <> struct Fmt<4> { static constexpr int epc = 32, xdw = 16; };
 template <> struct Fmt<8> { static constexpr int epc = 16, xdw = 8; };
 
-// The float16 pairs of one 16-byte chunk of offset-binary codes (1024 + code
-// + offset in each half), in the order the staged activations use.
-template <int WB>
-__device__ __forceinline__ void extract_chunk(uint4 w, uint32_t *h)
+// The float16 pairs of one 16-byte chunk of offset-binary int8 codes (1024
+// + code + 128 in each half), in the order the staged activations use.
+__device__ __forceinline__ void extract_chunk8(uint4 w, uint32_t *h)
 {
     const uint32_t d[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        if constexpr (WB == 4) {
-            const uint32_t d8 = d[q] >> 8;
-            h[4 * q + 0] = and_or(d[q], 0x000F000Fu, kMagic);
-            h[4 * q + 1] = and_or(d[q], 0x00F000F0u, kMagic);
-            h[4 * q + 2] = and_or(d8, 0x000F000Fu, kMagic);
-            h[4 * q + 3] = and_or(d8, 0x00F000F0u, kMagic);
-        } else {
-            h[2 * q + 0] = and_or(d[q], 0x00FF00FFu, kMagic);
-            h[2 * q + 1] = and_or(d[q] >> 8, 0x00FF00FFu, kMagic);
-        }
+        h[2 * q + 0] = and_or(d[q], 0x00FF00FFu, kMagic);
+        h[2 * q + 1] = and_or(d[q] >> 8, 0x00FF00FFu, kMagic);
     }
 }
 
@@ -92,51 +86,88 @@ __device__ __forceinline__ uint32_t pack2(__fp16 lo, __fp16 hi)
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Stage one chunk of activations (already scaled) for the dot product and
-// return the correction 1032*sum(A) + 1152*sum(B) (int4) or 1152*sum (int8).
-template <int WB>
-__device__ __forceinline__ float stage_chunk(const float4 *src, float scale, uint32_t *xs)
+// Stage one int8 chunk of activations (16 values, scaled by `scale`) as
+// float16 pairs for the dot product; returns the correction 1152 * sum.
+__device__ __forceinline__ float stage_chunk8(const float4 *src, float scale, uint32_t *xs)
 {
-    constexpr int epc = Fmt<WB>::epc;
-    float v[epc];
+    float v[16];
 #pragma unroll
-    for (int q = 0; q < epc / 4; ++q) {
+    for (int q = 0; q < 4; ++q) {
         const float4 f4 = src[q];
         v[4 * q + 0] = f4.x * scale;
         v[4 * q + 1] = f4.y * scale;
         v[4 * q + 2] = f4.z * scale;
         v[4 * q + 3] = f4.w * scale;
     }
-    if constexpr (WB == 4) {
-        float sa = 0.0f, sb = 0.0f;
+    float s = 0.0f;
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const float *e = v + 8 * blk;
-            __fp16 a0 = to_h(e[0]), a4 = to_h(e[4]), a2 = to_h(e[2]), a6 = to_h(e[6]);
-            __fp16 b1 = to_h(e[1] * 0.0625f), b5 = to_h(e[5] * 0.0625f);
-            __fp16 b3 = to_h(e[3] * 0.0625f), b7 = to_h(e[7] * 0.0625f);
-            xs[4 * blk + 0] = pack2(a0, a4);
-            xs[4 * blk + 1] = pack2(b1, b5);
-            xs[4 * blk + 2] = pack2(a2, a6);
-            xs[4 * blk + 3] = pack2(b3, b7);
-            sa += ((float)a0 + (float)a4) + ((float)a2 + (float)a6);
-            sb += ((float)b1 + (float)b5) + ((float)b3 + (float)b7);
-        }
-        return 1032.0f * sa + 1152.0f * sb;
-    } else {
-        float s = 0.0f;
+    for (int dw = 0; dw < 4; ++dw) {
+        const float *e = v + 4 * dw;
+        __fp16 a0 = to_h(e[0]), a1 = to_h(e[1]), a2 = to_h(e[2]), a3 = to_h(e[3]);
+        xs[2 * dw + 0] = pack2(a0, a2);
+        xs[2 * dw + 1] = pack2(a1, a3);
+        s += ((float)a0 + (float)a2) + ((float)a1 + (float)a3);
+    }
+    return 1152.0f * s;
+}
+
+// int4 codes against integer activations: v_dot8c_i32_i4 (eight signed
+// 4-bit products into an int32). Each staged chunk of 32 activations,
+// already scaled into [-2^14, 2^14], is rounded to integers X and written
+// as four signed base-16 digit planes (X = sum_p 16^p d_p, d_p in [-8, 7]:
+// the nibbles of X + 0x8888, each XOR 8); a dword of codes (offset binary,
+// XOR 0x88888888 gives two's complement) meets each plane in one
+// instruction. Every product and sum is exact in int32 and the chunk total
+// (below 2^23) converts to float32 exactly: the only rounding is x -> X, 16
+// bits against float16's 11.
+// Stage one chunk (32 scaled values) as digit planes: xs[4 g + p] holds
+// plane p of elements 8g .. 8g+7, element 8g+j in nibble j.
+__device__ __forceinline__ void stage_chunk_int4(const float4 *src, float scale, uint32_t *xs)
+{
+    int u[32];
 #pragma unroll
-        for (int dw = 0; dw < 4; ++dw) {
-            const float *e = v + 4 * dw;
-            __fp16 a0 = to_h(e[0]), a1 = to_h(e[1]), a2 = to_h(e[2]), a3 = to_h(e[3]);
-            xs[2 * dw + 0] = pack2(a0, a2);
-            xs[2 * dw + 1] = pack2(a1, a3);
-            s += ((float)a0 + (float)a2) + ((float)a1 + (float)a3);
+    for (int q = 0; q < 8; ++q) {
+        const float4 f4 = src[q];
+        u[4 * q + 0] = (int)rintf(f4.x * scale) + 0x8888;
+        u[4 * q + 1] = (int)rintf(f4.y * scale) + 0x8888;
+        u[4 * q + 2] = (int)rintf(f4.z * scale) + 0x8888;
+        u[4 * q + 3] = (int)rintf(f4.w * scale) + 0x8888;
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        // element e and e + 4 of the group in one word: their nibbles of
+        // plane p land at bits 4e and 4e + 16 once shifted by 4e - 4p
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            pk[e] = (uint32_t)(u[8 * g + e] & 0xFFFF) | ((uint32_t)(u[8 * g + e + 4] & 0xFFFF) << 16);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t nib = pk[e] & (0x000F000Fu << (4 * p));
+                word |= (e >= p) ? (nib << (4 * (e - p))) : (nib >> (4 * (p - e)));
+            }
+            xs[4 * g + p] = word ^ 0x88888888u;
         }
-        return 1152.0f * s;
     }
 }
 
+// sum of the lane's 32 codes (one 16-byte chunk, offset binary) times the
+// staged integer activations of the chunk
+__device__ __forceinline__ int dot_int4(const uint4 &w, const uint32_t *xs)
+{
+    const uint32_t cw[4] = {w.x ^ 0x88888888u, w.y ^ 0x88888888u, w.z ^ 0x88888888u,
+                            w.w ^ 0x88888888u};
+    int a[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            a[p] = __builtin_amdgcn_sdot8((int)cw[g], (int)xs[4 * g + p], a[p], false);
+    return ((a[3] * 16 + a[2]) * 16 + a[1]) * 16 + a[0];
+}
 
 // staged activations per token per chunk: XDW dwords, the correction and the
 // chunk's inverse scale
@@ -433,7 +464,11 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
             sh = min(126, max(-126, 14 - ex));
         }
         uint32_t xs[XDW];
-        const float corr = stage_chunk<WB>(v, ldexpf(1.0f, sh), xs);
+        float corr = 0.0f;
+        if constexpr (WB == 4)
+            stage_chunk_int4(v, ldexpf(1.0f, sh), xs);
+        else
+            corr = stage_chunk8(v, ldexpf(1.0f, sh), xs);
         lds_ci[i * NCH + c] = make_float2(corr, ldexpf(1.0f, -sh));
 #pragma unroll
         for (int u = 0; u < XQ; ++u)
@@ -471,10 +506,13 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
         for (int u = 0; u < UB; ++u) {
             if (j0 + u >= n_mine) break;
             const int c = (slice + KS * (j0 + u)) * 4 + q;  // this lane's chunk
-            // codes -> float16 once per unit, then used for every token
+            // int8: codes -> float16 once per unit, then used for every token
+            constexpr bool kInt = WB == 4;
             uint32_t hw[NM][XDW];
+            if constexpr (!kInt) {
 #pragma unroll
-            for (int m = 0; m < NM; ++m) extract_chunk<WB>(w[u][m], hw[m]);
+                for (int m = 0; m < NM; ++m) extract_chunk8(w[u][m], hw[m]);
+            }
 #pragma unroll
             for (int i = 0; i < TB; ++i) {
                 if (i >= count) break;
@@ -489,9 +527,13 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
                 }
                 const float2 ci = lds_ci[i * NCH + c];  // correction, inverse scale
 #pragma unroll
-                for (int m = 0; m < NM; ++m)
-                    acc[i][m] = fmaf(sc[u][m] * ci.y, dot_halves<XDW>(hw[m], xs) - ci.x,
-                                     acc[i][m]);
+                for (int m = 0; m < NM; ++m) {
+                    if constexpr (kInt)
+                        acc[i][m] = fmaf(sc[u][m] * ci.y, (float)dot_int4(w[u][m], xs), acc[i][m]);
+                    else
+                        acc[i][m] = fmaf(sc[u][m] * ci.y, dot_halves<XDW>(hw[m], xs) - ci.x,
+                                         acc[i][m]);
+                }
             }
         }
     }
