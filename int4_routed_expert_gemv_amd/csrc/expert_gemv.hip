@@ -23,10 +23,8 @@
 //    signed base-16 digit planes; a dword of codes (offset binary, one XOR
 //    to two's complement) meets each plane in one v_dot8c_i32_i4, exact in
 //    int32 (stage_chunk_int4, dot_int4);
-//  * int8: codes are turned into float16 in registers by OR-ing them into
-//    the mantissa of 1024.0 (offset binary, so the value is 1024 + q + 128
-//    exactly) and multiplied with the float16 chunk by v_dot2_f32_f16, which
-//    accumulates in float32; 1152 times the chunk's sum is taken off once;
+//  * int8: the same with two signed base-256 digit planes and
+//    v_dot4c_i32_i8 (stage_chunk_int8, dot_int8);
 //  * partial sums of a row are added across its lanes with DPP and lane
 //    reads, always in the same order.
 #include <hip/hip_ext.h>
@@ -36,79 +34,53 @@
 namespace moe {
 namespace {
 
-typedef __fp16 h2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
-
-constexpr uint32_t kMagic = 0x64006400u;  // two float16 1024.0
-
+// codes per 16-byte lane chunk, staged activation dwords per chunk
 template <int WB> struct Fmt;
 template <> struct Fmt<4> { static constexpr int epc = 32, xdw = 16; };
 template <> struct Fmt<8> { static constexpr int epc = 16, xdw = 8; };
 
-// The float16 pairs of one 16-byte chunk of offset-binary int8 codes (1024
-// + code + 128 in each half), in the order the staged activations use.
-__device__ __forceinline__ void extract_chunk8(uint4 w, uint32_t *h)
+// int8 codes against integer activations: v_dot4c_i32_i8 (four signed
+// 8-bit products into an int32). A staged run of 16 activations, scaled into
+// [-2^14, 2^14], is rounded to integers X and kept as two signed base-256
+// digit planes (the bytes of X + 0x8080, each XOR 0x80: X = d_0 + 256 d_1);
+// a dword of codes (offset binary, XOR 0x80808080 gives two's complement)
+// meets each plane in one instruction. The run's sum is exact in int32; its
+// conversion to float32 rounds once (relative 2^-24) above 2^24.
+__device__ __forceinline__ void stage_chunk_int8(const float4 *src, float scale, uint32_t *xs)
 {
-    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        h[2 * q + 0] = and_or(d[q], 0x00FF00FFu, kMagic);
-        h[2 * q + 1] = and_or(d[q] >> 8, 0x00FF00FFu, kMagic);
-    }
-}
-
-// Sum of N float16 pair products in float32, as two interleaved chains (the
-// even and the odd pairs) added at the end, so that consecutive dot
-// instructions do not wait on each other.
-template <int N>
-__device__ __forceinline__ float dot_halves(const uint32_t *h, const uint32_t *xs)
-{
-    float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll
-    for (int q = 0; q < N; q += 2) {
-        a0 = __builtin_amdgcn_fdot2(as_h2(h[q]), as_h2(xs[q]), a0, false);
-        a1 = __builtin_amdgcn_fdot2(as_h2(h[q + 1]), as_h2(xs[q + 1]), a1, false);
-    }
-    return a0 + a1;
-}
-
-// float -> float16 with values below the smallest normal float16 set to zero,
-// so the dot product and the correction term see the same number
-__device__ __forceinline__ __fp16 to_h(float v)
-{
-    return fabsf(v) < 6.103515625e-05f ? (__fp16)0.0f : (__fp16)v;
-}
-
-__device__ __forceinline__ uint32_t pack2(__fp16 lo, __fp16 hi)
-{
-    h2_t v = {lo, hi};
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-// Stage one int8 chunk of activations (16 values, scaled by `scale`) as
-// float16 pairs for the dot product; returns the correction 1152 * sum.
-__device__ __forceinline__ float stage_chunk8(const float4 *src, float scale, uint32_t *xs)
-{
-    float v[16];
+    int u[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const float4 f4 = src[q];
-        v[4 * q + 0] = f4.x * scale;
-        v[4 * q + 1] = f4.y * scale;
-        v[4 * q + 2] = f4.z * scale;
-        v[4 * q + 3] = f4.w * scale;
+        u[4 * q + 0] = (int)rintf(f4.x * scale) + 0x8080;
+        u[4 * q + 1] = (int)rintf(f4.y * scale) + 0x8080;
+        u[4 * q + 2] = (int)rintf(f4.z * scale) + 0x8080;
+        u[4 * q + 3] = (int)rintf(f4.w * scale) + 0x8080;
     }
-    float s = 0.0f;
 #pragma unroll
-    for (int dw = 0; dw < 4; ++dw) {
-        const float *e = v + 4 * dw;
-        __fp16 a0 = to_h(e[0]), a1 = to_h(e[1]), a2 = to_h(e[2]), a3 = to_h(e[3]);
-        xs[2 * dw + 0] = pack2(a0, a2);
-        xs[2 * dw + 1] = pack2(a1, a3);
-        s += ((float)a0 + (float)a2) + ((float)a1 + (float)a3);
+    for (int g = 0; g < 4; ++g) {
+        // elements e and e + 2 of the group in one word: their bytes of plane
+        // p land at bytes e and e + 2 once shifted by 8 (e - p)
+        const uint32_t p0 = (uint32_t)(u[4 * g] & 0xFFFF) | ((uint32_t)(u[4 * g + 2] & 0xFFFF) << 16);
+        const uint32_t p1 = (uint32_t)(u[4 * g + 1] & 0xFFFF) | ((uint32_t)(u[4 * g + 3] & 0xFFFF) << 16);
+        xs[2 * g + 0] = ((p0 & 0x00FF00FFu) | ((p1 & 0x00FF00FFu) << 8)) ^ 0x80808080u;
+        xs[2 * g + 1] = (((p0 >> 8) & 0x00FF00FFu) | (p1 & 0xFF00FF00u)) ^ 0x80808080u;
     }
-    return 1152.0f * s;
+}
+
+// sum of the lane's 16 int8 codes (one 16-byte chunk, offset binary) times
+// the staged integer activations of the chunk
+__device__ __forceinline__ int dot_int8(const uint4 &w, const uint32_t *xs)
+{
+    const uint32_t cw[4] = {w.x ^ 0x80808080u, w.y ^ 0x80808080u, w.z ^ 0x80808080u,
+                            w.w ^ 0x80808080u};
+    int a0 = 0, a1 = 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        a0 = __builtin_amdgcn_sdot4((int)cw[g], (int)xs[2 * g], a0, false);
+        a1 = __builtin_amdgcn_sdot4((int)cw[g], (int)xs[2 * g + 1], a1, false);
+    }
+    return a1 * 256 + a0;
 }
 
 // int4 codes against integer activations: v_dot8c_i32_i4 (eight signed
@@ -169,8 +141,8 @@ __device__ __forceinline__ int dot_int4(const uint4 &w, const uint32_t *xs)
     return ((a[3] * 16 + a[2]) * 16 + a[1]) * 16 + a[0];
 }
 
-// staged activations per token per chunk: XDW dwords, the correction and the
-// chunk's inverse scale
+// staged activations per token per chunk: XDW dwords, and a float2 whose
+// second member is the chunk's inverse scale
 __host__ __device__ constexpr int stage_bytes(int wb) { return (wb == 4 ? 16 : 8) * 4 + 8; }
 
 // rounds of (token, chunk) activation pairs loaded before the weight loads
@@ -464,12 +436,11 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
             sh = min(126, max(-126, 14 - ex));
         }
         uint32_t xs[XDW];
-        float corr = 0.0f;
         if constexpr (WB == 4)
             stage_chunk_int4(v, ldexpf(1.0f, sh), xs);
         else
-            corr = stage_chunk8(v, ldexpf(1.0f, sh), xs);
-        lds_ci[i * NCH + c] = make_float2(corr, ldexpf(1.0f, -sh));
+            stage_chunk_int8(v, ldexpf(1.0f, sh), xs);
+        lds_ci[i * NCH + c] = make_float2(0.0f, ldexpf(1.0f, -sh));
 #pragma unroll
         for (int u = 0; u < XQ; ++u)
             lds_x[(i * XQ + u) * NCH + c] = make_uint4(xs[4 * u], xs[4 * u + 1], xs[4 * u + 2],
@@ -506,13 +477,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
         for (int u = 0; u < UB; ++u) {
             if (j0 + u >= n_mine) break;
             const int c = (slice + KS * (j0 + u)) * 4 + q;  // this lane's chunk
-            // int8: codes -> float16 once per unit, then used for every token
-            constexpr bool kInt = WB == 4;
-            uint32_t hw[NM][XDW];
-            if constexpr (!kInt) {
-#pragma unroll
-                for (int m = 0; m < NM; ++m) extract_chunk8(w[u][m], hw[m]);
-            }
+
 #pragma unroll
             for (int i = 0; i < TB; ++i) {
                 if (i >= count) break;
@@ -525,14 +490,11 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
                     xs[4 * qq + 2] = v.z;
                     xs[4 * qq + 3] = v.w;
                 }
-                const float2 ci = lds_ci[i * NCH + c];  // correction, inverse scale
+                const float2 ci = lds_ci[i * NCH + c];  // (unused, inverse scale)
 #pragma unroll
                 for (int m = 0; m < NM; ++m) {
-                    if constexpr (kInt)
-                        acc[i][m] = fmaf(sc[u][m] * ci.y, (float)dot_int4(w[u][m], xs), acc[i][m]);
-                    else
-                        acc[i][m] = fmaf(sc[u][m] * ci.y, dot_halves<XDW>(hw[m], xs) - ci.x,
-                                         acc[i][m]);
+                    const int d = WB == 4 ? dot_int4(w[u][m], xs) : dot_int8(w[u][m], xs);
+                    acc[i][m] = fmaf(sc[u][m] * ci.y, (float)d, acc[i][m]);
                 }
             }
         }
