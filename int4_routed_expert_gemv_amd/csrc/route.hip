@@ -38,6 +38,16 @@ __device__ __forceinline__ float wave_sum_dpp(float v)
     return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
+// pairwise sum of W per-wave partial sums, always in the same order
+template <int W>
+__device__ __forceinline__ float tree_sum(const float *p)
+{
+    if constexpr (W == 1)
+        return p[0];
+    else
+        return tree_sum<W / 2>(p) + tree_sum<W / 2>(p + W / 2);
+}
+
 constexpr int kTokGroup = 4;
 // batches up to this many tokens use the one-workgroup-per-expert GEMV router
 constexpr int kGemvMaxTokens = 16;
@@ -94,7 +104,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_gemv_kernel(
         }
         __syncthreads();
         if (tid < kTokGroup && t0 + tid < N) {
-            const float l = (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]);
+            const float l = tree_sum<kRouterThreads / kWave>(part[tid]);
             scores[(size_t)(t0 + tid) * E + e] = sigmoidf(l + bias);
         }
         __syncthreads();
