@@ -296,6 +296,14 @@ def main():
         for name, code in (("gemv", 0), ("mfma", 1), ("small", 2)):
             c[name + "_experts"] = int((ps == code).sum())
             c[name + "_tokens"] = int(T[ps == code].sum())
+        # a 128-token group's remainder of at most 32 tokens past a full item
+        # runs on the 32-token pass (its weights streamed there once more)
+        if mfma_ok and N > GEMV_BATCH:
+            r = T % 128
+            rem = (ps == 1) & (T > 128) & (r > 0) & (r <= 32)
+            c["mfma_tokens"] -= int(r[rem].sum())
+            c["small_tokens"] += int(r[rem].sum())
+            c["small_experts"] += int(rem.sum())
         calib[key] = c
 
     if stack:

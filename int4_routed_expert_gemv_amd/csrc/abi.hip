@@ -104,15 +104,20 @@ FwdLayout fwd_layout(const Geo &g, int N, int k, int has_shared, int mfma_min_to
         L.max_mitems = big ? (int)(ceil_div(A, kMfmaBigTokens) + ue_big +
                                    (has_shared ? ceil_div(N, kMfmaBigTokens) : 0))
                            : 0;
-        long long sm = ceil_div(A, kMfmaSmallTokens) + ue_small +
+        // every group on this pass, and (with the 128-token pass) the
+        // remainder of each group on that one, adds at most one partly
+        // filled item
+        long long sm = ceil_div(A, kMfmaSmallTokens) + (big ? ue : ue_small) +
                        (has_shared ? ceil_div(N, kMfmaSmallTokens) : 0);
         if (big) {
             // below tstar an expert is at most ceil((tstar - 1) / 32) items; experts
             // moved over from the 128-token pass had fewer than kMinBigItems of
-            // its items between them, so at most (kMinBigItems - 1) * 128 tokens
+            // its items between them, so at most (kMinBigItems - 1) * 128 tokens;
+            // each group left on the 128-token pass adds at most one remainder
             const long long below = (ue + (has_shared ? 1 : 0)) * ceil_div(L.tstar - 1, kMfmaSmallTokens);
             const long long moved = (long long)(kMinBigItems - 1) * (kMfmaBigTokens / kMfmaSmallTokens + 1);
-            if (below + moved < sm) sm = below + moved;
+            const long long rems = ue_big + (has_shared ? 1 : 0);
+            if (below + moved + rems < sm) sm = below + moved + rems;
         }
         L.max_sitems = small ? (int)sm : 0;
     }

@@ -598,13 +598,23 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Fwd f)
     }
     int pass = pass_of(f, T);
     int sh_pass = f.has_shared ? pass_of(f, f.N) : -1;
+    // A group on the 128-token pass whose last item would hold at most 32
+    // tokens past a full one gives that remainder to the 32-token pass: a
+    // 128-token item computes all of its token blocks whatever it holds.
+    const bool small_on = f.max_sitems > 0;
+    auto big_part = [&](int cnt) {
+        const int r = cnt % kMfmaBigTokens;
+        return (small_on && cnt > kMfmaBigTokens && r > 0 && r <= kMfmaSmallTokens) ? cnt - r
+                                                                                      : cnt;
+    };
     if (f.max_mitems > 0 && f.max_sitems > 0) {
         // a handful of 128-token items would run nearly alone (a few
         // workgroups each): give them to the 32-token pass instead, where
         // they run among the others
         int n_big;
-        block_excl_scan(pass == 1 ? (T + kMfmaBigTokens - 1) / kMfmaBigTokens : 0, n_big);
-        if (sh_pass == 1) n_big += (f.N + kMfmaBigTokens - 1) / kMfmaBigTokens;
+        block_excl_scan(pass == 1 ? (big_part(T) + kMfmaBigTokens - 1) / kMfmaBigTokens : 0,
+                        n_big);
+        if (sh_pass == 1) n_big += (big_part(f.N) + kMfmaBigTokens - 1) / kMfmaBigTokens;
         if (n_big < kMinBigItems) {
             if (pass == 1) pass = 2;
             if (sh_pass == 1) sh_pass = 2;
@@ -617,17 +627,30 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Fwd f)
 #pragma unroll
     for (int l = 0; l < 3; ++l) {
         const int sz = sizes[l], mx = maxes[l];
-        const int nsh = sh_pass == l ? (f.N + sz - 1) / sz : 0;
-        const int nb = pass == l ? (T + sz - 1) / sz : 0;
+        // the tokens [beg, end) of a group of cnt tokens on pass p that list l takes
+        auto span = [&](int p, int cnt, int &beg, int &end) {
+            beg = end = 0;
+            if (p == l) {
+                end = l == 1 ? big_part(cnt) : cnt;
+            } else if (p == 1 && l == 2) {  // the remainder of a 128-token group
+                beg = big_part(cnt);
+                end = cnt;
+            }
+        };
+        int sb, se, eb, ee;
+        span(sh_pass, f.N, sb, se);
+        span(pass, T, eb, ee);
+        const int nsh = (se - sb + sz - 1) / sz;
+        const int nb = (ee - eb + sz - 1) / sz;
         int tot;
         const int base = nsh + block_excl_scan(nb, tot);  // uniform call: every thread
         if (mx <= 0) continue;
         for (int b = u; b < nsh && b < mx; b += kPlanThreads) {
-            Item it = {-1, f.A + b * sz, min(sz, f.N - b * sz), 0};
+            Item it = {-1, f.A + sb + b * sz, min(sz, se - sb - b * sz), 0};
             lists[l][b] = it;
         }
         for (int b = 0; b < nb && base + b < mx; ++b) {
-            Item it = {e, s0 + b * sz, min(sz, T - b * sz), 0};
+            Item it = {e, s0 + eb + b * sz, min(sz, ee - eb - b * sz), 0};
             lists[l][base + b] = it;
         }
         if (u == 0) *counts[l] = min(nsh + tot, mx);
