@@ -267,8 +267,11 @@ moe_status moe_expert_forward(const moe_expert_pool *pool /* (host) */,
  *     2 tokens, which the GEMV takes in one item per expert), negative turns
  *     it off;
  *   otherwise: the streaming GEMV kernels.
- * When both matrix-core passes are on and the 128-token pass would get fewer
- * than 32 items, those experts join the 32-token pass (a few large items
+ * When both matrix-core passes are on, a group on the 128-token pass whose
+ * last item would hold at most 32 tokens past a full one gives those tokens
+ * to the 32-token pass (a 128-token item computes all of its tile), and
+ * when the 128-token pass would get fewer than 32 items, those experts join
+ * the 32-token pass (a few large items
  * would otherwise run with a few workgroups each); when n_tokens and k alone
  * bound it below 32 items, the 128-token kernels are not launched at all.
  * The matrix-core passes need int4 weights and d_model, d_ff multiples of
