@@ -282,6 +282,9 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
                 for (int m = 0; m < NM; ++m) bf[t][m] = dequant8<WB, !POST>(bw[t][m], s, s2[t][m]);
 #pragma unroll
             for (int mb = 0; mb < MF; ++mb) {
+                // 32-token items: a second token block with no token of the
+                // item is skipped (uniform over the workgroup)
+                if (MF == 2 && mb == 1 && count <= 16) continue;
                 const half8_t af =
                     *reinterpret_cast<const half8_t *>(&As[cur][mb * 16 + r16][QW * q + 8 * s]);
 #pragma unroll
