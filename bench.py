@@ -50,6 +50,9 @@ def parse():
                    help="tokens per step instead of the workload's (e.g. a speculative "
                         "verify batch of 1 + drafts through the stack)")
     p.add_argument("--k", type=int, default=None, help="experts per token instead of the workload's")
+    p.add_argument("--small-min", type=int, default=None,
+                   help="experts with at least this many tokens take the 32-token matrix-core "
+                        "pass (moe_forward_options.mfma_small_min_tokens; default: the library's)")
     p.add_argument("--group", type=int, default=None,
                    help="scale group of the int4 layers instead of the workload's (e.g. 64)")
     p.add_argument("--layers", type=int, default=8, help="layer pools rotated over the steps")
@@ -239,10 +242,17 @@ def main():
     hip_rt = ctypes.CDLL("libamdhip64.so")
     hip_rt.hipMemcpyAsync.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
 
+    base_opts = None
+    if args.small_min is not None:
+        base_opts = moe.ForwardOptions()
+        base_opts.mfma_small_min_tokens = args.small_min
+
     def run_layer(s, ev=None):
         route, fwd = plans[s % n_plan]
         rc = Lb.moe_route_union(*route)
-        if ev is None:
+        if ev is None and base_opts is not None:
+            rc |= Lb.moe_expert_forward_ex(*fwd, ctypes.byref(base_opts))
+        elif ev is None:
             rc |= Lb.moe_expert_forward(*fwd)
         else:
             rc |= Lb.moe_expert_forward_ex(*fwd, ctypes.byref(ev))
@@ -269,7 +279,8 @@ def main():
     # tokens go to the 128-token matrix-core pass, those with at least
     # SMALL_MIN to the 32-token pass, the rest to the GEMVs; the shared
     # expert by the batch size
-    MFMA_MIN, SMALL_MIN = 32, 2
+    MFMA_MIN = 32
+    SMALL_MIN = args.small_min if args.small_min is not None else 2
     mfma_ok = spec.wbits == 4 and d % 64 == 0 and f % 64 == 0
     calib = {}
 
@@ -280,7 +291,7 @@ def main():
         T = np.asarray(T)
         big = (T >= MFMA_MIN) & mfma_ok
         # batches of up to GEMV_BATCH tokens stay on the GEMV (the library's default)
-        small = ~big & (T >= SMALL_MIN) & mfma_ok & (N > GEMV_BATCH)
+        small = ~big & (T >= SMALL_MIN) & mfma_ok & (N > GEMV_BATCH or args.small_min is not None)
         if big.any() and np.sum((T[big] + 127) // 128) < MIN_BIG_ITEMS:
             small, big = small | big, np.zeros_like(big)
         return np.where(big, 1, np.where(small, 2, 0))
@@ -298,7 +309,7 @@ def main():
             c[name + "_tokens"] = int(T[ps == code].sum())
         # a 128-token group's remainder of at most 32 tokens past a full item
         # runs on the 32-token pass (its weights streamed there once more)
-        if mfma_ok and N > GEMV_BATCH:
+        if mfma_ok and (N > GEMV_BATCH or args.small_min is not None) and SMALL_MIN > 0:
             r = T % 128
             rem = (ps == 1) & (T > 128) & (r > 0) & (r <= 32)
             c["mfma_tokens"] -= int(r[rem].sum())
@@ -334,7 +345,9 @@ def main():
     # the other steps run without them.
     every = max(1, K // 64)
     sampled = [s_ for s_ in range(K) if s_ % every == 0]
-    evs = {s_: moe.ForwardOptions(*[hip.event() for _ in range(12)], 0, 0) for s_ in sampled}
+    evs = {s_: moe.ForwardOptions(*[hip.event() for _ in range(12)], 0,
+                                  args.small_min if args.small_min is not None else 0)
+           for s_ in sampled}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s_ in range(K):
