@@ -404,3 +404,29 @@ def test_decode1_direct_combine_is_deterministic():
         np.testing.assert_array_equal(again["y"], first["y"])
     del pool
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("d,f,wbits,group", [(16384, 128, 4, 128), (128, 16384, 4, 128),
+                                             (16384, 128, 8, 0), (128, 16384, 8, 0)])
+def test_largest_model_dims(d, f, wbits, group):
+    """d_model or d_ff at the largest size the library accepts (16384), int4
+    with groups of 128 and int8 with per-row scales: the GEMV's staged
+    activations and the matrix-core passes' hidden rows at their longest, on
+    each pass alone and mixed, against one oracle run."""
+    base = synth.CONFIGS["tiny"]
+    div = 16 if wbits == 8 else 1
+    spec = dataclasses.replace(base.layer, d=d, f=f, wbits=wbits, group=group,
+                               scale_lo=0.005 / div, scale_hi=0.02 / div)
+    cfg = dataclasses.replace(base, n_tokens=40, k=4, layers=(spec,))
+    spec, x, wr, b, blocks, shared, _ = oracle_then_pool(cfg)
+    say(f"[largest dims] d={d} f={f} wbits={wbits} G={group} N={cfg.n_tokens} k={cfg.k}")
+    ref = oracle.layer_step(x, wr, b, cfg.k, blocks, shared, spec.d, spec.f, spec.wbits,
+                            spec.group)
+    pool = upload_pool(spec, blocks, shared)
+    for big, small in PASSES + [(None, None)]:
+        got = run_layer(pool, x, wr, b, cfg.k, mfma_min_tokens=big, mfma_small_min_tokens=small)
+        check_routing(got, ref, spec.n_experts)
+        err = check_y(got["y"], ref["y"])
+        say(f"[largest dims] big={big} small={small} max rel err {err:.2e}")
+    del pool
+    torch.cuda.empty_cache()
