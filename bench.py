@@ -1,10 +1,10 @@
 #!/usr/bin/env python3
 """Throughput of the routed-expert layer step on one MI355X.
 
-A step is one pass of the whole layer step over one batch: route + top-k,
-union + permutation and hit counters (moe_route_union), then expert math +
-combine (moe_expert_forward), on one stream. Inputs are synthetic and
-already resident in HBM.
+A step is one pass of the whole layer step over one batch, one
+moe_layer_step call on one stream: route + top-k, union + permutation and hit
+counters, then expert math + combine (for one token the routing runs inside
+the gate/up GEMV launch). Inputs are synthetic and already resident in HBM.
 
 Default workload ("decode1"): one GLM-5.2-shaped decode layer (d_model 6144,
 d_ff 2048, 256 routed + 1 shared int4 experts with float32 scales per 128,
@@ -211,7 +211,7 @@ def main():
     perm = torch.empty(A, dtype=torch.int32, device=dev)
     counters = torch.zeros((L_rot, E), dtype=torch.int64, device=dev)
     y = torch.empty((N, d), dtype=torch.float32, device=dev)
-    ws_bytes = max(moe.workspace_size(p.desc, N, k) for p in pools)
+    ws_bytes = max(moe.layer_step_workspace_size(p.desc, N, k) for p in pools)
     hbuf = torch.empty((N, d), dtype=torch.float32, device=dev)   # residual stream
     abuf = torch.empty((N, d), dtype=torch.float32, device=dev)   # normalised layer input
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -227,15 +227,12 @@ def main():
         l, bi = s % L_rot, s % nb
         x = abuf if stack else xs[bi]
         wr, b = routers[l]
-        # Route, Union and Learn in one call (moe_route_union), then the experts
-        route = (vp(x.data_ptr()), N, d, vp(wr.data_ptr()), vp(b.data_ptr()), E, k,
-                 vp(ids.data_ptr()), vp(w.data_ptr()), vp(union_ids.data_ptr()),
-                 vp(n_union.data_ptr()), vp(offsets.data_ptr()), vp(perm.data_ptr()),
-                 vp(counters[l].data_ptr()), vp(ws.data_ptr()), ws_bytes, stream)
-        fwd = (ctypes.byref(pools[l].desc), vp(x.data_ptr()), N, k, vp(w.data_ptr()),
-               vp(union_ids.data_ptr()), vp(n_union.data_ptr()), vp(offsets.data_ptr()),
-               vp(perm.data_ptr()), vp(y.data_ptr()), vp(ws.data_ptr()), ws_bytes, stream)
-        return route, fwd
+        # Route, Union, Learn and the experts in one call (moe_layer_step)
+        return (ctypes.byref(pools[l].desc), vp(x.data_ptr()), N, d, vp(wr.data_ptr()),
+                vp(b.data_ptr()), k, vp(ids.data_ptr()), vp(w.data_ptr()),
+                vp(union_ids.data_ptr()), vp(n_union.data_ptr()), vp(offsets.data_ptr()),
+                vp(perm.data_ptr()), vp(counters[l].data_ptr()), vp(y.data_ptr()),
+                vp(ws.data_ptr()), ws_bytes, stream)
 
     plans = [step_args(s) for s in range(L_rot if stack else L_rot * nb)]
     n_plan = len(plans)
@@ -248,14 +245,8 @@ def main():
         base_opts.mfma_small_min_tokens = args.small_min
 
     def run_layer(s, ev=None):
-        route, fwd = plans[s % n_plan]
-        rc = Lb.moe_route_union(*route)
-        if ev is None and base_opts is not None:
-            rc |= Lb.moe_expert_forward_ex(*fwd, ctypes.byref(base_opts))
-        elif ev is None:
-            rc |= Lb.moe_expert_forward(*fwd)
-        else:
-            rc |= Lb.moe_expert_forward_ex(*fwd, ctypes.byref(ev))
+        opt = ev if ev is not None else base_opts
+        rc = Lb.moe_layer_step(*plans[s % n_plan], None if opt is None else ctypes.byref(opt))
         if rc:
             raise RuntimeError(f"layer step failed with status {rc}")
 

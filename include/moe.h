@@ -323,11 +323,40 @@ moe_status moe_hit_count(const int32_t *topk_ids, int n_tokens, int k, int n_exp
 moe_status moe_residual_rmsnorm(float *h, const float *y, float *a, int n_tokens,
                                 int d_model, float eps, hipStream_t stream);
 
+/*
+ * A whole layer step in one call: moe_route_union (router bias inside the
+ * sigmoid, no options) followed by moe_expert_forward, with the same
+ * arguments, checks (all made before anything is enqueued) and outputs, bit
+ * for bit; d_model must equal pool->d_model and the router has
+ * pool->n_experts rows. counters may be NULL. For one token the top-k, union,
+ * permutation and counting run inside the gate/up GEMV launch: every
+ * workgroup of a routed expert takes the top-k of the router's scores itself
+ * and workgroup 0 writes the routing outputs, so a decode step is three
+ * launches (router, gate/up, down) instead of four. workspace: at least
+ * moe_layer_step_workspace_size(pool, n_tokens, k) bytes, 256-byte aligned
+ * (the router's output, then the expert step's workspace); its contents
+ * afterwards are unspecified. opt (host, may be NULL): as for
+ * moe_expert_forward_ex (events around the expert kernels, pass thresholds);
+ * a positive threshold makes a one-token step take the two calls' kernels.
+ * Colibri pages: "Exact Architecture and Data-Flow Reconstruction", stages
+ * (1) Route, (2) Union and (5) Learn, and the three-matrix expert MLP with
+ * the always-on shared expert.
+ */
+moe_status moe_layer_step(const moe_expert_pool *pool /* (host) */, const float *x,
+                          int n_tokens, int d_model, const float *w_router,
+                          const float *b_router, int k, int32_t *topk_ids, float *topk_w,
+                          int32_t *union_ids, int32_t *n_union, int32_t *expert_offsets,
+                          int32_t *perm, uint64_t *counters, float *y, void *workspace,
+                          size_t ws_bytes, hipStream_t stream,
+                          const moe_forward_options *opt /* (host) */);
+
 /* Workspace sizes in bytes (host-only arithmetic, no HIP calls). */
 size_t moe_route_workspace_size(int n_tokens, int n_experts);
 size_t moe_forward_workspace_size(const moe_expert_pool *pool, int n_tokens, int k);
 /* The larger of the two, for one buffer shared by a layer step's calls. */
 size_t moe_workspace_size(const moe_expert_pool *pool, int n_tokens, int k);
+/* The sum of the two (0 for invalid arguments): moe_layer_step's workspace. */
+size_t moe_layer_step_workspace_size(const moe_expert_pool *pool, int n_tokens, int k);
 
 /* Bytes of one expert block (same for the canonical and device layouts). */
 size_t moe_block_bytes(int d_model, int d_ff, int wbits, int group);

@@ -348,12 +348,16 @@ moe_status moe_route_union(const float *x, int n_tokens, int d_model, const floa
                               workspace, ws_bytes, stream, nullptr);
 }
 
-moe_status moe_route_union_ex(const float *x, int n_tokens, int d_model, const float *w_router,
-                              const float *b_router, int n_experts, int k, int32_t *topk_ids,
-                              float *topk_w, int32_t *union_ids, int32_t *n_union,
-                              int32_t *expert_offsets, int32_t *perm, uint64_t *counters,
-                              void *workspace, size_t ws_bytes, hipStream_t stream,
-                              const moe_route_options *opt)
+// What route_union_impl does after its checks.
+enum class RouteMode { all, check_only, router_only };
+
+static moe_status route_union_impl(const float *x, int n_tokens, int d_model,
+                                   const float *w_router, const float *b_router, int n_experts,
+                                   int k, int32_t *topk_ids, float *topk_w, int32_t *union_ids,
+                                   int32_t *n_union, int32_t *expert_offsets, int32_t *perm,
+                                   uint64_t *counters, void *workspace, size_t ws_bytes,
+                                   hipStream_t stream, const moe_route_options *opt,
+                                   RouteMode mode, int *P_out, const float **b_out)
 {
     // every check of moe_route_topk, moe_union and moe_hit_count, before any launch
     if (n_tokens < 0 || d_model <= 0) return MOE_EINVAL;
@@ -376,11 +380,17 @@ moe_status moe_route_union_ex(const float *x, int n_tokens, int d_model, const f
     TopkOpt to;
     if (!route_options(opt, b_router, &b_in, &to)) return MOE_EINVAL;
     if (to.sel && ((uintptr_t)to.sel % 4)) return MOE_EALIGN;
+    if (mode == RouteMode::check_only) return MOE_OK;
     float *scores = static_cast<float *>(workspace);
     const int P = router_slices(n_tokens, d_model, n_experts);
     if (launch_router(x, n_tokens, d_model, w_router, b_in, n_experts, scores, stream) !=
         hipSuccess)
         return MOE_EHIP;
+    if (mode == RouteMode::router_only) {
+        *P_out = P;
+        *b_out = b_in;
+        return MOE_OK;
+    }
     if (n_tokens <= route_tail_max_tokens())
         return launch_route_tail(scores, P, b_in, n_tokens, n_experts, k, topk_ids, topk_w,
                                  union_ids, n_union, expert_offsets, perm, counters, stream,
@@ -410,6 +420,18 @@ moe_status moe_route_union_ex(const float *x, int n_tokens, int d_model, const f
     return MOE_OK;
 }
 
+moe_status moe_route_union_ex(const float *x, int n_tokens, int d_model, const float *w_router,
+                              const float *b_router, int n_experts, int k, int32_t *topk_ids,
+                              float *topk_w, int32_t *union_ids, int32_t *n_union,
+                              int32_t *expert_offsets, int32_t *perm, uint64_t *counters,
+                              void *workspace, size_t ws_bytes, hipStream_t stream,
+                              const moe_route_options *opt)
+{
+    return route_union_impl(x, n_tokens, d_model, w_router, b_router, n_experts, k, topk_ids,
+                            topk_w, union_ids, n_union, expert_offsets, perm, counters, workspace,
+                            ws_bytes, stream, opt, RouteMode::all, nullptr, nullptr);
+}
+
 moe_status moe_expert_forward(const moe_expert_pool *pool, const float *x, int n_tokens, int k,
                               const float *topk_w, const int32_t *union_ids,
                               const int32_t *n_union, const int32_t *expert_offsets,
@@ -420,11 +442,22 @@ moe_status moe_expert_forward(const moe_expert_pool *pool, const float *x, int n
                                  perm, y, workspace, ws_bytes, stream, nullptr);
 }
 
-moe_status moe_expert_forward_ex(const moe_expert_pool *pool, const float *x, int n_tokens, int k,
-                                 const float *topk_w, const int32_t *union_ids,
-                                 const int32_t *n_union, const int32_t *expert_offsets,
-                                 const int32_t *perm, float *y, void *workspace, size_t ws_bytes,
-                                 hipStream_t stream, const moe_forward_options *ev)
+// The routing a one-token moe_layer_step hands to the gate/up kernel.
+struct InRoute {
+    const float *scores;
+    int P;
+    const float *b;
+    int32_t *ids;
+    float *w;
+    uint64_t *counters;
+};
+
+static moe_status forward_impl(const moe_expert_pool *pool, const float *x, int n_tokens, int k,
+                               const float *topk_w, const int32_t *union_ids,
+                               const int32_t *n_union, const int32_t *expert_offsets,
+                               const int32_t *perm, float *y, void *workspace, size_t ws_bytes,
+                               hipStream_t stream, const moe_forward_options *ev,
+                               bool check_only, const InRoute *ir)
 {
     Geo g;
     moe_status st = resolve_geo(pool, &g);
@@ -450,9 +483,16 @@ moe_status moe_expert_forward_ex(const moe_expert_pool *pool, const float *x, in
                                    ev ? ev->mfma_small_min_tokens : 0);
     if (!workspace || ws_bytes < (size_t)L.total) return MOE_EWORKSPACE;
     if (!aligned(workspace)) return MOE_EALIGN;
+    if (check_only) return MOE_OK;
 
     char *ws = static_cast<char *>(workspace);
     Fwd f;
+    f.route_in = ir ? ir->scores : nullptr;
+    f.route_P = ir ? ir->P : 1;
+    f.route_b = ir ? ir->b : nullptr;
+    f.route_ids = ir ? ir->ids : nullptr;
+    f.route_w = ir ? ir->w : nullptr;
+    f.route_counters = ir ? reinterpret_cast<unsigned long long *>(ir->counters) : nullptr;
     f.g = g;
     f.pool = static_cast<const uint8_t *>(pool->pool);
     f.stride = pool->expert_bytes;
@@ -519,6 +559,81 @@ moe_status moe_expert_forward_ex(const moe_expert_pool *pool, const float *x, in
         launch_combine(f.o, topk_w, n_tokens, k, g.d, (int)A, has_shared, y, stream) != hipSuccess)
         return MOE_EHIP;
     return MOE_OK;
+}
+
+moe_status moe_expert_forward_ex(const moe_expert_pool *pool, const float *x, int n_tokens, int k,
+                                 const float *topk_w, const int32_t *union_ids,
+                                 const int32_t *n_union, const int32_t *expert_offsets,
+                                 const int32_t *perm, float *y, void *workspace, size_t ws_bytes,
+                                 hipStream_t stream, const moe_forward_options *ev)
+{
+    return forward_impl(pool, x, n_tokens, k, topk_w, union_ids, n_union, expert_offsets, perm, y,
+                        workspace, ws_bytes, stream, ev, false, nullptr);
+}
+
+size_t moe_layer_step_workspace_size(const moe_expert_pool *pool, int n_tokens, int k)
+{
+    if (!pool) return 0;
+    const size_t a = moe_route_workspace_size(n_tokens, pool->n_experts);
+    const size_t b = moe_forward_workspace_size(pool, n_tokens, k);
+    return a && b ? a + b : 0;
+}
+
+moe_status moe_layer_step(const moe_expert_pool *pool, const float *x, int n_tokens, int d_model,
+                          const float *w_router, const float *b_router, int k, int32_t *topk_ids,
+                          float *topk_w, int32_t *union_ids, int32_t *n_union,
+                          int32_t *expert_offsets, int32_t *perm, uint64_t *counters, float *y,
+                          void *workspace, size_t ws_bytes, hipStream_t stream,
+                          const moe_forward_options *opt)
+{
+    if (!pool) return MOE_EINVAL;
+    Geo g;
+    moe_status st = resolve_geo(pool, &g);
+    if (st != MOE_OK) return st;
+    if (d_model != pool->d_model) return MOE_ESHAPE;
+    st = check_k(k, pool->n_experts);
+    if (st != MOE_OK) return st;
+    if (n_tokens < 0) return MOE_EINVAL;
+    const size_t need = moe_layer_step_workspace_size(pool, n_tokens, k);
+    if (n_tokens > 0 && (!workspace || need == 0 || ws_bytes < need)) return MOE_EWORKSPACE;
+    // the router's output first, the expert step's workspace after it
+    const size_t rs = moe_route_workspace_size(n_tokens, pool->n_experts);
+    char *ws = static_cast<char *>(workspace);
+    void *fws = ws ? ws + rs : nullptr;
+    const size_t fbytes = ws_bytes > rs ? ws_bytes - rs : 0;
+    // every check of both calls before anything is enqueued
+    st = route_union_impl(x, n_tokens, d_model, w_router, b_router, pool->n_experts, k,
+                                     topk_ids, topk_w, union_ids, n_union, expert_offsets, perm,
+                                     counters, workspace, rs, stream, nullptr,
+                                     RouteMode::check_only, nullptr, nullptr);
+    if (st != MOE_OK) return st;
+    st = forward_impl(pool, x, n_tokens, k, topk_w, union_ids, n_union, expert_offsets, perm, y,
+                      fws, fbytes, stream, opt, true, nullptr);
+    if (st != MOE_OK || n_tokens == 0) return st;
+    // a positive threshold can put a single token on the matrix cores
+    const bool gemv_only = !opt || (opt->mfma_min_tokens <= 0 && opt->mfma_small_min_tokens <= 0);
+    if (n_tokens != 1 || !gemv_only) {
+        st = route_union_impl(x, n_tokens, d_model, w_router, b_router, pool->n_experts, k,
+                              topk_ids, topk_w, union_ids, n_union, expert_offsets, perm,
+                              counters, workspace, rs, stream, nullptr, RouteMode::all, nullptr,
+                              nullptr);
+        if (st != MOE_OK) return st;
+        return forward_impl(pool, x, n_tokens, k, topk_w, union_ids, n_union, expert_offsets,
+                            perm, y, fws, fbytes, stream, opt, false, nullptr);
+    }
+    // one token: the router, then the expert kernels, the top-k, union and
+    // counting taken inside the gate/up GEMV launch
+    InRoute ir;
+    ir.scores = static_cast<const float *>(workspace);
+    ir.ids = topk_ids;
+    ir.w = topk_w;
+    ir.counters = counters;
+    st = route_union_impl(x, n_tokens, d_model, w_router, b_router, pool->n_experts, k, topk_ids,
+                          topk_w, union_ids, n_union, expert_offsets, perm, counters, workspace,
+                          rs, stream, nullptr, RouteMode::router_only, &ir.P, &ir.b);
+    if (st != MOE_OK) return st;
+    return forward_impl(pool, x, n_tokens, k, topk_w, union_ids, n_union, expert_offsets, perm, y,
+                        fws, fbytes, stream, opt, false, &ir);
 }
 
 moe_status moe_residual_rmsnorm(float *h, const float *y, float *a, int n_tokens, int d_model,

@@ -30,6 +30,7 @@
 #include <hip/hip_ext.h>
 
 #include "internal.h"
+#include "topk.h"
 
 namespace moe {
 namespace {
@@ -255,6 +256,8 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
     __shared__ Item s_item;
     __shared__ int s_expert;
     __shared__ float red[NW][TB][NM][kUnitRows];
+    __shared__ int32_t s_rt_lds[MOE_MAX_K], s_rt_ids[MOE_MAX_K];  // routing inside (one token)
+    __shared__ float s_rt_w[MOE_MAX_K];
 
     const Fwd &f = ga.f;
     const Geo &g = f.g;
@@ -274,7 +277,51 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
     int expert;
     Item it;
     bool resolved = true;
-    if (GATEUP && ga.plan_here == 2) {
+    if (GATEUP && ga.plan_here == 2 && f.route_in) {
+        // one token, routed here: every workgroup of a routed item takes the
+        // top-k of the router's output (the same code and inputs as the route
+        // tail, so the same ids); union slot j holds the j-th smallest id.
+        // Workgroup 0 also writes the routing outputs for the down kernel and
+        // the caller (an extra workgroup doing only that measured slower).
+        const int nsh = f.has_shared ? 1 : 0;
+        const bool writer = blockIdx.x == 0;
+        const bool route = writer || item_idx >= nsh;
+        resolved = false;
+        if (tid == 0) s_expert = item_idx < nsh ? -1 : -2;
+        if (wave == 0 && route)
+            topk_wave<false>(f.route_in, f.route_P, f.route_b, 1, g.E, f.k, 0,
+                             writer ? f.route_ids : s_rt_ids, writer ? f.route_w : s_rt_w,
+                             s_rt_lds);
+        __syncthreads();
+        if (wave == 0 && route) {
+            const int k = f.k;
+            const int id = lane < k ? s_rt_lds[lane] : 0x7FFFFFFF;
+            int r = 0;  // rank of this lane's id among the k (distinct) ids
+            for (int i = 0; i < k; ++i) r += s_rt_lds[i] < id ? 1 : 0;
+            if (lane < k) {
+                if (item_idx - nsh == r) s_expert = id;
+                if (writer) {
+                    const_cast<int32_t *>(f.union_ids)[r] = id;
+                    const_cast<int32_t *>(f.perm)[r] = lane;
+                    if (f.route_counters) atomicAdd(&f.route_counters[id], 1ull);
+                }
+            }
+            if (writer) {
+                for (int e = lane; e <= g.E; e += kWave) {
+                    int c = 0;
+                    for (int i = 0; i < k; ++i) c += s_rt_lds[i] < e ? 1 : 0;
+                    const_cast<int32_t *>(f.offsets)[e] = c;
+                }
+                if (lane == 0) {
+                    *const_cast<int32_t *>(f.n_union) = k;
+                    *f.n_items = nsh + k;
+                }
+            }
+        }
+        __syncthreads();
+        expert = s_expert;
+        if (expert == -2) return;  // beyond the union: uniform exit
+    } else if (GATEUP && ga.plan_here == 2) {
         // every expert has at most n_tokens <= TB tokens: one item per union
         // slot, after the shared expert's single item
         const int nsh = f.has_shared ? 1 : 0;
@@ -794,6 +841,7 @@ hipError_t launch_gateup(const Fwd &f, hipStream_t s)
     a.plan_here = max_union <= kWave && f.max_mitems == 0 && f.max_sitems == 0
                       ? (f.N <= f.tb ? 2 : 1)
                       : 0;
+    if (f.route_in && (a.plan_here != 2 || f.N != 1)) return hipErrorInvalidValue;
     if (!a.plan_here) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, f);
         const hipError_t e = hipGetLastError();

@@ -68,6 +68,17 @@ struct Fwd {
     int direct;              // 1: the GEMV down kernel adds the gate-weighted rows into y
                              // itself (at most two addends per element, y cleared by
                              // the gate/up kernel); 0: the combine kernel writes y
+    // One-token layer step (moe_layer_step): when route_in is not null the
+    // gate/up GEMV kernel takes the top-k of the router's output itself, and
+    // workgroup 0 writes the top-k (route_ids, route_w = w), the union,
+    // offsets, permutation (into union_ids, n_union, offsets, perm) and the
+    // hit counts; the down kernel reads them after the launch boundary.
+    const float *route_in;   // router output: P slices of [E] (P = 1: final scores)
+    int route_P;
+    const float *route_b;    // router bias (used when P > 1), may be null
+    int32_t *route_ids;      // [k]
+    float *route_w;          // [k], the same buffer as w
+    unsigned long long *route_counters;  // [E] or null
     Item *items;             // [max_items] work list (workspace)
     int32_t *n_items;        // [1]
     int tb;                  // tokens per GEMV work item

@@ -330,3 +330,34 @@ def test_cache_calls_reject_a_null_cache():
     for name in ("moe_cache_pin", "moe_cache_prefetch"):
         assert getattr(L, name)(None, ids.ctypes.data, 4, None, None, None) == moe.MOE_EINVAL
     assert L.moe_cache_resident(None, None, None) == moe.MOE_EINVAL
+
+
+def _step(pool, N=1, k=1, d=None, ws=FAKE, wsb=1 << 30, x=FAKE, wr=FAKE, y=FAKE):
+    d = pool.d_model if d is None else d
+    return moe.lib().moe_layer_step(ctypes.byref(pool), x, N, d, wr, None, k, FAKE, FAKE, FAKE,
+                                    FAKE, FAKE, FAKE, None, y, ws, wsb, None, None)
+
+
+def test_layer_step_argument_checks():
+    """moe_layer_step makes every check of moe_route_union and
+    moe_expert_forward before launching anything."""
+    p = _pool()
+    need = moe.layer_step_workspace_size(p, 1, 1)
+    assert need == moe.route_workspace_size(1, 16) + moe.forward_workspace_size(p, 1, 1)
+    assert moe.layer_step_workspace_size(_pool(wbits=3), 1, 1) == 0
+    assert _step(p, wsb=need - 1) == moe.MOE_EWORKSPACE
+    assert _step(p, ws=None) == moe.MOE_EWORKSPACE
+    assert _step(p, d=512) == moe.MOE_ESHAPE                  # d_model differs from the pool's
+    assert _step(p, k=17) == moe.MOE_EINVAL                   # k above n_experts
+    assert _step(p, k=0) == moe.MOE_EINVAL
+    assert _step(p, x=None) == moe.MOE_EINVAL
+    assert _step(p, wr=None) == moe.MOE_EINVAL
+    assert _step(p, y=None) == moe.MOE_EINVAL
+    assert _step(p, x=FAKE + 4) == moe.MOE_EALIGN
+    assert _step(p, ws=FAKE + 64, wsb=1 << 30) == moe.MOE_EALIGN
+    assert _step(_pool(d=250), d=250) == moe.MOE_ESHAPE       # not a multiple of 128
+    assert _step(p, N=-1) == moe.MOE_EINVAL
+    assert _step(p, N=0) == moe.MOE_OK                        # an empty batch is a no-op
+    assert moe.lib().moe_layer_step(None, FAKE, 1, 256, FAKE, None, 1, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None,
+                                    None) == moe.MOE_EINVAL

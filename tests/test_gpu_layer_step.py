@@ -1,0 +1,139 @@
+"""moe_layer_step (route, union, count and the expert step in one call)
+against moe_route_union + moe_expert_forward on the same inputs, bit for bit,
+and against the oracle.
+
+One token takes the routing inside the gate/up GEMV launch; larger batches
+take the two calls' kernels. Counters must accumulate as with the two calls.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import int4_routed_expert_gemv_amd as moe
+import oracle
+import synth
+from tests import layer_cases as lc
+from tests.gpu_layer import run_layer, upload_pool
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _layer_step(pool, x, wr, b, k, counters=None, options=None):
+    N, d = x.shape
+    E = pool.desc.n_experts
+    dev = "cuda"
+    xd = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
+    wrd = torch.from_numpy(np.ascontiguousarray(wr, np.float32)).to(dev)
+    bd = None if b is None else torch.from_numpy(np.ascontiguousarray(b, np.float32)).to(dev)
+    ids = torch.full((N, k), -7, dtype=torch.int32, device=dev)
+    w = torch.full((N, k), -7.0, dtype=torch.float32, device=dev)
+    union_ids = torch.full((E,), -1, dtype=torch.int32, device=dev)
+    n_union = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    offsets = torch.full((E + 1,), -1, dtype=torch.int32, device=dev)
+    perm = torch.full((N * k,), -1, dtype=torch.int32, device=dev)
+    cnt = torch.zeros(E, dtype=torch.int64, device=dev) if counters is None else counters
+    y = torch.full((N, d), float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(moe.layer_step_workspace_size(pool.desc, N, k), 1), dtype=torch.uint8,
+                     device=dev)
+    moe.layer_step(pool.desc, xd, wrd, bd, k, ids, w, union_ids, n_union, offsets, perm, cnt, y,
+                   ws, options=options)
+    torch.cuda.synchronize()
+    nu = int(n_union.item())
+    return dict(ids=ids.cpu().numpy(), w=w.cpu().numpy(), union_ids=union_ids.cpu().numpy()[:nu],
+                n_union=nu, offsets=offsets.cpu().numpy(), perm=perm.cpu().numpy(),
+                counters=cnt.cpu().numpy().astype(np.uint64), y=y.cpu().numpy(), counters_t=cnt)
+
+
+def _compare(cfg, shared=True):
+    spec = cfg.layers[0]
+    x, wr, b, _, _ = lc.layer_inputs(cfg, 0)
+    blocks, sh = lc.canonical_pool(cfg, 0)
+    if not shared:
+        sh = None
+    say(f"[layer_step] {cfg.name} N={cfg.n_tokens} k={cfg.k} d={spec.d} f={spec.f} "
+        f"E={spec.n_experts} wbits={spec.wbits} shared={shared}")
+    ref = oracle.layer_step(x, wr, b, cfg.k, blocks, sh, spec.d, spec.f, spec.wbits, spec.group)
+    pool = upload_pool(spec, blocks, sh)
+    two = run_layer(pool, x, wr, b, cfg.k, fused_route=True)
+    one = _layer_step(pool, x, wr, b, cfg.k)
+    for key in ("ids", "w", "union_ids", "offsets", "perm", "counters", "y"):
+        np.testing.assert_array_equal(one[key], two[key], err_msg=key)
+    assert one["n_union"] == two["n_union"]
+    np.testing.assert_array_equal(one["ids"], ref["ids"])
+    np.testing.assert_array_equal(one["union_ids"], ref["union_ids"])
+    np.testing.assert_array_equal(one["perm"], ref["perm"])
+    np.testing.assert_array_equal(one["counters"], ref["counters"])
+    err = lc.rel_err_rows(one["y"], ref["y"]).max()
+    assert err <= 2e-3, f"max per-token relative error {err:.3e}"
+    # counters accumulate over calls
+    again = _layer_step(pool, x, wr, b, cfg.k, counters=one["counters_t"])
+    np.testing.assert_array_equal(again["counters"], 2 * ref["counters"])
+    np.testing.assert_array_equal(again["y"], one["y"])
+    say(f"[layer_step] equal to the two calls, max rel err {err:.2e}")
+    del pool
+    torch.cuda.empty_cache()
+
+
+def test_decode1():
+    _compare(synth.CONFIGS["decode1"])
+
+
+@pytest.mark.parametrize("k", [2, 8])
+def test_decode_shapes_one_token_topk(k):
+    _compare(dataclasses.replace(synth.CONFIGS["decode1"], k=k))
+
+
+@pytest.mark.parametrize("N,k,shared", [(1, 1, True), (1, 1, False), (1, 2, False), (1, 5, True),
+                                        (1, 16, True), (2, 3, True), (4, 8, True),
+                                        (40, 4, True)])
+def test_tiny(N, k, shared):
+    _compare(dataclasses.replace(synth.CONFIGS["tiny"], n_tokens=N, k=k), shared=shared)
+
+
+@pytest.mark.parametrize("E,k", [(1000, 32), (1024, 7), (65, 3)])
+def test_one_token_many_experts(E, k):
+    base = synth.CONFIGS["tiny"]
+    cfg = dataclasses.replace(base, n_tokens=1, k=k,
+                              layers=(dataclasses.replace(base.layer, n_experts=E),))
+    _compare(cfg)
+
+
+def test_one_token_int8():
+    base = synth.CONFIGS["tiny"]
+    spec = dataclasses.replace(base.layer, wbits=8, group=0, scale_lo=0.005 / 16,
+                               scale_hi=0.02 / 16)
+    _compare(dataclasses.replace(base, n_tokens=1, k=3, layers=(spec,)))
+
+
+@pytest.mark.parametrize("big,small", [(1, -1), (-1, 1), (-1, -1)])
+def test_one_token_with_thresholds(big, small):
+    """Options: a positive threshold puts the one token on a matrix-core pass
+    (the two calls' kernels), -1 on both keeps the routing inside the gate/up
+    launch; each equals moe_expert_forward_ex with the same thresholds."""
+    cfg = dataclasses.replace(synth.CONFIGS["tiny"], n_tokens=1, k=3)
+    spec = cfg.layers[0]
+    x, wr, b, _, _ = lc.layer_inputs(cfg, 0)
+    blocks, sh = lc.canonical_pool(cfg, 0)
+    say(f"[layer_step] thresholds big={big} small={small}")
+    ref = oracle.layer_step(x, wr, b, cfg.k, blocks, sh, spec.d, spec.f, spec.wbits, spec.group)
+    pool = upload_pool(spec, blocks, sh)
+    opts = moe.ForwardOptions()
+    opts.mfma_min_tokens = big
+    opts.mfma_small_min_tokens = small
+    one = _layer_step(pool, x, wr, b, cfg.k, options=opts)
+    two = run_layer(pool, x, wr, b, cfg.k, fused_route=True, mfma_min_tokens=big,
+                    mfma_small_min_tokens=small)
+    for key in ("ids", "w", "union_ids", "offsets", "perm", "counters", "y"):
+        np.testing.assert_array_equal(one[key], two[key], err_msg=key)
+    np.testing.assert_array_equal(one["ids"], ref["ids"])
+    assert lc.rel_err_rows(one["y"], ref["y"]).max() <= 2e-3
+    del pool
+    torch.cuda.empty_cache()
