@@ -61,3 +61,31 @@ def run_layer(pool, x, wr, b, k, ids_in=None, w_in=None, counters=None, device="
     return dict(ids=ids.cpu().numpy(), w=w.cpu().numpy(), union_ids=union_ids.cpu().numpy()[:nu],
                 n_union=nu, offsets=offsets.cpu().numpy(), perm=perm.cpu().numpy(),
                 counters=cnt.cpu().numpy().astype(np.uint64), y=y.cpu().numpy(), counters_t=cnt)
+
+
+def run_layer_step(pool, x, wr, b, k, counters=None, options=None, device="cuda"):
+    """moe_layer_step on fresh output buffers (filled with values the call
+    must overwrite); returns the results as numpy arrays."""
+    N, d = x.shape
+    E = pool.desc.n_experts
+    dev = device
+    xd = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
+    wrd = torch.from_numpy(np.ascontiguousarray(wr, np.float32)).to(dev)
+    bd = None if b is None else torch.from_numpy(np.ascontiguousarray(b, np.float32)).to(dev)
+    ids = torch.full((N, k), -7, dtype=torch.int32, device=dev)
+    w = torch.full((N, k), -7.0, dtype=torch.float32, device=dev)
+    union_ids = torch.full((E,), -1, dtype=torch.int32, device=dev)
+    n_union = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    offsets = torch.full((E + 1,), -1, dtype=torch.int32, device=dev)
+    perm = torch.full((N * k,), -1, dtype=torch.int32, device=dev)
+    cnt = torch.zeros(E, dtype=torch.int64, device=dev) if counters is None else counters
+    y = torch.full((N, d), float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(moe.layer_step_workspace_size(pool.desc, N, k), 1), dtype=torch.uint8,
+                     device=dev)
+    moe.layer_step(pool.desc, xd, wrd, bd, k, ids, w, union_ids, n_union, offsets, perm, cnt, y,
+                   ws, options=options)
+    torch.cuda.synchronize()
+    nu = int(n_union.item())
+    return dict(ids=ids.cpu().numpy(), w=w.cpu().numpy(), union_ids=union_ids.cpu().numpy()[:nu],
+                n_union=nu, offsets=offsets.cpu().numpy(), perm=perm.cpu().numpy(),
+                counters=cnt.cpu().numpy().astype(np.uint64), y=y.cpu().numpy(), counters_t=cnt)

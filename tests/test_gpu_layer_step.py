@@ -16,7 +16,7 @@ import int4_routed_expert_gemv_amd as moe
 import oracle
 import synth
 from tests import layer_cases as lc
-from tests.gpu_layer import run_layer, upload_pool
+from tests.gpu_layer import run_layer, run_layer_step, upload_pool
 
 pytestmark = pytest.mark.gpu
 
@@ -24,32 +24,6 @@ pytestmark = pytest.mark.gpu
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
-
-
-def _layer_step(pool, x, wr, b, k, counters=None, options=None):
-    N, d = x.shape
-    E = pool.desc.n_experts
-    dev = "cuda"
-    xd = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
-    wrd = torch.from_numpy(np.ascontiguousarray(wr, np.float32)).to(dev)
-    bd = None if b is None else torch.from_numpy(np.ascontiguousarray(b, np.float32)).to(dev)
-    ids = torch.full((N, k), -7, dtype=torch.int32, device=dev)
-    w = torch.full((N, k), -7.0, dtype=torch.float32, device=dev)
-    union_ids = torch.full((E,), -1, dtype=torch.int32, device=dev)
-    n_union = torch.full((1,), -1, dtype=torch.int32, device=dev)
-    offsets = torch.full((E + 1,), -1, dtype=torch.int32, device=dev)
-    perm = torch.full((N * k,), -1, dtype=torch.int32, device=dev)
-    cnt = torch.zeros(E, dtype=torch.int64, device=dev) if counters is None else counters
-    y = torch.full((N, d), float("nan"), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(moe.layer_step_workspace_size(pool.desc, N, k), 1), dtype=torch.uint8,
-                     device=dev)
-    moe.layer_step(pool.desc, xd, wrd, bd, k, ids, w, union_ids, n_union, offsets, perm, cnt, y,
-                   ws, options=options)
-    torch.cuda.synchronize()
-    nu = int(n_union.item())
-    return dict(ids=ids.cpu().numpy(), w=w.cpu().numpy(), union_ids=union_ids.cpu().numpy()[:nu],
-                n_union=nu, offsets=offsets.cpu().numpy(), perm=perm.cpu().numpy(),
-                counters=cnt.cpu().numpy().astype(np.uint64), y=y.cpu().numpy(), counters_t=cnt)
 
 
 def _compare(cfg, shared=True):
@@ -63,7 +37,7 @@ def _compare(cfg, shared=True):
     ref = oracle.layer_step(x, wr, b, cfg.k, blocks, sh, spec.d, spec.f, spec.wbits, spec.group)
     pool = upload_pool(spec, blocks, sh)
     two = run_layer(pool, x, wr, b, cfg.k, fused_route=True)
-    one = _layer_step(pool, x, wr, b, cfg.k)
+    one = run_layer_step(pool, x, wr, b, cfg.k)
     for key in ("ids", "w", "union_ids", "offsets", "perm", "counters", "y"):
         np.testing.assert_array_equal(one[key], two[key], err_msg=key)
     assert one["n_union"] == two["n_union"]
@@ -74,7 +48,7 @@ def _compare(cfg, shared=True):
     err = lc.rel_err_rows(one["y"], ref["y"]).max()
     assert err <= 2e-3, f"max per-token relative error {err:.3e}"
     # counters accumulate over calls
-    again = _layer_step(pool, x, wr, b, cfg.k, counters=one["counters_t"])
+    again = run_layer_step(pool, x, wr, b, cfg.k, counters=one["counters_t"])
     np.testing.assert_array_equal(again["counters"], 2 * ref["counters"])
     np.testing.assert_array_equal(again["y"], one["y"])
     say(f"[layer_step] equal to the two calls, max rel err {err:.2e}")
@@ -128,7 +102,7 @@ def test_one_token_with_thresholds(big, small):
     opts = moe.ForwardOptions()
     opts.mfma_min_tokens = big
     opts.mfma_small_min_tokens = small
-    one = _layer_step(pool, x, wr, b, cfg.k, options=opts)
+    one = run_layer_step(pool, x, wr, b, cfg.k, options=opts)
     two = run_layer(pool, x, wr, b, cfg.k, fused_route=True, mfma_min_tokens=big,
                     mfma_small_min_tokens=small)
     for key in ("ids", "w", "union_ids", "offsets", "perm", "counters", "y"):
