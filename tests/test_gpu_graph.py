@@ -1,5 +1,5 @@
-"""The layer step (moe_route_union + moe_expert_forward) captured in a HIP
-graph and replayed.
+"""The layer step (moe_route_union + moe_expert_forward, or moe_layer_step)
+captured in a HIP graph and replayed.
 
 Every entry point enqueues kernels on the caller's stream and nothing else (no
 allocation, no memset, no host synchronisation), so a serving loop can capture
@@ -20,7 +20,7 @@ import int4_routed_expert_gemv_amd as moe
 import oracle
 import synth
 from tests import layer_cases as lc
-from tests.gpu_layer import upload_pool, workspace
+from tests.gpu_layer import upload_pool
 
 pytestmark = pytest.mark.gpu
 
@@ -44,11 +44,21 @@ def _buffers(N, k, d, E):
     )
 
 
-def _step(pool, xd, wrd, bd, k, t, ws, opts):
+def _step(pool, xd, wrd, bd, k, t, ws, opts, one_call=False):
+    if one_call:
+        moe.layer_step(pool.desc, xd, wrd, bd, k, t["ids"], t["w"], t["union_ids"], t["n_union"],
+                       t["offsets"], t["perm"], t["cnt"], t["y"], ws, options=opts)
+        return
     moe.route_union(xd, wrd, bd, k, t["ids"], t["w"], t["union_ids"], t["n_union"],
                     t["offsets"], t["perm"], t["cnt"], ws)
     moe.expert_forward(pool.desc, xd, k, t["w"], t["union_ids"], t["n_union"], t["offsets"],
                        t["perm"], t["y"], ws, options=opts)
+
+
+def _ws(pool, N, k):
+    # large enough for both forms of the step
+    n = max(moe.workspace_size(pool.desc, N, k), moe.layer_step_workspace_size(pool.desc, N, k))
+    return torch.empty(n, dtype=torch.uint8, device="cuda")
 
 
 def _snapshot(t):
@@ -76,12 +86,15 @@ def _case(name, n_tokens=None, k=None):
 # 32-token pass), 300 tokens top-4 over 16 experts with every expert on the
 # 128-token pass, and 20 tokens top-8 (the router's workgroup-tiled path and
 # the separate union kernel) with the default passes
-CASES = [("decode1", None, None, None), ("decode64", None, None, None), ("tiny", 300, 4, 1),
-         ("tiny", 20, 8, None)]
+CASES = [("decode1", None, None, None, False), ("decode64", None, None, None, False),
+         ("tiny", 300, 4, 1, False), ("tiny", 20, 8, None, False),
+         # moe_layer_step: one token (routing inside the gate/up launch), 20 tokens
+         ("decode1", None, None, None, True), ("tiny", 1, 4, None, True),
+         ("tiny", 20, 8, None, True)]
 
 
-@pytest.mark.parametrize("name,n_tokens,k,big", CASES)
-def test_graph_replay_equals_eager(name, n_tokens, k, big):
+@pytest.mark.parametrize("name,n_tokens,k,big,one_call", CASES)
+def test_graph_replay_equals_eager(name, n_tokens, k, big, one_call):
     cfg = _case(name, n_tokens, k)
     opts = None
     if big is not None:
@@ -90,7 +103,8 @@ def test_graph_replay_equals_eager(name, n_tokens, k, big):
         opts.mfma_small_min_tokens = -1
     spec = cfg.layers[0]
     N, k, d, E = cfg.n_tokens, cfg.k, spec.d, spec.n_experts
-    say(f"[graph] {name} N={N} k={k} d={d} f={spec.f} E={E} mfma_min_tokens={big}")
+    say(f"[graph] {name} N={N} k={k} d={d} f={spec.f} E={E} mfma_min_tokens={big} "
+        f"one_call={one_call}")
     x0, wr, b, _, _ = lc.layer_inputs(cfg, 0)
     blocks, shared = lc.canonical_pool(cfg, 0)
     ref = oracle.layer_step(x0, wr, b, k, blocks, shared, spec.d, spec.f, spec.wbits, spec.group)
@@ -104,24 +118,24 @@ def test_graph_replay_equals_eager(name, n_tokens, k, big):
     eager = []
     for xv in xs:
         t = _buffers(N, k, d, E)
-        _step(pool, xv, wrd, bd, k, t, workspace(pool, N, k), opts)
+        _step(pool, xv, wrd, bd, k, t, _ws(pool, N, k), opts, one_call)
         torch.cuda.synchronize()
         eager.append(_snapshot(t))
 
     # capture one step on static buffers
     st = _buffers(N, k, d, E)
-    ws = workspace(pool, N, k)
+    ws = _ws(pool, N, k)
     xd = xs[0].clone()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        _step(pool, xd, wrd, bd, k, st, ws, opts)
+        _step(pool, xd, wrd, bd, k, st, ws, opts, one_call)
     torch.cuda.synchronize()
     st["cnt"].zero_()
 
     order = [0, 1, 0, 1, 1]
     other = _buffers(N, k, d, E)
-    other_ws = workspace(pool, N, k)
+    other_ws = _ws(pool, N, k)
     for r, i in enumerate(order):
         xd.copy_(xs[i])
         g.replay()
@@ -134,7 +148,7 @@ def test_graph_replay_equals_eager(name, n_tokens, k, big):
             err = lc.rel_err_rows(got["y"], ref["y"]).max()
             assert err <= 2e-3, f"max per-token relative error {err:.3e}"
         # eager work of the program between replays, on other buffers
-        _step(pool, xs[1 - i], wrd, bd, k, other, other_ws, opts)
+        _step(pool, xs[1 - i], wrd, bd, k, other, other_ws, opts, one_call)
         torch.cuda.synchronize()
         _same(_snapshot(other), eager[1 - i])
         say(f"[graph] {name} replay {r} (batch {i}) equals the eager step")
