@@ -328,16 +328,21 @@ moe_status moe_residual_rmsnorm(float *h, const float *y, float *a, int n_tokens
  * sigmoid, no options) followed by moe_expert_forward, with the same
  * arguments, checks (all made before anything is enqueued) and outputs, bit
  * for bit; d_model must equal pool->d_model and the router has
- * pool->n_experts rows. counters may be NULL. For one token the top-k, union,
- * permutation and counting run inside the gate/up GEMV launch: every
- * workgroup of a routed expert takes the top-k of the router's scores itself
- * and workgroup 0 writes the routing outputs, so a decode step is three
- * launches (router, gate/up, down) instead of four. workspace: at least
+ * pool->n_experts rows. counters may be NULL. For one or two tokens with
+ * k <= 2 whose experts all stay on the GEMV pass (the default thresholds),
+ * the top-k, union, permutation and counting run inside the gate/up GEMV
+ * launch: every workgroup of a routed expert takes the top-k of the router's
+ * scores itself and workgroup 0 writes the routing outputs, so a decode step
+ * is three launches (router, gate/up, down; a combine after them when an
+ * output row has more than two terms) instead of four or five. At larger k
+ * the argmax rounds every workgroup would run cost more than the launch they
+ * save, and the two calls' kernels run. workspace: at least
  * moe_layer_step_workspace_size(pool, n_tokens, k) bytes, 256-byte aligned
  * (the router's output, then the expert step's workspace); its contents
  * afterwards are unspecified. opt (host, may be NULL): as for
  * moe_expert_forward_ex (events around the expert kernels, pass thresholds);
- * a positive threshold makes a one-token step take the two calls' kernels.
+ * a threshold that moves an expert to the matrix cores makes the step take
+ * the two calls' kernels.
  * Colibri pages: "Exact Architecture and Data-Flow Reconstruction", stages
  * (1) Route, (2) Union and (5) Learn, and the three-matrix expert MLP with
  * the always-on shared expert.

@@ -571,6 +571,11 @@ moe_status moe_expert_forward_ex(const moe_expert_pool *pool, const float *x, in
                         workspace, ws_bytes, stream, ev, false, nullptr);
 }
 
+// moe_layer_step takes the routing inside the gate/up launch up to this k:
+// every workgroup of a routed expert pays k argmax rounds before its weight
+// loads, which outweighs the route-tail launch it saves at larger k.
+constexpr int kInsideMaxK = 2;
+
 size_t moe_layer_step_workspace_size(const moe_expert_pool *pool, int n_tokens, int k)
 {
     if (!pool) return 0;
@@ -610,9 +615,15 @@ moe_status moe_layer_step(const moe_expert_pool *pool, const float *x, int n_tok
     st = forward_impl(pool, x, n_tokens, k, topk_w, union_ids, n_union, expert_offsets, perm, y,
                       fws, fbytes, stream, opt, true, nullptr);
     if (st != MOE_OK || n_tokens == 0) return st;
-    // a positive threshold can put a single token on the matrix cores
-    const bool gemv_only = !opt || (opt->mfma_min_tokens <= 0 && opt->mfma_small_min_tokens <= 0);
-    if (n_tokens != 1 || !gemv_only) {
+    // Up to two tokens whose experts all stay on the GEMV with one item per
+    // expert (a positive threshold can move them to the matrix cores) take
+    // the routing inside the gate/up launch.
+    const FwdLayout L = fwd_layout(g, n_tokens, k, pool->shared != nullptr,
+                                   opt ? opt->mfma_min_tokens : 0,
+                                   opt ? opt->mfma_small_min_tokens : 0);
+    const bool inside = n_tokens <= 2 && k <= kInsideMaxK && L.max_mitems == 0 &&
+                        L.max_sitems == 0 && n_tokens <= L.tb;
+    if (!inside) {
         st = route_union_impl(x, n_tokens, d_model, w_router, b_router, pool->n_experts, k,
                               topk_ids, topk_w, union_ids, n_union, expert_offsets, perm,
                               counters, workspace, rs, stream, nullptr, RouteMode::all, nullptr,
@@ -621,8 +632,8 @@ moe_status moe_layer_step(const moe_expert_pool *pool, const float *x, int n_tok
         return forward_impl(pool, x, n_tokens, k, topk_w, union_ids, n_union, expert_offsets,
                             perm, y, fws, fbytes, stream, opt, false, nullptr);
     }
-    // one token: the router, then the expert kernels, the top-k, union and
-    // counting taken inside the gate/up GEMV launch
+    // the router, then the expert kernels, the top-k, union and counting
+    // taken inside the gate/up GEMV launch
     InRoute ir;
     ir.scores = static_cast<const float *>(workspace);
     ir.ids = topk_ids;

@@ -251,13 +251,16 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
     constexpr int UC = 4 * EPC;              // columns per unit
     constexpr int NM = GATEUP ? 2 : 1;       // gate and up, or down
     constexpr int TPW = NW / KS;             // unit rows per workgroup
+    static_assert(!GATEUP || NW >= 2, "routing inside takes a wave per token, two tokens");
 
     extern __shared__ uint4 lds_x[];         // [TB][XQ][NCH] staged activations
     __shared__ Item s_item;
     __shared__ int s_expert;
     __shared__ float red[NW][TB][NM][kUnitRows];
-    __shared__ int32_t s_rt_lds[MOE_MAX_K], s_rt_ids[MOE_MAX_K];  // routing inside (one token)
-    __shared__ float s_rt_w[MOE_MAX_K];
+    // routing inside (one or two tokens)
+    __shared__ int32_t s_rt_lds[2 * MOE_MAX_K], s_rt_ids[2 * MOE_MAX_K];
+    __shared__ float s_rt_w[2 * MOE_MAX_K];
+    __shared__ int s_rt_tok[2];  // tokens of this item, in assignment order
 
     const Fwd &f = ga.f;
     const Geo &g = f.g;
@@ -278,49 +281,85 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
     Item it;
     bool resolved = true;
     if (GATEUP && ga.plan_here == 2 && f.route_in) {
-        // one token, routed here: every workgroup of a routed item takes the
-        // top-k of the router's output (the same code and inputs as the route
-        // tail, so the same ids); union slot j holds the j-th smallest id.
-        // Workgroup 0 also writes the routing outputs for the down kernel and
-        // the caller (an extra workgroup doing only that measured slower).
+        // one or two tokens, routed here: every workgroup of a routed item
+        // takes the top-k of the router's output (a wave per token; the same
+        // code and inputs as the route tail, so the same ids). Union slot u
+        // holds the u-th smallest distinct id; the permutation is the stable
+        // sort of the assignments by id. Workgroup 0 also writes the routing
+        // outputs for the down kernel and the caller (an extra workgroup
+        // doing only that measured slower).
         const int nsh = f.has_shared ? 1 : 0;
         const bool writer = blockIdx.x == 0;
         const bool route = writer || item_idx >= nsh;
-        resolved = false;
-        if (tid == 0) s_expert = item_idx < nsh ? -1 : -2;
-        if (wave == 0 && route)
-            topk_wave<false>(f.route_in, f.route_P, f.route_b, 1, g.E, f.k, 0,
+        const int A = f.A;  // at most 2 * MOE_MAX_K = 64 assignments: one per lane
+        if (tid == 0) {
+            Item none;
+            none.expert = -2;
+            none.p0 = 0;
+            none.count = 0;
+            none.pad = 0;
+            s_item = none;
+        }
+        if (route && wave < f.N)
+            topk_wave<false>(f.route_in, f.route_P, f.route_b, f.N, g.E, f.k, wave,
                              writer ? f.route_ids : s_rt_ids, writer ? f.route_w : s_rt_w,
                              s_rt_lds);
         __syncthreads();
         if (wave == 0 && route) {
-            const int k = f.k;
-            const int id = lane < k ? s_rt_lds[lane] : 0x7FFFFFFF;
-            int r = 0;  // rank of this lane's id among the k (distinct) ids
-            for (int i = 0; i < k; ++i) r += s_rt_lds[i] < id ? 1 : 0;
-            if (lane < k) {
-                if (item_idx - nsh == r) s_expert = id;
-                if (writer) {
-                    const_cast<int32_t *>(f.union_ids)[r] = id;
-                    const_cast<int32_t *>(f.perm)[r] = lane;
-                    if (f.route_counters) atomicAdd(&f.route_counters[id], 1ull);
-                }
+            const int id = lane < A ? s_rt_lds[lane] : 0x7FFFFFFF;
+            int lt = 0, cnt = 0, before = 0;  // ids below, equal ids, equal ids of lower lanes
+            for (int b = 0; b < A; ++b) {
+                const int o = s_rt_lds[b];
+                lt += o < id ? 1 : 0;
+                cnt += o == id ? 1 : 0;
+                before += (o == id && b < lane) ? 1 : 0;
+            }
+            const bool first = lane < A && before == 0;
+            const unsigned long long fm = __ballot(first);
+            int u = 0;  // distinct ids below this one
+            for (int b = 0; b < A; ++b)
+                u += (((fm >> b) & 1ull) && s_rt_lds[b] < id) ? 1 : 0;
+            // the permutation is written in this launch: the item's tokens
+            // come from LDS (at most two occurrences of an id, one per token)
+            if (lane < A && item_idx - nsh == u) s_rt_tok[before] = lane / f.k;
+            if (first && item_idx - nsh == u) {
+                Item r;
+                r.expert = id;
+                r.p0 = lt;
+                r.count = cnt;
+                r.pad = 0;
+                s_item = r;
             }
             if (writer) {
+                if (lane < A) const_cast<int32_t *>(f.perm)[lt + before] = lane;
+                if (first) {
+                    const_cast<int32_t *>(f.union_ids)[u] = id;
+                    if (f.route_counters)
+                        atomicAdd(&f.route_counters[id], (unsigned long long)cnt);
+                }
                 for (int e = lane; e <= g.E; e += kWave) {
                     int c = 0;
-                    for (int i = 0; i < k; ++i) c += s_rt_lds[i] < e ? 1 : 0;
+                    for (int b = 0; b < A; ++b) c += s_rt_lds[b] < e ? 1 : 0;
                     const_cast<int32_t *>(f.offsets)[e] = c;
                 }
                 if (lane == 0) {
-                    *const_cast<int32_t *>(f.n_union) = k;
-                    *f.n_items = nsh + k;
+                    *const_cast<int32_t *>(f.n_union) = __popcll(fm);
+                    *f.n_items = nsh + __popcll(fm);
                 }
             }
         }
         __syncthreads();
-        expert = s_expert;
-        if (expert == -2) return;  // beyond the union: uniform exit
+        if (item_idx < nsh) {
+            it.expert = -1;
+            it.p0 = f.A;
+            it.count = f.N;
+            it.pad = 0;
+        } else {
+            it = s_item;
+            if (it.expert == -2) return;  // beyond the union: uniform exit
+        }
+        expert = it.expert;
+        if (wg == 0 && tid == 0) f.items[item_idx] = it;
     } else if (GATEUP && ga.plan_here == 2) {
         // every expert has at most n_tokens <= TB tokens: one item per union
         // slot, after the shared expert's single item
@@ -453,8 +492,12 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
             r = (size_t)p;
         else if (it.expert < 0)
             r = (size_t)(p - f.A);
+        else if (f.N == 1)
+            r = 0;
+        else if (f.route_in)  // routing inside: the permutation is still being written
+            r = (size_t)s_rt_tok[i];
         else  // values read from the permutation are clamped into range
-            r = f.N == 1 ? 0 : (size_t)(min(max(f.perm[p], 0), f.A - 1) / f.k);
+            r = (size_t)(min(max(f.perm[p], 0), f.A - 1) / f.k);
         return in + r * K + (size_t)c * EPC;
     };
     constexpr int PRE = pre_rounds(TB);
@@ -841,7 +884,7 @@ hipError_t launch_gateup(const Fwd &f, hipStream_t s)
     a.plan_here = max_union <= kWave && f.max_mitems == 0 && f.max_sitems == 0
                       ? (f.N <= f.tb ? 2 : 1)
                       : 0;
-    if (f.route_in && (a.plan_here != 2 || f.N != 1)) return hipErrorInvalidValue;
+    if (f.route_in && (a.plan_here != 2 || f.N > 2)) return hipErrorInvalidValue;
     if (!a.plan_here) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, f);
         const hipError_t e = hipGetLastError();

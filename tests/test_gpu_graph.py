@@ -88,9 +88,10 @@ def _case(name, n_tokens=None, k=None):
 # the separate union kernel) with the default passes
 CASES = [("decode1", None, None, None, False), ("decode64", None, None, None, False),
          ("tiny", 300, 4, 1, False), ("tiny", 20, 8, None, False),
-         # moe_layer_step: one token (routing inside the gate/up launch), 20 tokens
+         # moe_layer_step: one and two tokens (routing inside the gate/up
+         # launch), 20 tokens
          ("decode1", None, None, None, True), ("tiny", 1, 4, None, True),
-         ("tiny", 20, 8, None, True)]
+         ("tiny", 2, 8, None, True), ("tiny", 20, 8, None, True)]
 
 
 @pytest.mark.parametrize("name,n_tokens,k,big,one_call", CASES)

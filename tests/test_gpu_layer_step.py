@@ -2,8 +2,8 @@
 against moe_route_union + moe_expert_forward on the same inputs, bit for bit,
 and against the oracle.
 
-One token takes the routing inside the gate/up GEMV launch; larger batches
-take the two calls' kernels. Counters must accumulate as with the two calls.
+One or two tokens take the routing inside the gate/up GEMV launch; larger
+batches take the two calls' kernels. Counters must accumulate as with the two calls.
 """
 import dataclasses
 import sys
@@ -65,26 +65,37 @@ def test_decode_shapes_one_token_topk(k):
     _compare(dataclasses.replace(synth.CONFIGS["decode1"], k=k))
 
 
+@pytest.mark.parametrize("k", [1, 8])
+def test_decode_shapes_two_tokens(k):
+    """A two-token verify batch on the decode layer's shapes (Zipf router
+    bias, so the two tokens share experts): routing inside the gate/up
+    launch with items of one and two tokens."""
+    _compare(dataclasses.replace(synth.CONFIGS["decode64"], n_tokens=2, k=k))
+
+
 @pytest.mark.parametrize("N,k,shared", [(1, 1, True), (1, 1, False), (1, 2, False), (1, 5, True),
-                                        (1, 16, True), (2, 3, True), (4, 8, True),
-                                        (40, 4, True)])
+                                        (1, 16, True), (2, 1, True), (2, 1, False), (2, 2, False),
+                                        (2, 3, True), (2, 8, True), (2, 16, False), (3, 2, True),
+                                        (4, 8, True), (40, 4, True)])
 def test_tiny(N, k, shared):
     _compare(dataclasses.replace(synth.CONFIGS["tiny"], n_tokens=N, k=k), shared=shared)
 
 
-@pytest.mark.parametrize("E,k", [(1000, 32), (1024, 7), (65, 3)])
-def test_one_token_many_experts(E, k):
+@pytest.mark.parametrize("E,k,N", [(1000, 32, 1), (1024, 7, 1), (65, 3, 1), (1000, 32, 2),
+                                   (65, 5, 2)])
+def test_one_token_many_experts(E, k, N):
     base = synth.CONFIGS["tiny"]
-    cfg = dataclasses.replace(base, n_tokens=1, k=k,
+    cfg = dataclasses.replace(base, n_tokens=N, k=k,
                               layers=(dataclasses.replace(base.layer, n_experts=E),))
     _compare(cfg)
 
 
-def test_one_token_int8():
+@pytest.mark.parametrize("N", [1, 2])
+def test_one_token_int8(N):
     base = synth.CONFIGS["tiny"]
     spec = dataclasses.replace(base.layer, wbits=8, group=0, scale_lo=0.005 / 16,
                                scale_hi=0.02 / 16)
-    _compare(dataclasses.replace(base, n_tokens=1, k=3, layers=(spec,)))
+    _compare(dataclasses.replace(base, n_tokens=N, k=3, layers=(spec,)))
 
 
 @pytest.mark.parametrize("big,small", [(1, -1), (-1, 1), (-1, -1)])
