@@ -724,7 +724,7 @@ def measured_ceiling(moe, hip, torch, bound, bytes_per_launch, achieved):
     a loop of independent float16 MFMA products (moe_probe_mfma_f16). Timed
     with HIP events taken by the probe launches themselves."""
     import numpy as np
-    L = moe.lib()
+    L = moe.probe_lib()
     vp = ctypes.c_void_p
     stream = vp(torch.cuda.current_stream().cuda_stream)
     ev = [hip.event() for _ in range(2)]

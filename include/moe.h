@@ -38,13 +38,25 @@
  *     synchronisation. After an error the outputs are unspecified.
  *   - n_tokens == 0 is a successful no-op.
  *   - Row-major layouts throughout. x is [n_tokens][d_model] float32.
- *   - The activations are staged through float16 inside the expert kernels.
- *     The GEMV kernels first scale each run of 32 (int4) or 16 (int8)
- *     consecutive values by the power of two that brings its largest
- *     magnitude into [2^13, 2^14); the matrix-core kernels convert x and the
- *     hidden values without scaling. Inputs must be finite, and |x| and every
- *     hidden value |silu(g) * u| must stay below 65504, which holds with a
- *     wide margin for normalised activations.
+ *   - Arithmetic of the expert kernels (routing, SiLU and the combine are
+ *     float32 throughout):
+ *       GEMV pass (experts with one or a few tokens): each run of 32 (int4)
+ *       or 16 (int8) consecutive activations is scaled by the power of two
+ *       that brings its largest magnitude into [2^13, 2^14) and rounded to a
+ *       16-bit integer; the products with the codes are exact integer dot
+ *       products (v_dot8c_i32_i4 on four base-16 digit planes, or
+ *       v_dot4c_i32_i8 on two base-256 planes), scaled in float32 per run.
+ *       Matrix-core passes (groups of tokens): x and the hidden values are
+ *       rounded to float16, unscaled, and multiplied with float16 codes on
+ *       v_mfma_f32_16x16x32_f16 with float32 accumulation. The group scale is
+ *       applied to the float32 products of each 128-column step when the
+ *       scale groups cover whole 128-column units (G == 0 or a multiple of
+ *       128); otherwise (and on the 128-token pass) code * scale is rounded
+ *       to float16 before the product, so such scales must be normal float16
+ *       values (2^-14 <= scale <= 65504; the host does not check this).
+ *     Inputs must be finite, and |x| and every hidden value |silu(g) * u|
+ *     must stay below 65504, which holds with a wide margin for normalised
+ *     activations.
  */
 #ifndef MOE_H
 #define MOE_H

@@ -21,6 +21,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# measurement probes (include/moe_probe.h): a library of their own, loaded by
+# the benchmark only
+PROBE_LIB_PATH = os.path.join(_HERE, "libmoe_probe.so")
 
 MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP, MOE_EIO = (
     0, -1, -2, -3, -4, -5, -6)
@@ -119,8 +122,6 @@ def lib():
         L.moe_workspace_size.argtypes = [P, i32, i32]
         L.moe_block_bytes.argtypes = [i32, i32, i32, i32]
         L.moe_pack_expert.argtypes = [vp, P, vp]
-        L.moe_probe_stream_read.argtypes = [vp, sz, i32, i32, vp, sz, vp, vp, vp]
-        L.moe_probe_mfma_f16.argtypes = [vp, i32, i32, vp, vp, vp]
         L.moe_cache_create.argtypes = [i32, i32, sz, sz, vp, vp, vp, ctypes.POINTER(vp)]
         L.moe_cache_create.restype = i32
         L.moe_cache_destroy.argtypes = [vp]
@@ -145,13 +146,34 @@ def lib():
         for name in ("moe_route_topk", "moe_route_topk_ex", "moe_union", "moe_route_union",
                      "moe_route_union_ex", "moe_expert_forward",
                      "moe_expert_forward_ex", "moe_hit_count", "moe_layer_step",
-                     "moe_residual_rmsnorm", "moe_pack_expert", *PROBE_EXPORTED):
+                     "moe_residual_rmsnorm", "moe_pack_expert"):
             getattr(L, name).restype = i32
         for name in ("moe_route_workspace_size", "moe_forward_workspace_size",
                      "moe_workspace_size", "moe_layer_step_workspace_size", "moe_block_bytes"):
             getattr(L, name).restype = sz
         _lib = L
     return _lib
+
+
+_probe_lib = None
+
+
+def probe_lib():
+    """The loaded libmoe_probe.so: measured ceilings of the GPU (a streaming
+    read, a loop of matrix-core products), not part of the layer step."""
+    global _probe_lib
+    if _probe_lib is None:
+        if not os.path.exists(PROBE_LIB_PATH):
+            raise ImportError(f"{PROBE_LIB_PATH} is missing: build it with "
+                              "`python -m int4_routed_expert_gemv_amd.build`")
+        L = ctypes.CDLL(PROBE_LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.moe_probe_stream_read.argtypes = [vp, sz, i32, i32, vp, sz, vp, vp, vp]
+        L.moe_probe_mfma_f16.argtypes = [vp, i32, i32, vp, vp, vp]
+        for name in PROBE_EXPORTED:
+            getattr(L, name).restype = i32
+        _probe_lib = L
+    return _probe_lib
 
 
 def strerror(status: int) -> str:

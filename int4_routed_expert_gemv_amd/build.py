@@ -1,4 +1,6 @@
-"""Builds libmoe.so (the HIP library behind include/moe.h) for gfx950, in-tree."""
+"""Builds, in-tree for gfx950, libmoe.so (the HIP library behind include/moe.h
+and include/moe_cache.h) and libmoe_probe.so (the measurement probes of
+include/moe_probe.h, loaded by the benchmark only)."""
 import glob
 import os
 import subprocess
@@ -8,6 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
+PROBE_DIR = os.path.join(HERE, "probe")
+PROBE_LIB = os.path.join(HERE, "libmoe_probe.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -20,27 +24,34 @@ FLAGS = [
 ]
 
 
-def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+def sources(folder=CSRC):
+    return sorted(glob.glob(os.path.join(folder, "*.hip")))
 
 
 def build(jobs: int = 8, verbose: bool = False) -> str:
+    """Compiles every source (all at once, up to `jobs` in parallel), then
+    links the product library and the probe library."""
     os.makedirs(OBJ_DIR, exist_ok=True)
-    procs, objs = [], []
-    for src in sources():
-        obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-        objs.append(obj)
-        cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
-        if len(procs) >= jobs:
-            _wait(procs.pop(0))
+    procs = []
+    libs = {LIB: [], PROBE_LIB: []}
+    for lib, folder in ((LIB, CSRC), (PROBE_LIB, PROBE_DIR)):
+        for src in sources(folder):
+            obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+            libs[lib].append(obj)
+            cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                stderr=subprocess.STDOUT)))
+            if len(procs) >= jobs:
+                _wait(procs.pop(0))
     for p in procs:
         _wait(p)
-    tmp = LIB + ".tmp"
-    subprocess.check_call([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
+    for lib, objs in libs.items():
+        tmp = lib + ".tmp"
+        subprocess.check_call([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs,
+                               "-o", tmp])
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -229,15 +229,17 @@ __device__ int find_item(const Fwd &f, int item_idx, Item *out)
     return nsh + __builtin_amdgcn_readlane(incl, kWave - 1);
 }
 
-// One workgroup (4 waves) computes 4/KS unit rows (16 output rows each) of
+// One workgroup (NW waves) computes NW/KS unit rows (16 output rows each) of
 // one work item: up to TB tokens of one expert. KS waves share a unit row,
 // each taking every KS-th unit along it. The item's activations are staged
-// once in LDS (float16, each chunk scaled by a power of two, in the order the
-// dot product consumes them). Each lane reads one 16-byte slot per unit (a
-// wave reads the whole 1 KB unit), turns its 32 (int4) or 16 (int8) codes
-// into float16 pairs once and takes dot products with every token's chunk.
-// Partial sums are added over the four lanes of a row with lane shuffles and
-// over the KS waves of a unit row in LDS, always in the same order.
+// once in LDS as integer digit planes (each chunk scaled by a power of two
+// and rounded to 16 bits, in the order the dot product consumes them). Each
+// lane reads one 16-byte slot per unit (a wave reads the whole 1 KB unit) and
+// takes exact integer dot products of its 32 (int4) or 16 (int8) codes with
+// every token's staged chunk (dot_int4 / dot_int8), scaled in float32 per
+// chunk. Partial sums are added over the four lanes of a row with lane
+// shuffles and over the KS waves of a unit row in LDS, always in the same
+// order.
 //
 // gate/up pass with a union of at most 64 experts: the workgroup finds its
 // item from the union itself (no separate planning launch) and records the
@@ -476,11 +478,12 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
 
     // ---- stage the activations: loads first, then the weights ----------------
     // (token, chunk) pairs are spread over the threads; a round covers one
-    // pair per thread. Each pair is staged on its own: float16 scaled by the
-    // power of two that brings the chunk's largest magnitude into
-    // [2^13, 2^14) (exact, undone per chunk with the group scale). The first
-    // rounds are loaded before the weight loads are issued, so their data do
-    // not wait behind the weights.
+    // pair per thread. Each pair is staged on its own: scaled by the power of
+    // two that brings the chunk's largest magnitude into [2^13, 2^14),
+    // rounded to 16-bit integers and split into digit planes (the scale is
+    // undone per chunk with the group scale). The first rounds are loaded
+    // before the weight loads are issued, so their data do not wait behind
+    // the weights.
     const int NPAIR = TB * NCH;
     const int ROUNDS = (NPAIR + kGemvThreads - 1) / kGemvThreads;
     auto pair_src = [&](int pq) -> const float * {

@@ -32,13 +32,19 @@ def test_exports_every_declared_symbol():
     assert set(cache) == set(moe.CACHE_EXPORTED)
     out = subprocess.check_output(["nm", "-D", "--defined-only", moe.LIB_PATH], text=True)
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
-    for n in names + probes + cache:
+    for n in names + cache:
         assert n in exported, n
         assert hasattr(moe.lib(), n)
+    # the measurement probes live in their own library, not in the product one
+    out = subprocess.check_output(["nm", "-D", "--defined-only", moe.PROBE_LIB_PATH], text=True)
+    probe_exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for n in probes:
+        assert n in probe_exported and n not in exported, n
+        assert hasattr(moe.probe_lib(), n)
 
 
 def test_probe_argument_checks():
-    L = moe.lib()
+    L = moe.probe_lib()
     # size not a multiple of 1024, bad batch, bad workgroup, sink too small, misaligned
     assert L.moe_probe_stream_read(FAKE, 1000, 3, 4, FAKE, 1 << 20, None, None, None) == moe.MOE_EINVAL
     assert L.moe_probe_stream_read(FAKE, 1 << 20, 5, 4, FAKE, 1 << 20, None, None, None) == moe.MOE_EINVAL
