@@ -1,35 +1,46 @@
 #!/usr/bin/env python3
 """Throughput of the routed-expert layer step on one MI355X.
 
-A step is one pass of the whole layer step over one batch, one
-moe_layer_step call on one stream: route + top-k, union + permutation and hit
-counters, then expert math + combine (for one token the routing runs inside
-the gate/up GEMV launch). Inputs are synthetic and already resident in HBM.
+A step is one pass of the whole hot path over one batch of synthetic tokens
+already resident in HBM: per layer, route + top-k, union + permutation and hit
+counters, then the expert math and the combine, all through the C ABI
+(moe_layer_step) on one stream.
 
-Default workload ("decode1"): one GLM-5.2-shaped decode layer (d_model 6144,
-d_ff 2048, 256 routed + 1 shared int4 experts with float32 scales per 128,
-top-1, 1 token per step). Successive steps walk through --layers independently
-drawn layer pools (each its own router and experts), as a decode pass walks
-through a model's layers, so the 256 MB Infinity Cache cannot serve a
-repeated working set.
+Default run (no --config): the headline is the largest single-GPU workload,
+"stack8_draft": 8 GLM-5.2-shaped int4 MoE layers (d_model 6144, d_ff 2048,
+256 routed + 1 shared expert, top-8, Zipf(1.1) router bias per layer) and an
+int8 draft-head layer, 256 decode tokens per step, the layers chained through
+a residual RMS norm; a step runs all 9 layers. Two sub-records follow it in
+the same JSON line: "decode1" (one token, top-1: the single-token GEMV path,
+8 layer pools rotated so the 256 MB Infinity Cache cannot serve a looped
+working set) and "prefill4096" (4096 tokens, top-8, flat router bias: the
+128-token matrix-core pass). --config NAME measures one workload alone.
 
-Prints one JSON line. `roofline` is for the gate/up kernel of the pass
-(GEMV, 32-token or 128-token matrix-core) whose launches take longest, timed
-with HIP events that the kernel dispatches take on the library's stream, on
-an evenly spread sample of about 64 timed steps (event-taking launches cost
-the host tens of microseconds, so the other steps run without them).
+Each workload is measured in three passes over the same steps:
+  1. wall clock: W untimed warm-up steps, then exactly K steps between two
+     torch.cuda.synchronize() calls, with no events or other instrumentation;
+     `value` (tokens/s) and `ms_per_step` come from this pass only;
+  2. per-step GPU time: the same steps again with one HIP event recorded on
+     the stream between consecutive steps, for the p10 / p50 / p90 step times;
+  3. per-kernel time: a sample of steps whose expert kernels take HIP events at
+     their own start and end (hipExtLaunchKernelGGL on the library's stream),
+     for the roofline of the dominant kernel: its algorithmic bytes (or flops)
+     per launch over its mean duration. Event-taking launches cost the host
+     microseconds each, which is why this pass is separate.
 `roofline.measured_ceiling` is what the simplest kernel of the same kind
 reaches on this GPU (a plain streaming read of the same bytes per launch, or
 a loop of independent matrix-core products), beside the published peak.
-`cpu_baseline` is the CPU oracle timed on this host on a bounded sample of
-the same workload.
+`cpu_baseline` is the CPU oracle (float64, OpenMP) timed on this host on a
+bounded sample of the headline workload.
 """
 import argparse
 import ctypes
 import dataclasses
+import glob
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -39,13 +50,36 @@ METRIC = "MoE-layer tokens/s and expert-weight HBM GB/s (% of 8 TB/s peak) on 1 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0   # dense float16 matrix-core peak
 
+# Arithmetic of each pass of the layer step
+DTYPE_BY_PASS = {
+    "router": "f32 (sums and sigmoid)",
+    "gemv": "int4 codes x int16 activations as four base-16 digit planes (v_dot8c_i32_i4), "
+            "int8 codes x two base-256 planes (v_dot4c_i32_i8): exact int32 per 32/16-column "
+            "run, scaled in f32",
+    "small": "f16 codes x f16 activations -> f32 accumulate (v_mfma_f32_16x16x32_f16), "
+             "32-token items",
+    "mfma": "f16 codes x f16 activations -> f32 accumulate (v_mfma_f32_16x16x32_f16), "
+            "128-token items",
+    "combine": "f32",
+}
+DTYPE = "int4/int8 weights; f16 MFMA and int16-digit dot products, f32 accumulate"
+
+# Defaults of the sub-records of the headline run (independent of --steps,
+# which applies to the headline)
+SUB_RUNS = {"decode1": dict(steps=2000, warmup=400, layers=8, batches=16),
+            "prefill4096": dict(steps=20, warmup=4, layers=2, batches=2)}
+KERNEL_SAMPLES = 64   # layer steps whose kernels take events (pass 3), at least
+
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=2000)
-    p.add_argument("--warmup", type=int, default=400)
-    p.add_argument("--config", default="decode1")
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default=None,
+                   help="measure this workload alone (tiny, decode1, decode64, prefill4096, "
+                        "stack8_draft); default: stack8_draft with decode1 and prefill4096 "
+                        "sub-records")
     p.add_argument("--tokens", type=int, default=None,
                    help="tokens per step instead of the workload's (e.g. a speculative "
                         "verify batch of 1 + drafts through the stack)")
@@ -55,10 +89,16 @@ def parse():
                         "pass (moe_forward_options.mfma_small_min_tokens; default: the library's)")
     p.add_argument("--group", type=int, default=None,
                    help="scale group of the int4 layers instead of the workload's (e.g. 64)")
-    p.add_argument("--layers", type=int, default=8, help="layer pools rotated over the steps")
+    p.add_argument("--layers", type=int, default=8,
+                   help="layer pools rotated over the steps (single-layer workloads)")
     p.add_argument("--batches", type=int, default=16, help="distinct token batches rotated")
-    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--cpu-tokens", type=int, default=64,
+                   help="tokens of the headline batch the CPU oracle runs through the stack")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="time budget of the CPU oracle on single-layer workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-subrecords", action="store_true",
+                   help="default run: the headline workload only")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run one plain device copy of 1 GiB (to scale HBM counters)")
     p.add_argument("--cache-stack", type=int, default=None, metavar="SLOTS",
@@ -73,6 +113,10 @@ def parse():
                    help="comma-separated HBM slot counts: measure the Place stage (experts in "
                         "pinned host memory, an HBM cache of that many slots per layer) instead")
     return p.parse_args()
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
 
 
 def copy_calibration():
@@ -122,10 +166,12 @@ class Hip:
 
     def __init__(self):
         self.L = ctypes.CDLL("libamdhip64.so")
-        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
-                                               ctypes.c_void_p]
-        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        vp = ctypes.c_void_p
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(vp)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        self.L.hipEventDestroy.argtypes = [vp]
+        self.L.hipEventRecord.argtypes = [vp, vp]
+        self.L.hipMemcpyAsync.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
 
     def event(self):
         e = ctypes.c_void_p()
@@ -142,21 +188,515 @@ class Hip:
         return ms.value
 
 
+# ---------------------------------------------------------------- environment
+
+def _gpu_sysfs_dir(torch):
+    """sysfs folder of cuda:0 (matched by PCI address), or None."""
+    try:
+        p = torch.cuda.get_device_properties(0)
+        bdf = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}"
+    except Exception:
+        return None
+    for dev in glob.glob("/sys/class/drm/card*/device"):
+        try:
+            if os.path.basename(os.path.realpath(dev)).startswith(bdf):
+                return dev
+        except OSError:
+            pass
+    return None
+
+
+def _current_mhz(path):
+    """The active level of a pp_dpm_* file ("N: 2400Mhz *"), in MHz."""
+    with open(path) as fh:
+        for line in fh:
+            if line.rstrip().endswith("*"):
+                return int(line.split(":")[1].strip().lower().split("mhz")[0])
+    return None
+
+
+class ClockSampler:
+    """Samples the GPU's current SCLK and MCLK (sysfs pp_dpm_sclk / pp_dpm_mclk)
+    every few milliseconds on a side thread while a timed region runs."""
+
+    def __init__(self, torch, period=0.005):
+        self.dir = _gpu_sysfs_dir(torch)
+        self.period = period
+        self.samples = []
+        self._stop = threading.Event()
+        self._t = None
+
+    def __enter__(self):
+        if self.dir:
+            self._t = threading.Thread(target=self._run, daemon=True)
+            self._t.start()
+        return self
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append((_current_mhz(os.path.join(self.dir, "pp_dpm_sclk")),
+                                     _current_mhz(os.path.join(self.dir, "pp_dpm_mclk"))))
+            except (OSError, ValueError, IndexError):
+                return
+            time.sleep(self.period)
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._t:
+            self._t.join()
+
+    def summary(self):
+        s = [v for v in self.samples if v[0] is not None]
+        if not s:
+            return {"sclk_mhz": None, "mclk_mhz": None, "samples": 0,
+                    "note": "GPU clock files not readable on this host"}
+        sc = sorted(v[0] for v in s)
+        mc = sorted(v[1] for v in s if v[1] is not None)
+        return {"sclk_mhz": {"min": sc[0], "median": sc[len(sc) // 2], "max": sc[-1]},
+                "mclk_mhz": ({"min": mc[0], "median": mc[len(mc) // 2], "max": mc[-1]}
+                             if mc else None),
+                "samples": len(s), "source": self.dir}
+
+
+def host_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
+    return {"cpu_model": model, "nproc": nproc, "cpu_count": os.cpu_count()}
+
+
+def percentiles(v):
+    import numpy as np
+    v = np.asarray(v, np.float64)
+    return {"p10": float(np.percentile(v, 10)), "p50": float(np.percentile(v, 50)),
+            "p90": float(np.percentile(v, 90)), "mean": float(v.mean()), "n": int(v.size)}
+
+
+# ---------------------------------------------------------------- workloads
+
+def build_workload(name, args, steps, warmup, layers, batches, dev, tokens=None, k=None,
+                   group=None, small_min=None):
+    """HBM-resident pools, routers and token batches of one workload, and the
+    C-ABI calls of its steps with their arguments converted once."""
+    import numpy as np
+    import torch
+
+    import int4_routed_expert_gemv_amd as moe
+    import synth
+
+    base = synth.CONFIGS[name]
+    if group is not None:
+        base = dataclasses.replace(base, layers=tuple(
+            dataclasses.replace(ls, group=group) if ls.wbits == 4 else ls for ls in base.layers))
+    if tokens is not None:
+        base = dataclasses.replace(base, n_tokens=tokens)
+    if k is not None:
+        base = dataclasses.replace(base, k=k)
+    spec = base.layer
+    stack = len(base.layers) > 1
+    if stack:
+        cfg, L_rot = base, len(base.layers)
+    else:
+        L_rot = layers
+        cfg = dataclasses.replace(base, layers=(spec,) * L_rot)
+    N, k, E, d, f = cfg.n_tokens, cfg.k, spec.n_experts, spec.d, spec.f
+    nb = max(1, min(batches, steps + warmup))
+    t0 = time.time()
+    pools, routers = [], []
+    for l in range(L_rot):
+        ls = cfg.layers[l]
+        blocks = synth.expert_pool(cfg, l)
+        shared = synth.shared_block(cfg, l)
+        pools.append(moe.DevicePool(d, f, E, ls.wbits, ls.group, blocks, shared, dev))
+        del blocks
+        wr, b = synth.router(cfg, l)
+        routers.append((torch.from_numpy(wr).to(dev), torch.from_numpy(b).to(dev)))
+        say(f"[bench] {name}: layer pool {l + 1}/{L_rot} resident")
+    tok_cfg = dataclasses.replace(cfg, n_tokens=N * nb)
+    xs_host = synth.tokens(tok_cfg).reshape(nb, N, d)
+    xs = torch.from_numpy(xs_host).to(dev)
+    w = dict(
+        ids=torch.empty((N, k), dtype=torch.int32, device=dev),
+        w=torch.empty((N, k), dtype=torch.float32, device=dev),
+        union_ids=torch.empty(E, dtype=torch.int32, device=dev),
+        n_union=torch.empty(1, dtype=torch.int32, device=dev),
+        offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+        perm=torch.empty(N * k, dtype=torch.int32, device=dev),
+        counters=torch.zeros((L_rot, E), dtype=torch.int64, device=dev),
+        y=torch.empty((N, d), dtype=torch.float32, device=dev),
+        hbuf=torch.empty((N, d), dtype=torch.float32, device=dev),   # residual stream
+        abuf=torch.empty((N, d), dtype=torch.float32, device=dev),   # normalised layer input
+    )
+    ws_bytes = max(moe.layer_step_workspace_size(p.desc, N, k) for p in pools)
+    w["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    return dict(name=name, cfg=cfg, base=base, spec=spec, stack=stack, L_rot=L_rot, N=N, k=k, E=E,
+                d=d, f=f, nb=nb, pools=pools, routers=routers, xs=xs, xs_host=xs_host,
+                bufs=w, ws_bytes=ws_bytes, small_min=small_min, setup_s=time.time() - t0)
+
+
+class Runner:
+    """Launches the steps of a workload through the C ABI (moe_layer_step, and
+    moe_residual_rmsnorm between the layers of a stack)."""
+
+    def __init__(self, wl, hip, torch):
+        import int4_routed_expert_gemv_amd as moe
+        self.wl, self.hip = wl, hip
+        self.moe = moe
+        self.L = moe.lib()
+        vp = ctypes.c_void_p
+        self.vp = vp
+        self.stream = vp(torch.cuda.current_stream().cuda_stream)
+        b = wl["bufs"]
+        self.base_opts = None
+        if wl["small_min"] is not None:
+            self.base_opts = moe.ForwardOptions()
+            self.base_opts.mfma_small_min_tokens = wl["small_min"]
+        N, d, k = wl["N"], wl["d"], wl["k"]
+
+        def args(l, x):
+            wr, bias = wl["routers"][l]
+            return (ctypes.byref(wl["pools"][l].desc), vp(x.data_ptr()), N, d, vp(wr.data_ptr()),
+                    vp(bias.data_ptr()), k, vp(b["ids"].data_ptr()), vp(b["w"].data_ptr()),
+                    vp(b["union_ids"].data_ptr()), vp(b["n_union"].data_ptr()),
+                    vp(b["offsets"].data_ptr()), vp(b["perm"].data_ptr()),
+                    vp(b["counters"][l].data_ptr()), vp(b["y"].data_ptr()),
+                    vp(b["ws"].data_ptr()), wl["ws_bytes"], self.stream)
+
+        if wl["stack"]:
+            self.layer_args = [args(l, b["abuf"]) for l in range(wl["L_rot"])]
+        else:
+            # one plan per (layer pool, batch) pair: step s takes plan s % n_plan
+            self.plans = [args(p % wl["L_rot"], wl["xs"][p % wl["nb"]])
+                          for p in range(wl["L_rot"] * wl["nb"])]
+
+    def layer(self, a, opt):
+        o = opt if opt is not None else self.base_opts
+        rc = self.L.moe_layer_step(*a, None if o is None else ctypes.byref(o))
+        if rc:
+            raise RuntimeError(f"moe_layer_step failed with status {rc}")
+
+    def step(self, s, evs=None, sync_layers=None):
+        """Step s; evs: per layer, a ForwardOptions with events (or None);
+        sync_layers(l): called after each layer (calibration only)."""
+        wl = self.wl
+        if not wl["stack"]:
+            self.layer(self.plans[s % len(self.plans)], evs[0] if evs else None)
+            if sync_layers:
+                sync_layers(s % len(self.plans))
+            return
+        b, vp = wl["bufs"], self.vp
+        x = wl["xs"][s % wl["nb"]]
+        rc = self.hip.L.hipMemcpyAsync(vp(b["hbuf"].data_ptr()), vp(x.data_ptr()),
+                                       x.numel() * 4, 3, self.stream)
+        for l in range(wl["L_rot"]):
+            rc |= self.L.moe_residual_rmsnorm(vp(b["hbuf"].data_ptr()),
+                                              vp(b["y"].data_ptr()) if l else None,
+                                              vp(b["abuf"].data_ptr()), wl["N"], wl["d"],
+                                              ctypes.c_float(1e-6), self.stream)
+            if rc:
+                raise RuntimeError(f"stack step failed with status {rc}")
+            self.layer(self.layer_args[l], evs[l] if evs else None)
+            if sync_layers:
+                sync_layers((s % wl["nb"], l))
+
+
+def calibrate(wl, runner, torch, small_min):
+    """Which experts each (layer, batch) step streams and on which pass (the
+    library's default thresholds): experts with at least 32 tokens go to the
+    128-token matrix-core pass, those with at least small_min (2) to the
+    32-token pass, the rest (and every expert of a batch of at most 2 tokens)
+    to the GEMV; fewer than 32 items of 128 tokens join the 32-token pass; a
+    128-token group's remainder of at most 32 tokens past a full item goes to
+    the 32-token pass. The shared expert counts as an expert of N tokens."""
+    import numpy as np
+    MFMA_MIN, MIN_BIG_ITEMS, GEMV_BATCH = 32, 32, 2
+    SMALL_MIN = small_min if small_min is not None else 2
+    N, d, f = wl["N"], wl["d"], wl["f"]
+    b = wl["bufs"]
+    calib = {}
+
+    def pass_of(T, mfma_ok):
+        T = np.asarray(T)
+        big = (T >= MFMA_MIN) & mfma_ok
+        small = ~big & (T >= SMALL_MIN) & mfma_ok & (N > GEMV_BATCH or small_min is not None)
+        if big.any() and np.sum((T[big] + 127) // 128) < MIN_BIG_ITEMS:
+            small, big = small | big, np.zeros_like(big)
+        return np.where(big, 1, np.where(small, 2, 0))
+
+    def record(key):
+        torch.cuda.synchronize()
+        l = key[1] if wl["stack"] else key % wl["L_rot"]
+        ls = wl["cfg"].layers[l]
+        mfma_ok = ls.wbits == 4 and d % 64 == 0 and f % 64 == 0
+        nu = int(b["n_union"].item())
+        uid = b["union_ids"][:nu].cpu().numpy()
+        off = b["offsets"].cpu().numpy()
+        T = np.concatenate([off[uid + 1] - off[uid], [N]])  # routed, then shared
+        ps = pass_of(T, mfma_ok)
+        c = dict(union=nu, wbits=ls.wbits, group=ls.group, layer=l)
+        for name, code in (("gemv", 0), ("mfma", 1), ("small", 2)):
+            c[name + "_experts"] = int((ps == code).sum())
+            c[name + "_tokens"] = int(T[ps == code].sum())
+        if mfma_ok and (N > GEMV_BATCH or small_min is not None) and SMALL_MIN > 0:
+            r = T % 128
+            rem = (ps == 1) & (T > 128) & (r > 0) & (r <= 32)
+            c["mfma_tokens"] -= int(r[rem].sum())
+            c["small_tokens"] += int(r[rem].sum())
+            c["small_experts"] += int(rem.sum())
+        calib[key] = c
+
+    n = wl["nb"] if wl["stack"] else len(runner.plans)
+    for s in range(n):
+        runner.step(s, sync_layers=record)
+    torch.cuda.synchronize()
+    return calib
+
+
+def layer_sizes(moe, d, f, c):
+    """(whole block bytes, gate + up bytes) of one expert of layer record c."""
+    bb = moe.block_bytes(d, f, c["wbits"], c["group"])
+    q_gu = f * d * c["wbits"] // 8
+    s_gu = f * (d // c["group"] if c["group"] else 1) * 4
+    return bb, 2 * (q_gu + s_gu)
+
+
+KERNEL_LABELS = {
+    "gemv": ("gemv_kernel<gate/up> (expert gate and up projections, SiLU product)",
+             "moe::gemv_kernel<true, {wb}, 1"),
+    "small": ("mfma_kernel<gate/up, 32 tokens> (small-group gate and up on the matrix cores)",
+              "moe::mfma_kernel<true, {wb}, 2"),
+    "mfma": ("mfma_kernel<gate/up, 128 tokens> (grouped GEMM of gate and up, SiLU product)",
+             "moe::mfma_kernel<true, {wb}, 8"),
+}
+
+
+def measure(wl, args, steps, warmup, hip, torch, traffic_key):
+    """The three passes (wall clock, per-step events, per-kernel events) over
+    one workload; returns its record (no cpu_baseline)."""
+    import numpy as np
+
+    import int4_routed_expert_gemv_amd as moe
+    name, N, k, d, f, E = wl["name"], wl["N"], wl["k"], wl["d"], wl["f"], wl["E"]
+    stack = wl["stack"]
+    runner = Runner(wl, hip, torch)
+    calib = calibrate(wl, runner, torch, wl["small_min"])
+    mean_union = float(np.mean([c["union"] for c in calib.values()]))
+    n_plan = wl["nb"] if stack else len(runner.plans)
+
+    def keys_of(s):
+        """calibration keys of the layers step s runs"""
+        if stack:
+            return [(s % wl["nb"], l) for l in range(wl["L_rot"])]
+        return [s % n_plan]
+
+    # ---- pass 1: wall clock, nothing but the steps ----------------------------
+    for s in range(warmup):
+        runner.step(s)
+    torch.cuda.synchronize()
+    say(f"[bench] {name}: setup {wl['setup_s']:.1f}s, mean union {mean_union:.1f}; "
+        f"timing {steps} steps")
+    K = steps
+    with ClockSampler(torch) as clocks:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(K):
+            runner.step(warmup + s)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / K * 1e3
+
+    # ---- pass 2: per-step GPU time --------------------------------------------
+    evs = [hip.event() for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    for s in range(K):
+        hip.L.hipEventRecord(evs[s], runner.stream)
+        runner.step(warmup + s)
+    hip.L.hipEventRecord(evs[K], runner.stream)
+    torch.cuda.synchronize()
+    step_ms = [hip.elapsed_ms(evs[s], evs[s + 1]) for s in range(K)]
+    for e in evs:
+        hip.L.hipEventDestroy(e)
+
+    # ---- pass 3: per-kernel events on a sample of steps ------------------------
+    # the same K steps once more, every `every`-th one with events on its
+    # expert kernels and the others plain, so that the GPU stays as busy as
+    # in pass 1 (back-to-back instrumented steps would leave it idle between
+    # the short decode steps, and kernels started from idle run longer)
+    per_step_layers = wl["L_rot"] if stack else 1
+    n_samp = max(1, min(K, -(-KERNEL_SAMPLES // per_step_layers)))
+    every = max(1, K // n_samp)
+    samp_steps = [warmup + s for s in range(0, every * n_samp, every)]
+    fo = {}
+    for s in samp_steps:
+        fo[s] = [moe.ForwardOptions(*[hip.event() for _ in range(12)], 0,
+                                    wl["small_min"] if wl["small_min"] is not None else 0)
+                 for _ in range(per_step_layers)]
+    torch.cuda.synchronize()
+    for s in range(warmup, warmup + max(K, every * n_samp)):
+        runner.step(s, evs=fo.get(s))
+    torch.cuda.synchronize()
+    fo = [fo[s] for s in samp_steps]
+
+    def ms(e, a, b):
+        try:
+            return hip.elapsed_ms(getattr(e, a), getattr(e, b))
+        except AssertionError:  # the kernel was not launched in that step
+            return None
+
+    # per pass and weight width: (algorithmic gate/up bytes, flops, gate/up
+    # time, down bytes, down time) of every sampled launch
+    launches = {}
+    for s, opts in zip(samp_steps, fo):
+        for key, o in zip(keys_of(s), opts):
+            c = calib[key]
+            bb, gub = layer_sizes(moe, d, f, c)
+            for pname, pre in (("gemv", ""), ("mfma", "mfma_"), ("small", "small_")):
+                t_gu = ms(o, pre + "gateup_start", pre + "gateup_end")
+                t_dn = ms(o, pre + "down_start", pre + "down_end")
+                if t_gu is None or c[pname + "_experts"] == 0:
+                    continue
+                launches.setdefault((pname, c["wbits"]), []).append(
+                    (c[pname + "_experts"] * gub, 4.0 * d * f * c[pname + "_tokens"], t_gu,
+                     c[pname + "_experts"] * (bb - gub), t_dn))
+    for opts in fo:
+        for o in opts:
+            for fld, _ in moe.ForwardOptions._fields_[:12]:
+                hip.L.hipEventDestroy(getattr(o, fld))
+
+    passes = {}
+    for (pname, wb), v in launches.items():
+        v = np.asarray([(a, b_, c_, d_, e_ if e_ is not None else np.nan) for a, b_, c_, d_, e_ in v])
+        t_gu = v[:, 2].mean() / 1e3
+        t_dn = np.nanmean(v[:, 4]) / 1e3 if np.isfinite(v[:, 4]).any() else None
+        gu_b, fl, dn_b = v[:, 0].mean(), v[:, 1].mean(), v[:, 3].mean()
+        passes[f"{pname}_int{wb}"] = {
+            "kernel": KERNEL_LABELS[pname][1].format(wb=wb), "launches": int(len(v)),
+            "avg_launch_us": t_gu * 1e6, "bytes_per_launch": gu_b, "achieved_GBps": gu_b / 1e9 / t_gu,
+            "flops_per_launch": fl, "achieved_TFLOPs": fl / 1e12 / t_gu,
+            "total_ms_in_sample": float(v[:, 2].sum()),
+            "down_avg_launch_us": t_dn * 1e6 if t_dn else None,
+            "down_GBps": dn_b / 1e9 / t_dn if t_dn else None, "dtype": DTYPE_BY_PASS[pname]}
+
+    # algorithmic bytes of the timed steps (pass 1)
+    expert_bytes = router_bytes = 0
+    for s in range(K):
+        for key in keys_of(warmup + s):
+            c = calib[key]
+            bb, _ = layer_sizes(moe, d, f, c)
+            expert_bytes += (c["union"] + 1) * bb
+            router_bytes += E * d * 4 + E * 4
+
+    roof = None
+    if passes:
+        # the dominant kernel: the gate/up kernel with the most time in the sample
+        top = max(passes, key=lambda n: passes[n]["total_ms_in_sample"])
+        pz = passes[top]
+        pname = top.split("_")[0]
+        if pname == "mfma":
+            roof = {"bound": "mfma", "achieved": pz["achieved_TFLOPs"],
+                    "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": pz["achieved_TFLOPs"] / MFMA_F16_PEAK_TFLOPS}
+        else:
+            roof = {"bound": "hbm", "achieved": pz["achieved_GBps"], "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": pz["achieved_GBps"] / HBM_PEAK_GBS}
+        roof["traffic"] = measured_traffic(traffic_key, pz["kernel"]) if traffic_key else None
+        roof["kernel"] = KERNEL_LABELS[pname][0] + f", int{top.split('int')[1]} weights"
+        roof["kernel_symbol"] = pz["kernel"]
+        roof["avg_launch_us"] = pz["avg_launch_us"]
+        roof["algorithmic_per_launch"] = (pz["flops_per_launch"] if pname == "mfma"
+                                          else pz["bytes_per_launch"])
+        roof["timing"] = (f"HIP events taken by the kernel's own dispatches on the library's "
+                          f"stream, {pz['launches']} launches: every {every}th of the timed "
+                          f"steps, run again after the timed region")
+        roof["passes"] = passes
+        roof["measured_ceiling"] = measured_ceiling(moe, hip, torch, roof["bound"],
+                                                    pz["bytes_per_launch"], roof["achieved"])
+    steps_pct = percentiles(step_ms)
+    rec = {
+        "metric": METRIC,
+        "value": N * K / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": warmup,
+        "ms_per_step": ms_per_step,
+        "step_ms_events": steps_pct,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE,
+        "dtype_by_pass": DTYPE_BY_PASS,
+        "data": "synthetic",
+        "config": {
+            "workload": wl["workload"],
+            "n_tokens": N, "k": k, "d_model": d, "d_ff": f, "n_experts": E,
+            "wbits": [ls.wbits for ls in wl["cfg"].layers] if stack else wl["spec"].wbits,
+            "group": wl["spec"].group, "layers_per_step": wl["L_rot"] if stack else 1,
+            "layer_pools": wl["L_rot"], "token_batches": wl["nb"], "mean_union": mean_union,
+        },
+        "expert_GBps": expert_bytes / 1e9 / elapsed,
+        "expert_frac_of_peak": expert_bytes / 1e9 / elapsed / HBM_PEAK_GBS,
+        "step_GBps": (expert_bytes + router_bytes) / 1e9 / elapsed,
+        "algorithmic_bytes_per_step": (expert_bytes + router_bytes) / K,
+        "clocks": clocks.summary(),
+        "roofline": roof,
+    }
+    if stack:
+        rec["layer_tokens_per_s"] = N * wl["L_rot"] * K / elapsed
+    say(f"[bench] {name}: {rec['value']:.1f} tokens/s, {ms_per_step * 1e3:.1f} us/step "
+        f"(events p50 {steps_pct['p50'] * 1e3:.1f} us)"
+        + (f"; {roof['kernel_symbol']} {roof['avg_launch_us']:.1f} us, frac {roof['frac']:.3f}"
+           if roof else ""))
+    return rec
+
+
+def workload_label(wl, args_like):
+    cfg, base = wl["cfg"], wl["base"]
+    return (f"{cfg.name}: {base.description}" +
+            ("" if wl["stack"] else f"; {wl['L_rot']} layer pools rotated") +
+            (f"; int4 scale groups of {args_like.get('group')}" if args_like.get("group") else "") +
+            (f"; {wl['N']} tokens per step" if args_like.get("tokens") is not None else "") +
+            (f"; top-{wl['k']}" if args_like.get("k") is not None else ""))
+
+
+def run_workload(name, args, steps, warmup, layers, batches, hip, torch, dev, tokens=None, k=None,
+                 group=None, small_min=None, keep=False):
+    wl = build_workload(name, args, steps, warmup, layers, batches, dev, tokens=tokens, k=k,
+                        group=group, small_min=small_min)
+    wl["workload"] = workload_label(wl, dict(group=group, tokens=tokens, k=k))
+    plain = tokens is None and k is None
+    traffic_key = (name if group is None else f"{name}_g{group}") if plain else None
+    rec = measure(wl, args, steps, warmup, hip, torch, traffic_key)
+    if keep:
+        return rec, wl
+    del wl
+    torch.cuda.empty_cache()
+    return rec, None
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
-
-    import int4_routed_expert_gemv_amd as moe
-    import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.cache_slots:
@@ -167,306 +707,31 @@ def main():
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    base = synth.CONFIGS[args.config]
-    if args.group is not None:
-        base = dataclasses.replace(base, layers=tuple(
-            dataclasses.replace(ls, group=args.group) if ls.wbits == 4 else ls
-            for ls in base.layers))
-    if args.tokens is not None:
-        base = dataclasses.replace(base, n_tokens=args.tokens)
-    if args.k is not None:
-        base = dataclasses.replace(base, k=args.k)
-    spec = base.layer
-    stack = len(base.layers) > 1
-    if stack:
-        # a step is one pass through the whole stack (layers chained on the GPU)
-        cfg = base
-        L_rot = len(cfg.layers)
-    else:
-        L_rot = args.layers
-        cfg = dataclasses.replace(base, layers=(spec,) * L_rot)
-    N, k, E, d, f = cfg.n_tokens, cfg.k, spec.n_experts, spec.d, spec.f
-    A = N * k
-    nb = max(1, min(args.batches, args.steps + args.warmup))
-    t_setup = time.time()
-
-    # --- inputs resident in HBM -------------------------------------------
-    pools, routers = [], []
-    for l in range(L_rot):
-        ls = cfg.layers[l]
-        blocks = synth.expert_pool(cfg, l)
-        shared = synth.shared_block(cfg, l)
-        pools.append(moe.DevicePool(d, f, E, ls.wbits, ls.group, blocks, shared, dev))
-        del blocks
-        wr, b = synth.router(cfg, l)
-        routers.append((torch.from_numpy(wr).to(dev), torch.from_numpy(b).to(dev)))
-        print(f"[bench] layer pool {l + 1}/{L_rot} resident", file=sys.stderr, flush=True)
-    tok_cfg = dataclasses.replace(cfg, n_tokens=N * nb)
-    xs = torch.from_numpy(synth.tokens(tok_cfg).reshape(nb, N, d)).to(dev)
-    ids = torch.empty((N, k), dtype=torch.int32, device=dev)
-    w = torch.empty((N, k), dtype=torch.float32, device=dev)
-    union_ids = torch.empty(E, dtype=torch.int32, device=dev)
-    n_union = torch.empty(1, dtype=torch.int32, device=dev)
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    perm = torch.empty(A, dtype=torch.int32, device=dev)
-    counters = torch.zeros((L_rot, E), dtype=torch.int64, device=dev)
-    y = torch.empty((N, d), dtype=torch.float32, device=dev)
-    ws_bytes = max(moe.layer_step_workspace_size(p.desc, N, k) for p in pools)
-    hbuf = torch.empty((N, d), dtype=torch.float32, device=dev)   # residual stream
-    abuf = torch.empty((N, d), dtype=torch.float32, device=dev)   # normalised layer input
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-
-    # --- raw C-ABI calls with their arguments converted once ---------------
-    Lb = moe.lib()
-    vp = ctypes.c_void_p
-    stream = vp(torch.cuda.current_stream().cuda_stream)
     hip = Hip()
-
-    def step_args(s):
-        l, bi = s % L_rot, s % nb
-        x = abuf if stack else xs[bi]
-        wr, b = routers[l]
-        # Route, Union, Learn and the experts in one call (moe_layer_step)
-        return (ctypes.byref(pools[l].desc), vp(x.data_ptr()), N, d, vp(wr.data_ptr()),
-                vp(b.data_ptr()), k, vp(ids.data_ptr()), vp(w.data_ptr()),
-                vp(union_ids.data_ptr()), vp(n_union.data_ptr()), vp(offsets.data_ptr()),
-                vp(perm.data_ptr()), vp(counters[l].data_ptr()), vp(y.data_ptr()),
-                vp(ws.data_ptr()), ws_bytes, stream)
-
-    plans = [step_args(s) for s in range(L_rot if stack else L_rot * nb)]
-    n_plan = len(plans)
-    hip_rt = ctypes.CDLL("libamdhip64.so")
-    hip_rt.hipMemcpyAsync.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
-
-    base_opts = None
-    if args.small_min is not None:
-        base_opts = moe.ForwardOptions()
-        base_opts.mfma_small_min_tokens = args.small_min
-
-    def run_layer(s, ev=None):
-        opt = ev if ev is not None else base_opts
-        rc = Lb.moe_layer_step(*plans[s % n_plan], None if opt is None else ctypes.byref(opt))
-        if rc:
-            raise RuntimeError(f"layer step failed with status {rc}")
-
-    def run(s, ev=None):
-        if not stack:
-            run_layer(s, ev)
-            return
-        # h = x (device copy), then per layer: h += y (from layer 1 on),
-        # a = rms(h), layer(a) -> y
-        x = xs[s % nb]
-        rc = hip_rt.hipMemcpyAsync(vp(hbuf.data_ptr()), vp(x.data_ptr()), x.numel() * 4, 3, stream)
-        for l in range(L_rot):
-            rc |= Lb.moe_residual_rmsnorm(vp(hbuf.data_ptr()), vp(y.data_ptr()) if l else None,
-                                          vp(abuf.data_ptr()), N, d, ctypes.c_float(1e-6), stream)
-            if rc:
-                raise RuntimeError(f"stack step failed with status {rc}")
-            run_layer(l, ev if l == 0 else None)
-
-    # which experts each (layer, batch) step streams and on which kernels
-    # (the library's default thresholds): experts with at least MFMA_MIN
-    # tokens go to the 128-token matrix-core pass, those with at least
-    # SMALL_MIN to the 32-token pass, the rest to the GEMVs; the shared
-    # expert by the batch size
-    MFMA_MIN = 32
-    SMALL_MIN = args.small_min if args.small_min is not None else 2
-    mfma_ok = spec.wbits == 4 and d % 64 == 0 and f % 64 == 0
-    calib = {}
-
-    MIN_BIG_ITEMS = 32  # fewer 128-token items than this join the 32-token pass
-    GEMV_BATCH = 2      # batches of at most this many tokens keep every expert on the GEMV
-
-    def pass_of(T):
-        T = np.asarray(T)
-        big = (T >= MFMA_MIN) & mfma_ok
-        # batches of up to GEMV_BATCH tokens stay on the GEMV (the library's default)
-        small = ~big & (T >= SMALL_MIN) & mfma_ok & (N > GEMV_BATCH or args.small_min is not None)
-        if big.any() and np.sum((T[big] + 127) // 128) < MIN_BIG_ITEMS:
-            small, big = small | big, np.zeros_like(big)
-        return np.where(big, 1, np.where(small, 2, 0))
-
-    def record(key, l):
-        torch.cuda.synchronize()
-        nu = int(n_union.item())
-        uid = union_ids[:nu].cpu().numpy()
-        off = offsets.cpu().numpy()
-        T = np.concatenate([off[uid + 1] - off[uid], [N]])  # routed, then shared
-        ps = pass_of(T)
-        c = dict(union=nu, wbits=cfg.layers[l].wbits, group=cfg.layers[l].group)
-        for name, code in (("gemv", 0), ("mfma", 1), ("small", 2)):
-            c[name + "_experts"] = int((ps == code).sum())
-            c[name + "_tokens"] = int(T[ps == code].sum())
-        # a 128-token group's remainder of at most 32 tokens past a full item
-        # runs on the 32-token pass (its weights streamed there once more)
-        if mfma_ok and (N > GEMV_BATCH or args.small_min is not None) and SMALL_MIN > 0:
-            r = T % 128
-            rem = (ps == 1) & (T > 128) & (r > 0) & (r <= 32)
-            c["mfma_tokens"] -= int(r[rem].sum())
-            c["small_tokens"] += int(r[rem].sum())
-            c["small_experts"] += int(rem.sum())
-        calib[key] = c
-
-    if stack:
-        x0 = xs[0]
-        hip_rt.hipMemcpyAsync(vp(hbuf.data_ptr()), vp(x0.data_ptr()), x0.numel() * 4, 3, stream)
-        for l in range(L_rot):
-            Lb.moe_residual_rmsnorm(vp(hbuf.data_ptr()), vp(y.data_ptr()) if l else None,
-                                    vp(abuf.data_ptr()), N, d, ctypes.c_float(1e-6), stream)
-            run_layer(l)
-            record(l, l)
-    else:
-        for s_ in range(n_plan):
-            run(s_)
-            record(s_, s_ % L_rot)
-    for _ in range(args.warmup):
-        run(_)
-    torch.cuda.synchronize()
-    mean_union = float(np.mean([c["union"] for c in calib.values()]))
-    print(f"[bench] setup {time.time() - t_setup:.1f}s; mean union {mean_union:.1f}",
-          file=sys.stderr, flush=True)
-
-    # --- timed region -------------------------------------------------------
-    K = args.steps
-    # Kernel durations come from HIP events that the dispatches themselves
-    # take (start and end of each expert kernel) on a sample of the timed
-    # steps, evenly spread: about 64 of them, or every step of a short run.
-    # Event-taking launches cost the host tens of microseconds per step, so
-    # the other steps run without them.
-    every = max(1, K // 64)
-    sampled = [s_ for s_ in range(K) if s_ % every == 0]
-    evs = {s_: moe.ForwardOptions(*[hip.event() for _ in range(12)], 0,
-                                  args.small_min if args.small_min is not None else 0)
-           for s_ in sampled}
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s_ in range(K):
-        run(args.warmup + s_, evs.get(s_))
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
-
-    def ms(e, a, b):
-        try:
-            return hip.elapsed_ms(getattr(e, a), getattr(e, b))
-        except AssertionError:  # the kernel was not launched in that step
-            return None
-
-    # per pass: event-timed gate/up and down launches of every timed step
-    timed = {}
-    for name, pre in (("gemv", ""), ("mfma", "mfma_"), ("small", "small_")):
-        timed[name] = ([ms(evs[s_], pre + "gateup_start", pre + "gateup_end") for s_ in sampled],
-                       [ms(evs[s_], pre + "down_start", pre + "down_end") for s_ in sampled])
-    for e in evs.values():
-        for fld, _ in moe.ForwardOptions._fields_[:12]:
-            hip.L.hipEventDestroy(getattr(e, fld))
-
-    # --- algorithmic bytes and flops ------------------------------------------
-    def sizes(c):
-        bb = moe.block_bytes(d, f, c["wbits"], c["group"])
-        q_gu = f * d * c["wbits"] // 8
-        s_gu = f * (d // c["group"] if c["group"] else 1) * 4
-        return bb, 2 * (q_gu + s_gu)
-
-    # the calibration entry of the (first) layer the events of a step cover
-    step_key = [0 if stack else (args.warmup + s_) % n_plan for s_ in range(K)]
-    layer_keys = list(range(L_rot)) if stack else None
-    expert_bytes = 0
-    router_bytes = 0
-    for s_ in range(K):
-        keys = layer_keys if stack else [step_key[s_]]
-        for key in keys:
-            c = calib[key]
-            bb, _ = sizes(c)
-            expert_bytes += (c["union"] + 1) * bb
-            router_bytes += E * d * 4 + E * 4
-    ms_per_step = elapsed / K * 1e3
-    tokens_per_s = N * K / elapsed
-    expert_gbs = expert_bytes / 1e9 / elapsed
-
-    def avg(v):
-        v = [x for x in v if x is not None]
-        return float(np.mean(v)) if v else None
-
-    # Gate/up kernels of the three passes. The GEMV and 32-token passes are
-    # HBM-bound: algorithmic bytes = gate and up codes + scales of every
-    # expert the pass handles, once. The 128-token pass is matrix-core bound:
-    # algorithmic flops = 2 (gate, up) x 2 x d x f per token it handles.
-    steps_c = [calib[step_key[s_]] for s_ in sampled]  # the steps whose kernels were timed
-    passes = {}
-    for name in ("gemv", "small", "mfma"):
-        gu_t, dn_t = timed[name]
-        if not avg(gu_t):
-            continue
-        t_gu, t_dn = avg(gu_t) / 1e3, (avg(dn_t) / 1e3 if avg(dn_t) else None)
-        gu_b = float(np.mean([c[name + "_experts"] * sizes(c)[1] for c in steps_c]))
-        dn_b = float(np.mean([c[name + "_experts"] * (sizes(c)[0] - sizes(c)[1]) for c in steps_c]))
-        fl = float(np.mean([4.0 * d * f * c[name + "_tokens"] for c in steps_c]))
-        passes[name] = {"avg_launch_us": t_gu * 1e6, "bytes_per_launch": gu_b,
-                        "achieved_GBps": gu_b / 1e9 / t_gu, "flops_per_launch": fl,
-                        "achieved_TFLOPs": fl / 1e12 / t_gu,
-                        "down_avg_launch_us": t_dn * 1e6 if t_dn else None,
-                        "down_GBps": dn_b / 1e9 / t_dn if t_dn else None}
-    labels = {"gemv": ("gemv_kernel<gate/up> (expert gate and up projections, SiLU product)",
-                       "moe::gemv_kernel<true, 4, 1"),
-              "small": ("mfma_kernel<gate/up, 32 tokens> (small-group gate and up on the "
-                        "matrix cores)", "moe::mfma_kernel<true, 4, 2"),
-              "mfma": ("mfma_kernel<gate/up, 128 tokens> (grouped GEMM of gate and up, SiLU "
-                       "product)", "moe::mfma_kernel<true, 4, 8")}
-    roof = None
-    if passes:
-        # the roofline is reported for the pass whose gate/up launch is longest
-        top = max(passes, key=lambda n: passes[n]["avg_launch_us"])
-        pz = passes[top]
-        if top == "mfma":
-            roof = {"bound": "mfma", "achieved": pz["achieved_TFLOPs"],
-                    "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": pz["achieved_TFLOPs"] / MFMA_F16_PEAK_TFLOPS}
-        else:
-            roof = {"bound": "hbm", "achieved": pz["achieved_GBps"], "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": pz["achieved_GBps"] / HBM_PEAK_GBS}
-        roof["traffic"] = (None if args.tokens is not None or args.k is not None else measured_traffic(
-            args.config if args.group is None else f"{args.config}_g{args.group}",
-            labels[top][1]))
-        roof["kernel"] = labels[top][0]
-        roof["passes"] = passes
-        roof["measured_ceiling"] = measured_ceiling(moe, hip, torch, roof["bound"],
-                                                    pz["bytes_per_launch"], roof["achieved"])
-
-    result = {
-        "metric": METRIC,
-        "value": tokens_per_s,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "int4xf16->f32" if spec.wbits == 4 else "int8xf16->f32",
-        "data": "synthetic",
-        "config": {
-            "workload": (f"{cfg.name}: {base.description}" +
-                         ("" if stack else f"; {L_rot} layer pools rotated") +
-                         (f"; int4 scale groups of {args.group}" if args.group else "") +
-                         (f"; {N} tokens per step" if args.tokens is not None else "") +
-                         (f"; top-{k}" if args.k is not None else "")),
-            "n_tokens": N, "k": k, "d_model": d, "d_ff": f, "n_experts": E,
-            "wbits": spec.wbits, "group": spec.group, "layers_per_step": L_rot if stack else 1,
-            "layer_pools": L_rot, "mean_union": mean_union,
-        },
-        "expert_GBps": expert_gbs,
-        "expert_frac_of_peak": expert_gbs / HBM_PEAK_GBS,
-        "step_GBps": (expert_bytes + router_bytes) / 1e9 / elapsed,
-        "roofline": roof,
-        "cpu_baseline": None,
-    }
-
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, spec, args, xs.cpu().numpy())
-    print(json.dumps(result), flush=True)
+    name = args.config or "stack8_draft"
+    rec, wl = run_workload(name, args, args.steps, args.warmup, args.layers, args.batches, hip,
+                           torch, dev, tokens=args.tokens, k=args.k, group=args.group,
+                           small_min=args.small_min, keep=not args.no_cpu_baseline)
+    cpu_inputs = None
+    if wl is not None:
+        cpu_inputs = (wl["cfg"], wl["stack"], wl["xs_host"])
+        del wl
+        torch.cuda.empty_cache()
+    if args.config is None and not args.no_subrecords:
+        subs = {}
+        for sub, kw in SUB_RUNS.items():
+            r, _ = run_workload(sub, args, kw["steps"], kw["warmup"], kw["layers"], kw["batches"],
+                                hip, torch, dev)
+            for key in ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline",
+                        "dtype_by_pass", "data", "unit"):
+                r.pop(key, None)
+            subs[sub] = r
+        rec["sub_records"] = subs
+    rec["host"] = host_info()
+    rec["cpu_baseline"] = None
+    if cpu_inputs is not None:
+        rec["cpu_baseline"] = cpu_baseline(*cpu_inputs, args)
+    print(json.dumps(rec), flush=True)
 
 
 def cache_bench(args):
@@ -773,16 +1038,45 @@ def measured_ceiling(moe, hip, torch, bound, bytes_per_launch, achieved):
     return out
 
 
-def cpu_baseline(cfg, spec, args, xs_host):
-    """The oracle as it is, on this host's cores, over a bounded sample of the
-    same workload: consecutive steps on the first layer pool until the time
-    budget is used."""
+def cpu_baseline(cfg, stack, xs_host, args):
+    """The oracle as it stands (plain C, float64 arithmetic, OpenMP over
+    independent rows), timed on this host's cores over a bounded sample of
+    the same workload. A stack: the first --cpu-tokens tokens of the first
+    batch through every layer (RMS norm, route, top-k, union, counters,
+    experts, combine per layer); each layer's inputs are drawn from the seed
+    before its timed part. A single layer: consecutive steps on the first
+    layer pool for --cpu-seconds."""
+    import numpy as np
+
     import oracle
     import synth
+    threads = oracle.threads()
+    if stack:
+        T = max(1, min(args.cpu_tokens, cfg.n_tokens))
+        h = xs_host[0][:T].astype(np.float64)
+        busy = 0.0
+        for l, ls in enumerate(cfg.layers):
+            blocks = synth.expert_pool(cfg, l)
+            shared = synth.shared_block(cfg, l)
+            wr, b = synth.router(cfg, l)
+            t0 = time.perf_counter()
+            a = oracle.rms_normalize(h, 1e-6)
+            ref = oracle.layer_step(a, wr, b, cfg.k, blocks, shared, ls.d, ls.f, ls.wbits,
+                                    ls.group)
+            h = h + ref["y"]
+            busy += time.perf_counter() - t0
+            del blocks
+            say(f"[bench] cpu oracle: layer {l + 1}/{len(cfg.layers)}, {busy:.1f}s so far")
+        return {"value": T / busy, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                "arith": "float64",
+                "sample": f"{T} of the {cfg.n_tokens} tokens of one {cfg.name} batch through all "
+                          f"{len(cfg.layers)} layers (oracle: RMS norm, router, top-k, union, "
+                          f"counters, experts, combine per layer), {busy:.1f}s of oracle time; "
+                          f"float64 oracle with OpenMP"}
+    spec = cfg.layers[0]
     blocks = synth.expert_pool(cfg, 0)
     shared = synth.shared_block(cfg, 0)
     wr, b = synth.router(cfg, 0)
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     n_steps, tokens = 0, 0
     t0 = time.perf_counter()
     while True:
@@ -793,13 +1087,10 @@ def cpu_baseline(cfg, spec, args, xs_host):
         if time.perf_counter() - t0 >= args.cpu_seconds:
             break
     el = time.perf_counter() - t0
-    n_layers = len(cfg.layers) if len(set(cfg.layers)) > 1 else 1
-    # a stack step runs every layer: scale the first layer's rate to the stack
-    return {"value": tokens / el / n_layers, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "arith": "float64",
             "sample": f"{n_steps} steps ({tokens} tokens) of the {cfg.name} layer step on the "
-                      f"first layer pool, {el:.1f}s, float64 oracle with OpenMP"
-                      + (f"; rate divided by the {n_layers} layers of a stack step"
-                         if n_layers > 1 else "")}
+                      f"first layer pool, {el:.1f}s, float64 oracle with OpenMP"}
 
 
 if __name__ == "__main__":

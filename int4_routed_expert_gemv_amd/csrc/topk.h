@@ -15,7 +15,19 @@ namespace moe {
 constexpr int kMaxSlices = 16;
 constexpr int kMaxPerLane = MOE_MAX_EXPERTS / kWave;  // 16
 
-__device__ __forceinline__ float sigmoidf(float l) { return 1.0f / (1.0f + expf(-l)); }
+// 1 / (1 + e^-l) in float32. For l >= 0 it is taken as 1 - e / (1 + e) with
+// e = e^-l: the small term keeps its relative precision and only the final
+// subtraction rounds, so scores close to 1 (saturated logits) stay as far
+// apart as their float32 values are; 1 / (1 + e) would round 1 + e first and
+// merge scores up to 2^-23 apart. For l < 0 the quotient is already precise.
+__device__ __forceinline__ float sigmoidf(float l)
+{
+    if (l >= 0.0f) {
+        const float e = expf(-l);
+        return 1.0f - e / (1.0f + e);
+    }
+    return 1.0f / (1.0f + expf(-l));
+}
 
 // Order-preserving map of float bits onto unsigned integers (NaN above +inf).
 __device__ __forceinline__ uint32_t sortable(float v)

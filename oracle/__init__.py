@@ -60,6 +60,8 @@ def lib():
         L.oracle_expert_forward.argtypes = [vp, sz, i32, vp, i32, i32, i32, i32,
                                             vp, i32, i32, vp, vp, vp]
         L.oracle_rms_normalize.argtypes = [vp, i32, i32, ctypes.c_double, vp]
+        L.oracle_threads.restype = i32
+        L.oracle_threads.argtypes = []
         _lib = L
     return _lib
 
@@ -67,6 +69,11 @@ def lib():
 def _c(a, dtype):
     a = np.ascontiguousarray(a, dtype=dtype)
     return a, a.ctypes.data
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops run with on this host."""
+    return int(lib().oracle_threads())
 
 
 def block_bytes(d, f, wbits, group) -> int:

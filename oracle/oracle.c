@@ -35,9 +35,23 @@
  * float32 because the top-k decision is taken on float32 scores.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Number of threads an OpenMP parallel region of this library runs with
+ * (reported next to timings of the oracle; no arithmetic). */
+int oracle_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+    return n;
+}
 
 /* ---- canonical expert block ------------------------------------------- */
 

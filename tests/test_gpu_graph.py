@@ -76,6 +76,7 @@ def _same(a, b):
 
 
 def _case(name, n_tokens=None, k=None):
+    """The workload's config, with n_tokens and top-k replaced when given."""
     cfg = synth.CONFIGS[name]
     if n_tokens is not None:
         cfg = dataclasses.replace(cfg, n_tokens=n_tokens, k=k)
@@ -86,16 +87,19 @@ def _case(name, n_tokens=None, k=None):
 # 32-token pass), 300 tokens top-4 over 16 experts with every expert on the
 # 128-token pass, and 20 tokens top-8 (the router's workgroup-tiled path and
 # the separate union kernel) with the default passes
-CASES = [("decode1", None, None, None, False), ("decode64", None, None, None, False),
-         ("tiny", 300, 4, 1, False), ("tiny", 20, 8, None, False),
+CASES = [("decode1", None, None, None, False, False), ("decode64", None, None, None, False, False),
+         ("tiny", 300, 4, 1, False, False), ("tiny", 20, 8, None, False, False),
          # moe_layer_step: one and two tokens (routing inside the gate/up
          # launch), 20 tokens
-         ("decode1", None, None, None, True), ("tiny", 1, 4, None, True),
-         ("tiny", 2, 8, None, True), ("tiny", 20, 8, None, True)]
+         ("decode1", None, None, None, True, False), ("tiny", 1, 4, None, True, False),
+         ("tiny", 2, 8, None, True, False), ("tiny", 20, 8, None, True, False),
+         # two identical tokens: routed items of two tokens inside the launch
+         ("tiny", 2, 1, None, True, True), ("tiny", 2, 2, None, True, True),
+         ("decode64", 2, 2, None, True, True)]
 
 
-@pytest.mark.parametrize("name,n_tokens,k,big,one_call", CASES)
-def test_graph_replay_equals_eager(name, n_tokens, k, big, one_call):
+@pytest.mark.parametrize("name,n_tokens,k,big,one_call,dup", CASES)
+def test_graph_replay_equals_eager(name, n_tokens, k, big, one_call, dup):
     cfg = _case(name, n_tokens, k)
     opts = None
     if big is not None:
@@ -105,8 +109,10 @@ def test_graph_replay_equals_eager(name, n_tokens, k, big, one_call):
     spec = cfg.layers[0]
     N, k, d, E = cfg.n_tokens, cfg.k, spec.d, spec.n_experts
     say(f"[graph] {name} N={N} k={k} d={d} f={spec.f} E={E} mfma_min_tokens={big} "
-        f"one_call={one_call}")
+        f"one_call={one_call} dup={dup}")
     x0, wr, b, _, _ = lc.layer_inputs(cfg, 0)
+    if dup:  # every token a copy of token 0: the tokens share their experts
+        x0 = np.ascontiguousarray(np.broadcast_to(x0[:1], x0.shape))
     blocks, shared = lc.canonical_pool(cfg, 0)
     ref = oracle.layer_step(x0, wr, b, k, blocks, shared, spec.d, spec.f, spec.wbits, spec.group)
     pool = upload_pool(spec, blocks, shared)

@@ -26,14 +26,18 @@ def say(*a):
     sys.stdout.flush()
 
 
-def _compare(cfg, shared=True):
+def _compare(cfg, shared=True, dup=False):
     spec = cfg.layers[0]
     x, wr, b, _, _ = lc.layer_inputs(cfg, 0)
+    if dup:
+        # every token a copy of token 0 (each token's gaps stay clear): all
+        # tokens pick the same experts, so each routed item holds every token
+        x = np.ascontiguousarray(np.broadcast_to(x[:1], x.shape))
     blocks, sh = lc.canonical_pool(cfg, 0)
     if not shared:
         sh = None
     say(f"[layer_step] {cfg.name} N={cfg.n_tokens} k={cfg.k} d={spec.d} f={spec.f} "
-        f"E={spec.n_experts} wbits={spec.wbits} shared={shared}")
+        f"E={spec.n_experts} wbits={spec.wbits} shared={shared} dup={dup}")
     ref = oracle.layer_step(x, wr, b, cfg.k, blocks, sh, spec.d, spec.f, spec.wbits, spec.group)
     pool = upload_pool(spec, blocks, sh)
     two = run_layer(pool, x, wr, b, cfg.k, fused_route=True)
@@ -45,6 +49,10 @@ def _compare(cfg, shared=True):
     np.testing.assert_array_equal(one["union_ids"], ref["union_ids"])
     np.testing.assert_array_equal(one["perm"], ref["perm"])
     np.testing.assert_array_equal(one["counters"], ref["counters"])
+    np.testing.assert_array_equal(one["offsets"], ref["offsets"])
+    if dup:
+        assert len(ref["union_ids"]) == cfg.k and np.all(ref["counters"][ref["union_ids"]] ==
+                                                          cfg.n_tokens)
     err = lc.rel_err_rows(one["y"], ref["y"]).max()
     assert err <= 2e-3, f"max per-token relative error {err:.3e}"
     # counters accumulate over calls
@@ -71,6 +79,16 @@ def test_decode_shapes_two_tokens(k):
     bias, so the two tokens share experts): routing inside the gate/up
     launch with items of one and two tokens."""
     _compare(dataclasses.replace(synth.CONFIGS["decode64"], n_tokens=2, k=k))
+
+
+@pytest.mark.parametrize("k", [1, 2])
+@pytest.mark.parametrize("name", ["decode64", "tiny"])
+@pytest.mark.parametrize("shared", [True, False])
+def test_two_tokens_same_experts(name, k, shared):
+    """Two identical tokens: the in-launch routing of one or two tokens meets
+    a routed expert that holds both of them (items of two tokens, the second
+    token found at permutation position 1, a hit count of 2 per expert)."""
+    _compare(dataclasses.replace(synth.CONFIGS[name], n_tokens=2, k=k), shared=shared, dup=True)
 
 
 @pytest.mark.parametrize("N,k,shared", [(1, 1, True), (1, 1, False), (1, 2, False), (1, 5, True),
