@@ -367,6 +367,32 @@ moe_status moe_layer_step(const moe_expert_pool *pool /* (host) */, const float 
                           size_t ws_bytes, hipStream_t stream,
                           const moe_forward_options *opt /* (host) */);
 
+/*
+ * moe_layer_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The workspace is a fixed array of
+ * MOE_SCRATCH_BYTES in the library's own device memory, one per GPU, held
+ * until the process ends; the call allocates nothing. Same arguments (minus
+ * workspace and ws_bytes), checks, kernels and outputs as moe_layer_step.
+ * A step whose moe_layer_step_workspace_size exceeds MOE_SCRATCH_BYTES is
+ * rejected with MOE_EWORKSPACE before any HIP call (at the GLM-5.2 shapes,
+ * d_model 6144, d_ff 2048, 256 experts: up to 128 tokens at top-8, 256
+ * tokens at top-1). Every call on one GPU shares that GPU's array and leaves
+ * its contents behind (the step reads nothing it has not written in the same
+ * call): calls that overlap on one GPU (other streams or threads) race and
+ * must be ordered by the caller. MOE_EHIP if the array's device address
+ * cannot be found (first call on a device).
+ */
+#define MOE_SCRATCH_BYTES ((size_t)64 << 20)
+
+moe_status moe_layer_step_noalloc(const moe_expert_pool *pool /* (host) */, const float *x,
+                                  int n_tokens, int d_model, const float *w_router,
+                                  const float *b_router, int k, int32_t *topk_ids,
+                                  float *topk_w, int32_t *union_ids, int32_t *n_union,
+                                  int32_t *expert_offsets, int32_t *perm, uint64_t *counters,
+                                  float *y, hipStream_t stream,
+                                  const moe_forward_options *opt /* (host) */);
+
 /* Workspace sizes in bytes (host-only arithmetic, no HIP calls). */
 size_t moe_route_workspace_size(int n_tokens, int n_experts);
 size_t moe_forward_workspace_size(const moe_expert_pool *pool, int n_tokens, int k);

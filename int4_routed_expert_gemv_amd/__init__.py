@@ -36,8 +36,9 @@ EXPORTED = [
     "moe_expert_forward", "moe_expert_forward_ex",
     "moe_hit_count", "moe_residual_rmsnorm", "moe_route_workspace_size", "moe_forward_workspace_size",
     "moe_workspace_size", "moe_block_bytes", "moe_pack_expert", "moe_strerror",
-    "moe_layer_step", "moe_layer_step_workspace_size",
+    "moe_layer_step", "moe_layer_step_workspace_size", "moe_layer_step_noalloc",
 ]
+MOE_SCRATCH_BYTES = 64 << 20  # the workspace array of moe_layer_step_noalloc, per GPU
 
 
 # measured-ceiling probes (include/moe_probe.h), not part of the layer step
@@ -115,6 +116,8 @@ def lib():
         L.moe_hit_count.argtypes = [vp, i32, i32, i32, vp, vp]
         L.moe_layer_step.argtypes = [P, vp, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                      vp, vp, sz, vp, ctypes.POINTER(ForwardOptions)]
+        L.moe_layer_step_noalloc.argtypes = [P, vp, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp,
+                                             vp, vp, vp, vp, ctypes.POINTER(ForwardOptions)]
         L.moe_layer_step_workspace_size.argtypes = [P, i32, i32]
         L.moe_residual_rmsnorm.argtypes = [vp, vp, vp, i32, i32, f32, vp]
         L.moe_route_workspace_size.argtypes = [i32, i32]
@@ -146,6 +149,7 @@ def lib():
         for name in ("moe_route_topk", "moe_route_topk_ex", "moe_union", "moe_route_union",
                      "moe_route_union_ex", "moe_expert_forward",
                      "moe_expert_forward_ex", "moe_hit_count", "moe_layer_step",
+                     "moe_layer_step_noalloc",
                      "moe_residual_rmsnorm", "moe_pack_expert"):
             getattr(L, name).restype = i32
         for name in ("moe_route_workspace_size", "moe_forward_workspace_size",
@@ -300,6 +304,34 @@ def layer_step(pool: PoolDesc, x, w_router, b_router, k, topk_ids, topk_w, union
                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 _stream(stream), None if options is None else ctypes.byref(options)),
            "moe_layer_step")
+
+
+def layer_step_noalloc(pool: PoolDesc, x, w_router, b_router, k, topk_ids, topk_w, union_ids,
+                       n_union, expert_offsets, perm, counters, y, stream=None,
+                       options: ForwardOptions | None = None):
+    """moe_layer_step_noalloc: layer_step with the library's own workspace
+    array (no workspace argument, nothing allocated); raises MoeError with
+    MOE_EWORKSPACE when the step needs more than MOE_SCRATCH_BYTES."""
+    import torch
+    _expect(x, torch.float32, "x")
+    _expect(w_router, torch.float32, "w_router")
+    _expect(b_router, torch.float32, "b_router")
+    _expect(topk_w, torch.float32, "topk_w")
+    _expect(y, torch.float32, "y")
+    for t, n in ((topk_ids, "topk_ids"), (union_ids, "union_ids"), (n_union, "n_union"),
+                 (expert_offsets, "expert_offsets"), (perm, "perm")):
+        _expect(t, torch.int32, n)
+    if counters is not None and counters.dtype not in (torch.int64, torch.uint64):
+        raise TypeError("counters: expected a 64-bit integer tensor")
+    if w_router.shape[0] != pool.n_experts:
+        raise ValueError("w_router: expected one row per routed expert of the pool")
+    N, d = x.shape
+    _check(lib().moe_layer_step_noalloc(ctypes.byref(pool), _ptr(x), N, d, _ptr(w_router),
+                                        _ptr(b_router), k, _ptr(topk_ids), _ptr(topk_w),
+                                        _ptr(union_ids), _ptr(n_union), _ptr(expert_offsets),
+                                        _ptr(perm), _ptr(counters), _ptr(y), _stream(stream),
+                                        None if options is None else ctypes.byref(options)),
+           "moe_layer_step_noalloc")
 
 
 def route_union(x, w_router, b_router, k, topk_ids, topk_w, union_ids, n_union, expert_offsets,

@@ -367,3 +367,18 @@ def test_layer_step_argument_checks():
     assert moe.lib().moe_layer_step(None, FAKE, 1, 256, FAKE, None, 1, FAKE, FAKE, FAKE, FAKE,
                                     FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None,
                                     None) == moe.MOE_EINVAL
+
+
+def test_layer_step_noalloc_rejects_oversize_steps_before_any_hip_call():
+    """moe_layer_step_noalloc: a step whose workspace exceeds the library's
+    array (MOE_SCRATCH_BYTES) and a missing pool are refused on the host,
+    so this runs without a GPU."""
+    assert moe.MOE_SCRATCH_BYTES == 64 << 20
+    glm = _pool(d=6144, f=2048, E=256, group=128)
+    assert moe.layer_step_workspace_size(glm, 128, 8) <= moe.MOE_SCRATCH_BYTES
+    assert moe.layer_step_workspace_size(glm, 256, 8) > moe.MOE_SCRATCH_BYTES
+    L = moe.lib()
+    args = (FAKE, 256, 6144, FAKE, None, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+            None)
+    assert L.moe_layer_step_noalloc(ctypes.byref(glm), *args) == moe.MOE_EWORKSPACE
+    assert L.moe_layer_step_noalloc(None, *args) == moe.MOE_EINVAL
