@@ -24,6 +24,12 @@ FLAGS = [
 ]
 
 
+# per-source flags: the matrix-core kernels keep their MFMA results in
+# ordinary vector registers, so the float32 scaling of each step's products
+# reads them directly (no copies out of the accumulation registers)
+EXTRA = {"expert_mfma.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+
+
 def sources(folder=CSRC):
     return sorted(glob.glob(os.path.join(folder, "*.hip")))
 
@@ -38,7 +44,7 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
         for src in sources(folder):
             obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
             libs[lib].append(obj)
-            cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+            cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,

@@ -26,10 +26,12 @@
 //    gate/up epilogue) and are copied into LDS one unit step at a time,
 //    double-buffered, loaded one step ahead;
 //  * each wave owns one or two unit rows and all MT tokens; weight
-//    loads run two steps ahead of the matrix cores.
+//    loads run up to four steps ahead of the matrix cores.
 // Workgroups are mapped so that those sharing an expert (and so its weights
 // and its tokens) land on the same XCD and share its L2.
 #include <hip/hip_ext.h>
+
+#include <type_traits>
 
 #include "internal.h"
 
@@ -70,8 +72,12 @@ __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast
 // int4: the codes of 32-bit word s (element j in bits 4j..4j+3), in the
 //   column order 0,4,1,5,2,6,3,7;
 // int8: the bytes of words 2s and 2s+1, in the column order 0,2,1,3,4,6,5,7.
-// Codes are offset binary: ORed into the mantissa of 1024 and the offset
-// taken off exactly, then (SCALED) one rounding by the scale.
+// Codes are offset binary (u = q + 8). ORed into the mantissa of 1024, a code
+// in bits 0..3 of a half gives 1024 + u, one in bits 4..7 gives 1024 + 16 u
+// (both exact); the first loses 1032 (one packed add), the second is scaled
+// by 1/16 and loses 72 (one packed fused multiply-add): q exactly either way,
+// with one shift per word instead of three. Then (SCALED) one rounding by the
+// scale.
 template <int WB, bool SCALED = true>
 __device__ __forceinline__ half8_t dequant8(const uint4 &u, int s, half2_t s2)
 {
@@ -80,11 +86,13 @@ __device__ __forceinline__ half8_t dequant8(const uint4 &u, int s, half2_t s2)
     half2_t p[4];
     if constexpr (WB == 4) {
         const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
-        const uint32_t w = d[s], m = 0x000F000Fu;
-        p[0] = as_h2(and_or(w, m, magic)) - off;
-        p[1] = as_h2(and_or(w >> 4, m, magic)) - off;
-        p[2] = as_h2(and_or(w >> 8, m, magic)) - off;
-        p[3] = as_h2(and_or(w >> 12, m, magic)) - off;
+        const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+        const half2_t off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+        const uint32_t w = d[s], w8 = w >> 8, lo = 0x000F000Fu, hi = 0x00F000F0u;
+        p[0] = as_h2(and_or(w, lo, magic)) - off;
+        p[1] = __builtin_elementwise_fma(as_h2(and_or(w, hi, magic)), sixteenth, off16);
+        p[2] = as_h2(and_or(w8, lo, magic)) - off;
+        p[3] = __builtin_elementwise_fma(as_h2(and_or(w8, hi, magic)), sixteenth, off16);
     } else {
         const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
         const uint32_t w0 = d[2 * s], w1 = d[2 * s + 1], m = 0x00FF00FFu;
@@ -125,9 +133,9 @@ struct MfmaArgs {
 
 // One workgroup: one MFMA item (<= MT tokens of one expert) x
 // rows_per_wg(GATEUP, MF) rows; each wave owns 16 or 32 rows and all MT
-// tokens. Weight loads run two unit steps
-// ahead of the matrix cores (registers), activations are double-buffered in
-// LDS.
+// tokens. Weight loads run two (128-token items) or four (32-token items)
+// unit steps ahead of the matrix cores (registers), activations are
+// double-buffered in LDS.
 // POST: the codes enter the matrix cores unscaled (exact small integers) and
 // each step's float32 products are scaled per row afterwards; for scale
 // groups that cover whole unit steps (or whole rows), with fewer vector
@@ -230,8 +238,13 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
             sb[t][0] = reinterpret_cast<const float *>(blk + g.off_ds) + s0;
         }
     }
+    // scale group of unit step kb: one value for the whole wave when the
+    // groups cover whole unit steps (or rows), else per lane quarter
+    const int G = g.group;
+    const bool grp_uniform = G == 0 || G % kUC == 0;
     auto load_b = [&](int kb, uint4 (&bw)[TW][NM], float (&bs)[TW][NM]) {
-        const int grp = g.group ? (kb * kUC + q * QW) / g.group : 0;
+        int grp = 0;
+        if (G) grp = grp_uniform ? (kb * kUC) / G : (kb * kUC + q * QW) / G;
 #pragma unroll
         for (int t = 0; t < TW; ++t)
 #pragma unroll
@@ -251,141 +264,125 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[m][t][mb][r] = 0.0f;
 
-    // half of a unit step on LDS buffer `cur` and weights (bw, bs): k-steps
-    // s_lo .. s_lo + NS/2 - 1 of 32, each lane's quarter q covering columns
-    // QW q + 8s .. + 8
-    f32x4_t tmp[POST ? NM : 1][POST ? TW : 1][POST ? MF : 1];  // a step's unscaled products
-    auto compute = [&](int cur, const uint4 (&bw)[TW][NM], const float (&bs)[TW][NM], int s_lo) {
-        half2_t s2[TW][NM];
-#pragma unroll
-        for (int t = 0; t < TW; ++t)
-#pragma unroll
-            for (int m = 0; m < NM; ++m) s2[t][m] = half2_t{(_Float16)bs[t][m], (_Float16)bs[t][m]};
-        if constexpr (POST) {
-            if (s_lo == 0) {
-#pragma unroll
-                for (int m = 0; m < NM; ++m)
-#pragma unroll
-                    for (int t = 0; t < TW; ++t)
-#pragma unroll
-                        for (int mb = 0; mb < MF; ++mb)
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) tmp[m][t][mb][r] = 0.0f;
-            }
-        }
-#pragma unroll
-        for (int s = s_lo; s < s_lo + NS / 2; ++s) {
-            half8_t bf[TW][NM];
+    // weight stages in registers: 32-token items (short steps, fewer
+    // accumulators) keep four steps in flight, 128-token items two
+    constexpr int D = MF <= 2 ? 4 : 2;
+    // The unit-step loop for NB active token blocks of 16: NB = MF, or 1 for a
+    // 32-token item holding at most 16 tokens, whose empty block then costs
+    // no products and no scaling (a choice made once per workgroup).
+    auto main_loop = [&](auto nb_tag) {
+        constexpr int NB = decltype(nb_tag)::value;
+        // half of a unit step on LDS buffer `cur` and weights (bw, bs):
+        // k-steps s_lo .. s_lo + NS/2 - 1 of 32, each lane's quarter q
+        // covering columns QW q + 8s .. + 8
+        f32x4_t tmp[POST ? NM : 1][POST ? TW : 1][POST ? NB : 1];  // a step's unscaled products
+        auto compute = [&](int cur, const uint4 (&bw)[TW][NM], const float (&bs)[TW][NM],
+                           int s_lo) {
+            half2_t s2[TW][NM];
 #pragma unroll
             for (int t = 0; t < TW; ++t)
 #pragma unroll
-                for (int m = 0; m < NM; ++m) bf[t][m] = dequant8<WB, !POST>(bw[t][m], s, s2[t][m]);
+                for (int m = 0; m < NM; ++m)
+                    s2[t][m] = half2_t{(_Float16)bs[t][m], (_Float16)bs[t][m]};
 #pragma unroll
-            for (int mb = 0; mb < MF; ++mb) {
-                // 32-token items: a second token block with no token of the
-                // item is skipped (uniform over the workgroup)
-                if (MF == 2 && mb == 1 && count <= 16) continue;
-                const half8_t af =
-                    *reinterpret_cast<const half8_t *>(&As[cur][mb * 16 + r16][QW * q + 8 * s]);
+            for (int s = s_lo; s < s_lo + NS / 2; ++s) {
+                half8_t bf[TW][NM];
 #pragma unroll
                 for (int t = 0; t < TW; ++t)
 #pragma unroll
-                    for (int m = 0; m < NM; ++m) {
-                        if constexpr (POST)
-                            tmp[m][t][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[t][m],
-                                                                                   tmp[m][t][mb], 0, 0, 0);
-                        else
-                            acc[m][t][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[t][m],
-                                                                                   acc[m][t][mb], 0, 0, 0);
-                    }
-            }
-        }
-        if constexpr (POST) {
-            if (s_lo + NS / 2 == NS) {
-                // the lane's accumulator column is its weight row (r16): one
-                // scale for its four tokens
+                    for (int m = 0; m < NM; ++m)
+                        bf[t][m] = dequant8<WB, !POST>(bw[t][m], s, s2[t][m]);
 #pragma unroll
-                for (int m = 0; m < NM; ++m)
+                for (int mb = 0; mb < NB; ++mb) {
+                    const half8_t af =
+                        *reinterpret_cast<const half8_t *>(&As[cur][mb * 16 + r16][QW * q + 8 * s]);
 #pragma unroll
                     for (int t = 0; t < TW; ++t)
 #pragma unroll
-                        for (int mb = 0; mb < MF; ++mb)
+                        for (int m = 0; m < NM; ++m) {
+                            if constexpr (POST) {
+                                // the step's first k-step starts from zero
+                                const f32x4_t c0 = {0.0f, 0.0f, 0.0f, 0.0f};
+                                tmp[m][t][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    af, bf[t][m], s == 0 ? c0 : tmp[m][t][mb], 0, 0, 0);
+                            } else {
+                                acc[m][t][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    af, bf[t][m], acc[m][t][mb], 0, 0, 0);
+                            }
+                        }
+                }
+            }
+            if constexpr (POST) {
+                if (s_lo + NS / 2 == NS) {
+                    // the lane's accumulator column is its weight row (r16):
+                    // one scale for its four tokens
 #pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                acc[m][t][mb][r] = fmaf(bs[t][m], tmp[m][t][mb][r], acc[m][t][mb][r]);
+                    for (int m = 0; m < NM; ++m)
+#pragma unroll
+                        for (int t = 0; t < TW; ++t)
+#pragma unroll
+                            for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    acc[m][t][mb][r] =
+                                        fmaf(bs[t][m], tmp[m][t][mb][r], acc[m][t][mb][r]);
+                }
+            }
+        };
+
+        // weights: a ring of D register stages (stage j holds the steps ks
+        // with ks % D == j), each reloaded with the step D ahead right after
+        // its products, so a load has D - 1 steps to arrive; activations: one
+        // register stage of half a step, loaded during the current step's
+        // products and stored to the other LDS buffer. D is even, so the LDS
+        // buffer of step ks + j (ks a multiple of D) is j % 2.
+        uint4 av[kVec];
+        uint4 bwr[D][TW][NM];
+        float bsr[D][TW][NM];
+        load_a(0, 0, av);
+#pragma unroll
+        for (int j = 0; j < D; ++j) load_b(min(j, n_kb - 1), bwr[j], bsr[j]);
+        store_a(0, 0, av);
+        if constexpr (NA == 2) {
+            load_a(0, 1, av);
+            store_a(0, 1, av);
+        }
+        __syncthreads();
+        // one step: products on LDS buffer `cur`; the next step's activations
+        // are loaded before the products and stored to the other buffer after
+        // them, so their latency is covered by the whole step. Loads are
+        // issued on every step (the last step reloads its own activations into
+        // the buffer no later step reads, the last D steps reload their
+        // weights), so that no load sits in a branch: each wait is then for the
+        // load it needs, not for every load in flight.
+        auto step = [&](int ks, int cur, const uint4 (&bw)[TW][NM], const float (&bs)[TW][NM]) {
+            const int kn = min(ks + 1, n_kb - 1);
+            uint4 an0[kVec], an1[kVec];
+            load_a(kn, 0, an0);
+            if constexpr (NA == 2) load_a(kn, 1, an1);
+            __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the products
+            compute(cur, bw, bs, 0);
+            compute(cur, bw, bs, NS / 2);
+            store_a(cur ^ 1, 0, an0);
+            if constexpr (NA == 2) store_a(cur ^ 1, 1, an1);
+            __syncthreads();
+        };
+        for (int ks = 0; ks < n_kb; ks += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                if (ks + j >= n_kb) break;
+                step(ks + j, j & 1, bwr[j], bsr[j]);
+                load_b(min(ks + j + D, n_kb - 1), bwr[j], bsr[j]);
             }
         }
     };
-
-    // weights: a ring of two register stages (stage j holds step ks with
-    // ks % 2 == j); activations: one register stage
-    // of half a step, loaded during the current step's products and stored to
-    // the other LDS buffer
-    uint4 av[kVec];
-    uint4 bw0[TW][NM], bw1[TW][NM];
-    float bs0[TW][NM], bs1[TW][NM];
-    load_a(0, 0, av);
-    load_b(0, bw0, bs0);
-    load_b(min(1, n_kb - 1), bw1, bs1);
-    store_a(0, 0, av);
-    if constexpr (NA == 2) {
-        load_a(0, 1, av);
-        store_a(0, 1, av);
-    }
-    __syncthreads();
-    // one step: products on LDS buffer `cur`; the next step's activations are
-    // loaded before the products and stored to the other buffer after them,
-    // so their latency is covered by the whole step. Loads are issued on
-    // every step (the last step reloads its own activations into the buffer
-    // no later step reads, the last two steps reload their weights), so that
-    // no load sits in a branch: each wait is then for the load it needs, not
-    // for every load in flight.
-    auto step = [&](int ks, int cur, const uint4 (&bw)[TW][NM], const float (&bs)[TW][NM]) {
-        const int kn = min(ks + 1, n_kb - 1);
-        uint4 an0[kVec], an1[kVec];
-        load_a(kn, 0, an0);
-        if constexpr (NA == 2) load_a(kn, 1, an1);
-        __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the products
-        compute(cur, bw, bs, 0);
-        compute(cur, bw, bs, NS / 2);
-        store_a(cur ^ 1, 0, an0);
-        if constexpr (NA == 2) store_a(cur ^ 1, 1, an1);
-        __syncthreads();
-    };
-    // Small items (short steps) compute from a copy of the stage, so the
-    // stage is reloaded before the products; large items (long steps, more
-    // registers) reload the stage after them.
-    constexpr bool kEarly = MF <= 2;
-    for (int ks = 0; ks < n_kb; ks += 2) {
-        // even step ks: LDS buffer 0, weights in stage 0
-        if constexpr (kEarly) {
-            uint4 bw[TW][NM];
-            float bs[TW][NM];
-#pragma unroll
-            for (int t = 0; t < TW; ++t)
-#pragma unroll
-                for (int m = 0; m < NM; ++m) { bw[t][m] = bw0[t][m]; bs[t][m] = bs0[t][m]; }
-            load_b(min(ks + 2, n_kb - 1), bw0, bs0);
-            step(ks, 0, bw, bs);
-        } else {
-            step(ks, 0, bw0, bs0);
-            load_b(min(ks + 2, n_kb - 1), bw0, bs0);
-        }
-        if (ks + 1 >= n_kb) break;
-        // odd step ks + 1: LDS buffer 1, weights in stage 1
-        if constexpr (kEarly) {
-            uint4 bw[TW][NM];
-            float bs[TW][NM];
-#pragma unroll
-            for (int t = 0; t < TW; ++t)
-#pragma unroll
-                for (int m = 0; m < NM; ++m) { bw[t][m] = bw1[t][m]; bs[t][m] = bs1[t][m]; }
-            load_b(min(ks + 3, n_kb - 1), bw1, bs1);
-            step(ks + 1, 1, bw, bs);
-        } else {
-            step(ks + 1, 1, bw1, bs1);
-            load_b(min(ks + 3, n_kb - 1), bw1, bs1);
-        }
+    if constexpr (MF == 2) {
+        if (count <= 16)
+            main_loop(std::integral_constant<int, 1>());
+        else
+            main_loop(std::integral_constant<int, 2>());
+    } else {
+        main_loop(std::integral_constant<int, MF>());
     }
 
     // epilogue: register r of block (t, mb) is token mb*16 + 4q + r, weight
