@@ -735,13 +735,16 @@ def main():
 
 
 def cache_bench(args):
-    """Place stage: each layer's routed experts in pinned host memory, an HBM
-    cache of C slots per layer (moe_cache_*, least recently used
-    replacement). A step routes the batch (moe_route_union), copies the union
-    to the host, places it (missing blocks copied on a second stream), then
-    runs the expert math through the slot table. Reported per slot count:
-    tokens/s, the hit rate over the timed steps and the bytes copied per
-    token next to the L*k*S*(1-h) estimate (here L = 1 layer per step)."""
+    """Place and Overlap stages: each layer's routed experts in pinned host
+    memory, an HBM cache of C slots per layer (moe_cache_*, least recently
+    used replacement). A step routes the batch (moe_route_union) and copies
+    the union to the host; then either ("place") places it, the missing
+    blocks copied on a second stream, and runs the expert math through the
+    slot table, or ("overlap", moe_cache_forward) runs the resident experts'
+    math while the missing blocks are copied, then the rest. Reported per
+    slot count and mode: tokens/s, the hit rate over the timed steps and the
+    bytes copied per token next to the L*k*S*(1-h) estimate (here L = 1
+    layer per step); and the step time with every expert resident."""
     import numpy as np
     import torch
 
@@ -749,7 +752,7 @@ def cache_bench(args):
     import synth
 
     dev = torch.device("cuda:0")
-    base = synth.CONFIGS[args.config]
+    base = synth.CONFIGS[args.config or "decode1"]
     if len(base.layers) > 1:
         sys.exit("--cache-slots measures single-layer workloads")
     spec = base.layer
@@ -786,42 +789,77 @@ def cache_bench(args):
                      device=dev)
     copy_stream = torch.cuda.Stream()  # default priority
     block = moe.block_bytes(d, f, spec.wbits, spec.group)
-    points = []
-    for C in [int(c) for c in args.cache_slots.split(",")]:
-        caches = [moe.ExpertCache(ly["desc"], C, ly["host"], dev) for ly in layers]
+
+    def resident_step_ms():
+        """the same steps with every expert resident (the compute alone)"""
+        pools = [moe.DevicePool(d, f, E, spec.wbits, spec.group, synth.expert_pool(cfg, l),
+                                synth.shared_block(cfg, l), dev) for l in range(L_rot)]
 
         def run(s_):
-            ly, cache = layers[s_ % L_rot], caches[s_ % L_rot]
+            ly, pl = layers[s_ % L_rot], pools[s_ % L_rot]
             x = xs[s_ % nb]
             moe.route_union(x, ly["wr"], ly["b"], k, ids, w, uid, nu, off, perm, cnt, ws)
-            n = int(nu.item())
-            cache.place(uid[:n].cpu().numpy(), copy_stream=copy_stream)
-            moe.expert_forward(cache.desc, x, k, w, uid, nu, off, perm, y, ws)
+            moe.expert_forward(pl.desc, x, k, w, uid, nu, off, perm, y, ws)
 
-        for s_ in range(args.warmup):
+        for s_ in range(min(args.warmup, 50)):
             run(s_)
         torch.cuda.synchronize()
-        h0 = [c.stats() for c in caches]
         t0 = time.perf_counter()
         for s_ in range(args.steps):
-            run(args.warmup + s_)
+            run(s_)
         torch.cuda.synchronize()
-        el = time.perf_counter() - t0
-        hits = sum(c.stats()[0] - h[0] for c, h in zip(caches, h0))
-        misses = sum(c.stats()[1] - h[1] for c, h in zip(caches, h0))
-        hr = hits / max(1, hits + misses)
-        tok = N * args.steps
-        points.append({"slots": C, "tokens_per_s": tok / el, "ms_per_step": el / args.steps * 1e3,
-                       "hit_rate": hr, "misses_per_step": misses / args.steps,
-                       "copied_bytes_per_token": misses * block / tok,
-                       "estimate_bytes_per_token": k * block * (1 - hr),
-                       "copied_GBps": misses * block / el / 1e9})
-        print(f"[cache bench] {C} slots: {points[-1]}", file=sys.stderr, flush=True)
-        for c in caches:
-            c.close()
-        del caches
+        el = (time.perf_counter() - t0) / args.steps * 1e3
+        del pools
+        torch.cuda.empty_cache()
+        return el
+
+    t_res = resident_step_ms()
+    points = []
+    for C in [int(c) for c in args.cache_slots.split(",")]:
+        for mode in ("place", "overlap"):
+            caches = [moe.ExpertCache(ly["desc"], C, ly["host"], dev) for ly in layers]
+
+            def run(s_):
+                ly, cache = layers[s_ % L_rot], caches[s_ % L_rot]
+                x = xs[s_ % nb]
+                moe.route_union(x, ly["wr"], ly["b"], k, ids, w, uid, nu, off, perm, cnt, ws)
+                n = int(nu.item())
+                union = uid[:n].cpu().numpy()
+                if mode == "overlap":
+                    # Place + Overlap: resident experts compute while the
+                    # missing ones are copied in
+                    cache.forward(x, k, w, uid, nu, off, perm, union, y, ws,
+                                  copy_stream=copy_stream)
+                else:
+                    cache.place(union, copy_stream=copy_stream)
+                    moe.expert_forward(cache.desc, x, k, w, uid, nu, off, perm, y, ws)
+
+            for s_ in range(args.warmup):
+                run(s_)
+            torch.cuda.synchronize()
+            h0 = [c.stats() for c in caches]
+            t0 = time.perf_counter()
+            for s_ in range(args.steps):
+                run(args.warmup + s_)
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t0
+            hits = sum(c.stats()[0] - h[0] for c, h in zip(caches, h0))
+            misses = sum(c.stats()[1] - h[1] for c, h in zip(caches, h0))
+            hr = hits / max(1, hits + misses)
+            tok = N * args.steps
+            points.append({"slots": C, "mode": mode, "tokens_per_s": tok / el,
+                           "ms_per_step": el / args.steps * 1e3,
+                           "hit_rate": hr, "misses_per_step": misses / args.steps,
+                           "copied_bytes_per_token": misses * block / tok,
+                           "estimate_bytes_per_token": k * block * (1 - hr),
+                           "copied_GBps": misses * block / el / 1e9})
+            print(f"[cache bench] {C} slots, {mode}: {points[-1]}", file=sys.stderr, flush=True)
+            for c in caches:
+                c.close()
+            del caches
     print(json.dumps({"metric": "layer-step tokens/s with experts placed from pinned host memory "
-                                "into an HBM cache (Place stage)",
+                                "into an HBM cache (Place stage, without and with Overlap)",
+                      "resident_ms_per_step": t_res,
                       "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                       "data": "synthetic",
                       "config": {"workload": f"{cfg.name}: {base.description}; {L_rot} layers, "

@@ -1,9 +1,10 @@
 /*
- * moe_cache.h - Place stage: a layer's routed experts held in a host tier
- * (pinned host memory) with an HBM cache of a fixed number of block slots,
- * per-layer least-recently-used replacement, and missing experts copied in
- * on a copy stream (the GPU's DMA engines) before the expert math that
- * needs them.
+ * moe_cache.h - Place and Overlap stages: a layer's routed experts held in a
+ * host tier (pinned host memory) with an HBM cache of a fixed number of block
+ * slots, per-layer least-recently-used replacement, and missing experts
+ * copied in on a copy stream (the GPU's DMA engines), either before the
+ * expert math (moe_cache_place) or while the resident experts compute
+ * (moe_cache_forward).
  *
  * Colibri pages: "Public Colibri Observation and Revision Ledger", section
  * "Exact Architecture and Data-Flow Reconstruction" (stage (3) Place: load
@@ -68,8 +69,44 @@ moe_status moe_cache_place(moe_cache *cache, const int32_t *union_ids, int n_uni
                            hipStream_t copy_stream, hipStream_t compute_stream,
                            int32_t *n_missed);
 
-/* Totals of moe_cache_place since creation: experts found resident, experts
- * copied in (pins and prefetches are not counted). */
+/*
+ * Place and Overlap, then the expert math, of one layer step through the
+ * cache (the pages' stages (3) and (4): the experts of a batch that are
+ * already in the fast tier are computed while the missing ones are read in).
+ * The union (union_host, as for moe_cache_place) is placed: hits and misses
+ * as in moe_cache_place, the block copies and the new slot table enqueued on
+ * copy_stream after the work already on compute_stream. Then, on
+ * compute_stream, without waiting for the copies: the expert kernels of the
+ * union's resident experts and of the shared expert. Then compute_stream
+ * waits for the copies and runs the kernels of the copied experts and the
+ * combine. When nothing is missing, one ordinary forward. y equals
+ * moe_expert_forward on a pool with every expert resident, bit for bit (the
+ * same kernels on the same work items).
+ *   shape: the layer's descriptor (d_model, d_ff, n_experts == the cache's,
+ *     wbits, group, shared); its pool, expert_bytes, slot_of and n_slots
+ *     are replaced by the cache's slots and table.
+ *   x ... perm, y, workspace, ws_bytes: as for moe_expert_forward (the device
+ *     union outputs of the same batch); union_host / n_union_host: the same
+ *     union on the host.
+ *   n_missed (host, may be NULL): experts copied in.
+ * Hits and misses count in moe_cache_stats. The cache keeps a small device
+ * array of each call's split, so successive calls on one cache must be
+ * ordered on compute_stream (the same stream, or streams the caller orders).
+ * Errors: those of moe_expert_forward and moe_cache_place (MOE_ESHAPE also
+ * when shape does not match the cache's blocks), checked before anything is
+ * enqueued or changed.
+ */
+moe_status moe_cache_forward(moe_cache *cache, const moe_expert_pool *shape /* (host) */,
+                             const float *x, int n_tokens, int k, const float *topk_w,
+                             const int32_t *union_ids, const int32_t *n_union,
+                             const int32_t *expert_offsets, const int32_t *perm,
+                             const int32_t *union_host /* (host) */, int n_union_host,
+                             float *y, void *workspace, size_t ws_bytes,
+                             hipStream_t copy_stream, hipStream_t compute_stream,
+                             int32_t *n_missed);
+
+/* Totals of moe_cache_place and moe_cache_forward since creation: experts
+ * found resident, experts copied in (pins and prefetches are not counted). */
 moe_status moe_cache_stats(const moe_cache *cache, uint64_t *hits, uint64_t *misses);
 
 /*

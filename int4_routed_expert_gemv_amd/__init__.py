@@ -44,7 +44,8 @@ MOE_SCRATCH_BYTES = 64 << 20  # the workspace array of moe_layer_step_noalloc, p
 # measured-ceiling probes (include/moe_probe.h), not part of the layer step
 PROBE_EXPORTED = ["moe_probe_stream_read", "moe_probe_mfma_f16"]
 # the expert cache of the Place stage (include/moe_cache.h)
-CACHE_EXPORTED = ["moe_cache_create", "moe_cache_destroy", "moe_cache_place", "moe_cache_stats",
+CACHE_EXPORTED = ["moe_cache_create", "moe_cache_destroy", "moe_cache_place", "moe_cache_forward",
+                  "moe_cache_stats",
                   "moe_cache_pin", "moe_cache_prefetch", "moe_cache_resident", "moe_usage_write",
                   "moe_usage_read", "moe_usage_hottest"]
 
@@ -131,6 +132,9 @@ def lib():
         L.moe_cache_destroy.restype = None
         L.moe_cache_place.argtypes = [vp, vp, i32, vp, vp, vp]
         L.moe_cache_place.restype = i32
+        L.moe_cache_forward.argtypes = [vp, P, vp, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp,
+                                        sz, vp, vp, vp]
+        L.moe_cache_forward.restype = i32
         L.moe_cache_stats.argtypes = [vp, vp, vp]
         L.moe_cache_stats.restype = i32
         for name in ("moe_cache_pin", "moe_cache_prefetch"):
@@ -473,6 +477,24 @@ class ExpertCache:
         _check(lib().moe_cache_place(self.handle, ids.ctypes.data if ids.size else None, ids.size,
                                      _stream(copy_stream), _stream(compute_stream),
                                      ctypes.byref(missed)), "moe_cache_place")
+        return int(missed.value)
+
+    def forward(self, x, k, topk_w, union_ids, n_union, expert_offsets, perm, union_host, y,
+                workspace, copy_stream=None, compute_stream=None) -> int:
+        """moe_cache_forward: Place the union (union_host, int32 numpy) and
+        run the expert math with the copies overlapping the resident experts'
+        kernels; returns the number of experts copied in."""
+        ids = np.ascontiguousarray(union_host, np.int32)
+        missed = ctypes.c_int32(0)
+        N = x.shape[0]
+        _check(lib().moe_cache_forward(self.handle, ctypes.byref(self.desc), _ptr(x), N, k,
+                                       _ptr(topk_w), _ptr(union_ids), _ptr(n_union),
+                                       _ptr(expert_offsets), _ptr(perm),
+                                       ids.ctypes.data if ids.size else None, ids.size, _ptr(y),
+                                       _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(copy_stream), _stream(compute_stream),
+                                       ctypes.byref(missed)), "moe_cache_forward")
         return int(missed.value)
 
     def pin(self, ids_host, copy_stream=None, compute_stream=None) -> int:

@@ -452,12 +452,18 @@ struct InRoute {
     uint64_t *counters;
 };
 
+// The phase of a two-phase forward (Fwd::phase), or none.
+struct Phase {
+    const uint8_t *mask;
+    int sel;
+};
+
 static moe_status forward_impl(const moe_expert_pool *pool, const float *x, int n_tokens, int k,
                                const float *topk_w, const int32_t *union_ids,
                                const int32_t *n_union, const int32_t *expert_offsets,
                                const int32_t *perm, float *y, void *workspace, size_t ws_bytes,
                                hipStream_t stream, const moe_forward_options *ev,
-                               bool check_only, const InRoute *ir)
+                               bool check_only, const InRoute *ir, const Phase *ph = nullptr)
 {
     Geo g;
     moe_status st = resolve_geo(pool, &g);
@@ -532,6 +538,10 @@ static moe_status forward_impl(const moe_expert_pool *pool, const float *x, int 
     // give the same sum in either order, so y is deterministic and equal to
     // the combine kernel's; one launch fewer.
     f.direct = (L.max_mitems == 0 && L.max_sitems == 0 && k + has_shared <= 2) ? 1 : 0;
+    // a two-phase forward combines once, after its second phase
+    f.phase = ph ? ph->mask : nullptr;
+    f.phase_sel = ph ? ph->sel : 0;
+    if (ph) f.direct = 0;
 
     f.ev_gu[0] = ev ? ev->gateup_start : nullptr;
     f.ev_gu[1] = ev ? ev->gateup_end : nullptr;
@@ -555,11 +565,12 @@ static moe_status forward_impl(const moe_expert_pool *pool, const float *x, int 
     if (launch_down(f, stream) != hipSuccess) return MOE_EHIP;
     if (launch_mfma(f, false, false, stream) != hipSuccess) return MOE_EHIP;
     if (launch_mfma(f, false, true, stream) != hipSuccess) return MOE_EHIP;
-    if (!f.direct &&
+    if (!f.direct && (!ph || ph->sel == 1) &&
         launch_combine(f.o, topk_w, n_tokens, k, g.d, (int)A, has_shared, y, stream) != hipSuccess)
         return MOE_EHIP;
     return MOE_OK;
 }
+
 
 moe_status moe_expert_forward_ex(const moe_expert_pool *pool, const float *x, int n_tokens, int k,
                                  const float *topk_w, const int32_t *union_ids,
@@ -710,3 +721,20 @@ moe_status moe_pack_expert(const void *canonical_block, const moe_expert_pool *s
 }
 
 }  // extern "C"
+
+namespace moe {
+
+moe_status expert_forward_phase(const moe_expert_pool *pool, const float *x, int n_tokens, int k,
+                                const float *topk_w, const int32_t *union_ids,
+                                const int32_t *n_union, const int32_t *expert_offsets,
+                                const int32_t *perm, float *y, void *workspace, size_t ws_bytes,
+                                hipStream_t stream, const uint8_t *phase, int phase_sel,
+                                bool check_only)
+{
+    Phase ph{phase, phase_sel};
+    return forward_impl(pool, x, n_tokens, k, topk_w, union_ids, n_union, expert_offsets, perm,
+                        y, workspace, ws_bytes, stream, nullptr, check_only, nullptr,
+                        phase ? &ph : nullptr);
+}
+
+}  // namespace moe

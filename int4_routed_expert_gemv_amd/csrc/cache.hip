@@ -1,7 +1,7 @@
-// cache.hip - Place stage: an HBM cache of expert block slots over a host
-// tier, per-layer least-recently-used replacement, block copies on a copy
-// stream, pinned experts, prefetch hints, and the persisted hit counters
-// (host code only).
+// cache.hip - Place and Overlap stages: an HBM cache of expert block slots
+// over a host tier, per-layer least-recently-used replacement, block copies
+// on a copy stream while the resident experts compute, pinned experts,
+// prefetch hints, and the persisted hit counters (host code only).
 //
 // Colibri pages: "Public Colibri Observation and Revision Ledger", section
 // "Exact Architecture and Data-Flow Reconstruction" (stage (3) Place, stage
@@ -40,6 +40,12 @@ struct moe_cache {
     hipEvent_t computed = nullptr;    // work on the compute stream before the copies
     int cur = 0;
     unsigned long long hits = 0, misses = 0;
+    // Overlap (moe_cache_forward): which experts of a step wait for copies
+    uint8_t *phase_dev = nullptr;     // device [E]: 0 resident, 1 being copied in
+    uint8_t *phase_staging = nullptr; // pinned [2][E]
+    hipEvent_t phase_sent[2] = {nullptr, nullptr};
+    bool phase_pending[2] = {false, false};
+    int phase_cur = 0;
 };
 
 namespace {
@@ -55,6 +61,14 @@ void release(moe_cache *c)
     }
     if (c->computed) (void)hipEventDestroy(c->computed);
     if (c->staging) (void)hipHostFree(c->staging);
+    for (int i = 0; i < 2; ++i) {
+        if (c->phase_sent[i]) {
+            if (c->phase_pending[i]) (void)hipEventSynchronize(c->phase_sent[i]);
+            (void)hipEventDestroy(c->phase_sent[i]);
+        }
+    }
+    if (c->phase_staging) (void)hipHostFree(c->phase_staging);
+    if (c->phase_dev) (void)hipFree(c->phase_dev);
     delete c;
 }
 
@@ -196,13 +210,19 @@ moe_status moe_cache_create(int n_experts, int n_slots, size_t block_bytes, size
     c->used.assign(n_slots, 0);
     if (hipHostMalloc(reinterpret_cast<void **>(&c->staging), 2 * sizeof(int32_t) * n_experts,
                       hipHostMallocDefault) != hipSuccess ||
+        hipHostMalloc(reinterpret_cast<void **>(&c->phase_staging), 2 * (size_t)n_experts,
+                      hipHostMallocDefault) != hipSuccess ||
+        hipMalloc(reinterpret_cast<void **>(&c->phase_dev), (size_t)n_experts) != hipSuccess ||
         hipEventCreateWithFlags(&c->copied[0], hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&c->copied[1], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&c->phase_sent[0], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&c->phase_sent[1], hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&c->computed, hipEventDisableTiming) != hipSuccess) {
         release(c);
         return MOE_EHIP;
     }
     for (int e = 0; e < n_experts; ++e) c->staging[e] = -1;
+    memset(c->phase_staging, 0, 2 * (size_t)n_experts);
     if (hipMemcpy(slot_table, c->staging, sizeof(int32_t) * n_experts, hipMemcpyHostToDevice) !=
         hipSuccess) {
         release(c);
@@ -228,6 +248,90 @@ moe_status moe_cache_place(moe_cache *c, const int32_t *union_ids, int n_union,
                                     true, &missed);
     if (n_missed) *n_missed = missed;
     return st;
+}
+
+moe_status moe_cache_forward(moe_cache *c, const moe_expert_pool *shape, const float *x,
+                             int n_tokens, int k, const float *topk_w, const int32_t *union_ids,
+                             const int32_t *n_union, const int32_t *expert_offsets,
+                             const int32_t *perm, const int32_t *union_host, int n_union_host,
+                             float *y, void *workspace, size_t ws_bytes, hipStream_t copy_stream,
+                             hipStream_t compute_stream, int32_t *n_missed)
+{
+    if (!c || !shape || n_union_host < 0 || (n_union_host > 0 && !union_host)) return MOE_EINVAL;
+    if (n_missed) *n_missed = 0;
+    if (shape->n_experts != c->E) return MOE_ESHAPE;
+    if (moe_block_bytes(shape->d_model, shape->d_ff, shape->wbits, shape->group) != c->bytes)
+        return MOE_ESHAPE;
+    // the layer as the expert kernels see it: the cache's slots and table
+    moe_expert_pool p = *shape;
+    p.pool = c->slots;
+    p.expert_bytes = c->stride;
+    p.slot_of = c->table_dev;
+    p.n_slots = c->C;
+    // every check of moe_expert_forward, and the room for the union, before
+    // anything changes or is enqueued
+    moe_status st = moe::expert_forward_phase(&p, x, n_tokens, k, topk_w, union_ids, n_union,
+                                              expert_offsets, perm, y, workspace, ws_bytes,
+                                              compute_stream, c->phase_dev, 0, true);
+    if (st != MOE_OK) return st;
+    int distinct, unpinned;
+    count_distinct(c, union_host, n_union_host, &distinct, &unpinned);
+    if (unpinned > c->C - c->n_pinned) return MOE_ESHAPE;
+    if (n_tokens == 0) return MOE_OK;
+    // copies of an earlier prefetch, not yet waited for: their experts count
+    // as resident below, so the compute stream waits for them first
+    if (c->unwaited) {
+        const int last = c->cur ^ 1;
+        if (hipStreamWaitEvent(compute_stream, c->copied[last], 0) != hipSuccess) return MOE_EHIP;
+        c->unwaited = false;
+    }
+    // phase of each union expert before placement: 0 resident, 1 copied in
+    const int b = c->phase_cur;
+    if (c->phase_pending[b] && hipEventSynchronize(c->phase_sent[b]) != hipSuccess)
+        return MOE_EHIP;
+    uint8_t *ph = c->phase_staging + (size_t)b * c->E;
+    int to_copy = 0;
+    for (int i = 0; i < n_union_host; ++i) {
+        const int e = union_host[i];
+        if (e < 0 || e >= c->E) continue;
+        ph[e] = c->slot_of[e] >= 0 ? 0 : 1;
+        to_copy += ph[e];
+    }
+    int missed = 0;
+    if (to_copy == 0) {
+        // nothing to copy: one plain forward
+        st = place_ids(c, union_host, n_union_host, copy_stream, compute_stream, true, true,
+                       &missed);
+        if (st != MOE_OK) return st;
+        return moe::expert_forward_phase(&p, x, n_tokens, k, topk_w, union_ids, n_union,
+                                         expert_offsets, perm, y, workspace, ws_bytes,
+                                         compute_stream, nullptr, 0, false);
+    }
+    if (hipMemcpyAsync(c->phase_dev, ph, (size_t)c->E, hipMemcpyHostToDevice, compute_stream) !=
+            hipSuccess ||
+        hipEventRecord(c->phase_sent[b], compute_stream) != hipSuccess)
+        return MOE_EHIP;
+    c->phase_pending[b] = true;
+    c->phase_cur = b ^ 1;
+    // Place: block copies and the new slot table on the copy stream (after
+    // the work already on the compute stream); the compute stream does not
+    // wait for them yet
+    st = place_ids(c, union_host, n_union_host, copy_stream, compute_stream, false, true, &missed);
+    if (st != MOE_OK) return st;
+    if (n_missed) *n_missed = missed;
+    // Overlap: the resident experts and the shared expert while the copies
+    // run (their slots and table entries do not change in this call), then
+    // the copied experts and the combine
+    st = moe::expert_forward_phase(&p, x, n_tokens, k, topk_w, union_ids, n_union,
+                                   expert_offsets, perm, y, workspace, ws_bytes, compute_stream,
+                                   c->phase_dev, 0, false);
+    if (st != MOE_OK) return st;
+    const int last = c->cur ^ 1;  // the event place_ids recorded after this call's copies
+    if (hipStreamWaitEvent(compute_stream, c->copied[last], 0) != hipSuccess) return MOE_EHIP;
+    c->unwaited = false;
+    return moe::expert_forward_phase(&p, x, n_tokens, k, topk_w, union_ids, n_union,
+                                     expert_offsets, perm, y, workspace, ws_bytes,
+                                     compute_stream, c->phase_dev, 1, false);
 }
 
 moe_status moe_cache_prefetch(moe_cache *c, const int32_t *ids, int n, hipStream_t copy_stream,

@@ -432,6 +432,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
         if (wg == 0 && tid == 0 && it.count > 0) f.items[item_idx] = it;
         if (it.count <= 0) return;  // uniform: inconsistent offsets give no tokens
     }
+    if (!in_phase(f, it.expert)) return;  // uniform: the other phase's item
     const int count = min(it.count, TB);
 
     const uint8_t *blk = expert >= 0 ? expert_block(f, expert) : f.shared;

@@ -171,6 +171,7 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
     const int item_idx = logical / ma.n_tiles;
     const int ntile = logical % ma.n_tiles;
     const Item it = ma.items[item_idx];
+    if (!in_phase(f, it.expert)) return;  // uniform: the other phase's item
     const int count = min(it.count, MT);
     const uint8_t *blk = it.expert >= 0 ? expert_block(f, it.expert) : f.shared;
     const int K = GATEUP ? g.d : g.f;       // contraction length

@@ -65,6 +65,12 @@ struct Fwd {
     uint16_t *x16;           // [N][d] layer input
     uint16_t *h16;           // [A + N][f] hidden
     float *y;                // [N][d] layer output
+    // Two-phase forward (the cache's Overlap): when phase is not null, the
+    // expert kernels compute only the items of routed experts e with
+    // phase[e] == phase_sel, and of the shared expert when phase_sel == 0;
+    // the other workgroups leave at once.
+    const uint8_t *phase;    // [E] 0 or 1, or null: every item
+    int phase_sel;
     int direct;              // 1: the GEMV down kernel adds the gate-weighted rows into y
                              // itself (at most two addends per element, y cleared by
                              // the gate/up kernel); 0: the combine kernel writes y
@@ -99,6 +105,13 @@ struct Fwd {
     hipEvent_t ev_sdn[2];    // optional: the same for the 32-token MFMA down kernel
 };
 
+// Whether the current phase computes the item of this expert (-1: shared).
+__device__ __forceinline__ bool in_phase(const Fwd &f, int expert)
+{
+    if (!f.phase) return true;
+    return (expert >= 0 ? (int)f.phase[expert] : 0) == f.phase_sel;
+}
+
 // Block of routed expert e (0 <= e < E): its own place in the pool, or the
 // slot the expert cache gave it.
 __device__ __forceinline__ const uint8_t *expert_block(const Fwd &f, int e)
@@ -109,6 +122,16 @@ __device__ __forceinline__ const uint8_t *expert_block(const Fwd &f, int e)
 
 // ---- host helpers (abi.hip) --------------------------------------------
 moe_status resolve_geo(const moe_expert_pool *p, Geo *g);
+// moe_expert_forward restricted to one phase of a two-phase forward (see
+// Fwd::phase): phase_sel 0 computes the experts with phase[e] == 0 and the
+// shared expert, 1 the others and then the combine. check_only: the
+// argument checks alone, nothing enqueued.
+moe_status expert_forward_phase(const moe_expert_pool *pool, const float *x, int n_tokens, int k,
+                                const float *topk_w, const int32_t *union_ids,
+                                const int32_t *n_union, const int32_t *expert_offsets,
+                                const int32_t *perm, float *y, void *workspace, size_t ws_bytes,
+                                hipStream_t stream, const uint8_t *phase, int phase_sel,
+                                bool check_only);
 
 // ---- launchers (each in its own translation unit) ----------------------
 // Router: final scores [N][E], or raw partial sums [P][N][E] over P slices of

@@ -60,6 +60,13 @@ def lib():
         L.oracle_expert_forward.argtypes = [vp, sz, i32, vp, i32, i32, i32, i32,
                                             vp, i32, i32, vp, vp, vp]
         L.oracle_rms_normalize.argtypes = [vp, i32, i32, ctypes.c_double, vp]
+        u64p = vp
+        L.oracle_cache_place.restype = i32
+        L.oracle_cache_place.argtypes = [i32, i32, vp, u64p, vp, u64p, vp, i32, vp, vp]
+        L.oracle_cache_pin.restype = i32
+        L.oracle_cache_pin.argtypes = [i32, i32, vp, u64p, vp, u64p, vp, i32, vp]
+        L.oracle_cache_prefetch.argtypes = [i32, i32, vp, u64p, vp, u64p, vp, i32, vp]
+        L.oracle_usage_hottest.argtypes = [vp, i32, i32, vp]
         L.oracle_threads.restype = i32
         L.oracle_threads.argtypes = []
         _lib = L
@@ -202,3 +209,57 @@ def layer_step(x, w_router, b_router, k, pool, shared, d, f, wbits, group, count
     y = expert_forward(pool, shared, d, f, wbits, group, x, ids, w)
     return dict(scores=s, ids=ids, w=w, union_ids=u, offsets=off, perm=perm,
                 counters=counters, y=y)
+
+
+class LruCache:
+    """Place stage: a per-layer LRU cache of n_slots expert blocks (the
+    arithmetic is oracle_cache_* in oracle.c; this class only holds the
+    state arrays). place/pin/prefetch return (hits, misses), misses and
+    copies; place and pin raise ValueError when refused (state unchanged)."""
+
+    def __init__(self, n_slots, n_experts):
+        self.n_slots, self.n_experts = n_slots, n_experts
+        self.expert_in = np.full(n_slots, -1, np.int32)
+        self.last_use = np.zeros(n_slots, np.uint64)
+        self.pinned = np.zeros(n_slots, np.int32)
+        self.clock = np.zeros(1, np.uint64)
+
+    def _args(self):
+        return (self.n_slots, self.n_experts, self.expert_in.ctypes.data,
+                self.last_use.ctypes.data, self.pinned.ctypes.data, self.clock.ctypes.data)
+
+    def place(self, ids):
+        ids = np.ascontiguousarray(ids, np.int32)
+        h, m = np.zeros(1, np.int32), np.zeros(1, np.int32)
+        if lib().oracle_cache_place(*self._args(), ids.ctypes.data, ids.size, h.ctypes.data,
+                                    m.ctypes.data):
+            raise ValueError("union larger than the unpinned slots")
+        return int(h[0]), int(m[0])
+
+    def pin(self, ids):
+        ids = np.ascontiguousarray(ids, np.int32)
+        m = np.zeros(1, np.int32)
+        if lib().oracle_cache_pin(*self._args(), ids.ctypes.data, ids.size, m.ctypes.data):
+            raise ValueError("pin set larger than the slots")
+        return int(m[0])
+
+    def prefetch(self, ids):
+        ids = np.ascontiguousarray(ids, np.int32)
+        c = np.zeros(1, np.int32)
+        lib().oracle_cache_prefetch(*self._args(), ids.ctypes.data, ids.size, c.ctypes.data)
+        return int(c[0])
+
+    def slot_of(self):
+        """[n_experts] slot of each expert, -1 when not resident."""
+        so = np.full(self.n_experts, -1, np.int32)
+        for s, e in enumerate(self.expert_in):
+            if e >= 0:
+                so[e] = s
+        return so
+
+
+def usage_hottest(counters, n):
+    c = np.ascontiguousarray(counters, np.uint64)
+    ids = np.empty(n, np.int32)
+    lib().oracle_usage_hottest(c.ctypes.data, c.size, n, ids.ctypes.data)
+    return ids

@@ -392,3 +392,152 @@ void oracle_rms_normalize(const double *h, int n_tokens, int d, double eps, floa
         for (int i = 0; i < d; ++i) a[(size_t)t * d + i] = (float)(ht[i] * inv);
     }
 }
+
+/* ---- Place: a per-layer LRU cache of expert blocks -------------------- */
+
+/* The pages' stage (3) Place loads the experts a batch is missing into a
+ * faster tier and reuses the resident ones, with a per-layer LRU cache;
+ * hot experts may be pinned from the hit counters, and the next layer's
+ * experts may be prefetched ("Public Colibri Observation and Revision
+ * Ledger", "Exact Architecture and Data-Flow Reconstruction" stage (3) and
+ * "Cache/Prefetch Design Comparison"). The pages give no tie rule; the
+ * reading here:
+ *   - a call takes a list of expert ids; ids outside [0, n_experts) and
+ *     repeats are ignored;
+ *   - the call is refused (state unchanged, return -1) when its distinct
+ *     experts not held by a pinned slot outnumber the unpinned slots;
+ *   - the call's clock advances by one; every resident id is a hit and its
+ *     slot's last use becomes the clock;
+ *   - then, in list order, every missing id takes the slot with the
+ *     smallest last use among the slots that are not pinned and not
+ *     already taken by this call (never-used slots have last use 0; the
+ *     lowest slot index among equals), evicting its expert.
+ * State lives in caller arrays: expert_in[n_slots] (expert or -1),
+ * last_use[n_slots], pinned[n_slots] (0/1), *clock. */
+int oracle_cache_place(int n_slots, int n_experts, int32_t *expert_in, uint64_t *last_use,
+                       const int32_t *pinned, uint64_t *clock, const int32_t *ids, int n,
+                       int32_t *hits, int32_t *misses)
+{
+    int *seen = (int *)calloc((size_t)n_experts, sizeof(int));
+    int *taken = (int *)calloc((size_t)n_slots, sizeof(int));
+    int n_unpinned_slots = 0, need = 0;
+    for (int s = 0; s < n_slots; ++s) n_unpinned_slots += !pinned[s];
+    for (int i = 0; i < n; ++i) {
+        int e = ids[i];
+        if (e < 0 || e >= n_experts || seen[e]) continue;
+        seen[e] = 1;
+        int in_pinned = 0;
+        for (int s = 0; s < n_slots; ++s)
+            if (expert_in[s] == e && pinned[s]) in_pinned = 1;
+        need += !in_pinned;
+    }
+    if (need > n_unpinned_slots) {
+        free(seen);
+        free(taken);
+        return -1;
+    }
+    memset(seen, 0, sizeof(int) * (size_t)n_experts);
+    *clock += 1;
+    int h = 0, m = 0;
+    for (int i = 0; i < n; ++i) {  /* hits */
+        int e = ids[i];
+        if (e < 0 || e >= n_experts || seen[e]) continue;
+        for (int s = 0; s < n_slots; ++s)
+            if (expert_in[s] == e) {
+                seen[e] = 1;
+                taken[s] = 1;
+                last_use[s] = *clock;
+                ++h;
+            }
+    }
+    for (int i = 0; i < n; ++i) {  /* misses, in list order */
+        int e = ids[i];
+        if (e < 0 || e >= n_experts || seen[e]) continue;
+        seen[e] = 1;
+        int victim = -1;
+        for (int s = 0; s < n_slots; ++s)
+            if (!pinned[s] && !taken[s] && (victim < 0 || last_use[s] < last_use[victim]))
+                victim = s;
+        expert_in[victim] = e;
+        taken[victim] = 1;
+        last_use[victim] = *clock;
+        ++m;
+    }
+    free(seen);
+    free(taken);
+    if (hits) *hits = h;
+    if (misses) *misses = m;
+    return 0;
+}
+
+/* Pin: the new pin set replaces the old one. A set of more distinct experts
+ * than slots is refused (-1, nothing changed); otherwise every slot is
+ * unpinned, the ids are placed as above and the slots holding them are
+ * pinned. *misses = experts copied in. */
+int oracle_cache_pin(int n_slots, int n_experts, int32_t *expert_in, uint64_t *last_use,
+                     int32_t *pinned, uint64_t *clock, const int32_t *ids, int n,
+                     int32_t *misses)
+{
+    int distinct = 0;
+    for (int i = 0; i < n; ++i) {
+        int dup = 0;
+        if (ids[i] < 0 || ids[i] >= n_experts) continue;
+        for (int j = 0; j < i; ++j) dup |= ids[j] == ids[i];
+        distinct += !dup;
+    }
+    if (distinct > n_slots) return -1;
+    for (int s = 0; s < n_slots; ++s) pinned[s] = 0;
+    int32_t h = 0, m = 0;
+    if (oracle_cache_place(n_slots, n_experts, expert_in, last_use, pinned, clock, ids, n, &h, &m))
+        return -1;
+    for (int i = 0; i < n; ++i)
+        for (int s = 0; s < n_slots; ++s)
+            if (ids[i] >= 0 && ids[i] < n_experts && expert_in[s] == ids[i]) pinned[s] = 1;
+    if (misses) *misses = m;
+    return 0;
+}
+
+/* Prefetch: place the longest prefix of ids whose distinct experts not held
+ * by a pinned slot fit in the unpinned slots. *copied = experts copied in. */
+void oracle_cache_prefetch(int n_slots, int n_experts, int32_t *expert_in, uint64_t *last_use,
+                           const int32_t *pinned, uint64_t *clock, const int32_t *ids, int n,
+                           int32_t *copied)
+{
+    int take = 0;
+    for (int len = 1; len <= n; ++len) {
+        /* does the prefix of this length fit? (count as oracle_cache_place) */
+        int need = 0, room = 0;
+        for (int s = 0; s < n_slots; ++s) room += !pinned[s];
+        for (int i = 0; i < len; ++i) {
+            int e = ids[i], dup = 0, in_pinned = 0;
+            if (e < 0 || e >= n_experts) continue;
+            for (int j = 0; j < i; ++j) dup |= ids[j] == e;
+            if (dup) continue;
+            for (int s = 0; s < n_slots; ++s)
+                if (expert_in[s] == e && pinned[s]) in_pinned = 1;
+            need += !in_pinned;
+        }
+        if (need > room) break;
+        take = len;
+    }
+    int32_t h = 0, m = 0;
+    oracle_cache_place(n_slots, n_experts, expert_in, last_use, pinned, clock, ids, take, &h, &m);
+    if (copied) *copied = m;
+}
+
+/* The n experts with the most hits, most first, the lower id among equal
+ * counts (the pages pin the experts their hit counters show hottest). */
+void oracle_usage_hottest(const uint64_t *counters, int n_experts, int n, int32_t *ids)
+{
+    int *order = (int *)malloc(sizeof(int) * (size_t)n_experts);
+    for (int e = 0; e < n_experts; ++e) {  /* insertion sort by (count desc, id asc) */
+        int j = e;
+        while (j > 0 && counters[order[j - 1]] < counters[e]) {
+            order[j] = order[j - 1];
+            --j;
+        }
+        order[j] = e;
+    }
+    for (int i = 0; i < n; ++i) ids[i] = order[i];
+    free(order);
+}

@@ -1,9 +1,10 @@
 """Place stage on the GPU: an HBM cache of expert slots over pinned host
 memory (moe_cache_*), with the expert math reading blocks through the slot
 table. Placement must not change results: every layer step through the
-cache equals, bit for bit, the same step with every expert resident; the
-hit / miss accounting follows least-recently-used replacement (checked
-against a plain model of it here)."""
+cache equals, bit for bit, the same step with every expert resident, and
+the oracle's layer step (routing bit for bit, outputs within 2e-3); the
+hits, misses, copies and slot assignments follow the oracle's per-layer
+LRU model (oracle.LruCache) call by call."""
 import dataclasses
 import sys
 
@@ -12,6 +13,7 @@ import pytest
 import torch
 
 import int4_routed_expert_gemv_amd as moe
+import oracle
 import synth
 from tests import layer_cases as lc
 from tests.gpu_layer import upload_pool, workspace
@@ -24,65 +26,6 @@ def say(*a):
     sys.stdout.flush()
 
 
-class LruModel:
-    """Least-recently-used slots: hits are refreshed first; each miss takes
-    the least recently used slot not held by the current union and not
-    pinned (lowest slot index among equals). pin() places a set and keeps
-    its slots; prefetch() places the longest prefix of its list that fits in
-    the unpinned slots."""
-
-    def __init__(self, n_slots):
-        self.expert_in = [-1] * n_slots
-        self.last = [0] * n_slots
-        self.pinned = [False] * n_slots
-        self.tick = 0
-
-    def pin(self, ids):
-        self.pinned = [False] * len(self.expert_in)
-        _, misses = self.place(ids)
-        for s, e in enumerate(self.expert_in):
-            if e in set(ids):
-                self.pinned[s] = True
-        return misses
-
-    def _unpinned_needed(self, ids):
-        slot_of = {e: s for s, e in enumerate(self.expert_in) if e >= 0}
-        return len({e for e in ids if not (e in slot_of and self.pinned[slot_of[e]])})
-
-    def prefetch(self, ids):
-        room = len(self.expert_in) - sum(self.pinned)
-        take = 0
-        for i in range(len(ids)):
-            if self._unpinned_needed(ids[:i + 1]) > room:
-                break
-            take = i + 1
-        return self.place(ids[:take])[1]
-
-    def place(self, ids):
-        self.tick += 1
-        used = [False] * len(self.expert_in)
-        slot_of = {e: s for s, e in enumerate(self.expert_in) if e >= 0}
-        hits = misses = 0
-        for e in ids:
-            if e in slot_of and not used[slot_of[e]]:
-                used[slot_of[e]] = True
-                self.last[slot_of[e]] = self.tick
-                hits += 1
-        for e in ids:
-            if e in slot_of:
-                continue
-            cands = [s for s in range(len(used)) if not used[s] and not self.pinned[s]]
-            v = min(cands, key=lambda s: (self.last[s], s))
-            if self.expert_in[v] >= 0:
-                del slot_of[self.expert_in[v]]
-            self.expert_in[v] = e
-            slot_of[e] = v
-            used[v] = True
-            self.last[v] = self.tick
-            misses += 1
-        return hits, misses
-
-
 def pinned_blocks(pool):
     """The pool's packed device-layout blocks copied back into pinned host memory."""
     host = torch.empty((pool.desc.n_experts, pool.stride), dtype=torch.uint8, pin_memory=True)
@@ -90,8 +33,9 @@ def pinned_blocks(pool):
     return host
 
 
-def step(desc, x, wr, b, k, ws, cache=None, counters=None):
-    """route_union -> (place) -> expert_forward on the current stream."""
+def step(desc, x, wr, b, k, ws, cache=None, counters=None, routing=None):
+    """route_union -> (place) -> expert_forward on the current stream.
+    routing: a dict that receives the routing outputs (host arrays)."""
     N, d = x.shape
     E = desc.n_experts
     dev = "cuda"
@@ -111,7 +55,22 @@ def step(desc, x, wr, b, k, ws, cache=None, counters=None):
         missed = cache.place(union, copy_stream=cache_stream(), compute_stream=None)
     y = torch.empty((N, d), dtype=torch.float32, device=dev)
     moe.expert_forward(desc, x, k, w, uid, nu, off, perm, y, ws)
+    if routing is not None:
+        torch.cuda.synchronize()
+        n = int(nu.item())
+        routing.update(ids=ids.cpu().numpy(), union_ids=uid.cpu().numpy()[:n],
+                       offsets=off.cpu().numpy(), perm=perm.cpu().numpy())
     return y, union, missed
+
+
+def check_against_oracle(x, wr, b, k, blocks, shared, spec, y, routing):
+    """routing bit for bit and y within 2e-3 (per token) of the oracle's step"""
+    ref = oracle.layer_step(x, wr, b, k, blocks, shared, spec.d, spec.f, spec.wbits, spec.group)
+    for key in ("ids", "union_ids", "offsets", "perm"):
+        np.testing.assert_array_equal(routing[key], ref[key], err_msg=key)
+    err = lc.rel_err_rows(y, ref["y"]).max()
+    assert err <= 2e-3, f"max per-token relative error {err:.3e}"
+    return err
 
 
 _copy_stream = None
@@ -134,10 +93,11 @@ def test_cache_steps_equal_resident_pool(N, k, slots):
     spec = cfg.layers[0]
     x_all, wr, b, _, _ = lc.layer_inputs(cfg, 0)
     blocks, shared = lc.canonical_pool(cfg, 0)
+    blocks_c, shared_c = blocks.copy(), shared.copy()   # canonical copies for the oracle
     pool = upload_pool(spec, blocks, shared)
     host = pinned_blocks(pool)
     cache = moe.ExpertCache(pool.desc, slots, host)
-    model = LruModel(slots)
+    model = oracle.LruCache(slots, spec.n_experts)
     dev = "cuda"
     wrd = torch.from_numpy(np.ascontiguousarray(wr, np.float32)).to(dev)
     bd = torch.from_numpy(np.ascontiguousarray(b, np.float32)).to(dev)
@@ -146,14 +106,18 @@ def test_cache_steps_equal_resident_pool(N, k, slots):
     for it in range(6):
         x = torch.from_numpy(np.ascontiguousarray(x_all[it * N:(it + 1) * N])).to(dev)
         y_res, _, _ = step(pool.desc, x, wrd, bd, k, ws)
-        y_cache, union, missed = step(cache.desc, x, wrd, bd, k, ws, cache=cache)
+        rt = {}
+        y_cache, union, missed = step(cache.desc, x, wrd, bd, k, ws, cache=cache, routing=rt)
         torch.cuda.synchronize()
         hits, misses = model.place([int(e) for e in union])
         tot_h += hits
         tot_m += misses
+        err = check_against_oracle(x_all[it * N:(it + 1) * N], wr, b, k, blocks_c, shared_c,
+                                   spec, y_cache.cpu().numpy(), rt)
         say(f"[cache] N={N} k={k} slots={slots} step {it}: union {len(union)} missed {missed} "
-            f"(model {misses})")
+            f"(oracle model {misses}), max rel err {err:.2e}")
         assert missed == misses
+        np.testing.assert_array_equal(cache.resident()[0], model.slot_of())
         np.testing.assert_array_equal(y_cache.cpu().numpy(), y_res.cpu().numpy())
     assert cache.stats() == (tot_h, tot_m)
     # every resident expert's slot holds its block
@@ -191,10 +155,11 @@ def test_pinned_and_prefetched_experts():
     spec = cfg.layers[0]
     x_all, wr, b, _, _ = lc.layer_inputs(cfg, 0)
     blocks, shared = lc.canonical_pool(cfg, 0)
+    blocks_c, shared_c = blocks.copy(), shared.copy()   # canonical copies for the oracle
     pool = upload_pool(spec, blocks, shared)
     host = pinned_blocks(pool)
     cache = moe.ExpertCache(pool.desc, slots, host)
-    model = LruModel(slots)
+    model = oracle.LruCache(slots, spec.n_experts)
     dev = "cuda"
     wrd = torch.from_numpy(np.ascontiguousarray(wr, np.float32)).to(dev)
     bd = torch.from_numpy(np.ascontiguousarray(b, np.float32)).to(dev)
@@ -223,13 +188,18 @@ def test_pinned_and_prefetched_experts():
             n_pf = cache.prefetch(np.array(pred, np.int32), copy_stream=cache_stream())
             assert n_pf == model.prefetch(pred)
         y_res, _, _ = step(pool.desc, x, wrd, bd, k, ws)
-        y_cache, union, missed = step(cache.desc, x, wrd, bd, k, ws, cache=cache)
+        rt = {}
+        y_cache, union, missed = step(cache.desc, x, wrd, bd, k, ws, cache=cache, routing=rt)
         torch.cuda.synchronize()
         hits, misses = model.place([int(e) for e in union])
         tot_h += hits
         tot_m += misses
-        say(f"[pin/prefetch] step {it}: union {union.tolist()} missed {missed} (model {misses})")
+        check_against_oracle(x_all[it * N:(it + 1) * N], wr, b, k, blocks_c, shared_c, spec,
+                             y_cache.cpu().numpy(), rt)
+        say(f"[pin/prefetch] step {it}: union {union.tolist()} missed {missed} "
+            f"(oracle model {misses})")
         assert missed == misses
+        np.testing.assert_array_equal(cache.resident()[0], model.slot_of())
         if it % 2:
             assert missed == 0   # every expert of the union was prefetched
         np.testing.assert_array_equal(y_cache.cpu().numpy(), y_res.cpu().numpy())
@@ -245,4 +215,95 @@ def test_pinned_and_prefetched_experts():
             assert torch.equal(slots_host[table[e]], host[e]), e
     assert cache.pin(np.array([], np.int32)) == 0
     assert not cache.resident()[1].any()
+    cache.close()
+
+
+@pytest.mark.parametrize("N,k,slots,E", [(1, 1, 3, 16), (4, 2, 8, 16), (3, 4, 16, 16),
+                                          (64, 4, 16, 16), (24, 3, 52, 64)])
+def test_cache_forward_overlap(N, k, slots, E):
+    """moe_cache_forward: the resident experts and the shared expert computed
+    while the missing blocks are copied in, then the copied experts and the
+    combine. Every step equals the resident pool bit for bit and the oracle's
+    layer step; misses and slot assignments follow the oracle's LRU model
+    (cold cache first, then partly warm; 16 slots over 16 experts ends fully
+    resident, the no-copy path; 64 tokens, and 24 tokens over 64 experts with
+    52 slots, run the matrix-core passes on partly cached unions).
+    Odd steps prefetch part of the next union first, so the forward also
+    meets prefetched blocks whose copies it must wait for."""
+    base = synth.CONFIGS["tiny"]
+    cfg = dataclasses.replace(base, n_tokens=N * 8, k=k,
+                              layers=(dataclasses.replace(base.layer, n_experts=E),))
+    spec = cfg.layers[0]
+    x_all, wr, b, _, _ = lc.layer_inputs(cfg, 0)
+    blocks, shared = lc.canonical_pool(cfg, 0)
+    blocks_c, shared_c = blocks.copy(), shared.copy()
+    pool = upload_pool(spec, blocks, shared)
+    cache = moe.ExpertCache(pool.desc, slots, pinned_blocks(pool))
+    model = oracle.LruCache(slots, spec.n_experts)
+    dev = "cuda"
+    wrd = torch.from_numpy(np.ascontiguousarray(wr, np.float32)).to(dev)
+    bd = torch.from_numpy(np.ascontiguousarray(b, np.float32)).to(dev)
+    ws = workspace(pool, N, k)
+    tot_h = tot_m = 0
+    for it in range(8):
+        x = torch.from_numpy(np.ascontiguousarray(x_all[it * N:(it + 1) * N])).to(dev)
+        y_res, _, _ = step(pool.desc, x, wrd, bd, k, ws)
+        y_res = y_res.cpu().numpy()
+        ids = torch.empty((N, k), dtype=torch.int32, device=dev)
+        w = torch.empty((N, k), dtype=torch.float32, device=dev)
+        uid = torch.full((E,), -1, dtype=torch.int32, device=dev)
+        nu = torch.zeros(1, dtype=torch.int32, device=dev)
+        off = torch.zeros(E + 1, dtype=torch.int32, device=dev)
+        perm = torch.zeros(N * k, dtype=torch.int32, device=dev)
+        moe.route_union(x, wrd, bd, k, ids, w, uid, nu, off, perm, None, ws)
+        n = int(nu.item())
+        union = uid[:n].cpu().numpy()
+        if it % 2 == 1 and n > 1:
+            pf = union[: n // 2]
+            assert cache.prefetch(pf, copy_stream=cache_stream()) == model.prefetch(pf)
+        y = torch.full((N, spec.d), float("nan"), dtype=torch.float32, device=dev)
+        missed = cache.forward(x, k, w, uid, nu, off, perm, union, y, ws,
+                               copy_stream=cache_stream())
+        torch.cuda.synchronize()
+        hits, misses = model.place([int(e) for e in union])
+        tot_h += hits
+        tot_m += misses
+        rt = dict(ids=ids.cpu().numpy(), union_ids=union, offsets=off.cpu().numpy(),
+                  perm=perm.cpu().numpy())
+        err = check_against_oracle(x_all[it * N:(it + 1) * N], wr, b, k, blocks_c, shared_c,
+                                   spec, y.cpu().numpy(), rt)
+        say(f"[overlap] N={N} k={k} slots={slots} step {it}: union {n} missed {missed} "
+            f"(oracle model {misses}), max rel err {err:.2e}")
+        assert missed == misses
+        np.testing.assert_array_equal(cache.resident()[0], model.slot_of())
+        np.testing.assert_array_equal(y.cpu().numpy(), y_res)
+    assert cache.stats() == (tot_h, tot_m)
+    cache.close()
+
+
+def test_cache_forward_argument_checks():
+    """Refusals before anything changes: a union larger than the slots, a
+    pool shape that does not match the cache's blocks, a missing workspace."""
+    cfg = dataclasses.replace(synth.CONFIGS["tiny"], n_tokens=4, k=2)
+    spec = cfg.layers[0]
+    blocks, shared = lc.canonical_pool(cfg, 0)
+    pool = upload_pool(spec, blocks, shared)
+    cache = moe.ExpertCache(pool.desc, 2, pinned_blocks(pool))
+    dev = "cuda"
+    E, N, k = spec.n_experts, 4, 2
+    x = torch.zeros((N, spec.d), dtype=torch.float32, device=dev)
+    w = torch.zeros((N, k), dtype=torch.float32, device=dev)
+    uid = torch.zeros(E, dtype=torch.int32, device=dev)
+    nu = torch.zeros(1, dtype=torch.int32, device=dev)
+    off = torch.zeros(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.zeros(N * k, dtype=torch.int32, device=dev)
+    y = torch.zeros((N, spec.d), dtype=torch.float32, device=dev)
+    ws = workspace(pool, N, k)
+    with pytest.raises(moe.MoeError) as e:
+        cache.forward(x, k, w, uid, nu, off, perm, np.array([0, 1, 2], np.int32), y, ws)
+    assert e.value.status == moe.MOE_ESHAPE
+    with pytest.raises(moe.MoeError) as e:
+        cache.forward(x, k, w, uid, nu, off, perm, np.array([0], np.int32), y, ws[:16])
+    assert e.value.status == moe.MOE_EWORKSPACE
+    assert cache.stats() == (0, 0) and not (cache.resident()[0] >= 0).any()
     cache.close()

@@ -24,6 +24,14 @@ MUTATIONS = {
     "combine_weight_slot": ("double w = (double)topk_w[(size_t)t * k + j];",
                             "double w = (double)topk_w[(size_t)t * k];"),
     "rms_mean": ("sqrt(ss / d + eps)", "sqrt(ss / (d - 1) + eps)"),
+    "lru_evicts_most_recent": ("(victim < 0 || last_use[s] < last_use[victim])",
+                               "(victim < 0 || last_use[s] > last_use[victim])"),
+    "lru_ties_to_highest_slot": ("(victim < 0 || last_use[s] < last_use[victim])",
+                                 "(victim < 0 || last_use[s] <= last_use[victim])"),
+    "lru_hit_not_refreshed": ("                taken[s] = 1;\n                last_use[s] = *clock;\n                ++h;",
+                              "                taken[s] = 1;\n                ++h;"),
+    "hottest_ties_to_higher_id": ("counters[order[j - 1]] < counters[e]",
+                                  "counters[order[j - 1]] <= counters[e]"),
 }
 
 

@@ -443,3 +443,83 @@ def test_rms_normalize_closed_form():
     np.testing.assert_allclose(a[1], np.ones(4), rtol=1e-7)
     a = oracle.rms_normalize(np.full((1, 8), 1e-3), eps=1e-6)
     np.testing.assert_allclose(a[0], np.full(8, 1e-3 / math.sqrt(1e-6 + 1e-6)), rtol=1e-6)
+
+
+# ---------------------------------------------------------------- Place (LRU cache)
+
+def test_cache_hand_traces():
+    """The oracle's per-layer LRU cache reproduces hand-worked traces: hits,
+    misses, refusals, pins and prefetches, and the slot contents after each
+    call (tests/golden/cache_lru_hand.json)."""
+    g = json.load(open(os.path.join(GOLD, "cache_lru_hand.json")))
+    for tr in g["traces"]:
+        c = oracle.LruCache(tr["n_slots"], tr["n_experts"])
+        for st in tr["steps"]:
+            before = (c.expert_in.copy(), c.pinned.copy())
+            try:
+                r = getattr(c, st["op"])(st["ids"])
+                r = list(r) if isinstance(r, tuple) else r
+            except ValueError:
+                r = None
+                np.testing.assert_array_equal(c.expert_in, before[0])
+                np.testing.assert_array_equal(c.pinned, before[1])
+            assert r == st["expect"], st
+            assert c.expert_in.tolist() == st["slots"], st
+            if "pinned" in st:
+                assert c.pinned.tolist() == st["pinned"], st
+
+
+def _stack_distance_misses(seq, n_slots):
+    """Misses of an LRU cache of n_slots on single-expert accesses, from the
+    textbook stack-distance property: an access misses exactly when at least
+    n_slots distinct other experts were used since its expert's previous
+    access, or when there was no previous access."""
+    misses = 0
+    for i, e in enumerate(seq):
+        prev = [j for j in range(i) if seq[j] == e]
+        if not prev:
+            misses += 1
+            continue
+        between = set(seq[prev[-1] + 1:i])
+        misses += len(between) >= n_slots
+    return misses
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_cache_matches_lru_stack_distance(seed):
+    """One expert per call, no pins: for every cache size, the oracle's misses
+    equal the count given by LRU stack distances, computed by brute force."""
+    rng = np.random.default_rng(seed)
+    E = 12
+    # a skewed stream, so that reuse distances of every size occur
+    seq = [int(v) for v in rng.zipf(1.3, size=300) % E]
+    for C in range(1, E + 1):
+        c = oracle.LruCache(C, E)
+        misses = sum(c.place([e])[1] for e in seq)
+        assert misses == _stack_distance_misses(seq, C), C
+
+
+def test_cache_large_enough_misses_each_expert_once():
+    """A cache with a slot for every expert only takes compulsory misses, for
+    unions of any size; every hit or miss is counted once per distinct id."""
+    rng = np.random.default_rng(5)
+    E = 20
+    c = oracle.LruCache(E, E)
+    seen, tot_h, tot_m = set(), 0, 0
+    for _ in range(50):
+        u = rng.integers(0, E, size=int(rng.integers(1, 8))).tolist()
+        h, m = c.place(u)
+        assert m == len(set(u) - seen)
+        assert h + m == len(set(u))
+        seen |= set(u)
+        tot_h += h
+        tot_m += m
+    assert tot_m == len(seen)
+
+
+def test_usage_hottest_brute_force():
+    rng = np.random.default_rng(9)
+    counts = rng.integers(0, 6, size=40).astype(np.uint64)   # many equal counts
+    want = sorted(range(40), key=lambda e: (-int(counts[e]), e))
+    for n in (0, 1, 7, 40):
+        assert oracle.usage_hottest(counts, n).tolist() == want[:n]
