@@ -109,6 +109,10 @@ def parse():
     p.add_argument("--pin", type=int, default=32, help="experts pinned per layer (--cache-stack)")
     p.add_argument("--lookahead-top", type=int, default=None,
                    help="--cache-stack: prefetch only each token's first M predicted experts")
+    p.add_argument("--spec-drafts", default=None, metavar="D1,D2,..",
+                   help="speculative decoding cycles on the stack workload: D draft steps "
+                        "through the int8 draft layer, then a verify batch of 1 + D tokens "
+                        "through the 8 int4 layers (moe_stack_forward), for each listed D")
     p.add_argument("--cache-slots", default=None,
                    help="comma-separated HBM slot counts: measure the Place stage (experts in "
                         "pinned host memory, an HBM cache of that many slots per layer) instead")
@@ -705,6 +709,9 @@ def main():
     if args.cache_stack:
         cache_stack_bench(args)
         return
+    if args.spec_drafts:
+        spec_bench(args)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     hip = Hip()
@@ -1016,6 +1023,88 @@ def cache_stack_bench(args):
                                  "pinned_per_layer": n_pin, "lookahead_top": top or k,
                                  "n_experts": E,
                                  "block_bytes": block},
+                      "points": points}), flush=True)
+
+
+def spec_bench(args):
+    """Speculative decoding through the same kernels (Colibri README,
+    "Speculative decoding, honestly"): per cycle, D draft steps of one token
+    each through the int8 draft-head layer (g_i = g_(i-1) + draft(rms(g_(i-1)))),
+    then the verify batch [g_0 .. g_D] through the 8 int4 layers, all with
+    moe_stack_forward. Reported per D: the cycle time, its draft and verify
+    parts, and the tokens per second if every draft were accepted, next to
+    plain one-token decode through the 8 int4 layers (D = 0). Acceptance
+    itself needs a trained model and is not measured."""
+    import numpy as np
+    import torch
+
+    import int4_routed_expert_gemv_amd as moe
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    Ds = sorted({int(v) for v in args.spec_drafts.split(",")} | {0})
+    wl = build_workload("stack8_draft", args, 1, 0, 1, 1, dev)
+    k, d, L = wl["k"], wl["d"], wl["L_rot"]
+    descs = [(wl["pools"][l].desc, wl["routers"][l][0], wl["routers"][l][1], None)
+             for l in range(L)]
+    draft = moe.layer_descs(descs[L - 1:])
+    main = moe.layer_descs(descs[:L - 1])
+    maxD = max(Ds)
+    ws = torch.empty(max(moe.stack_workspace_size(draft, 1, k),
+                         moe.stack_workspace_size(main, 1 + maxD, k)), dtype=torch.uint8,
+                     device=dev)
+    x0 = torch.from_numpy(synth.tokens(dataclasses.replace(wl["cfg"], n_tokens=1))).to(dev)
+    g = torch.empty((1 + maxD, d), dtype=torch.float32, device=dev)
+    hip = Hip()
+    evs = [hip.event() for _ in range(3)]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def cycle(D, ev=False):
+        g[0].copy_(x0[0])
+        if ev:
+            hip.L.hipEventRecord(evs[0], stream)
+        for i in range(1, D + 1):
+            g[i].copy_(g[i - 1])
+            moe.stack_forward(draft, g[i:i + 1], k, ws)
+        if ev:
+            hip.L.hipEventRecord(evs[1], stream)
+        moe.stack_forward(main, g[:D + 1], k, ws)
+        if ev:
+            hip.L.hipEventRecord(evs[2], stream)
+
+    points = []
+    for D in Ds:
+        for _ in range(max(2, args.warmup)):
+            cycle(D)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            cycle(D)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / args.steps * 1e3
+        dr, vf = [], []
+        for _ in range(min(args.steps, 20)):
+            cycle(D, ev=True)
+            torch.cuda.synchronize()
+            dr.append(hip.elapsed_ms(evs[0], evs[1]) if D else 0.0)
+            vf.append(hip.elapsed_ms(evs[1], evs[2]))
+        pt = {"drafts": D, "verify_tokens": D + 1, "ms_per_cycle": ms,
+              "draft_ms": float(np.median(dr)), "verify_ms": float(np.median(vf)),
+              "tokens_per_s_all_accepted": (D + 1) / ms * 1e3}
+        points.append(pt)
+        say(f"[spec] {pt}")
+    base = points[0]["ms_per_cycle"]
+    for pt in points:
+        pt["speedup_all_accepted"] = pt["tokens_per_s_all_accepted"] / (1e3 / base)
+    print(json.dumps({"metric": "speculative decoding cycles through the layer stack: D draft "
+                                "steps on the int8 draft layer + a verify batch of 1 + D tokens "
+                                "on the 8 int4 layers",
+                      "unit": "ms per cycle", "n_gpus": 1, "steps": args.steps,
+                      "data": "synthetic",
+                      "config": {"workload": "stack8_draft layers: 8 int4 GLM-5.2-shaped layers "
+                                             "(top-8, Zipf(1.1) bias) + the int8 draft layer",
+                                 "k": k, "d_model": d},
                       "points": points}), flush=True)
 
 

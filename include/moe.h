@@ -393,6 +393,45 @@ moe_status moe_layer_step_noalloc(const moe_expert_pool *pool /* (host) */, cons
                                   float *y, hipStream_t stream,
                                   const moe_forward_options *opt /* (host) */);
 
+/*
+ * A stack of layers chained through a residual stream, in one call. The
+ * pages keep the dense layers (attention, norms) out of the expert path and
+ * give no formula for joining the MoE layers; the reading here is a pre-norm
+ * residual with a parameter-free RMS norm: for l = 0 .. n_layers-1,
+ *   a = h / sqrt(mean_i h[i]^2 + eps),  y = layer_l(a),  h += y,
+ * each layer_l a moe_layer_step (router bias inside the sigmoid, top-k,
+ * union, counters, experts, combine) with its own pool, router and hit
+ * counters. This is the path of a stack workload and of the speculative
+ * decoding flow: draft steps through the int8 draft-head layer, then the
+ * 1 + D token verify batch through the main layers with the same kernels
+ * (Colibri README, "Speculative decoding, honestly").
+ *   layers (host) [n_layers]: every pool with the same d_model and
+ *     n_experts; w_router [n_experts][d_model] (16-byte aligned),
+ *     b_router [n_experts] or NULL, counters [n_experts] uint64 (8-byte
+ *     aligned) or NULL (device pointers).
+ *   h [n_tokens][d_model] float32 (device, 16-byte aligned): the stack's
+ *     input, overwritten with its output.
+ *   topk_ids_out (device [n_layers][n_tokens][k] int32, or NULL): each
+ *     layer's expert ids.
+ *   workspace: moe_stack_workspace_size(layers, n_layers, n_tokens, k) bytes,
+ *     MOE_ALIGN-aligned; its contents afterwards are unspecified.
+ * Every layer's checks are made before anything is enqueued.
+ */
+typedef struct {
+    moe_expert_pool pool;
+    const float *w_router;
+    const float *b_router;
+    uint64_t *counters;
+} moe_layer_desc;
+
+moe_status moe_stack_forward(const moe_layer_desc *layers /* (host) */, int n_layers,
+                             int n_tokens, int k, float eps, float *h, int32_t *topk_ids_out,
+                             void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace of moe_stack_forward (0 for invalid arguments). */
+size_t moe_stack_workspace_size(const moe_layer_desc *layers /* (host) */, int n_layers,
+                                int n_tokens, int k);
+
 /* Workspace sizes in bytes (host-only arithmetic, no HIP calls). */
 size_t moe_route_workspace_size(int n_tokens, int n_experts);
 size_t moe_forward_workspace_size(const moe_expert_pool *pool, int n_tokens, int k);

@@ -37,6 +37,7 @@ EXPORTED = [
     "moe_hit_count", "moe_residual_rmsnorm", "moe_route_workspace_size", "moe_forward_workspace_size",
     "moe_workspace_size", "moe_block_bytes", "moe_pack_expert", "moe_strerror",
     "moe_layer_step", "moe_layer_step_workspace_size", "moe_layer_step_noalloc",
+    "moe_stack_forward", "moe_stack_workspace_size",
 ]
 MOE_SCRATCH_BYTES = 64 << 20  # the workspace array of moe_layer_step_noalloc, per GPU
 
@@ -90,6 +91,12 @@ class PoolDesc(ctypes.Structure):
     ]
 
 
+class LayerDesc(ctypes.Structure):
+    """struct moe_layer_desc: one layer of a stack (pool, router, counters)"""
+    _fields_ = [("pool", PoolDesc), ("w_router", ctypes.c_void_p), ("b_router", ctypes.c_void_p),
+                ("counters", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -120,6 +127,9 @@ def lib():
         L.moe_layer_step_noalloc.argtypes = [P, vp, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp,
                                              vp, vp, vp, vp, ctypes.POINTER(ForwardOptions)]
         L.moe_layer_step_workspace_size.argtypes = [P, i32, i32]
+        LD = ctypes.POINTER(LayerDesc)
+        L.moe_stack_forward.argtypes = [LD, i32, i32, i32, f32, vp, vp, vp, sz, vp]
+        L.moe_stack_workspace_size.argtypes = [LD, i32, i32, i32]
         L.moe_residual_rmsnorm.argtypes = [vp, vp, vp, i32, i32, f32, vp]
         L.moe_route_workspace_size.argtypes = [i32, i32]
         L.moe_forward_workspace_size.argtypes = [P, i32, i32]
@@ -153,11 +163,12 @@ def lib():
         for name in ("moe_route_topk", "moe_route_topk_ex", "moe_union", "moe_route_union",
                      "moe_route_union_ex", "moe_expert_forward",
                      "moe_expert_forward_ex", "moe_hit_count", "moe_layer_step",
-                     "moe_layer_step_noalloc",
+                     "moe_layer_step_noalloc", "moe_stack_forward",
                      "moe_residual_rmsnorm", "moe_pack_expert"):
             getattr(L, name).restype = i32
         for name in ("moe_route_workspace_size", "moe_forward_workspace_size",
-                     "moe_workspace_size", "moe_layer_step_workspace_size", "moe_block_bytes"):
+                     "moe_workspace_size", "moe_layer_step_workspace_size", "moe_block_bytes",
+                     "moe_stack_workspace_size"):
             getattr(L, name).restype = sz
         _lib = L
     return _lib
@@ -388,6 +399,33 @@ def expert_forward(pool: PoolDesc, x, k, topk_w, union_ids, n_union, expert_offs
         _check(lib().moe_expert_forward(*args), "moe_expert_forward")
     else:
         _check(lib().moe_expert_forward_ex(*args, ctypes.byref(options)), "moe_expert_forward_ex")
+
+
+def layer_descs(layers):
+    """A ctypes array of LayerDesc from (pool descriptor, w_router, b_router,
+    counters) tuples (tensors or None)."""
+    arr = (LayerDesc * len(layers))()
+    for i, (desc, wr, b, cnt) in enumerate(layers):
+        arr[i] = LayerDesc(desc, _ptr(wr), _ptr(b), _ptr(cnt))
+    return arr
+
+
+def stack_workspace_size(layers, n_tokens, k) -> int:
+    """layers: the result of layer_descs()"""
+    return int(lib().moe_stack_workspace_size(layers, len(layers), n_tokens, k))
+
+
+def stack_forward(layers, h, k, workspace, topk_ids_out=None, eps=1e-6, stream=None):
+    """moe_stack_forward: h [N][d] (in: the stack's input, out: its output)
+    through every layer of `layers` (layer_descs()), chained by the residual
+    RMS norm; topk_ids_out [L][N][k] int32 or None."""
+    import torch
+    _expect(h, torch.float32, "h")
+    _expect(topk_ids_out, torch.int32, "topk_ids_out")
+    N = h.shape[0]
+    _check(lib().moe_stack_forward(layers, len(layers), N, k, eps, _ptr(h), _ptr(topk_ids_out),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "moe_stack_forward")
 
 
 def residual_rmsnorm(h, y, a, eps=1e-6, stream=None):

@@ -595,12 +595,33 @@ size_t moe_layer_step_workspace_size(const moe_expert_pool *pool, int n_tokens, 
     return a && b ? a + b : 0;
 }
 
+static moe_status layer_step_impl(const moe_expert_pool *pool, const float *x, int n_tokens,
+                                  int d_model, const float *w_router, const float *b_router, int k,
+                                  int32_t *topk_ids, float *topk_w, int32_t *union_ids,
+                                  int32_t *n_union, int32_t *expert_offsets, int32_t *perm,
+                                  uint64_t *counters, float *y, void *workspace, size_t ws_bytes,
+                                  hipStream_t stream, const moe_forward_options *opt,
+                                  bool check_only);
+
 moe_status moe_layer_step(const moe_expert_pool *pool, const float *x, int n_tokens, int d_model,
                           const float *w_router, const float *b_router, int k, int32_t *topk_ids,
                           float *topk_w, int32_t *union_ids, int32_t *n_union,
                           int32_t *expert_offsets, int32_t *perm, uint64_t *counters, float *y,
                           void *workspace, size_t ws_bytes, hipStream_t stream,
                           const moe_forward_options *opt)
+{
+    return layer_step_impl(pool, x, n_tokens, d_model, w_router, b_router, k, topk_ids, topk_w,
+                           union_ids, n_union, expert_offsets, perm, counters, y, workspace,
+                           ws_bytes, stream, opt, false);
+}
+
+static moe_status layer_step_impl(const moe_expert_pool *pool, const float *x, int n_tokens,
+                                  int d_model, const float *w_router, const float *b_router, int k,
+                                  int32_t *topk_ids, float *topk_w, int32_t *union_ids,
+                                  int32_t *n_union, int32_t *expert_offsets, int32_t *perm,
+                                  uint64_t *counters, float *y, void *workspace, size_t ws_bytes,
+                                  hipStream_t stream, const moe_forward_options *opt,
+                                  bool check_only)
 {
     if (!pool) return MOE_EINVAL;
     Geo g;
@@ -625,7 +646,7 @@ moe_status moe_layer_step(const moe_expert_pool *pool, const float *x, int n_tok
     if (st != MOE_OK) return st;
     st = forward_impl(pool, x, n_tokens, k, topk_w, union_ids, n_union, expert_offsets, perm, y,
                       fws, fbytes, stream, opt, true, nullptr);
-    if (st != MOE_OK || n_tokens == 0) return st;
+    if (st != MOE_OK || n_tokens == 0 || check_only) return st;
     // Up to two tokens whose experts all stay on the GEMV with one item per
     // expert (a positive threshold can move them to the matrix cores) take
     // the routing inside the gate/up launch.
@@ -723,6 +744,17 @@ moe_status moe_pack_expert(const void *canonical_block, const moe_expert_pool *s
 }  // extern "C"
 
 namespace moe {
+
+moe_status layer_step_check(const moe_expert_pool *pool, const float *x, int n_tokens, int d_model,
+                            const float *w_router, const float *b_router, int k,
+                            int32_t *topk_ids, float *topk_w, int32_t *union_ids,
+                            int32_t *n_union, int32_t *expert_offsets, int32_t *perm,
+                            uint64_t *counters, float *y, void *workspace, size_t ws_bytes)
+{
+    return layer_step_impl(pool, x, n_tokens, d_model, w_router, b_router, k, topk_ids, topk_w,
+                           union_ids, n_union, expert_offsets, perm, counters, y, workspace,
+                           ws_bytes, nullptr, nullptr, true);
+}
 
 moe_status expert_forward_phase(const moe_expert_pool *pool, const float *x, int n_tokens, int k,
                                 const float *topk_w, const int32_t *union_ids,

@@ -122,6 +122,12 @@ __device__ __forceinline__ const uint8_t *expert_block(const Fwd &f, int e)
 
 // ---- host helpers (abi.hip) --------------------------------------------
 moe_status resolve_geo(const moe_expert_pool *p, Geo *g);
+// Every check of moe_layer_step on these arguments, nothing enqueued.
+moe_status layer_step_check(const moe_expert_pool *pool, const float *x, int n_tokens, int d_model,
+                            const float *w_router, const float *b_router, int k,
+                            int32_t *topk_ids, float *topk_w, int32_t *union_ids,
+                            int32_t *n_union, int32_t *expert_offsets, int32_t *perm,
+                            uint64_t *counters, float *y, void *workspace, size_t ws_bytes);
 // moe_expert_forward restricted to one phase of a two-phase forward (see
 // Fwd::phase): phase_sel 0 computes the experts with phase[e] == 0 and the
 // shared expert, 1 the others and then the combine. check_only: the

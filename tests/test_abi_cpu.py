@@ -382,3 +382,32 @@ def test_layer_step_noalloc_rejects_oversize_steps_before_any_hip_call():
             None)
     assert L.moe_layer_step_noalloc(ctypes.byref(glm), *args) == moe.MOE_EWORKSPACE
     assert L.moe_layer_step_noalloc(None, *args) == moe.MOE_EINVAL
+
+
+def test_stack_forward_argument_checks():
+    """moe_stack_forward: every layer's checks before anything is enqueued."""
+    L = moe.lib()
+    p = _pool()
+    layers = moe.layer_descs([(p, None, None, None), (p, None, None, None)])
+    for ld in layers:
+        ld.w_router = FAKE
+    need = moe.stack_workspace_size(layers, 4, 2)
+    assert need > moe.layer_step_workspace_size(p, 4, 2)   # one layer step's, reused
+    assert L.moe_stack_forward(None, 1, 4, 2, 1e-6, FAKE, None, FAKE, 1 << 30, None) == moe.MOE_EINVAL
+    assert L.moe_stack_forward(layers, 0, 4, 2, 1e-6, FAKE, None, FAKE, 1 << 30, None) == moe.MOE_EINVAL
+    assert L.moe_stack_forward(layers, 2, 4, 2, -1.0, FAKE, None, FAKE, 1 << 30, None) == moe.MOE_EINVAL
+    assert L.moe_stack_forward(layers, 2, 4, 2, 1e-6, FAKE, None, FAKE, need - 1,
+                               None) == moe.MOE_EWORKSPACE
+    assert L.moe_stack_forward(layers, 2, 4, 2, 1e-6, None, None, FAKE, need, None) == moe.MOE_EINVAL
+    assert L.moe_stack_forward(layers, 2, 4, 2, 1e-6, FAKE + 4, None, FAKE, need,
+                               None) == moe.MOE_EALIGN
+    assert L.moe_stack_forward(layers, 2, 4, 17, 1e-6, FAKE, None, FAKE, 1 << 30,
+                               None) == moe.MOE_EINVAL            # k above n_experts
+    assert L.moe_stack_forward(layers, 2, 0, 2, 1e-6, None, None, None, 0, None) == moe.MOE_OK
+    layers[1].w_router = None                                    # the second layer's router
+    assert L.moe_stack_forward(layers, 2, 4, 2, 1e-6, FAKE, None, FAKE, need, None) == moe.MOE_EINVAL
+    layers[1].w_router = FAKE
+    layers[1].pool = _pool(d=512)                                # layers of different widths
+    assert moe.stack_workspace_size(layers, 4, 2) == 0
+    assert L.moe_stack_forward(layers, 2, 4, 2, 1e-6, FAKE, None, FAKE, 1 << 30,
+                               None) == moe.MOE_ESHAPE
