@@ -419,14 +419,14 @@ class Runner:
 def calibrate(wl, runner, torch, small_min):
     """Which experts each (layer, batch) step streams and on which pass (the
     library's default thresholds): experts with at least 32 tokens go to the
-    128-token matrix-core pass, those with at least small_min (2) to the
-    32-token pass, the rest (and every expert of a batch of at most 2 tokens)
-    to the GEMV; fewer than 32 items of 128 tokens join the 32-token pass; a
+    128-token matrix-core pass, those with at least small_min (default 1) to
+    the 32-token pass, the rest (and every expert of a batch of at most 2
+    tokens) to the GEMV; fewer than 32 items of 128 tokens join the 32-token pass; a
     128-token group's remainder of at most 32 tokens past a full item goes to
     the 32-token pass. The shared expert counts as an expert of N tokens."""
     import numpy as np
     MFMA_MIN, MIN_BIG_ITEMS, GEMV_BATCH = 32, 32, 2
-    SMALL_MIN = small_min if small_min is not None else 2
+    SMALL_MIN = small_min if small_min is not None else 1
     N, d, f = wl["N"], wl["d"], wl["f"]
     b = wl["bufs"]
     calib = {}
@@ -443,7 +443,9 @@ def calibrate(wl, runner, torch, small_min):
         torch.cuda.synchronize()
         l = key[1] if wl["stack"] else key % wl["L_rot"]
         ls = wl["cfg"].layers[l]
-        mfma_ok = ls.wbits == 4 and d % 64 == 0 and f % 64 == 0
+        # the matrix-core passes take int4 and int8 layers alike (every
+        # supported shape has whole 128- or 64-column units)
+        mfma_ok = True
         nu = int(b["n_union"].item())
         uid = b["union_ids"][:nu].cpu().numpy()
         off = b["offsets"].cpu().numpy()

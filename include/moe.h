@@ -275,9 +275,9 @@ moe_status moe_expert_forward(const moe_expert_pool *pool /* (host) */,
  *   T >= mfma_min_tokens: grouped GEMM on the matrix cores, 128-token tiles;
  *     0 selects the default (32), a negative value turns this pass off;
  *   mfma_small_min_tokens <= T < mfma_min_tokens: the same kernels with
- *     32-token tiles; 0 selects the default (2, and off for batches of up to
- *     2 tokens, which the GEMV takes in one item per expert), negative turns
- *     it off;
+ *     32-token tiles; 0 selects the default (1: every expert not on the
+ *     128-token pass; off for batches of up to 2 tokens, which the GEMV
+ *     takes in one item per expert), negative turns it off;
  *   otherwise: the streaming GEMV kernels.
  * When both matrix-core passes are on, a group on the 128-token pass whose
  * last item would hold at most 32 tokens past a full one gives those tokens
@@ -286,8 +286,8 @@ moe_status moe_expert_forward(const moe_expert_pool *pool /* (host) */,
  * the 32-token pass (a few large items
  * would otherwise run with a few workgroups each); when n_tokens and k alone
  * bound it below 32 items, the 128-token kernels are not launched at all.
- * The matrix-core passes need int4 weights and d_model, d_ff multiples of
- * 64; otherwise every expert uses the GEMV.
+ * The matrix-core passes take int4 and int8 layers alike (every supported
+ * shape is a whole number of 1 KB code units per row).
  * events: each non-NULL event is taken by the dispatch of the kernel it
  *   names (hipExtLaunchKernelGGL), at that kernel's start or end. Events are
  *   created and owned by the caller; a kernel that a call does not launch

@@ -194,30 +194,6 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
     }
     __syncthreads();
 
-    // activation loads, one part of a step (kHalf columns) at a time: thread
-    // -> (token row, 16-byte chunks of the kHalf columns)
-    constexpr int kHalf = kUC / NA;
-    constexpr int kParts = kThreads / MT;          // threads per token row
-    constexpr int kCols = kHalf / kParts;          // columns per thread per part
-    constexpr int kVec = kCols / 8;                // 16-byte chunks per thread
-    static_assert(kVec >= 1, "at least one 16-byte chunk per thread");
-    const int a_row = tid / kParts, a_q = tid % kParts;
-    const int a_src = s_src[a_row];
-    // rows past the item's tokens load token 0's row (every load is issued on
-    // every path, so waits stay exact); their products land in accumulator
-    // rows that are never stored
-    const uint16_t *a_ptr = in + (size_t)(a_src >= 0 ? a_src : s_src[0]) * K + a_q * kCols;
-    auto load_a = [&](int kb, int hf, uint4 (&av)[kVec]) {
-#pragma unroll
-        for (int c = 0; c < kVec; ++c)
-            av[c] = reinterpret_cast<const uint4 *>(a_ptr + (size_t)kb * kUC + hf * kHalf)[c];
-    };
-    auto store_a = [&](int buf, int hf, const uint4 (&av)[kVec]) {
-        uint4 *dst = reinterpret_cast<uint4 *>(&As[buf][a_row][hf * kHalf + a_q * kCols]);
-#pragma unroll
-        for (int c = 0; c < kVec; ++c) dst[c] = make_uint4(av[c].x, av[c].y, av[c].z, av[c].w);
-    };
-
     // weights: this wave's unit rows; lane slot = (row in unit, quarter)
     const int r16 = lane % kUnitRows, q = lane / kUnitRows;
     const int rt0 = ntile * (kNT / kUnitRows) + wave * TW;  // first unit row of the wave
@@ -273,6 +249,35 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
     // no products and no scaling (a choice made once per workgroup).
     auto main_loop = [&](auto nb_tag) {
         constexpr int NB = decltype(nb_tag)::value;
+        // activation tile of a step: kRows token rows, loaded in kNA parts
+        // (kHalf columns each): thread -> (token row, 16-byte chunks). A loop
+        // with fewer token blocks than the item's tile stages only its own
+        // rows when a step's columns then still split into whole chunks per
+        // thread (int4 32-token items of at most 16 tokens: half the bytes).
+        constexpr bool kFew = NB < MF && kUC / (kThreads / (16 * NB)) >= 8;
+        constexpr int kRows = kFew ? 16 * NB : MT;
+        constexpr int kNA = kFew ? 1 : NA;
+        constexpr int kHalf = kUC / kNA;
+        constexpr int kParts = kThreads / kRows;       // threads per token row
+        constexpr int kCols = kHalf / kParts;          // columns per thread per part
+        constexpr int kVec = kCols / 8;                // 16-byte chunks per thread
+        static_assert(kVec >= 1, "at least one 16-byte chunk per thread");
+        const int a_row = tid / kParts, a_q = tid % kParts;
+        const int a_src = s_src[a_row];
+        // rows past the item's tokens load token 0's row (every load is issued
+        // on every path, so waits stay exact); their products land in
+        // accumulator rows that are never stored
+        const uint16_t *a_ptr = in + (size_t)(a_src >= 0 ? a_src : s_src[0]) * K + a_q * kCols;
+        auto load_a = [&](int kb, int hf, uint4 (&av)[kVec]) {
+#pragma unroll
+            for (int c = 0; c < kVec; ++c)
+                av[c] = reinterpret_cast<const uint4 *>(a_ptr + (size_t)kb * kUC + hf * kHalf)[c];
+        };
+        auto store_a = [&](int buf, int hf, const uint4 (&av)[kVec]) {
+            uint4 *dst = reinterpret_cast<uint4 *>(&As[buf][a_row][hf * kHalf + a_q * kCols]);
+#pragma unroll
+            for (int c = 0; c < kVec; ++c) dst[c] = make_uint4(av[c].x, av[c].y, av[c].z, av[c].w);
+        };
         // half of a unit step on LDS buffer `cur` and weights (bw, bs):
         // k-steps s_lo .. s_lo + NS/2 - 1 of 32, each lane's quarter q
         // covering columns QW q + 8s .. + 8
@@ -337,42 +342,70 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
         // register stage of half a step, loaded during the current step's
         // products and stored to the other LDS buffer. D is even, so the LDS
         // buffer of step ks + j (ks a multiple of D) is j % 2.
-        uint4 av[kVec];
+        // activations: a ring of AD register stages (AD = 2 for the gate/up
+        // of 32-token items: each step's tile is loaded two steps ahead of
+        // its products; the others load one step ahead: down items keep
+        // their registers for occupancy, and 128-token items, whose steps
+        // are long, measured slower with two)
+        constexpr int AD = (GATEUP && MF <= 2) ? 2 : 1;
+        uint4 ar[2][kNA][kVec];
         uint4 bwr[D][TW][NM];
         float bsr[D][TW][NM];
-        load_a(0, 0, av);
+        if constexpr (AD == 2) {
+            // the tiles of steps 0 and 1 in flight with the first weights
 #pragma unroll
-        for (int j = 0; j < D; ++j) load_b(min(j, n_kb - 1), bwr[j], bsr[j]);
-        store_a(0, 0, av);
-        if constexpr (NA == 2) {
-            load_a(0, 1, av);
-            store_a(0, 1, av);
+            for (int j = 0; j < AD; ++j) {
+                load_a(min(j, n_kb - 1), 0, ar[j][0]);
+                if constexpr (kNA == 2) load_a(min(j, n_kb - 1), 1, ar[j][kNA - 1]);
+            }
+#pragma unroll
+            for (int j = 0; j < D; ++j) load_b(min(j, n_kb - 1), bwr[j], bsr[j]);
+            store_a(0, 0, ar[0][0]);
+            if constexpr (kNA == 2) store_a(0, 1, ar[0][kNA - 1]);
+        } else {
+            // one half of step 0's tile in registers at a time
+            load_a(0, 0, ar[0][0]);
+#pragma unroll
+            for (int j = 0; j < D; ++j) load_b(min(j, n_kb - 1), bwr[j], bsr[j]);
+            store_a(0, 0, ar[0][0]);
+            if constexpr (kNA == 2) {
+                load_a(0, 1, ar[0][0]);
+                store_a(0, 1, ar[0][0]);
+            }
         }
         __syncthreads();
-        // one step: products on LDS buffer `cur`; the next step's activations
-        // are loaded before the products and stored to the other buffer after
-        // them, so their latency is covered by the whole step. Loads are
-        // issued on every step (the last step reloads its own activations into
-        // the buffer no later step reads, the last D steps reload their
-        // weights), so that no load sits in a branch: each wait is then for the
-        // load it needs, not for every load in flight.
-        auto step = [&](int ks, int cur, const uint4 (&bw)[TW][NM], const float (&bs)[TW][NM]) {
-            const int kn = min(ks + 1, n_kb - 1);
-            uint4 an0[kVec], an1[kVec];
-            load_a(kn, 0, an0);
-            if constexpr (NA == 2) load_a(kn, 1, an1);
+        // one step: the tile of step ks + AD is loaded into the register
+        // stage `a_far`, products on LDS buffer `cur`, then the tile of step
+        // ks + 1 (`a_next`, loaded AD - 1 steps earlier) is stored to the
+        // other buffer. Loads are issued on every step (past the end they
+        // reload the last step, into a buffer no later step reads), so that
+        // no load sits in a branch: each wait is then for the load it needs.
+        auto step = [&](int ks, int cur, uint4 (&a_next)[kNA][kVec], uint4 (&a_far)[kNA][kVec],
+                        const uint4 (&bw)[TW][NM], const float (&bs)[TW][NM]) {
+            const int kf = min(ks + AD, n_kb - 1);
+            load_a(kf, 0, a_far[0]);
+            if constexpr (kNA == 2) load_a(kf, 1, a_far[kNA - 1]);
             __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the products
             compute(cur, bw, bs, 0);
             compute(cur, bw, bs, NS / 2);
-            store_a(cur ^ 1, 0, an0);
-            if constexpr (NA == 2) store_a(cur ^ 1, 1, an1);
+            store_a(cur ^ 1, 0, a_next[0]);
+            if constexpr (kNA == 2) store_a(cur ^ 1, 1, a_next[kNA - 1]);
             __syncthreads();
         };
+        // AD = 2: the two stages alternate (D is even, so stage j % 2 holds
+        // step ks + j's tile until it is stored); AD = 1: each step loads and
+        // stores the next tile through registers of its own
         for (int ks = 0; ks < n_kb; ks += D) {
 #pragma unroll
             for (int j = 0; j < D; ++j) {
                 if (ks + j >= n_kb) break;
-                step(ks + j, j & 1, bwr[j], bsr[j]);
+                if constexpr (AD == 2) {
+                    step(ks + j, j & 1, ar[(j + 1) & 1], ar[j & 1], bwr[j], bsr[j]);
+                } else {
+                    // the tile lives in registers within the step only
+                    uint4 at[kNA][kVec];
+                    step(ks + j, j & 1, at, at, bwr[j], bsr[j]);
+                }
                 load_b(min(ks + j + D, n_kb - 1), bwr[j], bsr[j]);
             }
         }

@@ -83,10 +83,10 @@ def _case(name, n_tokens=None, k=None):
     return cfg
 
 
-# one token top-1 (GEMV, direct combine), 64 tokens top-8 (GEMV and the
-# 32-token pass), 300 tokens top-4 over 16 experts with every expert on the
-# 128-token pass, and 20 tokens top-8 (the router's workgroup-tiled path and
-# the separate union kernel) with the default passes
+# one token top-1 (GEMV, direct combine), 64 tokens top-8 (the 32-token
+# pass), 300 tokens top-4 over 16 experts with every expert on the 128-token
+# pass, and 20 tokens top-8 (the router's workgroup-tiled path and the
+# separate union kernel) with the default passes
 CASES = [("decode1", None, None, None, False, False), ("decode64", None, None, None, False, False),
          ("tiny", 300, 4, 1, False, False), ("tiny", 20, 8, None, False, False),
          # moe_layer_step: one and two tokens (routing inside the gate/up
