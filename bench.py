@@ -92,7 +92,7 @@ def parse():
     p.add_argument("--layers", type=int, default=8,
                    help="layer pools rotated over the steps (single-layer workloads)")
     p.add_argument("--batches", type=int, default=16, help="distinct token batches rotated")
-    p.add_argument("--cpu-tokens", type=int, default=64,
+    p.add_argument("--cpu-tokens", type=int, default=128,
                    help="tokens of the headline batch the CPU oracle runs through the stack")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="time budget of the CPU oracle on single-layer workloads")
