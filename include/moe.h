@@ -285,7 +285,8 @@ moe_status moe_expert_forward(const moe_expert_pool *pool /* (host) */,
  * when the 128-token pass would get fewer than 32 items, those experts join
  * the 32-token pass (a few large items
  * would otherwise run with a few workgroups each); when n_tokens and k alone
- * bound it below 32 items, the 128-token kernels are not launched at all.
+ * bound it below 32 items, or (default thresholds) n_tokens * k is below
+ * 32 * 128, the 128-token kernels are not launched at all.
  * The matrix-core passes take int4 and int8 layers alike (every supported
  * shape is a whole number of 1 KB code units per row).
  * events: each non-NULL event is taken by the dispatch of the kernel it

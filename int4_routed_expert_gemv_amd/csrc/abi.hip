@@ -67,10 +67,16 @@ FwdLayout fwd_layout(const Geo &g, int N, int k, int has_shared, int mfma_min_to
     if (big && mf && small_min_tokens >= 0 && N >= L.tsmall && L.tsmall < L.tstar) {
         // at most this many 128-token items: each expert reaching tstar adds
         // one partly filled item. Below kMinBigItems the planner moves them
-        // all to the 32-token pass, so that pass alone is launched.
+        // all to the 32-token pass, so that pass alone is launched. With the
+        // default thresholds, batches of fewer assignments than kMinBigItems
+        // full items take the 32-token pass alone as well: there the planner
+        // nearly always leaves the 128-token pass empty, and an empty launch
+        // pair still costs about 9 us
         const long long most = ceil_div(A, kMfmaBigTokens) + A / L.tstar +
                                (has_shared && N >= L.tstar ? ceil_div(N, kMfmaBigTokens) : 0);
-        if (most < kMinBigItems) big = false;
+        if (most < kMinBigItems ||
+            (mfma_min_tokens == 0 && A < (long long)kMinBigItems * kMfmaBigTokens))
+            big = false;
     }
     bool small = mf && small_min_tokens >= 0 && N >= L.tsmall && !(big && L.tsmall >= L.tstar);
     // By default, the smallest batches stay on the GEMV: one item per expert
@@ -316,7 +322,7 @@ moe_status moe_union(const int32_t *topk_ids, int n_tokens, int k, int n_experts
     if (n_tokens == 0) return MOE_OK;
     if (!topk_ids || !union_ids || !n_union || !expert_offsets || !perm) return MOE_EINVAL;
     if (launch_union(topk_ids, n_tokens * k, n_experts, union_ids, n_union, expert_offsets, perm,
-                     stream) != hipSuccess)
+                     nullptr, stream) != hipSuccess)
         return MOE_EHIP;
     return MOE_OK;
 }
@@ -351,8 +357,9 @@ moe_status moe_route_union(const float *x, int n_tokens, int d_model, const floa
                               workspace, ws_bytes, stream, nullptr);
 }
 
-// What route_union_impl does after its checks.
-enum class RouteMode { all, check_only, router_only };
+// What route_union_impl does after its checks (router_plan: nothing, but
+// the router's slice count and bias are returned).
+enum class RouteMode { all, check_only, router_plan };
 
 static moe_status route_union_impl(const float *x, int n_tokens, int d_model,
                                    const float *w_router, const float *b_router, int n_experts,
@@ -386,14 +393,14 @@ static moe_status route_union_impl(const float *x, int n_tokens, int d_model,
     if (mode == RouteMode::check_only) return MOE_OK;
     float *scores = static_cast<float *>(workspace);
     const int P = router_slices(n_tokens, d_model, n_experts);
-    if (launch_router(x, n_tokens, d_model, w_router, b_in, n_experts, scores, stream) !=
-        hipSuccess)
-        return MOE_EHIP;
-    if (mode == RouteMode::router_only) {
+    if (mode == RouteMode::router_plan) {
         *P_out = P;
         *b_out = b_in;
         return MOE_OK;
     }
+    if (launch_router(x, n_tokens, d_model, w_router, b_in, n_experts, scores, stream) !=
+        hipSuccess)
+        return MOE_EHIP;
     if (n_tokens <= route_tail_max_tokens())
         return launch_route_tail(scores, P, b_in, n_tokens, n_experts, k, topk_ids, topk_w,
                                  union_ids, n_union, expert_offsets, perm, counters, stream,
@@ -414,11 +421,9 @@ static moe_status route_union_impl(const float *x, int n_tokens, int d_model,
                    ? MOE_OK
                    : MOE_EHIP;
     }
-    if (launch_union(topk_ids, A, n_experts, union_ids, n_union, expert_offsets, perm, stream) !=
-        hipSuccess)
-        return MOE_EHIP;
-    if (counters && launch_hit_count(topk_ids, n_tokens * k, n_experts, counters, stream) !=
-                        hipSuccess)
+    // the union kernel adds the hit counts itself
+    if (launch_union(topk_ids, A, n_experts, union_ids, n_union, expert_offsets, perm, counters,
+                     stream) != hipSuccess)
         return MOE_EHIP;
     return MOE_OK;
 }
@@ -445,14 +450,18 @@ moe_status moe_expert_forward(const moe_expert_pool *pool, const float *x, int n
                                  perm, y, workspace, ws_bytes, stream, nullptr);
 }
 
-// The routing a one-token moe_layer_step hands to the gate/up kernel.
+// The routing a one- or two-token moe_layer_step hands to the expert
+// kernels: the router (launched by forward_impl) writes scores, and the
+// gate/up kernel takes the top-k.
 struct InRoute {
-    const float *scores;
+    float *scores;
     int P;
     const float *b;
     int32_t *ids;
     float *w;
     uint64_t *counters;
+    const float *x, *wr;  // router inputs
+    int d;
 };
 
 // The phase of a two-phase forward (Fwd::phase), or none.
@@ -466,7 +475,8 @@ static moe_status forward_impl(const moe_expert_pool *pool, const float *x, int 
                                const int32_t *n_union, const int32_t *expert_offsets,
                                const int32_t *perm, float *y, void *workspace, size_t ws_bytes,
                                hipStream_t stream, const moe_forward_options *ev,
-                               bool check_only, const InRoute *ir, const Phase *ph = nullptr)
+                               bool check_only, const InRoute *ir, const Phase *ph = nullptr,
+                               const StackNorm *sn = nullptr, bool *normed = nullptr)
 {
     Geo g;
     moe_status st = resolve_geo(pool, &g);
@@ -558,6 +568,9 @@ static moe_status forward_impl(const moe_expert_pool *pool, const float *x, int 
     f.ev_sgu[1] = ev ? ev->small_gateup_end : nullptr;
     f.ev_sdn[0] = ev ? ev->small_down_start : nullptr;
     f.ev_sdn[1] = ev ? ev->small_down_end : nullptr;
+    if (ir && launch_router(ir->x, n_tokens, ir->d, ir->wr, ir->b, g.E, ir->scores, stream) !=
+                  hipSuccess)
+        return MOE_EHIP;
     // gate/up of every pass (the first launch also builds the work lists),
     // then down of every pass, then the combine
     if (launch_gateup(f, stream) != hipSuccess) return MOE_EHIP;
@@ -568,9 +581,19 @@ static moe_status forward_impl(const moe_expert_pool *pool, const float *x, int 
     if (launch_down(f, stream) != hipSuccess) return MOE_EHIP;
     if (launch_mfma(f, false, false, stream) != hipSuccess) return MOE_EHIP;
     if (launch_mfma(f, false, true, stream) != hipSuccess) return MOE_EHIP;
-    if (!f.direct && (!ph || ph->sel == 1) &&
-        launch_combine(f.o, topk_w, n_tokens, k, g.d, (int)A, has_shared, y, stream) != hipSuccess)
-        return MOE_EHIP;
+    if (!f.direct && (!ph || ph->sel == 1)) {
+        if (sn && combine_norm_supported(g.d, sn->h, sn->a)) {
+            // a layer stack: the combine goes straight into the residual
+            // stream and the next layer's norm
+            if (launch_combine_norm(f.o, topk_w, n_tokens, k, g.d, (int)A, has_shared, sn->h,
+                                    sn->a, sn->eps, stream) != hipSuccess)
+                return MOE_EHIP;
+            if (normed) *normed = true;
+        } else if (launch_combine(f.o, topk_w, n_tokens, k, g.d, (int)A, has_shared, y, stream) !=
+                   hipSuccess) {
+            return MOE_EHIP;
+        }
+    }
     return MOE_OK;
 }
 
@@ -604,7 +627,8 @@ static moe_status layer_step_impl(const moe_expert_pool *pool, const float *x, i
                                   int32_t *n_union, int32_t *expert_offsets, int32_t *perm,
                                   uint64_t *counters, float *y, void *workspace, size_t ws_bytes,
                                   hipStream_t stream, const moe_forward_options *opt,
-                                  bool check_only);
+                                  bool check_only, const StackNorm *sn = nullptr,
+                                  bool *normed = nullptr);
 
 moe_status moe_layer_step(const moe_expert_pool *pool, const float *x, int n_tokens, int d_model,
                           const float *w_router, const float *b_router, int k, int32_t *topk_ids,
@@ -624,7 +648,7 @@ static moe_status layer_step_impl(const moe_expert_pool *pool, const float *x, i
                                   int32_t *n_union, int32_t *expert_offsets, int32_t *perm,
                                   uint64_t *counters, float *y, void *workspace, size_t ws_bytes,
                                   hipStream_t stream, const moe_forward_options *opt,
-                                  bool check_only)
+                                  bool check_only, const StackNorm *sn, bool *normed)
 {
     if (!pool) return MOE_EINVAL;
     Geo g;
@@ -665,21 +689,25 @@ static moe_status layer_step_impl(const moe_expert_pool *pool, const float *x, i
                               nullptr);
         if (st != MOE_OK) return st;
         return forward_impl(pool, x, n_tokens, k, topk_w, union_ids, n_union, expert_offsets,
-                            perm, y, fws, fbytes, stream, opt, false, nullptr);
+                            perm, y, fws, fbytes, stream, opt, false, nullptr, nullptr, sn,
+                            normed);
     }
     // the router, then the expert kernels, the top-k, union and counting
     // taken inside the gate/up GEMV launch
     InRoute ir;
-    ir.scores = static_cast<const float *>(workspace);
+    ir.scores = static_cast<float *>(workspace);
     ir.ids = topk_ids;
     ir.w = topk_w;
     ir.counters = counters;
+    ir.x = x;
+    ir.wr = w_router;
+    ir.d = d_model;
     st = route_union_impl(x, n_tokens, d_model, w_router, b_router, pool->n_experts, k, topk_ids,
                           topk_w, union_ids, n_union, expert_offsets, perm, counters, workspace,
-                          rs, stream, nullptr, RouteMode::router_only, &ir.P, &ir.b);
+                          rs, stream, nullptr, RouteMode::router_plan, &ir.P, &ir.b);
     if (st != MOE_OK) return st;
     return forward_impl(pool, x, n_tokens, k, topk_w, union_ids, n_union, expert_offsets, perm, y,
-                        fws, fbytes, stream, opt, false, &ir);
+                        fws, fbytes, stream, opt, false, &ir, nullptr, sn, normed);
 }
 
 moe_status moe_residual_rmsnorm(float *h, const float *y, float *a, int n_tokens, int d_model,
@@ -757,6 +785,19 @@ moe_status layer_step_check(const moe_expert_pool *pool, const float *x, int n_t
     return layer_step_impl(pool, x, n_tokens, d_model, w_router, b_router, k, topk_ids, topk_w,
                            union_ids, n_union, expert_offsets, perm, counters, y, workspace,
                            ws_bytes, nullptr, nullptr, true);
+}
+
+moe_status layer_step_norm(const moe_expert_pool *pool, const float *x, int n_tokens, int d_model,
+                           const float *w_router, const float *b_router, int k,
+                           int32_t *topk_ids, float *topk_w, int32_t *union_ids,
+                           int32_t *n_union, int32_t *expert_offsets, int32_t *perm,
+                           uint64_t *counters, float *y, void *workspace, size_t ws_bytes,
+                           hipStream_t stream, const StackNorm *sn, bool *normed)
+{
+    *normed = false;
+    return layer_step_impl(pool, x, n_tokens, d_model, w_router, b_router, k, topk_ids, topk_w,
+                           union_ids, n_union, expert_offsets, perm, counters, y, workspace,
+                           ws_bytes, stream, nullptr, false, sn, normed);
 }
 
 moe_status expert_forward_phase(const moe_expert_pool *pool, const float *x, int n_tokens, int k,

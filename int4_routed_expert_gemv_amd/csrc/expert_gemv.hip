@@ -29,6 +29,8 @@
 //    reads, always in the same order.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "internal.h"
 #include "topk.h"
 
@@ -245,7 +247,7 @@ __device__ int find_item(const Fwd &f, int item_idx, Item *out)
 // item from the union itself (no separate planning launch) and records the
 // item list for the down pass.
 template <bool GATEUP, int WB, int TB, int NW, int KS, int UB>
-__global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
+__device__ __forceinline__ void gemv_body(const GemvArgs &ga, const int bid, const int nblk)
 {
     constexpr int kGemvThreads = NW * kWave;
     constexpr int XDW = Fmt<WB>::xdw, EPC = Fmt<WB>::epc;
@@ -271,12 +273,12 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
         // the down kernel adds its rows into y: clear y one launch ahead
         // (every workgroup a part, before any of them can leave early)
         const long long n4 = (long long)f.N * g.d / 4;
-        for (long long i = (long long)blockIdx.x * kGemvThreads + tid; i < n4;
-             i += (long long)gridDim.x * kGemvThreads)
+        for (long long i = (long long)bid * kGemvThreads + tid; i < n4;
+             i += (long long)nblk * kGemvThreads)
             reinterpret_cast<float4 *>(f.y)[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
-    const int item_idx = blockIdx.x / ga.n_wg;
-    const int wg = blockIdx.x % ga.n_wg;
+    const int item_idx = bid / ga.n_wg;
+    const int wg = bid % ga.n_wg;
     // The expert is needed first (the weight loads only depend on it); the
     // item's tokens are resolved after when possible.
     int expert;
@@ -291,7 +293,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
         // outputs for the down kernel and the caller (an extra workgroup
         // doing only that measured slower).
         const int nsh = f.has_shared ? 1 : 0;
-        const bool writer = blockIdx.x == 0;
+        const bool writer = bid == 0;
         const bool route = writer || item_idx >= nsh;
         const int A = f.A;  // at most 2 * MOE_MAX_K = 64 assignments: one per lane
         if (tid == 0) {
@@ -638,6 +640,12 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
     }
 }
 
+template <bool GATEUP, int WB, int TB, int NW, int KS, int UB>
+__global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs ga)
+{
+    gemv_body<GATEUP, WB, TB, NW, KS, UB>(ga, blockIdx.x, gridDim.x);
+}
+
 // ---- work list for larger unions ---------------------------------------------
 
 constexpr int kPlanThreads = 1024;
@@ -778,14 +786,77 @@ __global__ __launch_bounds__(256) void combine_kernel(
     reinterpret_cast<float4 *>(y + (size_t)t * d)[q] = acc;
 }
 
-__global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
+// Residual RMS norm of token rows, one workgroup of kNormThreads per token.
+// Rows of d = 4 nq floats (nq <= RV * kNormThreads, 16-byte aligned) keep
+// their values in registers: thread j owns the float4 chunks j, j +
+// kNormThreads, ...; its sum of squares runs over its chunks in order (x, y,
+// z, w), then over the wave, then the four waves' sums pairwise. Other rows
+// take residual_rmsnorm_kernel, with one element per thread at a time.
+constexpr int kNormThreads = 256;
+
+// The rest of the norm for a row whose values (h + y) are in v: the sum of
+// squares, then a = v / sqrt(mean + eps). Shared by the residual norm and the
+// combine that ends in it, so both give the same a for the same v.
+template <int RV>
+__device__ __forceinline__ void norm_finish(const float4 (&v)[RV], int nq, int d, float eps,
+                                            float4 *__restrict__ a4)
+{
+    __shared__ float part[kNormThreads / kWave];
+    const int tid = threadIdx.x;
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < RV; ++j) {
+        if (tid + j * kNormThreads < nq) {
+            ss = fmaf(v[j].x, v[j].x, ss);
+            ss = fmaf(v[j].y, v[j].y, ss);
+            ss = fmaf(v[j].z, v[j].z, ss);
+            ss = fmaf(v[j].w, v[j].w, ss);
+        }
+    }
+    ss = wave_sum(ss);
+    if (tid % kWave == 0) part[tid / kWave] = ss;
+    __syncthreads();
+    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+    const float r = 1.0f / sqrtf(tot / (float)d + eps);
+#pragma unroll
+    for (int j = 0; j < RV; ++j) {
+        const int q = tid + j * kNormThreads;
+        if (q < nq) a4[q] = make_float4(v[j].x * r, v[j].y * r, v[j].z * r, v[j].w * r);
+    }
+}
+
+template <int RV>
+__global__ __launch_bounds__(kNormThreads) void residual_rmsnorm_vec_kernel(
     float *__restrict__ h, const float *__restrict__ y, float *__restrict__ a, int d, float eps)
 {
-    __shared__ float part[256 / kWave];
+    const int t = blockIdx.x, tid = threadIdx.x, nq = d / 4;
+    float4 *h4 = reinterpret_cast<float4 *>(h + (size_t)t * d);
+    float4 v[RV], u[RV];
+#pragma unroll
+    for (int j = 0; j < RV; ++j) {  // every load issued before the first add
+        const int q = min(tid + j * kNormThreads, nq - 1);
+        v[j] = h4[q];
+        if (y) u[j] = reinterpret_cast<const float4 *>(y + (size_t)t * d)[q];
+    }
+    if (y) {
+#pragma unroll
+        for (int j = 0; j < RV; ++j) {
+            v[j] = make_float4(v[j].x + u[j].x, v[j].y + u[j].y, v[j].z + u[j].z, v[j].w + u[j].w);
+            const int q = tid + j * kNormThreads;
+            if (q < nq) h4[q] = v[j];
+        }
+    }
+    norm_finish<RV>(v, nq, d, eps, reinterpret_cast<float4 *>(a + (size_t)t * d));
+}
+
+__global__ __launch_bounds__(kNormThreads) void residual_rmsnorm_kernel(
+    float *__restrict__ h, const float *__restrict__ y, float *__restrict__ a, int d, float eps)
+{
+    __shared__ float part[kNormThreads / kWave];
     const int t = blockIdx.x;
     float *ht = h + (size_t)t * d;
     float ss = 0.0f;
-    for (int i = threadIdx.x; i < d; i += 256) {
+    for (int i = threadIdx.x; i < d; i += kNormThreads) {
         float v = ht[i];
         if (y) {
             v += y[(size_t)t * d + i];
@@ -798,7 +869,79 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
     __syncthreads();
     const float tot = (part[0] + part[1]) + (part[2] + part[3]);
     const float r = 1.0f / sqrtf(tot / (float)d + eps);
-    for (int i = threadIdx.x; i < d; i += 256) a[(size_t)t * d + i] = ht[i] * r;
+    for (int i = threadIdx.x; i < d; i += kNormThreads) a[(size_t)t * d + i] = ht[i] * r;
+}
+
+// The combine of a layer step followed by the residual norm that starts the
+// next one, for a stack of layers: y[t] (the combine's value, in its order
+// of rounding) is added into h[t] and a[t] = rms_norm(h[t]), without writing
+// y. Gives exactly the h and a of combine_kernel then
+// residual_rmsnorm_vec_kernel.
+template <int RV>
+__global__ __launch_bounds__(kNormThreads) void combine_norm_kernel(
+    const float *__restrict__ o, const float *__restrict__ w, int k, int d, int A, int has_shared,
+    float *__restrict__ h, float *__restrict__ a, float eps)
+{
+#pragma clang fp contract(off)
+    const int t = blockIdx.x, tid = threadIdx.x, nq = d / 4;
+    float4 *h4 = reinterpret_cast<float4 *>(h + (size_t)t * d);
+    float4 v[RV], acc[RV];
+#pragma unroll
+    for (int j = 0; j < RV; ++j) {
+        const int q = min(tid + j * kNormThreads, nq - 1);
+        v[j] = h4[q];
+        acc[j] = has_shared ? reinterpret_cast<const float4 *>(o + (size_t)(A + t) * d)[q]
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int i = 0; i < k; ++i) {
+        const float wi = w[(size_t)t * k + i];
+        if (wi == 0.0f) continue;  // adds nothing; a dropped slot's row is never written
+        const float4 *oi = reinterpret_cast<const float4 *>(o + ((size_t)t * k + i) * d);
+        float4 u[RV];
+#pragma unroll
+        for (int j = 0; j < RV; ++j) u[j] = oi[min(tid + j * kNormThreads, nq - 1)];
+#pragma unroll
+        for (int j = 0; j < RV; ++j) {
+            acc[j].x = acc[j].x + wi * u[j].x;
+            acc[j].y = acc[j].y + wi * u[j].y;
+            acc[j].z = acc[j].z + wi * u[j].z;
+            acc[j].w = acc[j].w + wi * u[j].w;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < RV; ++j) {
+        v[j] = make_float4(v[j].x + acc[j].x, v[j].y + acc[j].y, v[j].z + acc[j].z,
+                           v[j].w + acc[j].w);
+        const int q = tid + j * kNormThreads;
+        if (q < nq) h4[q] = v[j];
+    }
+    norm_finish<RV>(v, nq, d, eps, reinterpret_cast<float4 *>(a + (size_t)t * d));
+}
+
+// float4 chunks per thread of the register-resident norm for rows of d
+// floats, or 0 when such rows take the element-wise kernel
+int norm_vec_width(int d)
+{
+    if (d % 4) return 0;
+    const int rv = (d / 4 + kNormThreads - 1) / kNormThreads;
+    for (int w : {1, 2, 4, 6, 8, 12, 16})
+        if (rv <= w) return w;
+    return 0;
+}
+
+template <typename F>
+hipError_t with_norm_width(int rv, F &&go)
+{
+    switch (rv) {
+    case 1: return go(std::integral_constant<int, 1>());
+    case 2: return go(std::integral_constant<int, 2>());
+    case 4: return go(std::integral_constant<int, 4>());
+    case 6: return go(std::integral_constant<int, 6>());
+    case 8: return go(std::integral_constant<int, 8>());
+    case 12: return go(std::integral_constant<int, 12>());
+    case 16: return go(std::integral_constant<int, 16>());
+    default: return hipErrorInvalidValue;
+    }
 }
 
 // ---- dispatch -------------------------------------------------------------
@@ -833,23 +976,39 @@ hipError_t run_gemv(GemvArgs a, hipStream_t s)
 //     wave per unit row with all its units;
 //   longer rows: 4 waves of up to 12 units at a time; single tokens: 4
 //     waves of 4 at a time, or (few workgroups, up to 48 units) 8 waves of 6.
+struct GemvCfg {
+    int nw, ks, ub;  // waves per workgroup, waves per unit row, units per batch
+    bool is(int w, int k, int u) const { return nw == w && ks == k && ub == u; }
+};
+
+GemvCfg gemv_cfg(int epc, bool gateup, const Geo &g, int tb, int max_items)
+{
+    const int K = gateup ? g.d : g.f;
+    const int rows = gateup ? g.f : g.d;
+    const int n_kb = K / (4 * epc);
+    const long long wgs = (long long)max_items * (rows / kUnitRows);
+    const bool few = wgs < kFewWorkgroups;
+    if (n_kb == 1) return {4, 1, 4};
+    if (n_kb < 4) return {4, 2, 4};
+    if (n_kb <= 16) {
+        if (few) return {4, 4, 4};
+        return n_kb <= 8 ? GemvCfg{4, 1, 8} : GemvCfg{4, 1, 16};
+    }
+    if (tb == 1 && n_kb <= 48 && few) return {8, 8, 6};
+    if (tb == 1) return {4, 4, 4};
+    return {4, 4, kUnitBatch};
+}
+
 template <bool GATEUP, int WB, int TB>
 hipError_t run_ks(const GemvArgs &a, hipStream_t s)
 {
-    const int K = GATEUP ? a.f.g.d : a.f.g.f;
-    const int rows = GATEUP ? a.f.g.f : a.f.g.d;
-    const int n_kb = K / (4 * Fmt<WB>::epc);
-    const long long wgs = (long long)a.f.max_items * (rows / kUnitRows);
-    const bool few = wgs < kFewWorkgroups;
-    if (n_kb == 1) return run_gemv<GATEUP, WB, TB, 4, 1, 4>(a, s);
-    if (n_kb < 4) return run_gemv<GATEUP, WB, TB, 4, 2, 4>(a, s);
-    if (n_kb <= 16) {
-        if (few) return run_gemv<GATEUP, WB, TB, 4, 4, 4>(a, s);
-        return n_kb <= 8 ? run_gemv<GATEUP, WB, TB, 4, 1, 8>(a, s)
-                         : run_gemv<GATEUP, WB, TB, 4, 1, 16>(a, s);
-    }
-    if (TB == 1 && n_kb <= 48 && few) return run_gemv<GATEUP, WB, TB, 8, 8, 6>(a, s);
-    if (TB == 1) return run_gemv<GATEUP, WB, TB, 4, 4, 4>(a, s);
+    const GemvCfg c = gemv_cfg(Fmt<WB>::epc, GATEUP, a.f.g, TB, a.f.max_items);
+    if (c.is(4, 1, 4)) return run_gemv<GATEUP, WB, TB, 4, 1, 4>(a, s);
+    if (c.is(4, 2, 4)) return run_gemv<GATEUP, WB, TB, 4, 2, 4>(a, s);
+    if (c.is(4, 4, 4)) return run_gemv<GATEUP, WB, TB, 4, 4, 4>(a, s);
+    if (c.is(4, 1, 8)) return run_gemv<GATEUP, WB, TB, 4, 1, 8>(a, s);
+    if (c.is(4, 1, 16)) return run_gemv<GATEUP, WB, TB, 4, 1, 16>(a, s);
+    if (c.is(8, 8, 6)) return run_gemv<GATEUP, WB, TB, 8, 8, 6>(a, s);
     return run_gemv<GATEUP, WB, TB, 4, 4, kUnitBatch>(a, s);
 }
 
@@ -918,8 +1077,34 @@ hipError_t launch_combine(const float *o, const float *w, int N, int k, int d, i
 hipError_t launch_residual_rmsnorm(float *h, const float *y, float *a, int N, int d, float eps,
                                    hipStream_t s)
 {
-    hipLaunchKernelGGL(residual_rmsnorm_kernel, dim3(N), dim3(256), 0, s, h, y, a, d, eps);
-    return hipGetLastError();
+    const bool al = (uintptr_t)h % 16 == 0 && (uintptr_t)y % 16 == 0 && (uintptr_t)a % 16 == 0;
+    const int rv = al ? norm_vec_width(d) : 0;
+    if (!rv) {
+        hipLaunchKernelGGL(residual_rmsnorm_kernel, dim3(N), dim3(kNormThreads), 0, s, h, y, a, d,
+                           eps);
+        return hipGetLastError();
+    }
+    return with_norm_width(rv, [&](auto w) {
+        hipLaunchKernelGGL(residual_rmsnorm_vec_kernel<decltype(w)::value>, dim3(N),
+                           dim3(kNormThreads), 0, s, h, y, a, d, eps);
+        return hipGetLastError();
+    });
+}
+
+bool combine_norm_supported(int d, const float *h, const float *a)
+{
+    return norm_vec_width(d) > 0 && (uintptr_t)h % 16 == 0 && (uintptr_t)a % 16 == 0;
+}
+
+hipError_t launch_combine_norm(const float *o, const float *w, int N, int k, int d, int A,
+                               int has_shared, float *h, float *a, float eps, hipStream_t s)
+{
+    if (!combine_norm_supported(d, h, a)) return hipErrorInvalidValue;
+    return with_norm_width(norm_vec_width(d), [&](auto wd) {
+        hipLaunchKernelGGL(combine_norm_kernel<decltype(wd)::value>, dim3(N), dim3(kNormThreads),
+                           0, s, o, w, k, d, A, has_shared, h, a, eps);
+        return hipGetLastError();
+    });
 }
 
 }  // namespace moe

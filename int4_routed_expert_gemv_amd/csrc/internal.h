@@ -128,6 +128,20 @@ moe_status layer_step_check(const moe_expert_pool *pool, const float *x, int n_t
                             int32_t *topk_ids, float *topk_w, int32_t *union_ids,
                             int32_t *n_union, int32_t *expert_offsets, int32_t *perm,
                             uint64_t *counters, float *y, void *workspace, size_t ws_bytes);
+// The residual stream of a layer stack: a layer step given one may end with
+// h += y and a = rms_norm(h, eps) in its combine launch (y is then not
+// written) and says so in *normed.
+struct StackNorm {
+    float *h;
+    float *a;
+    float eps;
+};
+moe_status layer_step_norm(const moe_expert_pool *pool, const float *x, int n_tokens, int d_model,
+                           const float *w_router, const float *b_router, int k,
+                           int32_t *topk_ids, float *topk_w, int32_t *union_ids,
+                           int32_t *n_union, int32_t *expert_offsets, int32_t *perm,
+                           uint64_t *counters, float *y, void *workspace, size_t ws_bytes,
+                           hipStream_t stream, const StackNorm *sn, bool *normed);
 // moe_expert_forward restricted to one phase of a two-phase forward (see
 // Fwd::phase): phase_sel 0 computes the experts with phase[e] == 0 and the
 // shared expert, 1 the others and then the combine. check_only: the
@@ -149,8 +163,9 @@ hipError_t launch_router(const float *x, int N, int d, const float *wr, const fl
 struct TopkOpt;
 hipError_t launch_topk(const float *in, int P, const float *b, int N, int E, int k,
                        int32_t *ids, float *w, hipStream_t s, TopkOpt opt);
+// union and permutation in one workgroup; counters (may be null) += the counts
 hipError_t launch_union(const int32_t *ids, int A, int E, int32_t *union_ids, int32_t *n_union,
-                        int32_t *offsets, int32_t *perm, hipStream_t s);
+                        int32_t *offsets, int32_t *perm, uint64_t *counters, hipStream_t s);
 hipError_t launch_hit_count(const int32_t *ids, int A, int E, uint64_t *counters, hipStream_t s);
 // Top-k, union and hit counting of a batch of at most route_tail_max_tokens()
 // tokens in one workgroup (counters may be null).
@@ -183,6 +198,11 @@ hipError_t launch_combine(const float *o, const float *w, int N, int k, int d, i
                           int has_shared, float *y, hipStream_t s);
 hipError_t launch_residual_rmsnorm(float *h, const float *y, float *a, int N, int d, float eps,
                                    hipStream_t s);
+// The combine followed by the residual norm of a layer stack (h += y, a =
+// rms_norm(h), y not written), when the rows take the register-resident norm.
+bool combine_norm_supported(int d, const float *h, const float *a);
+hipError_t launch_combine_norm(const float *o, const float *w, int N, int k, int d, int A,
+                               int has_shared, float *h, float *a, float eps, hipStream_t s);
 
 // ---- device helpers ----------------------------------------------------
 

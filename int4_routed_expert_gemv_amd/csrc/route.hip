@@ -233,15 +233,122 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(
     }
 }
 
+// Larger batches, d a multiple of 128: the same product on the matrix cores in
+// float32 (v_mfma_f32_16x16x4f32: exact float32 products, float32 sums). A
+// workgroup of 4 waves computes a 32-token x 32-expert tile over one K slice
+// (of P); each wave takes a quarter of the slice and the four partial tiles
+// are added in LDS in wave order. Both operands come straight from memory,
+// 16 bytes per lane: within each 16-column block lane l reads columns
+// 4 (l / 16) .. + 3 of token row (or router row) l % 16, and k-step j of the
+// block takes component j of every lane, so a step multiplies matching
+// columns of x and Wr (a permutation of the contraction order, the same for
+// every output). Loads run kRD blocks ahead of the products (kRD even, and
+// every wave's column count a multiple of 32). Rows past N or E
+// read the last row; their outputs are dropped. The output is as
+// router_gemm_kernel's: final scores when P == 1, raw partial sums
+// [P][N][E] otherwise.
+constexpr int kRT = 32;      // tokens and experts per workgroup tile
+constexpr int kRW = 4;       // waves per workgroup, each a quarter of the K slice
+constexpr int kRD = 4;       // 16-column blocks of operands in flight per wave
+
+typedef float rf32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
+    const float *__restrict__ x, int N, int d, const float *__restrict__ wr,
+    const float *__restrict__ b, int E, int P, float *__restrict__ out)
+{
+    __shared__ float red[kRW][kRT][kRT + 1];
+    const int t0 = blockIdx.x * kRT, e0 = blockIdx.y * kRT, p = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+    const int r = lane % 16, kq = lane / 16;
+    const int kw = d / (P * kRW);                    // this wave's columns
+    const int kbeg = p * (d / P) + wv * kw + 4 * kq;
+    const int nb = kw / 16;                          // 16-column blocks
+    const float *xr[2], *wp[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        xr[i] = x + (size_t)min(t0 + 16 * i + r, N - 1) * d + kbeg;
+        wp[i] = wr + (size_t)min(e0 + 16 * i + r, E - 1) * d + kbeg;
+    }
+    float4 xa[kRD][2], wb[kRD][2];
+    auto load = [&](int blk, float4 (&xv)[2], float4 (&wv4)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            xv[i] = *reinterpret_cast<const float4 *>(xr[i] + (size_t)blk * 16);
+            wv4[i] = *reinterpret_cast<const float4 *>(wp[i] + (size_t)blk * 16);
+        }
+    };
+    rf32x4_t acc[2][2], part[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = rf32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kRD; ++s) load(min(s, nb - 1), xa[s], wb[s]);
+    // every load is issued on every path (past the end they reload the last
+    // block into a stage no later step reads), so each wait is for one stage.
+    // Each pair of blocks (32 columns) is summed from zero on its own and then
+    // added to the running sum, which keeps the long dot products' rounding
+    // error near that of a blocked sum (the running sum takes d / 32 adds,
+    // not d / 4)
+    for (int b0 = 0; b0 < nb; b0 += kRD) {
+#pragma unroll
+        for (int s = 0; s < kRD; ++s) {
+            if (b0 + s >= nb) break;
+            const float xs[2][4] = {{xa[s][0].x, xa[s][0].y, xa[s][0].z, xa[s][0].w},
+                                    {xa[s][1].x, xa[s][1].y, xa[s][1].z, xa[s][1].w}};
+            const float ws[2][4] = {{wb[s][0].x, wb[s][0].y, wb[s][0].z, wb[s][0].w},
+                                    {wb[s][1].x, wb[s][1].y, wb[s][1].z, wb[s][1].w}};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int it = 0; it < 2; ++it)
+#pragma unroll
+                    for (int ie = 0; ie < 2; ++ie)
+                        part[it][ie] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            xs[it][j], ws[ie][j],
+                            (s % 2 == 0 && j == 0) ? rf32x4_t{0.f, 0.f, 0.f, 0.f} : part[it][ie],
+                            0, 0, 0);
+            if (s % 2 == 1) {
+#pragma unroll
+                for (int it = 0; it < 2; ++it)
+#pragma unroll
+                    for (int ie = 0; ie < 2; ++ie) acc[it][ie] += part[it][ie];
+            }
+            load(min(b0 + s + kRD, nb - 1), xa[s], wb[s]);
+        }
+    }
+    // register v of block (it, ie): token 16 it + 4 kq + v, expert 16 ie + r
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int ie = 0; ie < 2; ++ie)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) red[wv][16 * it + 4 * kq + v][16 * ie + r] = acc[it][ie][v];
+    __syncthreads();
+    for (int o = tid; o < kRT * kRT; o += kRW * kWave) {
+        const int tt = o / kRT, ee = o % kRT;
+        const int t = t0 + tt, e = e0 + ee;
+        if (t >= N || e >= E) continue;
+        float v = red[0][tt][ee];
+#pragma unroll
+        for (int w = 1; w < kRW; ++w) v += red[w][tt][ee];
+        if (P == 1)
+            out[(size_t)t * E + e] = sigmoidf(v + (b ? b[e] : 0.0f));
+        else
+            out[((size_t)p * N + t) * E + e] = v;
+    }
+}
+
 // One wave per token (the selection itself is topk_wave).
-template <bool OPT>
+template <bool OPT, int PB>
 __global__ __launch_bounds__(256) void topk_kernel(
     const float *__restrict__ in, int P, const float *__restrict__ b, int N, int E, int k,
     int32_t *__restrict__ ids, float *__restrict__ w, TopkOpt opt)
 {
     const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     if (t >= N) return;
-    topk_wave<OPT>(in, P, b, N, E, k, t, ids, w, nullptr, opt);
+    topk_wave<OPT, PB>(in, P, b, N, E, k, t, ids, w, nullptr, opt);
 }
 
 }  // namespace
@@ -257,10 +364,22 @@ int router_slices_bound(int N, int E)
     return p;
 }
 
+// whether launch_router takes the matrix-core router
+bool router_on_mfma(int N, int d) { return N > kGemvMaxTokens && d % (kRW * 32) == 0; }
+
 int router_slices(int N, int d, int E)
 {
     if (N <= kGemvMaxTokens) return 1;
-    int p = router_slices_bound(N, E);
+    const int bound = router_slices_bound(N, E);
+    if (router_on_mfma(N, d)) {
+        // K slices until the 32 x 32 tiles give 256 workgroups (one per
+        // compute unit: each holds four waves on the matrix cores)
+        const long long tiles = (long long)((N + kRT - 1) / kRT) * ((E + kRT - 1) / kRT);
+        int p = 1;
+        while (p < bound && tiles * p < 256 && d % (2 * p * kRW * 32) == 0) p *= 2;
+        return p;
+    }
+    int p = bound;
     while (p > 1 && (d % (p * kTK)) != 0) p /= 2;
     return p;
 }
@@ -283,6 +402,11 @@ hipError_t launch_router(const float *x, int N, int d, const float *wr, const fl
         else
             hipLaunchKernelGGL(router_gemv_stream_kernel, dim3(E), dim3(kRouterThreads), 0, s, x,
                                N, d, wr, b, E, out);
+    } else if (router_on_mfma(N, d)) {
+        const int P = router_slices(N, d, E);
+        dim3 grid((N + kRT - 1) / kRT, (E + kRT - 1) / kRT, P);
+        hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(kRW * kWave), 0, s, x, N, d, wr, b, E, P,
+                           out);
     } else {
         const int P = router_slices(N, d, E);
         dim3 grid((N + kTM - 1) / kTM, (E + kTN - 1) / kTN, P);
@@ -295,10 +419,19 @@ hipError_t launch_topk(const float *in, int P, const float *b, int N, int E, int
                        float *w, hipStream_t s, TopkOpt opt)
 {
     const int per_block = 4;
-    hipLaunchKernelGGL(opt.any() ? topk_kernel<true> : topk_kernel<false>,
-                       dim3((N + per_block - 1) / per_block), dim3(per_block * kWave), 0, s, in, P,
-                       b, N, E, k, ids, w, opt);
-    return hipGetLastError();
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3((N + per_block - 1) / per_block), dim3(per_block * kWave), 0,
+                           s, in, P, b, N, E, k, ids, w, opt);
+        return hipGetLastError();
+    };
+    // the slice bound fixes how many partial sums each lane loads at a time
+    const bool o = opt.any();
+    if (P <= 1) return o ? go(topk_kernel<true, 1>) : go(topk_kernel<false, 1>);
+    if (P <= 2) return o ? go(topk_kernel<true, 2>) : go(topk_kernel<false, 2>);
+    if (P <= 4) return o ? go(topk_kernel<true, 4>) : go(topk_kernel<false, 4>);
+    if (P <= 8) return o ? go(topk_kernel<true, 8>) : go(topk_kernel<false, 8>);
+    if (P <= kMaxSlices) return o ? go(topk_kernel<true, kMaxSlices>) : go(topk_kernel<false, kMaxSlices>);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace moe

@@ -1,7 +1,8 @@
 // stack.hip - a stack of MoE layers chained through the residual stream, one
 // call: for each layer, the residual RMS norm of the stream, the layer step
 // (route, union, counters, experts, combine), and the layer's output added
-// back. This is how the speculative-decoding flow runs its draft steps (the
+// back. Where a layer step ends with the combine kernel, that launch also adds
+// the output into the stream and takes the next norm. This is how the speculative-decoding flow runs its draft steps (the
 // int8 draft-head layer) and its verify batch (the int4 layers) through the
 // same kernels (Colibri README, "Speculative decoding, honestly": draft
 // tokens are verified as one batch by the main layers).
@@ -99,19 +100,24 @@ moe_status moe_stack_forward(const moe_layer_desc *layers, int n_layers, int n_t
         if (st != MOE_OK) return st;
     }
     if (topk_ids_out && ((uintptr_t)topk_ids_out % 4)) return MOE_EALIGN;
+    bool normed = false;  // the last layer step ended with h += y, a = rms(h)
     for (int l = 0; l < n_layers; ++l) {
         const moe_layer_desc &ly = layers[l];
         int32_t *ids = topk_ids_out ? topk_ids_out + l * nk : reinterpret_cast<int32_t *>(ws + L.ids);
-        // h += y of the layer before (none before the first), a = rms(h)
-        moe_status st = moe_residual_rmsnorm(h, l ? y : nullptr, a, n_tokens, d, eps, stream);
+        // h += y of the layer before (none before the first), a = rms(h),
+        // unless that layer's combine did it
+        moe_status st = MOE_OK;
+        if (!normed) st = moe_residual_rmsnorm(h, l ? y : nullptr, a, n_tokens, d, eps, stream);
         if (st != MOE_OK) return st;
-        st = moe_layer_step(&ly.pool, a, n_tokens, d, ly.w_router, ly.b_router, k, ids, w, uid,
-                            nu, off, perm, ly.counters, y, sws, sbytes, stream, nullptr);
+        const moe::StackNorm sn{h, a, eps};
+        st = moe::layer_step_norm(&ly.pool, a, n_tokens, d, ly.w_router, ly.b_router, k, ids, w,
+                                  uid, nu, off, perm, ly.counters, y, sws, sbytes, stream, &sn,
+                                  &normed);
         if (st != MOE_OK) return st;
     }
     // the last layer's output joins the stream (the norm it also computes
     // goes to the scratch a)
-    return moe_residual_rmsnorm(h, y, a, n_tokens, d, eps, stream);
+    return normed ? MOE_OK : moe_residual_rmsnorm(h, y, a, n_tokens, d, eps, stream);
 }
 
 }  // extern "C"

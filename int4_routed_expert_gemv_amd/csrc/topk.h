@@ -36,6 +36,39 @@ __device__ __forceinline__ uint32_t sortable(float v)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// (bh, bl) = the larger of (bh, bl) and (oh, ol), compared as one 64-bit key
+__device__ __forceinline__ void key_max(uint32_t &bh, uint32_t &bl, uint32_t oh, uint32_t ol)
+{
+    if (oh > bh || (oh == bh && ol > bl)) {
+        bh = oh;
+        bl = ol;
+    }
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+
+// The largest 64-bit key (bh, bl) of the wave, in every lane: within each
+// row of 16 lanes by DPP moves (quad swaps, then the half-row and row
+// mirrors), then over the four rows by lane reads. Every lane of the wave
+// must be active.
+__device__ __forceinline__ void wave_max_key(uint32_t &bh, uint32_t &bl)
+{
+    key_max(bh, bl, dpp_u32<0xB1>(bh), dpp_u32<0xB1>(bl));    // lanes i ^ 1
+    key_max(bh, bl, dpp_u32<0x4E>(bh), dpp_u32<0x4E>(bl));    // lanes i ^ 2
+    key_max(bh, bl, dpp_u32<0x141>(bh), dpp_u32<0x141>(bl));  // half-row mirror
+    key_max(bh, bl, dpp_u32<0x140>(bh), dpp_u32<0x140>(bl));  // row mirror
+    uint32_t h = __builtin_amdgcn_readlane(bh, 0), l = __builtin_amdgcn_readlane(bl, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r)
+        key_max(h, l, __builtin_amdgcn_readlane(bh, 16 * r), __builtin_amdgcn_readlane(bl, 16 * r));
+    bh = h;
+    bl = l;
+}
+
 // Opt-in router variant. sel (may be null): a bias that only steers the
 // selection, the key of expert e being the float32 sum s + sel[e] while the
 // weight stays the score; norm: each weight is divided by the sum of the k
@@ -63,8 +96,9 @@ struct TopkOpt {
 // winner writes ids/w[t * k + j] and, when lds_ids is not null,
 // lds_ids[t * k + j].
 // OPT false: the options are ignored (the default reading, compiled without
-// them); true: they apply.
-template <bool OPT>
+// them); true: they apply. PB: a bound of P known at compile time (the
+// partial sums of 64 / PB experts per lane are loaded at a time).
+template <bool OPT, int PB = kMaxSlices>
 __device__ __forceinline__ void topk_wave(const float *__restrict__ in, int P,
                                           const float *__restrict__ b, int N, int E, int k, int t,
                                           int32_t *__restrict__ ids, float *__restrict__ w,
@@ -84,16 +118,17 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ in, int P,
         // the partial sums of kGroup experts per lane at a time, every load
         // of a group issued together (slices past P and experts past E read
         // valid entries that are not used), then added in slice order
-        constexpr int kGroup = 4;
+        constexpr int kSl = PB < kMaxSlices ? PB : kMaxSlices;
+        constexpr int kGroup = (64 / kSl) < kMaxPerLane ? 64 / kSl : kMaxPerLane;
 #pragma unroll
         for (int g = 0; g < kMaxPerLane; g += kGroup) {
             if (g * kWave >= E) break;
-            float part[kGroup][kMaxSlices], bias[kGroup];
+            float part[kGroup][kSl], bias[kGroup];
 #pragma unroll
             for (int mm = 0; mm < kGroup; ++mm) {
                 const int e = min(lane + (g + mm) * kWave, E - 1);
 #pragma unroll
-                for (int p = 0; p < kMaxSlices; ++p)
+                for (int p = 0; p < kSl; ++p)
                     part[mm][p] = in[((size_t)min(p, P - 1) * N + t) * E + e];
                 bias[mm] = b ? b[e] : 0.0f;
             }
@@ -102,7 +137,7 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ in, int P,
                 const int e = lane + (g + mm) * kWave;
                 float l = 0.0f;
 #pragma unroll
-                for (int p = 0; p < kMaxSlices; ++p)
+                for (int p = 0; p < kSl; ++p)
                     if (p < P) l += part[mm][p];
                 sv[g + mm] = e < E ? sigmoidf(l + bias[mm]) : 0.0f;
             }
@@ -137,11 +172,7 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ in, int P,
 #pragma unroll
         for (int m = 1; m < kMaxPerLane; ++m)
             if (m == bm) bs = sv[m];
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            uint32_t oh = __shfl_xor(bh, o, kWave), ol = __shfl_xor(bl, o, kWave);
-            if (oh > bh || (oh == bh && ol > bl)) { bh = oh; bl = ol; }
-        }
+        wave_max_key(bh, bl);
         const int id = (int)(0xFFFFFFFFu - bl);
         if (bm >= 0 && lane + bm * kWave == id) {
             // the lane holding the winner records it

@@ -34,29 +34,55 @@ __device__ __forceinline__ int wave_incl_scan_int(int v)
     return v;
 }
 
-// Union and permutation by one workgroup of kUnionThreads threads. ids may
-// point to global or LDS memory. On return cnt[e] (LDS) holds expert e's
-// number of assignments for e < E.
+// waves of a union workgroup, each with its own chunk of the assignments
+constexpr int kUnionWaves = kUnionThreads / kWave;
+
+// Union and permutation by one workgroup of kUnionThreads threads. The
+// assignments are cut into kUnionWaves contiguous chunks of whole 64-lane
+// rounds, one per wave, in ascending order. ids may point to global or LDS
+// memory; when stage is not null (LDS room for A ids) the ids are copied
+// there as the histogram reads them and read back from there. hist: LDS of
+// kUnionWaves * E ints (per-wave counts, then per-wave first positions); base:
+// LDS of E ints. When counters is not null, counters[e] += expert e's count
+// (the Learn stage's hit counts).
 __device__ __forceinline__ void union_block(const int32_t *ids, int A, int E,
                                             int32_t *__restrict__ union_ids,
                                             int32_t *__restrict__ n_union,
                                             int32_t *__restrict__ offsets,
-                                            int32_t *__restrict__ perm, int *cnt, int *base)
+                                            int32_t *__restrict__ perm,
+                                            unsigned long long *__restrict__ counters, int *hist,
+                                            int *base, int *stage)
 {
     const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+    const int C = ((A + kUnionWaves - 1) / kUnionWaves + kWave - 1) / kWave * kWave;
+    const int a0 = min(A, wv * C), a1 = min(A, a0 + C);
+    int *hw = hist + wv * E;  // this wave's counts, then its positions
 
-    for (int e = tid; e < E; e += kUnionThreads) cnt[e] = 0;
+    for (int i = tid; i < kUnionWaves * E; i += kUnionThreads) hist[i] = 0;
     __syncthreads();
-    // integer histogram: the result does not depend on the order of the adds
-    for (int a = tid; a < A; a += kUnionThreads) {
-        int e = ids[a];
-        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    // per-wave integer histograms: the result does not depend on the order
+    // of the adds
+    for (int a = a0 + lane; a < a1; a += kWave) {
+        const int e = ids[a];
+        if (stage) stage[a] = e;
+        if (e >= 0 && e < E) atomicAdd(&hw[e], 1);
     }
     __syncthreads();
+    if (stage) ids = stage;
 
-    // exclusive prefix sums over experts, one expert per thread (E <= 1024):
-    // counts -> offsets, and "used" flags -> positions in union_ids
-    const int c = tid < E ? cnt[tid] : 0;
+    // per expert (a thread each, E <= 1024): its count, and where each
+    // wave's assignments start within the expert's slice (the counts of the
+    // waves before it)
+    int c = 0;
+    if (tid < E) {
+        for (int w = 0; w < kUnionWaves; ++w) {
+            const int h = hist[w * E + tid];
+            hist[w * E + tid] = c;
+            c += h;
+        }
+    }
+    // exclusive prefix sums over experts: counts -> offsets, and "used"
+    // flags -> positions in union_ids
     const int used = c > 0 ? 1 : 0;
     // wave-level inclusive scans of (c, used) packed as c * 2048 + used
     // (c <= A < 2^20 is checked on the host, so the pack cannot overflow)
@@ -66,17 +92,17 @@ __device__ __forceinline__ void union_block(const int32_t *ids, int A, int E,
         long long u = __shfl_up(v, o, kWave);
         if (lane >= o) v += u;
     }
-    __shared__ long long wtot[kUnionThreads / kWave];
+    __shared__ long long wtot[kUnionWaves];
     if (lane == kWave - 1) wtot[wv] = v;
     __syncthreads();
     if (wv == 0) {
-        long long s = lane < kUnionThreads / kWave ? wtot[lane] : 0;
+        long long x = lane < kUnionWaves ? wtot[lane] : 0;
 #pragma unroll
         for (int o = 1; o < kWave; o <<= 1) {
-            long long u = __shfl_up(s, o, kWave);
-            if (lane >= o) s += u;
+            long long u = __shfl_up(x, o, kWave);
+            if (lane >= o) x += u;
         }
-        if (lane < kUnionThreads / kWave) wtot[lane] = s;  // inclusive
+        if (lane < kUnionWaves) wtot[lane] = x;  // inclusive
     }
     __syncthreads();
     long long incl = v + (wv > 0 ? wtot[wv - 1] : 0);
@@ -86,46 +112,47 @@ __device__ __forceinline__ void union_block(const int32_t *ids, int A, int E,
         offsets[tid] = off;
         base[tid] = off;
         if (used) union_ids[upos] = tid;
+        if (counters && used) atomicAdd(&counters[tid], (unsigned long long)c);
     }
     if (tid == kUnionThreads - 1) {
-        const long long tot = wtot[kUnionThreads / kWave - 1];
+        const long long tot = wtot[kUnionWaves - 1];
         offsets[E] = (int)(tot / 2048);
         *n_union = (int)(tot % 2048);
     }
     __syncthreads();
 
-    // stable scatter by one wave, 64 assignments at a time in ascending a: the
-    // rank of an assignment among the earlier lanes with the same expert comes
-    // from ballots on the bits of the expert id
-    if (wv == 0) {
-        const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-        for (int a0 = 0; a0 < A; a0 += kWave) {
-            const int a = a0 + lane;
-            int e = a < A ? ids[a] : -1;
-            const bool valid = e >= 0 && e < E;
-            if (!valid) e = -1;
-            unsigned long long peers = __ballot(valid);
+    // stable scatter: every wave its own chunk, 64 assignments at a time in
+    // ascending a; an assignment goes to its expert's offset + the earlier
+    // waves' count + its rank among the earlier assignments of its wave with
+    // the same expert (ballots on the bits of the expert id)
+    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    for (int r0 = a0; r0 < a1; r0 += kWave) {
+        const int a = r0 + lane;
+        int e = a < a1 ? ids[a] : -1;
+        const bool valid = e >= 0 && e < E;
+        if (!valid) e = -1;
+        unsigned long long peers = __ballot(valid);
 #pragma unroll
-            for (int bit = 0; bit < 11; ++bit) {  // E <= 1024 < 2^11, and -1 stays apart
-                const unsigned long long m = __ballot((e >> bit) & 1);
-                peers &= ((e >> bit) & 1) ? m : ~m;
-            }
-            int rank = 0, b = 0;
-            if (valid) {
-                rank = __popcll(peers & lt);
-                b = base[e];
-            }
-            // all reads of base[] finish before any lane writes it back
-            __builtin_amdgcn_s_waitcnt(kLdsWait);
-            __builtin_amdgcn_wave_barrier();
-            if (valid) {
-                perm[b + rank] = a;
-                const bool last = (peers >> lane) == 1ull;  // highest peer lane
-                if (last) base[e] = b + rank + 1;
-            }
-            __builtin_amdgcn_s_waitcnt(kLdsWait);
-            __builtin_amdgcn_wave_barrier();
+        for (int bit = 0; bit < 11; ++bit) {  // E <= 1024 < 2^11, and -1 stays apart
+            const unsigned long long m = __ballot((e >> bit) & 1);
+            peers &= ((e >> bit) & 1) ? m : ~m;
         }
+        int rank = 0, bw = 0, bo = 0;
+        if (valid) {
+            rank = __popcll(peers & lt);
+            bw = hw[e];
+            bo = base[e];
+        }
+        // all reads of hw[] finish before any lane writes it back
+        __builtin_amdgcn_s_waitcnt(kLdsWait);
+        __builtin_amdgcn_wave_barrier();
+        if (valid) {
+            perm[bo + bw + rank] = a;
+            const bool last = (peers >> lane) == 1ull;  // highest peer lane
+            if (last) hw[e] = bw + rank + 1;
+        }
+        __builtin_amdgcn_s_waitcnt(kLdsWait);
+        __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
 }
@@ -200,13 +227,19 @@ __device__ __forceinline__ void union_wave(const int32_t *ids, int A, int E,
     }
 }
 
+// ids of up to this many assignments are staged in LDS by union_kernel
+constexpr int kUnionStage = 4096;
+
 __global__ __launch_bounds__(kUnionThreads) void union_kernel(
     const int32_t *__restrict__ ids, int A, int E, int32_t *__restrict__ union_ids,
-    int32_t *__restrict__ n_union, int32_t *__restrict__ offsets, int32_t *__restrict__ perm)
+    int32_t *__restrict__ n_union, int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
+    unsigned long long *__restrict__ counters)
 {
-    __shared__ int cnt[MOE_MAX_EXPERTS];
+    __shared__ int hist[kUnionWaves * MOE_MAX_EXPERTS];
     __shared__ int base[MOE_MAX_EXPERTS];
-    union_block(ids, A, E, union_ids, n_union, offsets, perm, cnt, base);
+    __shared__ int stage[kUnionStage];
+    union_block(ids, A, E, union_ids, n_union, offsets, perm, counters, hist, base,
+                A <= kUnionStage ? stage : nullptr);
 }
 
 // Route tail of a small batch (N <= kTailTokens): one wave per token selects
@@ -228,6 +261,7 @@ __global__ __launch_bounds__(kUnionThreads) void route_tail_kernel(
     __shared__ int32_t s_ids[kTailTokens * MOE_MAX_K];
     __shared__ int cnt[MOE_MAX_EXPERTS];
     __shared__ int base[MOE_MAX_EXPERTS];
+    __shared__ int hist[kUnionWaves * MOE_MAX_EXPERTS];
     const int tid = threadIdx.x, A = N * k;
     for (int a = tid; a < A; a += blockDim.x) s_ids[a] = -1;
     __syncthreads();
@@ -238,10 +272,7 @@ __global__ __launch_bounds__(kUnionThreads) void route_tail_kernel(
         if (t == 0) union_wave(s_ids, A, E, union_ids, n_union, offsets, perm, counters, cnt);
         return;
     }
-    union_block(s_ids, A, E, union_ids, n_union, offsets, perm, cnt, base);
-    if (counters)
-        for (int e = tid; e < E; e += kUnionThreads)
-            if (cnt[e]) atomicAdd(&counters[e], (unsigned long long)cnt[e]);
+    union_block(s_ids, A, E, union_ids, n_union, offsets, perm, counters, hist, base, nullptr);
 }
 
 // ---- large batches: union, permutation and counts over several workgroups --
@@ -408,10 +439,10 @@ __global__ __launch_bounds__(kHitThreads) void hit_count_kernel(
 }  // namespace
 
 hipError_t launch_union(const int32_t *ids, int A, int E, int32_t *union_ids, int32_t *n_union,
-                        int32_t *offsets, int32_t *perm, hipStream_t s)
+                        int32_t *offsets, int32_t *perm, uint64_t *counters, hipStream_t s)
 {
     hipLaunchKernelGGL(union_kernel, dim3(1), dim3(kUnionThreads), 0, s, ids, A, E, union_ids,
-                       n_union, offsets, perm);
+                       n_union, offsets, perm, reinterpret_cast<unsigned long long *>(counters));
     return hipGetLastError();
 }
 
