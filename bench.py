@@ -351,8 +351,10 @@ def build_workload(name, args, steps, warmup, layers, batches, dev, tokens=None,
 
 
 class Runner:
-    """Launches the steps of a workload through the C ABI (moe_layer_step, and
-    moe_residual_rmsnorm between the layers of a stack)."""
+    """Launches the steps of a workload through the C ABI: moe_layer_step for
+    a single layer; for a stack, moe_stack_forward (or, when events or
+    per-layer callbacks are asked for, moe_residual_rmsnorm and
+    moe_layer_step per layer)."""
 
     def __init__(self, wl, hip, torch):
         import int4_routed_expert_gemv_amd as moe
@@ -380,6 +382,18 @@ class Runner:
 
         if wl["stack"]:
             self.layer_args = [args(l, b["abuf"]) for l in range(wl["L_rot"])]
+            # the timed steps run the whole stack in one moe_stack_forward call;
+            # calibration and the per-kernel event pass take its layers one
+            # moe_layer_step at a time (the same kernels and outputs, bit for
+            # bit, except that the stack call joins each combine with the next
+            # residual norm)
+            self.stack_layers = moe.layer_descs(
+                [(wl["pools"][l].desc, wl["routers"][l][0], wl["routers"][l][1],
+                  b["counters"][l]) for l in range(wl["L_rot"])])
+            nbytes = moe.stack_workspace_size(self.stack_layers, N, k)
+            if nbytes <= 0:
+                raise RuntimeError("moe_stack_workspace_size rejected the stack")
+            self.stack_ws = torch.empty(nbytes, dtype=torch.uint8, device=b["y"].device)
         else:
             # one plan per (layer pool, batch) pair: step s takes plan s % n_plan
             self.plans = [args(p % wl["L_rot"], wl["xs"][p % wl["nb"]])
@@ -404,6 +418,14 @@ class Runner:
         x = wl["xs"][s % wl["nb"]]
         rc = self.hip.L.hipMemcpyAsync(vp(b["hbuf"].data_ptr()), vp(x.data_ptr()),
                                        x.numel() * 4, 3, self.stream)
+        if evs is None and sync_layers is None:
+            rc |= self.L.moe_stack_forward(self.stack_layers, wl["L_rot"], wl["N"], wl["k"],
+                                           ctypes.c_float(1e-6), vp(b["hbuf"].data_ptr()), None,
+                                           vp(self.stack_ws.data_ptr()), self.stack_ws.numel(),
+                                           self.stream)
+            if rc:
+                raise RuntimeError(f"stack step failed with status {rc}")
+            return
         for l in range(wl["L_rot"]):
             rc |= self.L.moe_residual_rmsnorm(vp(b["hbuf"].data_ptr()),
                                               vp(b["y"].data_ptr()) if l else None,
@@ -421,7 +443,8 @@ def calibrate(wl, runner, torch, small_min):
     library's default thresholds): experts with at least 32 tokens go to the
     128-token matrix-core pass, those with at least small_min (default 1) to
     the 32-token pass, the rest (and every expert of a batch of at most 2
-    tokens) to the GEMV; fewer than 32 items of 128 tokens join the 32-token pass; a
+    tokens) to the GEMV; fewer than 32 items of 128 tokens, or fewer than
+    32 * 128 assignments in the batch, join the 32-token pass; a
     128-token group's remainder of at most 32 tokens past a full item goes to
     the 32-token pass. The shared expert counts as an expert of N tokens."""
     import numpy as np
@@ -435,7 +458,8 @@ def calibrate(wl, runner, torch, small_min):
         T = np.asarray(T)
         big = (T >= MFMA_MIN) & mfma_ok
         small = ~big & (T >= SMALL_MIN) & mfma_ok & (N > GEMV_BATCH or small_min is not None)
-        if big.any() and np.sum((T[big] + 127) // 128) < MIN_BIG_ITEMS:
+        if big.any() and (np.sum((T[big] + 127) // 128) < MIN_BIG_ITEMS or
+                          N * wl["k"] < MIN_BIG_ITEMS * 128):
             small, big = small | big, np.zeros_like(big)
         return np.where(big, 1, np.where(small, 2, 0))
 
@@ -549,6 +573,7 @@ def measure(wl, args, steps, warmup, hip, torch, traffic_key):
         fo[s] = [moe.ForwardOptions(*[hip.event() for _ in range(12)], 0,
                                     wl["small_min"] if wl["small_min"] is not None else 0)
                  for _ in range(per_step_layers)]
+    ev_fields = [n for n, t in moe.ForwardOptions._fields_ if t is ctypes.c_void_p]
     torch.cuda.synchronize()
     for s in range(warmup, warmup + max(K, every * n_samp)):
         runner.step(s, evs=fo.get(s))
@@ -578,7 +603,7 @@ def measure(wl, args, steps, warmup, hip, torch, traffic_key):
                      c[pname + "_experts"] * (bb - gub), t_dn))
     for opts in fo:
         for o in opts:
-            for fld, _ in moe.ForwardOptions._fields_[:12]:
+            for fld in ev_fields:
                 hip.L.hipEventDestroy(getattr(o, fld))
 
     passes = {}
@@ -593,7 +618,8 @@ def measure(wl, args, steps, warmup, hip, torch, traffic_key):
             "flops_per_launch": fl, "achieved_TFLOPs": fl / 1e12 / t_gu,
             "total_ms_in_sample": float(v[:, 2].sum()),
             "down_avg_launch_us": t_dn * 1e6 if t_dn else None,
-            "down_GBps": dn_b / 1e9 / t_dn if t_dn else None, "dtype": DTYPE_BY_PASS[pname]}
+            "down_GBps": dn_b / 1e9 / t_dn if t_dn else None,
+            "dtype": DTYPE_BY_PASS[pname]}
 
     # algorithmic bytes of the timed steps (pass 1)
     expert_bytes = router_bytes = 0
@@ -609,7 +635,7 @@ def measure(wl, args, steps, warmup, hip, torch, traffic_key):
         # the dominant kernel: the gate/up kernel with the most time in the sample
         top = max(passes, key=lambda n: passes[n]["total_ms_in_sample"])
         pz = passes[top]
-        pname = top.split("_")[0]
+        pname = top.rsplit("_int", 1)[0]
         if pname == "mfma":
             roof = {"bound": "mfma", "achieved": pz["achieved_TFLOPs"],
                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
