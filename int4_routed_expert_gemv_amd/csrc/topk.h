@@ -98,12 +98,15 @@ struct TopkOpt {
 // OPT false: the options are ignored (the default reading, compiled without
 // them); true: they apply. PB: a bound of P known at compile time (the
 // partial sums of 64 / PB experts per lane are loaded at a time).
-template <bool OPT, int PB = kMaxSlices>
-__device__ __forceinline__ void topk_wave(const float *__restrict__ in, int P,
-                                          const float *__restrict__ b, int N, int E, int k, int t,
-                                          int32_t *__restrict__ ids, float *__restrict__ w,
-                                          int32_t *lds_ids, TopkOpt opt = TopkOpt())
+// MPL: experts per lane the code is unrolled for (E <= 64 * MPL).
+template <bool OPT, int PB, int MPL>
+__device__ __forceinline__ void topk_wave_impl(const float *__restrict__ in, int P,
+                                               const float *__restrict__ b, int N, int E, int k,
+                                               int t, int32_t *__restrict__ ids,
+                                               float *__restrict__ w, int32_t *lds_ids,
+                                               TopkOpt opt)
 {
+    constexpr int kMaxPerLane = MPL;
     const int lane = threadIdx.x % kWave;
     uint32_t hi[kMaxPerLane];
     float sv[kMaxPerLane] = {};
@@ -201,6 +204,19 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ in, int P,
             !keep ? 0.0f : (opt.norm ? wmine / wsum * opt.scale : wmine * opt.scale);
         if (lds_ids) lds_ids[t * k + lane] = idv;
     }
+}
+
+template <bool OPT, int PB = kMaxSlices>
+__device__ __forceinline__ void topk_wave(const float *__restrict__ in, int P,
+                                          const float *__restrict__ b, int N, int E, int k, int t,
+                                          int32_t *__restrict__ ids, float *__restrict__ w,
+                                          int32_t *lds_ids, TopkOpt opt = TopkOpt())
+{
+    // up to 256 experts, each round scans four candidates per lane, not 16
+    if (E <= 4 * kWave)
+        topk_wave_impl<OPT, PB, 4>(in, P, b, N, E, k, t, ids, w, lds_ids, opt);
+    else
+        topk_wave_impl<OPT, PB, kMaxPerLane>(in, P, b, N, E, k, t, ids, w, lds_ids, opt);
 }
 
 }  // namespace moe
