@@ -3,6 +3,7 @@ and include/moe_cache.h) and libmoe_probe.so (the measurement probes of
 include/moe_probe.h, loaded by the benchmark only)."""
 import glob
 import os
+import re
 import subprocess
 import sys
 
@@ -57,8 +58,53 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
         tmp = lib + ".tmp"
         subprocess.check_call([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs,
                                "-o", tmp])
+        missing = kernels_without_code(tmp)
+        if missing:
+            os.remove(tmp)
+            raise RuntimeError(f"{os.path.basename(lib)}: host code launches kernels that its "
+                               f"gfx950 code object lacks: {missing}")
         os.replace(tmp, lib)
     return LIB
+
+
+_STUB = re.compile(rb"_Z[A-Za-z0-9_]*__device_stub__[A-Za-z0-9_]*")
+_PREFIX = "__device_stub__"
+
+
+def _kernel_of_stub(sym: str):
+    """The mangled kernel name of a host launch stub's: the stub's name with
+    the prefix taken out of its identifier (lengths read in order, so the
+    anonymous namespace's own digits are not mistaken for one)."""
+    i = 3 if sym.startswith("_ZN") else 2
+    while i < len(sym) and sym[i].isdigit():
+        j = i
+        while sym[j].isdigit():
+            j += 1
+        n = int(sym[i:j])
+        ident = sym[j:j + n]
+        if ident.startswith(_PREFIX):
+            return sym[:i] + str(n - len(_PREFIX)) + ident[len(_PREFIX):] + sym[j + n:]
+        i = j + n
+    return None
+
+
+def kernels_without_code(path: str) -> list:
+    """Kernels whose host launch stub is in the library but whose kernel
+    descriptor (name.kd) is not in its device code object. A library like
+    that (e.g. host and device passes of one source that saw different
+    versions of it) fails in the HIP runtime when it first loads the code
+    object. Returns [] when the code object is not readable as plain text
+    (no descriptor names at all)."""
+    blob = open(path, "rb").read()
+    kds = {k.decode() for k in re.findall(rb"([A-Za-z0-9_]+)\.kd", blob)}
+    if not kds:
+        return []
+    missing = set()
+    for m in _STUB.finditer(blob):
+        name = _kernel_of_stub(m.group(0).decode())
+        if name is not None and name not in kds:
+            missing.add(name)
+    return sorted(missing)
 
 
 def _wait(item):

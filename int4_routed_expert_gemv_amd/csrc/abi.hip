@@ -573,8 +573,10 @@ static moe_status forward_impl(const moe_expert_pool *pool, const float *x, int 
         return MOE_EHIP;
     // gate/up of every pass (the first launch also builds the work lists),
     // then down of every pass, then the combine
-    if (launch_gateup(f, stream) != hipSuccess) return MOE_EHIP;
-    if ((f.max_mitems > 0 || f.max_sitems > 0) && launch_stage_x16(f, stream) != hipSuccess)
+    bool x16_staged = false;
+    if (launch_gateup(f, stream, &x16_staged) != hipSuccess) return MOE_EHIP;
+    if ((f.max_mitems > 0 || f.max_sitems > 0) && !x16_staged &&
+        launch_stage_x16(f, stream) != hipSuccess)
         return MOE_EHIP;
     if (launch_mfma(f, true, false, stream) != hipSuccess) return MOE_EHIP;
     if (launch_mfma(f, true, true, stream) != hipSuccess) return MOE_EHIP;

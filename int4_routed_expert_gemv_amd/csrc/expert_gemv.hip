@@ -683,7 +683,7 @@ __device__ __forceinline__ int pass_of(const Fwd &f, int T)
 // slot. Each expert goes to the list of its pass in slices of that list's
 // tokens per item (tb, 128 or 32); in every list the shared expert comes
 // first, then the union experts in union order.
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(Fwd f)
+__device__ __forceinline__ void plan_body(const Fwd &f)
 {
     const int u = threadIdx.x;
     const int E = f.g.E;
@@ -757,6 +757,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Fwd f)
         }
         if (u == 0) *counts[l] = min(nsh + tot, mx);
     }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(Fwd f) { plan_body(f); }
+
+// The planning workgroup (block 0) and, in the other blocks, the float16
+// copy of x for the matrix-core passes (independent work, one launch).
+template <int WB>
+__global__ __launch_bounds__(kPlanThreads) void plan_stage_kernel(Fwd f, long long n8)
+{
+    if (blockIdx.x == 0) {
+        plan_body(f);
+        return;
+    }
+    const long long i = (long long)(blockIdx.x - 1) * kPlanThreads + threadIdx.x;
+    if (i < n8) stage_x16_group<WB>(f.x, i, f.x16);
 }
 
 // ---- combine and chaining ---------------------------------------------------
@@ -1035,8 +1050,9 @@ int gemv_tokens_per_item(const Geo &g, int max_tokens)
     return tb;
 }
 
-hipError_t launch_gateup(const Fwd &f, hipStream_t s)
+hipError_t launch_gateup(const Fwd &f, hipStream_t s, bool *x16_staged)
 {
+    *x16_staged = false;
     GemvArgs a;
     a.f = f;
     a.n_wg = 0;
@@ -1049,7 +1065,18 @@ hipError_t launch_gateup(const Fwd &f, hipStream_t s)
                       : 0;
     if (f.route_in && (a.plan_here != 2 || f.N > 2)) return hipErrorInvalidValue;
     if (!a.plan_here) {
-        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, f);
+        if (f.max_mitems > 0 || f.max_sitems > 0) {
+            // the matrix-core passes run: their x16 in the same launch
+            const long long n8 = (long long)f.N * f.g.d / 8;
+            const dim3 grid((unsigned)(1 + (n8 + kPlanThreads - 1) / kPlanThreads));
+            if (f.g.wbits == 8)
+                hipLaunchKernelGGL(plan_stage_kernel<8>, grid, dim3(kPlanThreads), 0, s, f, n8);
+            else
+                hipLaunchKernelGGL(plan_stage_kernel<4>, grid, dim3(kPlanThreads), 0, s, f, n8);
+            *x16_staged = true;
+        } else {
+            hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, f);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -114,14 +114,6 @@ __device__ __forceinline__ half8_t dequant8(const uint4 &u, int s, half2_t s2)
     return r;
 }
 
-// Column j of an 8-column group goes to position perm8<WB>(j) of the
-// float16 operand, matching dequant8.
-template <int WB>
-__device__ __forceinline__ int perm8(int j)
-{
-    if constexpr (WB == 4) return j < 4 ? 2 * j : 2 * (j - 4) + 1;
-    else return (j & 4) | ((j & 1) << 1) | ((j >> 1) & 1);
-}
 
 struct MfmaArgs {
     Fwd f;
@@ -136,11 +128,19 @@ struct MfmaArgs {
 // tokens. Weight loads run two (128-token items) or four (32-token items)
 // unit steps ahead of the matrix cores (registers), activations are
 // double-buffered in LDS.
-// POST: the codes enter the matrix cores unscaled (exact small integers) and
-// each step's float32 products are scaled per row afterwards; for scale
-// groups that cover whole unit steps (or whole rows), with fewer vector
-// instructions per code and no float16 rounding of code x scale.
-template <bool GATEUP, int WB, int MF, bool POST>
+// Where the scales are applied (SM):
+//  kScaleCode: each code times its group's scale, rounded to float16, enters
+//    the matrix cores (any group size);
+//  kScaleStep: the codes enter unscaled (exact small integers) and each unit
+//    step's float32 products are scaled per row afterwards (groups that cover
+//    whole unit steps): fewer vector instructions per code, no float16
+//    rounding of code x scale;
+//  kScaleRow: one scale per row (group 0): the unscaled products accumulate
+//    over the whole row and the float32 sums are scaled once, in the
+//    epilogue (no per-step work at all).
+constexpr int kScaleCode = 0, kScaleStep = 1, kScaleRow = 2;
+
+template <bool GATEUP, int WB, int MF, int SM>
 __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs ma)
 {
     constexpr int kThreads = waves_per_wg(MF) * 64;
@@ -281,6 +281,7 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
         // half of a unit step on LDS buffer `cur` and weights (bw, bs):
         // k-steps s_lo .. s_lo + NS/2 - 1 of 32, each lane's quarter q
         // covering columns QW q + 8s .. + 8
+        constexpr bool POST = SM == kScaleStep;
         f32x4_t tmp[POST ? NM : 1][POST ? TW : 1][POST ? NB : 1];  // a step's unscaled products
         auto compute = [&](int cur, const uint4 (&bw)[TW][NM], const float (&bs)[TW][NM],
                            int s_lo) {
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
                 for (int t = 0; t < TW; ++t)
 #pragma unroll
                     for (int m = 0; m < NM; ++m)
-                        bf[t][m] = dequant8<WB, !POST>(bw[t][m], s, s2[t][m]);
+                        bf[t][m] = dequant8<WB, SM == kScaleCode>(bw[t][m], s, s2[t][m]);
 #pragma unroll
                 for (int mb = 0; mb < NB; ++mb) {
                     const half8_t af =
@@ -425,6 +426,17 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
     for (int t = 0; t < TW; ++t) {
         const int row = (rt0 + t) * kUnitRows + r16;
         if (rt0 + t >= n_rt) continue;
+        if constexpr (SM == kScaleRow) {
+            // the row's one scale per matrix, on the whole row's sums
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                const float sc = sb[t][m][0];
+#pragma unroll
+                for (int mb = 0; mb < MF; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[m][t][mb][r] *= sc;
+            }
+        }
 #pragma unroll
         for (int mb = 0; mb < MF; ++mb) {
 #pragma unroll
@@ -448,21 +460,12 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
     }
 }
 
-// x [N][d] float32 -> x16 [N][d] float16, each 8-column group in the order
-// the MFMA weight operand takes its codes (one thread per group).
 template <int WB>
 __global__ __launch_bounds__(256) void stage_x16_kernel(const float *__restrict__ x, long long n8,
                                                         uint16_t *__restrict__ x16)
 {
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n8) return;
-    const float4 a = reinterpret_cast<const float4 *>(x)[2 * i];
-    const float4 b = reinterpret_cast<const float4 *>(x)[2 * i + 1];
-    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    half8_t h;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) h[perm8<WB>(j)] = (_Float16)v[j];
-    reinterpret_cast<half8_t *>(x16)[i] = h;
+    if (i < n8) stage_x16_group<WB>(x, i, x16);
 }
 
 }  // namespace
@@ -472,16 +475,16 @@ bool mfma_supported(const Geo &g)
     return (g.wbits == 4 && g.ucols == MFmt<4>::UC) || (g.wbits == 8 && g.ucols == MFmt<8>::UC);
 }
 
-template <bool GATEUP, int WB, int MF, bool POST>
+template <bool GATEUP, int WB, int MF, int SM>
 hipError_t run_mfma(const MfmaArgs &a, long long blocks, const hipEvent_t *ev, hipStream_t s)
 {
     constexpr int kThreads = waves_per_wg(MF) * 64;
     const dim3 grid((unsigned)blocks);
     if (ev[0] || ev[1])  // events taken by the dispatch itself, around this kernel only
-        hipExtLaunchKernelGGL((mfma_kernel<GATEUP, WB, MF, POST>), grid, dim3(kThreads), 0, s, ev[0], ev[1],
+        hipExtLaunchKernelGGL((mfma_kernel<GATEUP, WB, MF, SM>), grid, dim3(kThreads), 0, s, ev[0], ev[1],
                               0, a);
     else
-        hipLaunchKernelGGL((mfma_kernel<GATEUP, WB, MF, POST>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((mfma_kernel<GATEUP, WB, MF, SM>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -511,27 +514,34 @@ hipError_t launch_mfma(const Fwd &f, bool gateup, bool small, hipStream_t s)
     if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     const hipEvent_t *ev = small ? (gateup ? f.ev_sgu : f.ev_sdn) : (gateup ? f.ev_mgu : f.ev_mdn);
     constexpr int kSmall = kMfmaSmallTokens / 16, kBig = kMfmaBigTokens / 16;
-    // small items: scales after the products when every scale group covers
-    // whole unit steps (G == 0: whole rows)
-    const bool post = small && (f.g.group == 0 || f.g.group % f.g.ucols == 0);
+    // where the scales go: per row when a row has one scale (int8 layers:
+    // the draft head's format), per unit step for 32-token items whose
+    // groups cover whole steps, else per code
+    const int G = f.g.group;
+    const bool post = small && (G == 0 || G % f.g.ucols == 0);
     if (f.g.wbits == 8) {
+        if (G == 0)
+            return small ? (gateup ? run_mfma<true, 8, kSmall, kScaleRow>(a, blocks, ev, s)
+                                   : run_mfma<false, 8, kSmall, kScaleRow>(a, blocks, ev, s))
+                         : (gateup ? run_mfma<true, 8, kBig, kScaleRow>(a, blocks, ev, s)
+                                   : run_mfma<false, 8, kBig, kScaleRow>(a, blocks, ev, s));
         if (post)
-            return gateup ? run_mfma<true, 8, kSmall, true>(a, blocks, ev, s)
-                          : run_mfma<false, 8, kSmall, true>(a, blocks, ev, s);
+            return gateup ? run_mfma<true, 8, kSmall, kScaleStep>(a, blocks, ev, s)
+                          : run_mfma<false, 8, kSmall, kScaleStep>(a, blocks, ev, s);
         if (small)
-            return gateup ? run_mfma<true, 8, kSmall, false>(a, blocks, ev, s)
-                          : run_mfma<false, 8, kSmall, false>(a, blocks, ev, s);
-        return gateup ? run_mfma<true, 8, kBig, false>(a, blocks, ev, s)
-                      : run_mfma<false, 8, kBig, false>(a, blocks, ev, s);
+            return gateup ? run_mfma<true, 8, kSmall, kScaleCode>(a, blocks, ev, s)
+                          : run_mfma<false, 8, kSmall, kScaleCode>(a, blocks, ev, s);
+        return gateup ? run_mfma<true, 8, kBig, kScaleCode>(a, blocks, ev, s)
+                      : run_mfma<false, 8, kBig, kScaleCode>(a, blocks, ev, s);
     }
     if (post)
-        return gateup ? run_mfma<true, 4, kSmall, true>(a, blocks, ev, s)
-                      : run_mfma<false, 4, kSmall, true>(a, blocks, ev, s);
+        return gateup ? run_mfma<true, 4, kSmall, kScaleStep>(a, blocks, ev, s)
+                      : run_mfma<false, 4, kSmall, kScaleStep>(a, blocks, ev, s);
     if (small)
-        return gateup ? run_mfma<true, 4, kSmall, false>(a, blocks, ev, s)
-                      : run_mfma<false, 4, kSmall, false>(a, blocks, ev, s);
-    return gateup ? run_mfma<true, 4, kBig, false>(a, blocks, ev, s)
-                  : run_mfma<false, 4, kBig, false>(a, blocks, ev, s);
+        return gateup ? run_mfma<true, 4, kSmall, kScaleCode>(a, blocks, ev, s)
+                      : run_mfma<false, 4, kSmall, kScaleCode>(a, blocks, ev, s);
+    return gateup ? run_mfma<true, 4, kBig, kScaleCode>(a, blocks, ev, s)
+                  : run_mfma<false, 4, kBig, kScaleCode>(a, blocks, ev, s);
 }
 
 }  // namespace moe

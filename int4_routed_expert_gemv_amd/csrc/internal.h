@@ -183,7 +183,9 @@ hipError_t launch_route_tail(const float *in, int P, const float *b, int N, int 
                              int32_t *offsets, int32_t *perm, uint64_t *counters, hipStream_t s,
                              TopkOpt opt);
 int gemv_tokens_per_item(const Geo &g, int n_tokens);
-hipError_t launch_gateup(const Fwd &f, hipStream_t s);
+// The GEMV gate/up pass and, when a planning launch is needed, that launch
+// first; *x16_staged: whether it also wrote x16 (the matrix-core passes').
+hipError_t launch_gateup(const Fwd &f, hipStream_t s, bool *x16_staged);
 hipError_t launch_down(const Fwd &f, hipStream_t s);
 bool mfma_supported(const Geo &g);
 constexpr int kMfmaBigTokens = 128;   // tokens per item of the large-group MFMA pass
@@ -192,7 +194,8 @@ constexpr int kMfmaSmallTokens = 32;  // tokens per item of the small-group MFMA
 constexpr int kMinBigItems = 32;
 // small = false: the 128-token items (mitems), true: the 32-token items (sitems)
 hipError_t launch_mfma(const Fwd &f, bool gateup, bool small, hipStream_t s);
-// x -> x16 for the matrix-core passes
+// x -> x16 for the matrix-core passes (launch_gateup does it in the
+// planning launch when that runs; launch_stage_x16 on its own otherwise)
 hipError_t launch_stage_x16(const Fwd &f, hipStream_t s);
 hipError_t launch_combine(const float *o, const float *w, int N, int k, int d, int A,
                           int has_shared, float *y, hipStream_t s);
@@ -205,6 +208,32 @@ hipError_t launch_combine_norm(const float *o, const float *w, int N, int k, int
                                int has_shared, float *h, float *a, float eps, hipStream_t s);
 
 // ---- device helpers ----------------------------------------------------
+
+// Column j of an 8-column group goes to position perm8<WB>(j) of the matrix
+// cores' float16 operand, in the order the weight operand takes its codes
+// (int4: the low nibbles of a word's four bytes, then the high nibbles).
+template <int WB>
+__device__ __forceinline__ int perm8(int j)
+{
+    if constexpr (WB == 4) return j < 4 ? 2 * j : 2 * (j - 4) + 1;
+    else return (j & 4) | ((j & 1) << 1) | ((j >> 1) & 1);
+}
+
+// x [N][d] float32 -> x16 [N][d] float16 for the matrix-core passes: the
+// 8-column group i, each column at its perm8 position.
+template <int WB>
+__device__ __forceinline__ void stage_x16_group(const float *__restrict__ x, long long i,
+                                                uint16_t *__restrict__ x16)
+{
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    const float4 a = reinterpret_cast<const float4 *>(x)[2 * i];
+    const float4 b = reinterpret_cast<const float4 *>(x)[2 * i + 1];
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    h8 h;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[perm8<WB>(j)] = (_Float16)v[j];
+    reinterpret_cast<h8 *>(x16)[i] = h;
+}
 
 // (a & m) | o in one instruction (v_and_or_b32; the compiler emits an AND
 // and an OR for constant masks). m goes in a scalar register, o in a vector

@@ -43,6 +43,17 @@ def test_exports_every_declared_symbol():
         assert hasattr(moe.probe_lib(), n)
 
 
+def test_every_launched_kernel_has_gfx950_code():
+    """Each kernel the host code can launch has a descriptor in the library's
+    code object (host and device passes built from one version of a source)."""
+    from int4_routed_expert_gemv_amd import build
+    for path in (moe.LIB_PATH, moe.PROBE_LIB_PATH):
+        stubs = {m.decode() for m in build._STUB.findall(open(path, "rb").read())}
+        assert stubs, path
+        assert all(build._kernel_of_stub(s) for s in stubs), path
+        assert build.kernels_without_code(path) == [], path
+
+
 def test_probe_argument_checks():
     L = moe.probe_lib()
     # size not a multiple of 1024, bad batch, bad workgroup, sink too small, misaligned
