@@ -25,7 +25,7 @@
 //    (x converted once per call by stage_x16_kernel, h written so by the
 //    gate/up epilogue) and are copied into LDS one unit step at a time,
 //    double-buffered, loaded one step ahead;
-//  * each wave owns one or two unit rows and all MT tokens; weight
+//  * each wave owns two or four unit rows and all MT tokens; weight
 //    loads run up to four steps ahead of the matrix cores.
 // Workgroups are mapped so that those sharing an expert (and so its weights
 // and its tokens) land on the same XCD and share its L2.
@@ -44,14 +44,16 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // Waves per workgroup and unit rows per wave. 32-token items: 4 waves of 2
 // unit rows. 128-token items: 8 waves (two per SIMD, so one wave's products
-// overlap the other's operand work) of 1 unit row for gate/up (two matrices)
-// or 2 for down; their accumulators (128 tokens x the wave's rows) then fit
-// the registers of two waves per SIMD. Either way a workgroup covers 128
-// rows of gate/up or 128 / 256 rows of down.
+// overlap the other's operand work) of 2 unit rows for gate/up (two
+// matrices) or 4 for down: 64 weight rows per wave, so each activation
+// fragment read from LDS feeds 64 rows of products; the accumulators (128
+// tokens x 64 rows, 128 registers) still fit two waves per SIMD. A workgroup
+// covers 128 rows of gate/up or 128 of down (32-token items), 256 of gate/up
+// or 512 of down (128-token items).
 __host__ __device__ constexpr int waves_per_wg(int mf) { return mf < 8 ? 4 : 8; }
 __host__ __device__ constexpr int tiles_per_wave(bool gateup, int mf)
 {
-    return mf < 8 ? 2 : (gateup ? 1 : 2);
+    return mf < 8 ? 2 : (gateup ? 2 : 4);
 }
 __host__ __device__ constexpr int rows_per_wg(bool gateup, int mf)
 {
@@ -124,7 +126,7 @@ struct MfmaArgs {
 };
 
 // One workgroup: one MFMA item (<= MT tokens of one expert) x
-// rows_per_wg(GATEUP, MF) rows; each wave owns 16 or 32 rows and all MT
+// rows_per_wg(GATEUP, MF) rows; each wave owns 32 or 64 rows and all MT
 // tokens. Weight loads run two (128-token items) or four (32-token items)
 // unit steps ahead of the matrix cores (registers), activations are
 // double-buffered in LDS.
@@ -318,6 +320,10 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
                             }
                         }
                 }
+                // 128-token items: one k-step's operands live at a time
+                // (hoisting the next k-steps' dequantisation spills the
+                // accumulators of 64 rows x 128 tokens)
+                if constexpr (MF == 8) __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (POST) {
                 if (s_lo + NS / 2 == NS) {
