@@ -22,9 +22,9 @@
 //    0,4,1,5,2,6,3,7 on both operands, which lets one 32-bit word of codes
 //    feed one MFMA operand without shuffles;
 //  * activations come as float16 rows already in the operand's column order
-//    (x converted once per call by stage_x16_kernel, h written so by the
-//    gate/up epilogue) and are copied into LDS one unit step at a time,
-//    double-buffered, loaded one step ahead;
+//    (x converted once per call by plan_stage_kernel or stage_x16_kernel, h
+//    written so by the gate/up epilogue) and are copied into LDS one unit
+//    step at a time, double-buffered;
 //  * each wave owns two or four unit rows and all MT tokens; weight
 //    loads run up to four steps ahead of the matrix cores.
 // Workgroups are mapped so that those sharing an expert (and so its weights
