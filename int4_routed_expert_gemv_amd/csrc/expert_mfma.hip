@@ -70,42 +70,50 @@ template <> struct MFmt<8> { static constexpr int UC = 64, NS = 2, QW = 16, NA =
 
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 
-// The 8 codes of k-step s of a lane's 16 bytes times the scale, as float16:
+// The 8 codes of k-step s of a lane's 16 bytes as float16:
 // int4: the codes of 32-bit word s (element j in bits 4j..4j+3), in the
 //   column order 0,4,1,5,2,6,3,7;
 // int8: the bytes of words 2s and 2s+1, in the column order 0,2,1,3,4,6,5,7.
-// Codes are offset binary (u = q + 8). ORed into the mantissa of 1024, a code
-// in bits 0..3 of a half gives 1024 + u, one in bits 4..7 gives 1024 + 16 u
-// (both exact); the first loses 1032 (one packed add), the second is scaled
-// by 1/16 and loses 72 (one packed fused multiply-add): q exactly either way,
-// with one shift per word instead of three. Then (SCALED) one rounding by the
-// scale.
-template <int WB, bool SCALED = true>
+// Codes are offset binary (u = q + 8, or q + 128). ORed into the mantissa of
+// 1024 (one AND-OR per pair of codes, exact), a code in bits 0..3 of a half
+// gives 1024 + u = 1032 + q, one in bits 4..7 gives 1024 + 16 u = 1152 + 16 q
+// (its activation is stored divided by 16, so the product is (72 + q) x),
+// an int8 code 1024 + u = 1152 + q. One shift per word brings the other
+// half of the codes into place. DQ says what leaves:
+//   kDqBiased: those biased values (the bias is taken out on the matrix
+//     cores, by products with a constant operand: bias_operand);
+//   kDqExact: q (16 q in bits 4..7), one packed subtraction per pair;
+//   kDqScaled: that times the group scale, one float16 rounding.
+constexpr int kDqBiased = 0, kDqExact = 1, kDqScaled = 2;
+
+template <int WB, int DQ>
 __device__ __forceinline__ half8_t dequant8(const uint4 &u, int s, half2_t s2)
 {
     const uint32_t magic = 0x64006400u;
     const uint32_t d[4] = {u.x, u.y, u.z, u.w};
-    half2_t p[4];
+    uint32_t v[4];
     if constexpr (WB == 4) {
-        const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
-        const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-        const half2_t off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
         const uint32_t w = d[s], w8 = w >> 8, lo = 0x000F000Fu, hi = 0x00F000F0u;
-        p[0] = as_h2(and_or(w, lo, magic)) - off;
-        p[1] = __builtin_elementwise_fma(as_h2(and_or(w, hi, magic)), sixteenth, off16);
-        p[2] = as_h2(and_or(w8, lo, magic)) - off;
-        p[3] = __builtin_elementwise_fma(as_h2(and_or(w8, hi, magic)), sixteenth, off16);
+        v[0] = and_or(w, lo, magic);
+        v[1] = and_or(w, hi, magic);
+        v[2] = and_or(w8, lo, magic);
+        v[3] = and_or(w8, hi, magic);
     } else {
-        const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
         const uint32_t w0 = d[2 * s], w1 = d[2 * s + 1], m = 0x00FF00FFu;
-        p[0] = as_h2(and_or(w0, m, magic)) - off;
-        p[1] = as_h2(and_or(w0 >> 8, m, magic)) - off;
-        p[2] = as_h2(and_or(w1, m, magic)) - off;
-        p[3] = as_h2(and_or(w1 >> 8, m, magic)) - off;
+        v[0] = and_or(w0, m, magic);
+        v[1] = and_or(w0 >> 8, m, magic);
+        v[2] = and_or(w1, m, magic);
+        v[3] = and_or(w1 >> 8, m, magic);
     }
-    if constexpr (SCALED) {
+    half2_t p[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = p[i] * s2;
+    for (int i = 0; i < 4; ++i) {
+        p[i] = as_h2(v[i]);
+        if constexpr (DQ != kDqBiased) {
+            const _Float16 off = (WB == 4 && (i & 1) == 0) ? (_Float16)1032.0f : (_Float16)1152.0f;
+            p[i] = p[i] - half2_t{off, off};
+        }
+        if constexpr (DQ == kDqScaled) p[i] = p[i] * s2;
     }
     half8_t r;
 #pragma unroll
@@ -113,6 +121,20 @@ __device__ __forceinline__ half8_t dequant8(const uint4 &u, int s, half2_t s2)
         r[2 * i] = p[i][0];
         r[2 * i + 1] = p[i][1];
     }
+    return r;
+}
+
+// The weight operand whose products with the activations give minus the
+// biases that kDqBiased leaves: -1032 at the low-nibble positions, -1152 at
+// the others (int8: everywhere). Exact in float16. The product does not
+// depend on the weight row, so one accumulator per token block carries it.
+template <int WB>
+__device__ __forceinline__ half8_t bias_operand()
+{
+    half8_t r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        r[i] = (WB == 4 && (i & 2) == 0) ? (_Float16)-1032.0f : (_Float16)-1152.0f;
     return r;
 }
 
@@ -242,6 +264,21 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
             for (int mb = 0; mb < MF; ++mb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[m][t][mb][r] = 0.0f;
+    // Codes scaled per unit step on the 32-token gate/up pass enter the
+    // matrix cores biased (kDqBiased: four fewer vector instructions per
+    // eight int4 codes); one more product per token block and k-step against
+    // bias_operand sums minus the biases of the step in bacc, which is added
+    // to the step's products before they are scaled. The other passes
+    // subtract the biases in the vector units: down has one matrix, so the
+    // bias products would be half as many again as its own and it measured
+    // slower; carried over a whole row (one scale per row) the float32 sums
+    // of the biased products and of the biases cancel too many bits; the
+    // 128-token passes are bound by the matrix cores.
+    constexpr bool BIAS = SM == kScaleStep && MF <= 2 && GATEUP;
+    constexpr int DQ = SM == kScaleCode ? kDqScaled : (BIAS ? kDqBiased : kDqExact);
+    f32x4_t bacc[BIAS ? MF : 1];
+#pragma unroll
+    for (int mb = 0; mb < (BIAS ? MF : 1); ++mb) bacc[mb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     // weight stages in registers: 32-token items (short steps, fewer
     // accumulators) keep four steps in flight, 128-token items two
@@ -300,11 +337,16 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
                 for (int t = 0; t < TW; ++t)
 #pragma unroll
                     for (int m = 0; m < NM; ++m)
-                        bf[t][m] = dequant8<WB, SM == kScaleCode>(bw[t][m], s, s2[t][m]);
+                        bf[t][m] = dequant8<WB, DQ>(bw[t][m], s, s2[t][m]);
 #pragma unroll
                 for (int mb = 0; mb < NB; ++mb) {
                     const half8_t af =
                         *reinterpret_cast<const half8_t *>(&As[cur][mb * 16 + r16][QW * q + 8 * s]);
+                    if constexpr (BIAS) {
+                        const f32x4_t c0 = {0.0f, 0.0f, 0.0f, 0.0f};
+                        bacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            af, bias_operand<WB>(), s == 0 ? c0 : bacc[mb], 0, 0, 0);
+                    }
 #pragma unroll
                     for (int t = 0; t < TW; ++t)
 #pragma unroll
@@ -336,9 +378,11 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
 #pragma unroll
                             for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
-                                for (int r = 0; r < 4; ++r)
-                                    acc[m][t][mb][r] =
-                                        fmaf(bs[t][m], tmp[m][t][mb][r], acc[m][t][mb][r]);
+                                for (int r = 0; r < 4; ++r) {
+                                    float v = tmp[m][t][mb][r];
+                                    if constexpr (BIAS) v += bacc[mb][r];
+                                    acc[m][t][mb][r] = fmaf(bs[t][m], v, acc[m][t][mb][r]);
+                                }
                 }
             }
         };
@@ -454,7 +498,9 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
                     // hidden value as the down pass's float16 operand: row
                     // `row` of this pass is column `row` of the down pass
                     const float gv = acc[0][t][mb][r], uv = acc[NM - 1][t][mb][r];
-                    const _Float16 hv = (_Float16)(gv / (1.0f + expf(-gv)) * uv);
+                    // (times act16_factor of its column in the down pass)
+                    const _Float16 hv = (_Float16)(gv / (1.0f + expf(-gv)) * uv *
+                                                   act16_factor<WB>(row & 7));
                     f.h16[(size_t)p * rows + (row & ~7) + perm8<WB>(row & 7)] =
                         __builtin_bit_cast(uint16_t, hv);
                 } else {

@@ -219,8 +219,18 @@ __device__ __forceinline__ int perm8(int j)
     else return (j & 4) | ((j & 1) << 1) | ((j >> 1) & 1);
 }
 
+// Factor applied to column j of an 8-column group in the matrix cores'
+// float16 operand: int4 codes in the high nibble of their byte (odd j) enter
+// the products as 16 u (the nibble's own bit position in a float16 mantissa),
+// so their activations are stored divided by 16 (exact: a power of two).
+template <int WB>
+__host__ __device__ constexpr float act16_factor(int j)
+{
+    return (WB == 4 && (j & 1)) ? 0.0625f : 1.0f;
+}
+
 // x [N][d] float32 -> x16 [N][d] float16 for the matrix-core passes: the
-// 8-column group i, each column at its perm8 position.
+// 8-column group i, each column at its perm8 position, times act16_factor.
 template <int WB>
 __device__ __forceinline__ void stage_x16_group(const float *__restrict__ x, long long i,
                                                 uint16_t *__restrict__ x16)
@@ -231,7 +241,7 @@ __device__ __forceinline__ void stage_x16_group(const float *__restrict__ x, lon
     const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     h8 h;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) h[perm8<WB>(j)] = (_Float16)v[j];
+    for (int j = 0; j < 8; ++j) h[perm8<WB>(j)] = (_Float16)(v[j] * act16_factor<WB>(j));
     reinterpret_cast<h8 *>(x16)[i] = h;
 }
 
