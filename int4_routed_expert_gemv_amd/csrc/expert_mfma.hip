@@ -164,8 +164,16 @@ struct MfmaArgs {
 //    epilogue (no per-step work at all).
 constexpr int kScaleCode = 0, kScaleStep = 1, kScaleRow = 2;
 
+// Workgroups per compute unit the register allocation must allow: the
+// 32-token down kernels keep four (four waves per SIMD, 128 registers).
+__host__ __device__ constexpr int min_wgs_per_cu(bool gateup, int mf)
+{
+    return (!gateup && mf <= 2) ? 4 : 1;
+}
+
 template <bool GATEUP, int WB, int MF, int SM>
-__global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs ma)
+__global__ __launch_bounds__(waves_per_wg(MF) * 64, min_wgs_per_cu(GATEUP, MF)) void mfma_kernel(
+    MfmaArgs ma)
 {
     constexpr int kThreads = waves_per_wg(MF) * 64;
     constexpr int MT = 16 * MF;  // tokens per item
@@ -393,12 +401,12 @@ __global__ __launch_bounds__(waves_per_wg(MF) * 64, 1) void mfma_kernel(MfmaArgs
         // register stage of half a step, loaded during the current step's
         // products and stored to the other LDS buffer. D is even, so the LDS
         // buffer of step ks + j (ks a multiple of D) is j % 2.
-        // activations: a ring of AD register stages (AD = 2 for the gate/up
-        // of 32-token items: each step's tile is loaded two steps ahead of
-        // its products; the others load one step ahead: down items keep
-        // their registers for occupancy, and 128-token items, whose steps
-        // are long, measured slower with two)
-        constexpr int AD = (GATEUP && MF <= 2) ? 2 : 1;
+        // activations: a ring of AD register stages (AD = 2 for 32-token
+        // items but int8 down: each step's tile is loaded two steps ahead of
+        // its products; the others load one step ahead: the int8 down kernel
+        // measured slower with two, and so did 128-token items, whose steps
+        // are long)
+        constexpr int AD = (MF <= 2 && (GATEUP || WB == 4)) ? 2 : 1;
         uint4 ar[2][kNA][kVec];
         uint4 bwr[D][TW][NM];
         float bsr[D][TW][NM];
