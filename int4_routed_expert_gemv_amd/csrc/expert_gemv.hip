@@ -908,19 +908,30 @@ __global__ __launch_bounds__(kNormThreads) void combine_norm_kernel(
         acc[j] = has_shared ? reinterpret_cast<const float4 *>(o + (size_t)(A + t) * d)[q]
                             : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    for (int i = 0; i < k; ++i) {
-        const float wi = w[(size_t)t * k + i];
-        if (wi == 0.0f) continue;  // adds nothing; a dropped slot's row is never written
-        const float4 *oi = reinterpret_cast<const float4 *>(o + ((size_t)t * k + i) * d);
-        float4 u[RV];
+    // the rows of KC slots are loaded together, then added in slot order
+    constexpr int KC = RV <= 6 ? 8 : (RV <= 12 ? 4 : 2);
+    for (int i0 = 0; i0 < k; i0 += KC) {
+        float4 u[KC][RV];
+        float wc[KC];
 #pragma unroll
-        for (int j = 0; j < RV; ++j) u[j] = oi[min(tid + j * kNormThreads, nq - 1)];
+        for (int c = 0; c < KC; ++c) {
+            const int i = min(i0 + c, k - 1);
+            wc[c] = i0 + c < k ? w[(size_t)t * k + i] : 0.0f;
+            const float4 *oi = reinterpret_cast<const float4 *>(o + ((size_t)t * k + i) * d);
 #pragma unroll
-        for (int j = 0; j < RV; ++j) {
-            acc[j].x = acc[j].x + wi * u[j].x;
-            acc[j].y = acc[j].y + wi * u[j].y;
-            acc[j].z = acc[j].z + wi * u[j].z;
-            acc[j].w = acc[j].w + wi * u[j].w;
+            for (int j = 0; j < RV; ++j) u[c][j] = oi[min(tid + j * kNormThreads, nq - 1)];
+        }
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            const float wi = wc[c];
+            if (wi == 0.0f) continue;  // adds nothing; a dropped slot's row is never written
+#pragma unroll
+            for (int j = 0; j < RV; ++j) {
+                acc[j].x = acc[j].x + wi * u[c][j].x;
+                acc[j].y = acc[j].y + wi * u[c][j].y;
+                acc[j].z = acc[j].z + wi * u[c][j].z;
+                acc[j].w = acc[j].w + wi * u[c][j].w;
+            }
         }
     }
 #pragma unroll
