@@ -8,23 +8,27 @@
 // scales).
 //
 // For one expert and up to MT of its tokens (MT = 128 for large groups, 32
-// for small ones), a workgroup of 4 or 8 waves computes 128 output rows (of
-// gate and up together), or 128 / 256 rows of down, over the full contraction:
+// for small ones), a workgroup of 4 or 8 waves computes 128 or 256 output
+// rows of gate and up (each), or 128 or 512 rows of down, over the full
+// contraction:
 //   gate/up:  h[p][r] = silu(sum_c Wg[r][c] x_t[c]) * (sum_c Wu[r][c] x_t[c])
 //   down:     o[out(p)][r] = sum_c Wd[r][c] h[p][c]
 // on v_mfma_f32_16x16x32_f16 (float16 products, float32 accumulation):
 //  * the weights are read in their 1 KB units (16 rows x 128 int4 columns):
 //    one 16-byte load per lane is one unit, and the lane's 32 codes are its
 //    weight operand for four MFMA steps; they are expanded in registers: OR
-//    into the mantissa of 1024 (exact), subtract 1032 (exact), multiply by
-//    the group scale (one float16 rounding);
+//    into the mantissa of 1024 (exact, a constant bias per code position),
+//    then the bias subtracted (exact) or, in the 32-token gate/up pass with
+//    one scale per unit step, taken out by products of the activations with
+//    a constant operand; where groups are finer than a unit step, times the
+//    group scale (one float16 rounding);
 //  * within each 8-column group the columns are taken in the order
 //    0,4,1,5,2,6,3,7 on both operands, which lets one 32-bit word of codes
 //    feed one MFMA operand without shuffles;
 //  * activations come as float16 rows already in the operand's column order
 //    (x converted once per call by plan_stage_kernel or stage_x16_kernel, h
-//    written so by the gate/up epilogue) and are copied into LDS one unit
-//    step at a time, double-buffered;
+//    written so by the gate/up epilogue; int4 high-nibble columns divided by
+//    16) and are copied into LDS one unit step at a time, double-buffered;
 //  * each wave owns two or four unit rows and all MT tokens; weight
 //    loads run up to four steps ahead of the matrix cores.
 // Workgroups are mapped so that those sharing an expert (and so its weights
