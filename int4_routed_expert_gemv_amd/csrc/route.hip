@@ -247,87 +247,88 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(
 // read the last row; their outputs are dropped. The output is as
 // router_gemm_kernel's: final scores when P == 1, raw partial sums
 // [P][N][E] otherwise.
-constexpr int kRT = 32;      // tokens and experts per workgroup tile
+constexpr int kRT = 32;      // tokens and experts per workgroup tile (the large one: 64)
 constexpr int kRW = 4;       // waves per workgroup, each a quarter of the K slice
-constexpr int kRD = 4;       // 16-column blocks of operands in flight per wave
+constexpr int kRD = 4;       // 16-column blocks of operands in flight per wave (large tile: 2)
 
 typedef float rf32x4_t __attribute__((ext_vector_type(4)));
 
+// RT x RT tiles (RT = 32, or 64 for batches that give at least 256 such
+// tiles: each operand block then feeds twice the products, which halves the
+// operand bytes per product), RD blocks of operands in flight.
+template <int RT, int RD>
 __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
     const float *__restrict__ x, int N, int d, const float *__restrict__ wr,
     const float *__restrict__ b, int E, int P, float *__restrict__ out)
 {
-    __shared__ float red[kRW][kRT][kRT + 1];
-    const int t0 = blockIdx.x * kRT, e0 = blockIdx.y * kRT, p = blockIdx.z;
+    constexpr int NT = RT / 16;  // 16-row blocks per tile side
+    __shared__ float red[kRW][RT][RT + 1];
+    const int t0 = blockIdx.x * RT, e0 = blockIdx.y * RT, p = blockIdx.z;
     const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
     const int r = lane % 16, kq = lane / 16;
     const int kw = d / (P * kRW);                    // this wave's columns
     const int kbeg = p * (d / P) + wv * kw + 4 * kq;
     const int nb = kw / 16;                          // 16-column blocks
-    const float *xr[2], *wp[2];
+    const float *xr[NT], *wp[NT];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NT; ++i) {
         xr[i] = x + (size_t)min(t0 + 16 * i + r, N - 1) * d + kbeg;
         wp[i] = wr + (size_t)min(e0 + 16 * i + r, E - 1) * d + kbeg;
     }
-    float4 xa[kRD][2], wb[kRD][2];
-    auto load = [&](int blk, float4 (&xv)[2], float4 (&wv4)[2]) {
+    float4 xa[RD][NT], wb[RD][NT];
+    auto load = [&](int blk, float4 (&xv)[NT], float4 (&wv4)[NT]) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NT; ++i) {
             xv[i] = *reinterpret_cast<const float4 *>(xr[i] + (size_t)blk * 16);
             wv4[i] = *reinterpret_cast<const float4 *>(wp[i] + (size_t)blk * 16);
         }
     };
-    rf32x4_t acc[2][2], part[2][2];
+    rf32x4_t acc[NT][NT], part[NT][NT];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NT; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = rf32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NT; ++j) acc[i][j] = rf32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < kRD; ++s) load(min(s, nb - 1), xa[s], wb[s]);
+    for (int s = 0; s < RD; ++s) load(min(s, nb - 1), xa[s], wb[s]);
     // every load is issued on every path (past the end they reload the last
     // block into a stage no later step reads), so each wait is for one stage.
     // Each pair of blocks (32 columns) is summed from zero on its own and then
     // added to the running sum, which keeps the long dot products' rounding
     // error near that of a blocked sum (the running sum takes d / 32 adds,
     // not d / 4)
-    for (int b0 = 0; b0 < nb; b0 += kRD) {
+    for (int b0 = 0; b0 < nb; b0 += RD) {
 #pragma unroll
-        for (int s = 0; s < kRD; ++s) {
+        for (int s = 0; s < RD; ++s) {
             if (b0 + s >= nb) break;
-            const float xs[2][4] = {{xa[s][0].x, xa[s][0].y, xa[s][0].z, xa[s][0].w},
-                                    {xa[s][1].x, xa[s][1].y, xa[s][1].z, xa[s][1].w}};
-            const float ws[2][4] = {{wb[s][0].x, wb[s][0].y, wb[s][0].z, wb[s][0].w},
-                                    {wb[s][1].x, wb[s][1].y, wb[s][1].z, wb[s][1].w}};
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int it = 0; it < 2; ++it)
+                for (int it = 0; it < NT; ++it)
 #pragma unroll
-                    for (int ie = 0; ie < 2; ++ie)
+                    for (int ie = 0; ie < NT; ++ie)
                         part[it][ie] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                            xs[it][j], ws[ie][j],
+                            xa[s][it][j], wb[s][ie][j],
                             (s % 2 == 0 && j == 0) ? rf32x4_t{0.f, 0.f, 0.f, 0.f} : part[it][ie],
                             0, 0, 0);
             if (s % 2 == 1) {
 #pragma unroll
-                for (int it = 0; it < 2; ++it)
+                for (int it = 0; it < NT; ++it)
 #pragma unroll
-                    for (int ie = 0; ie < 2; ++ie) acc[it][ie] += part[it][ie];
+                    for (int ie = 0; ie < NT; ++ie) acc[it][ie] += part[it][ie];
             }
-            load(min(b0 + s + kRD, nb - 1), xa[s], wb[s]);
+            load(min(b0 + s + RD, nb - 1), xa[s], wb[s]);
         }
     }
     // register v of block (it, ie): token 16 it + 4 kq + v, expert 16 ie + r
 #pragma unroll
-    for (int it = 0; it < 2; ++it)
+    for (int it = 0; it < NT; ++it)
 #pragma unroll
-        for (int ie = 0; ie < 2; ++ie)
+        for (int ie = 0; ie < NT; ++ie)
 #pragma unroll
             for (int v = 0; v < 4; ++v) red[wv][16 * it + 4 * kq + v][16 * ie + r] = acc[it][ie][v];
     __syncthreads();
-    for (int o = tid; o < kRT * kRT; o += kRW * kWave) {
-        const int tt = o / kRT, ee = o % kRT;
+    for (int o = tid; o < RT * RT; o += kRW * kWave) {
+        const int tt = o / RT, ee = o % RT;
         const int t = t0 + tt, e = e0 + ee;
         if (t >= N || e >= E) continue;
         float v = red[0][tt][ee];
@@ -404,9 +405,17 @@ hipError_t launch_router(const float *x, int N, int d, const float *wr, const fl
                                N, d, wr, b, E, out);
     } else if (router_on_mfma(N, d)) {
         const int P = router_slices(N, d, E);
-        dim3 grid((N + kRT - 1) / kRT, (E + kRT - 1) / kRT, P);
-        hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(kRW * kWave), 0, s, x, N, d, wr, b, E, P,
-                           out);
+        // one slice and at least 256 tiles of 64: the large tile
+        const long long big = (long long)((N + 63) / 64) * ((E + 63) / 64);
+        if (P == 1 && big >= 256) {
+            dim3 grid((N + 63) / 64, (E + 63) / 64, 1);
+            hipLaunchKernelGGL((router_mfma_kernel<64, 2>), grid, dim3(kRW * kWave), 0, s, x, N, d,
+                               wr, b, E, P, out);
+        } else {
+            dim3 grid((N + kRT - 1) / kRT, (E + kRT - 1) / kRT, P);
+            hipLaunchKernelGGL((router_mfma_kernel<kRT, kRD>), grid, dim3(kRW * kWave), 0, s, x, N,
+                               d, wr, b, E, P, out);
+        }
     } else {
         const int P = router_slices(N, d, E);
         dim3 grid((N + kTM - 1) / kTM, (E + kTN - 1) / kTN, P);
