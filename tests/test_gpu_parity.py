@@ -370,14 +370,18 @@ def test_route_union_many_experts(E, N, k):
     full_parity(cfg, fused_route=True)
 
 
-def test_group64_scales_every_pass():
+@pytest.mark.parametrize("group", [64, 0, 256])
+def test_group_sizes_every_pass(group):
     """Scale groups of 64 inputs (the container format the README's "Get
-    started" names, gs64) on the decode layer's shapes: each pass alone and
-    the default mix, against one oracle run."""
+    started" names, gs64), one scale per row (0) and groups spanning two
+    128-column unit steps (256), int4, on the decode layer's shapes: each
+    pass alone and the default mix, against one oracle run. (Groups of 64
+    scale each code on the matrix-core passes; 0 and 256 take the 32-token
+    pass's per-step scaling and its bias chain.)"""
     base = synth.CONFIGS["decode64"]
-    cfg = dataclasses.replace(base, layers=(dataclasses.replace(base.layers[0], group=64),))
+    cfg = dataclasses.replace(base, layers=(dataclasses.replace(base.layers[0], group=group),))
     spec, x, wr, b, blocks, shared, _ = oracle_then_pool(cfg)
-    say(f"[gs64] N={cfg.n_tokens} k={cfg.k} G={spec.group}")
+    say(f"[gs{group}] N={cfg.n_tokens} k={cfg.k} G={spec.group}")
     ref = oracle.layer_step(x, wr, b, cfg.k, blocks, shared, spec.d, spec.f, spec.wbits,
                             spec.group)
     pool = upload_pool(spec, blocks, shared)
@@ -385,7 +389,7 @@ def test_group64_scales_every_pass():
         got = run_layer(pool, x, wr, b, cfg.k, mfma_min_tokens=big, mfma_small_min_tokens=small)
         check_routing(got, ref, spec.n_experts)
         err = check_y(got["y"], ref["y"])
-        say(f"[gs64] big={big} small={small} max rel err {err:.2e}")
+        say(f"[gs{group}] big={big} small={small} max rel err {err:.2e}")
     del pool
     torch.cuda.empty_cache()
 
