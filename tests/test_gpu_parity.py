@@ -238,11 +238,13 @@ def test_workspace_size_covers_every_threshold(N, k, big, small):
     full_parity(tiny(n_tokens=N, k=min(k, 16)), mfma_min_tokens=big, mfma_small_min_tokens=small)
 
 
-@pytest.mark.parametrize("group", [0, 32])
+@pytest.mark.parametrize("group", [0, 32, 64, 128])
 @pytest.mark.parametrize("big,small", PASSES)
 def test_tiny_int8_passes(group, big, small):
     """int8 codes (the draft layer's format) on each pass alone and mixed,
-    with per-row and with grouped scales."""
+    with per-row scales, groups finer than a 64-column unit (each code
+    scaled) and groups of whole units (the 32-token pass's per-step scaling
+    and bias chain)."""
     base = synth.CONFIGS["tiny"]
     spec = dataclasses.replace(base.layer, wbits=8, group=group, scale_lo=0.005 / 16,
                                scale_hi=0.02 / 16)
