@@ -360,11 +360,13 @@ def test_single_token_zero_gate_equals_dropped_slot(wbits):
 
 
 @pytest.mark.parametrize("E,N,k", [(1000, 2, 32), (1000, 3, 32), (1024, 1, 7), (65, 9, 7),
-                                   (1000, 40, 32)])
+                                   (1000, 40, 32), (300, 4096, 8)])
 def test_route_union_many_experts(E, N, k):
     """Expert counts that are not a multiple of 64, up to the largest
     supported, on both union paths of the route tail (one wave up to 64
-    assignments, the workgroup above) and the separate kernels (40 tokens)."""
+    assignments, the workgroup above), the separate kernels (40 tokens), and
+    the router's 64 x 64 tiles with a partly filled last expert tile (4096
+    tokens, 300 experts)."""
     base = synth.CONFIGS["tiny"]
     cfg = dataclasses.replace(base, n_tokens=N, k=k,
                               layers=(dataclasses.replace(base.layer, n_experts=E),))
