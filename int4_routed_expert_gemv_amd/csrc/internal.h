@@ -211,7 +211,8 @@ hipError_t launch_combine_norm(const float *o, const float *w, int N, int k, int
 
 // Column j of an 8-column group goes to position perm8<WB>(j) of the matrix
 // cores' float16 operand, in the order the weight operand takes its codes
-// (int4: the low nibbles of a word's four bytes, then the high nibbles).
+// (int4: columns 0,4,1,5,2,6,3,7, i.e. the low nibbles of bytes 0 and 2,
+// their high nibbles, then the same of bytes 1 and 3; int8: 0,2,1,3,4,6,5,7).
 template <int WB>
 __device__ __forceinline__ int perm8(int j)
 {
