@@ -159,10 +159,11 @@ struct MfmaArgs {
 // Where the scales are applied (SM):
 //  kScaleCode: each code times its group's scale, rounded to float16, enters
 //    the matrix cores (any group size);
-//  kScaleStep: the codes enter unscaled (exact small integers) and each unit
-//    step's float32 products are scaled per row afterwards (groups that cover
-//    whole unit steps): fewer vector instructions per code, no float16
-//    rounding of code x scale;
+//  kScaleStep: the codes enter unscaled (exact small integers, or exact
+//    biased values whose biases the gate/up kernel takes out with its bias
+//    chain) and each unit step's float32 products are scaled per row
+//    afterwards (groups that cover whole unit steps): fewer vector
+//    instructions per code, no float16 rounding of code x scale;
 //  kScaleRow: one scale per row (group 0): the unscaled products accumulate
 //    over the whole row and the float32 sums are scaled once, in the
 //    epilogue (no per-step work at all).
